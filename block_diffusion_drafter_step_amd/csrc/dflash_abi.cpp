@@ -1,0 +1,519 @@
+// C-ABI entry points of libdflash (declared in include/dflash.h).
+//
+// Every call validates all of its arguments on the host before it touches
+// the GPU, so an invalid call has no side effects and needs no device; only
+// then does it carve the caller's workspace and enqueue the kernels on the
+// caller's stream.  Nothing here allocates, frees or synchronises.
+#include "dflash.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kernels.h"
+
+using namespace dfl;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dflash_status fail(dflash_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+#define TRY(expr)                              \
+  do {                                         \
+    const dflash_status s_ = (expr);           \
+    if (s_ != DFLASH_OK) return s_;            \
+  } while (0)
+
+dflash_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(DFLASH_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = 0;
+  return DFLASH_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+dflash_status need_ptr(const void *p, const char *name) {
+  if (!p) return fail(DFLASH_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(DFLASH_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return DFLASH_OK;
+}
+
+dflash_status check_act(int32_t act) {
+  if (act != DFLASH_F32 && act != DFLASH_BF16)
+    return fail(DFLASH_ERR_INVALID_ARG, "act must be DFLASH_F32 or DFLASH_BF16 (got %d)", act);
+  return DFLASH_OK;
+}
+
+// A projection weight: shape [rows][cols]; fp32 with fp32 activations, bf16
+// or Q8_0 with bf16 activations (`allow_q8` false: the act type only).
+dflash_status check_weight(const dflash_weight *w, const char *name, int64_t rows, int64_t cols,
+                           int32_t act, bool allow_q8) {
+  if (!w) return fail(DFLASH_ERR_INVALID_ARG, "%s is NULL", name);
+  if (w->rows != rows || w->cols != cols)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s is [%lld][%lld], expected [%lld][%lld]", name,
+                (long long)w->rows, (long long)w->cols, (long long)rows, (long long)cols);
+  if (w->dtype == DFLASH_Q8_0) {
+    if (!allow_q8) return fail(DFLASH_ERR_UNSUPPORTED, "%s cannot be Q8_0", name);
+    if (act != DFLASH_BF16)
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: Q8_0 weights need bf16 activations", name);
+    if (cols % 32) return fail(DFLASH_ERR_INVALID_ARG, "%s: Q8_0 needs cols %% 32 == 0", name);
+    TRY(need_ptr(w->scales, "Q8_0 scales"));
+  } else if (w->dtype != act) {
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: dtype %d does not match the activation type %d", name,
+                w->dtype, act);
+  }
+  TRY(need_ptr(w->data, name));
+  return DFLASH_OK;
+}
+
+dflash_status check_ws(void *ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return DFLASH_OK;
+  if (!ws) return fail(DFLASH_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned16(ws)) return fail(DFLASH_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(DFLASH_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return DFLASH_OK;
+}
+
+// bump allocator over the caller's workspace (256-byte aligned pieces)
+struct Carve {
+  char *base;
+  size_t off = 0;
+  explicit Carve(void *p) : base((char *)p) {}
+  void *take(size_t bytes) {
+    void *p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  }
+};
+
+int wkind_of(const dflash_weight *w) { return w->dtype == DFLASH_Q8_0 ? W_Q8_0 : W_SAME; }
+
+WSet wset(std::initializer_list<const dflash_weight *> ws) {
+  WSet s;
+  memset(&s, 0, sizeof s);
+  int n = 0, tot = 0;
+  for (const dflash_weight *w : ws) {
+    s.data[n] = w->data;
+    s.scales[n] = w->scales;
+    s.rows[n] = (int)w->rows;
+    tot += (int)w->rows;
+    s.K = (int)w->cols;
+    ++n;
+  }
+  s.n_seg = n;
+  s.n_total = tot;
+  return s;
+}
+
+ASrc asrc1(const void *p, int k) {
+  ASrc a;
+  memset(&a, 0, sizeof a);
+  a.ptr[0] = p;
+  a.n_src = 1;
+  a.k_per_src = k;
+  return a;
+}
+
+OutSpec out_f32(void *p, long ld) {
+  OutSpec o;
+  memset(&o, 0, sizeof o);
+  o.mode = OUT_F32;
+  o.out = p;
+  o.ld = ld;
+  return o;
+}
+
+OutSpec out_act(void *p, long ld, const void *resid, long ld_resid) {
+  OutSpec o = out_f32(p, ld);
+  o.mode = OUT_ACT;
+  o.resid = resid;
+  o.ld_resid = ld_resid;
+  return o;
+}
+
+hipError_t gemm(int act, int wkind, const ASrc &A, int M, const WSet &W, float *part,
+                const OutSpec &o, hipStream_t st) {
+  if (M <= kSkinnyMaxM) return launch_skinny_gemm(act, wkind, A, M, W, part, o, st);
+  return launch_tile_gemm(act, wkind, A, M, W, o, st);
+}
+
+size_t gemm_partial_bytes(int M, int N, int K) {
+  return M <= kSkinnyMaxM ? skinny_partial_floats(N, K) * sizeof(float) : 0;
+}
+
+constexpr int64_t kMaxRows = (int64_t)1 << 26;
+
+// --- workspace sizes (buffers in the act type are sized for fp32) --------------
+
+size_t inject_ws(int32_t n_layers, int64_t n, int32_t d_t, int32_t d, int32_t kv) {
+  Carve c(nullptr);
+  c.take(std::max(gemm_partial_bytes((int)n, d, n_layers * d_t), gemm_partial_bytes((int)n, 2 * kv, d)));
+  c.take((size_t)n * d * 4);  // y
+  c.take((size_t)n * d * 4);  // z
+  return c.off;
+}
+
+size_t conv_ws(int32_t n_blocks, int32_t B, int32_t C, int32_t G, int32_t T) {
+  Carve c(nullptr);
+  const int64_t M = (int64_t)n_blocks * B;
+  c.take(gemm_partial_bytes((int)M, T * G, C));
+  c.take((size_t)M * T * G * 4);  // delta
+  return c.off;
+}
+
+size_t attn_ws(int32_t B, int32_t d, int32_t Hq, int32_t Hkv, int32_t hd, int64_t n_ctx) {
+  Carve c(nullptr);
+  const int qdim = Hq * hd, kv = Hkv * hd;
+  c.take(std::max(gemm_partial_bytes(B, qdim + 2 * kv, d), gemm_partial_bytes(B, d, qdim)));
+  c.take((size_t)B * (qdim + 2 * kv) * 4);  // Q | Kb | Vb
+  int chunk, n_split;
+  attn_plan(n_ctx + B, Hkv, &chunk, &n_split);
+  c.take((size_t)Hq * B * n_split * hd * 4);  // partial O
+  c.take((size_t)Hq * B * n_split * 2 * 4);   // partial (max, sum)
+  c.take((size_t)B * qdim * 4);               // O
+  return c.off;
+}
+
+size_t topk_ws(int64_t V, int32_t K) {
+  Carve c(nullptr);
+  const int n_wg = topk_plan_wgs(V);
+  c.take((size_t)n_wg * 16 * K * 4);
+  c.take((size_t)n_wg * 16 * K * 4);
+  c.take((size_t)n_wg * 16 * 2 * 4);
+  return c.off;
+}
+
+size_t sel_ws(int32_t B, int32_t r, int32_t d) {
+  Carve c(nullptr);
+  c.take(gemm_partial_bytes(B, r, d));
+  c.take((size_t)B * r * 4);
+  return c.off;
+}
+
+dflash_status check_cache(const dflash_kv_cache *cache, int32_t act) {
+  if (!cache) return fail(DFLASH_ERR_INVALID_ARG, "cache is NULL");
+  if (cache->dtype != act)
+    return fail(DFLASH_ERR_INVALID_ARG, "cache dtype %d does not match the activation type %d",
+                cache->dtype, act);
+  if (cache->head_dim != 64 && cache->head_dim != 128)
+    return fail(DFLASH_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", cache->head_dim);
+  if (cache->n_kv_heads < 1) return fail(DFLASH_ERR_INVALID_ARG, "n_kv_heads must be >= 1");
+  if (cache->capacity < 1 || cache->capacity > kMaxRows)
+    return fail(DFLASH_ERR_INVALID_ARG, "cache capacity out of range");
+  TRY(need_ptr(cache->k, "cache.k"));
+  TRY(need_ptr(cache->v, "cache.v"));
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dflash_status_string(int32_t s) {
+  switch (s) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_ERR_INVALID_ARG: return "invalid argument";
+    case DFLASH_ERR_UNSUPPORTED: return "unsupported";
+    case DFLASH_ERR_CAPACITY: return "KV-cache capacity exceeded";
+    case DFLASH_ERR_WORKSPACE: return "workspace missing or too small";
+    case DFLASH_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char *dflash_last_error(void) { return g_err; }
+
+int32_t dflash_version(void) { return 100; }
+
+size_t dflash_inject_workspace(int32_t n_layers, int64_t n_tokens, int32_t d_t, int32_t d,
+                               int32_t kv, int32_t act) {
+  (void)act;
+  if (n_layers < 1 || n_tokens < 1 || d_t < 1 || d < 1 || kv < 1) return 0;
+  return inject_ws(n_layers, n_tokens, d_t, d, kv);
+}
+
+size_t dflash_conv_workspace(int32_t n_blocks, int32_t B, int32_t C, int32_t G, int32_t T) {
+  if (n_blocks < 1 || B < 1 || C < 1 || G < 1 || T < 1) return 0;
+  return conv_ws(n_blocks, B, C, G, T);
+}
+
+size_t dflash_block_attn_workspace(int32_t B, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, int64_t n_ctx) {
+  if (B < 1 || d < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1 || n_ctx < 0) return 0;
+  return attn_ws(B, d, n_q_heads, n_kv_heads, head_dim, n_ctx);
+}
+
+size_t dflash_topk_unary_workspace(int32_t B, int64_t V, int32_t K) {
+  (void)B;
+  if (V < 1 || K < 1) return 0;
+  return topk_ws(V, K);
+}
+
+size_t dflash_selector_edges_workspace(int32_t B, int32_t r, int32_t d, int32_t K) {
+  (void)K;
+  if (B < 1 || r < 1 || d < 1) return 0;
+  return sel_ws(B, r, d);
+}
+
+// ---------------------------------------------------------------------------
+
+dflash_status dflash_inject(const void *const *layer_hidden, int32_t n_layers, int64_t n_tokens,
+                            int32_t d_t, int32_t act, const dflash_weight *fc, const void *gamma,
+                            float eps, const dflash_weight *wk, const dflash_weight *wv,
+                            const dflash_kv_cache *cache, int64_t pos0, void *ws, size_t ws_bytes,
+                            void *stream) {
+  TRY(check_act(act));
+  if (!layer_hidden) return fail(DFLASH_ERR_INVALID_ARG, "layer_hidden is NULL");
+  if (n_layers < 1 || n_layers > DFLASH_MAX_LAYERS)
+    return fail(DFLASH_ERR_INVALID_ARG, "n_layers must be in [1, %d]", DFLASH_MAX_LAYERS);
+  if (n_tokens < 1 || n_tokens > kMaxRows) return fail(DFLASH_ERR_INVALID_ARG, "n_tokens out of range");
+  if (d_t < 64 || d_t % 64) return fail(DFLASH_ERR_INVALID_ARG, "d_t must be a positive multiple of 64");
+  for (int l = 0; l < n_layers; ++l) TRY(need_ptr(layer_hidden[l], "layer_hidden[l]"));
+  if (!fc) return fail(DFLASH_ERR_INVALID_ARG, "fc is NULL");
+  const int64_t d = fc->rows;
+  if (d < 64 || d % 64) return fail(DFLASH_ERR_INVALID_ARG, "d (fc rows) must be a positive multiple of 64");
+  TRY(check_weight(fc, "fc", d, (int64_t)n_layers * d_t, act, true));
+  TRY(check_cache(cache, act));
+  const int64_t kv = (int64_t)cache->n_kv_heads * cache->head_dim;
+  TRY(check_weight(wk, "wk", kv, d, act, true));
+  TRY(check_weight(wv, "wv", kv, d, act, true));
+  if (wk->dtype != wv->dtype) return fail(DFLASH_ERR_UNSUPPORTED, "wk and wv must share a dtype");
+  if (gamma) TRY(need_ptr(gamma, "gamma"));
+  if (!(eps >= 0.f)) return fail(DFLASH_ERR_INVALID_ARG, "eps must be >= 0");
+  if (pos0 < 0 || pos0 + n_tokens > cache->capacity)
+    return fail(DFLASH_ERR_CAPACITY, "rows [%lld, %lld) exceed capacity %lld", (long long)pos0,
+                (long long)(pos0 + n_tokens), (long long)cache->capacity);
+  const size_t need = inject_ws(n_layers, n_tokens, d_t, (int)d, (int)kv);
+  TRY(check_ws(ws, ws_bytes, need));
+
+  hipStream_t st = (hipStream_t)stream;
+  Carve c(ws);
+  const int n = (int)n_tokens;
+  float *part = (float *)c.take(std::max(gemm_partial_bytes(n, (int)d, n_layers * d_t),
+                                         gemm_partial_bytes(n, 2 * (int)kv, (int)d)));
+  float *y = (float *)c.take((size_t)n * d * 4);
+  void *z = c.take((size_t)n * d * 4);
+
+  ASrc A;
+  memset(&A, 0, sizeof A);
+  for (int l = 0; l < n_layers; ++l) A.ptr[l] = layer_hidden[l];
+  A.n_src = n_layers;
+  A.k_per_src = d_t;
+  hipError_t e = gemm(act, wkind_of(fc), A, n, wset({fc}), part, out_f32(y, d), st);
+  if (e != hipSuccess) return launched(e, "fc");
+  e = launch_rmsnorm(act, y, n, (int)d, gamma, eps, z, st);
+  if (e != hipSuccess) return launched(e, "rmsnorm");
+  OutSpec oc;
+  memset(&oc, 0, sizeof oc);
+  oc.mode = OUT_CACHE;
+  oc.ck = cache->k;
+  oc.cv = cache->v;
+  oc.hd = cache->head_dim;
+  oc.split = (int)kv;
+  oc.cap = cache->capacity;
+  oc.pos0 = pos0;
+  e = gemm(act, wkind_of(wk), asrc1(z, (int)d), n, wset({wk, wv}), part, oc, st);
+  return launched(e, "wk/wv");
+}
+
+dflash_status dflash_conv(const void *x, int32_t n_blocks, int32_t B, int32_t C, int32_t G,
+                          int32_t T, int32_t act, const void *base, const dflash_weight *w_delta,
+                          void *out, void *ws, size_t ws_bytes, void *stream) {
+  TRY(check_act(act));
+  TRY(need_ptr(x, "x"));
+  TRY(need_ptr(base, "base"));
+  TRY(need_ptr(out, "out"));
+  if (n_blocks < 1 || B < 1 || (int64_t)n_blocks * B > kMaxRows)
+    return fail(DFLASH_ERR_INVALID_ARG, "n_blocks and B must be >= 1");
+  if (C < 64 || C % 64) return fail(DFLASH_ERR_INVALID_ARG, "C must be a positive multiple of 64");
+  if (G < 1 || C % G) return fail(DFLASH_ERR_INVALID_ARG, "G must divide C");
+  if (T < 1 || T > 16) return fail(DFLASH_ERR_INVALID_ARG, "T must be in [1, 16]");
+  TRY(check_weight(w_delta, "w_delta", (int64_t)T * G, C, act, false));
+  const size_t need = conv_ws(n_blocks, B, C, G, T);
+  TRY(check_ws(ws, ws_bytes, need));
+
+  hipStream_t st = (hipStream_t)stream;
+  Carve c(ws);
+  const int M = n_blocks * B;
+  float *part = (float *)c.take(gemm_partial_bytes(M, T * G, C));
+  float *delta = (float *)c.take((size_t)M * T * G * 4);
+  hipError_t e = gemm(act, W_SAME, asrc1(x, C), M, wset({w_delta}), part, out_f32(delta, T * G), st);
+  if (e != hipSuccess) return launched(e, "delta");
+  e = launch_conv(act, x, n_blocks, B, C, G, T, base, delta, out, st);
+  return launched(e, "conv");
+}
+
+dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, int32_t d,
+                                int32_t n_q_heads, int32_t act, const dflash_weight *wq,
+                                const dflash_weight *wk, const dflash_weight *wv,
+                                const dflash_weight *wo, const dflash_kv_cache *cache,
+                                int64_t n_ctx, float scale, void *out, void *ws, size_t ws_bytes,
+                                void *stream) {
+  TRY(check_act(act));
+  TRY(need_ptr(u, "u"));
+  if (residual) TRY(need_ptr(residual, "residual"));
+  TRY(need_ptr(out, "out"));
+  if (B < 1 || B > DFLASH_MAX_BLOCK)
+    return fail(DFLASH_ERR_INVALID_ARG, "B must be in [1, %d]", DFLASH_MAX_BLOCK);
+  if (d < 64 || d % 64) return fail(DFLASH_ERR_INVALID_ARG, "d must be a positive multiple of 64");
+  TRY(check_cache(cache, act));
+  const int Hkv = cache->n_kv_heads, hd = cache->head_dim;
+  if (n_q_heads < 1 || n_q_heads % Hkv)
+    return fail(DFLASH_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (n_q_heads / Hkv > 8) return fail(DFLASH_ERR_UNSUPPORTED, "at most 8 query heads per KV head");
+  const int64_t qdim = (int64_t)n_q_heads * hd, kv = (int64_t)Hkv * hd;
+  TRY(check_weight(wq, "wq", qdim, d, act, true));
+  TRY(check_weight(wk, "wk", kv, d, act, true));
+  TRY(check_weight(wv, "wv", kv, d, act, true));
+  TRY(check_weight(wo, "wo", d, qdim, act, true));
+  if (wq->dtype != wk->dtype || wq->dtype != wv->dtype)
+    return fail(DFLASH_ERR_UNSUPPORTED, "wq, wk and wv must share a dtype");
+  if (n_ctx < 0 || n_ctx > cache->capacity)
+    return fail(DFLASH_ERR_CAPACITY, "n_ctx %lld outside [0, capacity %lld]", (long long)n_ctx,
+                (long long)cache->capacity);
+  if (!(scale >= 0.f)) return fail(DFLASH_ERR_INVALID_ARG, "scale must be >= 0");
+  const size_t need = attn_ws(B, d, n_q_heads, Hkv, hd, n_ctx);
+  TRY(check_ws(ws, ws_bytes, need));
+
+  hipStream_t st = (hipStream_t)stream;
+  Carve c(ws);
+  const int nqkv = (int)(qdim + 2 * kv);
+  float *part = (float *)c.take(std::max(gemm_partial_bytes(B, nqkv, d), gemm_partial_bytes(B, d, (int)qdim)));
+  void *qkv = c.take((size_t)B * nqkv * 4);
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  attn_plan(n_ctx + B, Hkv, &a.chunk, &a.n_split);
+  a.part_o = (float *)c.take((size_t)n_q_heads * B * a.n_split * hd * 4);
+  a.part_ml = (float *)c.take((size_t)n_q_heads * B * a.n_split * 2 * 4);
+  void *o = c.take((size_t)B * qdim * 4);
+
+  hipError_t e = gemm(act, wkind_of(wq), asrc1(u, d), B, wset({wq, wk, wv}), part,
+                      out_act(qkv, nqkv, nullptr, 0), st);
+  if (e != hipSuccess) return launched(e, "qkv");
+  a.qkv = qkv;
+  a.ck = cache->k;
+  a.cv = cache->v;
+  a.cap = cache->capacity;
+  a.n_ctx = n_ctx;
+  a.B = B;
+  a.Hq = n_q_heads;
+  a.Hkv = Hkv;
+  a.hd = hd;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)hd);
+  a.o = o;
+  e = launch_attention(act, a, st);
+  if (e != hipSuccess) return launched(e, "attention");
+  e = gemm(act, wkind_of(wo), asrc1(o, (int)qdim), B, wset({wo}), part, out_act(out, d, residual, d), st);
+  return launched(e, "wo");
+}
+
+dflash_status dflash_topk_unary(const void *h, int32_t B, int32_t act,
+                                const dflash_weight *lm_head, int32_t K, int32_t *idx,
+                                float *unary, void *ws, size_t ws_bytes, void *stream) {
+  TRY(check_act(act));
+  TRY(need_ptr(h, "h"));
+  TRY(need_ptr(idx, "idx"));
+  TRY(need_ptr(unary, "unary"));
+  if (B < 1 || B > DFLASH_MAX_BLOCK)
+    return fail(DFLASH_ERR_INVALID_ARG, "B must be in [1, %d]", DFLASH_MAX_BLOCK);
+  if (!lm_head) return fail(DFLASH_ERR_INVALID_ARG, "lm_head is NULL");
+  const int64_t V = lm_head->rows, d = lm_head->cols;
+  if (d < 64 || d % 64) return fail(DFLASH_ERR_INVALID_ARG, "d must be a positive multiple of 64");
+  if (V < 1 || V >= ((int64_t)1 << 31)) return fail(DFLASH_ERR_INVALID_ARG, "V out of range");
+  TRY(check_weight(lm_head, "lm_head", V, d, act, true));
+  if (K < 1 || K > DFLASH_MAX_TOPK || K > V)
+    return fail(DFLASH_ERR_INVALID_ARG, "K must be in [1, min(V, %d)]", DFLASH_MAX_TOPK);
+  const size_t need = topk_ws(V, K);
+  TRY(check_ws(ws, ws_bytes, need));
+
+  Carve c(ws);
+  TopkArgs a;
+  memset(&a, 0, sizeof a);
+  a.h = h;
+  a.B = B;
+  a.d = (int)d;
+  a.w = lm_head->data;
+  a.scales = lm_head->scales;
+  a.V = V;
+  a.K = K;
+  a.n_wg = topk_plan_wgs(V);
+  a.part_val = (float *)c.take((size_t)a.n_wg * 16 * K * 4);
+  a.part_idx = (int *)c.take((size_t)a.n_wg * 16 * K * 4);
+  a.part_ms = (float *)c.take((size_t)a.n_wg * 16 * 2 * 4);
+  a.idx = idx;
+  a.unary = unary;
+  return launched(launch_topk(act, wkind_of(lm_head), a, (hipStream_t)stream), "topk");
+}
+
+dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
+                                    const dflash_weight *proj, const void *cb_pred,
+                                    const void *cb_succ, int64_t V, const int32_t *idx,
+                                    const float *unary, int32_t K, int32_t anchor, float *edges,
+                                    int32_t *path, void *ws, size_t ws_bytes, void *stream) {
+  TRY(check_act(act));
+  TRY(need_ptr(h, "h"));
+  TRY(need_ptr(cb_pred, "cb_pred"));
+  TRY(need_ptr(cb_succ, "cb_succ"));
+  TRY(need_ptr(idx, "idx"));
+  TRY(need_ptr(unary, "unary"));
+  TRY(need_ptr(edges, "edges"));
+  TRY(need_ptr(path, "path"));
+  if (B < 1 || B > DFLASH_MAX_BLOCK)
+    return fail(DFLASH_ERR_INVALID_ARG, "B must be in [1, %d]", DFLASH_MAX_BLOCK);
+  if (K < 1 || K > DFLASH_MAX_TOPK)
+    return fail(DFLASH_ERR_INVALID_ARG, "K must be in [1, %d]", DFLASH_MAX_TOPK);
+  if (!proj) return fail(DFLASH_ERR_INVALID_ARG, "proj is NULL");
+  const int64_t r = proj->rows, d = proj->cols;
+  if (r < 16 || r % 16 || r > 256) return fail(DFLASH_ERR_INVALID_ARG, "r must be a multiple of 16 in [16, 256]");
+  if (d < 64 || d % 64) return fail(DFLASH_ERR_INVALID_ARG, "d must be a positive multiple of 64");
+  TRY(check_weight(proj, "proj", r, d, act, false));
+  if (V < K || V >= ((int64_t)1 << 31)) return fail(DFLASH_ERR_INVALID_ARG, "V must be in [K, 2^31)");
+  if (anchor < -1 || anchor >= V) return fail(DFLASH_ERR_INVALID_ARG, "anchor must be in [-1, V)");
+  const size_t need = sel_ws(B, (int)r, (int)d);
+  TRY(check_ws(ws, ws_bytes, need));
+
+  hipStream_t st = (hipStream_t)stream;
+  Carve c(ws);
+  float *part = (float *)c.take(gemm_partial_bytes(B, (int)r, (int)d));
+  float *pj = (float *)c.take((size_t)B * r * 4);
+  hipError_t e = gemm(act, W_SAME, asrc1(h, (int)d), B, wset({proj}), part, out_f32(pj, r), st);
+  if (e != hipSuccess) return launched(e, "project");
+  SelArgs a;
+  a.proj = pj;
+  a.cb_pred = cb_pred;
+  a.cb_succ = cb_succ;
+  a.V = V;
+  a.r = (int)r;
+  a.B = B;
+  a.K = K;
+  a.anchor = anchor;
+  a.idx = idx;
+  a.unary = unary;
+  a.edges = edges;
+  a.path = path;
+  return launched(launch_selector(act, a, st), "selector");
+}
+
+dflash_status dflash_accept_len(const int32_t *draft, const int32_t *target, int32_t n_seq,
+                                int32_t B, int32_t *accept, void *stream) {
+  TRY(need_ptr(draft, "draft"));
+  TRY(need_ptr(target, "target"));
+  TRY(need_ptr(accept, "accept"));
+  if (n_seq < 1 || B < 1) return fail(DFLASH_ERR_INVALID_ARG, "n_seq and B must be >= 1");
+  return launched(launch_accept(draft, target, n_seq, B, accept, (hipStream_t)stream), "accept");
+}
+
+}  // extern "C"

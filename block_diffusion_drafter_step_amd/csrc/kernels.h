@@ -1,0 +1,136 @@
+// Host-side launchers of the libdflash kernels and the plain structs that
+// describe their operands.  Included by the kernel sources and by the C-ABI
+// layer; nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dfl {
+
+enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
+enum WKind { W_SAME = 0, W_Q8_0 = 1 };  // weight stored in the act type, or Q8_0
+
+constexpr int kMaxSrc = 16;  // K-concatenated activation sources
+constexpr int kMaxSeg = 3;   // N-concatenated weights
+
+// Activation operand [M][K] given as up to kMaxSrc arrays [M][k_per_src]
+// side by side along K (the concatenation is never materialised).
+struct ASrc {
+  const void *ptr[kMaxSrc];
+  int n_src;
+  int k_per_src;  // columns of each array; K = n_src * k_per_src
+};
+
+// Up to kMaxSeg weights [rows_s][K] stacked along N (rows 0..rows_0-1 are
+// weight 0, and so on).  All share K and the storage kind.
+struct WSet {
+  const void *data[kMaxSeg];
+  const void *scales[kMaxSeg];  // Q8_0: fp16 [rows][K/32]
+  int rows[kMaxSeg];
+  int n_seg;
+  int n_total;
+  int K;
+};
+
+// Where a GEMM's fp32 result Y[t][n] goes.
+enum OutMode {
+  OUT_F32 = 0,    // float out[t * ld + col0 + n]
+  OUT_ACT = 1,    // act out[t * ld + col0 + n] = round(Y + resid[t * ld_resid + n])
+  OUT_CACHE = 2   // n < split -> K cache, else V cache; head n / hd, row pos0 + t
+};
+
+struct OutSpec {
+  int mode;
+  void *out;
+  long ld;
+  long col0;
+  const void *resid;  // OUT_ACT: optional residual in the act type
+  long ld_resid;
+  void *ck;
+  void *cv;
+  int hd;
+  int split;          // OUT_CACHE: columns that go to K
+  long cap;
+  long pos0;
+};
+
+// ---- GEMM family -----------------------------------------------------------
+
+// Rows of the weight-streaming path: M <= 16 activation rows.
+constexpr int kSkinnyMaxM = 16;
+
+// Workspace floats of the split-K partials of a skinny GEMM.
+size_t skinny_partial_floats(int n_total, int K);
+// Y = X . W^T for M <= 16 rows: split-K partials, then a fixed-order reduce
+// into `out`.  `part` holds skinny_partial_floats() floats.
+hipError_t launch_skinny_gemm(int act, int wkind, const ASrc &X, int M, const WSet &W, float *part,
+                              const OutSpec &out, hipStream_t st);
+// Y = A . W^T for any M (tiled MFMA GEMM, LDS-staged, no split-K).
+hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet &W,
+                            const OutSpec &out, hipStream_t st);
+
+// ---- injection -----------------------------------------------------------------
+// z[t] = round(y[t] / sqrt(mean(y[t]^2) + eps) * gamma), y fp32 [n][d].
+hipError_t launch_rmsnorm(int act, const float *y, int n, int d, const void *gamma, float eps,
+                          void *z, hipStream_t st);
+
+// ---- conv ------------------------------------------------------------------------
+// out[b][i][c] = sum_t (base[t][c] + delta[b*B + i][t*G + g(c)]) * x[b][i - t][c]
+hipError_t launch_conv(int act, const void *x, int n_blocks, int B, int C, int G, int T,
+                       const void *base, const float *delta, void *out, hipStream_t st);
+
+// ---- attention ---------------------------------------------------------------------
+struct AttnArgs {
+  const void *qkv;   // [B][Hq*hd + 2*Hkv*hd] in the act type: Q | Kb | Vb
+  const void *ck;    // cache [Hkv][cap][hd]
+  const void *cv;
+  long cap;
+  long n_ctx;
+  int B, Hq, Hkv, hd;
+  float scale;
+  int chunk;         // keys per split
+  int n_split;
+  float *part_o;     // [Hq][B][n_split][hd]
+  float *part_ml;    // [Hq][B][n_split][2]
+  void *o;           // [B][Hq*hd] in the act type
+};
+void attn_plan(long n_keys, int Hkv, int *chunk, int *n_split);
+hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st);
+
+// ---- LM head top-K -------------------------------------------------------------------
+struct TopkArgs {
+  const void *h;      // [B][d] in the act type
+  int B, d;
+  const void *w;      // [V][d] codes or values
+  const void *scales; // Q8_0 scales or null
+  long V;
+  int K;
+  int n_wg;
+  float *part_val;    // [n_wg][16][K]
+  int *part_idx;      // [n_wg][16][K]
+  float *part_ms;     // [n_wg][16][2]
+  int *idx;           // [B][K]
+  float *unary;       // [B][K]
+};
+int topk_plan_wgs(long V);
+hipError_t launch_topk(int act, int wkind, const TopkArgs &a, hipStream_t st);
+
+// ---- selector ------------------------------------------------------------------------
+struct SelArgs {
+  const float *proj;  // [B][r] fp32
+  const void *cb_pred, *cb_succ;  // [V][r] act type
+  long V;
+  int r, B, K, anchor;
+  const int *idx;
+  const float *unary;
+  float *edges;       // [B][K][K]
+  int *path;          // [B]
+};
+hipError_t launch_selector(int act, const SelArgs &a, hipStream_t st);
+
+hipError_t launch_accept(const int *draft, const int *target, int n_seq, int B, int *accept,
+                         hipStream_t st);
+
+}  // namespace dfl

@@ -1,0 +1,118 @@
+"""Device staging and orchestration of the draft block step (host logic only).
+
+`to_device` moves the seeded inputs of synth.Workload onto the GPU in the
+storage formats libdflash reads; `BlockStep` owns the outputs and
+workspaces of one block step and enqueues the six library calls in order on
+one stream.  No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import dflash as D
+from . import synth
+
+
+def act_tensor(a: np.ndarray, act: str, device="cuda") -> torch.Tensor:
+    if act == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def weight_tensor(w: dict, device="cuda") -> D.Weight:
+    if w["dtype"] == "q8_0":
+        return D.Weight("q8_0", torch.from_numpy(w["data"]).to(device),
+                        torch.from_numpy(w["scales"]).to(device))
+    return D.Weight(w["dtype"], act_tensor(w["data"], w["dtype"], device))
+
+
+def act_dtype(act: str):
+    return torch.bfloat16 if act == "bf16" else torch.float32
+
+
+def new_cache(cfg, device="cuda") -> D.KVCache:
+    shp = (cfg.Hkv, cfg.cap, cfg.hd)
+    return D.KVCache(torch.zeros(shp, dtype=act_dtype(cfg.act), device=device),
+                     torch.zeros(shp, dtype=act_dtype(cfg.act), device=device))
+
+
+class DeviceWeights:
+    """All weights of one draft layer plus the shared head and selector."""
+
+    def __init__(self, w: synth.Workload, device="cuda"):
+        cfg = w.cfg
+        self.cfg = cfg
+        self.fc = weight_tensor(w.fc(), device)
+        self.wq = weight_tensor(w.wq(), device)
+        self.wk = weight_tensor(w.wk(), device)
+        self.wv = weight_tensor(w.wv(), device)
+        self.wo = weight_tensor(w.wo(), device)
+        self.base = act_tensor(w.conv_base(), cfg.act, device)
+        self.w_delta = weight_tensor(w.w_delta(), device)
+        self.w_lm = weight_tensor(w.w_lm(), device)
+        w.drop("wlm")
+        self.sel_P = weight_tensor(w.sel_proj(), device)
+        A, Bc = w.codebooks()
+        self.cb_pred = act_tensor(A, cfg.act, device)
+        self.cb_succ = act_tensor(Bc, cfg.act, device)
+
+
+class BlockStep:
+    """Buffers of one block step: conv -> block attention (+ residual) ->
+    LM-head top-K -> selector edges + path -> accept length; optionally an
+    injection of `inject_n` rows first."""
+
+    def __init__(self, cfg, weights: DeviceWeights, cache: D.KVCache, inject_n: int = 0, device="cuda"):
+        self.cfg, self.W, self.cache = cfg, weights, cache
+        dt = act_dtype(cfg.act)
+        B, d = cfg.B, cfg.d
+        self.u = torch.empty((1, B, cfg.C), dtype=dt, device=device)
+        self.h = torch.empty((B, d), dtype=dt, device=device)
+        self.idx = torch.empty((B, cfg.K), dtype=torch.int32, device=device)
+        self.unary = torch.empty((B, cfg.K), dtype=torch.float32, device=device)
+        self.edges = torch.empty((B, cfg.K, cfg.K), dtype=torch.float32, device=device)
+        self.path = torch.empty((1, B), dtype=torch.int32, device=device)
+        self.accept = torch.empty((1,), dtype=torch.int32, device=device)
+        self.inject_n = inject_n
+        n_ctx_max = cache.k.shape[1]
+        sizes = [D.dflash_conv_workspace(1, B, cfg.C, cfg.G, cfg.T),
+                 D.dflash_block_attn_workspace(B, d, cfg.Hq, cfg.Hkv, cfg.hd, n_ctx_max),
+                 D.dflash_topk_unary_workspace(B, cfg.V, cfg.K),
+                 D.dflash_selector_edges_workspace(B, cfg.r, d, cfg.K)]
+        if inject_n:
+            sizes.append(D.dflash_inject_workspace(cfg.L_t, inject_n, cfg.d_t, d, cfg.kv, cfg.act))
+        # one workspace reused by every call: the calls are stream-ordered
+        self.ws = D.workspace(max(sizes), device)
+
+    def inject(self, hidden, pos0: int, stream=None):
+        W = self.W
+        D.dflash_inject(hidden, W.fc, None, self.cfg.eps, W.wk, W.wv, self.cache, pos0, self.ws, stream)
+
+    def conv(self, x, stream=None):
+        D.dflash_conv(x, self.cfg.G, self.W.base, self.W.w_delta, self.u, self.ws, stream)
+
+    def attn(self, x, n_ctx: int, stream=None):
+        W = self.W
+        D.dflash_block_attn(self.u[0], x[0], self.cfg.Hq, W.wq, W.wk, W.wv, W.wo, self.cache, n_ctx, 0.0,
+                            self.h, self.ws, stream)
+
+    def topk(self, stream=None):
+        D.dflash_topk_unary(self.h, self.W.w_lm, self.cfg.K, self.idx, self.unary, self.ws, stream)
+
+    def select(self, anchor: int, stream=None):
+        W = self.W
+        D.dflash_selector_edges(self.h, W.sel_P, W.cb_pred, W.cb_succ, self.idx, self.unary, anchor,
+                                self.edges, self.path[0], self.ws, stream)
+
+    def accept_len(self, target, stream=None):
+        D.dflash_accept_len(self.path, target, self.accept, stream)
+
+    def run(self, x, n_ctx: int, anchor: int, target, hidden=None, pos0: int = 0, stream=None):
+        if self.inject_n:
+            self.inject(hidden, pos0, stream)
+        self.conv(x, stream)
+        self.attn(x, n_ctx, stream)
+        self.topk(stream)
+        self.select(anchor, stream)
+        self.accept_len(target, stream)

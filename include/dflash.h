@@ -1,0 +1,225 @@
+/*
+ * dflash.h - C ABI of libdflash, the DFlash / DFlash2 draft block step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The draft block step, as the pages describe it:
+ *   "dflash: port #219 onto feature (rebased full CL)", Root Cause and "Why We
+ *     Can't Easily Fix It": target features -> encode (fc matmul + norm) ->
+ *     inject KV -> draft.
+ *   "Turbo dflash", Overview: a light draft model proposes a block of tokens
+ *     from target hidden states; "Deferred KV Injection Optimization", The
+ *     Problem: injection is the Wk / Wv matmuls plus a write into the draft
+ *     decoder's own KV cache, which the decoder reads when it drafts.
+ *   "spec : add DFlash2 support (local convolution + candidate selector)",
+ *     Overview: the grouped dynamic depthwise convolution and the candidate
+ *     selector edge formula.
+ *   "dflash: pass missing NVFP4 scales to attention operations", Overview:
+ *     every per-block weight scale of the injection K/V, the decoder Q/K/V and
+ *     both output projections must be applied.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Memory.  Every pointer argument is a device pointer unless the argument's
+ *   comment says "host".  The caller allocates and owns everything, including
+ *   the workspace; the library never allocates, frees or synchronises.
+ * - Layout.  Activations are row-major [rows][features].  A weight is
+ *   row-major [out][in] ("rows" x "cols").  The KV cache is
+ *   [n_kv_heads][capacity][head_dim] for K and for V; column c of a K or V
+ *   projection row belongs to head c / head_dim, dim c % head_dim.
+ * - Types.  Activations, the KV cache, the conv base, W_delta, the selector
+ *   projection and codebooks are either all fp32 or all bf16 (the "act" type).
+ *   With fp32 activations every weight is fp32; with bf16 activations the fc,
+ *   Wq, Wk, Wv, Wo and LM-head weights are bf16 or Q8_0.  Arithmetic is fp32.
+ * - Q8_0.  Blocks of 32 int8 codes along the input dim share one fp16 scale:
+ *   data is int8 [rows][cols], scales is fp16 [rows][cols/32].  The value a
+ *   kernel multiplies with is bf16_rne(fp32(scale) * code), i.e. the weight
+ *   is dequantised to bf16 (round to nearest even) before the bf16 matrix
+ *   multiply; every block's scale is applied.
+ * - Rounding.  Values a call stores in the act type are rounded once from
+ *   fp32 (bf16: round to nearest even).  fp32 outputs are not rounded.
+ * - Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  A call only enqueues work; its outputs are valid when the stream
+ *   reaches it, and every pointer must stay valid until then.
+ * - Errors.  Every call checks its arguments before enqueueing anything: on
+ *   an error it returns a non-OK status, writes nothing and launches nothing;
+ *   dflash_last_error() then describes the problem (thread-local).  A kernel
+ *   launch failure returns DFLASH_ERR_LAUNCH.  Nothing is thrown.
+ * - Alignment.  Device pointers must be 16-byte aligned.
+ * - Reentrancy.  The library holds no state between calls; calls on
+ *   different streams with disjoint outputs and workspaces may overlap.
+ * - Workspace.  A call that needs scratch device memory takes (ws, ws_bytes);
+ *   the matching *_workspace() function returns the bytes it needs for the
+ *   given shapes (0 for none).  A smaller workspace -> DFLASH_ERR_WORKSPACE.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, bad shape or type mix */
+  DFLASH_ERR_UNSUPPORTED = 2,  /* valid request outside what the kernels implement */
+  DFLASH_ERR_CAPACITY = 3,     /* KV-cache rows out of range */
+  DFLASH_ERR_WORKSPACE = 4,    /* workspace missing or too small */
+  DFLASH_ERR_LAUNCH = 5        /* a kernel launch failed */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1, DFLASH_Q8_0 = 2 } dflash_dtype;
+
+/* A weight [rows][cols] (out x in).  data: fp32 / bf16 values or int8 Q8_0
+ * codes; scales: fp16 [rows][cols/32] for Q8_0, else NULL. */
+typedef struct {
+  int32_t dtype;  /* dflash_dtype */
+  int32_t reserved;
+  int64_t rows;
+  int64_t cols;
+  const void *data;
+  const void *scales;
+} dflash_weight;
+
+/* The draft decoder's KV cache: K and V each [n_kv_heads][capacity][head_dim]
+ * in the act type.  head_dim is 64 or 128. */
+typedef struct {
+  int32_t dtype;  /* DFLASH_F32 or DFLASH_BF16 */
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t reserved;
+  int64_t capacity;
+  void *k;
+  void *v;
+} dflash_kv_cache;
+
+/* Limits checked by every call. */
+#define DFLASH_MAX_LAYERS 16   /* target layers concatenated by dflash_inject */
+#define DFLASH_MAX_BLOCK 16    /* B: drafted tokens per block */
+#define DFLASH_MAX_TOPK 32     /* K */
+
+/* (1) KV injection.
+ * "dflash: port #219 onto feature", Root Cause: the encoder is an fc matmul
+ * over the chosen target layers' features plus a norm; "Turbo dflash", The
+ * Problem: injection is the Wk / Wv projections plus the cache write; the
+ * merge log on the NVFP4-scales page: encoder and injection run as one pass.
+ *   h = [h_1 | ... | h_L]        concat along features, layers in the given order
+ *   y = h . fc^T                 fc [d][L*d_t]                       (fp32)
+ *   z = y / sqrt(mean(y^2) + eps) * gamma                            (act type)
+ *   K = z . Wk^T, V = z . Wv^T   Wk, Wv [Hkv*hd][d]                  (act type)
+ *   cache.k[h][pos0 + t][j] = K[t][h*hd + j], same for V, t < n_tokens.
+ * layer_hidden: HOST array of n_layers device pointers, each [n_tokens][d_t]
+ * in `act`.  gamma: [d] in `act`, or NULL for ones.  Requires
+ * 0 <= pos0 && pos0 + n_tokens <= capacity (else DFLASH_ERR_CAPACITY),
+ * d_t % 64 == 0, d % 64 == 0, n_tokens >= 1.  Cache rows outside
+ * [pos0, pos0 + n_tokens) are not touched. */
+dflash_status dflash_inject(const void *const *layer_hidden, int32_t n_layers, int64_t n_tokens,
+                            int32_t d_t, int32_t act, const dflash_weight *fc, const void *gamma,
+                            float eps, const dflash_weight *wk, const dflash_weight *wv,
+                            const dflash_kv_cache *cache, int64_t pos0, void *ws, size_t ws_bytes,
+                            void *stream);
+size_t dflash_inject_workspace(int32_t n_layers, int64_t n_tokens, int32_t d_t, int32_t d,
+                               int32_t kv, int32_t act);
+
+/* (2) DFlash2 grouped dynamic depthwise convolution.
+ * "spec : add DFlash2 support", Overview:
+ *   out[i,c] = sum_{t<T} (base[t,c] + delta[i,t,g(c)]) * x[i-t,c]
+ * with delta[i][t*G + g] = x[i] . W_delta[t*G + g] (predicted from the input,
+ * shared by the channels of a group), contiguous groups g(c) = c / (C/G),
+ * tap 0 = the current position, x before the block start = 0.
+ * x, out: [n_blocks][B][C] in `act` (blocks are independent); base: [T][C]
+ * in `act`; w_delta: [T*G][C] in `act`.  Requires C % G == 0, C % 64 == 0,
+ * 1 <= T <= 16, 1 <= B. */
+dflash_status dflash_conv(const void *x, int32_t n_blocks, int32_t B, int32_t C, int32_t G,
+                          int32_t T, int32_t act, const void *base, const dflash_weight *w_delta,
+                          void *out, void *ws, size_t ws_bytes, void *stream);
+size_t dflash_conv_workspace(int32_t n_blocks, int32_t B, int32_t C, int32_t G, int32_t T);
+
+/* (3) Non-causal block attention with the injected context.
+ * "Turbo dflash", Overview (block diffusion drafting) and The Problem (the
+ * decoder reads the injected cache); the NVFP4-scales page, Overview (Q, K, V
+ * and output projections):
+ *   Q = u Wq^T, Kb = u Wk^T, Vb = u Wv^T                               (act type)
+ *   for query head h, KV head g = h / (Hq/Hkv):
+ *     O_h = softmax(Q_h [Kctx_g | Kb_g]^T * scale) [Vctx_g | Vb_g]      (act type)
+ *   out = residual + O Wo^T                                            (act type)
+ * No mask: every block position sees all n_ctx context rows and all B block
+ * rows.  The block's K/V are not written to the cache.
+ * u, residual, out: [B][d] in `act` (residual NULL = none); Wq [Hq*hd][d],
+ * Wk, Wv [Hkv*hd][d], Wo [d][Hq*hd]; scale 0 = 1/sqrt(hd).  Requires
+ * 1 <= B <= DFLASH_MAX_BLOCK, Hq % Hkv == 0, 0 <= n_ctx <= capacity,
+ * d % 64 == 0. */
+dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, int32_t d,
+                                int32_t n_q_heads, int32_t act, const dflash_weight *wq,
+                                const dflash_weight *wk, const dflash_weight *wv,
+                                const dflash_weight *wo, const dflash_kv_cache *cache,
+                                int64_t n_ctx, float scale, void *out, void *ws, size_t ws_bytes,
+                                void *stream);
+size_t dflash_block_attn_workspace(int32_t B, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, int64_t n_ctx);
+
+/* (4) Shared LM head, top-K candidates and log-softmax unary scores.
+ * "Turbo dflash", Overview (the draft uses the target's output matrix);
+ * "spec : add DFlash2 support", Overview ("unary[c] is the draft's own score
+ * for c") and the top-k review (small K over a wide vocabulary):
+ *   l = h . W_lm^T  (fp32, never stored)
+ *   idx[i] = the K largest l[i][.], largest first, equal logits -> lower index
+ *   unary[i][k] = l[i][idx[i][k]] - log(sum_v exp(l[i][v]))
+ * h: [B][d] in `act`, W_lm [V][d]; idx int32 [B][K]; unary fp32 [B][K].
+ * Requires 1 <= B <= DFLASH_MAX_BLOCK, 1 <= K <= min(V, DFLASH_MAX_TOPK),
+ * d % 64 == 0.  Deterministic: the same inputs give bitwise-equal outputs. */
+dflash_status dflash_topk_unary(const void *h, int32_t B, int32_t act,
+                                const dflash_weight *lm_head, int32_t K, int32_t *idx,
+                                float *unary, void *ws, size_t ws_bytes, void *stream);
+size_t dflash_topk_unary_workspace(int32_t B, int64_t V, int32_t K);
+
+/* (5) Candidate-selector edges and the best path through them.
+ * "spec : add DFlash2 support", Overview:
+ *   edge(p -> c) = < A[p] (.) project(h), B[c] > + unary[c]
+ * A = cb_pred, B = cb_succ [V][r] (the selector_predecessor / successor
+ * codebooks), project(h) = h . P^T with P = proj [r][d] (selector_hidden).
+ * Position i's candidates are c_{i,b} = idx[i][b]; its predecessors are
+ * p_{i,a} = idx[i-1][a] for i >= 1 and the anchor token (the last accepted
+ * token) for i = 0, so
+ *   edges[i][a][b] = sum_rho A[p_{i,a}][rho] * proj[i][rho] * B[c_{i,b}][rho]
+ *                    + unary[i][b]
+ * Row 0 has one predecessor slot: edges[0][a >= 1][.] = -inf, and with
+ * anchor = -1 edges[0][0][b] = unary[0][b].  The readout is the max-sum path:
+ *   s_0[b] = edges[0][0][b];  s_i[b] = max_a s_{i-1}[a] + edges[i][a][b]
+ * (ties -> lower a), final slot argmax_b s_{B-1}[b] (ties -> lower b), and
+ * path[i] = idx[i][slot_i].
+ * h: [B][d] in `act`; idx int32 [B][K] with values in [0, V); unary fp32
+ * [B][K]; edges fp32 [B][K][K]; path int32 [B].  Requires
+ * 1 <= B <= DFLASH_MAX_BLOCK, 1 <= K <= DFLASH_MAX_TOPK, r % 16 == 0,
+ * r <= 256, -1 <= anchor < V, d % 64 == 0.  Indices in idx outside [0, V)
+ * are clamped into range by the kernel (never read out of bounds). */
+dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
+                                    const dflash_weight *proj, const void *cb_pred,
+                                    const void *cb_succ, int64_t V, const int32_t *idx,
+                                    const float *unary, int32_t K, int32_t anchor, float *edges,
+                                    int32_t *path, void *ws, size_t ws_bytes, void *stream);
+size_t dflash_selector_edges_workspace(int32_t B, int32_t r, int32_t d, int32_t K);
+
+/* (6) Greedy accept length.
+ * "dflash: port #219 onto feature", benchmark sweep (greedy sampling) and
+ * "spec : add DFlash2 support", Overview table (acceptance per block):
+ *   accept[s] = max{ m : draft[s][j] == target[s][j] for all j < m }
+ * draft, target int32 [n_seq][B]; accept int32 [n_seq].  Requires n_seq >= 1,
+ * B >= 1. */
+dflash_status dflash_accept_len(const int32_t *draft, const int32_t *target, int32_t n_seq,
+                                int32_t B, int32_t *accept, void *stream);
+
+/* Text of a status code (static storage). */
+const char *dflash_status_string(int32_t status);
+/* Detail of the last non-OK return on this thread ("" if none). */
+const char *dflash_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t dflash_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

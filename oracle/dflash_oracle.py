@@ -281,6 +281,21 @@ def lm_logits(h: np.ndarray, w_lm: np.ndarray, row_chunk: int = 32768) -> np.nda
     return out
 
 
+def lm_logits_stored(h: np.ndarray, w: dict, row_chunk: int = 16384) -> np.ndarray:
+    """logits = h . W_lm^T with W_lm given in storage form (decoded a chunk
+    of rows at a time, so a 1.5 GB head never exists in fp64 at once)."""
+    V = w["rows"]
+    out = np.empty((h.shape[0], V))
+    for r0 in range(0, V, row_chunk):
+        r1 = min(V, r0 + row_chunk)
+        if w["dtype"] == "q8_0":
+            blk = q8_0_to_f64(w["data"][r0:r1], w["scales"][r0:r1])
+        else:
+            blk = act_to_f64(w["data"][r0:r1], w["dtype"])
+        out[:, r0:r1] = h @ blk.T
+    return out
+
+
 def topk_unary_from_logits(logits: np.ndarray, K: int) -> dict:
     idx = top_k_select(logits, K)
     lse = logsumexp_rows(logits)

@@ -1,0 +1,184 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects bad arguments before it touches a GPU.
+
+Every call here fails validation (no launch ever happens), and the
+fake-pointer cases are skipped where a GPU is visible so that no kernel can
+ever see a made-up address.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from block_diffusion_drafter_step_amd import dflash as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake device pointers only without a GPU")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(D.lib_path()):
+        from block_diffusion_drafter_step_amd import build
+        build.build(verbose=False)
+    return D.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared()
+    assert len(names) >= 14
+    out = subprocess.run(["nm", "-D", "--defined-only", D.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dflash_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(lib, n)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.dflash_status_string(0) == b"ok"
+    assert b"workspace" in lib.dflash_status_string(4)
+    assert lib.dflash_status_string(99) == b"unknown status"
+    assert lib.dflash_version() >= 100
+
+
+def test_workspace_queries_are_host_only(lib):
+    a = lib.dflash_inject_workspace(5, 16, 5120, 5120, 1024, 1)
+    b = lib.dflash_inject_workspace(5, 32768, 5120, 5120, 1024, 1)
+    assert 0 < a < b
+    assert lib.dflash_block_attn_workspace(16, 5120, 32, 8, 128, 32768) > \
+        lib.dflash_block_attn_workspace(16, 5120, 32, 8, 128, 1024)
+    assert lib.dflash_topk_unary_workspace(16, 151936, 8) > 0
+    assert lib.dflash_conv_workspace(1, 16, 5120, 64, 4) > 0
+    assert lib.dflash_selector_edges_workspace(16, 64, 5120, 8) > 0
+    assert lib.dflash_inject_workspace(0, 16, 5120, 5120, 1024, 1) == 0
+
+
+FAKE = 0x10000        # aligned, never dereferenced: every case below is invalid
+
+
+def W(dtype, rows, cols, data=FAKE, scales=None):
+    return D._Weight(dtype, 0, rows, cols, data, scales)
+
+
+def cache(dtype=1, h=8, hd=128, cap=4096, k=FAKE, v=FAKE):
+    return D._Cache(dtype, h, hd, 0, cap, k, v)
+
+
+def err(lib):
+    return lib.dflash_last_error().decode()
+
+
+@no_gpu
+def test_inject_rejections(lib):
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    fc, wk, wv, c = W(1, 256, 512), W(1, 1024, 256), W(1, 1024, 256), cache()
+    ref = ctypes.byref
+
+    def call(arr=arr, n_layers=2, n=16, d_t=256, act=1, fc=fc, wk=wk, wv=wv, c=c, pos0=0, ws=FAKE, wsb=1 << 30):
+        return lib.dflash_inject(arr, n_layers, n, d_t, act, ref(fc), None, 1e-6, ref(wk), ref(wv), ref(c),
+                                 pos0, ws, wsb, None)
+
+    assert call(act=7) == 1
+    assert call(n_layers=0) == 1
+    assert call(n_layers=17) == 1
+    assert call(n=0) == 1
+    assert call(d_t=100) == 1
+    assert call(fc=W(1, 256, 500)) == 1 and "fc" in err(lib)
+    assert call(fc=W(0, 256, 512)) == 1                       # fp32 weight with bf16 activations
+    assert call(fc=W(2, 256, 512, scales=None)) == 1          # Q8_0 without scales
+    assert call(fc=W(1, 256, 512, data=FAKE + 8)) == 1        # misaligned
+    assert call(wk=W(1, 512, 256)) == 1                       # kv mismatch with the cache
+    assert call(wk=W(2, 1024, 256, scales=FAKE)) == 2         # wk / wv dtypes differ
+    assert call(c=cache(hd=96)) == 2
+    assert call(c=cache(dtype=0)) == 1
+    assert call(pos0=4090) == 3 and "capacity" in err(lib)
+    assert call(pos0=-1) == 3
+    assert call(ws=None) == 4
+    assert call(wsb=16) == 4
+    bad = (ctypes.c_void_p * 2)(FAKE, None)
+    assert call(arr=bad) == 1
+
+
+@no_gpu
+def test_conv_rejections(lib):
+    ref = ctypes.byref
+    wd = W(1, 4 * 8, 256)
+
+    def call(nb=1, B=8, C=256, G=8, T=4, act=1, w=wd, ws=FAKE, wsb=1 << 30):
+        return lib.dflash_conv(FAKE, nb, B, C, G, T, act, FAKE, ref(w), FAKE, ws, wsb, None)
+
+    assert call(C=200) == 1
+    assert call(G=7) == 1
+    assert call(T=0) == 1
+    assert call(T=17) == 1
+    assert call(B=0) == 1
+    assert call(w=W(1, 33, 256)) == 1
+    assert call(w=W(2, 32, 256, scales=FAKE)) == 2            # W_delta cannot be Q8_0
+    assert call(wsb=8) == 4
+
+
+@no_gpu
+def test_attn_rejections(lib):
+    ref = ctypes.byref
+    wq, wk, wv, wo = W(1, 4096, 5120), W(1, 1024, 5120), W(1, 1024, 5120), W(1, 5120, 4096)
+
+    def call(B=16, d=5120, Hq=32, c=cache(), n_ctx=1024, wq=wq, wk=wk, wo=wo, scale=0.0, wsb=1 << 30):
+        return lib.dflash_block_attn(FAKE, None, B, d, Hq, 1, ref(wq), ref(wk), ref(wv), ref(wo), ref(c), n_ctx,
+                                     scale, FAKE, FAKE, wsb, None)
+
+    assert call(B=0) == 1
+    assert call(B=17) == 1
+    assert call(Hq=30) == 1
+    assert call(Hq=80, wq=W(1, 80 * 128, 5120), wo=W(1, 5120, 80 * 128)) == 2   # 10 q heads per kv head
+    assert call(n_ctx=5000) == 3
+    assert call(n_ctx=-1) == 3
+    assert call(wo=W(1, 5120, 4000)) == 1
+    assert call(wk=W(2, 1024, 5120, scales=FAKE)) == 2
+    assert call(scale=-1.0) == 1
+    assert call(wsb=1024) == 4
+
+
+@no_gpu
+def test_topk_and_selector_rejections(lib):
+    ref = ctypes.byref
+    lm = W(1, 1000, 256)
+    assert lib.dflash_topk_unary(FAKE, 16, 1, ref(lm), 0, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.dflash_topk_unary(FAKE, 16, 1, ref(lm), 33, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.dflash_topk_unary(FAKE, 16, 1, ref(W(1, 20, 256)), 21, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.dflash_topk_unary(FAKE, 17, 1, ref(lm), 8, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.dflash_topk_unary(FAKE, 16, 1, ref(lm), 8, FAKE, FAKE, FAKE, 4, None) == 4
+    assert lib.dflash_topk_unary(FAKE, 16, 1, ref(W(2, 1000, 250, scales=FAKE)), 8, FAKE, FAKE, FAKE, 1 << 30,
+                                 None) == 1
+    P = W(1, 64, 256)
+
+    def sel(r=64, V=1000, K=8, anchor=3, B=16, P=P, wsb=1 << 30):
+        return lib.dflash_selector_edges(FAKE, B, 1, ref(P), FAKE, FAKE, V, FAKE, FAKE, K, anchor, FAKE, FAKE,
+                                         FAKE, wsb, None)
+
+    assert sel(P=W(1, 63, 256)) == 1
+    assert sel(P=W(1, 512, 256)) == 1
+    assert sel(anchor=1000) == 1
+    assert sel(anchor=-2) == 1
+    assert sel(K=33) == 1
+    assert sel(V=4) == 1
+    assert sel(wsb=0) == 4
+    assert lib.dflash_accept_len(FAKE, FAKE, 0, 8, FAKE, None) == 1
+    assert lib.dflash_accept_len(None, FAKE, 1, 8, FAKE, None) == 1
+
+
+def test_binding_refuses_host_tensors():
+    x = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        D._ptr(x)
