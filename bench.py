@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Throughput of the DFlash / DFlash2 draft block step on one MI355X.
+
+One step is one pass of the whole hot path over one block of synthetic
+input: inject 16 accepted tokens' target features (fc + RMSNorm + Wk/Wv into
+the cache), the DFlash2 grouped dynamic conv, non-causal block attention over
+the injected context plus the block, the LM head with top-K and unary
+scores, the selector edges with their best path, and the accept length.
+
+Default workload (the 32k-context setting, Qwen-27B-shaped bf16 layer): the
+cache holds 32768 injected rows (written by a timed 32768-token prefill
+injection, reported on its own as MFMA TFLOP/s), each step re-injects the last
+16 context rows and drafts one B = 16 block over 32768 + 16 keys.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2|c1|c3|c4] [--no-cpu]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
+METRIC = "draft block steps/s + drafted tok/s at 32k ctx; % HBM / MFMA peak"
+WORKLOADS = {"c1": "c1_qwen27b_1k", "c2": "c2_prefill_32k", "c3": "c3_decode_64k", "c4": "c4_q8_0_32k"}
+COUNTERS = os.path.join(ROOT, "profiles", "lmhead_topk_c2_counters.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU-baseline leg")
+    ap.add_argument("--prefill-reps", type=int, default=3)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    return ap.parse_args()
+
+
+def src_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_diffusion_drafter_step_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters():
+    """HBM bytes per LM-head launch from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel source changed since."""
+    try:
+        c = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if c.get("source_hash") != src_hash("topk.hip", "common.h"):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.calib_copy:
+        n = 1 << 28                     # 2^28 floats = 1 GiB read + 1 GiB written per copy
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": 4 * n, "calib_copy_bytes_written": 4 * n, "reps": 5}))
+        return
+
+    from block_diffusion_drafter_step_amd import configs, pipeline, synth, workmodel
+    from block_diffusion_drafter_step_amd import dflash as D
+
+    D.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = configs.get(WORKLOADS[args.workload])
+    decode64 = cfg.prefill_kv > 0
+    inj_n = 16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + cfg.seed)
+    adt = pipeline.act_dtype(cfg.act)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(adt)
+
+    host = synth.Workload(cfg)
+    W = pipeline.DeviceWeights(host, drop_host=args.no_cpu)
+    cache = pipeline.new_cache(cfg)
+    prefill = None
+    if decode64:
+        # long-context decode: the cache already holds prefill_kv seeded rows
+        cache.k[:, :cfg.prefill_kv].copy_(randn(cfg.Hkv, cfg.prefill_kv, cfg.hd))
+        cache.v[:, :cfg.prefill_kv].copy_(randn(cfg.Hkv, cfg.prefill_kv, cfg.hd))
+        n_ctx0 = cfg.prefill_kv
+    else:
+        # prefill injection of n_ctx tokens (the MFMA-bound tile GEMM path)
+        n = cfg.n_ctx
+        hid = [randn(n, cfg.d_t) for _ in range(cfg.L_t)]
+        ws = D.workspace(D.dflash_inject_workspace(cfg.L_t, n, cfg.d_t, cfg.d, cfg.kv, cfg.act))
+        D.dflash_inject(hid, W.fc, None, cfg.eps, W.wk, W.wv, cache, 0, ws)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(args.prefill_reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            D.dflash_inject(hid, W.fc, None, cfg.eps, W.wk, W.wv, cache, 0, ws)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 1e3)
+        fl = workmodel.inject_flops(n, cfg.L_t, cfg.d_t, cfg.d, cfg.kv)
+        t = float(np.median(times))
+        prefill = {"tokens": n, "ms": round(t * 1e3, 3), "tflop": round(fl / 1e12, 3),
+                   "achieved_tflops": round(fl / t / 1e12, 1), "peak_tflops": MFMA_BF16_PEAK_TFS,
+                   "frac": round(fl / t / 1e12 / MFMA_BF16_PEAK_TFS, 4), "bound": "mfma"}
+        del hid, ws
+        n_ctx0 = cfg.n_ctx
+        torch.cuda.empty_cache()
+
+    step = pipeline.BlockStep(cfg, W, cache, inject_n=inj_n)
+    hid16 = [randn(inj_n, cfg.d_t) for _ in range(cfg.L_t)]
+    x = randn(1, cfg.B, cfg.d)
+    anchor = int(host.anchor()[0])
+    target = torch.randint(0, cfg.V, (1, cfg.B), generator=gen, device=dev, dtype=torch.int32)
+
+    def positions(i):
+        """(pos0 of the 16 injected rows, context rows attended) for step i."""
+        if decode64:
+            s = i % cfg.steps
+            return n_ctx0 + inj_n * s, n_ctx0 + inj_n * (s + 1)
+        return n_ctx0 - inj_n, n_ctx0
+
+    names = ["inject", "conv", "attn", "topk", "select", "accept"]
+    calls = [lambda i: step.inject(hid16, positions(i)[0]),
+             lambda i: step.conv(x),
+             lambda i: step.attn(x, positions(i)[1]),
+             lambda i: step.topk(),
+             lambda i: step.select(anchor),
+             lambda i: step.accept_len(target)]
+
+    for i in range(args.warmup):
+        for c in calls:
+            c(i)
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, wall clock between two device synchronisations;
+    # the LM-head call (the dominant kernel) is bracketed by HIP events on its
+    # stream every EVERY-th step (an event record costs a few microseconds of
+    # queue time, so bracketing every call of every step would distort the step)
+    K = args.steps
+    EVERY = 4
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range((K + EVERY - 1) // EVERY)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        calls[0](i)
+        calls[1](i)
+        calls[2](i)
+        if i % EVERY == 0:
+            ev[i // EVERY][0].record()
+            calls[3](i)
+            ev[i // EVERY][1].record()
+        else:
+            calls[3](i)
+        calls[4](i)
+        calls[5](i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / K
+    steps_s = K / (t1 - t0)
+    topk_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # per-call breakdown: a separate pass after the timed region, events around every call
+    nb = min(K, 100)
+    evc = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+           for _ in range(nb)]
+    for i in range(nb):
+        for j, c in enumerate(calls):
+            evc[i][j][0].record()
+            c(i)
+            evc[i][j][1].record()
+    torch.cuda.synchronize()
+    per = {n: float(np.mean([evc[i][j][0].elapsed_time(evc[i][j][1]) for i in range(nb)]))
+           for j, n in enumerate(names)}
+
+    if decode64:
+        ctx_mean = float(np.mean([positions(i)[1] for i in range(cfg.steps)]))
+    else:
+        ctx_mean = n_ctx0
+    step_bytes = workmodel.step_bytes(cfg, int(ctx_mean), inject_n=inj_n)
+    lm_bytes = workmodel.lmhead_bytes(cfg)
+    lm_gbs = lm_bytes / (topk_ms * 1e-3) / 1e9
+    attn_bytes = workmodel.attn_bytes(cfg, int(ctx_mean))
+    roofline = {"bound": "hbm", "kernel": "dflash_topk_unary (lmhead_topk_kernel + topk_merge_kernel)",
+                "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_counters(),
+                "bytes_per_launch": lm_bytes, "launch_ms": round(topk_ms, 4),
+                "launch_samples": len(ev)}
+
+    out = {"metric": METRIC, "value": round(steps_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": K,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if cfg.weight == "bf16" else "bf16 x q8_0",
+           "data": "synthetic (seeded; random weights of the workload's shapes)",
+           "config": {"workload": f"{cfg.name}: decode step at {int(ctx_mean)}-row context",
+                      "B": cfg.B, "n_ctx": int(ctx_mean), "inject_per_step": inj_n, "d": cfg.d,
+                      "L_t": cfg.L_t, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "hd": cfg.hd, "C": cfg.C, "G": cfg.G,
+                      "T": cfg.T, "V": cfg.V, "K": cfg.K, "r": cfg.r, "weights": cfg.weight},
+           "drafted_tok_per_s": round(steps_s * cfg.B, 1),
+           "step_bytes": step_bytes,
+           "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "roofline": roofline,
+           "per_call_ms": {k: round(v, 4) for k, v in per.items()},
+           "per_call_note": "separate pass after the timed region, HIP events around each call",
+           "attn_gbs": round(attn_bytes / (per["attn"] * 1e-3) / 1e9, 1)}
+    if prefill:
+        out["prefill"] = prefill
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cfg, host, int(ctx_mean), inj_n)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, host, n_ctx, inj_n):
+    """The oracle (fp64 numpy, untuned) running one whole block step of the
+    same workload on the host cores: injection of 16 rows, conv, attention over
+    n_ctx + B keys, LM head over V, selector, accept."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle as O
+    from block_diffusion_drafter_step_amd import synth
+
+    t_setup = time.perf_counter()
+    f = O.weight_to_f64
+    a = lambda t: O.act_to_f64(t, cfg.act)
+    bp = cfg.act == "bf16"
+    # the context rows the step attends are drawn on the host (same distribution)
+    ck = a(synth.normal(cfg.seed, "cpu.ck", (cfg.Hkv, n_ctx, cfg.hd), 1.0, cfg.act))
+    cv = a(synth.normal(cfg.seed, "cpu.cv", (cfg.Hkv, n_ctx, cfg.hd), 1.0, cfg.act))
+    hid = [a(synth.normal(cfg.seed, f"cpu.hid.{l}", (inj_n, cfg.d_t), 1.0, cfg.act)) for l in range(cfg.L_t)]
+    x = a(host.x())[0]
+    A, Bc = host.codebooks()
+    A, Bc = a(A), a(Bc)
+    anchor = int(host.anchor()[0])
+    setup = time.perf_counter() - t_setup
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    inj = O.inject(hid, f(host.fc()), None, cfg.eps, f(host.wk()), f(host.wv()), bp)
+    ck[:, n_ctx - inj_n:] = inj["k"].reshape(inj_n, cfg.Hkv, cfg.hd).transpose(1, 0, 2)
+    cv[:, n_ctx - inj_n:] = inj["v"].reshape(inj_n, cfg.Hkv, cfg.hd).transpose(1, 0, 2)
+    c = O.conv(x[None], a(host.conv_base()), f(host.w_delta()), cfg.G, bp)
+    at = O.block_attn(c["u"][0], x, f(host.wq()), f(host.wk()), f(host.wv()), f(host.wo()), ck, cv, n_ctx,
+                      cfg.Hq, 0.0, bp)
+    logits = O.lm_logits_stored(at["out"], host.w_lm())
+    tk = O.topk_unary_from_logits(logits, cfg.K)
+    sel = O.selector(at["out"], f(host.sel_proj()), A, Bc, tk["idx"], tk["unary"], anchor)
+    O.accept_len(sel["path"][None, :], sel["path"][None, :])
+    t = time.perf_counter() - t0
+    return {"value": round(1.0 / t, 5), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one whole oracle block step of the same workload ({t:.1f} s; fp64 numpy, "
+                      f"untuned; input staging {setup:.1f} s not counted)",
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

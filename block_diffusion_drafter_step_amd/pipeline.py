@@ -40,7 +40,7 @@ def new_cache(cfg, device="cuda") -> D.KVCache:
 class DeviceWeights:
     """All weights of one draft layer plus the shared head and selector."""
 
-    def __init__(self, w: synth.Workload, device="cuda"):
+    def __init__(self, w: synth.Workload, device="cuda", drop_host: bool = True):
         cfg = w.cfg
         self.cfg = cfg
         self.fc = weight_tensor(w.fc(), device)
@@ -51,7 +51,8 @@ class DeviceWeights:
         self.base = act_tensor(w.conv_base(), cfg.act, device)
         self.w_delta = weight_tensor(w.w_delta(), device)
         self.w_lm = weight_tensor(w.w_lm(), device)
-        w.drop("wlm")
+        if drop_host:
+            w.drop("wlm")
         self.sel_P = weight_tensor(w.sel_proj(), device)
         A, Bc = w.codebooks()
         self.cb_pred = act_tensor(A, cfg.act, device)
