@@ -233,24 +233,78 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   }
 }
 
-// O[t][h*hd + d] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, splits in order
+// O[t][h*hd + d] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One workgroup per (query head, token): thread (p, q) owns dims 4q..4q+3 and
+// the splits s = p, p + P, ... (P = 256 / (HD/4)); the P partial sums are then
+// added in p order through LDS, so the result is bitwise reproducible.
+constexpr int kMaxSplit = 1024;
+
 template <typename TA, int HD>
-__global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  constexpr int NQ = HD / 4, P = 256 / NQ;
+  __shared__ float wsp[kMaxSplit];
+  __shared__ float red[8];
+  __shared__ float4 part[P][NQ];
   const int ht = blockIdx.x;  // hq * B + t
   const int hq = ht / a.B, t = ht - hq * a.B;
-  const int d = threadIdx.x;
-  const float *ml = a.part_ml + (long)ht * a.n_split * 2;
-  float M = -__builtin_inff();
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, acc = 0.f;
-  const float *po = a.part_o + (long)ht * a.n_split * HD + d;
-  for (int s = 0; s < a.n_split; ++s) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ns = a.n_split;
+  const float *ml = a.part_ml + (long)ht * ns * 2;
+  float mx = -__builtin_inff();
+  for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, ml[2 * s]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float lsum = 0.f;
+  for (int s = tid; s < ns; s += 256) {
     const float m = ml[2 * s];
     const float w = m == -__builtin_inff() ? 0.f : exp2f(m - M);
-    L += w * ml[2 * s + 1];
-    acc += w * po[(long)s * HD];
+    wsp[s] = w;
+    lsum += w * ml[2 * s + 1];
   }
-  reinterpret_cast<TA *>(a.o)[(long)t * a.Hq * HD + (long)hq * HD + d] = from_f32<TA>(acc / L);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lsum += shfl_xor(lsum, o);
+  __syncthreads();
+  if (lane == 0) red[4 + wave] = lsum;
+  __syncthreads();
+  const float L = (red[4] + red[5]) + (red[6] + red[7]);
+  const int q = tid % NQ, p = tid / NQ;
+  const float *po = a.part_o + (long)ht * ns * HD + 4 * q;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = p;
+  for (; s + 3 * P < ns; s += 4 * P) {
+    float4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const float4 *>(po + (long)(s + j * P) * HD);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float w = wsp[s + j * P];
+      acc.x += w * v[j].x; acc.y += w * v[j].y; acc.z += w * v[j].z; acc.w += w * v[j].w;
+    }
+  }
+  for (; s < ns; s += P) {
+    const float4 v = *reinterpret_cast<const float4 *>(po + (long)s * HD);
+    const float w = wsp[s];
+    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+  }
+  part[p][q] = acc;
+  __syncthreads();
+  if (p == 0) {
+    float4 r = part[0][q];
+#pragma unroll
+    for (int j = 1; j < P; ++j) {
+      const float4 v = part[j][q];
+      r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
+    }
+    TA *o = reinterpret_cast<TA *>(a.o) + (long)t * a.Hq * HD + (long)hq * HD + 4 * q;
+    const float inv = 1.0f / L;
+    o[0] = from_f32<TA>(r.x * inv);
+    o[1] = from_f32<TA>(r.y * inv);
+    o[2] = from_f32<TA>(r.z * inv);
+    o[3] = from_f32<TA>(r.w * inv);
+  }
 }
 
 void attn_plan(long n_keys, int Hkv, int *chunk, int *n_split) {
@@ -268,7 +322,7 @@ static void attn_launch_t(const AttnArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((attn_split_kernel<TA, HD, 1>), dim3(a.n_split, a.Hkv), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((attn_split_kernel<TA, HD, 2>), dim3(a.n_split, a.Hkv), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((attn_combine_kernel<TA, HD>), dim3(a.Hq * a.B), dim3(HD), 0, st, a);
+  hipLaunchKernelGGL((attn_combine_kernel<TA, HD>), dim3(a.Hq * a.B), dim3(256), 0, st, a);
 }
 
 hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st) {

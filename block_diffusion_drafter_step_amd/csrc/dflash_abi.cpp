@@ -189,7 +189,8 @@ size_t attn_ws(int32_t B, int32_t d, int32_t Hq, int32_t Hkv, int32_t hd, int64_
 
 size_t topk_ws(int64_t V, int32_t K) {
   Carve c(nullptr);
-  const int n_wg = topk_plan_wgs(V);
+  // sized for the larger of the two plans (bf16/fp32 or Q8_0 weights)
+  const int n_wg = std::max(topk_plan_wgs(V, W_SAME), topk_plan_wgs(V, W_Q8_0));
   c.take((size_t)n_wg * 16 * K * 4);
   c.take((size_t)n_wg * 16 * K * 4);
   c.take((size_t)n_wg * 16 * 2 * 4);
@@ -449,7 +450,8 @@ dflash_status dflash_topk_unary(const void *h, int32_t B, int32_t act,
   a.scales = lm_head->scales;
   a.V = V;
   a.K = K;
-  a.n_wg = topk_plan_wgs(V);
+  a.n_wg = topk_plan_wgs(V, wkind_of(lm_head));
+  a.n_waves = topk_plan_waves(V, wkind_of(lm_head));
   a.part_val = (float *)c.take((size_t)a.n_wg * 16 * K * 4);
   a.part_idx = (int *)c.take((size_t)a.n_wg * 16 * K * 4);
   a.part_ms = (float *)c.take((size_t)a.n_wg * 16 * 2 * 4);

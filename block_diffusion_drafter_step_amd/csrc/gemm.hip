@@ -14,6 +14,7 @@
 //    along K (the concatenated target-layer features are never materialised).
 #include "common.h"
 #include "kernels.h"
+#include "stream.h"
 
 namespace dfl {
 
@@ -62,95 +63,56 @@ __device__ __forceinline__ int seg_of(const WSet &W, int n, int *local) {
 // skinny (weight-streaming) GEMM
 // ---------------------------------------------------------------------------
 
-template <typename TA, int WK>
-struct WRow {
-  const void *p;
-  const uint16_t *s;
-  __device__ __forceinline__ auto frag(int k) const {
-    if constexpr (WK == W_Q8_0) {
-      const uint2 c = *reinterpret_cast<const uint2 *>(reinterpret_cast<const int8_t *>(p) + k);
-      return dequant8(c, half_bits_to_f32(s[k >> 5]));
-    } else {
-      return load_frag(reinterpret_cast<const TA *>(p) + k);
-    }
-  }
-};
-
-template <typename TA, int WK>
-__device__ __forceinline__ WRow<TA, WK> wrow_of(const WSet &W, int n) {
-  int lr;
-  const int s = seg_of(W, n, &lr);
-  WRow<TA, WK> r;
-  if constexpr (WK == W_Q8_0) {
-    r.p = reinterpret_cast<const int8_t *>(pick(W.data, s)) + (long)lr * W.K;
-    r.s = reinterpret_cast<const uint16_t *>(pick(W.scales, s)) + (long)lr * (W.K >> 5);
-  } else {
-    r.p = reinterpret_cast<const TA *>(pick(W.data, s)) + (long)lr * W.K;
-    r.s = nullptr;
-  }
-  return r;
-}
-
-template <typename TA, int WK, int RT>
+// Workgroup (x, y): 4 waves, each owning TPW consecutive 16-row tiles of the
+// stacked weight, over k-range y.  Partials part[y][n][16] (fp32).
+template <typename TA, int WK, int TPW>
 __global__ __launch_bounds__(256) void skinny_gemm_kernel(ASrc X, int M, WSet W, int kchunk,
                                                           float *__restrict__ part) {
-  using FA = decltype(WRow<TA, WK>().frag(0));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int N = W.n_total, K = W.K;
-  const int tile0 = (blockIdx.x * 4 + wave) * RT;
-  if (tile0 * 16 >= N) return;
+  const int ntile = (N + 15) >> 4;
+  const int tile0 = (blockIdx.x * 4 + wave) * TPW;
+  const int cnt = min(TPW, ntile - tile0);
+  if (cnt <= 0) return;
   const int k0 = blockIdx.y * kchunk;
   const int k1 = min(K, k0 + kchunk);
 
-  WRow<TA, WK> wr[RT];
+  SRow<TA, WK> rows[TPW];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) wr[t] = wrow_of<TA, WK>(W, min((tile0 + t) * 16 + r16, N - 1));
+  for (int u = 0; u < TPW; ++u) {
+    int lr;
+    const int n = min((tile0 + u) * 16 + r16, N - 1);
+    const int sg = seg_of(W, n, &lr);
+    rows[u] = srow<TA, WK>(pick(W.data, sg), pick(W.scales, sg), lr, K);
+  }
   const bool tok_ok = r16 < M;
   const int kps = X.k_per_src;
-  const long xoff = (long)min(r16, M - 1) * kps + 8 * g;
+  const long trow = (long)min(r16, M - 1) * kps;
 
-  f32x4 acc[RT];
+  f32x4 acc[TPW];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = zero4();
-
-  // walk the K range one activation source at a time
+  for (int u = 0; u < TPW; ++u) acc[u] = zero4();
+  // walk the k-range one activation source at a time
   for (int s = k0 / kps; s * kps < k1; ++s) {
     const int ka = max(k0, s * kps), kb = min(k1, (s + 1) * kps);
-    const TA *xr = reinterpret_cast<const TA *>(pick(X.ptr, s)) + xoff - (long)s * kps;
-    int k = ka;
-    for (; k + 256 <= kb; k += 256) {
-      Frag<TA> b[8];
-      FA a[RT][8];
+    const TA *xr = reinterpret_cast<const TA *>(pick(X.ptr, s)) + trow - (long)s * kps;
+    stream_range<TA, WK, TPW>(xr, rows, cnt, ka, kb, g, tok_ok, acc);
+  }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = tok_ok ? load_frag(xr + k + 32 * j) : frag_zero<TA>();
+  for (int u = 0; u < TPW; ++u) {
+    if (u < cnt) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a[t][j] = wr[t].frag(k + 32 * j + 8 * g);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int t = 0; t < RT; ++t) mma(acc[t], a[t][j], b[j]);
-    }
-    for (; k < kb; k += 32) {
-      const Frag<TA> b = tok_ok ? load_frag(xr + k) : frag_zero<TA>();
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const FA a = wr[t].frag(k + 8 * g);
-        mma(acc[t], a, b);
+      for (int i = 0; i < 4; ++i) {
+        const int n = (tile0 + u) * 16 + 4 * g + i;
+        if (n < N) part[((long)blockIdx.y * N + n) * 16 + r16] = acc[u][i];
       }
     }
   }
-#pragma unroll
-  for (int t = 0; t < RT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = (tile0 + t) * 16 + 4 * g + i;
-      if (n < N) part[((long)blockIdx.y * N + n) * 16 + r16] = acc[t][i];
-    }
 }
 
+// Y[t][n] = sum over k-ranges of the partials, in range order (bitwise
+// reproducible); 8 ranges' loads are issued together to hide their latency.
 template <typename TA>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part,
                                                             int ksplit, int N, int M, OutSpec o) {
@@ -158,9 +120,21 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
   const long n = id >> 2;
   const int tg = (int)(id & 3);
   if (n >= N) return;
+  const float *p = part + n * 16 + 4 * tg;
+  const long stride = (long)N * 16;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int ks = 0; ks < ksplit; ++ks) {
-    const float4 v = *reinterpret_cast<const float4 *>(part + ((long)ks * N + n) * 16 + 4 * tg);
+  int ks = 0;
+  for (; ks + 8 <= ksplit; ks += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const float4 *>(p + (ks + j) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
+    }
+  }
+  for (; ks < ksplit; ++ks) {
+    const float4 v = *reinterpret_cast<const float4 *>(p + ks * stride);
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
   const float vals[4] = {s.x, s.y, s.z, s.w};
@@ -172,19 +146,32 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 }
 
 struct SkinnyPlan {
-  int rt, kchunk, ksplit, row_groups;
+  int tpw, kchunk, ksplit, groups;
 };
 
+// about DFL_SKINNY_WAVES waves: TPW tiles per wave, the k-range split to match
+#ifndef DFL_SKINNY_WAVES
+#define DFL_SKINNY_WAVES 2048
+#endif
+// tiles per wave: 4 for long k-ranges (the injection fc), 2 otherwise
+#ifndef DFL_SKINNY_TPW_LONGK
+#define DFL_SKINNY_TPW_LONGK 4
+#endif
+#ifndef DFL_SKINNY_TPW
+#define DFL_SKINNY_TPW 2
+#endif
 static SkinnyPlan skinny_plan(int N, int K) {
   SkinnyPlan p;
-  p.rt = N >= 4096 ? 2 : 1;
-  p.row_groups = (N + 64 * p.rt - 1) / (64 * p.rt);
-  const int target_wgs = 1024;
-  int ks = (target_wgs + p.row_groups - 1) / p.row_groups;
+  const int ntile = (N + 15) / 16;
+  p.tpw = ntile >= 256 ? (K >= 16384 ? DFL_SKINNY_TPW_LONGK : DFL_SKINNY_TPW) : 1;
+  const int wave_groups = (ntile + p.tpw - 1) / p.tpw;
+  p.groups = (wave_groups + 3) / 4;
+  int ks = (DFL_SKINNY_WAVES + wave_groups - 1) / wave_groups;
   if (ks < 1) ks = 1;
   int kc = (K + ks - 1) / ks;
-  kc = ((kc + 255) / 256) * 256;
-  if (kc > K) kc = ((K + 31) / 32) * 32;
+  kc = ((kc + 63) / 64) * 64;
+  if (kc < 128) kc = 128;
+  if (kc > K) kc = K;
   p.kchunk = kc;
   p.ksplit = (K + kc - 1) / kc;
   return p;
@@ -199,8 +186,11 @@ template <typename TA, int WK>
 static hipError_t skinny_launch_t(const ASrc &X, int M, const WSet &W, float *part,
                                   const OutSpec &out, hipStream_t st) {
   const SkinnyPlan p = skinny_plan(W.n_total, W.K);
-  dim3 grid(p.row_groups, p.ksplit);
-  if (p.rt == 2)
+  dim3 grid(p.groups, p.ksplit);
+  if (p.tpw == 4)
+    hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 4>), grid, dim3(256), 0, st, X, M, W, p.kchunk,
+                       part);
+  else if (p.tpw == 2)
     hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 2>), grid, dim3(256), 0, st, X, M, W, p.kchunk,
                        part);
   else

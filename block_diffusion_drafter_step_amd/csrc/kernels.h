@@ -108,13 +108,15 @@ struct TopkArgs {
   long V;
   int K;
   int n_wg;
+  int n_waves;        // waves that own vocabulary tiles (<= 4 * n_wg)
   float *part_val;    // [n_wg][16][K]
   int *part_idx;      // [n_wg][16][K]
   float *part_ms;     // [n_wg][16][2]
   int *idx;           // [B][K]
   float *unary;       // [B][K]
 };
-int topk_plan_wgs(long V);
+int topk_plan_wgs(long V, int wkind);
+int topk_plan_waves(long V, int wkind);
 hipError_t launch_topk(int act, int wkind, const TopkArgs &a, hipStream_t st);
 
 // ---- selector ------------------------------------------------------------------------

@@ -60,9 +60,10 @@ hipError_t launch_rmsnorm(int act, const float *y, int n, int d, const void *gam
 // ---------------------------------------------------------------------------
 // Grouped dynamic depthwise conv ("spec : add DFlash2 support", Overview):
 // out[i,c] = sum_t (base[t,c] + delta[i, t*G + g(c)]) * x[i-t, c], x[<0] = 0.
-// One thread owns 4 adjacent channels of one block and walks the B positions,
-// keeping the last T inputs in registers, so x is read once and out written
-// once (the kernel is a pure stream when many blocks are batched).
+// One thread per (block, position, 4 adjacent channels): its T input rows,
+// T delta values per channel and T base values are independent loads issued
+// together, so a single block costs one memory round trip, and a batch of
+// blocks is a pure stream (x read T times from cache, out written once).
 // ---------------------------------------------------------------------------
 template <typename TA, int TM>
 __global__ __launch_bounds__(256) void conv_kernel(const TA *__restrict__ x, int n_blocks, int B,
@@ -72,51 +73,37 @@ __global__ __launch_bounds__(256) void conv_kernel(const TA *__restrict__ x, int
                                                    TA *__restrict__ out) {
   const long id = (long)blockIdx.x * 256 + threadIdx.x;
   const int c4 = C >> 2;
-  const long b = id / c4;
-  if (b >= n_blocks) return;
-  const int c = (int)(id - b * c4) * 4;
+  const long row = id / c4;           // block * B + position
+  if (row >= (long)n_blocks * B) return;
+  const int c = (int)(id - row * c4) * 4;
+  const int i = (int)(row % B);
   const int cpg = C / G;
-  int gidx[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) gidx[j] = (c + j) / cpg;
-  float bs[TM][4];
-#pragma unroll
-  for (int t = 0; t < TM; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bs[t][j] = t < T ? to_f32(base[(long)t * C + c + j]) : 0.f;
-  float hist[TM][4];
-#pragma unroll
-  for (int t = 0; t < TM; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hist[t][j] = 0.f;
-  const TA *xb = x + b * (long)B * C + c;
-  TA *ob = out + b * (long)B * C + c;
   const int TG = T * G;
-  for (int i = 0; i < B; ++i) {
+  const float *dl = delta + row * (long)TG;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float xv[TM][4], bv[TM][4], dv[TM][4];
 #pragma unroll
-    for (int t = TM - 1; t > 0; --t)
+  for (int t = 0; t < TM; ++t) {
+    const bool ok = t < T && i - t >= 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) hist[t][j] = hist[t - 1][j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hist[0][j] = to_f32(xb[(long)i * C + j]);
-    const float *dl = delta + (b * B + i) * (long)TG;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      if (t < T) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] += (bs[t][j] + dl[t * G + gidx[j]]) * hist[t][j];
-      }
+    for (int j = 0; j < 4; ++j) {
+      xv[t][j] = ok ? to_f32(x[(row - t) * C + c + j]) : 0.f;
+      bv[t][j] = t < T ? to_f32(base[(long)t * C + c + j]) : 0.f;
+      dv[t][j] = t < T ? dl[t * G + (c + j) / cpg] : 0.f;
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ob[(long)i * C + j] = from_f32<TA>(acc[j]);
   }
+#pragma unroll
+  for (int t = 0; t < TM; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += (bv[t][j] + dv[t][j]) * xv[t][j];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[row * C + c + j] = from_f32<TA>(acc[j]);
 }
 
 template <typename TA>
 static void conv_launch_t(const void *x, int n_blocks, int B, int C, int G, int T, const void *base,
                           const float *delta, void *out, hipStream_t st) {
-  const long threads = (long)n_blocks * (C / 4);
+  const long threads = (long)n_blocks * B * (C / 4);
   const dim3 grid((unsigned)((threads + 255) / 256));
   const TA *xp = reinterpret_cast<const TA *>(x);
   const TA *bp = reinterpret_cast<const TA *>(base);
@@ -144,57 +131,74 @@ hipError_t launch_conv(int act, const void *x, int n_blocks, int B, int C, int G
 // ---------------------------------------------------------------------------
 // Candidate-selector edges and max-sum path ("spec : add DFlash2 support",
 // Overview): edge(p -> c) = < A[p] (.) proj(h), B[c] > + unary[c].
-// One workgroup: the B*K*K rank-r triple products, then the K-state path
-// recursion one position at a time, then the backtrack.
+// selector_edges_kernel: one workgroup per position i stages its K candidate
+// rows of B and its predecessor rows of A (scaled by proj[i]) in LDS and forms
+// the K x K rank-r dot products.  selector_path_kernel: one workgroup runs
+// the K-state max-sum recursion over the positions and the backtrack.
 // ---------------------------------------------------------------------------
 constexpr int kSelMaxB = 16, kSelMaxK = 32, kSelMaxR = 256;
 
+__device__ __forceinline__ int clamp_idx(int v, long V) {
+  return v < 0 ? 0 : (v >= V ? (int)(V - 1) : v);   // never read out of bounds
+}
+
 template <typename TA>
-__global__ __launch_bounds__(256) void selector_kernel(SelArgs a) {
-  __shared__ float sproj[kSelMaxB * kSelMaxR];
+__global__ __launch_bounds__(256) void selector_edges_kernel(SelArgs a) {
+  extern __shared__ float sm[];
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x, K = a.K, r = a.r, rl = a.r + 1;   // +1: LDS bank spread
+  float *ap = sm;                 // [K][r+1]  A[pred] * proj[i]
+  float *bp = sm + K * rl;        // [K][r+1]  B[cand]
+  const TA *A = reinterpret_cast<const TA *>(a.cb_pred);
+  const TA *Bc = reinterpret_cast<const TA *>(a.cb_succ);
+  const float *pj = a.proj + (long)i * r;
+  const int npred = i == 0 ? (a.anchor < 0 ? 0 : 1) : K;
+  for (int e = tid; e < K * r; e += 256) {
+    const int b = e / r, rho = e - b * r;
+    const int c = clamp_idx(a.idx[i * K + b], a.V);
+    bp[b * rl + rho] = to_f32(Bc[(long)c * r + rho]);
+    if (b < npred) {
+      const int p = i == 0 ? a.anchor : clamp_idx(a.idx[(i - 1) * K + b], a.V);
+      ap[b * rl + rho] = to_f32(A[(long)p * r + rho]) * pj[rho];
+    }
+  }
+  __syncthreads();
+  const float *un = a.unary + (long)i * K;
+  float *eo = a.edges + (long)i * K * K;
+  for (int e = tid; e < K * K; e += 256) {
+    const int ai = e / K, bi = e - ai * K;
+    float v;
+    if (i == 0 && ai > 0) {
+      v = -__builtin_inff();
+    } else if (npred == 0) {
+      v = un[bi];
+    } else {
+      const float *x = ap + ai * rl, *y = bp + bi * rl;
+      float s = 0.f;
+      for (int k = 0; k < r; ++k) s += x[k] * y[k];
+      v = s + un[bi];
+    }
+    eo[e] = v;
+  }
+}
+
+// s_0[b] = edge[0][0][b]; s_i[b] = max_a s_{i-1}[a] + edge[i][a][b] (first max wins)
+__global__ __launch_bounds__(256) void selector_path_kernel(SelArgs a) {
+  __shared__ float se[kSelMaxB * kSelMaxK * kSelMaxK];
   __shared__ int sidx[kSelMaxB * kSelMaxK];
-  __shared__ float sun[kSelMaxB * kSelMaxK];
   __shared__ float score[2][kSelMaxK];
   __shared__ int back[kSelMaxB * kSelMaxK];
   const int tid = threadIdx.x;
-  const int B = a.B, K = a.K, r = a.r;
-  const TA *A = reinterpret_cast<const TA *>(a.cb_pred);
-  const TA *Bc = reinterpret_cast<const TA *>(a.cb_succ);
-  for (int e = tid; e < B * r; e += 256) sproj[e] = a.proj[e];
-  for (int e = tid; e < B * K; e += 256) {
-    int v = a.idx[e];
-    sidx[e] = v < 0 ? 0 : (v >= a.V ? (int)(a.V - 1) : v);   // never read out of bounds
-    sun[e] = a.unary[e];
-  }
+  const int B = a.B, K = a.K;
+  for (int e = tid; e < B * K * K; e += 256) se[e] = a.edges[e];
+  for (int e = tid; e < B * K; e += 256) sidx[e] = clamp_idx(a.idx[e], a.V);
   __syncthreads();
-  const float ninf = -__builtin_inff();
-  for (int e = tid; e < B * K * K; e += 256) {
-    const int i = e / (K * K), ab = e - i * K * K, ai = ab / K, bi = ab - ai * K;
-    float v;
-    if (i == 0 && ai > 0) {
-      v = ninf;
-    } else if (i == 0 && a.anchor < 0) {
-      v = sun[bi];
-    } else {
-      const long p = i == 0 ? a.anchor : sidx[(i - 1) * K + ai];
-      const long c = sidx[i * K + bi];
-      const TA *ap = A + p * r;
-      const TA *bp = Bc + c * r;
-      const float *pj = sproj + i * r;
-      float s = 0.f;
-      for (int k = 0; k < r; ++k) s += to_f32(ap[k]) * pj[k] * to_f32(bp[k]);
-      v = s + sun[i * K + bi];
-    }
-    a.edges[e] = v;
-  }
-  __syncthreads();
-  // s_0[b] = edge[0][0][b]; s_i[b] = max_a s_{i-1}[a] + edge[i][a][b] (first max wins)
-  if (tid < K) score[0][tid] = a.edges[tid];
+  if (tid < K) score[0][tid] = se[tid];
   __syncthreads();
   for (int i = 1; i < B; ++i) {
     const int cur = (i - 1) & 1;
     if (tid < K) {
-      const float *ei = a.edges + (long)i * K * K;
+      const float *ei = se + i * K * K;
       float best = score[cur][0] + ei[tid];
       int arg = 0;
       for (int ai = 1; ai < K; ++ai) {
@@ -226,10 +230,14 @@ __global__ __launch_bounds__(256) void selector_kernel(SelArgs a) {
 }
 
 hipError_t launch_selector(int act, const SelArgs &a, hipStream_t st) {
+  const size_t lds = (size_t)2 * a.K * (a.r + 1) * sizeof(float);
   if (act == ACT_F32)
-    hipLaunchKernelGGL((selector_kernel<float>), dim3(1), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((selector_edges_kernel<float>), dim3(a.B), dim3(256), lds, st, a);
   else
-    hipLaunchKernelGGL((selector_kernel<bf16>), dim3(1), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((selector_edges_kernel<bf16>), dim3(a.B), dim3(256), lds, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(selector_path_kernel, dim3(1), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

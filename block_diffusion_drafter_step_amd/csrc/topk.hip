@@ -17,6 +17,7 @@
 // (logit descending, index ascending) throughout.
 #include "common.h"
 #include "kernels.h"
+#include "stream.h"
 
 namespace dfl {
 
@@ -47,26 +48,30 @@ __device__ __forceinline__ void list_insert(float (&v)[KM], int (&ix)[KM], float
   }
 }
 
-template <typename TA, int WK>
-struct LmRow {
-  const void *p;
-  const uint16_t *s;
-};
-
-template <typename TA, int WK, int KM>
+template <typename TA, int WK, int KM, int TPW>
 __global__ __launch_bounds__(256) void lmhead_topk_kernel(TopkArgs a) {
-  constexpr int RT = 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int d = a.d;
   const long V = a.V;
   const long ntiles = (V + 15) / 16;
-  const long nwaves = (long)gridDim.x * 4;
+  const long nw = a.n_waves;
   const long wid = (long)blockIdx.x * 4 + wave;
-  const long t_beg = wid * ntiles / nwaves, t_end = (wid + 1) * ntiles / nwaves;
+  // contiguous, balanced tile ranges: every wave owns floor or ceil of ntiles / nw
+  const long t_beg = wid < nw ? wid * ntiles / nw : ntiles;
+  const long t_end = wid < nw ? (wid + 1) * ntiles / nw : ntiles;
+  const int cnt = (int)(t_end - t_beg);
   const bool tok_ok = r16 < a.B;
-  const TA *hr = reinterpret_cast<const TA *>(a.h) + (long)min(r16, a.B - 1) * d + 8 * g;
-  const bool vec_scales = (d & 255) == 0;
+  const TA *hr = reinterpret_cast<const TA *>(a.h) + (long)min(r16, a.B - 1) * d;
+
+  SRow<TA, WK> rows[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u)
+    rows[u] = srow<TA, WK>(a.w, a.scales, min((t_beg + u) * 16 + r16, V - 1), d);
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) acc[u] = zero4();
+  if (cnt > 0) stream_range<TA, WK, TPW>(hr, rows, cnt, 0, d, g, tok_ok, acc);
 
   float tv[KM];
   int ti[KM];
@@ -76,89 +81,16 @@ __global__ __launch_bounds__(256) void lmhead_topk_kernel(TopkArgs a) {
     ti[j] = 0x7fffffff;
   }
   float m = -__builtin_inff(), ssum = 0.f;
-
-  for (long t = t_beg; t < t_end; t += RT) {
-    const void *wp[RT];
-    const uint16_t *sp[RT];
+  // fold: lane holds rows (t_beg+u)*16 + 4g + i of token r16, visited in increasing order
 #pragma unroll
-    for (int u = 0; u < RT; ++u) {
-      const long row = min((t + u) * 16 + r16, V - 1);
-      if constexpr (WK == W_Q8_0) {
-        wp[u] = reinterpret_cast<const int8_t *>(a.w) + row * d;
-        sp[u] = reinterpret_cast<const uint16_t *>(a.scales) + row * (d >> 5);
-      } else {
-        wp[u] = reinterpret_cast<const TA *>(a.w) + row * d;
-        sp[u] = nullptr;
-      }
-    }
-    f32x4 acc[RT];
-#pragma unroll
-    for (int u = 0; u < RT; ++u) acc[u] = zero4();
-    int k = 0;
-    for (; k + 256 <= d; k += 256) {
-      Frag<TA> b[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = tok_ok ? load_frag(hr + k + 32 * j) : frag_zero<TA>();
-      if constexpr (WK == W_Q8_0) {
-        Frag<bf16> af[RT][8];
-#pragma unroll
-        for (int u = 0; u < RT; ++u) {
-          const int8_t *q = reinterpret_cast<const int8_t *>(wp[u]) + k + 8 * g;
-          uint2 c[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) c[j] = *reinterpret_cast<const uint2 *>(q + 32 * j);
-          float sc[8];
-          if (vec_scales) {
-            const uint4 s4 = *reinterpret_cast<const uint4 *>(sp[u] + (k >> 5));
-            const uint32_t w4[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              sc[j] = half_bits_to_f32((uint16_t)(w4[j >> 1] >> (16 * (j & 1))));
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sc[j] = half_bits_to_f32(sp[u][(k >> 5) + j]);
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) af[u][j] = dequant8(c[j], sc[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int u = 0; u < RT; ++u) mma(acc[u], af[u][j], b[j]);
-      } else {
-        Frag<TA> af[RT][8];
-#pragma unroll
-        for (int u = 0; u < RT; ++u)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            af[u][j] = load_frag(reinterpret_cast<const TA *>(wp[u]) + k + 32 * j + 8 * g);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int u = 0; u < RT; ++u) mma(acc[u], af[u][j], b[j]);
-      }
-    }
-    for (; k < d; k += 32) {
-      const Frag<TA> b = tok_ok ? load_frag(hr + k) : frag_zero<TA>();
-#pragma unroll
-      for (int u = 0; u < RT; ++u) {
-        if constexpr (WK == W_Q8_0) {
-          const uint2 c = *reinterpret_cast<const uint2 *>(reinterpret_cast<const int8_t *>(wp[u]) + k + 8 * g);
-          mma(acc[u], dequant8(c, half_bits_to_f32(sp[u][k >> 5])), b);
-        } else {
-          mma(acc[u], load_frag(reinterpret_cast<const TA *>(wp[u]) + k + 8 * g), b);
-        }
-      }
-    }
-    // fold: lane holds rows (t+u)*16 + 4g + i of token r16
-#pragma unroll
-    for (int u = 0; u < RT; ++u) {
+  for (int u = 0; u < TPW; ++u) {
+    if (u < cnt) {
       float v[4];
       float tmax = -__builtin_inff();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const long row = (t + u) * 16 + 4 * g + i;
-        v[i] = (t + u < t_end && row < V) ? acc[u][i] : -__builtin_inff();
+        const long row = (t_beg + u) * 16 + 4 * g + i;
+        v[i] = row < V ? acc[u][i] : -__builtin_inff();
         tmax = fmaxf(tmax, v[i]);
       }
       if (tmax > m) {
@@ -168,7 +100,7 @@ __global__ __launch_bounds__(256) void lmhead_topk_kernel(TopkArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (v[i] != -__builtin_inff()) ssum += exp2f((v[i] - m) * kL2e);
-        list_insert<KM>(tv, ti, v[i], (int)((t + u) * 16 + 4 * g + i));
+        list_insert<KM>(tv, ti, v[i], (int)((t_beg + u) * 16 + 4 * g + i));
       }
     }
   }
@@ -241,32 +173,52 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkArgs a) {
     ti[j] = 0x7fffffff;
   }
   float m = -__builtin_inff(), s = 0.f;
-  for (int w = tid; w < a.n_wg; w += 256) {
-    const long ob = (long)w * 16 + tok;
-    const float pm = a.part_ms[ob * 2], ps = a.part_ms[ob * 2 + 1];
-    if (ps > 0.f) {
-      if (pm > m) {
-        s = s * exp2f((m - pm) * kL2e);
-        m = pm;
-      }
-      s += ps * exp2f((pm - m) * kL2e);
-    }
-    for (int k = 0; k < K; ++k) {
-      const float v = a.part_val[ob * K + k];
-      const int ix = a.part_idx[ob * K + k];
-      // general insertion by (value desc, index asc)
-      if (better(v, ix, tv[KM - 1], ti[KM - 1])) {
-        tv[KM - 1] = v;
-        ti[KM - 1] = ix;
+  // every partial this thread merges is loaded before any is used (one
+  // memory round trip: the partials come from other XCDs' workgroups)
+  constexpr int PPT = 4;   // partial lists per thread per round
+  for (int w0 = tid; w0 < a.n_wg; w0 += 256 * PPT) {
+    float pm[PPT], ps[PPT], pv[PPT][KM];
+    int pi[PPT][KM];
 #pragma unroll
-        for (int j = KM - 1; j > 0; --j) {
-          const bool sw = better(tv[j], ti[j], tv[j - 1], ti[j - 1]);
-          const float xv = tv[j - 1];
-          const int xi = ti[j - 1];
-          tv[j - 1] = sw ? tv[j] : xv;
-          ti[j - 1] = sw ? ti[j] : xi;
-          tv[j] = sw ? xv : tv[j];
-          ti[j] = sw ? xi : ti[j];
+    for (int q = 0; q < PPT; ++q) {
+      const int w = w0 + 256 * q;
+      const bool ok = w < a.n_wg;
+      const long ob = (long)(ok ? w : 0) * 16 + tok;
+      pm[q] = ok ? a.part_ms[ob * 2] : -__builtin_inff();
+      ps[q] = ok ? a.part_ms[ob * 2 + 1] : 0.f;
+#pragma unroll
+      for (int k = 0; k < KM; ++k) {
+        pv[q][k] = (ok && k < K) ? a.part_val[ob * K + k] : -__builtin_inff();
+        pi[q][k] = (ok && k < K) ? a.part_idx[ob * K + k] : 0x7fffffff;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      if (ps[q] > 0.f) {
+        if (pm[q] > m) {
+          s = s * exp2f((m - pm[q]) * kL2e);
+          m = pm[q];
+        }
+        s += ps[q] * exp2f((pm[q] - m) * kL2e);
+      }
+#pragma unroll
+      for (int k = 0; k < KM; ++k) {
+        const float v = pv[q][k];
+        const int ix = pi[q][k];
+        // general insertion by (value desc, index asc)
+        if (better(v, ix, tv[KM - 1], ti[KM - 1])) {
+          tv[KM - 1] = v;
+          ti[KM - 1] = ix;
+#pragma unroll
+          for (int j = KM - 1; j > 0; --j) {
+            const bool sw = better(tv[j], ti[j], tv[j - 1], ti[j - 1]);
+            const float xv = tv[j - 1];
+            const int xi = ti[j - 1];
+            tv[j - 1] = sw ? tv[j] : xv;
+            ti[j - 1] = sw ? ti[j] : xi;
+            tv[j] = sw ? xv : tv[j];
+            ti[j] = sw ? xi : ti[j];
+          }
         }
       }
     }
@@ -334,26 +286,59 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkArgs a) {
   }
 }
 
-int topk_plan_wgs(long V) {
+// about DFL_TOPK_WAVES waves, each owning at most TPW consecutive 16-row
+// tiles of W_lm
+// (Q8_0 weights: DFL_TOPK_WAVES_Q8, more waves with fewer tiles each, as the
+// dequantisation needs more registers per tile)
+#ifndef DFL_TOPK_WAVES
+#define DFL_TOPK_WAVES 2048
+#endif
+#ifndef DFL_TOPK_WAVES_Q8
+#define DFL_TOPK_WAVES_Q8 4096
+#endif
+static const int kTpwChoices[] = {1, 2, 4, 5, 6, 8, 12, 16};
+
+static int topk_tpw(long V, int wkind) {
   const long ntiles = (V + 15) / 16;
-  long wgs = 512;
-  // every wave should own at least one 16-row tile
-  if (wgs * 4 > ntiles) wgs = (ntiles + 3) / 4;
-  return (int)(wgs < 1 ? 1 : wgs);
+  const long target = wkind == W_Q8_0 ? DFL_TOPK_WAVES_Q8 : DFL_TOPK_WAVES;
+  const long need = (ntiles + target - 1) / target;
+  for (int c : kTpwChoices)
+    if (c >= need) return c;
+  return 16;
+}
+
+int topk_plan_waves(long V, int wkind) {
+  const long ntiles = (V + 15) / 16;
+  const int tpw = topk_tpw(V, wkind);
+  return (int)((ntiles + tpw - 1) / tpw);
+}
+
+int topk_plan_wgs(long V, int wkind) { return (topk_plan_waves(V, wkind) + 3) / 4; }
+
+template <typename TA, int WK, int KM, int TPW>
+static void topk_launch_t(const TopkArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL((lmhead_topk_kernel<TA, WK, KM, TPW>), dim3(a.n_wg), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((topk_merge_kernel<KM>), dim3(a.B), dim3(256), 0, st, a);
 }
 
 template <typename TA, int WK, int KM>
-static void topk_launch_t(const TopkArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((lmhead_topk_kernel<TA, WK, KM>), dim3(a.n_wg), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((topk_merge_kernel<KM>), dim3(a.B), dim3(256), 0, st, a);
+static void topk_launch_tpw(const TopkArgs &a, hipStream_t st) {
+  switch (topk_tpw(a.V, WK)) {
+    case 1: topk_launch_t<TA, WK, KM, 1>(a, st); break;
+    case 2: topk_launch_t<TA, WK, KM, 2>(a, st); break;
+    case 4: topk_launch_t<TA, WK, KM, 4>(a, st); break;
+    case 5: topk_launch_t<TA, WK, KM, 5>(a, st); break;
+    case 6: topk_launch_t<TA, WK, KM, 6>(a, st); break;
+    case 8: topk_launch_t<TA, WK, KM, 8>(a, st); break;
+    case 12: topk_launch_t<TA, WK, KM, 12>(a, st); break;
+    default: topk_launch_t<TA, WK, KM, 16>(a, st); break;
+  }
 }
 
 template <typename TA, int WK>
 static void topk_launch_k(const TopkArgs &a, hipStream_t st) {
-  if (a.K <= 4) topk_launch_t<TA, WK, 4>(a, st);
-  else if (a.K <= 8) topk_launch_t<TA, WK, 8>(a, st);
-  else if (a.K <= 16) topk_launch_t<TA, WK, 16>(a, st);
-  else topk_launch_t<TA, WK, 32>(a, st);
+  if (a.K <= 8) topk_launch_tpw<TA, WK, 8>(a, st);
+  else topk_launch_tpw<TA, WK, 32>(a, st);
 }
 
 hipError_t launch_topk(int act, int wkind, const TopkArgs &a, hipStream_t st) {
