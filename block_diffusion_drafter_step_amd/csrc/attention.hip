@@ -19,7 +19,14 @@
 
 namespace dfl {
 
-constexpr int kAttnKT = 64;   // keys per LDS tile
+// keys per LDS tile (64 or 128) and the number of split workgroups aimed for
+#ifndef DFL_ATTN_KT
+#define DFL_ATTN_KT 64
+#endif
+#ifndef DFL_ATTN_WGS
+#define DFL_ATTN_WGS 512
+#endif
+constexpr int kAttnKT = DFL_ATTN_KT;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // four consecutive elements moved as one 8-byte (bf16) or 16-byte (fp32) access
@@ -32,7 +39,7 @@ template <typename TA, int HD>
 struct AttnCfg {
   static constexpr int KPAD = 16 / (int)sizeof(TA);
   static constexpr int KLD = HD + KPAD;             // K tile row (elements)
-  static constexpr int VLD = kAttnKT + 4;           // Vt row: 64 keys + 4
+  static constexpr int VLD = kAttnKT + 4;           // Vt row: the tile's keys + 4
   static constexpr int VEC = 16 / (int)sizeof(TA);  // elements per 16-byte chunk
   static constexpr int NQF = HD / 32;               // Q fragments (k-steps over dims)
   static constexpr int NDT = HD / 16;               // 16-dim output tiles
@@ -308,12 +315,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 }
 
 void attn_plan(long n_keys, int Hkv, int *chunk, int *n_split) {
-  const long target = 512 / (Hkv > 0 ? Hkv : 1) > 0 ? 512 / (Hkv > 0 ? Hkv : 1) : 1;
+  const int hk = Hkv > 0 ? Hkv : 1;
+  long target = DFL_ATTN_WGS / hk;
+  if (target < 1) target = 1;
   long c = (n_keys + target - 1) / target;
   c = ((c + kAttnKT - 1) / kAttnKT) * kAttnKT;
   if (c < kAttnKT) c = kAttnKT;
+  long ns = (n_keys + c - 1) / c;
+  // the combine kernel holds one weight per split in LDS
+  while (ns > kMaxSplit) {
+    c += kAttnKT;
+    ns = (n_keys + c - 1) / c;
+  }
   *chunk = (int)c;
-  *n_split = (int)((n_keys + c - 1) / c);
+  *n_split = (int)(ns < 1 ? 1 : ns);
 }
 
 template <typename TA, int HD>

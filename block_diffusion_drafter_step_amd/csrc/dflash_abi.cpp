@@ -156,6 +156,11 @@ size_t gemm_partial_bytes(int M, int N, int K) {
 
 constexpr int64_t kMaxRows = (int64_t)1 << 26;
 
+// LM head: h resident in LDS (1) or the streaming kernel only (0)
+#ifndef DFL_TOPK_RESIDENT
+#define DFL_TOPK_RESIDENT 1
+#endif
+
 // --- workspace sizes (buffers in the act type are sized for fp32) --------------
 
 size_t inject_ws(int32_t n_layers, int64_t n, int32_t d_t, int32_t d, int32_t kv) {
@@ -189,8 +194,9 @@ size_t attn_ws(int32_t B, int32_t d, int32_t Hq, int32_t Hkv, int32_t hd, int64_
 
 size_t topk_ws(int64_t V, int32_t K) {
   Carve c(nullptr);
-  // sized for the larger of the two plans (bf16/fp32 or Q8_0 weights)
-  const int n_wg = std::max(topk_plan_wgs(V, W_SAME), topk_plan_wgs(V, W_Q8_0));
+  // sized for the largest plan: streaming (bf16/fp32 or Q8_0 weights) or one
+  // resident workgroup per CU
+  const int n_wg = std::max(std::max(topk_plan_wgs(V, W_SAME), topk_plan_wgs(V, W_Q8_0)), kMaxCUs);
   c.take((size_t)n_wg * 16 * K * 4);
   c.take((size_t)n_wg * 16 * K * 4);
   c.take((size_t)n_wg * 16 * 2 * 4);
@@ -450,8 +456,21 @@ dflash_status dflash_topk_unary(const void *h, int32_t B, int32_t act,
   a.scales = lm_head->scales;
   a.V = V;
   a.K = K;
-  a.n_wg = topk_plan_wgs(V, wkind_of(lm_head));
-  a.n_waves = topk_plan_waves(V, wkind_of(lm_head));
+  const size_t lds = topk_lds_bytes(B, (int)d, act, K);
+  const int cus = std::min(device_cu_count(), kMaxCUs);
+  // resident path for bf16 / fp32 heads (measured faster there); Q8_0 heads
+  // stream (their dequantisation favours more waves)
+  if (DFL_TOPK_RESIDENT && lm_head->dtype != DFLASH_Q8_0 && lds <= kMaxLdsBytes && d % 128 == 0 &&
+      (long)cus * 4 <= (V + 15) / 16) {
+    a.lds_path = 1;
+    a.lds_bytes = (int)lds;
+    a.n_wg = cus;
+    a.n_waves = cus * 4;
+  } else {
+    a.lds_path = 0;
+    a.n_wg = topk_plan_wgs(V, wkind_of(lm_head));
+    a.n_waves = topk_plan_waves(V, wkind_of(lm_head));
+  }
   a.part_val = (float *)c.take((size_t)a.n_wg * 16 * K * 4);
   a.part_idx = (int *)c.take((size_t)a.n_wg * 16 * K * 4);
   a.part_ms = (float *)c.take((size_t)a.n_wg * 16 * 2 * 4);

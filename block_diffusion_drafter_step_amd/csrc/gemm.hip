@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(ASrc X, int M, WSet W,
   for (int s = k0 / kps; s * kps < k1; ++s) {
     const int ka = max(k0, s * kps), kb = min(k1, (s + 1) * kps);
     const TA *xr = reinterpret_cast<const TA *>(pick(X.ptr, s)) + trow - (long)s * kps;
-    stream_range<TA, WK, TPW>(xr, rows, cnt, ka, kb, g, tok_ok, acc);
+    stream_k<TA, WK, TPW>(xr, rows, cnt, ka, kb, g, tok_ok, acc);
   }
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {

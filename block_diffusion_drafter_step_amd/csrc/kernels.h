@@ -109,6 +109,8 @@ struct TopkArgs {
   int K;
   int n_wg;
   int n_waves;        // waves that own vocabulary tiles (<= 4 * n_wg)
+  int lds_path;       // 1: h resident in LDS, one persistent workgroup per CU
+  int lds_bytes;      // dynamic LDS of the resident path
   float *part_val;    // [n_wg][16][K]
   int *part_idx;      // [n_wg][16][K]
   float *part_ms;     // [n_wg][16][2]
@@ -116,6 +118,11 @@ struct TopkArgs {
   float *unary;       // [B][K]
 };
 int topk_plan_wgs(long V, int wkind);
+// LDS bytes of the h-resident LM-head kernel (h block or merge arrays)
+size_t topk_lds_bytes(int B, int d, int act, int K);
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+constexpr int kMaxCUs = 1024;
+int device_cu_count();
 int topk_plan_waves(long V, int wkind);
 hipError_t launch_topk(int act, int wkind, const TopkArgs &a, hipStream_t st);
 

@@ -8,6 +8,13 @@
 // Each weight load instruction reads 16 rows x 64 contiguous bytes straight
 // into registers; measured on MI355X this pattern streams at ~6 TB/s.
 //
+// Two forms of the chunk loop: guarded (loads only for tiles the wave owns and
+// chunks that exist) and unguarded (every load issued, rows clamped, results
+// past the end discarded; the compiler can then wait for one chunk at a time
+// instead of all outstanding loads).  Measured on MI355X the guarded form is
+// faster for these kernels (injection fc 65 vs 80 us, streaming LM head 308 vs
+// 388 us), so it is the default (DFL_STREAM_GUARDED).
+//
 // k-slot layouts (any assignment is valid if A and B fragments agree):
 //   bf16 / fp32 weights: MFMA j of a chunk takes k = 32 j + 8 g .. + 8 from
 //                        lane group g.
@@ -116,6 +123,91 @@ __device__ __forceinline__ void chunk_load(Chunk<TA, WK, TPW, NJ> &ch, const TA 
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int off = k + 64 * (j >> 1) + 16 * g + 8 * (j & 1);
+      ch.b[j] = load_frag(reinterpret_cast<const bf16 *>(xr) + off);
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+      for (int m = 0; m < NJ / 2; ++m) {
+        const int off = k + 64 * m + 16 * g;
+        ch.c[u][m] = wload16(reinterpret_cast<const int8_t *>(rows[u].p) + off);
+        ch.sc[u][m] = half_bits_to_f32(rows[u].s[off >> 5]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) ch.b[j] = load_frag(xr + k + 32 * j + 8 * g);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        ch.a[u][j] = wfrag(reinterpret_cast<const TA *>(rows[u].p) + k + 32 * j + 8 * g);
+    }
+  }
+}
+
+template <typename TA, int WK, int TPW, int NJ>
+__device__ __forceinline__ void chunk_mma(const Chunk<TA, WK, TPW, NJ> &ch, f32x4 (&acc)[TPW]) {
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    if constexpr (WK == W_Q8_0) {
+#pragma unroll
+      for (int m = 0; m < NJ / 2; ++m) {
+        mma(acc[u], dq8(ch.c[u][m].x, ch.c[u][m].y, ch.sc[u][m]), ch.b[2 * m]);
+        mma(acc[u], dq8(ch.c[u][m].z, ch.c[u][m].w, ch.sc[u][m]), ch.b[2 * m + 1]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) mma(acc[u], ch.a[u][j], ch.b[j]);
+    }
+  }
+}
+
+// acc[u] += W_u[16 rows][ka, kb) . X[16 tokens][ka, kb)^T for u < cnt; ka, kb
+// multiples of 64.  xr points at this lane's token row of X (xr[k] = X[t][k]).
+// Software-pipelined: the next 128-wide chunk's loads are issued before the
+// current chunk's MFMAs, so two chunks of loads are in flight per wave.
+template <typename TA, int WK, int TPW>
+__device__ __forceinline__ void stream_range(const TA *xr, const SRow<TA, WK> (&rows)[TPW], int cnt,
+                                             int ka, int kb, int g, bool tok_ok,
+                                             f32x4 (&acc)[TPW]) {
+  (void)cnt;
+  (void)tok_ok;
+  const int nfull = (kb - ka) >> 7;
+  int k = ka;
+  if (nfull > 0) {
+    const int klast = ka + (nfull - 1) * 128;
+    Chunk<TA, WK, TPW, 4> c0, c1;
+    chunk_load(c0, xr, rows, 0, k, g, true);
+    int c = 0;
+    for (; c + 2 <= nfull; c += 2) {
+      chunk_load(c1, xr, rows, 0, k + 128, g, true);
+      chunk_mma(c0, acc);
+      chunk_load(c0, xr, rows, 0, min(k + 256, klast), g, true);
+      chunk_mma(c1, acc);
+      k += 256;
+    }
+    if (c < nfull) {   // odd count: c0 holds the last chunk
+      chunk_mma(c0, acc);
+      k += 128;
+    }
+  }
+  if (k < kb) {
+    Chunk<TA, WK, TPW, 2> ct;
+    chunk_load(ct, xr, rows, 0, k, g, true);
+    chunk_mma(ct, acc);
+  }
+}
+
+// ---- guarded-load variant (loads under `u < cnt` and prefetch conditions) ----
+template <typename TA, int WK, int TPW, int NJ>
+__device__ __forceinline__ void chunk_load_g(Chunk<TA, WK, TPW, NJ> &ch, const TA *xr,
+                                           const SRow<TA, WK> (&rows)[TPW], int cnt, int k, int g,
+                                           bool tok_ok) {
+  if constexpr (WK == W_Q8_0) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int off = k + 64 * (j >> 1) + 16 * g + 8 * (j & 1);
       ch.b[j] = tok_ok ? load_frag(reinterpret_cast<const bf16 *>(xr) + off) : frag_zero<bf16>();
     }
 #pragma unroll
@@ -145,7 +237,7 @@ __device__ __forceinline__ void chunk_load(Chunk<TA, WK, TPW, NJ> &ch, const TA 
 }
 
 template <typename TA, int WK, int TPW, int NJ>
-__device__ __forceinline__ void chunk_mma(const Chunk<TA, WK, TPW, NJ> &ch, int cnt,
+__device__ __forceinline__ void chunk_mma_g(const Chunk<TA, WK, TPW, NJ> &ch, int cnt,
                                           f32x4 (&acc)[TPW]) {
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
@@ -164,46 +256,55 @@ __device__ __forceinline__ void chunk_mma(const Chunk<TA, WK, TPW, NJ> &ch, int 
   }
 }
 
-// Chunks of loads kept in flight per wave by stream_range (1 or 2).
-#ifndef DFL_STREAM_DEPTH
-#define DFL_STREAM_DEPTH 2
-#endif
 
 // acc[u] += W_u[16 rows][ka, kb) . X[16 tokens][ka, kb)^T for u < cnt; ka, kb
 // multiples of 64.  xr points at this lane's token row of X (xr[k] = X[t][k]).
 // Software-pipelined: the next 128-wide chunk's loads are issued before the
 // current chunk's MFMAs, so two chunks of loads are in flight per wave.
 template <typename TA, int WK, int TPW>
-__device__ __forceinline__ void stream_range(const TA *xr, const SRow<TA, WK> (&rows)[TPW], int cnt,
+__device__ __forceinline__ void stream_range_g(const TA *xr, const SRow<TA, WK> (&rows)[TPW], int cnt,
                                              int ka, int kb, int g, bool tok_ok,
                                              f32x4 (&acc)[TPW]) {
   const int nfull = (kb - ka) >> 7;
   int k = ka;
-  if (DFL_STREAM_DEPTH == 1) {
+  if (false) {
     for (; k + 128 <= kb; k += 128) {
       Chunk<TA, WK, TPW, 4> c0;
-      chunk_load(c0, xr, rows, cnt, k, g, tok_ok);
-      chunk_mma(c0, cnt, acc);
+      chunk_load_g(c0, xr, rows, cnt, k, g, tok_ok);
+      chunk_mma_g(c0, cnt, acc);
     }
   } else if (nfull > 0) {
     Chunk<TA, WK, TPW, 4> c0, c1;
-    chunk_load(c0, xr, rows, cnt, k, g, tok_ok);
+    chunk_load_g(c0, xr, rows, cnt, k, g, tok_ok);
     for (int c = 0; c < nfull; c += 2) {
-      if (c + 1 < nfull) chunk_load(c1, xr, rows, cnt, k + 128, g, tok_ok);
-      chunk_mma(c0, cnt, acc);
+      if (c + 1 < nfull) chunk_load_g(c1, xr, rows, cnt, k + 128, g, tok_ok);
+      chunk_mma_g(c0, cnt, acc);
       k += 128;
       if (c + 1 < nfull) {
-        if (c + 2 < nfull) chunk_load(c0, xr, rows, cnt, k + 128, g, tok_ok);
-        chunk_mma(c1, cnt, acc);
+        if (c + 2 < nfull) chunk_load_g(c0, xr, rows, cnt, k + 128, g, tok_ok);
+        chunk_mma_g(c1, cnt, acc);
         k += 128;
       }
     }
   }
   if (k < kb) {
     Chunk<TA, WK, TPW, 2> ct;
-    chunk_load(ct, xr, rows, cnt, k, g, tok_ok);
-    chunk_mma(ct, cnt, acc);
+    chunk_load_g(ct, xr, rows, cnt, k, g, tok_ok);
+    chunk_mma_g(ct, cnt, acc);
   }
+}
+
+#ifndef DFL_STREAM_GUARDED
+#define DFL_STREAM_GUARDED 1
+#endif
+
+template <typename TA, int WK, int TPW>
+__device__ __forceinline__ void stream_k(const TA *xr, const SRow<TA, WK> (&rows)[TPW], int cnt, int ka,
+                                         int kb, int g, bool tok_ok, f32x4 (&acc)[TPW]) {
+  if (DFL_STREAM_GUARDED)
+    stream_range_g<TA, WK, TPW>(xr, rows, cnt, ka, kb, g, tok_ok, acc);
+  else
+    stream_range<TA, WK, TPW>(xr, rows, cnt, ka, kb, g, tok_ok, acc);
 }
 
 }  // namespace dfl

@@ -48,6 +48,86 @@ __device__ __forceinline__ void list_insert(float (&v)[KM], int (&ix)[KM], float
   }
 }
 
+// Merge the 16 per-lane lists of each token in a workgroup (4 lane groups x
+// 4 waves) and write the workgroup's partial (top-K, max, sum of exp) per token.
+// Thread (token = tid / 16, list q = tid % 16) offers its list's head; a
+// 16-lane argmax by (value desc, index asc) picks the next entry K times.
+template <int KM>
+__device__ __forceinline__ void wg_merge_write(const float (&tv)[KM], const int (&ti)[KM], float m,
+                                               float ssum, const TopkArgs &a, float *lv, int *li,
+                                               float *lm, float *ls) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    lv[tid * KM + j] = tv[j];
+    li[tid * KM + j] = ti[j];
+  }
+  lm[tid] = m;
+  ls[tid] = ssum;
+  __syncthreads();
+  const int tok = tid >> 4, q = tid & 15;
+  // list q of token tok was written by thread (q/4)*64 + (q%4)*16 + tok
+  const int src = (q >> 2) * 64 + (q & 3) * 16 + tok;
+  const float pm = lm[src];
+  float M = pm;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, shfl_xor(M, o));
+  float ps = ls[src] > 0.f ? ls[src] * exp2f((pm - M) * kL2e) : 0.f;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) ps += shfl_xor(ps, o);
+  const long ob = (long)blockIdx.x * 16 + tok;
+  if (q == 0) {
+    a.part_ms[ob * 2] = M;
+    a.part_ms[ob * 2 + 1] = ps;
+  }
+  int head = 0;
+  for (int k = 0; k < a.K; ++k) {
+    float bv = head < KM ? lv[src * KM + head] : -__builtin_inff();
+    int bi = head < KM ? li[src * KM + head] : 0x7fffffff;
+    int bq = q;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float ov = shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o, kWave);
+      const int oq = __shfl_xor(bq, o, kWave);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+        bq = oq;
+      }
+    }
+    if (bq == q) ++head;
+    if (q == 0) {
+      a.part_val[ob * a.K + k] = bv;
+      a.part_idx[ob * a.K + k] = bi;
+    }
+  }
+}
+
+// Fold one 16-row tile's logits (lane: rows row0 + 4g + i of token r16) into
+// the running (max, sum of exp) and the sorted top-KM list.
+template <int KM>
+__device__ __forceinline__ void fold_tile(const f32x4 &acc, long row0, long V, int g, float &m,
+                                          float &ssum, float (&tv)[KM], int (&ti)[KM]) {
+  float v[4];
+  float tmax = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const long row = row0 + 4 * g + i;
+    v[i] = row < V ? acc[i] : -__builtin_inff();
+    tmax = fmaxf(tmax, v[i]);
+  }
+  if (tmax > m) {
+    ssum *= exp2f((m - tmax) * kL2e);
+    m = tmax;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (v[i] != -__builtin_inff()) ssum += exp2f((v[i] - m) * kL2e);
+    list_insert<KM>(tv, ti, v[i], (int)(row0 + 4 * g + i));
+  }
+}
+
 template <typename TA, int WK, int KM, int TPW>
 __global__ __launch_bounds__(256) void lmhead_topk_kernel(TopkArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -71,7 +151,7 @@ __global__ __launch_bounds__(256) void lmhead_topk_kernel(TopkArgs a) {
   f32x4 acc[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) acc[u] = zero4();
-  if (cnt > 0) stream_range<TA, WK, TPW>(hr, rows, cnt, 0, d, g, tok_ok, acc);
+  if (cnt > 0) stream_k<TA, WK, TPW>(hr, rows, cnt, 0, d, g, tok_ok, acc);
 
   float tv[KM];
   int ti[KM];
@@ -105,59 +185,171 @@ __global__ __launch_bounds__(256) void lmhead_topk_kernel(TopkArgs a) {
     }
   }
 
-  // merge the 16 lists of each token (4 lane groups x 4 waves) through LDS:
-  // thread (token = tid / 16, list q = tid % 16) offers its list's head; a
-  // 16-lane argmax by (value desc, index asc) picks the next entry K times
   __shared__ float lv[256 * KM];
   __shared__ int li[256 * KM];
   __shared__ float lm[256], ls[256];
+  wg_merge_write<KM>(tv, ti, m, ssum, a, lv, li, lm, ls);
+}
+
+// ---------------------------------------------------------------------------
+// LM head with the B x d activation block resident in LDS.  One persistent
+// workgroup per CU stages h once (so h is fetched 256 times per launch, not
+// once per wave per chunk); each wave then streams its contiguous range of
+// 16-row tiles, one tile at a time, through a DEPTH-deep ring of 128-wide
+// chunks that runs across tile boundaries, so DEPTH chunks of weight loads
+// are always in flight.  h rows are stored with the fragment index (8
+// elements) XORed by (token & 15): the 16 lanes reading one k-chunk of 16
+// tokens hit 16 different bank groups.
+// ---------------------------------------------------------------------------
+#ifndef DFL_LMH_DEPTH
+#define DFL_LMH_DEPTH 2
+#endif
+
+template <typename TA, int WK>
+struct LmStage {
+  Frag<TA> a[WK == W_Q8_0 ? 1 : 4];
+  uint4 c[WK == W_Q8_0 ? 2 : 1];
+  float sc[WK == W_Q8_0 ? 2 : 1];
+};
+
+// element k of token t's row, swizzled in units of one 8-element MFMA
+// fragment (16 bytes of bf16, 32 of fp32), so a fragment stays contiguous
+template <typename TA>
+__device__ __forceinline__ int hsw(int t, int k, int d) {
+  const int mask = ((d >> 3) & 15) == 0 ? 15 : 7;
+  const int ch = k >> 3;
+  return t * d + ((ch ^ (t & mask)) << 3) + (k & 7);
+}
+
+// (d % 128 == 0 on this path: every chunk is whole, so no load is guarded)
+template <typename TA, int WK>
+__device__ __forceinline__ void lm_stage_load(LmStage<TA, WK> &s, const void *w, const void *scales,
+                                              long row, int d, int k, int g) {
+  if constexpr (WK == W_Q8_0) {
+    const int8_t *p = reinterpret_cast<const int8_t *>(w) + row * d;
+    const uint16_t *sp = reinterpret_cast<const uint16_t *>(scales) + row * (d >> 5);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int off = k + 64 * m + 16 * g;
+      s.c[m] = *reinterpret_cast<const uint4 *>(p + off);
+      s.sc[m] = half_bits_to_f32(sp[off >> 5]);
+    }
+  } else {
+    const TA *p = reinterpret_cast<const TA *>(w) + row * d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s.a[j] = load_frag(p + k + 32 * j + 8 * g);
+  }
+}
+
+template <typename TA, int WK>
+__device__ __forceinline__ void lm_stage_mma(const LmStage<TA, WK> &s, const TA *hrow, int d, int k,
+                                             int g, int tok, f32x4 &acc) {
+  if constexpr (WK == W_Q8_0) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int off = k + 64 * m + 16 * g;
+      const Frag<bf16> b0 = load_frag(hrow + hsw<TA>(tok, off, d));
+      const Frag<bf16> b1 = load_frag(hrow + hsw<TA>(tok, off + 8, d));
+      mma(acc, dq8(s.c[m].x, s.c[m].y, s.sc[m]), b0);
+      mma(acc, dq8(s.c[m].z, s.c[m].w, s.sc[m]), b1);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const Frag<TA> b = load_frag(hrow + hsw<TA>(tok, k + 32 * j + 8 * g, d));
+      mma(acc, s.a[j], b);
+    }
+  }
+}
+
+template <typename TA, int WK, int KM>
+__global__ __launch_bounds__(256) void lmhead_topk_lds_kernel(TopkArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  TA *hs = reinterpret_cast<TA *>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int d = a.d, B = a.B;
+  const long V = a.V;
+  constexpr int VEC = 16 / (int)sizeof(TA);
+  // stage h (B rows) into LDS, swizzled
+  const TA *hg = reinterpret_cast<const TA *>(a.h);
+  for (int c = tid; c < B * (d / VEC); c += 256) {
+    const int t = c / (d / VEC), k = (c - t * (d / VEC)) * VEC;
+    *reinterpret_cast<uint4 *>(hs + hsw<TA>(t, k, d)) =
+        *reinterpret_cast<const uint4 *>(hg + (long)t * d + k);
+  }
+  __syncthreads();
+
+  const long ntiles = (V + 15) / 16;
+  const long nw = (long)gridDim.x * 4;
+  const long wid = (long)blockIdx.x * 4 + wave;
+  const long t_beg = wid * ntiles / nw, t_end = (wid + 1) * ntiles / nw;
+  const int nck = d / 128;
+  const int total = (int)(t_end - t_beg) * nck;
+  // tokens past B read token B-1's row (valid data); their columns are unused
+  const int tok = min(r16, B - 1);
+
+  float tv[KM];
+  int ti[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
-    lv[tid * KM + j] = tv[j];
-    li[tid * KM + j] = ti[j];
+    tv[j] = -__builtin_inff();
+    ti[j] = 0x7fffffff;
   }
-  lm[tid] = m;
-  ls[tid] = ssum;
-  __syncthreads();
-  {
-    const int tok = tid >> 4, q = tid & 15;
-    // list q of token tok was written by thread (q/4)*64 + (q%4)*16 + tok
-    const int src = (q >> 2) * 64 + (q & 3) * 16 + tok;
-    float pm = lm[src];
-    float M = pm;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, shfl_xor(M, o));
-    float ps = ls[src] > 0.f ? ls[src] * exp2f((pm - M) * kL2e) : 0.f;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) ps += shfl_xor(ps, o);
-    const long ob = (long)blockIdx.x * 16 + tok;
-    if (q == 0) {
-      a.part_ms[ob * 2] = M;
-      a.part_ms[ob * 2 + 1] = ps;
+  float m = -__builtin_inff(), ssum = 0.f;
+
+  constexpr int D = DFL_LMH_DEPTH;
+  LmStage<TA, WK> st[D];
+  // load cursor (tile lt, chunk lk); it stops at the wave's last chunk, so the
+  // refills past the end re-read that chunk (a cache hit) instead of branching
+  const long t_last = t_end > t_beg ? t_end - 1 : t_beg;
+  long lt = t_beg;
+  int lk = 0;
+  auto advance = [&]() {
+    if (lk + 1 < nck) {
+      ++lk;
+    } else if (lt < t_last) {
+      lk = 0;
+      ++lt;
     }
-    int head = 0;
-    for (int k = 0; k < a.K; ++k) {
-      float bv = head < KM ? lv[src * KM + head] : -__builtin_inff();
-      int bi = head < KM ? li[src * KM + head] : 0x7fffffff;
-      int bq = q;
+  };
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float ov = shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o, kWave);
-        const int oq = __shfl_xor(bq, o, kWave);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-          bq = oq;
+  for (int s = 0; s < D; ++s) {
+    lm_stage_load(st[s], a.w, a.scales, min(lt * 16 + r16, V - 1), d, lk * 128, g);
+    advance();
+  }
+  long ct = t_beg;
+  int ck = 0;
+  f32x4 acc = zero4();
+  for (int c = 0; c < total; c += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      if (c + s < total) {
+        lm_stage_mma(st[s], hs, d, ck * 128, g, tok, acc);
+        lm_stage_load(st[s], a.w, a.scales, min(lt * 16 + r16, V - 1), d, lk * 128, g);
+        advance();
+        if (++ck == nck) {
+          fold_tile<KM>(acc, ct * 16, V, g, m, ssum, tv, ti);
+          acc = zero4();
+          ck = 0;
+          ++ct;
         }
       }
-      if (bq == q) ++head;
-      if (q == 0) {
-        a.part_val[ob * a.K + k] = bv;
-        a.part_idx[ob * a.K + k] = bi;
-      }
     }
   }
+  __syncthreads();   // every wave is done with hs: reuse the LDS for the merge
+  float *lv = reinterpret_cast<float *>(smem);
+  int *li = reinterpret_cast<int *>(lv + 256 * KM);
+  float *lm = reinterpret_cast<float *>(li + 256 * KM);
+  float *ls = lm + 256;
+  wg_merge_write<KM>(tv, ti, m, ssum, a, lv, li, lm, ls);
+}
+
+size_t topk_lds_bytes(int B, int d, int act, int K) {
+  const int km = K <= 8 ? 8 : 32;
+  const size_t h = (size_t)B * d * (act == ACT_F32 ? 4 : 2);
+  const size_t mg = (size_t)256 * km * 8 + 256 * 8;
+  return h > mg ? h : mg;
 }
 
 // one workgroup per token: merge n_wg partial lists and (max, sum) pairs
@@ -335,10 +527,25 @@ static void topk_launch_tpw(const TopkArgs &a, hipStream_t st) {
   }
 }
 
+template <typename TA, int WK, int KM>
+static void topk_launch_lds(const TopkArgs &a, hipStream_t st) {
+  auto *kern = &lmhead_topk_lds_kernel<TA, WK, KM>;
+  // more than 64 KB of dynamic LDS has to be allowed explicitly
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes);
+  hipLaunchKernelGGL(kern, dim3(a.n_wg), dim3(256), (size_t)a.lds_bytes, st, a);
+  hipLaunchKernelGGL((topk_merge_kernel<KM>), dim3(a.B), dim3(256), 0, st, a);
+}
+
 template <typename TA, int WK>
 static void topk_launch_k(const TopkArgs &a, hipStream_t st) {
-  if (a.K <= 8) topk_launch_tpw<TA, WK, 8>(a, st);
-  else topk_launch_tpw<TA, WK, 32>(a, st);
+  if (a.lds_path) {
+    if (a.K <= 8) topk_launch_lds<TA, WK, 8>(a, st);
+    else topk_launch_lds<TA, WK, 32>(a, st);
+  } else {
+    if (a.K <= 8) topk_launch_tpw<TA, WK, 8>(a, st);
+    else topk_launch_tpw<TA, WK, 32>(a, st);
+  }
 }
 
 hipError_t launch_topk(int act, int wkind, const TopkArgs &a, hipStream_t st) {
@@ -346,6 +553,19 @@ hipError_t launch_topk(int act, int wkind, const TopkArgs &a, hipStream_t st) {
   else if (wkind == W_Q8_0) topk_launch_k<bf16, W_Q8_0>(a, st);
   else topk_launch_k<bf16, W_SAME>(a, st);
   return hipGetLastError();
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace dfl
