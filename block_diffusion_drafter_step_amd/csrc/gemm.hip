@@ -358,10 +358,348 @@ static void tile_launch_t(const ASrc &A, int M, const WSet &W, const OutSpec &ou
     hipLaunchKernelGGL((tile_gemm_kernel<TA, WK, OUT_CACHE>), grid, dim3(256), 0, st, A, M, W, out);
 }
 
+// ---------------------------------------------------------------------------
+// big-tile GEMM for the prefill injection: 256 x 256 x 64 tiles, 4 waves each
+// computing a 128 x 128 block (8 x 8 MFMA tiles, 256 fp32 accumulators), so
+// every fragment read from LDS feeds 8 MFMAs and LDS bandwidth stays below the
+// MFMA rate.  Double-buffered LDS (2 x 2 x 256 x 72 bf16 = 147 KB), the next
+// k-tile prefetched into registers while the current one is multiplied.
+// Tiles are ordered XCD-aware: workgroups are dealt to the 8 XCDs round-robin,
+// so each XCD is given a contiguous band of M-tiles, walked in groups of 4
+// M-tiles x all N-tiles, and the workgroups resident on one XCD share A and B
+// tiles in that XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8;
+
+template <int WK>
+struct BigLoader {
+  uint4 a[8];
+  uint4 w[8];      // SAME: 16-byte chunks; Q8_0: 4 x 16 codes in w[0..3]
+  float sc[4];
+
+  __device__ __forceinline__ void load(const ASrc &A, int M, const WSet &W, int m0, int n0, int k0,
+                                       int tid) {
+    const int s = k0 / A.k_per_src;
+    const int kl = k0 - s * A.k_per_src;
+    const bf16 *src = reinterpret_cast<const bf16 *>(pick(A.ptr, s));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = tid + 256 * j;          // 2048 chunks: row c / 8, chunk c % 8
+      const int row = c >> 3, ch = c & 7;
+      const int m = min(m0 + row, M - 1);
+      a[j] = *reinterpret_cast<const uint4 *>(src + (long)m * A.k_per_src + kl + ch * 8);
+    }
+    if constexpr (WK == W_Q8_0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = tid + 256 * j;        // 1024 chunks of 16 codes: row c / 4, chunk c % 4
+        const int row = c >> 2, ch = c & 3;
+        const int n = min(n0 + row, W.n_total - 1);
+        int lr;
+        const int sg = seg_of(W, n, &lr);
+        const int8_t *q = reinterpret_cast<const int8_t *>(pick(W.data, sg)) + (long)lr * W.K + k0 + ch * 16;
+        w[j] = *reinterpret_cast<const uint4 *>(q);
+        const uint16_t *scp = reinterpret_cast<const uint16_t *>(pick(W.scales, sg)) + (long)lr * (W.K >> 5);
+        sc[j] = half_bits_to_f32(scp[(k0 + ch * 16) >> 5]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = tid + 256 * j;
+        const int row = c >> 3, ch = c & 7;
+        const int n = min(n0 + row, W.n_total - 1);
+        int lr;
+        const int sg = seg_of(W, n, &lr);
+        w[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const bf16 *>(pick(W.data, sg)) +
+                                                (long)lr * W.K + k0 + ch * 8);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(bf16 *As, bf16 *Ws, int tid) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c >> 3, ch = c & 7;
+      *reinterpret_cast<uint4 *>(As + row * GLD + ch * 8) = a[j];
+    }
+    if constexpr (WK == W_Q8_0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = tid + 256 * j;
+        const int row = c >> 2, ch = c & 3;
+        const Frag<bf16> lo = dequant8(make_uint2(w[j].x, w[j].y), sc[j]);
+        const Frag<bf16> hi = dequant8(make_uint2(w[j].z, w[j].w), sc[j]);
+        *reinterpret_cast<bf16x8 *>(Ws + row * GLD + ch * 16) = lo.v;
+        *reinterpret_cast<bf16x8 *>(Ws + row * GLD + ch * 16 + 8) = hi.v;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = tid + 256 * j;
+        const int row = c >> 3, ch = c & 7;
+        *reinterpret_cast<uint4 *>(Ws + row * GLD + ch * 8) = w[j];
+      }
+    }
+  }
+};
+
+// workgroup id -> (m-tile, n-tile)
+__device__ __forceinline__ void big_tile_of(int L, int mt, int nt, int *tm, int *tn) {
+  const int T = mt * nt;
+  int j = L;
+  if ((mt & 7) == 0) {                      // deal a contiguous band of m-tiles to each XCD
+    const int per = T >> 3;
+    j = (L & 7) * per + (L >> 3);
+  }
+  // groups of 4 m-tiles x all n-tiles, m fastest inside a group
+  const int GM = 4;
+  const int grp = j / (GM * nt);
+  const int rem = j - grp * GM * nt;
+  const int gm = min(GM, mt - grp * GM);
+  *tn = rem / gm;
+  *tm = grp * GM + (rem - *tn * gm);
+}
+
+template <int WK, int OM>
+__global__ __launch_bounds__(256) void big_gemm_kernel(ASrc A, int M, WSet W, OutSpec o) {
+  extern __shared__ __attribute__((aligned(16))) char smem_big[];
+  bf16 *As = reinterpret_cast<bf16 *>(smem_big);            // [2][256][GLD]
+  bf16 *Ws = As + 2 * GBM * GLD;                            // [2][256][GLD]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int mt = (M + GBM - 1) / GBM, nt = (W.n_total + GBN - 1) / GBN;
+  int tm, tn;
+  big_tile_of(blockIdx.x, mt, nt, &tm, &tn);
+  const int m0 = tm * GBM, n0 = tn * GBN;
+  const int nk = W.K / GBK;
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = zero4();
+
+  BigLoader<WK> ld;
+  ld.load(A, M, W, m0, n0, 0, tid);
+  ld.store(As, Ws, tid);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    ld.load(A, M, W, m0, n0, min(kt + 1, nk - 1) * GBK, tid);
+    const bf16 *as = As + cur * GBM * GLD + (wm * 128 + r16) * GLD + 8 * g;
+    const bf16 *ws = Ws + cur * GBN * GLD + (wn * 128 + r16) * GLD + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < GBK; kk += 32) {
+      Frag<bf16> fb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fb[j] = load_frag(ws + 16 * j * GLD + kk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const Frag<bf16> fa = load_frag(as + 16 * i * GLD + kk);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mma(acc[i][j], fa, fb[j]);
+      }
+    }
+    ld.store(As + (cur ^ 1) * GBM * GLD, Ws + (cur ^ 1) * GBN * GLD, tid);
+    __syncthreads();
+  }
+  // acc[i][j][v]: row m0 + wm*128 + 16 i + 4 g + v, column n0 + wn*128 + 16 j + r16
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + wn * 128 + 16 * j + r16;
+      if (n >= W.n_total) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * 128 + 16 * i + 4 * g + v;
+        if (m < M) store_out_m<bf16, OM>(o, m, n, acc[i][j][v]);
+      }
+    }
+}
+
+constexpr size_t kBigLds = (size_t)2 * (GBM + GBN) * GLD * sizeof(bf16);
+
+template <int WK>
+static void big_launch_t(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
+  const int mt = (M + GBM - 1) / GBM, nt = (W.n_total + GBN - 1) / GBN;
+  const dim3 grid(mt * nt);
+  if (out.mode == OUT_F32) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&big_gemm_kernel<WK, OUT_F32>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
+    hipLaunchKernelGGL((big_gemm_kernel<WK, OUT_F32>), grid, dim3(256), kBigLds, st, A, M, W, out);
+  } else if (out.mode == OUT_ACT) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&big_gemm_kernel<WK, OUT_ACT>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
+    hipLaunchKernelGGL((big_gemm_kernel<WK, OUT_ACT>), grid, dim3(256), kBigLds, st, A, M, W, out);
+  } else {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&big_gemm_kernel<WK, OUT_CACHE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
+    hipLaunchKernelGGL((big_gemm_kernel<WK, OUT_CACHE>), grid, dim3(256), kBigLds, st, A, M, W, out);
+  }
+}
+
+#ifndef DFL_BIG_GEMM_MIN_M
+#define DFL_BIG_GEMM_MIN_M 1024
+#endif
+
+// ---------------------------------------------------------------------------
+// prefill GEMM with direct-to-LDS loads (bf16 activations and weights).
+// 256 x 256 tile, k-step 32, 4 waves each owning a 128 x 128 block.  Global
+// memory is copied into LDS by global_load_lds_dwordx4 (no register staging)
+// into a 4-stage ring of 32 KB stages, so three k-steps of loads are in flight
+// while one is multiplied; one barrier per k-step.  A wave instruction writes
+// 1 KB of LDS in lane order (16 rows x 64 bytes); within a row the four
+// 16-byte slots hold chunks c ^ ((row / 4) & 3), so the 16 rows read by one
+// fragment load fall in 16 different bank groups.
+// ---------------------------------------------------------------------------
+constexpr int DBM = 256, DBN = 256, DBK = 32, DSTAGES = 4;
+constexpr int DSTAGE_BYTES = (DBM + DBN) * DBK * 2;   // 32 KB
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void *g, lds_void *l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ int dslot(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+// issue one stage: A rows [m0, m0+256) and W rows [n0, n0+256), k [k0, k0+32)
+__device__ __forceinline__ void dma_stage(char *stage, const ASrc &A, int M, const WSet &W, int m0,
+                                          int n0, int k0, int wave, int lane) {
+  const int s = k0 / A.k_per_src;
+  const int kl = k0 - s * A.k_per_src;
+  const bf16 *src = reinterpret_cast<const bf16 *>(pick(A.ptr, s));
+  const int rl = lane >> 2, slot = lane & 3;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (wave * 4 + j) * 16 + rl;
+    const int c = dslot(row, slot);
+    const int m = min(m0 + row, M - 1);
+    dma16(src + (long)m * A.k_per_src + kl + 8 * c,
+          (lds_void *)(stage + (wave * 4 + j) * 1024));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (wave * 4 + j) * 16 + rl;
+    const int c = dslot(row, slot);
+    const int n = min(n0 + row, W.n_total - 1);
+    int lr;
+    const int sg = seg_of(W, n, &lr);
+    const bf16 *wp = reinterpret_cast<const bf16 *>(pick(W.data, sg)) + (long)lr * W.K + k0 + 8 * c;
+    dma16(wp, (lds_void *)(stage + DBM * DBK * 2 + (wave * 4 + j) * 1024));
+  }
+}
+
+template <int OM>
+__global__ __launch_bounds__(256) void dma_gemm_kernel(ASrc A, int M, WSet W, OutSpec o) {
+  extern __shared__ __attribute__((aligned(1024))) char smem_dma[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int mt = (M + DBM - 1) / DBM, nt = (W.n_total + DBN - 1) / DBN;
+  int tm, tn;
+  big_tile_of(blockIdx.x, mt, nt, &tm, &tn);
+  const int m0 = tm * DBM, n0 = tn * DBN;
+  const int nk = W.K / DBK;
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = zero4();
+
+  // prologue: stages 0 .. DSTAGES-2 in flight (re-issuing the last k-step when
+  // nk is short keeps the count of outstanding loads fixed)
+#pragma unroll
+  for (int s = 0; s < DSTAGES - 1; ++s)
+    dma_stage(smem_dma + s * DSTAGE_BYTES, A, M, W, m0, n0, min(s, nk - 1) * DBK, wave, lane);
+
+  // this lane's fragment rows and swizzled slots
+  const int ar = wm * 128 + r16, br = wn * 128 + r16;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vm<8 * (DSTAGES - 2)>();   // this wave's loads of stage kt have landed
+    __syncthreads();                 // ... everyone's, and stage kt-1 is no longer read
+    dma_stage(smem_dma + ((kt + DSTAGES - 1) % DSTAGES) * DSTAGE_BYTES, A, M, W, m0, n0,
+              min(kt + DSTAGES - 1, nk - 1) * DBK, wave, lane);
+    const char *st = smem_dma + (kt % DSTAGES) * DSTAGE_BYTES;
+    const bf16 *as = reinterpret_cast<const bf16 *>(st);
+    const bf16 *ws = reinterpret_cast<const bf16 *>(st + DBM * DBK * 2);
+    Frag<bf16> fb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = br + 16 * j;
+      fb[j] = load_frag(ws + row * DBK + 8 * dslot(row, g));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = ar + 16 * i;
+      const Frag<bf16> fa = load_frag(as + row * DBK + 8 * dslot(row, g));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mma(acc[i][j], fa, fb[j]);
+    }
+  }
+  wait_vm<0>();
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + wn * 128 + 16 * j + r16;
+      if (n >= W.n_total) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * 128 + 16 * i + 4 * g + v;
+        if (m < M) store_out_m<bf16, OM>(o, m, n, acc[i][j][v]);
+      }
+    }
+}
+
+constexpr size_t kDmaLds = (size_t)DSTAGES * DSTAGE_BYTES;
+
+static void dma_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
+  const int mt = (M + DBM - 1) / DBM, nt = (W.n_total + DBN - 1) / DBN;
+  const dim3 grid(mt * nt);
+  if (out.mode == OUT_F32) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma_gemm_kernel<OUT_F32>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds);
+    hipLaunchKernelGGL((dma_gemm_kernel<OUT_F32>), grid, dim3(256), kDmaLds, st, A, M, W, out);
+  } else if (out.mode == OUT_ACT) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma_gemm_kernel<OUT_ACT>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds);
+    hipLaunchKernelGGL((dma_gemm_kernel<OUT_ACT>), grid, dim3(256), kDmaLds, st, A, M, W, out);
+  } else {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma_gemm_kernel<OUT_CACHE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds);
+    hipLaunchKernelGGL((dma_gemm_kernel<OUT_CACHE>), grid, dim3(256), kDmaLds, st, A, M, W, out);
+  }
+}
+
+#ifndef DFL_PREFILL_KERNEL
+#define DFL_PREFILL_KERNEL 2     // 0: 128-tile, 1: 256-tile register-staged, 2: 256-tile direct-to-LDS
+#endif
+
+
 hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet &W,
                             const OutSpec &out, hipStream_t st) {
   if (act == ACT_F32)
     tile_launch_t<float, W_SAME>(A, M, W, out, st);
+  else if (M >= DFL_BIG_GEMM_MIN_M && wkind == W_SAME && DFL_PREFILL_KERNEL == 2)
+    dma_launch(A, M, W, out, st);
+  else if (M >= DFL_BIG_GEMM_MIN_M && wkind == W_Q8_0 && DFL_PREFILL_KERNEL >= 1)
+    big_launch_t<W_Q8_0>(A, M, W, out, st);
+  else if (M >= DFL_BIG_GEMM_MIN_M && DFL_PREFILL_KERNEL >= 1)
+    big_launch_t<W_SAME>(A, M, W, out, st);
   else if (wkind == W_Q8_0)
     tile_launch_t<bf16, W_Q8_0>(A, M, W, out, st);
   else
