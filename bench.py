@@ -63,7 +63,7 @@ def traffic_from_counters():
         c = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
-    if c.get("source_hash") != src_hash("topk.hip", "common.h"):
+    if c.get("source_hash") != src_hash("topk.hip", "common.h", "stream.h", "dflash_abi.cpp"):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -212,7 +212,7 @@ def main():
     lm_bytes = workmodel.lmhead_bytes(cfg)
     lm_gbs = lm_bytes / (topk_ms * 1e-3) / 1e9
     attn_bytes = workmodel.attn_bytes(cfg, int(ctx_mean))
-    roofline = {"bound": "hbm", "kernel": "dflash_topk_unary (lmhead_topk_kernel + topk_merge_kernel)",
+    roofline = {"bound": "hbm", "kernel": "dflash_topk_unary (LM-head top-K kernel + topk_merge_kernel)",
                 "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_counters(),
                 "bytes_per_launch": lm_bytes, "launch_ms": round(topk_ms, 4),
