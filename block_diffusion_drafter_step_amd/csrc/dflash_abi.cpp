@@ -87,11 +87,13 @@ dflash_status check_ws(void *ws, size_t ws_bytes, size_t need) {
   return DFLASH_OK;
 }
 
-// bump allocator over the caller's workspace (256-byte aligned pieces)
+// bump allocator over the caller's workspace (256-byte aligned pieces); the
+// completion counters always come first
 struct Carve {
   char *base;
   size_t off = 0;
-  explicit Carve(void *p) : base((char *)p) {}
+  unsigned *counters;
+  explicit Carve(void *p) : base((char *)p) { counters = (unsigned *)take(kCounterBytes); }
   void *take(size_t bytes) {
     void *p = base ? base + off : nullptr;
     off += (bytes + 255) & ~(size_t)255;
@@ -144,9 +146,9 @@ OutSpec out_act(void *p, long ld, const void *resid, long ld_resid) {
   return o;
 }
 
-hipError_t gemm(int act, int wkind, const ASrc &A, int M, const WSet &W, float *part,
+hipError_t gemm(int act, int wkind, const ASrc &A, int M, const WSet &W, float *part, unsigned *cnt,
                 const OutSpec &o, hipStream_t st) {
-  if (M <= kSkinnyMaxM) return launch_skinny_gemm(act, wkind, A, M, W, part, o, st);
+  if (M <= kSkinnyMaxM) return launch_skinny_gemm(act, wkind, A, M, W, part, cnt, o, st);
   return launch_tile_gemm(act, wkind, A, M, W, o, st);
 }
 
@@ -319,7 +321,7 @@ dflash_status dflash_inject(const void *const *layer_hidden, int32_t n_layers, i
   for (int l = 0; l < n_layers; ++l) A.ptr[l] = layer_hidden[l];
   A.n_src = n_layers;
   A.k_per_src = d_t;
-  hipError_t e = gemm(act, wkind_of(fc), A, n, wset({fc}), part, out_f32(y, d), st);
+  hipError_t e = gemm(act, wkind_of(fc), A, n, wset({fc}), part, c.counters, out_f32(y, d), st);
   if (e != hipSuccess) return launched(e, "fc");
   e = launch_rmsnorm(act, y, n, (int)d, gamma, eps, z, st);
   if (e != hipSuccess) return launched(e, "rmsnorm");
@@ -332,7 +334,7 @@ dflash_status dflash_inject(const void *const *layer_hidden, int32_t n_layers, i
   oc.split = (int)kv;
   oc.cap = cache->capacity;
   oc.pos0 = pos0;
-  e = gemm(act, wkind_of(wk), asrc1(z, (int)d), n, wset({wk, wv}), part, oc, st);
+  e = gemm(act, wkind_of(wk), asrc1(z, (int)d), n, wset({wk, wv}), part, c.counters, oc, st);
   return launched(e, "wk/wv");
 }
 
@@ -357,7 +359,7 @@ dflash_status dflash_conv(const void *x, int32_t n_blocks, int32_t B, int32_t C,
   const int M = n_blocks * B;
   float *part = (float *)c.take(gemm_partial_bytes(M, T * G, C));
   float *delta = (float *)c.take((size_t)M * T * G * 4);
-  hipError_t e = gemm(act, W_SAME, asrc1(x, C), M, wset({w_delta}), part, out_f32(delta, T * G), st);
+  hipError_t e = gemm(act, W_SAME, asrc1(x, C), M, wset({w_delta}), part, c.counters, out_f32(delta, T * G), st);
   if (e != hipSuccess) return launched(e, "delta");
   e = launch_conv(act, x, n_blocks, B, C, G, T, base, delta, out, st);
   return launched(e, "conv");
@@ -407,7 +409,7 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   a.part_ml = (float *)c.take((size_t)n_q_heads * B * a.n_split * 2 * 4);
   void *o = c.take((size_t)B * qdim * 4);
 
-  hipError_t e = gemm(act, wkind_of(wq), asrc1(u, d), B, wset({wq, wk, wv}), part,
+  hipError_t e = gemm(act, wkind_of(wq), asrc1(u, d), B, wset({wq, wk, wv}), part, c.counters,
                       out_act(qkv, nqkv, nullptr, 0), st);
   if (e != hipSuccess) return launched(e, "qkv");
   a.qkv = qkv;
@@ -423,7 +425,7 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   a.o = o;
   e = launch_attention(act, a, st);
   if (e != hipSuccess) return launched(e, "attention");
-  e = gemm(act, wkind_of(wo), asrc1(o, (int)qdim), B, wset({wo}), part, out_act(out, d, residual, d), st);
+  e = gemm(act, wkind_of(wo), asrc1(o, (int)qdim), B, wset({wo}), part, c.counters, out_act(out, d, residual, d), st);
   return launched(e, "wo");
 }
 
@@ -510,7 +512,7 @@ dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
   Carve c(ws);
   float *part = (float *)c.take(gemm_partial_bytes(B, (int)r, (int)d));
   float *pj = (float *)c.take((size_t)B * r * 4);
-  hipError_t e = gemm(act, W_SAME, asrc1(h, (int)d), B, wset({proj}), part, out_f32(pj, r), st);
+  hipError_t e = gemm(act, W_SAME, asrc1(h, (int)d), B, wset({proj}), part, c.counters, out_f32(pj, r), st);
   if (e != hipSuccess) return launched(e, "project");
   SelArgs a;
   a.proj = pj;

@@ -6,12 +6,15 @@
 //    is streamed from HBM exactly once and that stream is the whole cost, so
 //    each wave keeps its W fragments in registers straight from global memory
 //    (no LDS), the 16 rows fill the N side of a 16x16x32 MFMA, and split-K
-//    gives enough waves to keep HBM busy; partials are summed in a fixed order
-//    by a second kernel (bitwise reproducible).
+//    gives enough waves to keep HBM busy; partial sums are always added in a
+//    fixed order (bitwise reproducible), by a second kernel for large
+//    weights, in LDS and by the last workgroup to finish for small ones.
 //  * tiled: many rows (a 32k-token prefill injection).  MFMA-bound; classic
 //    LDS-staged tiles with double buffering and a register prefetch of the
 //    next k-tile.  The activation operand may be several arrays side by side
 //    along K (the concatenated target-layer features are never materialised).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "stream.h"
@@ -63,152 +66,303 @@ __device__ __forceinline__ int seg_of(const WSet &W, int n, int *local) {
 // skinny (weight-streaming) GEMM
 // ---------------------------------------------------------------------------
 
-// Workgroup (x, y): 4 waves, each owning TPW consecutive 16-row tiles of the
-// stacked weight, over k-range y.  Partials part[y][n][16] (fp32).
-template <typename TA, int WK, int TPW>
-__global__ __launch_bounds__(256) void skinny_gemm_kernel(ASrc X, int M, WSet W, int kchunk,
-                                                          float *__restrict__ part) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Two arrangements of the waves of workgroup (x, y) over the tiles (TPW
+// consecutive 16-row tiles of the stacked weight per wave) and the k-ranges:
+//  * SPLIT_TILES: wave w owns tile group WPG x + w over k-range y and writes
+//    its own partials part[y][tile][lane] (float4), summed in k-range order
+//    by splitk_reduce_kernel.  Best for large weights: each wave streams
+//    independently.
+//  * otherwise: all waves own tile group x and stream the WPG consecutive
+//    k-ranges (WPG y + wave) * kchunk of it; their accumulators are summed in
+//    LDS in a fixed pairwise order.  With one k-group the workgroup writes
+//    the outputs.  Otherwise it writes one partial per tile, and the last
+//    workgroup of the tile group to finish -- found with the counter cnt[x],
+//    which it returns to zero -- sums the partials in k-group order and
+//    writes the outputs: one kernel, bitwise reproducible (the order never
+//    depends on which workgroup finishes last).  Partials are written and
+//    read with device-scope (cross-XCD coherent) accesses, so no cache-wide
+//    write-back or invalidate is needed, and no workgroup ever waits for
+//    another.  Best for small weights, where a second launch would cost more
+//    than the stream.  cnt == nullptr: partials only, as for SPLIT_TILES.
+template <typename TA, int WK, int TPW, int WPG, bool SPLIT_TILES>
+__global__ __launch_bounds__(WPG * 64, WPG >= 8 ? WPG / 4 : 2) void skinny_gemm_kernel(
+    ASrc X, int M, WSet W, int kchunk, float *__restrict__ part, unsigned *__restrict__ cnt,
+    OutSpec o) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: tiles, k-range and loop bounds stay uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int N = W.n_total, K = W.K;
   const int ntile = (N + 15) >> 4;
-  const int tile0 = (blockIdx.x * 4 + wave) * TPW;
-  const int cnt = min(TPW, ntile - tile0);
-  if (cnt <= 0) return;
-  const int k0 = blockIdx.y * kchunk;
+  const int tile0 = (SPLIT_TILES ? blockIdx.x * WPG + wave : blockIdx.x) * TPW;
+  const int tcnt = min(TPW, ntile - tile0);
+  // SPLIT_TILES: a wave past the last tile has nothing to do (no barrier
+  // follows); otherwise never taken (the grid covers the tiles exactly)
+  if (tcnt <= 0) return;
+  const int k0 = (SPLIT_TILES ? blockIdx.y : blockIdx.y * WPG + wave) * kchunk;
   const int k1 = min(K, k0 + kchunk);
-
-  SRow<TA, WK> rows[TPW];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    int lr;
-    const int n = min((tile0 + u) * 16 + r16, N - 1);
-    const int sg = seg_of(W, n, &lr);
-    rows[u] = srow<TA, WK>(pick(W.data, sg), pick(W.scales, sg), lr, K);
-  }
-  const bool tok_ok = r16 < M;
-  const int kps = X.k_per_src;
-  const long trow = (long)min(r16, M - 1) * kps;
 
   f32x4 acc[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) acc[u] = zero4();
-  // walk the k-range one activation source at a time
-  for (int s = k0 / kps; s * kps < k1; ++s) {
-    const int ka = max(k0, s * kps), kb = min(k1, (s + 1) * kps);
-    const TA *xr = reinterpret_cast<const TA *>(pick(X.ptr, s)) + trow - (long)s * kps;
-    stream_k<TA, WK, TPW>(xr, rows, cnt, ka, kb, g, tok_ok, acc);
-  }
+  if (k0 < k1) {
+    SRow<TA, WK> rows[TPW];
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    if (u < cnt) {
+    for (int u = 0; u < TPW; ++u) {
+      int lr;
+      const int n = min((tile0 + u) * 16 + r16, N - 1);
+      const int sg = seg_of(W, n, &lr);
+      rows[u] = srow<TA, WK>(pick(W.data, sg), pick(W.scales, sg), lr, K);
+    }
+    const bool tok_ok = r16 < M;
+    const int kps = X.k_per_src;
+    const long trow = (long)min(r16, M - 1) * kps;
+    // walk the k-range one activation source at a time
+    for (int s = k0 / kps; s * kps < k1; ++s) {
+      const int ka = max(k0, s * kps), kb = min(k1, (s + 1) * kps);
+      const TA *xr = reinterpret_cast<const TA *>(pick(X.ptr, s)) + trow - (long)s * kps;
+      stream_k<TA, WK, TPW>(xr, rows, tcnt, ka, kb, g, tok_ok, acc);
+    }
+  }
+
+  const int nky = gridDim.y;
+  if constexpr (SPLIT_TILES) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      if (u < tcnt) {
+        if (nky > 1) {
+          reinterpret_cast<f32x4 *>(part)[((long)blockIdx.y * ntile + tile0 + u) * 64 + lane] = acc[u];
+        } else if (r16 < M) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = (tile0 + u) * 16 + 4 * g + i;
+            if (n < N) store_out<TA>(o, r16, n, acc[u][i]);
+          }
+        }
+      }
+    }
+    return;
+  } else {
+    // sum the waves' accumulators: thread (u, l) owns lane l of tile u
+    __shared__ f32x4 red[WPG][TPW][64];
+    __shared__ unsigned last;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) red[wave][u][lane] = acc[u];
+    __syncthreads();
+    const int u = tid >> 6;   // tile of this thread (threads beyond TPW * 64 idle)
+    const bool mine = u < tcnt;
+    f32x4 v = zero4();
+    if (mine) {
+      f32x4 t[WPG];
+#pragma unroll
+      for (int w = 0; w < WPG; ++w) t[w] = red[w][u][lane];
+#pragma unroll
+      for (int h = WPG / 2; h >= 1; h /= 2)
+#pragma unroll
+        for (int w = 0; w < h; ++w)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t[w][i] += t[w + h][i];
+      v = t[0];
+    }
+    if (nky > 1) {
+      const long tstride = (long)ntile * 256;
+      float *pp = part + (long)(tile0 + u) * 256 + lane * 4;
+      if (mine) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(pp + blockIdx.y * tstride + i, v[i], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (!cnt) return;
+      // this workgroup's partials are complete device-wide before it counts
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0)
+        last = __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(nky - 1);
+      __syncthreads();
+      if (!last) return;
+      if (tid == 0) __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!mine) return;
+      v = zero4();
+      int ky = 0;
+      for (; ky + 4 <= nky; ky += 4) {
+        float t[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            t[j][i] = __hip_atomic_load(pp + (ky + j) * tstride + i, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] += t[j][i];
+      }
+      for (; ky < nky; ++ky)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] += __hip_atomic_load(pp + ky * tstride + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (mine && r16 < M) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = (tile0 + u) * 16 + 4 * g + i;
-        if (n < N) part[((long)blockIdx.y * N + n) * 16 + r16] = acc[u][i];
+        if (n < N) store_out<TA>(o, r16, n, v[i]);
       }
     }
   }
 }
 
-// Y[t][n] = sum over k-ranges of the partials, in range order (bitwise
-// reproducible); 8 ranges' loads are issued together to hide their latency.
+// Outputs from the partials part[y][tile][lane] (float4) summed in k-group
+// order, as the last workgroup of skinny_gemm_kernel does; 8 k-groups' loads
+// are issued together to hide their latency.  One thread per (tile, lane).
 template <typename TA>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part,
-                                                            int ksplit, int N, int M, OutSpec o) {
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int nky,
+                                                            int N, int M, OutSpec o) {
+  const int ntile = (N + 15) >> 4;
   const long id = (long)blockIdx.x * 256 + threadIdx.x;
-  const long n = id >> 2;
-  const int tg = (int)(id & 3);
-  if (n >= N) return;
-  const float *p = part + n * 16 + 4 * tg;
-  const long stride = (long)N * 16;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  int ks = 0;
-  for (; ks + 8 <= ksplit; ks += 8) {
-    float4 v[8];
+  if (id >= (long)ntile * 64) return;
+  const int tile = (int)(id >> 6), lane = (int)(id & 63);
+  const int g = lane >> 4, r16 = lane & 15;
+  const long tstride = (long)ntile * 64;
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(part) + id;
+  f32x4 v = zero4();
+  int ky = 0;
+  for (; ky + 8 <= nky; ky += 8) {
+    f32x4 t[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const float4 *>(p + (ks + j) * stride);
+    for (int j = 0; j < 8; ++j) t[j] = src[(long)(ky + j) * tstride];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
-    }
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += t[j][i];
   }
-  for (; ks < ksplit; ++ks) {
-    const float4 v = *reinterpret_cast<const float4 *>(p + ks * stride);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-  }
-  const float vals[4] = {s.x, s.y, s.z, s.w};
+  for (; ky < nky; ++ky) {
+    const f32x4 t = src[(long)ky * tstride];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = 4 * tg + j;
-    if (t < M) store_out<TA>(o, t, n, vals[j]);
+    for (int i = 0; i < 4; ++i) v[i] += t[i];
+  }
+  if (r16 >= M) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = tile * 16 + 4 * g + i;
+    if (n < N) store_out<TA>(o, r16, n, v[i]);
   }
 }
 
 struct SkinnyPlan {
-  int tpw, kchunk, ksplit, groups;
+  int tpw, wpg, kchunk, kgroups, groups;
+  bool split_tiles;
 };
 
-// about DFL_SKINNY_WAVES waves: TPW tiles per wave, the k-range split to match
+// About DFL_SKINNY_WAVES waves.  Weights of at least DFL_SKINNY_BIG_TILES
+// tiles: SPLIT_TILES, 4 waves per workgroup, TPW tiles per wave (4 for long
+// k-ranges such as the injection fc, 2 otherwise; fp32 activations at most
+// 2, as 4 would not fit the registers), k-ranges of kchunk.  Smaller weights:
+// DFL_SKINNY_WPG waves per workgroup on one tile each, the k-range cut into
+// wpg * kgroups ranges.  k-ranges are multiples of 64, at least 128 wide.
 #ifndef DFL_SKINNY_WAVES
 #define DFL_SKINNY_WAVES 2048
 #endif
-// tiles per wave: 4 for long k-ranges (the injection fc), 2 otherwise
+#ifndef DFL_SKINNY_BIG_TILES
+#define DFL_SKINNY_BIG_TILES 256
+#endif
+#ifndef DFL_SKINNY_WPG
+#define DFL_SKINNY_WPG 8
+#endif
 #ifndef DFL_SKINNY_TPW_LONGK
 #define DFL_SKINNY_TPW_LONGK 4
 #endif
 #ifndef DFL_SKINNY_TPW
 #define DFL_SKINNY_TPW 2
 #endif
-static SkinnyPlan skinny_plan(int N, int K) {
+// 0: always sum the partials with splitk_reduce_kernel
+#ifndef DFL_SKINNY_COUNTERS
+#define DFL_SKINNY_COUNTERS 1
+#endif
+static SkinnyPlan skinny_plan(int N, int K, bool f32) {
   SkinnyPlan p;
   const int ntile = (N + 15) / 16;
-  p.tpw = ntile >= 256 ? (K >= 16384 ? DFL_SKINNY_TPW_LONGK : DFL_SKINNY_TPW) : 1;
-  const int wave_groups = (ntile + p.tpw - 1) / p.tpw;
-  p.groups = (wave_groups + 3) / 4;
-  int ks = (DFL_SKINNY_WAVES + wave_groups - 1) / wave_groups;
-  if (ks < 1) ks = 1;
-  int kc = (K + ks - 1) / ks;
-  kc = ((kc + 63) / 64) * 64;
-  if (kc < 128) kc = 128;
-  if (kc > K) kc = K;
-  p.kchunk = kc;
-  p.ksplit = (K + kc - 1) / kc;
+  p.split_tiles = ntile >= DFL_SKINNY_BIG_TILES;
+  if (p.split_tiles) {
+    p.tpw = K >= 16384 ? DFL_SKINNY_TPW_LONGK : DFL_SKINNY_TPW;
+    if (f32 && p.tpw > 2) p.tpw = 2;
+    p.wpg = 4;
+    const int wave_groups = (ntile + p.tpw - 1) / p.tpw;
+    p.groups = (wave_groups + p.wpg - 1) / p.wpg;
+    int ks = (DFL_SKINNY_WAVES + wave_groups - 1) / wave_groups;
+    if (ks < 1) ks = 1;
+    int kc = (K + ks - 1) / ks;
+    kc = ((kc + 63) / 64) * 64;
+    if (kc < 128) kc = 128;
+    p.kchunk = kc;
+    p.kgroups = (K + kc - 1) / kc;
+  } else {
+    p.tpw = 1;
+    p.wpg = DFL_SKINNY_WPG;
+    p.groups = ntile;
+    int kw = (DFL_SKINNY_WAVES + p.groups - 1) / p.groups;   // waves per tile
+    const int kw_max = (K + 127) / 128;
+    if (kw > kw_max) kw = kw_max;
+    if (kw < p.wpg) kw = p.wpg;
+    int kc = (K + kw - 1) / kw;
+    kc = ((kc + 63) / 64) * 64;
+    if (kc < 128) kc = 128;
+    p.kchunk = kc;
+    p.kgroups = (K + p.wpg * kc - 1) / (p.wpg * kc);
+  }
   return p;
 }
 
 size_t skinny_partial_floats(int n_total, int K) {
-  const SkinnyPlan p = skinny_plan(n_total, K);
-  return (size_t)p.ksplit * (size_t)n_total * 16;
+  size_t most = 0;
+  for (const bool f32 : {false, true}) {
+    const SkinnyPlan p = skinny_plan(n_total, K, f32);
+    if (p.kgroups > 1) most = std::max(most, (size_t)p.kgroups * (size_t)((n_total + 15) / 16) * 256);
+  }
+  return most;
 }
 
 template <typename TA, int WK>
-static hipError_t skinny_launch_t(const ASrc &X, int M, const WSet &W, float *part,
+static hipError_t skinny_launch_t(const ASrc &X, int M, const WSet &W, float *part, unsigned *cnt,
                                   const OutSpec &out, hipStream_t st) {
-  const SkinnyPlan p = skinny_plan(W.n_total, W.K);
-  dim3 grid(p.groups, p.ksplit);
-  if (p.tpw == 4)
-    hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 4>), grid, dim3(256), 0, st, X, M, W, p.kchunk,
-                       part);
-  else if (p.tpw == 2)
-    hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 2>), grid, dim3(256), 0, st, X, M, W, p.kchunk,
-                       part);
-  else
-    hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 1>), grid, dim3(256), 0, st, X, M, W, p.kchunk,
-                       part);
+  const SkinnyPlan p = skinny_plan(W.n_total, W.K, sizeof(TA) == 4);
+  const dim3 grid(p.groups, p.kgroups);
+  unsigned *c = nullptr;
+  if (p.split_tiles) {
+    if (sizeof(TA) == 2 && p.tpw == 4)
+      hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, sizeof(TA) == 2 ? 4 : 2, 4, true>), grid,
+                         dim3(256), 0, st, X, M, W, p.kchunk, part, c, out);
+    else if (p.tpw == 2)
+      hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 2, 4, true>), grid, dim3(256), 0, st, X, M, W,
+                         p.kchunk, part, c, out);
+    else
+      hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 1, 4, true>), grid, dim3(256), 0, st, X, M, W,
+                         p.kchunk, part, c, out);
+  } else {
+    c = DFL_SKINNY_COUNTERS && p.groups <= kMaxCounters ? cnt : nullptr;
+    if (p.wpg == 4)
+      hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 1, 4, false>), grid, dim3(256), 0, st, X, M, W,
+                         p.kchunk, part, c, out);
+    else
+      hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 1, 8, false>), grid, dim3(512), 0, st, X, M, W,
+                         p.kchunk, part, c, out);
+  }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long threads = (long)W.n_total * 4;
+  if (e != hipSuccess || c || p.kgroups == 1) return e;
+  const long threads = (long)((W.n_total + 15) / 16) * 64;
   hipLaunchKernelGGL((splitk_reduce_kernel<TA>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                     0, st, part, p.ksplit, W.n_total, M, out);
+                     0, st, part, p.kgroups, W.n_total, M, out);
   return hipGetLastError();
 }
 
 hipError_t launch_skinny_gemm(int act, int wkind, const ASrc &X, int M, const WSet &W, float *part,
-                              const OutSpec &out, hipStream_t st) {
-  if (act == ACT_F32) return skinny_launch_t<float, W_SAME>(X, M, W, part, out, st);
-  if (wkind == W_Q8_0) return skinny_launch_t<bf16, W_Q8_0>(X, M, W, part, out, st);
-  return skinny_launch_t<bf16, W_SAME>(X, M, W, part, out, st);
+                              unsigned *cnt, const OutSpec &out, hipStream_t st) {
+  if (act == ACT_F32) return skinny_launch_t<float, W_SAME>(X, M, W, part, cnt, out, st);
+  if (wkind == W_Q8_0) return skinny_launch_t<bf16, W_Q8_0>(X, M, W, part, cnt, out, st);
+  return skinny_launch_t<bf16, W_SAME>(X, M, W, part, cnt, out, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -61,12 +61,19 @@ struct OutSpec {
 // Rows of the weight-streaming path: M <= 16 activation rows.
 constexpr int kSkinnyMaxM = 16;
 
+// Completion counters at the start of every workspace: zero before a
+// kernel that uses them starts, and zero again when it ends.
+constexpr int kMaxCounters = 16384;
+constexpr size_t kCounterBytes = kMaxCounters * sizeof(unsigned);
+
 // Workspace floats of the split-K partials of a skinny GEMM.
 size_t skinny_partial_floats(int n_total, int K);
-// Y = X . W^T for M <= 16 rows: split-K partials, then a fixed-order reduce
-// into `out`.  `part` holds skinny_partial_floats() floats.
+// Y = X . W^T for M <= 16 rows: split-K partials summed in a fixed order by
+// the last workgroup of each tile group (counters `cnt`, kMaxCounters of
+// them), or by a second kernel when there are more tile groups than
+// counters.  `part` holds skinny_partial_floats() floats.
 hipError_t launch_skinny_gemm(int act, int wkind, const ASrc &X, int M, const WSet &W, float *part,
-                              const OutSpec &out, hipStream_t st);
+                              unsigned *cnt, const OutSpec &out, hipStream_t st);
 // Y = A . W^T for any M (tiled MFMA GEMM, LDS-staged, no split-K).
 hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet &W,
                             const OutSpec &out, hipStream_t st);

@@ -183,7 +183,8 @@ def dflash_selector_edges_workspace(B, r, d, K) -> int:
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    return torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
+    """A zero-filled workspace (its leading completion counters must start at zero)."""
+    return torch.zeros(max(16, nbytes), dtype=torch.uint8, device=device)
 
 
 # ---- the six calls -------------------------------------------------------------

@@ -50,6 +50,12 @@
  * - Workspace.  A call that needs scratch device memory takes (ws, ws_bytes);
  *   the matching *_workspace() function returns the bytes it needs for the
  *   given shapes (0 for none).  A smaller workspace -> DFLASH_ERR_WORKSPACE.
+ *   The first 64 KiB of a workspace hold completion counters that the
+ *   kernels expect at zero: fill a new workspace with zeros once before its
+ *   first use (hipMemset).  Every call returns the counters to zero by the
+ *   time its work completes, so a workspace can be reused by later calls
+ *   (of any entry point) without clearing it again, as long as nothing else
+ *   writes to it in between.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
