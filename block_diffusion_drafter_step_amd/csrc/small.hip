@@ -134,7 +134,8 @@ hipError_t launch_conv(int act, const void *x, int n_blocks, int B, int C, int G
 // selector_edges_kernel: one workgroup per position i stages its K candidate
 // rows of B and its predecessor rows of A (scaled by proj[i]) in LDS and forms
 // the K x K rank-r dot products.  selector_path_kernel: one workgroup runs
-// the K-state max-sum recursion over the positions and the backtrack.
+// the K-state max-sum recursion over the positions and the backtrack.  When
+// all candidate rows fit in LDS, selector_fused_kernel does both at once.
 // ---------------------------------------------------------------------------
 constexpr int kSelMaxB = 16, kSelMaxK = 32, kSelMaxR = 256;
 
@@ -229,7 +230,182 @@ __global__ __launch_bounds__(256) void selector_path_kernel(SelArgs a) {
   }
 }
 
+// The whole selector in one workgroup (used when the candidate rows fit in
+// LDS): gather every position's predecessor rows of A and candidate rows of B
+// with 16-byte loads issued together, form all B x K x K edges (the same
+// arithmetic, in the same order, as selector_edges_kernel; one edge per
+// thread, 16-element chunks of each dot product read from LDS at once), write
+// them, and run the max-sum recursion in one wave: lane b holds state b, its
+// back-pointers and candidate ids in registers, and each step reads its
+// K x K edges from LDS in one batch.
+template <typename TA, int KM>
+__global__ __launch_bounds__(1024) void selector_fused_kernel(SelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int EPV = 16 / sizeof(TA);   // elements per 16-byte vector
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = a.B, K = a.K, r = a.r, BK = a.B * a.K;
+  const int rs = r + EPV;                // padded LDS row stride (elements)
+  TA *rows = reinterpret_cast<TA *>(smem);            // [2][B*K][rs]: A side, B side
+  float *pj = reinterpret_cast<float *>(rows + 2 * BK * rs);   // [B][r]
+  float *se = pj + B * r;                                      // [B][K][K]
+  float *un = se + BK * K;                                     // [B][K]
+  int *sidx = reinterpret_cast<int *>(un + BK);                // [B][K]
+  for (int e = tid; e < BK; e += 1024) {
+    sidx[e] = clamp_idx(a.idx[e], a.V);
+    un[e] = a.unary[e];
+  }
+  for (int e = tid; e < B * r; e += 1024) pj[e] = a.proj[e];
+  __syncthreads();
+
+  const TA *A = reinterpret_cast<const TA *>(a.cb_pred);
+  const TA *Bc = reinterpret_cast<const TA *>(a.cb_succ);
+  const int anchor = a.anchor < 0 ? 0 : a.anchor;   // row unused without an anchor
+  const int vpr = r / EPV, nvec = 2 * BK * vpr;
+  constexpr int UNR = 4;
+  for (int v0 = tid; v0 < nvec; v0 += 1024 * UNR) {
+    uint4 buf[UNR];
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {   // past the end: reload the last vector
+      const int v = min(v0 + 1024 * j, nvec - 1);
+      const int row = v / vpr, part = v - row * vpr;
+      const TA *src;
+      if (row < BK) {   // predecessor a of position i: A[idx[i-1][a]] (A[anchor] at i = 0)
+        const int i = row / K, ai = row - i * K;
+        src = A + (long)(i == 0 ? anchor : sidx[(i - 1) * K + ai]) * r;
+      } else {          // candidate b of position i: B[idx[i][b]]
+        src = Bc + (long)sidx[row - BK] * r;
+      }
+      buf[j] = *reinterpret_cast<const uint4 *>(src + part * EPV);
+    }
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int v = v0 + 1024 * j;
+      if (v < nvec) {
+        const int row = v / vpr, part = v - row * vpr;
+        *reinterpret_cast<uint4 *>(rows + row * rs + part * EPV) = buf[j];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int e = tid; e < BK * K; e += 1024) {
+    const int i = e / (K * K), rem = e - i * K * K, ai = rem / K, bi = rem - ai * K;
+    const int npred = i == 0 ? (a.anchor < 0 ? 0 : 1) : K;
+    float v;
+    if (i == 0 && ai > 0) {
+      v = -__builtin_inff();
+    } else if (npred == 0) {
+      v = un[i * K + bi];
+    } else {
+      const TA *x = rows + (i * K + ai) * rs;
+      const TA *y = rows + (BK + i * K + bi) * rs;
+      const float *p = pj + i * r;
+      float acc = 0.f;
+      for (int k0 = 0; k0 < r; k0 += 16) {   // r is a multiple of 16
+        float xv[16], yv[16], pv[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          xv[k] = to_f32(x[k0 + k]);
+          yv[k] = to_f32(y[k0 + k]);
+          pv[k] = p[k0 + k];
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float ap = xv[k] * pv[k];
+          acc += ap * yv[k];
+        }
+      }
+      v = acc + un[i * K + bi];
+    }
+    se[e] = v;
+    a.edges[e] = v;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  // s_0[b] = edge[0][0][b]; s_i[b] = max_a s_{i-1}[a] + edge[i][a][b], the
+  // first (lowest a) maximum wins
+  const int bl = min(lane, K - 1);   // lanes >= K shadow state K-1 (never chosen)
+  float sc = se[bl];
+  int backr[kSelMaxB], sidr[kSelMaxB];
+  sidr[0] = sidx[bl];
+#pragma unroll
+  for (int i = 1; i < kSelMaxB; ++i) {
+    if (i < B) {
+      const float *ei = se + i * K * K;
+      float ecol[KM];
+#pragma unroll
+      for (int q = 0; q < KM; ++q) ecol[q] = ei[min(q, K - 1) * K + bl];
+      sidr[i] = sidx[i * K + bl];
+      float best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), 0)) + ecol[0];
+      int arg = 0;
+#pragma unroll
+      for (int q = 1; q < KM; ++q) {
+        if (q < K) {
+          const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), q)) + ecol[q];
+          if (v > best) {
+            best = v;
+            arg = q;
+          }
+        }
+      }
+      sc = best;
+      backr[i] = arg;
+    }
+  }
+  // best final state, the lowest b on ties
+  float bv = lane < K ? sc : -__builtin_inff();
+  int bb = lane < K ? lane : K;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float ov = shfl_xor(bv, o);
+    const int ob = __shfl_xor(bb, o, kWave);
+    if (ov > bv || (ov == bv && ob < bb)) {
+      bv = ov;
+      bb = ob;
+    }
+  }
+  int b = __builtin_amdgcn_readfirstlane(bb);
+#pragma unroll
+  for (int i = kSelMaxB - 1; i >= 0; --i) {
+    if (i < B) {
+      const int id = __builtin_amdgcn_readlane(sidr[i], b);
+      if (lane == 0) a.path[i] = id;
+      if (i > 0) b = __builtin_amdgcn_readlane(backr[i], b);
+    }
+  }
+}
+
+static size_t selector_fused_lds(int act, const SelArgs &a) {
+  const size_t es = act == ACT_F32 ? 4 : 2;
+  const size_t bk = (size_t)a.B * a.K;
+  return 2 * bk * (a.r + 16 / es) * es + ((size_t)a.B * a.r + bk * a.K + bk) * 4 + bk * 4;
+}
+
+template <typename TA, int KM>
+static void selector_fused_go(const SelArgs &a, size_t lds, hipStream_t st) {
+  auto *k = &selector_fused_kernel<TA, KM>;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(k, dim3(1), dim3(1024), lds, st, a);
+}
+
+#ifndef DFL_SEL_FUSED
+#define DFL_SEL_FUSED 1
+#endif
+
 hipError_t launch_selector(int act, const SelArgs &a, hipStream_t st) {
+  const size_t flds = selector_fused_lds(act, a);
+  if (DFL_SEL_FUSED && flds <= kMaxLdsBytes) {
+    if (act == ACT_F32) {
+      if (a.K <= 8) selector_fused_go<float, 8>(a, flds, st);
+      else selector_fused_go<float, 32>(a, flds, st);
+    } else {
+      if (a.K <= 8) selector_fused_go<bf16, 8>(a, flds, st);
+      else selector_fused_go<bf16, 32>(a, flds, st);
+    }
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)2 * a.K * (a.r + 1) * sizeof(float);
   if (act == ACT_F32)
     hipLaunchKernelGGL((selector_edges_kernel<float>), dim3(a.B), dim3(256), lds, st, a);

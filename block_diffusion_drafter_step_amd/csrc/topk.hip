@@ -353,77 +353,78 @@ size_t topk_lds_bytes(int B, int d, int act, int K) {
 }
 
 // one workgroup per token: merge n_wg partial lists and (max, sum) pairs
+// (value, index) as one 64-bit key whose unsigned order is the candidate
+// order: value descending, then index ascending.  High word: the float's bits
+// made monotonic; low word: the complemented index.  0 = no candidate.
+__device__ __forceinline__ unsigned long long cand_key(float v, int i) {
+  const unsigned u = __float_as_uint(v);
+  const unsigned o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | (unsigned)(~(unsigned)i);
+}
+__device__ __forceinline__ float key_value(unsigned long long k) {
+  const unsigned o = (unsigned)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_index(unsigned long long k) { return (int)~(unsigned)k; }
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x, int o) {
+  const int lo = __shfl_xor((int)(unsigned)x, o, kWave);
+  const int hi = __shfl_xor((int)(unsigned)(x >> 32), o, kWave);
+  return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+}
+
+// Final merge, one workgroup per token: thread t holds partial list t (and,
+// with more than 256 workgroup partials, merges lists t + 256 j into it), the
+// log-sum-exp is a fixed-order tree over the threads, and the K winners are
+// picked one at a time by a block-wide max over the list heads.  Every
+// vocabulary row sits in exactly one partial, so the winning key names the
+// one list whose head advances.
 template <int KM>
 __global__ __launch_bounds__(256) void topk_merge_kernel(TopkArgs a) {
   const int tok = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K;
-  float tv[KM];
-  int ti[KM];
+  unsigned long long key[KM];
 #pragma unroll
-  for (int j = 0; j < KM; ++j) {
-    tv[j] = -__builtin_inff();
-    ti[j] = 0x7fffffff;
-  }
+  for (int j = 0; j < KM; ++j) key[j] = 0;
   float m = -__builtin_inff(), s = 0.f;
-  // every partial this thread merges is loaded before any is used (one
-  // memory round trip: the partials come from other XCDs' workgroups)
-  constexpr int PPT = 4;   // partial lists per thread per round
-  for (int w0 = tid; w0 < a.n_wg; w0 += 256 * PPT) {
-    float pm[PPT], ps[PPT], pv[PPT][KM];
-    int pi[PPT][KM];
+  if (tid < a.n_wg) {
+    // entries j >= K re-read entry K-1 (in bounds) and are dropped
+    const long ob = (long)tid * 16 + tok;
+    float pv[KM];
+    int pi[KM];
 #pragma unroll
-    for (int q = 0; q < PPT; ++q) {
-      const int w = w0 + 256 * q;
-      const bool ok = w < a.n_wg;
-      const long ob = (long)(ok ? w : 0) * 16 + tok;
-      pm[q] = ok ? a.part_ms[ob * 2] : -__builtin_inff();
-      ps[q] = ok ? a.part_ms[ob * 2 + 1] : 0.f;
-#pragma unroll
-      for (int k = 0; k < KM; ++k) {
-        pv[q][k] = (ok && k < K) ? a.part_val[ob * K + k] : -__builtin_inff();
-        pi[q][k] = (ok && k < K) ? a.part_idx[ob * K + k] : 0x7fffffff;
-      }
+    for (int j = 0; j < KM; ++j) {
+      const long e = ob * K + min(j, K - 1);
+      pv[j] = a.part_val[e];
+      pi[j] = a.part_idx[e];
     }
+    m = a.part_ms[ob * 2];
+    s = a.part_ms[ob * 2 + 1];
 #pragma unroll
-    for (int q = 0; q < PPT; ++q) {
-      if (ps[q] > 0.f) {
-        if (pm[q] > m) {
-          s = s * exp2f((m - pm[q]) * kL2e);
-          m = pm[q];
-        }
-        s += ps[q] * exp2f((pm[q] - m) * kL2e);
+    for (int j = 0; j < KM; ++j) key[j] = j < K ? cand_key(pv[j], pi[j]) : 0ull;
+  }
+  for (int w = tid + 256; w < a.n_wg; w += 256) {
+    const long ob = (long)w * 16 + tok;
+    const float pm = a.part_ms[ob * 2], ps = a.part_ms[ob * 2 + 1];
+    if (ps > 0.f) {
+      if (pm > m) {
+        s = s * exp2f((m - pm) * kL2e);
+        m = pm;
       }
+      s += ps * exp2f((pm - m) * kL2e);
+    }
+    for (int j = 0; j < K; ++j) {
+      unsigned long long x = cand_key(a.part_val[ob * K + j], a.part_idx[ob * K + j]);
+      if (x <= key[KM - 1]) break;   // the partial list is sorted: no later entry fits
 #pragma unroll
-      for (int k = 0; k < KM; ++k) {
-        const float v = pv[q][k];
-        const int ix = pi[q][k];
-        // general insertion by (value desc, index asc)
-        if (better(v, ix, tv[KM - 1], ti[KM - 1])) {
-          tv[KM - 1] = v;
-          ti[KM - 1] = ix;
-#pragma unroll
-          for (int j = KM - 1; j > 0; --j) {
-            const bool sw = better(tv[j], ti[j], tv[j - 1], ti[j - 1]);
-            const float xv = tv[j - 1];
-            const int xi = ti[j - 1];
-            tv[j - 1] = sw ? tv[j] : xv;
-            ti[j - 1] = sw ? ti[j] : xi;
-            tv[j] = sw ? xv : tv[j];
-            ti[j] = sw ? xi : ti[j];
-          }
-        }
+      for (int q = 0; q < KM; ++q) {   // insert, keeping key[] descending
+        const unsigned long long hi = key[q] > x ? key[q] : x;
+        x = key[q] > x ? x : key[q];
+        key[q] = hi;
       }
     }
   }
-  __shared__ float lv[256 * KM];
-  __shared__ int li[256 * KM];
-  __shared__ float wm[4], wsum[4], wv[4];
-  __shared__ int wi[4], wq[4];
-#pragma unroll
-  for (int j = 0; j < KM; ++j) {
-    lv[tid * KM + j] = tv[j];
-    li[tid * KM + j] = ti[j];
-  }
+  __shared__ float wm[4], wsum[4];
+  __shared__ unsigned long long wbest[2][4];
   // log-sum-exp: fixed-order tree over the 256 threads
   float M = m;
 #pragma unroll
@@ -438,43 +439,28 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkArgs a) {
   __syncthreads();
   S = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
   const float lse = M + log2f(S) * kLn2;
-  int head = 0;
   for (int k = 0; k < K; ++k) {
-    float bv = head < KM ? lv[tid * KM + head] : -__builtin_inff();
-    int bi = head < KM ? li[tid * KM + head] : 0x7fffffff;
-    int bq = tid;
+    unsigned long long b = key[0];
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const float ov = shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o, kWave);
-      const int oq = __shfl_xor(bq, o, kWave);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-        bq = oq;
-      }
+      const unsigned long long x = shfl_xor_u64(b, o);
+      b = x > b ? x : b;
     }
-    if (lane == 0) {
-      wv[wave] = bv;
-      wi[wave] = bi;
-      wq[wave] = bq;
-    }
+    // two slots: a wave that runs ahead writes the other one
+    if (lane == 0) wbest[k & 1][wave] = b;
     __syncthreads();
-    float fv = wv[0];
-    int fi = wi[0], fq = wq[0];
+    unsigned long long w = wbest[k & 1][0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w)
-      if (better(wv[w], wi[w], fv, fi)) {
-        fv = wv[w];
-        fi = wi[w];
-        fq = wq[w];
-      }
-    if (fq == tid) ++head;
-    if (tid == 0) {
-      a.idx[(long)tok * K + k] = fi;
-      a.unary[(long)tok * K + k] = fv - lse;
+    for (int q = 1; q < 4; ++q) w = wbest[k & 1][q] > w ? wbest[k & 1][q] : w;
+    if (key[0] == w) {
+#pragma unroll
+      for (int j = 0; j < KM - 1; ++j) key[j] = key[j + 1];
+      key[KM - 1] = 0;
     }
-    __syncthreads();
+    if (tid == 0) {
+      a.idx[(long)tok * K + k] = key_index(w);
+      a.unary[(long)tok * K + k] = key_value(w) - lse;
+    }
   }
 }
 

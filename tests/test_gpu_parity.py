@@ -304,6 +304,9 @@ def test_selector_no_anchor_and_wide_k():
     run_selector(configs.get(0), anchor=-1)
     run_selector(cfg_small(1, K=32, B=16, r=256), tag="selK32")
     run_selector(cfg_small(1, K=1, B=1), tag="selK1")
+    # one-workgroup path with more than 64 KB of LDS (K=32, r=256 above does
+    # not fit in LDS and takes the two-kernel path)
+    run_selector(cfg_small(1, K=16, B=16, r=64), tag="selK16")
 
 
 def test_accept_len():
