@@ -46,31 +46,196 @@ struct AttnCfg {
 };
 
 // pointer to row `j` of the keys (or values) seen by KV head `kvh`
+// (a select, not a branch: loads stay unconditional)
 template <typename TA, int HD>
 __device__ __forceinline__ const TA *key_row(const AttnArgs &a, const TA *cache, int kvh, long j,
                                              int col_off) {
-  if (j < a.n_ctx) return cache + ((long)kvh * a.cap + j) * HD;
-  const long t = j - a.n_ctx;
+  const bool ctx = j < a.n_ctx;
+  const long t = ctx ? 0 : j - a.n_ctx;
   const long qld = (long)(a.Hq + 2 * a.Hkv) * HD;
-  return reinterpret_cast<const TA *>(a.qkv) + t * qld + col_off + (long)kvh * HD;
+  const TA *c = cache + ((long)kvh * a.cap + (ctx ? j : 0)) * HD;
+  const TA *b = reinterpret_cast<const TA *>(a.qkv) + t * qld + col_off + (long)kvh * HD;
+  return ctx ? c : b;
 }
 
-template <typename TA, int HD, int HPW>
-__global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
+// Staged tile: K copied as-is, V gathered 4 keys x 8 dims per thread and
+// written transposed.  Two LDS stages and two register sets: while the waves
+// compute on one stage, the next tile waits in registers and the one after is
+// in flight, so two tiles' loads overlap every compute phase.  Loads are
+// unconditional (keys past the chunk are clamped to its last key; their
+// scores are masked to -inf), which keeps the compiler's waits graded.
+template <typename TA, int HD>
+struct TileRegs {
   using C = AttnCfg<TA, HD>;
-  __shared__ __attribute__((aligned(16))) TA Ks[kAttnKT * C::KLD];
-  __shared__ __attribute__((aligned(16))) TA Vt[HD * C::VLD];
+  static constexpr int KCH = kAttnKT * HD / C::VEC;         // 16-byte K chunks per tile
+  static constexpr int VITEMS = (kAttnKT / 4) * (HD / 8);    // (4 keys x 8 dims) V items
+  static constexpr int KPT = (KCH + 255) / 256, VPT = (VITEMS + 255) / 256;
+};
+
+// the keys of one KV head that one split workgroup owns: [key0, key1)
+struct KeyRange {
+  const AttnArgs *a;
+  int kvh, kcol, vcol, ntile;
+  long key0, key1;
+};
+
+// tile tI (clamped to the last one) of the range into registers
+template <typename TA, int HD>
+__device__ __forceinline__ void attn_load_tile(const KeyRange &kr, int tid, int tI,
+                                               u32x4 (&rk)[TileRegs<TA, HD>::KPT],
+                                               Frag<TA> (&rv)[TileRegs<TA, HD>::VPT][4]) {
+  using C = AttnCfg<TA, HD>;
+  using R = TileRegs<TA, HD>;
+  const AttnArgs &a = *kr.a;
+  const TA *ck = reinterpret_cast<const TA *>(a.ck);
+  const TA *cv = reinterpret_cast<const TA *>(a.cv);
+  const long t0 = kr.key0 + (long)min(tI, kr.ntile - 1) * kAttnKT;
+#pragma unroll
+  for (int j = 0; j < R::KPT; ++j) {
+    const int c = min(tid + 256 * j, R::KCH - 1);
+    const int row = c / (HD / C::VEC), ch = c % (HD / C::VEC);
+    const long key = min(t0 + row, kr.key1 - 1);
+    rk[j] = *reinterpret_cast<const u32x4 *>(key_row<TA, HD>(a, ck, kr.kvh, key, kr.kcol) + ch * C::VEC);
+  }
+#pragma unroll
+  for (int j = 0; j < R::VPT; ++j) {
+    const int it = min(tid + 256 * j, R::VITEMS - 1);
+    const int kq = it / (HD / 8), d8 = it % (HD / 8);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long key = min(t0 + 4 * kq + u, kr.key1 - 1);
+      rv[j][u] = load_frag(key_row<TA, HD>(a, cv, kr.kvh, key, kr.vcol) + d8 * 8);
+    }
+  }
+}
+
+// registers -> one LDS stage (K as-is, V transposed)
+template <typename TA, int HD>
+__device__ __forceinline__ void attn_store_tile(TA *ks, TA *vt, int tid,
+                                                const u32x4 (&rk)[TileRegs<TA, HD>::KPT],
+                                                const Frag<TA> (&rv)[TileRegs<TA, HD>::VPT][4]) {
+  using C = AttnCfg<TA, HD>;
+  using R = TileRegs<TA, HD>;
+#pragma unroll
+  for (int j = 0; j < R::KPT; ++j) {
+    const int c = tid + 256 * j;
+    if (c < R::KCH) {
+      const int row = c / (HD / C::VEC), ch = c % (HD / C::VEC);
+      *reinterpret_cast<u32x4 *>(ks + row * C::KLD + ch * C::VEC) = rk[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < R::VPT; ++j) {
+    const int it = tid + 256 * j;
+    if (it < R::VITEMS) {
+      const int kq = it / (HD / 8), d8 = it % (HD / 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        Quad<TA> q4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) q4.v[u] = rv[j][u].v[e];
+        *reinterpret_cast<Quad<TA> *>(vt + (d8 * 8 + e) * C::VLD + 4 * kq) = q4;
+      }
+    }
+  }
+}
+
+// one tile from an LDS stage into this wave's running softmax and output
+template <typename TA, int HD, int HPW>
+__device__ __forceinline__ void attn_compute_tile(const TA *ks, const TA *vt, long t0, long key1,
+                                                  float sl2, int g, int r16,
+                                                  const Frag<TA> (&qf)[HPW][AttnCfg<TA, HD>::NQF],
+                                                  f32x4 (&o)[HPW][AttnCfg<TA, HD>::NDT],
+                                                  float (&m_run)[HPW], float (&l_run)[HPW],
+                                                  const bool (&active)[HPW]) {
+  using C = AttnCfg<TA, HD>;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    if (!active[hh]) continue;
+#pragma unroll
+    for (int sb = 0; sb < kAttnKT / 32; ++sb) {
+      // S^T for 32 keys: two 16-key tiles, lane holds keys 4g+i (+16), token r16
+      f32x4 s[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        s[st] = zero4();
+        const TA *kp = ks + (32 * sb + 16 * st + r16) * C::KLD + 8 * g;
+#pragma unroll
+        for (int f = 0; f < C::NQF; ++f) mma(s[st], load_frag(kp + 32 * f), qf[hh][f]);
+      }
+      float p[8];
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const long key = t0 + 32 * sb + 16 * st + 4 * g + i;
+          const float v = key < key1 ? s[st][i] * sl2 : -__builtin_inff();
+          p[st * 4 + i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[hh], mx);
+      const float alpha = m_new == -__builtin_inff() ? 1.f : exp2f(m_run[hh] - m_new);
+      // the row sum uses the probabilities exactly as the P.V product sees them
+      float ls = 0.f;
+      Frag<TA> pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pf.v[e] = from_f32<TA>(p[e] == -__builtin_inff() ? 0.f : exp2f(p[e] - m_new));
+        ls += to_f32(pf.v[e]);
+      }
+      ls += shfl_xor(ls, 16);
+      ls += shfl_xor(ls, 32);
+      l_run[hh] = l_run[hh] * alpha + ls;
+      m_run[hh] = m_new;
+      // O^T[dim][tok] += V^T[dim][keys] P^T[keys][tok]; lane slots: keys 4g..4g+3, 16+4g..
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        o[hh][dt] *= alpha;
+        const TA *vp = vt + (16 * dt + r16) * C::VLD + 32 * sb + 4 * g;
+        const Quad<TA> v0 = *reinterpret_cast<const Quad<TA> *>(vp);
+        const Quad<TA> v1 = *reinterpret_cast<const Quad<TA> *>(vp + 16);
+        Frag<TA> vf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf.v[e] = v0.v[e];
+          vf.v[4 + e] = v1.v[e];
+        }
+        mma(o[hh][dt], vf, pf);
+      }
+    }
+  }
+}
+
+// Staged tiles: two LDS stages and two register sets.  While the waves
+// compute on one stage, the next tile waits in registers and the one after is
+// in flight, so two tiles' loads overlap every compute phase; one barrier per
+// tile.  Loads are unconditional (keys past the chunk are clamped to its last
+// key and their scores masked to -inf), which keeps the compiler's waits
+// graded instead of draining every load at a branch.
+template <typename TA, int HD, int HPW>
+__global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
+  using C = AttnCfg<TA, HD>;
+  using R = TileRegs<TA, HD>;
+  constexpr int KS = kAttnKT * C::KLD, VS = HD * C::VLD;   // stage sizes (elements)
+  __shared__ __attribute__((aligned(16))) TA Ks[2 * KS];
+  __shared__ __attribute__((aligned(16))) TA Vt[2 * VS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int kvh = blockIdx.y, sp = blockIdx.x;
   const int grp = a.Hq / a.Hkv;
   const long S = a.n_ctx + a.B;
-  const long key0 = (long)sp * a.chunk;
-  const long key1 = min(S, key0 + a.chunk);
-  const TA *ck = reinterpret_cast<const TA *>(a.ck);
-  const TA *cv = reinterpret_cast<const TA *>(a.cv);
-  const int kcol = a.Hq * HD, vcol = (a.Hq + a.Hkv) * HD;
+  KeyRange kr;
+  kr.a = &a;
+  kr.kvh = kvh;
+  kr.kcol = a.Hq * HD;
+  kr.vcol = (a.Hq + a.Hkv) * HD;
+  kr.key0 = (long)sp * a.chunk;
+  kr.key1 = min(S, kr.key0 + a.chunk);
+  kr.ntile = (int)((kr.key1 - kr.key0 + kAttnKT - 1) / kAttnKT);
   const long qld = (long)(a.Hq + 2 * a.Hkv) * HD;
   const float sl2 = a.scale * kLog2e;
 
@@ -95,131 +260,30 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     l_run[hh] = 0.f;
   }
 
-  // tile loader: K chunks copied as-is; V gathered 4 keys x 8 dims per thread
-  // and written transposed
-  constexpr int KCH = kAttnKT * HD / C::VEC;            // 16-byte K chunks per tile
-  constexpr int VITEMS = (kAttnKT / 4) * (HD / 8);       // (4 keys x 8 dims) V items
-  constexpr int KPT = (KCH + 255) / 256, VPT = (VITEMS + 255) / 256;
-  uint4 kreg[KPT];
-  Frag<TA> vreg[VPT][4];
-
-  auto load_tile = [&](long t0) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c / (HD / C::VEC), ch = c % (HD / C::VEC);
-      const long key = t0 + row;
-      kreg[j] = make_uint4(0, 0, 0, 0);
-      if (c < KCH && key < key1)
-        kreg[j] = *reinterpret_cast<const uint4 *>(key_row<TA, HD>(a, ck, kvh, key, kcol) + ch * C::VEC);
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int it = tid + 256 * j;
-      const int kq = it / (HD / 8), d8 = it % (HD / 8);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const long key = t0 + 4 * kq + u;
-        vreg[j][u] = (it < VITEMS && key < key1)
-                         ? load_frag(key_row<TA, HD>(a, cv, kvh, key, vcol) + d8 * 8)
-                         : frag_zero<TA>();
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int c = tid + 256 * j;
-      if (c < KCH) {
-        const int row = c / (HD / C::VEC), ch = c % (HD / C::VEC);
-        *reinterpret_cast<uint4 *>(Ks + row * C::KLD + ch * C::VEC) = kreg[j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int it = tid + 256 * j;
-      if (it < VITEMS) {
-        const int kq = it / (HD / 8), d8 = it % (HD / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          Quad<TA> q4;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) q4.v[u] = vreg[j][u].v[e];
-          *reinterpret_cast<Quad<TA> *>(Vt + (d8 * 8 + e) * C::VLD + 4 * kq) = q4;
-        }
-      }
-    }
-  };
-
-  const int ntile = (int)((key1 - key0 + kAttnKT - 1) / kAttnKT);
-  load_tile(key0);
-  store_tile();
+  // tile n computes from stage n % 2
+  // (a native vector type: HIP's uint4 is a struct whose copies defeat
+  // register promotion of the two register sets)
+  u32x4 k0[R::KPT], k1[R::KPT];
+  Frag<TA> v0[R::VPT][4], v1[R::VPT][4];
+  const int ntile = kr.ntile;
+  attn_load_tile<TA, HD>(kr, tid, 0, k0, v0);
+  attn_store_tile<TA, HD>(Ks, Vt, tid, k0, v0);
+  attn_load_tile<TA, HD>(kr, tid, 1, k1, v1);
+  attn_load_tile<TA, HD>(kr, tid, 2, k0, v0);
   __syncthreads();
-  for (int tI = 0; tI < ntile; ++tI) {
-    const long t0 = key0 + (long)tI * kAttnKT;
-    const long tn = key0 + (long)min(tI + 1, ntile - 1) * kAttnKT;
-    load_tile(tn);
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      if (!active[hh]) continue;
-#pragma unroll
-      for (int sb = 0; sb < kAttnKT / 32; ++sb) {
-        // S^T for 32 keys: two 16-key tiles, lane holds keys 4g+i (+16), token r16
-        f32x4 s[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          s[st] = zero4();
-          const TA *kp = Ks + (32 * sb + 16 * st + r16) * C::KLD + 8 * g;
-#pragma unroll
-          for (int f = 0; f < C::NQF; ++f) mma(s[st], load_frag(kp + 32 * f), qf[hh][f]);
-        }
-        float p[8];
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const long key = t0 + 32 * sb + 16 * st + 4 * g + i;
-            const float v = key < key1 ? s[st][i] * sl2 : -__builtin_inff();
-            p[st * 4 + i] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[hh], mx);
-        const float alpha = m_new == -__builtin_inff() ? 1.f : exp2f(m_run[hh] - m_new);
-        // the row sum uses the probabilities exactly as the P.V product sees them
-        float ls = 0.f;
-        Frag<TA> pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pf.v[e] = from_f32<TA>(p[e] == -__builtin_inff() ? 0.f : exp2f(p[e] - m_new));
-          ls += to_f32(pf.v[e]);
-        }
-        ls += shfl_xor(ls, 16);
-        ls += shfl_xor(ls, 32);
-        l_run[hh] = l_run[hh] * alpha + ls;
-        m_run[hh] = m_new;
-        // O^T[dim][tok] += V^T[dim][keys] P^T[keys][tok]; lane slots: keys 4g..4g+3, 16+4g..
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) {
-          o[hh][dt] *= alpha;
-          const TA *vp = Vt + (16 * dt + r16) * C::VLD + 32 * sb + 4 * g;
-          const Quad<TA> v0 = *reinterpret_cast<const Quad<TA> *>(vp);
-          const Quad<TA> v1 = *reinterpret_cast<const Quad<TA> *>(vp + 16);
-          Frag<TA> vf;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vf.v[e] = v0.v[e];
-            vf.v[4 + e] = v1.v[e];
-          }
-          mma(o[hh][dt], vf, pf);
-        }
-      }
+  for (int tI = 0; tI < ntile; tI += 2) {
+    attn_compute_tile<TA, HD, HPW>(Ks, Vt, kr.key0 + (long)tI * kAttnKT, kr.key1, sl2, g, r16, qf, o,
+                                   m_run, l_run, active);
+    attn_store_tile<TA, HD>(Ks + KS, Vt + VS, tid, k1, v1);   // tile tI + 1
+    attn_load_tile<TA, HD>(kr, tid, tI + 3, k1, v1);
+    __syncthreads();
+    if (tI + 1 < ntile) {
+      attn_compute_tile<TA, HD, HPW>(Ks + KS, Vt + VS, kr.key0 + (long)(tI + 1) * kAttnKT, kr.key1,
+                                     sl2, g, r16, qf, o, m_run, l_run, active);
+      attn_store_tile<TA, HD>(Ks, Vt, tid, k0, v0);           // tile tI + 2
+      attn_load_tile<TA, HD>(kr, tid, tI + 4, k0, v0);
+      __syncthreads();
     }
-    __syncthreads();
-    store_tile();
-    __syncthreads();
   }
 
   // partials: lane holds dims 16*dt + 4g + i of token r16

@@ -463,11 +463,11 @@ dflash_status dflash_topk_unary(const void *h, int32_t B, int32_t act,
   // resident path for bf16 / fp32 heads (measured faster there); Q8_0 heads
   // stream (their dequantisation favours more waves)
   if (DFL_TOPK_RESIDENT && lm_head->dtype != DFLASH_Q8_0 && lds <= kMaxLdsBytes && d % 128 == 0 &&
-      (long)cus * 4 <= (V + 15) / 16) {
+      (long)cus * topk_lds_waves() <= (V + 15) / 16) {
     a.lds_path = 1;
     a.lds_bytes = (int)lds;
     a.n_wg = cus;
-    a.n_waves = cus * 4;
+    a.n_waves = cus * topk_lds_waves();
   } else {
     a.lds_path = 0;
     a.n_wg = topk_plan_wgs(V, wkind_of(lm_head));

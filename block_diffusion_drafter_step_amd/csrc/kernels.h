@@ -125,8 +125,10 @@ struct TopkArgs {
   float *unary;       // [B][K]
 };
 int topk_plan_wgs(long V, int wkind);
-// LDS bytes of the h-resident LM-head kernel (h block or merge arrays)
+// LDS bytes of the h-resident LM-head kernel (h block or merge arrays) and
+// its waves per workgroup
 size_t topk_lds_bytes(int B, int d, int act, int K);
+int topk_lds_waves();
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 constexpr int kMaxCUs = 1024;
 int device_cu_count();

@@ -74,7 +74,6 @@ __device__ __forceinline__ SRow<TA, WK> srow(const void *base, const void *scale
 #define DFL_NT_WEIGHTS 0
 #endif
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 wload16(const void *p) {
 #if DFL_NT_WEIGHTS

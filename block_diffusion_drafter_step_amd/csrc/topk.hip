@@ -52,10 +52,11 @@ __device__ __forceinline__ void list_insert(float (&v)[KM], int (&ix)[KM], float
 // 4 waves) and write the workgroup's partial (top-K, max, sum of exp) per token.
 // Thread (token = tid / 16, list q = tid % 16) offers its list's head; a
 // 16-lane argmax by (value desc, index asc) picks the next entry K times.
-template <int KM>
+template <int KM, int NW = 4>
 __device__ __forceinline__ void wg_merge_write(const float (&tv)[KM], const int (&ti)[KM], float m,
                                                float ssum, const TopkArgs &a, float *lv, int *li,
                                                float *lm, float *ls) {
+  constexpr int LQ = 4 * NW;   // lists per token: 4 lane groups per wave
   const int tid = threadIdx.x;
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
@@ -65,16 +66,16 @@ __device__ __forceinline__ void wg_merge_write(const float (&tv)[KM], const int 
   lm[tid] = m;
   ls[tid] = ssum;
   __syncthreads();
-  const int tok = tid >> 4, q = tid & 15;
+  const int tok = tid / LQ, q = tid % LQ;
   // list q of token tok was written by thread (q/4)*64 + (q%4)*16 + tok
   const int src = (q >> 2) * 64 + (q & 3) * 16 + tok;
   const float pm = lm[src];
   float M = pm;
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, shfl_xor(M, o));
+  for (int o = 1; o < LQ; o <<= 1) M = fmaxf(M, shfl_xor(M, o));
   float ps = ls[src] > 0.f ? ls[src] * exp2f((pm - M) * kL2e) : 0.f;
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) ps += shfl_xor(ps, o);
+  for (int o = 1; o < LQ; o <<= 1) ps += shfl_xor(ps, o);
   const long ob = (long)blockIdx.x * 16 + tok;
   if (q == 0) {
     a.part_ms[ob * 2] = M;
@@ -86,7 +87,7 @@ __device__ __forceinline__ void wg_merge_write(const float (&tv)[KM], const int 
     int bi = head < KM ? li[src * KM + head] : 0x7fffffff;
     int bq = q;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
+    for (int o = 1; o < LQ; o <<= 1) {
       const float ov = shfl_xor(bv, o);
       const int oi = __shfl_xor(bi, o, kWave);
       const int oq = __shfl_xor(bq, o, kWave);
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(256) void lmhead_topk_kernel(TopkArgs a) {
 // tokens hit 16 different bank groups.
 // ---------------------------------------------------------------------------
 #ifndef DFL_LMH_DEPTH
-#define DFL_LMH_DEPTH 2
+#define DFL_LMH_DEPTH 1
 #endif
 
 template <typename TA, int WK>
@@ -262,8 +263,8 @@ __device__ __forceinline__ void lm_stage_mma(const LmStage<TA, WK> &s, const TA 
   }
 }
 
-template <typename TA, int WK, int KM>
-__global__ __launch_bounds__(256) void lmhead_topk_lds_kernel(TopkArgs a) {
+template <typename TA, int WK, int KM, int NW>
+__global__ __launch_bounds__(NW * 64) void lmhead_topk_lds_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   TA *hs = reinterpret_cast<TA *>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(256) void lmhead_topk_lds_kernel(TopkArgs a) {
   constexpr int VEC = 16 / (int)sizeof(TA);
   // stage h (B rows) into LDS, swizzled
   const TA *hg = reinterpret_cast<const TA *>(a.h);
-  for (int c = tid; c < B * (d / VEC); c += 256) {
+  for (int c = tid; c < B * (d / VEC); c += NW * 64) {
     const int t = c / (d / VEC), k = (c - t * (d / VEC)) * VEC;
     *reinterpret_cast<uint4 *>(hs + hsw<TA>(t, k, d)) =
         *reinterpret_cast<const uint4 *>(hg + (long)t * d + k);
@@ -281,8 +282,8 @@ __global__ __launch_bounds__(256) void lmhead_topk_lds_kernel(TopkArgs a) {
   __syncthreads();
 
   const long ntiles = (V + 15) / 16;
-  const long nw = (long)gridDim.x * 4;
-  const long wid = (long)blockIdx.x * 4 + wave;
+  const long nw = (long)gridDim.x * NW;
+  const long wid = (long)blockIdx.x * NW + wave;
   const long t_beg = wid * ntiles / nw, t_end = (wid + 1) * ntiles / nw;
   const int nck = d / 128;
   const int total = (int)(t_end - t_beg) * nck;
@@ -339,16 +340,24 @@ __global__ __launch_bounds__(256) void lmhead_topk_lds_kernel(TopkArgs a) {
   }
   __syncthreads();   // every wave is done with hs: reuse the LDS for the merge
   float *lv = reinterpret_cast<float *>(smem);
-  int *li = reinterpret_cast<int *>(lv + 256 * KM);
-  float *lm = reinterpret_cast<float *>(li + 256 * KM);
-  float *ls = lm + 256;
-  wg_merge_write<KM>(tv, ti, m, ssum, a, lv, li, lm, ls);
+  int *li = reinterpret_cast<int *>(lv + NW * 64 * KM);
+  float *lm = reinterpret_cast<float *>(li + NW * 64 * KM);
+  float *ls = lm + NW * 64;
+  wg_merge_write<KM, NW>(tv, ti, m, ssum, a, lv, li, lm, ls);
 }
+
+// waves per workgroup of the h-resident LM head (4 or 8)
+#ifndef DFL_LMH_WAVES
+#define DFL_LMH_WAVES 8
+#endif
+
+int topk_lds_waves() { return DFL_LMH_WAVES; }
 
 size_t topk_lds_bytes(int B, int d, int act, int K) {
   const int km = K <= 8 ? 8 : 32;
   const size_t h = (size_t)B * d * (act == ACT_F32 ? 4 : 2);
-  const size_t mg = (size_t)256 * km * 8 + 256 * 8;
+  const size_t nt = DFL_LMH_WAVES * 64;
+  const size_t mg = nt * km * 8 + nt * 8;
   return h > mg ? h : mg;
 }
 
@@ -515,11 +524,11 @@ static void topk_launch_tpw(const TopkArgs &a, hipStream_t st) {
 
 template <typename TA, int WK, int KM>
 static void topk_launch_lds(const TopkArgs &a, hipStream_t st) {
-  auto *kern = &lmhead_topk_lds_kernel<TA, WK, KM>;
+  auto *kern = &lmhead_topk_lds_kernel<TA, WK, KM, DFL_LMH_WAVES>;
   // more than 64 KB of dynamic LDS has to be allowed explicitly
   (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes);
-  hipLaunchKernelGGL(kern, dim3(a.n_wg), dim3(256), (size_t)a.lds_bytes, st, a);
+  hipLaunchKernelGGL(kern, dim3(a.n_wg), dim3(DFL_LMH_WAVES * 64), (size_t)a.lds_bytes, st, a);
   hipLaunchKernelGGL((topk_merge_kernel<KM>), dim3(a.B), dim3(256), 0, st, a);
 }
 
