@@ -722,11 +722,15 @@ __device__ __forceinline__ void dma16(const void *g, lds_void *l) {
 // wait until at most N vector-memory operations of this wave are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N < 64, "vmcnt range");
+  static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__device__ __forceinline__ int dslot(int row, int c) { return c ^ ((row >> 2) & 3); }
+// 16-byte chunk c of a 64-byte LDS row is stored at slot c ^ ((row >> 1) & 3):
+// with this XOR the 16 rows x 4 chunks of one fragment read (ds_read_b128)
+// measured free of bank conflicts on gfx950, while XORing with row bits
+// 2-3 (or 0-1), or padding the rows, left 1.33 conflict cycles per read
+__device__ __forceinline__ int dslot(int row, int c) { return c ^ ((row >> 1) & 3); }
 
 // issue one stage: A rows [m0, m0+256) and W rows [n0, n0+256), k [k0, k0+32)
 __device__ __forceinline__ void dma_stage(char *stage, const ASrc &A, int M, const WSet &W, int m0,
@@ -819,6 +823,144 @@ __global__ __launch_bounds__(256) void dma_gemm_kernel(ASrc A, int M, WSet W, Ou
     }
 }
 
+// 256 x 256 block tile on 8 waves (2 along M x 4 along N, 128 x 64 each):
+// 128 accumulator registers per wave leave the fragments and addresses in
+// VGPRs (a 128 x 128 wave tile fills the VGPR file with accumulators and the
+// compiler shuttles operands through AGPRs), and two waves per SIMD hide each
+// other's LDS and barrier stalls.  Same 4-stage direct-to-LDS ring and
+// swizzle as dma_gemm_kernel; each wave issues 2 A and 2 W row blocks per
+// stage from row pointers fixed before the loop, and the activation source
+// advances without a division.
+#ifndef DFL_DMA8_STAGES
+#define DFL_DMA8_STAGES 4
+#endif
+constexpr int D8STAGES = DFL_DMA8_STAGES;
+
+template <int OM>
+__global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, OutSpec o) {
+  extern __shared__ __attribute__((aligned(1024))) char smem_dma8[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int mt = (M + DBM - 1) / DBM, nt = (W.n_total + DBN - 1) / DBN;
+  int tm, tn;
+  big_tile_of(blockIdx.x, mt, nt, &tm, &tn);
+  const int m0 = tm * DBM, n0 = tn * DBN;
+  const int nk = W.K / DBK;
+  const int kps = A.k_per_src;
+
+  // this lane's DMA rows: blocks 2*wave and 2*wave+1 of 16 rows, row rl,
+  // 16-byte chunk c of the k-step (stored at slot lane & 3)
+  const int rl = lane >> 2, slot = lane & 3;
+  long a_off[2];
+  const bf16 *w_row[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = (2 * wave + j) * 16 + rl;
+    const int c = dslot(row, slot);
+    a_off[j] = (long)min(m0 + row, M - 1) * kps + 8 * c;
+    int lr;
+    const int n = min(n0 + row, W.n_total - 1);
+    const int sg = seg_of(W, n, &lr);
+    w_row[j] = reinterpret_cast<const bf16 *>(pick(W.data, sg)) + (long)lr * W.K + 8 * c;
+  }
+  // next k-step to issue and its activation source
+  int ki = 0, src_i = 0, kl = 0;
+  const bf16 *src = reinterpret_cast<const bf16 *>(pick(A.ptr, 0));
+  auto issue = [&](char *stage) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      dma16(src + kl + a_off[j], (lds_void *)(stage + (2 * wave + j) * 1024));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      dma16(w_row[j] + ki * DBK, (lds_void *)(stage + DBM * DBK * 2 + (2 * wave + j) * 1024));
+    if (ki + 1 < nk) {   // past the last k-step the same one is issued again
+      ++ki;
+      kl += DBK;
+      if (kl == kps) {
+        kl = 0;
+        ++src_i;
+        src = reinterpret_cast<const bf16 *>(pick(A.ptr, src_i));
+      }
+    }
+  };
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+
+#pragma unroll
+  for (int s = 0; s < D8STAGES - 1; ++s) issue(smem_dma8 + s * DSTAGE_BYTES);
+
+  // The fragments of k-step kt+1 are read from LDS while the MFMAs of k-step
+  // kt run: one barrier per k-step makes stages kt and kt+1 complete for
+  // every wave, stage kt-1 (read a step ago) is then free for the next DMA.
+  const int ar = wm * 128 + r16, br = wn * 64 + r16;
+  auto read_frags = [&](int kt, Frag<bf16> (&fa)[8], Frag<bf16> (&fb)[4]) {
+    const char *st = smem_dma8 + (kt % D8STAGES) * DSTAGE_BYTES;
+    const bf16 *as = reinterpret_cast<const bf16 *>(st);
+    const bf16 *ws = reinterpret_cast<const bf16 *>(st + DBM * DBK * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = br + 16 * j;
+      fb[j] = load_frag(ws + row * DBK + 8 * dslot(row, g));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = ar + 16 * i;
+      fa[i] = load_frag(as + row * DBK + 8 * dslot(row, g));
+    }
+  };
+  auto mmas = [&](const Frag<bf16> (&fa)[8], const Frag<bf16> (&fb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mma(acc[i][j], fa[i], fb[j]);
+  };
+  // one k-step: wait for stage kt+1, refill the ring, read kt+1, multiply kt
+  auto step = [&](int kt, const Frag<bf16> (&fa)[8], const Frag<bf16> (&fb)[4],
+                  Frag<bf16> (&na)[8], Frag<bf16> (&nb)[4]) {
+    wait_vm<4 * (D8STAGES - 3)>();   // this wave's loads of stage kt+1 have landed
+    __syncthreads();                 // ... everyone's; stage kt-1 is no longer read
+    issue(smem_dma8 + ((kt + D8STAGES - 1) % D8STAGES) * DSTAGE_BYTES);
+    if (kt + 1 < nk) read_frags(kt + 1, na, nb);
+    mmas(fa, fb);
+  };
+  Frag<bf16> fa0[8], fb0[4], fa1[8], fb1[4];
+  wait_vm<4 * (D8STAGES - 2)>();
+  __syncthreads();
+  read_frags(0, fa0, fb0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, fa0, fb0, fa1, fb1);
+    if (kt + 1 < nk) step(kt + 1, fa1, fb1, fa0, fb0);
+  }
+  wait_vm<0>();
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 64 + 16 * j + r16;
+      if (n >= W.n_total) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * 128 + 16 * i + 4 * g + v;
+        if (m < M) store_out_m<bf16, OM>(o, m, n, acc[i][j][v]);
+      }
+    }
+}
+
+template <int OM>
+static void dma8_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st,
+                    size_t lds) {
+  const int mt = (M + DBM - 1) / DBM, nt = (W.n_total + DBN - 1) / DBN;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma8_gemm_kernel<OM>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((dma8_gemm_kernel<OM>), dim3(mt * nt), dim3(512), lds, st, A, M, W, out);
+}
+
 constexpr size_t kDmaLds = (size_t)DSTAGES * DSTAGE_BYTES;
 
 static void dma_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
@@ -840,7 +982,8 @@ static void dma_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, 
 }
 
 #ifndef DFL_PREFILL_KERNEL
-#define DFL_PREFILL_KERNEL 2     // 0: 128-tile, 1: 256-tile register-staged, 2: 256-tile direct-to-LDS
+#define DFL_PREFILL_KERNEL 3     // 0: 128-tile, 1: 256-tile register-staged, 2: 256-tile direct-to-LDS,
+                                 // 3: 256-tile direct-to-LDS on 8 waves
 #endif
 
 
@@ -848,7 +991,12 @@ hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet
                             const OutSpec &out, hipStream_t st) {
   if (act == ACT_F32)
     tile_launch_t<float, W_SAME>(A, M, W, out, st);
-  else if (M >= DFL_BIG_GEMM_MIN_M && wkind == W_SAME && DFL_PREFILL_KERNEL == 2)
+  else if (M >= DFL_BIG_GEMM_MIN_M && wkind == W_SAME && DFL_PREFILL_KERNEL == 3) {
+    const size_t lds = (size_t)D8STAGES * DSTAGE_BYTES;
+    if (out.mode == OUT_F32) dma8_go<OUT_F32>(A, M, W, out, st, lds);
+    else if (out.mode == OUT_ACT) dma8_go<OUT_ACT>(A, M, W, out, st, lds);
+    else dma8_go<OUT_CACHE>(A, M, W, out, st, lds);
+  } else if (M >= DFL_BIG_GEMM_MIN_M && wkind == W_SAME && DFL_PREFILL_KERNEL == 2)
     dma_launch(A, M, W, out, st);
   else if (M >= DFL_BIG_GEMM_MIN_M && wkind == W_Q8_0 && DFL_PREFILL_KERNEL >= 1)
     big_launch_t<W_Q8_0>(A, M, W, out, st);
