@@ -599,6 +599,9 @@ struct BigLoader {
 };
 
 // workgroup id -> (m-tile, n-tile)
+#ifndef DFL_TILE_GROUP_M
+#define DFL_TILE_GROUP_M 4
+#endif
 __device__ __forceinline__ void big_tile_of(int L, int mt, int nt, int *tm, int *tn) {
   const int T = mt * nt;
   int j = L;
@@ -606,8 +609,8 @@ __device__ __forceinline__ void big_tile_of(int L, int mt, int nt, int *tm, int 
     const int per = T >> 3;
     j = (L & 7) * per + (L >> 3);
   }
-  // groups of 4 m-tiles x all n-tiles, m fastest inside a group
-  const int GM = 4;
+  // groups of GM m-tiles x all n-tiles, m fastest inside a group
+  const int GM = DFL_TILE_GROUP_M;
   const int grp = j / (GM * nt);
   const int rem = j - grp * GM * nt;
   const int gm = min(GM, mt - grp * GM);
@@ -731,6 +734,19 @@ __device__ __forceinline__ void wait_vm() {
 // measured free of bank conflicts on gfx950, while XORing with row bits
 // 2-3 (or 0-1), or padding the rows, left 1.33 conflict cycles per read
 __device__ __forceinline__ int dslot(int row, int c) { return c ^ ((row >> 1) & 3); }
+
+// Workgroup barrier for the direct-to-LDS rings: the caller has waited for
+// its own stage loads (vmcnt); this waits for the wave's LDS reads, then
+// s_barrier.  Unlike __syncthreads, no workgroup release fence: that fence
+// would also wait for every direct-to-LDS load still in flight (they are
+// counted as vector-memory operations), draining the whole ring.  The empty
+// asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | ((0x3F >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // issue one stage: A rows [m0, m0+256) and W rows [n0, n0+256), k [k0, k0+32)
 __device__ __forceinline__ void dma_stage(char *stage, const ASrc &A, int M, const WSet &W, int m0,
@@ -924,14 +940,14 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
   auto step = [&](int kt, const Frag<bf16> (&fa)[8], const Frag<bf16> (&fb)[4],
                   Frag<bf16> (&na)[8], Frag<bf16> (&nb)[4]) {
     wait_vm<4 * (D8STAGES - 3)>();   // this wave's loads of stage kt+1 have landed
-    __syncthreads();                 // ... everyone's; stage kt-1 is no longer read
+    ring_barrier();                  // ... everyone's; stage kt-1 is no longer read
     issue(smem_dma8 + ((kt + D8STAGES - 1) % D8STAGES) * DSTAGE_BYTES);
     if (kt + 1 < nk) read_frags(kt + 1, na, nb);
     mmas(fa, fb);
   };
   Frag<bf16> fa0[8], fb0[4], fa1[8], fb1[4];
   wait_vm<4 * (D8STAGES - 2)>();
-  __syncthreads();
+  ring_barrier();
   read_frags(0, fa0, fb0);
   for (int kt = 0; kt < nk; kt += 2) {
     step(kt, fa0, fb0, fa1, fb1);
