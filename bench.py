@@ -111,7 +111,7 @@ def main():
     if decode64:
         # long-context decode: the cache already holds prefill_kv seeded rows
         cache.k[:, :cfg.prefill_kv].copy_(randn(cfg.Hkv, cfg.prefill_kv, cfg.hd))
-        cache.v[:, :cfg.prefill_kv].copy_(randn(cfg.Hkv, cfg.prefill_kv, cfg.hd))
+        cache.v[:, :cfg.prefill_kv // 32].copy_(randn(cfg.Hkv, cfg.prefill_kv // 32, cfg.hd, 32))   # V panels
         n_ctx0 = cfg.prefill_kv
     else:
         # prefill injection of n_ctx tokens (the MFMA-bound tile GEMM path)

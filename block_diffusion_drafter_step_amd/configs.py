@@ -64,10 +64,10 @@ class Config:
 
     @property
     def cap(self) -> int:
-        """KV-cache capacity in rows."""
+        """KV-cache capacity in rows (a multiple of 64, as the library requires)."""
         if self.capacity:
-            return self.capacity
-        return self.prefill_kv + self.n_ctx + self.inject_per_step * self.steps + 64
+            return -(-self.capacity // 64) * 64
+        return -(-(self.prefill_kv + self.n_ctx + self.inject_per_step * self.steps + 64) // 64) * 64
 
 
 def _qwen27b(**kw) -> Config:

@@ -3,238 +3,237 @@
 // the whole injected cache).
 //
 // The work is HBM-bound: every context K/V row is read once and used by all
-// query heads of its GQA group (Hq/Hkv heads x B block tokens).  A workgroup
-// owns one KV head and one contiguous chunk of keys (split-K over the context,
-// "flash-decoding"); its 4 waves share each 64-key K/V tile through LDS and
-// each wave runs one query head of the group against it:
-//   S^T = K_tile Q_h^T        (keys x tokens, 16x16x32 MFMA, K from LDS)
+// query heads of its GQA group (Hq/Hkv heads x B block tokens).  V is cached
+// in transposed panels of 32 positions ([Hkv][capacity/32][hd][32]), so the
+// K tile (32 keys x dims) and the V^T tile (dims x 32 keys) of a tile are
+// each one contiguous run of memory.  A workgroup
+// owns one KV head and one contiguous chunk of context keys (split-K over the
+// context, "flash-decoding"); 32-key K and V^T tiles stream through a 4-stage
+// LDS ring filled by direct-to-LDS loads, and each of its 4 waves runs one
+// query head of the group (two for 8-head groups) against every tile:
+//   S^T = K_tile Q_h^T        (keys x tokens, 16x16x32 MFMA)
 //   online softmax per token   (fp32, base-2 exponent, running max / sum)
-//   O^T += V_tile^T P^T        (dims x tokens; V is stored transposed in LDS)
-// The S^T layout leaves each lane with one token and eight keys, which is
-// exactly the B-operand layout P^T needs, so probabilities never leave
-// registers.  A second kernel merges the splits with their log-sum-exp
-// weights in a fixed order.
+//   O^T += V^T_tile P^T        (dims x tokens)
+// The keys of the two 16-key S^T tiles are interleaved (tile st, row m holds
+// key 8(m/4) + 4st + m%4), so each lane ends up holding eight consecutive
+// keys of one token: exactly the P^T operand whose matching V^T fragment is
+// one 16-byte run of a V^T row.  Probabilities never leave registers.  The
+// block's own B keys come from the Q | Kb | Vb buffer in the combine kernel,
+// which merges the splits and the block with their log-sum-exp weights in a
+// fixed order.
 #include "common.h"
 #include "kernels.h"
 
 namespace dfl {
 
-// keys per LDS tile (64 or 128) and the number of split workgroups aimed for
-#ifndef DFL_ATTN_KT
-#define DFL_ATTN_KT 64
-#endif
 #ifndef DFL_ATTN_WGS
 #define DFL_ATTN_WGS 512
 #endif
-constexpr int kAttnKT = DFL_ATTN_KT;
+constexpr int kAttnKT = 32;      // keys per tile (one ring stage)
+#ifndef DFL_ATTN_STAGES
+#define DFL_ATTN_STAGES 3
+#endif
+constexpr int kAttnStages = DFL_ATTN_STAGES;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// four consecutive elements moved as one 8-byte (bf16) or 16-byte (fp32) access
-template <typename TA>
-struct alignas(4 * sizeof(TA)) Quad {
-  TA v[4];
-};
+typedef __attribute__((address_space(3))) void attn_lds_void;
 
 template <typename TA, int HD>
 struct AttnCfg {
-  static constexpr int KPAD = 16 / (int)sizeof(TA);
-  static constexpr int KLD = HD + KPAD;             // K tile row (elements)
-  static constexpr int VLD = kAttnKT + 4;           // Vt row: the tile's keys + 4
-  static constexpr int VEC = 16 / (int)sizeof(TA);  // elements per 16-byte chunk
-  static constexpr int NQF = HD / 32;               // Q fragments (k-steps over dims)
-  static constexpr int NDT = HD / 16;               // 16-dim output tiles
+  static constexpr int ES = (int)sizeof(TA);
+  static constexpr int EPC = 16 / ES;                 // elements per 16-byte chunk
+  static constexpr int RK = HD * ES;                  // K tile row (one key), bytes
+  static constexpr int RV = kAttnKT * ES;             // V^T tile row (one dim), bytes
+  static constexpr int NKC = RK / 16, NVC = RV / 16;  // chunks per row
+  static constexpr int KBYTES = kAttnKT * RK;
+  static constexpr int STAGE = KBYTES + HD * RV;      // 2 * KT * HD * ES
+  static constexpr int NKI = KBYTES / 1024;           // 1 KB direct-to-LDS loads per stage
+  static constexpr int NI = STAGE / 1024;
+  static constexpr int NPW = NI / 4;                  // ... per wave
+  static constexpr int NQF = HD / 32;                 // Q fragments (k-steps over dims)
+  static constexpr int NDT = HD / 16;                 // 16-dim output tiles
+  static_assert(NI % 4 == 0, "stage must split evenly over 4 waves");
 };
 
-// pointer to row `j` of the keys (or values) seen by KV head `kvh`
-// (a select, not a branch: loads stay unconditional)
-template <typename TA, int HD>
-__device__ __forceinline__ const TA *key_row(const AttnArgs &a, const TA *cache, int kvh, long j,
-                                             int col_off) {
-  const bool ctx = j < a.n_ctx;
-  const long t = ctx ? 0 : j - a.n_ctx;
-  const long qld = (long)(a.Hq + 2 * a.Hkv) * HD;
-  const TA *c = cache + ((long)kvh * a.cap + (ctx ? j : 0)) * HD;
-  const TA *b = reinterpret_cast<const TA *>(a.qkv) + t * qld + col_off + (long)kvh * HD;
-  return ctx ? c : b;
+// LDS chunk slots.  K rows: the chunk XOR folds key-row bits 0-1 and 3-4,
+// which are distinct over the 16 (interleaved) keys of one S^T tile; V^T
+// rows: XOR with dim-row bits 1-2 (or 1-3).  Both were measured free of bank
+// conflicts for ds_read_b128 on gfx950; any XOR keeps each row a permutation.
+template <int NKC>
+__device__ __forceinline__ int kswz(int row, int c) {
+  return c ^ (((((row >> 3) & 3) << 2) | (row & 3)) & (NKC - 1));
+}
+template <int NVC>
+__device__ __forceinline__ int vswz(int row, int c) {
+  return c ^ ((row >> 1) & (NVC - 1));
 }
 
-// Staged tile: K copied as-is, V gathered 4 keys x 8 dims per thread and
-// written transposed.  Two LDS stages and two register sets: while the waves
-// compute on one stage, the next tile waits in registers and the one after is
-// in flight, so two tiles' loads overlap every compute phase.  Loads are
-// unconditional (keys past the chunk are clamped to its last key; their
-// scores are masked to -inf), which keeps the compiler's waits graded.
-template <typename TA, int HD>
-struct TileRegs {
-  using C = AttnCfg<TA, HD>;
-  static constexpr int KCH = kAttnKT * HD / C::VEC;         // 16-byte K chunks per tile
-  static constexpr int VITEMS = (kAttnKT / 4) * (HD / 8);    // (4 keys x 8 dims) V items
-  static constexpr int KPT = (KCH + 255) / 256, VPT = (VITEMS + 255) / 256;
-};
+// one direct-to-LDS 16-byte load per lane (lane i lands at byte 16 i)
+__device__ __forceinline__ void attn_dma16(const void *g, attn_lds_void *l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
 
-// the keys of one KV head that one split workgroup owns: [key0, key1)
+template <int N>
+__device__ __forceinline__ void attn_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait for this wave's LDS reads, then s_barrier; no workgroup fence (that
+// would also wait for every direct-to-LDS load still in flight)
+__device__ __forceinline__ void attn_ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | ((0x3F >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// the context keys [key0, key1) of KV head kvh that one workgroup owns
 struct KeyRange {
-  const AttnArgs *a;
-  int kvh, kcol, vcol, ntile;
+  const char *ck, *cv;   // this head's K rows and V^T panels
+  long cap;
   long key0, key1;
+  int ntile;
 };
 
-// tile tI (clamped to the last one) of the range into registers
+// Issue tile tI (clamped to the last) into `stage`: this wave's NPW of the
+// stage's 1 KB loads.  K rows past the chunk re-read its last key (they only
+// feed masked scores); a tile starts on a panel boundary, so its V^T is the
+// whole panel, which lies inside the capacity.
 template <typename TA, int HD>
-__device__ __forceinline__ void attn_load_tile(const KeyRange &kr, int tid, int tI,
-                                               u32x4 (&rk)[TileRegs<TA, HD>::KPT],
-                                               Frag<TA> (&rv)[TileRegs<TA, HD>::VPT][4]) {
+__device__ __forceinline__ void attn_issue(const KeyRange &kr, char *stage, int tI, int wave,
+                                           int lane) {
   using C = AttnCfg<TA, HD>;
-  using R = TileRegs<TA, HD>;
-  const AttnArgs &a = *kr.a;
-  const TA *ck = reinterpret_cast<const TA *>(a.ck);
-  const TA *cv = reinterpret_cast<const TA *>(a.cv);
   const long t0 = kr.key0 + (long)min(tI, kr.ntile - 1) * kAttnKT;
 #pragma unroll
-  for (int j = 0; j < R::KPT; ++j) {
-    const int c = min(tid + 256 * j, R::KCH - 1);
-    const int row = c / (HD / C::VEC), ch = c % (HD / C::VEC);
-    const long key = min(t0 + row, kr.key1 - 1);
-    rk[j] = *reinterpret_cast<const u32x4 *>(key_row<TA, HD>(a, ck, kr.kvh, key, kr.kcol) + ch * C::VEC);
-  }
-#pragma unroll
-  for (int j = 0; j < R::VPT; ++j) {
-    const int it = min(tid + 256 * j, R::VITEMS - 1);
-    const int kq = it / (HD / 8), d8 = it % (HD / 8);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const long key = min(t0 + 4 * kq + u, kr.key1 - 1);
-      rv[j][u] = load_frag(key_row<TA, HD>(a, cv, kr.kvh, key, kr.vcol) + d8 * 8);
+  for (int j = 0; j < C::NPW; ++j) {
+    const int q = wave + 4 * j;   // 1 KB piece of the stage
+    if (q < C::NKI) {
+      constexpr int RPI = 1024 / C::RK;   // key rows per piece
+      const int row = q * RPI + lane / C::NKC, slot = lane % C::NKC;
+      const long key = min(t0 + row, kr.key1 - 1);
+      attn_dma16(kr.ck + key * C::RK + 16 * kswz<C::NKC>(row, slot),
+                 (attn_lds_void *)(stage + q * 1024));
+    } else {
+      constexpr int RPI = 1024 / C::RV;   // dim rows per piece
+      const int qv = q - C::NKI;
+      const int d = qv * RPI + lane / C::NVC, slot = lane % C::NVC;
+      const char *panel = kr.cv + (t0 / kAttnKT) * (long)(HD * C::RV);
+      attn_dma16(panel + d * C::RV + 16 * vswz<C::NVC>(d, slot), (attn_lds_void *)(stage + q * 1024));
     }
   }
 }
 
-// registers -> one LDS stage (K as-is, V transposed)
-template <typename TA, int HD>
-__device__ __forceinline__ void attn_store_tile(TA *ks, TA *vt, int tid,
-                                                const u32x4 (&rk)[TileRegs<TA, HD>::KPT],
-                                                const Frag<TA> (&rv)[TileRegs<TA, HD>::VPT][4]) {
-  using C = AttnCfg<TA, HD>;
-  using R = TileRegs<TA, HD>;
+// an 8-element MFMA fragment of an LDS row from its (swizzled) 16-byte chunks
+template <typename TA>
+__device__ __forceinline__ Frag<TA> lds_frag2(const char *row, int c0, int c1);
+template <>
+__device__ __forceinline__ Frag<bf16> lds_frag2<bf16>(const char *row, int c0, int) {
+  return *reinterpret_cast<const Frag<bf16> *>(row + 16 * c0);
+}
+template <>
+__device__ __forceinline__ Frag<float> lds_frag2<float>(const char *row, int c0, int c1) {
+  Frag<float> f;
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(row + 16 * c0);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(row + 16 * c1);
 #pragma unroll
-  for (int j = 0; j < R::KPT; ++j) {
-    const int c = tid + 256 * j;
-    if (c < R::KCH) {
-      const int row = c / (HD / C::VEC), ch = c % (HD / C::VEC);
-      *reinterpret_cast<u32x4 *>(ks + row * C::KLD + ch * C::VEC) = rk[j];
-    }
+  for (int i = 0; i < 4; ++i) {
+    f.v[i] = a[i];
+    f.v[4 + i] = b[i];
   }
-#pragma unroll
-  for (int j = 0; j < R::VPT; ++j) {
-    const int it = tid + 256 * j;
-    if (it < R::VITEMS) {
-      const int kq = it / (HD / 8), d8 = it % (HD / 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        Quad<TA> q4;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) q4.v[u] = rv[j][u].v[e];
-        *reinterpret_cast<Quad<TA> *>(vt + (d8 * 8 + e) * C::VLD + 4 * kq) = q4;
-      }
-    }
-  }
+  return f;
 }
 
 // one tile from an LDS stage into this wave's running softmax and output
 template <typename TA, int HD, int HPW>
-__device__ __forceinline__ void attn_compute_tile(const TA *ks, const TA *vt, long t0, long key1,
-                                                  float sl2, int g, int r16,
-                                                  const Frag<TA> (&qf)[HPW][AttnCfg<TA, HD>::NQF],
-                                                  f32x4 (&o)[HPW][AttnCfg<TA, HD>::NDT],
-                                                  float (&m_run)[HPW], float (&l_run)[HPW],
-                                                  const bool (&active)[HPW]) {
+__device__ __forceinline__ void attn_tile(const char *stage, long t0, long key1, float sl2, int g,
+                                          int r16, const Frag<TA> (&qf)[HPW][AttnCfg<TA, HD>::NQF],
+                                          f32x4 (&o)[HPW][AttnCfg<TA, HD>::NDT], float (&m_run)[HPW],
+                                          float (&l_run)[HPW], const bool (&active)[HPW]) {
   using C = AttnCfg<TA, HD>;
+  constexpr int CPF = 8 / C::EPC;   // chunks per fragment (1 bf16, 2 fp32)
+  // K fragments of both S^T tiles (row m of tile st = key 8(m/4) + 4st + m%4)
+  Frag<TA> kf[2][C::NQF];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int row = 8 * (r16 >> 2) + 4 * st + (r16 & 3);
+    const char *kr = stage + row * C::RK;
+#pragma unroll
+    for (int f = 0; f < C::NQF; ++f) {
+      const int c = (32 * f + 8 * g) / C::EPC;
+      kf[st][f] = lds_frag2<TA>(kr, kswz<C::NKC>(row, c), kswz<C::NKC>(row, c + CPF - 1));
+    }
+  }
+  // V^T fragments: dims 16 dt + r16, keys 8g .. 8g+7
+  Frag<TA> vf[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) {
+    const int d = 16 * dt + r16;
+    const char *vr = stage + C::KBYTES + d * C::RV;
+    const int c = (8 * g) / C::EPC;
+    vf[dt] = lds_frag2<TA>(vr, vswz<C::NVC>(d, c), vswz<C::NVC>(d, c + CPF - 1));
+  }
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     if (!active[hh]) continue;
+    f32x4 s[2];
 #pragma unroll
-    for (int sb = 0; sb < kAttnKT / 32; ++sb) {
-      // S^T for 32 keys: two 16-key tiles, lane holds keys 4g+i (+16), token r16
-      f32x4 s[2];
+    for (int st = 0; st < 2; ++st) {
+      s[st] = zero4();
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s[st] = zero4();
-        const TA *kp = ks + (32 * sb + 16 * st + r16) * C::KLD + 8 * g;
+      for (int f = 0; f < C::NQF; ++f) mma(s[st], kf[st][f], qf[hh][f]);
+    }
+    // lane: token r16, keys 8g + 4st + i
+    float p[8];
+    float mx = -__builtin_inff();
 #pragma unroll
-        for (int f = 0; f < C::NQF; ++f) mma(s[st], load_frag(kp + 32 * f), qf[hh][f]);
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long key = t0 + 8 * g + 4 * st + i;
+        const float v = key < key1 ? s[st][i] * sl2 : -__builtin_inff();
+        p[st * 4 + i] = v;
+        mx = fmaxf(mx, v);
       }
-      float p[8];
-      float mx = -__builtin_inff();
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run[hh], mx);
+    const float alpha = m_new == -__builtin_inff() ? 1.f : exp2f(m_run[hh] - m_new);
+    // the row sum uses the probabilities exactly as the P.V product sees them
+    float ls = 0.f;
+    Frag<TA> pf;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+    for (int e = 0; e < 8; ++e) {
+      pf.v[e] = from_f32<TA>(p[e] == -__builtin_inff() ? 0.f : exp2f(p[e] - m_new));
+      ls += to_f32(pf.v[e]);
+    }
+    ls += shfl_xor(ls, 16);
+    ls += shfl_xor(ls, 32);
+    l_run[hh] = l_run[hh] * alpha + ls;
+    m_run[hh] = m_new;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const long key = t0 + 32 * sb + 16 * st + 4 * g + i;
-          const float v = key < key1 ? s[st][i] * sl2 : -__builtin_inff();
-          p[st * 4 + i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[hh], mx);
-      const float alpha = m_new == -__builtin_inff() ? 1.f : exp2f(m_run[hh] - m_new);
-      // the row sum uses the probabilities exactly as the P.V product sees them
-      float ls = 0.f;
-      Frag<TA> pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pf.v[e] = from_f32<TA>(p[e] == -__builtin_inff() ? 0.f : exp2f(p[e] - m_new));
-        ls += to_f32(pf.v[e]);
-      }
-      ls += shfl_xor(ls, 16);
-      ls += shfl_xor(ls, 32);
-      l_run[hh] = l_run[hh] * alpha + ls;
-      m_run[hh] = m_new;
-      // O^T[dim][tok] += V^T[dim][keys] P^T[keys][tok]; lane slots: keys 4g..4g+3, 16+4g..
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) {
-        o[hh][dt] *= alpha;
-        const TA *vp = vt + (16 * dt + r16) * C::VLD + 32 * sb + 4 * g;
-        const Quad<TA> v0 = *reinterpret_cast<const Quad<TA> *>(vp);
-        const Quad<TA> v1 = *reinterpret_cast<const Quad<TA> *>(vp + 16);
-        Frag<TA> vf;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vf.v[e] = v0.v[e];
-          vf.v[4 + e] = v1.v[e];
-        }
-        mma(o[hh][dt], vf, pf);
-      }
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      o[hh][dt] *= alpha;
+      mma(o[hh][dt], vf[dt], pf);
     }
   }
 }
 
-// Staged tiles: two LDS stages and two register sets.  While the waves
-// compute on one stage, the next tile waits in registers and the one after is
-// in flight, so two tiles' loads overlap every compute phase; one barrier per
-// tile.  Loads are unconditional (keys past the chunk are clamped to its last
-// key and their scores masked to -inf), which keeps the compiler's waits
-// graded instead of draining every load at a branch.
 template <typename TA, int HD, int HPW>
 __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
   using C = AttnCfg<TA, HD>;
-  using R = TileRegs<TA, HD>;
-  constexpr int KS = kAttnKT * C::KLD, VS = HD * C::VLD;   // stage sizes (elements)
-  __shared__ __attribute__((aligned(16))) TA Ks[2 * KS];
-  __shared__ __attribute__((aligned(16))) TA Vt[2 * VS];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  extern __shared__ __attribute__((aligned(1024))) char attn_smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int kvh = blockIdx.y, sp = blockIdx.x;
   const int grp = a.Hq / a.Hkv;
-  const long S = a.n_ctx + a.B;
   KeyRange kr;
-  kr.a = &a;
-  kr.kvh = kvh;
-  kr.kcol = a.Hq * HD;
-  kr.vcol = (a.Hq + a.Hkv) * HD;
+  kr.ck = reinterpret_cast<const char *>(a.ck) + (long)kvh * a.cap * C::RK;
+  kr.cv = reinterpret_cast<const char *>(a.cv) + (long)kvh * a.cap * HD * C::ES;   // cap/32 panels
+  kr.cap = a.cap;
   kr.key0 = (long)sp * a.chunk;
-  kr.key1 = min(S, kr.key0 + a.chunk);
+  kr.key1 = min(a.n_ctx, kr.key0 + a.chunk);
   kr.ntile = (int)((kr.key1 - kr.key0 + kAttnKT - 1) / kAttnKT);
   const long qld = (long)(a.Hq + 2 * a.Hkv) * HD;
   const float sl2 = a.scale * kLog2e;
@@ -260,31 +259,18 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
     l_run[hh] = 0.f;
   }
 
-  // tile n computes from stage n % 2
-  // (a native vector type: HIP's uint4 is a struct whose copies defeat
-  // register promotion of the two register sets)
-  u32x4 k0[R::KPT], k1[R::KPT];
-  Frag<TA> v0[R::VPT][4], v1[R::VPT][4];
-  const int ntile = kr.ntile;
-  attn_load_tile<TA, HD>(kr, tid, 0, k0, v0);
-  attn_store_tile<TA, HD>(Ks, Vt, tid, k0, v0);
-  attn_load_tile<TA, HD>(kr, tid, 1, k1, v1);
-  attn_load_tile<TA, HD>(kr, tid, 2, k0, v0);
-  __syncthreads();
-  for (int tI = 0; tI < ntile; tI += 2) {
-    attn_compute_tile<TA, HD, HPW>(Ks, Vt, kr.key0 + (long)tI * kAttnKT, kr.key1, sl2, g, r16, qf, o,
-                                   m_run, l_run, active);
-    attn_store_tile<TA, HD>(Ks + KS, Vt + VS, tid, k1, v1);   // tile tI + 1
-    attn_load_tile<TA, HD>(kr, tid, tI + 3, k1, v1);
-    __syncthreads();
-    if (tI + 1 < ntile) {
-      attn_compute_tile<TA, HD, HPW>(Ks + KS, Vt + VS, kr.key0 + (long)(tI + 1) * kAttnKT, kr.key1,
-                                     sl2, g, r16, qf, o, m_run, l_run, active);
-      attn_store_tile<TA, HD>(Ks, Vt, tid, k0, v0);           // tile tI + 2
-      attn_load_tile<TA, HD>(kr, tid, tI + 4, k0, v0);
-      __syncthreads();
-    }
+  // ring: tile t is read from stage t % S; stages t+1 .. t+S-2 are in flight
+  constexpr int S = kAttnStages;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) attn_issue<TA, HD>(kr, attn_smem + s * C::STAGE, s, wave, lane);
+  for (int tI = 0; tI < kr.ntile; ++tI) {
+    attn_wait_vm<C::NPW * (S - 2)>();   // this wave's loads of tile tI have landed
+    attn_ring_barrier();                // ... everyone's; tile tI-1 is no longer read
+    attn_issue<TA, HD>(kr, attn_smem + ((tI + S - 1) % S) * C::STAGE, tI + S - 1, wave, lane);
+    attn_tile<TA, HD, HPW>(attn_smem + (tI % S) * C::STAGE, kr.key0 + (long)tI * kAttnKT, kr.key1,
+                           sl2, g, r16, qf, o, m_run, l_run, active);
   }
+  attn_wait_vm<0>();
 
   // partials: lane holds dims 16*dt + 4g + i of token r16
 #pragma unroll
@@ -304,30 +290,57 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
   }
 }
 
-// O[t][h*hd + d] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One workgroup per (query head, token): thread (p, q) owns dims 4q..4q+3 and
-// the splits s = p, p + P, ... (P = 256 / (HD/4)); the P partial sums are then
-// added in p order through LDS, so the result is bitwise reproducible.
+// O[t][h*hd + d] = (sum_s 2^(m_s - M) O_s + 2^(m_b - M) O_b) /
+//                  (sum_s 2^(m_s - M) l_s + 2^(m_b - M) l_b),
+// where (m_b, l_b, O_b) is the block's own B keys, scored here from Q, Kb, Vb
+// (probabilities rounded to the act type as the split kernel rounds them).
+// One workgroup per (query head, token): thread (p, q) owns dims 4q..4q+3
+// and the splits s = p, p + P, ... (P = 256 / (HD/4)); the P partial sums are
+// added in p order through LDS and the block term last, so the result is
+// bitwise reproducible.
 constexpr int kMaxSplit = 1024;
 
 template <typename TA, int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  constexpr int NQ = HD / 4, P = 256 / NQ;
+  constexpr int NQ = HD / 4, P = 256 / NQ, DPP = HD / 16;
   __shared__ float wsp[kMaxSplit];
   __shared__ float red[8];
+  __shared__ float sblk[16];
   __shared__ float4 part[P][NQ];
   const int ht = blockIdx.x;  // hq * B + t
   const int hq = ht / a.B, t = ht - hq * a.B;
+  const int kvh = hq / (a.Hq / a.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ns = a.n_split;
-  const float *ml = a.part_ml + (long)ht * ns * 2;
+  const long qld = (long)(a.Hq + 2 * a.Hkv) * HD;
+  const TA *qkv = reinterpret_cast<const TA *>(a.qkv);
+
+  // block scores s_j = Q[t] . Kb[j] * scale (base 2): 16 threads per key
+  {
+    const int j = tid >> 4, q16 = tid & 15;
+    float sj = 0.f;
+    if (j < a.B) {
+      const TA *qr = qkv + (long)t * qld + (long)hq * HD + q16 * DPP;
+      const TA *kb = qkv + (long)j * qld + (long)(a.Hq + kvh) * HD + q16 * DPP;
+#pragma unroll
+      for (int e = 0; e < DPP; ++e) sj += to_f32(qr[e]) * to_f32(kb[e]);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) sj += shfl_xor(sj, o);
+    if (q16 == 0 && j < 16) sblk[j] = sj * a.scale * kLog2e;
+  }
   float mx = -__builtin_inff();
+  const float *ml = a.part_ml + (long)ht * ns * 2;
   for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, ml[2 * s]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
   if (lane == 0) red[wave] = mx;
   __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float mb = -__builtin_inff();
+  for (int j = 0; j < a.B; ++j) mb = fmaxf(mb, sblk[j]);
+  const float M = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), mb);
+  float lb = 0.f;
+  for (int j = 0; j < a.B; ++j) lb += to_f32(from_f32<TA>(exp2f(sblk[j] - mb)));
   float lsum = 0.f;
   for (int s = tid; s < ns; s += 256) {
     const float m = ml[2 * s];
@@ -340,7 +353,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   __syncthreads();
   if (lane == 0) red[4 + wave] = lsum;
   __syncthreads();
-  const float L = (red[4] + red[5]) + (red[6] + red[7]);
+  const float wb = exp2f(mb - M);
+  const float L = (red[4] + red[5]) + (red[6] + red[7]) + wb * lb;
   const int q = tid % NQ, p = tid / NQ;
   const float *po = a.part_o + (long)ht * ns * HD + 4 * q;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -369,6 +383,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
       const float4 v = part[j][q];
       r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
     }
+    // the block's keys: O_b = sum_j p_j Vb[j], added last
+    float4 ob = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < a.B; ++j) {
+      const float pj = to_f32(from_f32<TA>(exp2f(sblk[j] - mb)));
+      const TA *vb = qkv + (long)j * qld + (long)(a.Hq + a.Hkv + kvh) * HD + 4 * q;
+      ob.x += pj * to_f32(vb[0]); ob.y += pj * to_f32(vb[1]);
+      ob.z += pj * to_f32(vb[2]); ob.w += pj * to_f32(vb[3]);
+    }
+    r.x += wb * ob.x; r.y += wb * ob.y; r.z += wb * ob.z; r.w += wb * ob.w;
     TA *o = reinterpret_cast<TA *>(a.o) + (long)t * a.Hq * HD + (long)hq * HD + 4 * q;
     const float inv = 1.0f / L;
     o[0] = from_f32<TA>(r.x * inv);
@@ -378,7 +401,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
+// the cached context keys are split over about DFL_ATTN_WGS workgroups in
+// chunks of whole tiles; no context, no splits
 void attn_plan(long n_keys, int Hkv, int *chunk, int *n_split) {
+  if (n_keys <= 0) {
+    *chunk = kAttnKT;
+    *n_split = 0;
+    return;
+  }
   const int hk = Hkv > 0 ? Hkv : 1;
   long target = DFL_ATTN_WGS / hk;
   if (target < 1) target = 1;
@@ -392,15 +422,24 @@ void attn_plan(long n_keys, int Hkv, int *chunk, int *n_split) {
     ns = (n_keys + c - 1) / c;
   }
   *chunk = (int)c;
-  *n_split = (int)(ns < 1 ? 1 : ns);
+  *n_split = (int)ns;
+}
+
+template <typename TA, int HD, int HPW>
+static void attn_split_go(const AttnArgs &a, hipStream_t st) {
+  const size_t lds = (size_t)kAttnStages * AttnCfg<TA, HD>::STAGE;
+  auto *k = &attn_split_kernel<TA, HD, HPW>;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(k, dim3(a.n_split, a.Hkv), dim3(256), lds, st, a);
 }
 
 template <typename TA, int HD>
 static void attn_launch_t(const AttnArgs &a, hipStream_t st) {
-  if (a.Hq / a.Hkv <= 4)
-    hipLaunchKernelGGL((attn_split_kernel<TA, HD, 1>), dim3(a.n_split, a.Hkv), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_split_kernel<TA, HD, 2>), dim3(a.n_split, a.Hkv), dim3(256), 0, st, a);
+  if (a.n_split > 0) {
+    if (a.Hq / a.Hkv <= 4) attn_split_go<TA, HD, 1>(a, st);
+    else attn_split_go<TA, HD, 2>(a, st);
+  }
   hipLaunchKernelGGL((attn_combine_kernel<TA, HD>), dim3(a.Hq * a.B), dim3(256), 0, st, a);
 }
 

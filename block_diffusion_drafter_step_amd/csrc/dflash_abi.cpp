@@ -187,7 +187,7 @@ size_t attn_ws(int32_t B, int32_t d, int32_t Hq, int32_t Hkv, int32_t hd, int64_
   c.take(std::max(gemm_partial_bytes(B, qdim + 2 * kv, d), gemm_partial_bytes(B, d, qdim)));
   c.take((size_t)B * (qdim + 2 * kv) * 4);  // Q | Kb | Vb
   int chunk, n_split;
-  attn_plan(n_ctx + B, Hkv, &chunk, &n_split);
+  attn_plan(n_ctx, Hkv, &chunk, &n_split);
   c.take((size_t)Hq * B * n_split * hd * 4);  // partial O
   c.take((size_t)Hq * B * n_split * 2 * 4);   // partial (max, sum)
   c.take((size_t)B * qdim * 4);               // O
@@ -222,6 +222,9 @@ dflash_status check_cache(const dflash_kv_cache *cache, int32_t act) {
   if (cache->n_kv_heads < 1) return fail(DFLASH_ERR_INVALID_ARG, "n_kv_heads must be >= 1");
   if (cache->capacity < 1 || cache->capacity > kMaxRows)
     return fail(DFLASH_ERR_INVALID_ARG, "cache capacity out of range");
+  if (cache->capacity % 64)
+    return fail(DFLASH_ERR_INVALID_ARG, "cache capacity must be a multiple of 64 (got %lld)",
+                (long long)cache->capacity);
   TRY(need_ptr(cache->k, "cache.k"));
   TRY(need_ptr(cache->v, "cache.v"));
   return DFLASH_OK;
@@ -404,7 +407,7 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   void *qkv = c.take((size_t)B * nqkv * 4);
   AttnArgs a;
   memset(&a, 0, sizeof a);
-  attn_plan(n_ctx + B, Hkv, &a.chunk, &a.n_split);
+  attn_plan(n_ctx, Hkv, &a.chunk, &a.n_split);
   a.part_o = (float *)c.take((size_t)n_q_heads * B * a.n_split * hd * 4);
   a.part_ml = (float *)c.take((size_t)n_q_heads * B * a.n_split * 2 * 4);
   void *o = c.take((size_t)B * qdim * 4);

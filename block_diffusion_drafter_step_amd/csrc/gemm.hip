@@ -32,11 +32,16 @@ __device__ __forceinline__ void store_out_m(const OutSpec &o, long t, long n, fl
   } else if constexpr (OM == OUT_ACT) {
     if (o.resid) v += to_f32(reinterpret_cast<const TA *>(o.resid)[t * o.ld_resid + n]);
     reinterpret_cast<TA *>(o.out)[t * o.ld + o.col0 + n] = from_f32<TA>(v);
-  } else {
-    TA *dst = reinterpret_cast<TA *>(n < o.split ? o.ck : o.cv);
-    const long c = n < o.split ? n : n - o.split;
-    const long head = c / o.hd, dim = c - head * o.hd;
-    dst[(head * o.cap + o.pos0 + t) * o.hd + dim] = from_f32<TA>(v);
+  } else {   // K rows [head][pos][dim]; V in transposed 32-position panels [head][pos/32][dim][pos%32]
+    if (n < o.split) {
+      const long head = n / o.hd, dim = n - head * o.hd;
+      reinterpret_cast<TA *>(o.ck)[(head * o.cap + o.pos0 + t) * o.hd + dim] = from_f32<TA>(v);
+    } else {
+      const long c = n - o.split;
+      const long head = c / o.hd, dim = c - head * o.hd, pos = o.pos0 + t;
+      reinterpret_cast<TA *>(o.cv)[((head * (o.cap >> 5) + (pos >> 5)) * o.hd + dim) * 32 + (pos & 31)] =
+          from_f32<TA>(v);
+    }
   }
 }
 

@@ -117,7 +117,10 @@ class Weight:
 
 @dataclass
 class KVCache:
-    """K and V [n_kv_heads][capacity][head_dim] in the activation type."""
+    """K [n_kv_heads][capacity][head_dim] and V in transposed 32-position
+    panels, [n_kv_heads][capacity/32][head_dim][32], in the activation type;
+    capacity is a multiple of 64.  `v_panels` / `v_rows` convert V between
+    [n_kv_heads][positions][head_dim] and the panel layout."""
     k: torch.Tensor
     v: torch.Tensor
 
@@ -127,7 +130,22 @@ class KVCache:
 
     def c(self) -> _Cache:
         h, cap, hd = self.k.shape
+        if tuple(self.v.shape) != (h, cap // 32, hd, 32):
+            raise ValueError(f"V must be [n_kv_heads][capacity/32][head_dim][32] = "
+                             f"{(h, cap // 32, hd, 32)}, got {tuple(self.v.shape)}")
         return _Cache(_DT[self.act], h, hd, 0, cap, _ptr(self.k), _ptr(self.v))
+
+
+def v_panels(v_rows: torch.Tensor) -> torch.Tensor:
+    """[h][positions][hd] (positions a multiple of 32) -> [h][positions/32][hd][32]."""
+    h, n, hd = v_rows.shape
+    return v_rows.reshape(h, n // 32, 32, hd).permute(0, 1, 3, 2).contiguous()
+
+
+def v_rows(v_panel: torch.Tensor) -> torch.Tensor:
+    """[h][positions/32][hd][32] -> [h][positions][hd]."""
+    h, p, hd, _ = v_panel.shape
+    return v_panel.permute(0, 1, 3, 2).reshape(h, p * 32, hd)
 
 
 def _ptr(t: Optional[torch.Tensor]):

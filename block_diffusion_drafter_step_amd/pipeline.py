@@ -32,9 +32,10 @@ def act_dtype(act: str):
 
 
 def new_cache(cfg, device="cuda") -> D.KVCache:
-    shp = (cfg.Hkv, cfg.cap, cfg.hd)
-    return D.KVCache(torch.zeros(shp, dtype=act_dtype(cfg.act), device=device),
-                     torch.zeros(shp, dtype=act_dtype(cfg.act), device=device))
+    """Zeroed cache: K [Hkv][cap][hd], V in transposed panels [Hkv][cap/32][hd][32]."""
+    dt = act_dtype(cfg.act)
+    return D.KVCache(torch.zeros((cfg.Hkv, cfg.cap, cfg.hd), dtype=dt, device=device),
+                     torch.zeros((cfg.Hkv, cfg.cap // 32, cfg.hd, 32), dtype=dt, device=device))
 
 
 class DeviceWeights:

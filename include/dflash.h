@@ -89,8 +89,13 @@ typedef struct {
   const void *scales;
 } dflash_weight;
 
-/* The draft decoder's KV cache: K and V each [n_kv_heads][capacity][head_dim]
- * in the act type.  head_dim is 64 or 128. */
+/* The draft decoder's KV cache in the act type: K is [n_kv_heads][capacity]
+ * [head_dim] (a key is one contiguous row); V is stored in transposed panels
+ * of 32 positions, [n_kv_heads][capacity/32][head_dim][32]: element
+ * (h, pos, j) of V sits at ((h*(capacity/32) + pos/32)*head_dim + j)*32 +
+ * pos%32.  32 positions of K and of V^T are then each one contiguous block
+ * for the attention's streaming loads.  head_dim is 64 or 128; capacity is a
+ * multiple of 64. */
 typedef struct {
   int32_t dtype;  /* DFLASH_F32 or DFLASH_BF16 */
   int32_t n_kv_heads;
@@ -115,11 +120,13 @@ typedef struct {
  *   y = h . fc^T                 fc [d][L*d_t]                       (fp32)
  *   z = y / sqrt(mean(y^2) + eps) * gamma                            (act type)
  *   K = z . Wk^T, V = z . Wv^T   Wk, Wv [Hkv*hd][d]                  (act type)
- *   cache.k[h][pos0 + t][j] = K[t][h*hd + j], same for V, t < n_tokens.
+ *   cache.k[h][pos0 + t][j] = K[t][h*hd + j], t < n_tokens
+ *   V[t][h*hd + j] -> cache.v at position pos0 + t, head h, dim j
+ *                     (transposed 32-position panels, see above)
  * layer_hidden: HOST array of n_layers device pointers, each [n_tokens][d_t]
  * in `act`.  gamma: [d] in `act`, or NULL for ones.  Requires
  * 0 <= pos0 && pos0 + n_tokens <= capacity (else DFLASH_ERR_CAPACITY),
- * d_t % 64 == 0, d % 64 == 0, n_tokens >= 1.  Cache rows outside
+ * d_t % 64 == 0, d % 64 == 0, n_tokens >= 1.  Cache positions outside
  * [pos0, pos0 + n_tokens) are not touched. */
 dflash_status dflash_inject(const void *const *layer_hidden, int32_t n_layers, int64_t n_tokens,
                             int32_t d_t, int32_t act, const dflash_weight *fc, const void *gamma,
@@ -151,8 +158,9 @@ size_t dflash_conv_workspace(int32_t n_blocks, int32_t B, int32_t C, int32_t G, 
  *   for query head h, KV head g = h / (Hq/Hkv):
  *     O_h = softmax(Q_h [Kctx_g | Kb_g]^T * scale) [Vctx_g | Vb_g]      (act type)
  *   out = residual + O Wo^T                                            (act type)
- * No mask: every block position sees all n_ctx context rows and all B block
- * rows.  The block's K/V are not written to the cache.
+ * No mask: every block position sees all n_ctx context positions and all B
+ * block rows.  Kctx / Vctx are cache positions [0, n_ctx) (V read from its
+ * transposed panels).  The block's K/V are not written to the cache.
  * u, residual, out: [B][d] in `act` (residual NULL = none); Wq [Hq*hd][d],
  * Wk, Wv [Hkv*hd][d], Wo [d][Hq*hd]; scale 0 = 1/sqrt(hd).  Requires
  * 1 <= B <= DFLASH_MAX_BLOCK, Hq % Hkv == 0, 0 <= n_ctx <= capacity,

@@ -104,6 +104,7 @@ def test_inject_rejections(lib):
     assert call(c=cache(hd=96)) == 2
     assert call(c=cache(dtype=0)) == 1
     assert call(pos0=4090) == 3 and "capacity" in err(lib)
+    assert call(c=cache(cap=4000)) == 1 and "capacity" in err(lib)   # not a multiple of 64
     assert call(pos0=-1) == 3
     assert call(ws=None) == 4
     assert call(wsb=16) == 4

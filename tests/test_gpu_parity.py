@@ -61,7 +61,9 @@ def run_inject(cfg, n, pos0, rows=None, prefill=None):
     bp = cfg.act == "bf16"
     ref = O.inject([act_np(h[rows], cfg.act) for h in hid], wnp(fc), None, cfg.eps, wnp(wk), wnp(wv), bp)
     gk = f64(cache.k[:, pos0 + torch.as_tensor(rows, device="cuda"), :].permute(1, 0, 2).reshape(len(rows), -1))
-    gv = f64(cache.v[:, pos0 + torch.as_tensor(rows, device="cuda"), :].permute(1, 0, 2).reshape(len(rows), -1))
+    # V is cached in transposed 32-position panels
+    gv = f64(D.v_rows(cache.v)[:, pos0 + torch.as_tensor(rows, device="cuda"), :].permute(1, 0, 2)
+             .reshape(len(rows), -1))
     assert_close(gk, ref["k"], cfg.act, f"{cfg.name} cache K")
     assert_close(gv, ref["v"], cfg.act, f"{cfg.name} cache V")
     return cache
@@ -139,7 +141,7 @@ def test_conv_batched_32k_tokens():
 
 def run_attn(cfg, n_ctx, cap=None, resid=True, B=None):
     B = cfg.B if B is None else B
-    cap = cap or (n_ctx + 64)
+    cap = cap or -(-(n_ctx + 64) // 64) * 64   # the library wants a multiple of 64
     say(f"attn {cfg.name} B={B} n_ctx={n_ctx} cap={cap}")
     w = synth.Workload(cfg)
     shp = (cfg.Hkv, cap, cfg.hd)
@@ -148,7 +150,7 @@ def run_attn(cfg, n_ctx, cap=None, resid=True, B=None):
     u = synth.normal(cfg.seed, "attn.u", (B, cfg.d), 1.0, cfg.act)
     x = synth.normal(cfg.seed, "attn.x", (B, cfg.d), 1.0, cfg.act)
     wq, wk, wv, wo = w.wq(), w.wk(), w.wv(), w.wo()
-    cache = D.KVCache(dev(ck, cfg.act), dev(cv, cfg.act))
+    cache = D.KVCache(dev(ck, cfg.act), D.v_panels(dev(cv, cfg.act)))
     out = torch.empty((B, cfg.d), dtype=P.act_dtype(cfg.act), device="cuda")
     ws = D.workspace(D.dflash_block_attn_workspace(B, cfg.d, cfg.Hq, cfg.Hkv, cfg.hd, n_ctx))
     xd = dev(x, cfg.act)
