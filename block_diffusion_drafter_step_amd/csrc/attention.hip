@@ -425,6 +425,19 @@ void attn_plan(long n_keys, int Hkv, int *chunk, int *n_split) {
   *n_split = (int)ns;
 }
 
+// an upper bound on attn_plan's split count that never decreases with
+// n_keys (attn_plan's own count can: a longer context may round to longer
+// chunks), so a workspace sized for a maximum context fits every shorter one
+int attn_max_splits(long n_keys, int Hkv) {
+  if (n_keys <= 0) return 0;
+  const int hk = Hkv > 0 ? Hkv : 1;
+  long target = DFL_ATTN_WGS / hk;
+  if (target < 1) target = 1;
+  const long tiles = (n_keys + kAttnKT - 1) / kAttnKT;
+  long b = tiles < target ? tiles : target;
+  return (int)(b < kMaxSplit ? b : kMaxSplit);
+}
+
 template <typename TA, int HD, int HPW>
 static void attn_split_go(const AttnArgs &a, hipStream_t st) {
   const size_t lds = (size_t)kAttnStages * AttnCfg<TA, HD>::STAGE;

@@ -186,8 +186,7 @@ size_t attn_ws(int32_t B, int32_t d, int32_t Hq, int32_t Hkv, int32_t hd, int64_
   const int qdim = Hq * hd, kv = Hkv * hd;
   c.take(std::max(gemm_partial_bytes(B, qdim + 2 * kv, d), gemm_partial_bytes(B, d, qdim)));
   c.take((size_t)B * (qdim + 2 * kv) * 4);  // Q | Kb | Vb
-  int chunk, n_split;
-  attn_plan(n_ctx, Hkv, &chunk, &n_split);
+  const int n_split = attn_max_splits(n_ctx, Hkv);   // >= the plan's split count
   c.take((size_t)Hq * B * n_split * hd * 4);  // partial O
   c.take((size_t)Hq * B * n_split * 2 * 4);   // partial (max, sum)
   c.take((size_t)B * qdim * 4);               // O
@@ -408,8 +407,9 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   AttnArgs a;
   memset(&a, 0, sizeof a);
   attn_plan(n_ctx, Hkv, &a.chunk, &a.n_split);
-  a.part_o = (float *)c.take((size_t)n_q_heads * B * a.n_split * hd * 4);
-  a.part_ml = (float *)c.take((size_t)n_q_heads * B * a.n_split * 2 * 4);
+  const int ns_max = attn_max_splits(n_ctx, Hkv);
+  a.part_o = (float *)c.take((size_t)n_q_heads * B * ns_max * hd * 4);
+  a.part_ml = (float *)c.take((size_t)n_q_heads * B * ns_max * 2 * 4);
   void *o = c.take((size_t)B * qdim * 4);
 
   hipError_t e = gemm(act, wkind_of(wq), asrc1(u, d), B, wset({wq, wk, wv}), part, c.counters,

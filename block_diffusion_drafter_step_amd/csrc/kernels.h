@@ -104,6 +104,7 @@ struct AttnArgs {
   void *o;           // [B][Hq*hd] in the act type
 };
 void attn_plan(long n_keys, int Hkv, int *chunk, int *n_split);
+int attn_max_splits(long n_keys, int Hkv);
 hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st);
 
 // ---- LM head top-K -------------------------------------------------------------------

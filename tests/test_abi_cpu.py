@@ -60,6 +60,9 @@ def test_workspace_queries_are_host_only(lib):
     assert lib.dflash_block_attn_workspace(16, 5120, 32, 8, 128, 32768) > \
         lib.dflash_block_attn_workspace(16, 5120, 32, 8, 128, 1024)
     assert lib.dflash_topk_unary_workspace(16, 151936, 8) > 0
+    # a workspace sized for a longer context fits every shorter one
+    sizes = [lib.dflash_block_attn_workspace(16, 5120, 32, 8, 128, n) for n in range(0, 40000, 61)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))
     assert lib.dflash_conv_workspace(1, 16, 5120, 64, 4) > 0
     assert lib.dflash_selector_edges_workspace(16, 64, 5120, 8) > 0
     assert lib.dflash_inject_workspace(0, 16, 5120, 5120, 1024, 1) == 0
