@@ -165,10 +165,11 @@ def main():
 
     # timed region: whole steps, wall clock between two device synchronisations;
     # the LM-head call (the dominant kernel) is bracketed by HIP events on its
-    # stream every EVERY-th step (an event record costs a few microseconds of
-    # queue time, so bracketing every call of every step would distort the step)
+    # stream every EVERY-th step (an event record leaves a gap of several
+    # microseconds in the queue, so bracketing every call of every step would
+    # distort the step)
     K = args.steps
-    EVERY = 4
+    EVERY = 16
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range((K + EVERY - 1) // EVERY)]
     torch.cuda.synchronize()
