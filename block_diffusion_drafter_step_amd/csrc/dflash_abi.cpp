@@ -465,7 +465,7 @@ dflash_status dflash_topk_unary(const void *h, int32_t B, int32_t act,
   const int cus = std::min(device_cu_count(), kMaxCUs);
   // resident path for bf16 / fp32 heads (measured faster there); Q8_0 heads
   // stream (their dequantisation favours more waves)
-  if (DFL_TOPK_RESIDENT && lm_head->dtype != DFLASH_Q8_0 && lds <= kMaxLdsBytes && d % 128 == 0 &&
+  if (DFL_TOPK_RESIDENT && lds <= kMaxLdsBytes && d % 128 == 0 &&
       (long)cus * topk_lds_waves() <= (V + 15) / 16) {
     a.lds_path = 1;
     a.lds_bytes = (int)lds;

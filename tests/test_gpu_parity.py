@@ -218,10 +218,11 @@ def test_topk_ragged_and_extremes(V, K, B):
     run_topk(cfg_small(0, V=V, K=K, B=B), tag=f"topk{V}.{K}")
 
 
-@pytest.mark.parametrize("ci,V,K,B", [(1, 20007, 8, 16), (1, 16393, 32, 5), (4, 24583, 8, 8), (0, 70001, 3, 8)])
+@pytest.mark.parametrize("ci,V,K,B", [(1, 40009, 8, 16), (1, 32791, 32, 5), (4, 49157, 8, 8), (0, 70001, 3, 8)])
 def test_topk_resident_path_ragged(ci, V, K, B):
-    """Vocabularies with at least four 16-row tiles per CU take the LDS-resident
-    path; ragged last tile, K up to 32, Q8_0, fp32."""
+    """Vocabularies with at least eight 16-row tiles per CU (one per wave of
+    the 256 resident workgroups) take the LDS-resident path; ragged last tile,
+    uneven tiles per wave, K up to 32, Q8_0, fp32."""
     run_topk(cfg_small(ci, V=V, K=K, B=B), tag=f"topkr{V}.{K}")
 
 
