@@ -62,6 +62,14 @@ __device__ __forceinline__ Frag<float> load_frag(const float *p) {
   return f;
 }
 
+// eight consecutive elements stored as one (bf16: 16-byte, fp32: 32-byte) access
+__device__ __forceinline__ void store_frag(bf16 *p, const Frag<bf16> &f) {
+  *reinterpret_cast<bf16x8 *>(p) = f.v;
+}
+__device__ __forceinline__ void store_frag(float *p, const Frag<float> &f) {
+  *reinterpret_cast<f32x8 *>(p) = f.v;
+}
+
 // Q8_0: 8 int8 codes of one 32-block times the block's fp16 scale, each
 // product rounded to bf16 (the declared rounding point of the Q8_0 path).
 __device__ __forceinline__ Frag<bf16> dequant8(uint2 codes, float scale) {

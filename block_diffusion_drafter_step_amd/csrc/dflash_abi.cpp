@@ -349,6 +349,8 @@ dflash_status dflash_conv(const void *x, int32_t n_blocks, int32_t B, int32_t C,
   TRY(need_ptr(out, "out"));
   if (n_blocks < 1 || B < 1 || (int64_t)n_blocks * B > kMaxRows)
     return fail(DFLASH_ERR_INVALID_ARG, "n_blocks and B must be >= 1");
+  if (B > DFLASH_MAX_BLOCK)
+    return fail(DFLASH_ERR_INVALID_ARG, "B must be in [1, %d]", DFLASH_MAX_BLOCK);
   if (C < 64 || C % 64) return fail(DFLASH_ERR_INVALID_ARG, "C must be a positive multiple of 64");
   if (G < 1 || C % G) return fail(DFLASH_ERR_INVALID_ARG, "G must divide C");
   if (T < 1 || T > 16) return fail(DFLASH_ERR_INVALID_ARG, "T must be in [1, 16]");

@@ -1010,18 +1010,22 @@ static void dma_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, 
 
 hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet &W,
                             const OutSpec &out, hipStream_t st) {
+  // 256-wide tiles only when they still give every CU two workgroups (a
+  // narrow product such as the batched conv's delta takes 128-wide tiles)
+  const long tiles256 = (long)((M + 255) / 256) * ((W.n_total + 255) / 256);
+  const bool big = M >= DFL_BIG_GEMM_MIN_M && tiles256 >= 2L * device_cu_count();
   if (act == ACT_F32)
     tile_launch_t<float, W_SAME>(A, M, W, out, st);
-  else if (M >= DFL_BIG_GEMM_MIN_M && wkind == W_SAME && DFL_PREFILL_KERNEL == 3) {
+  else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 3) {
     const size_t lds = (size_t)D8STAGES * DSTAGE_BYTES;
     if (out.mode == OUT_F32) dma8_go<OUT_F32>(A, M, W, out, st, lds);
     else if (out.mode == OUT_ACT) dma8_go<OUT_ACT>(A, M, W, out, st, lds);
     else dma8_go<OUT_CACHE>(A, M, W, out, st, lds);
-  } else if (M >= DFL_BIG_GEMM_MIN_M && wkind == W_SAME && DFL_PREFILL_KERNEL == 2)
+  } else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 2)
     dma_launch(A, M, W, out, st);
-  else if (M >= DFL_BIG_GEMM_MIN_M && wkind == W_Q8_0 && DFL_PREFILL_KERNEL >= 1)
+  else if (big && wkind == W_Q8_0 && DFL_PREFILL_KERNEL >= 1)
     big_launch_t<W_Q8_0>(A, M, W, out, st);
-  else if (M >= DFL_BIG_GEMM_MIN_M && DFL_PREFILL_KERNEL >= 1)
+  else if (big && DFL_PREFILL_KERNEL >= 1)
     big_launch_t<W_SAME>(A, M, W, out, st);
   else if (wkind == W_Q8_0)
     tile_launch_t<bf16, W_Q8_0>(A, M, W, out, st);

@@ -60,10 +60,10 @@ hipError_t launch_rmsnorm(int act, const float *y, int n, int d, const void *gam
 // ---------------------------------------------------------------------------
 // Grouped dynamic depthwise conv ("spec : add DFlash2 support", Overview):
 // out[i,c] = sum_t (base[t,c] + delta[i, t*G + g(c)]) * x[i-t, c], x[<0] = 0.
-// One thread per (block, position, 4 adjacent channels): its T input rows,
-// T delta values per channel and T base values are independent loads issued
-// together, so a single block costs one memory round trip, and a batch of
-// blocks is a pure stream (x read T times from cache, out written once).
+// One thread per (block, 8 adjacent channels): it loads the block's B input
+// rows of its channels (16-byte loads, all issued together) and the T base
+// rows once, then forms the B outputs from registers, so x is read exactly
+// once and a batch of blocks is a pure stream; delta values come from cache.
 // ---------------------------------------------------------------------------
 template <typename TA, int TM>
 __global__ __launch_bounds__(256) void conv_kernel(const TA *__restrict__ x, int n_blocks, int B,
@@ -71,39 +71,77 @@ __global__ __launch_bounds__(256) void conv_kernel(const TA *__restrict__ x, int
                                                    const TA *__restrict__ base,
                                                    const float *__restrict__ delta,
                                                    TA *__restrict__ out) {
+  // thread = (block, 8-channel chunk); it walks the block's B <= 16 positions
+  // with every x row of the chunk in registers, so x is read exactly once
+  constexpr int BMAX = 16;
+  const int nch = C >> 3;
   const long id = (long)blockIdx.x * 256 + threadIdx.x;
-  const int c4 = C >> 2;
-  const long row = id / c4;           // block * B + position
-  if (row >= (long)n_blocks * B) return;
-  const int c = (int)(id - row * c4) * 4;
-  const int i = (int)(row % B);
+  const long blk = id / nch;
+  if (blk >= n_blocks) return;
+  const int c = (int)(id - blk * nch) * 8;
   const int cpg = C / G;
-  const int TG = T * G;
-  const float *dl = delta + row * (long)TG;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  float xv[TM][4], bv[TM][4], dv[TM][4];
+  // group of each channel: g(c) = c / cpg, one division, then boundaries
+  int gj[8];
+  {
+    int g = c / cpg, next = (g + 1) * cpg;
 #pragma unroll
-  for (int t = 0; t < TM; ++t) {
-    const bool ok = t < T && i - t >= 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xv[t][j] = ok ? to_f32(x[(row - t) * C + c + j]) : 0.f;
-      bv[t][j] = t < T ? to_f32(base[(long)t * C + c + j]) : 0.f;
-      dv[t][j] = t < T ? dl[t * G + (c + j) / cpg] : 0.f;
+    for (int j = 0; j < 8; ++j) {
+      if (c + j >= next) {
+        ++g;
+        next += cpg;
+      }
+      gj[j] = g;
     }
   }
+  const TA *xb = x + blk * (long)B * C + c;
+  Frag<TA> xr[BMAX];
 #pragma unroll
-  for (int t = 0; t < TM; ++t)
+  for (int i = 0; i < BMAX; ++i) xr[i] = load_frag(xb + (long)min(i, B - 1) * C);   // rows >= B unused
+  // base taps held in registers up to 8 taps; longer filters re-read them
+  // from cache per use (registers would otherwise spill)
+  constexpr int TR = TM <= 8 ? TM : 1;
+  Frag<TA> bv[TR];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] += (bv[t][j] + dv[t][j]) * xv[t][j];
+  for (int t = 0; t < TR; ++t) bv[t] = load_frag(base + (long)min(t, T - 1) * C + c);
+  const int TG = T * G;
+  // a chunk inside one channel group (the usual case: C/G a multiple of 8)
+  // needs one delta value per tap instead of eight
+  const bool one_group = gj[0] == gj[7];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) out[row * C + c + j] = from_f32<TA>(acc[j]);
+  for (int i = 0; i < BMAX; ++i) {
+    if (i < B) {   // guard, not break: keeps the loop fully unrolled (static register indices)
+      const float *dl = delta + (blk * B + i) * (long)TG;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        if (t < T && t <= i) {
+          float dv[8];
+          if (one_group) {
+            const float v = dl[t * G + gj[0]];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dv[j] = v;
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dv[j] = dl[t * G + gj[j]];
+          }
+          const Frag<TA> b = TM <= 8 ? bv[t < TR ? t : 0] : load_frag(base + (long)t * C + c);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            acc[j] += (to_f32(b.v[j]) + dv[j]) * to_f32(xr[i - t].v[j]);
+        }
+      }
+      Frag<TA> o;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o.v[j] = from_f32<TA>(acc[j]);
+      store_frag(out + (blk * B + i) * (long)C + c, o);
+    }
+  }
 }
 
 template <typename TA>
 static void conv_launch_t(const void *x, int n_blocks, int B, int C, int G, int T, const void *base,
                           const float *delta, void *out, hipStream_t st) {
-  const long threads = (long)n_blocks * B * (C / 4);
+  const long threads = (long)n_blocks * (C / 8);
   const dim3 grid((unsigned)((threads + 255) / 256));
   const TA *xp = reinterpret_cast<const TA *>(x);
   const TA *bp = reinterpret_cast<const TA *>(base);

@@ -144,7 +144,7 @@ size_t dflash_inject_workspace(int32_t n_layers, int64_t n_tokens, int32_t d_t, 
  * tap 0 = the current position, x before the block start = 0.
  * x, out: [n_blocks][B][C] in `act` (blocks are independent); base: [T][C]
  * in `act`; w_delta: [T*G][C] in `act`.  Requires C % G == 0, C % 64 == 0,
- * 1 <= T <= 16, 1 <= B. */
+ * 1 <= T <= 16, 1 <= B <= DFLASH_MAX_BLOCK. */
 dflash_status dflash_conv(const void *x, int32_t n_blocks, int32_t B, int32_t C, int32_t G,
                           int32_t T, int32_t act, const void *base, const dflash_weight *w_delta,
                           void *out, void *ws, size_t ws_bytes, void *stream);

@@ -128,6 +128,7 @@ def test_conv_rejections(lib):
     assert call(T=0) == 1
     assert call(T=17) == 1
     assert call(B=0) == 1
+    assert call(B=17) == 1
     assert call(w=W(1, 33, 256)) == 1
     assert call(w=W(2, 32, 256, scales=FAKE)) == 2            # W_delta cannot be Q8_0
     assert call(wsb=8) == 4
@@ -143,6 +144,7 @@ def test_attn_rejections(lib):
                                      scale, FAKE, FAKE, wsb, None)
 
     assert call(B=0) == 1
+    assert call(B=17) == 1
     assert call(B=17) == 1
     assert call(Hq=30) == 1
     assert call(Hq=80, wq=W(1, 80 * 128, 5120), wo=W(1, 5120, 80 * 128)) == 2   # 10 q heads per kv head
