@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU-baseline leg")
     ap.add_argument("--prefill-reps", type=int, default=3)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the batched-conv, per-kernel and streaming-ceiling measurements "
+                         "(for runs under an external profiler)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -205,6 +208,13 @@ def main():
     per = {n: float(np.mean([evc[i][j][0].elapsed_time(evc[i][j][1]) for i in range(nb)]))
            for j, n in enumerate(names)}
 
+    extras = {}
+    if not args.no_extras:
+        extras["conv_batched"] = conv_batched(cfg, W, randn)
+        ctx_prof = int(np.mean([positions(i)[1] for i in range(20)]))
+        extras["kernels"] = kernel_profile(cfg, calls, ctx_prof)
+        extras["hbm_ceiling"] = stream_ceiling()
+
     if decode64:
         ctx_mean = float(np.mean([positions(i)[1] for i in range(cfg.steps)]))
     else:
@@ -236,10 +246,110 @@ def main():
            "attn_gbs": round(attn_bytes / (per["attn"] * 1e-3) / 1e9, 1)}
     if prefill:
         out["prefill"] = prefill
+    out.update(extras)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, host, int(ctx_mean), inj_n)
     print(json.dumps(out), flush=True)
+
+
+def conv_batched(cfg, W, randn, tokens=32768, reps=20):
+    """The conv call over a batch of blocks holding `tokens` positions (2048
+    blocks of 16 at the 32k setting's token count), HBM bytes = x in + u out
+    + base + W_delta over the call time (HIP events on the current stream)."""
+    import torch
+    from block_diffusion_drafter_step_amd import dflash as D, workmodel
+    nb = tokens // cfg.B
+    x = randn(nb, cfg.B, cfg.C)
+    u = torch.empty_like(x)
+    ws = D.workspace(D.dflash_conv_workspace(nb, cfg.B, cfg.C, cfg.G, cfg.T))
+    for _ in range(3):
+        D.dflash_conv(x, cfg.G, W.base, W.w_delta, u, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        D.dflash_conv(x, cfg.G, W.base, W.w_delta, u, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    b = workmodel.conv_bytes(cfg, nb)
+    del x, u, ws
+    torch.cuda.empty_cache()
+    return {"blocks": nb, "B": cfg.B, "us": round(t * 1e6, 1), "bytes": b,
+            "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def kernel_profile(cfg, calls, n_ctx, steps=20):
+    """Average device time of every kernel over `steps` whole steps, from a
+    torch.profiler device trace (it records every dispatch of the process,
+    libdflash's included), and the HBM fractions of the kernels it names:
+    attention = KV bytes over (split + combine), LM head = its bytes over
+    (top-K kernel + merge)."""
+    import torch
+    from block_diffusion_drafter_step_amd import workmodel
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for i in range(steps):
+                for c in calls:
+                    c(i)
+            torch.cuda.synchronize()
+        avg = {}
+        for e in prof.key_averages():
+            tot = getattr(e, "device_time_total", None)
+            if tot is None:
+                tot = getattr(e, "cuda_time_total", 0.0)
+            if e.count and tot and ("dfl" in e.key):
+                avg[e.key] = (e.count, tot / e.count)
+    except Exception as ex:   # a profiler that cannot trace here leaves the rest of the line intact
+        return {"error": f"{type(ex).__name__}: {ex}"}
+
+    def us(sub):
+        return sum(v[1] for k, v in avg.items() if sub in k)
+
+    out = {"steps": steps, "avg_us": {k[:90]: round(v[1], 2) for k, v in sorted(avg.items(), key=lambda kv: -kv[1][1] * kv[1][0])}}
+    split, comb = us("attn_split_kernel"), us("attn_combine_kernel")
+    lm, merge = us("lmhead_topk"), us("topk_merge_kernel")
+    if split + comb > 0:
+        kv = workmodel.attn_kv_bytes(cfg, n_ctx)
+        out["attention_kv"] = {"n_ctx": n_ctx, "bytes": kv, "split_us": round(split, 2),
+                               "combine_us": round(comb, 2),
+                               "achieved": round(kv / ((split + comb) * 1e-6) / 1e9, 1),
+                               "frac": round(kv / ((split + comb) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                               "split_only_frac": round(kv / (split * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    if lm + merge > 0:
+        b = workmodel.lmhead_bytes(cfg)
+        out["lm_head"] = {"bytes": b, "us": round(lm + merge, 2),
+                          "frac": round(b / ((lm + merge) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def stream_ceiling(reps=10):
+    """Measured streaming rates of plain device kernels on 1 GiB: a copy (read +
+    write) and a sum (read)."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    r = {}
+    for name, fn, nbytes in [("copy", lambda: b.copy_(a), 8 * n), ("sum", lambda: a.sum(), 4 * n)]:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e-3
+        r[name + "_gbs"] = round(nbytes / t / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return r
 
 
 def cpu_baseline(cfg, host, n_ctx, inj_n):

@@ -851,36 +851,50 @@ __global__ __launch_bounds__(256) void dma_gemm_kernel(ASrc A, int M, WSet W, Ou
 // other's LDS and barrier stalls.  Same 4-stage direct-to-LDS ring and
 // swizzle as dma_gemm_kernel; each wave issues 2 A and 2 W row blocks per
 // stage from row pointers fixed before the loop, and the activation source
-// advances without a division.
+// advances without a division.  TBM = 128 halves the block along M (64 x 64
+// wave tiles, one A row block per wave per stage) for products whose 256-row
+// tiles would leave CUs idle, e.g. the conv's delta (N = T*G = 256).
 #ifndef DFL_DMA8_STAGES
 #define DFL_DMA8_STAGES 4
 #endif
 constexpr int D8STAGES = DFL_DMA8_STAGES;
 
-template <int OM>
+template <int TBM>
+constexpr int d8_stage_bytes() { return (TBM + DBN) * DBK * 2; }
+
+template <int OM, int TBM>
 __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, OutSpec o) {
+  static_assert(TBM == 256 || TBM == 128, "block rows");
+  constexpr int NA = TBM / 128;        // A row blocks each wave issues per stage
+  constexpr int MI = TBM / 32;         // 16-row fragments of a wave tile along M
+  constexpr int LPS = NA + 2;          // loads per wave per stage
+  constexpr int SB = d8_stage_bytes<TBM>();
   extern __shared__ __attribute__((aligned(1024))) char smem_dma8[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int wm = wave >> 2, wn = wave & 3;
-  const int mt = (M + DBM - 1) / DBM, nt = (W.n_total + DBN - 1) / DBN;
+  const int mt = (M + TBM - 1) / TBM, nt = (W.n_total + DBN - 1) / DBN;
   int tm, tn;
   big_tile_of(blockIdx.x, mt, nt, &tm, &tn);
-  const int m0 = tm * DBM, n0 = tn * DBN;
+  const int m0 = tm * TBM, n0 = tn * DBN;
   const int nk = W.K / DBK;
   const int kps = A.k_per_src;
 
-  // this lane's DMA rows: blocks 2*wave and 2*wave+1 of 16 rows, row rl,
-  // 16-byte chunk c of the k-step (stored at slot lane & 3)
+  // this lane's DMA rows: A blocks NA*wave+j and W blocks 2*wave+j of 16
+  // rows, row rl, 16-byte chunk c of the k-step (stored at slot lane & 3)
   const int rl = lane >> 2, slot = lane & 3;
-  long a_off[2];
+  long a_off[NA];
   const bf16 *w_row[2];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int row = (NA * wave + j) * 16 + rl;
+    a_off[j] = (long)min(m0 + row, M - 1) * kps + 8 * dslot(row, slot);
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = (2 * wave + j) * 16 + rl;
     const int c = dslot(row, slot);
-    a_off[j] = (long)min(m0 + row, M - 1) * kps + 8 * c;
     int lr;
     const int n = min(n0 + row, W.n_total - 1);
     const int sg = seg_of(W, n, &lr);
@@ -891,11 +905,11 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
   const bf16 *src = reinterpret_cast<const bf16 *>(pick(A.ptr, 0));
   auto issue = [&](char *stage) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      dma16(src + kl + a_off[j], (lds_void *)(stage + (2 * wave + j) * 1024));
+    for (int j = 0; j < NA; ++j)
+      dma16(src + kl + a_off[j], (lds_void *)(stage + (NA * wave + j) * 1024));
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      dma16(w_row[j] + ki * DBK, (lds_void *)(stage + DBM * DBK * 2 + (2 * wave + j) * 1024));
+      dma16(w_row[j] + ki * DBK, (lds_void *)(stage + TBM * DBK * 2 + (2 * wave + j) * 1024));
     if (ki + 1 < nk) {   // past the last k-step the same one is issued again
       ++ki;
       kl += DBK;
@@ -907,51 +921,51 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
     }
   };
 
-  f32x4 acc[8][4];
+  f32x4 acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
 
 #pragma unroll
-  for (int s = 0; s < D8STAGES - 1; ++s) issue(smem_dma8 + s * DSTAGE_BYTES);
+  for (int s = 0; s < D8STAGES - 1; ++s) issue(smem_dma8 + s * SB);
 
   // The fragments of k-step kt+1 are read from LDS while the MFMAs of k-step
   // kt run: one barrier per k-step makes stages kt and kt+1 complete for
   // every wave, stage kt-1 (read a step ago) is then free for the next DMA.
-  const int ar = wm * 128 + r16, br = wn * 64 + r16;
-  auto read_frags = [&](int kt, Frag<bf16> (&fa)[8], Frag<bf16> (&fb)[4]) {
-    const char *st = smem_dma8 + (kt % D8STAGES) * DSTAGE_BYTES;
+  const int ar = wm * (TBM / 2) + r16, br = wn * 64 + r16;
+  auto read_frags = [&](int kt, Frag<bf16> (&fa)[MI], Frag<bf16> (&fb)[4]) {
+    const char *st = smem_dma8 + (kt % D8STAGES) * SB;
     const bf16 *as = reinterpret_cast<const bf16 *>(st);
-    const bf16 *ws = reinterpret_cast<const bf16 *>(st + DBM * DBK * 2);
+    const bf16 *ws = reinterpret_cast<const bf16 *>(st + TBM * DBK * 2);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = br + 16 * j;
       fb[j] = load_frag(ws + row * DBK + 8 * dslot(row, g));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MI; ++i) {
       const int row = ar + 16 * i;
       fa[i] = load_frag(as + row * DBK + 8 * dslot(row, g));
     }
   };
-  auto mmas = [&](const Frag<bf16> (&fa)[8], const Frag<bf16> (&fb)[4]) {
+  auto mmas = [&](const Frag<bf16> (&fa)[MI], const Frag<bf16> (&fb)[4]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) mma(acc[i][j], fa[i], fb[j]);
   };
   // one k-step: wait for stage kt+1, refill the ring, read kt+1, multiply kt
-  auto step = [&](int kt, const Frag<bf16> (&fa)[8], const Frag<bf16> (&fb)[4],
-                  Frag<bf16> (&na)[8], Frag<bf16> (&nb)[4]) {
-    wait_vm<4 * (D8STAGES - 3)>();   // this wave's loads of stage kt+1 have landed
-    ring_barrier();                  // ... everyone's; stage kt-1 is no longer read
-    issue(smem_dma8 + ((kt + D8STAGES - 1) % D8STAGES) * DSTAGE_BYTES);
+  auto step = [&](int kt, const Frag<bf16> (&fa)[MI], const Frag<bf16> (&fb)[4],
+                  Frag<bf16> (&na)[MI], Frag<bf16> (&nb)[4]) {
+    wait_vm<LPS * (D8STAGES - 3)>();   // this wave's loads of stage kt+1 have landed
+    ring_barrier();                    // ... everyone's; stage kt-1 is no longer read
+    issue(smem_dma8 + ((kt + D8STAGES - 1) % D8STAGES) * SB);
     if (kt + 1 < nk) read_frags(kt + 1, na, nb);
     mmas(fa, fb);
   };
-  Frag<bf16> fa0[8], fb0[4], fa1[8], fb1[4];
-  wait_vm<4 * (D8STAGES - 2)>();
+  Frag<bf16> fa0[MI], fb0[4], fa1[MI], fb1[4];
+  wait_vm<LPS * (D8STAGES - 2)>();
   ring_barrier();
   read_frags(0, fa0, fb0);
   for (int kt = 0; kt < nk; kt += 2) {
@@ -960,26 +974,33 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
   }
   wait_vm<0>();
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + wn * 64 + 16 * j + r16;
       if (n >= W.n_total) continue;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * 128 + 16 * i + 4 * g + v;
+        const int m = m0 + wm * (TBM / 2) + 16 * i + 4 * g + v;
         if (m < M) store_out_m<bf16, OM>(o, m, n, acc[i][j][v]);
       }
     }
 }
 
-template <int OM>
-static void dma8_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st,
-                    size_t lds) {
-  const int mt = (M + DBM - 1) / DBM, nt = (W.n_total + DBN - 1) / DBN;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma8_gemm_kernel<OM>),
+template <int OM, int TBM>
+static void dma8_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
+  const int mt = (M + TBM - 1) / TBM, nt = (W.n_total + DBN - 1) / DBN;
+  const size_t lds = (size_t)D8STAGES * d8_stage_bytes<TBM>();
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma8_gemm_kernel<OM, TBM>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((dma8_gemm_kernel<OM>), dim3(mt * nt), dim3(512), lds, st, A, M, W, out);
+  hipLaunchKernelGGL((dma8_gemm_kernel<OM, TBM>), dim3(mt * nt), dim3(512), lds, st, A, M, W, out);
+}
+
+template <int TBM>
+static void dma8_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
+  if (out.mode == OUT_F32) dma8_go<OUT_F32, TBM>(A, M, W, out, st);
+  else if (out.mode == OUT_ACT) dma8_go<OUT_ACT, TBM>(A, M, W, out, st);
+  else dma8_go<OUT_CACHE, TBM>(A, M, W, out, st);
 }
 
 constexpr size_t kDmaLds = (size_t)DSTAGES * DSTAGE_BYTES;
@@ -1010,18 +1031,21 @@ static void dma_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, 
 
 hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet &W,
                             const OutSpec &out, hipStream_t st) {
-  // 256-wide tiles only when they still give every CU two workgroups (a
-  // narrow product such as the batched conv's delta takes 128-wide tiles)
+  // 256 x 256 tiles while they give every CU two workgroups; a narrow
+  // product (the batched conv's delta, N = 256) takes 128 x 256 tiles while
+  // those still cover the CUs, and the 128 x 128 tile kernel below that
+  const long cus = device_cu_count();
   const long tiles256 = (long)((M + 255) / 256) * ((W.n_total + 255) / 256);
-  const bool big = M >= DFL_BIG_GEMM_MIN_M && tiles256 >= 2L * device_cu_count();
+  const long tiles128 = (long)((M + 127) / 128) * ((W.n_total + 255) / 256);
+  const bool big = M >= DFL_BIG_GEMM_MIN_M && tiles256 >= 2 * cus;
+  const bool half = M >= DFL_BIG_GEMM_MIN_M && !big && tiles128 >= cus;
   if (act == ACT_F32)
     tile_launch_t<float, W_SAME>(A, M, W, out, st);
-  else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 3) {
-    const size_t lds = (size_t)D8STAGES * DSTAGE_BYTES;
-    if (out.mode == OUT_F32) dma8_go<OUT_F32>(A, M, W, out, st, lds);
-    else if (out.mode == OUT_ACT) dma8_go<OUT_ACT>(A, M, W, out, st, lds);
-    else dma8_go<OUT_CACHE>(A, M, W, out, st, lds);
-  } else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 2)
+  else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 3)
+    dma8_launch<256>(A, M, W, out, st);
+  else if (half && wkind == W_SAME && DFL_PREFILL_KERNEL == 3)
+    dma8_launch<128>(A, M, W, out, st);
+  else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 2)
     dma_launch(A, M, W, out, st);
   else if (big && wkind == W_Q8_0 && DFL_PREFILL_KERNEL >= 1)
     big_launch_t<W_Q8_0>(A, M, W, out, st);

@@ -61,19 +61,24 @@ hipError_t launch_rmsnorm(int act, const float *y, int n, int d, const void *gam
 // Grouped dynamic depthwise conv ("spec : add DFlash2 support", Overview):
 // out[i,c] = sum_t (base[t,c] + delta[i, t*G + g(c)]) * x[i-t, c], x[<0] = 0.
 // One thread per (block, 8 adjacent channels): it loads the block's B input
-// rows of its channels (16-byte loads, all issued together) and the T base
-// rows once, then forms the B outputs from registers, so x is read exactly
-// once and a batch of blocks is a pure stream; delta values come from cache.
+// rows of its channels (16-byte loads) and the T base rows once, then forms
+// the B outputs from registers, so x is read exactly once and a batch of
+// blocks is a pure stream.  Every load is issued before the first use, with
+// no branch between them, so a thread waits for memory once:
+//   DM = 1: C/G a multiple of 8, the 8 channels share one group, one delta
+//           value per (position, tap);
+//   DM = 2: C/G >= 8, the 8 channels span at most two groups, two values per
+//           (position, tap) and a per-channel select;
+//   DM = 0: anything else (or T > 4), eight loads per (position, tap), issued
+//           where they are used.
+// BM >= B bounds the positions a thread walks (8 or 16).
 // ---------------------------------------------------------------------------
-template <typename TA, int TM>
+template <typename TA, int TM, int DM, int BM>
 __global__ __launch_bounds__(256) void conv_kernel(const TA *__restrict__ x, int n_blocks, int B,
                                                    int C, int G, int T,
                                                    const TA *__restrict__ base,
                                                    const float *__restrict__ delta,
                                                    TA *__restrict__ out) {
-  // thread = (block, 8-channel chunk); it walks the block's B <= 16 positions
-  // with every x row of the chunk in registers, so x is read exactly once
-  constexpr int BMAX = 16;
   const int nch = C >> 3;
   const long id = (long)blockIdx.x * 256 + threadIdx.x;
   const long blk = id / nch;
@@ -94,9 +99,9 @@ __global__ __launch_bounds__(256) void conv_kernel(const TA *__restrict__ x, int
     }
   }
   const TA *xb = x + blk * (long)B * C + c;
-  Frag<TA> xr[BMAX];
+  Frag<TA> xr[BM];
 #pragma unroll
-  for (int i = 0; i < BMAX; ++i) xr[i] = load_frag(xb + (long)min(i, B - 1) * C);   // rows >= B unused
+  for (int i = 0; i < BM; ++i) xr[i] = load_frag(xb + (long)min(i, B - 1) * C);   // rows >= B unused
   // base taps held in registers up to 8 taps; longer filters re-read them
   // from cache per use (registers would otherwise spill)
   constexpr int TR = TM <= 8 ? TM : 1;
@@ -104,25 +109,35 @@ __global__ __launch_bounds__(256) void conv_kernel(const TA *__restrict__ x, int
 #pragma unroll
   for (int t = 0; t < TR; ++t) bv[t] = load_frag(base + (long)min(t, T - 1) * C + c);
   const int TG = T * G;
-  // a chunk inside one channel group (the usual case: C/G a multiple of 8)
-  // needs one delta value per tap instead of eight
-  const bool one_group = gj[0] == gj[7];
+  const float *db = delta + blk * (long)B * TG;   // this block's delta rows
+  constexpr int DI = DM ? BM : 1, DT = DM ? TM : 1;
+  float dA[DI][DT], dB[DM == 2 ? DI : 1][DM == 2 ? DT : 1];
+  if constexpr (DM != 0) {
 #pragma unroll
-  for (int i = 0; i < BMAX; ++i) {
+    for (int i = 0; i < BM; ++i)
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const float *r = db + (long)min(i, B - 1) * TG + min(t, T - 1) * G;
+        dA[i][t] = r[gj[0]];
+        if constexpr (DM == 2) dB[i][t] = r[gj[7]];
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < BM; ++i) {
     if (i < B) {   // guard, not break: keeps the loop fully unrolled (static register indices)
-      const float *dl = delta + (blk * B + i) * (long)TG;
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         if (t < T && t <= i) {
           float dv[8];
-          if (one_group) {
-            const float v = dl[t * G + gj[0]];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) dv[j] = v;
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) dv[j] = dl[t * G + gj[j]];
+          for (int j = 0; j < 8; ++j) {
+            if constexpr (DM == 1)
+              dv[j] = dA[i][t];
+            else if constexpr (DM == 2)
+              dv[j] = gj[j] == gj[0] ? dA[i][t] : dB[i][t];
+            else
+              dv[j] = db[(long)i * TG + t * G + gj[j]];
           }
           const Frag<TA> b = TM <= 8 ? bv[t < TR ? t : 0] : load_frag(base + (long)t * C + c);
 #pragma unroll
@@ -138,6 +153,29 @@ __global__ __launch_bounds__(256) void conv_kernel(const TA *__restrict__ x, int
   }
 }
 
+template <typename TA, int TM, int DM, int BM>
+static void conv_go(dim3 grid, const TA *x, int n_blocks, int B, int C, int G, int T, const TA *base,
+                    const float *delta, TA *out, hipStream_t st) {
+  hipLaunchKernelGGL((conv_kernel<TA, TM, DM, BM>), grid, dim3(256), 0, st, x, n_blocks, B, C, G, T,
+                     base, delta, out);
+}
+
+template <typename TA, int BM>
+static void conv_launch_bm(dim3 grid, const TA *x, int n_blocks, int B, int C, int G, int T,
+                           const TA *base, const float *delta, TA *out, hipStream_t st) {
+  const int cpg = C / G;
+  if (T <= 4 && cpg % 8 == 0)
+    conv_go<TA, 4, 1, BM>(grid, x, n_blocks, B, C, G, T, base, delta, out, st);
+  else if (T <= 4 && cpg >= 8)
+    conv_go<TA, 4, 2, BM>(grid, x, n_blocks, B, C, G, T, base, delta, out, st);
+  else if (T <= 4)
+    conv_go<TA, 4, 0, BM>(grid, x, n_blocks, B, C, G, T, base, delta, out, st);
+  else if (T <= 8)
+    conv_go<TA, 8, 0, BM>(grid, x, n_blocks, B, C, G, T, base, delta, out, st);
+  else
+    conv_go<TA, 16, 0, BM>(grid, x, n_blocks, B, C, G, T, base, delta, out, st);
+}
+
 template <typename TA>
 static void conv_launch_t(const void *x, int n_blocks, int B, int C, int G, int T, const void *base,
                           const float *delta, void *out, hipStream_t st) {
@@ -146,15 +184,10 @@ static void conv_launch_t(const void *x, int n_blocks, int B, int C, int G, int 
   const TA *xp = reinterpret_cast<const TA *>(x);
   const TA *bp = reinterpret_cast<const TA *>(base);
   TA *op = reinterpret_cast<TA *>(out);
-  if (T <= 4)
-    hipLaunchKernelGGL((conv_kernel<TA, 4>), grid, dim3(256), 0, st, xp, n_blocks, B, C, G, T, bp,
-                       delta, op);
-  else if (T <= 8)
-    hipLaunchKernelGGL((conv_kernel<TA, 8>), grid, dim3(256), 0, st, xp, n_blocks, B, C, G, T, bp,
-                       delta, op);
+  if (B <= 8)
+    conv_launch_bm<TA, 8>(grid, xp, n_blocks, B, C, G, T, bp, delta, op, st);
   else
-    hipLaunchKernelGGL((conv_kernel<TA, 16>), grid, dim3(256), 0, st, xp, n_blocks, B, C, G, T, bp,
-                       delta, op);
+    conv_launch_bm<TA, 16>(grid, xp, n_blocks, B, C, G, T, bp, delta, op, st);
 }
 
 hipError_t launch_conv(int act, const void *x, int n_blocks, int B, int C, int G, int T,

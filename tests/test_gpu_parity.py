@@ -129,10 +129,23 @@ def test_conv_single_tap_and_narrow_groups():
     run_conv(cfg_small(0, T=3, G=16, B=5), 2, tag="conv3")
 
 
+def test_conv_group_spans_and_long_filters():
+    """Every kernel arrangement: 12 channels per group at B = 16 (an
+    8-channel chunk spans two groups, as with 84 per group); fp32 at B = 16;
+    T = 6 and T = 16 filters; T = 9 with 3-channel groups."""
+    run_conv(cfg_small(1, C=768, G=64, T=4, B=16), 3, tag="conv12")
+    run_conv(cfg_small(0, C=256, G=8, T=4, B=16), 2, tag="convf16")
+    run_conv(cfg_small(0, C=256, G=8, T=6, B=16), 2, tag="conv6")
+    run_conv(cfg_small(1, C=128, G=16, T=16, B=16), 2, tag="conv16")
+    run_conv(cfg_small(0, C=192, G=64, T=9, B=3), 2, tag="conv9")
+
+
 def test_conv_batched_32k_tokens():
     """2048 blocks of 16 (32768 tokens, the 32k workload's token count) at
-    the Qwen-27B width, checked on every output."""
+    the Qwen-27B width, checked on every output; then 2050 blocks, whose
+    delta product ends in a ragged 32-row tile."""
     run_conv(configs.get(2), 2048, tag="convb")
+    run_conv(configs.get(2), 2050, tag="convr")
 
 
 # ---------------------------------------------------------------------------
