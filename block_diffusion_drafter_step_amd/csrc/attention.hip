@@ -24,6 +24,10 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef DFL_ATTN_NT_PART
+#define DFL_ATTN_NT_PART 0   // 1: split partials written with non-temporal stores
+#endif
+
 namespace dfl {
 
 #ifndef DFL_ATTN_WGS
@@ -279,6 +283,17 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
     const int hq = kvh * grp + wave + 4 * hh;
     const long base = ((long)hq * a.B + r16) * a.n_split + sp;
     float *po = a.part_o + base * HD;
+#if DFL_ATTN_NT_PART
+    // streamed past L2: the combine kernel reads them from memory anyway
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+      __builtin_nontemporal_store(f32x4{o[hh][dt][0], o[hh][dt][1], o[hh][dt][2], o[hh][dt][3]},
+                                  reinterpret_cast<f32x4 *>(po + 16 * dt + 4 * g));
+    if (g == 0) {
+      __builtin_nontemporal_store(m_run[hh], a.part_ml + base * 2);
+      __builtin_nontemporal_store(l_run[hh], a.part_ml + base * 2 + 1);
+    }
+#else
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -287,6 +302,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
       a.part_ml[base * 2] = m_run[hh];
       a.part_ml[base * 2 + 1] = l_run[hh];
     }
+#endif
   }
 }
 
@@ -294,111 +310,123 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
 //                  (sum_s 2^(m_s - M) l_s + 2^(m_b - M) l_b),
 // where (m_b, l_b, O_b) is the block's own B keys, scored here from Q, Kb, Vb
 // (probabilities rounded to the act type as the split kernel rounds them).
-// One workgroup per (query head, token): thread (p, q) owns dims 4q..4q+3
-// and the splits s = p, p + P, ... (P = 256 / (HD/4)); the P partial sums are
-// added in p order through LDS and the block term last, so the result is
-// bitwise reproducible.
+// One wave per (query head, token), no barriers: lane l owns dims
+// DPL*l .. DPL*l+DPL-1 (DPL = HD/64) and split l of every group of 64 splits;
+// every load of the first 64 splits and of the block is issued before the
+// first use.  Weights reach all lanes by readlane; splits are added in
+// increasing order and the block term last, so the result is bitwise
+// reproducible.
 constexpr int kMaxSplit = 1024;
 
 template <typename TA, int HD>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  constexpr int NQ = HD / 4, P = 256 / NQ, DPP = HD / 16;
-  __shared__ float wsp[kMaxSplit];
-  __shared__ float red[8];
-  __shared__ float sblk[16];
-  __shared__ float4 part[P][NQ];
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+  constexpr int DPL = HD / 64;
   const int ht = blockIdx.x;  // hq * B + t
   const int hq = ht / a.B, t = ht - hq * a.B;
   const int kvh = hq / (a.Hq / a.Hkv);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int ns = a.n_split;
   const long qld = (long)(a.Hq + 2 * a.Hkv) * HD;
   const TA *qkv = reinterpret_cast<const TA *>(a.qkv);
-
-  // block scores s_j = Q[t] . Kb[j] * scale (base 2): 16 threads per key
-  {
-    const int j = tid >> 4, q16 = tid & 15;
-    float sj = 0.f;
-    if (j < a.B) {
-      const TA *qr = qkv + (long)t * qld + (long)hq * HD + q16 * DPP;
-      const TA *kb = qkv + (long)j * qld + (long)(a.Hq + kvh) * HD + q16 * DPP;
-#pragma unroll
-      for (int e = 0; e < DPP; ++e) sj += to_f32(qr[e]) * to_f32(kb[e]);
-    }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) sj += shfl_xor(sj, o);
-    if (q16 == 0 && j < 16) sblk[j] = sj * a.scale * kLog2e;
-  }
-  float mx = -__builtin_inff();
+  const float *po = a.part_o + (long)ht * ns * HD + DPL * lane;
   const float *ml = a.part_ml + (long)ht * ns * 2;
-  for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, ml[2 * s]);
+
+  // loads: partial rows 0..63, (m, l) of split `lane`, Q, Kb[0..15], Vb[0..15]
+  float ov[64][DPL];
+  float2 mlv = make_float2(-__builtin_inff(), 0.f);
+  if (ns > 0) {
+#pragma unroll
+    for (int s = 0; s < 64; ++s)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ov[s][e] = po[(long)min(s, ns - 1) * HD + e];
+    if (lane < ns) mlv = *reinterpret_cast<const float2 *>(ml + 2 * lane);
+  }
+  float qv[DPL], kv[16][DPL], vv[16][DPL];
+  {
+    const TA *qr = qkv + (long)t * qld + (long)hq * HD + DPL * lane;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) qv[e] = to_f32(qr[e]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const TA *row = qkv + (long)min(j, a.B - 1) * qld + DPL * lane;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        kv[j][e] = to_f32(row[(long)(a.Hq + kvh) * HD + e]);
+        vv[j][e] = to_f32(row[(long)(a.Hq + a.Hkv + kvh) * HD + e]);
+      }
+    }
+  }
+
+  // block scores s_j = Q[t] . Kb[j] * scale (base 2), on every lane
+  float sb[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float x = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) x += qv[e] * kv[j][e];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += shfl_xor(x, o);
+    sb[j] = x * a.scale * kLog2e;
+  }
+  float mb = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < a.B) mb = fmaxf(mb, sb[j]);
+  float lb = 0.f, pb[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    pb[j] = j < a.B ? to_f32(from_f32<TA>(exp2f(sb[j] - mb))) : 0.f;
+    lb += pb[j];
+  }
+
+  // the global maximum over every split and the block
+  float mx = mlv.x;
+  for (int s = lane + 64; s < ns; s += 64) mx = fmaxf(mx, ml[2 * s]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  float mb = -__builtin_inff();
-  for (int j = 0; j < a.B; ++j) mb = fmaxf(mb, sblk[j]);
-  const float M = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), mb);
-  float lb = 0.f;
-  for (int j = 0; j < a.B; ++j) lb += to_f32(from_f32<TA>(exp2f(sblk[j] - mb)));
-  float lsum = 0.f;
-  for (int s = tid; s < ns; s += 256) {
-    const float m = ml[2 * s];
-    const float w = m == -__builtin_inff() ? 0.f : exp2f(m - M);
-    wsp[s] = w;
-    lsum += w * ml[2 * s + 1];
-  }
+  const float M = fmaxf(mx, mb);
+
+  // weighted sums over the splits, 64 at a time
+  float acc[DPL], lsum = 0.f;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lsum += shfl_xor(lsum, o);
-  __syncthreads();
-  if (lane == 0) red[4 + wave] = lsum;
-  __syncthreads();
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    float2 m_l = mlv;
+    if (s0 > 0) {
+      m_l = make_float2(-__builtin_inff(), 0.f);
+      if (s0 + lane < ns) m_l = *reinterpret_cast<const float2 *>(ml + 2 * (s0 + lane));
+#pragma unroll
+      for (int s = 0; s < 64; ++s)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) ov[s][e] = po[(long)min(s0 + s, ns - 1) * HD + e];
+    }
+    const float w = m_l.x == -__builtin_inff() ? 0.f : exp2f(m_l.x - M);   // zero past ns
+    float lw = w * m_l.y;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lw += shfl_xor(lw, o);
+    lsum += lw;
+#pragma unroll
+    for (int s = 0; s < 64; ++s) {
+      const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += ws * ov[s][e];
+    }
+  }
+
+  // the block's keys: O_b = sum_j p_j Vb[j], added last
   const float wb = exp2f(mb - M);
-  const float L = (red[4] + red[5]) + (red[6] + red[7]) + wb * lb;
-  const int q = tid % NQ, p = tid / NQ;
-  const float *po = a.part_o + (long)ht * ns * HD + 4 * q;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = p;
-  for (; s + 3 * P < ns; s += 4 * P) {
-    float4 v[4];
+  const float L = lsum + wb * lb;
+  float ob[DPL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const float4 *>(po + (long)(s + j * P) * HD);
+  for (int e = 0; e < DPL; ++e) {
+    ob[e] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float w = wsp[s + j * P];
-      acc.x += w * v[j].x; acc.y += w * v[j].y; acc.z += w * v[j].z; acc.w += w * v[j].w;
-    }
+    for (int j = 0; j < 16; ++j) ob[e] += pb[j] * vv[j][e];
   }
-  for (; s < ns; s += P) {
-    const float4 v = *reinterpret_cast<const float4 *>(po + (long)s * HD);
-    const float w = wsp[s];
-    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
-  }
-  part[p][q] = acc;
-  __syncthreads();
-  if (p == 0) {
-    float4 r = part[0][q];
+  TA *o = reinterpret_cast<TA *>(a.o) + (long)t * a.Hq * HD + (long)hq * HD + DPL * lane;
+  const float inv = 1.0f / L;
 #pragma unroll
-    for (int j = 1; j < P; ++j) {
-      const float4 v = part[j][q];
-      r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
-    }
-    // the block's keys: O_b = sum_j p_j Vb[j], added last
-    float4 ob = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < a.B; ++j) {
-      const float pj = to_f32(from_f32<TA>(exp2f(sblk[j] - mb)));
-      const TA *vb = qkv + (long)j * qld + (long)(a.Hq + a.Hkv + kvh) * HD + 4 * q;
-      ob.x += pj * to_f32(vb[0]); ob.y += pj * to_f32(vb[1]);
-      ob.z += pj * to_f32(vb[2]); ob.w += pj * to_f32(vb[3]);
-    }
-    r.x += wb * ob.x; r.y += wb * ob.y; r.z += wb * ob.z; r.w += wb * ob.w;
-    TA *o = reinterpret_cast<TA *>(a.o) + (long)t * a.Hq * HD + (long)hq * HD + 4 * q;
-    const float inv = 1.0f / L;
-    o[0] = from_f32<TA>(r.x * inv);
-    o[1] = from_f32<TA>(r.y * inv);
-    o[2] = from_f32<TA>(r.z * inv);
-    o[3] = from_f32<TA>(r.w * inv);
-  }
+  for (int e = 0; e < DPL; ++e) o[e] = from_f32<TA>((acc[e] + wb * ob[e]) * inv);
 }
 
 // the cached context keys are split over about DFL_ATTN_WGS workgroups in
@@ -453,7 +481,7 @@ static void attn_launch_t(const AttnArgs &a, hipStream_t st) {
     if (a.Hq / a.Hkv <= 4) attn_split_go<TA, HD, 1>(a, st);
     else attn_split_go<TA, HD, 2>(a, st);
   }
-  hipLaunchKernelGGL((attn_combine_kernel<TA, HD>), dim3(a.Hq * a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_combine_kernel<TA, HD>), dim3(a.Hq * a.B), dim3(64), 0, st, a);
 }
 
 hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st) {

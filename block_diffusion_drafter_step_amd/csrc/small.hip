@@ -153,6 +153,79 @@ __global__ __launch_bounds__(256) void conv_kernel(const TA *__restrict__ x, int
   }
 }
 
+// Few blocks (one draft block per step): one thread per (position, 8
+// channels), so a single block still spreads over B*C/8 threads; the T input
+// rows a position needs are re-read from cache by neighbouring positions.
+template <typename TA, int TM, int DM>
+__global__ __launch_bounds__(256) void conv_pos_kernel(const TA *__restrict__ x, int n_blocks, int B,
+                                                       int C, int G, int T,
+                                                       const TA *__restrict__ base,
+                                                       const float *__restrict__ delta,
+                                                       TA *__restrict__ out) {
+  const int nch = C >> 3;
+  const long id = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = id / nch;   // blk * B + i
+  if (row >= (long)n_blocks * B) return;
+  const int c = (int)(id - row * nch) * 8;
+  const int i = (int)(row % B);
+  const int cpg = C / G;
+  int gj[8];
+  {
+    int g = c / cpg, next = (g + 1) * cpg;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (c + j >= next) {
+        ++g;
+        next += cpg;
+      }
+      gj[j] = g;
+    }
+  }
+  const int TG = T * G;
+  const float *dr = delta + row * (long)TG;
+  Frag<TA> xr[TM], bv[TM];
+  float dA[TM], dB[DM == 2 ? TM : 1];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    const int tt = min(t, min(T - 1, i));   // taps past the block start or T read a valid row, unused
+    xr[t] = load_frag(x + (row - tt) * (long)C + c);
+    bv[t] = load_frag(base + (long)min(t, T - 1) * C + c);
+    if constexpr (DM != 0) {
+      dA[t] = dr[min(t, T - 1) * G + gj[0]];
+      if constexpr (DM == 2) dB[t] = dr[min(t, T - 1) * G + gj[7]];
+    }
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    if (t < T && t <= i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float dv;
+        if constexpr (DM == 1)
+          dv = dA[t];
+        else if constexpr (DM == 2)
+          dv = gj[j] == gj[0] ? dA[t] : dB[t];
+        else
+          dv = dr[t * G + gj[j]];
+        acc[j] += (to_f32(bv[t].v[j]) + dv) * to_f32(xr[t].v[j]);
+      }
+    }
+  }
+  Frag<TA> o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o.v[j] = from_f32<TA>(acc[j]);
+  store_frag(out + row * (long)C + c, o);
+}
+
+template <typename TA, int TM, int DM>
+static void conv_pos_go(const TA *x, int n_blocks, int B, int C, int G, int T, const TA *base,
+                        const float *delta, TA *out, hipStream_t st) {
+  const long threads = (long)n_blocks * B * (C / 8);
+  hipLaunchKernelGGL((conv_pos_kernel<TA, TM, DM>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                     0, st, x, n_blocks, B, C, G, T, base, delta, out);
+}
+
 template <typename TA, int TM, int DM, int BM>
 static void conv_go(dim3 grid, const TA *x, int n_blocks, int B, int C, int G, int T, const TA *base,
                     const float *delta, TA *out, hipStream_t st) {
@@ -184,6 +257,18 @@ static void conv_launch_t(const void *x, int n_blocks, int B, int C, int G, int 
   const TA *xp = reinterpret_cast<const TA *>(x);
   const TA *bp = reinterpret_cast<const TA *>(base);
   TA *op = reinterpret_cast<TA *>(out);
+  const int cpg = C / G;
+  if (grid.x < 64 && T <= 8) {   // too few workgroups to walk whole blocks: spread the positions
+    if (T <= 4 && cpg % 8 == 0)
+      conv_pos_go<TA, 4, 1>(xp, n_blocks, B, C, G, T, bp, delta, op, st);
+    else if (T <= 4 && cpg >= 8)
+      conv_pos_go<TA, 4, 2>(xp, n_blocks, B, C, G, T, bp, delta, op, st);
+    else if (T <= 4)
+      conv_pos_go<TA, 4, 0>(xp, n_blocks, B, C, G, T, bp, delta, op, st);
+    else
+      conv_pos_go<TA, 8, 0>(xp, n_blocks, B, C, G, T, bp, delta, op, st);
+    return;
+  }
   if (B <= 8)
     conv_launch_bm<TA, 8>(grid, xp, n_blocks, B, C, G, T, bp, delta, op, st);
   else

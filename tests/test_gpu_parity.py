@@ -117,7 +117,7 @@ def run_conv(cfg, nb, tag="conv"):
     assert_close(f64(out), ref["u"], cfg.act, f"{cfg.name} conv u (n_blocks={nb})")
 
 
-@pytest.mark.parametrize("ci,nb", [(0, 1), (0, 3), (1, 1), (4, 1), (1, 64), (0, 2048)])
+@pytest.mark.parametrize("ci,nb", [(0, 1), (0, 3), (1, 1), (4, 1), (1, 64), (4, 64), (0, 2048)])
 def test_conv(ci, nb):
     run_conv(configs.get(ci), nb)
 
@@ -130,14 +130,19 @@ def test_conv_single_tap_and_narrow_groups():
 
 
 def test_conv_group_spans_and_long_filters():
-    """Every kernel arrangement: 12 channels per group at B = 16 (an
+    """Every kernel arrangement, with few blocks (one thread per position)
+    and with many (one thread per block): 12 channels per group at B = 16 (an
     8-channel chunk spans two groups, as with 84 per group); fp32 at B = 16;
-    T = 6 and T = 16 filters; T = 9 with 3-channel groups."""
+    T = 6 and T = 16 filters; T = 9 and T = 2 with 3-channel groups."""
     run_conv(cfg_small(1, C=768, G=64, T=4, B=16), 3, tag="conv12")
     run_conv(cfg_small(0, C=256, G=8, T=4, B=16), 2, tag="convf16")
     run_conv(cfg_small(0, C=256, G=8, T=6, B=16), 2, tag="conv6")
     run_conv(cfg_small(1, C=128, G=16, T=16, B=16), 2, tag="conv16")
     run_conv(cfg_small(0, C=192, G=64, T=9, B=3), 2, tag="conv9")
+    # the same arrangements over enough blocks for the per-block kernel
+    run_conv(cfg_small(1, C=768, G=64, T=4, B=16), 200, tag="conv12b")
+    run_conv(cfg_small(1, C=384, G=128, T=2, B=8), 400, tag="conv3b")
+    run_conv(cfg_small(0, C=256, G=8, T=6, B=16), 600, tag="conv6b")
 
 
 def test_conv_batched_32k_tokens():
@@ -189,6 +194,13 @@ def test_attn_tiny_no_residual_short_block():
 @pytest.mark.parametrize("ci,n_ctx", [(1, 1024), (1, 1000), (2, 32768), (3, 65536 + 16), (4, 32768)])
 def test_attn_full(ci, n_ctx):
     run_attn(configs.get(ci), n_ctx)
+
+
+def test_attn_many_splits():
+    """More than 64 splits per KV head (two KV heads over a long context): the
+    combine kernel's multi-group path, with a partial last group."""
+    run_attn(cfg_small(0, n_ctx=5000), 5000)                           # fp32, hd 64: 157 splits
+    run_attn(cfg_small(1, Hq=8, Hkv=2, n_ctx=8000), 8000)              # bf16, hd 128: 250 splits
 
 
 def test_attn_deterministic():
