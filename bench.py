@@ -121,7 +121,8 @@ def main():
         n = cfg.n_ctx
         hid = [randn(n, cfg.d_t) for _ in range(cfg.L_t)]
         ws = D.workspace(D.dflash_inject_workspace(cfg.L_t, n, cfg.d_t, cfg.d, cfg.kv, cfg.act))
-        D.dflash_inject(hid, W.fc, None, cfg.eps, W.wk, W.wv, cache, 0, ws)
+        for _ in range(2):   # untimed: the first calls also ramp the clocks up
+            D.dflash_inject(hid, W.fc, None, cfg.eps, W.wk, W.wv, cache, 0, ws)
         torch.cuda.synchronize()
         times = []
         for _ in range(args.prefill_reps):

@@ -170,6 +170,11 @@ size_t inject_ws(int32_t n_layers, int64_t n, int32_t d_t, int32_t d, int32_t kv
   c.take(std::max(gemm_partial_bytes((int)n, d, n_layers * d_t), gemm_partial_bytes((int)n, 2 * kv, d)));
   c.take((size_t)n * d * 4);  // y
   c.take((size_t)n * d * 4);  // z
+  if (n >= kQ8ExpandMinM) {   // bf16 expansions of Q8_0 fc, Wk and Wv
+    c.take((size_t)d * n_layers * d_t * 2);
+    c.take((size_t)kv * d * 2);
+    c.take((size_t)kv * d * 2);
+  }
   return c.off;
 }
 
@@ -318,12 +323,28 @@ dflash_status dflash_inject(const void *const *layer_hidden, int32_t n_layers, i
   float *y = (float *)c.take((size_t)n * d * 4);
   void *z = c.take((size_t)n * d * 4);
 
+  // many rows: Q8_0 weights are expanded once to bf16 in the workspace
+  dflash_weight fc_e = *fc, wk_e = *wk, wv_e = *wv;
+  hipError_t e = hipSuccess;
+  if (n >= kQ8ExpandMinM) {
+    dflash_weight *ex[3] = {&fc_e, &wk_e, &wv_e};
+    for (dflash_weight *w : ex) {
+      void *buf = c.take((size_t)w->rows * w->cols * 2);
+      if (w->dtype != DFLASH_Q8_0) continue;
+      e = launch_expand_q8(w->data, w->scales, w->rows, (int)w->cols, buf, st);
+      if (e != hipSuccess) return launched(e, "Q8_0 expansion");
+      w->dtype = DFLASH_BF16;
+      w->data = buf;
+      w->scales = nullptr;
+    }
+  }
+
   ASrc A;
   memset(&A, 0, sizeof A);
   for (int l = 0; l < n_layers; ++l) A.ptr[l] = layer_hidden[l];
   A.n_src = n_layers;
   A.k_per_src = d_t;
-  hipError_t e = gemm(act, wkind_of(fc), A, n, wset({fc}), part, c.counters, out_f32(y, d), st);
+  e = gemm(act, wkind_of(&fc_e), A, n, wset({&fc_e}), part, c.counters, out_f32(y, d), st);
   if (e != hipSuccess) return launched(e, "fc");
   e = launch_rmsnorm(act, y, n, (int)d, gamma, eps, z, st);
   if (e != hipSuccess) return launched(e, "rmsnorm");
@@ -336,7 +357,7 @@ dflash_status dflash_inject(const void *const *layer_hidden, int32_t n_layers, i
   oc.split = (int)kv;
   oc.cap = cache->capacity;
   oc.pos0 = pos0;
-  e = gemm(act, wkind_of(wk), asrc1(z, (int)d), n, wset({wk, wv}), part, c.counters, oc, st);
+  e = gemm(act, wkind_of(&wk_e), asrc1(z, (int)d), n, wset({&wk_e, &wv_e}), part, c.counters, oc, st);
   return launched(e, "wk/wv");
 }
 

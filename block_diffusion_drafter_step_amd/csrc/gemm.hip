@@ -858,6 +858,9 @@ __global__ __launch_bounds__(256) void dma_gemm_kernel(ASrc A, int M, WSet W, Ou
 #define DFL_DMA8_STAGES 4
 #endif
 constexpr int D8STAGES = DFL_DMA8_STAGES;
+#ifndef DFL_DMA8_SCHED
+#define DFL_DMA8_SCHED 1   // 1: loads and LDS reads scheduled between a k-step's MFMAs
+#endif
 
 template <int TBM>
 constexpr int d8_stage_bytes() { return (TBM + DBN) * DBK * 2; }
@@ -903,13 +906,17 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
   // next k-step to issue and its activation source
   int ki = 0, src_i = 0, kl = 0;
   const bf16 *src = reinterpret_cast<const bf16 *>(pick(A.ptr, 0));
-  auto issue = [&](char *stage) {
+  // the loads of one stage (no branches, so they share a basic block with
+  // the k-step's MFMAs and can be scheduled between them)
+  auto issue_loads = [&](char *stage) {
 #pragma unroll
     for (int j = 0; j < NA; ++j)
       dma16(src + kl + a_off[j], (lds_void *)(stage + (NA * wave + j) * 1024));
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       dma16(w_row[j] + ki * DBK, (lds_void *)(stage + TBM * DBK * 2 + (2 * wave + j) * 1024));
+  };
+  auto advance = [&]() {
     if (ki + 1 < nk) {   // past the last k-step the same one is issued again
       ++ki;
       kl += DBK;
@@ -919,6 +926,10 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
         src = reinterpret_cast<const bf16 *>(pick(A.ptr, src_i));
       }
     }
+  };
+  auto issue = [&](char *stage) {
+    issue_loads(stage);
+    advance();
   };
 
   f32x4 acc[MI][4];
@@ -960,9 +971,30 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
                   Frag<bf16> (&na)[MI], Frag<bf16> (&nb)[4]) {
     wait_vm<LPS * (D8STAGES - 3)>();   // this wave's loads of stage kt+1 have landed
     ring_barrier();                    // ... everyone's; stage kt-1 is no longer read
+#if DFL_DMA8_SCHED
+    // one basic block: the stage loads and the fragment reads of kt+1 (the
+    // last k-step re-reads its own stage) issue between the MFMAs of kt,
+    // so the matrix pipe is fed right after the barrier
+    issue_loads(smem_dma8 + ((kt + D8STAGES - 1) % D8STAGES) * SB);
+    read_frags(min(kt + 1, nk - 1), na, nb);
+    mmas(fa, fb);
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global load
+    }
+#pragma unroll
+    for (int i = 0; i < MI + 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * MI - LPS - MI - 4, 0);
+    advance();
+#else
     issue(smem_dma8 + ((kt + D8STAGES - 1) % D8STAGES) * SB);
     if (kt + 1 < nk) read_frags(kt + 1, na, nb);
     mmas(fa, fb);
+#endif
   };
   Frag<bf16> fa0[MI], fb0[4], fa1[MI], fb1[4];
   wait_vm<LPS * (D8STAGES - 2)>();
@@ -1028,6 +1060,36 @@ static void dma_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, 
                                  // 3: 256-tile direct-to-LDS on 8 waves
 #endif
 
+
+// Q8_0 -> bf16 expansion: one thread per 32-code block (two 16-byte code
+// loads, one scale, four 16-byte stores), consecutive threads on consecutive
+// blocks of a row, so reads and writes are both contiguous.
+__global__ __launch_bounds__(256) void expand_q8_kernel(const int8_t *__restrict__ codes,
+                                                        const uint16_t *__restrict__ scales,
+                                                        long n_blocks, bf16 *__restrict__ out) {
+  const long b = (long)blockIdx.x * 256 + threadIdx.x;
+  if (b >= n_blocks) return;
+  const uint4 *src = reinterpret_cast<const uint4 *>(codes + 32 * b);
+  const uint4 c0 = src[0], c1 = src[1];
+  const float s = half_bits_to_f32(scales[b]);
+  bf16x8 *dst = reinterpret_cast<bf16x8 *>(out + 32 * b);
+  dst[0] = dequant8(make_uint2(c0.x, c0.y), s).v;
+  dst[1] = dequant8(make_uint2(c0.z, c0.w), s).v;
+  dst[2] = dequant8(make_uint2(c1.x, c1.y), s).v;
+  dst[3] = dequant8(make_uint2(c1.z, c1.w), s).v;
+}
+
+hipError_t launch_expand_q8(const void *codes, const void *scales, long rows, int cols, void *out,
+                            hipStream_t st) {
+  // blocks run along a row and rows are contiguous, so block b of the whole
+  // weight has its codes at 32 b and its scale at index b of [rows][cols/32]
+  const long nb = rows * (long)(cols / 32);
+  if (nb > 0)
+    hipLaunchKernelGGL(expand_q8_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const int8_t *>(codes), static_cast<const uint16_t *>(scales), nb,
+                       static_cast<bf16 *>(out));
+  return hipGetLastError();
+}
 
 hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet &W,
                             const OutSpec &out, hipStream_t st) {

@@ -78,6 +78,15 @@ hipError_t launch_skinny_gemm(int act, int wkind, const ASrc &X, int M, const WS
 hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet &W,
                             const OutSpec &out, hipStream_t st);
 
+// Products with at least this many activation rows expand a Q8_0 weight once
+// into bf16 (the same values the in-kernel dequantisation produces) and run
+// the bf16 tile GEMM: every 256-row tile would otherwise decode the whole
+// weight again.
+constexpr int kQ8ExpandMinM = 4096;
+// out[r][c] = bf16_rne(fp32(scales[r][c/32]) * codes[r][c]), cols % 32 == 0
+hipError_t launch_expand_q8(const void *codes, const void *scales, long rows, int cols, void *out,
+                            hipStream_t st);
+
 // ---- injection -----------------------------------------------------------------
 // z[t] = round(y[t] / sqrt(mean(y[t]^2) + eps) * gamma), y fp32 [n][d].
 hipError_t launch_rmsnorm(int act, const float *y, int n, int d, const void *gamma, float eps,

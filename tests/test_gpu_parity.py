@@ -100,6 +100,14 @@ def test_inject_prefill_32k_sampled(ci):
     run_inject(cfg, cfg.n_ctx, 0, rows=rows)
 
 
+@pytest.mark.parametrize("n", [4095, 4133])
+def test_inject_q8_0_around_expansion_threshold(n):
+    """Q8_0 fc / Wk / Wv on every row just below 4096 tokens (per-tile
+    dequantisation) and just above (one bf16 expansion per call), ragged tail."""
+    cfg = cfg_small(4, d=512, d_t=256, L_t=3, Hkv=2, capacity=4224)
+    run_inject(cfg, n, 17)
+
+
 # ---------------------------------------------------------------------------
 # (2) conv
 # ---------------------------------------------------------------------------
