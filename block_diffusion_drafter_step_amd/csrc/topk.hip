@@ -203,7 +203,10 @@ __global__ __launch_bounds__(256) void lmhead_topk_kernel(TopkArgs a) {
 // tokens hit 16 different bank groups.
 // ---------------------------------------------------------------------------
 #ifndef DFL_LMH_DEPTH
-#define DFL_LMH_DEPTH 1
+#define DFL_LMH_DEPTH 1      // chunks in flight per wave, bf16 / fp32 heads
+#endif
+#ifndef DFL_LMH_DEPTH_Q8
+#define DFL_LMH_DEPTH_Q8 2   // ... Q8_0 heads (half the bytes per chunk)
 #endif
 
 template <typename TA, int WK>
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(NW * 64) void lmhead_topk_lds_kernel(TopkArgs a) {
   }
   float m = -__builtin_inff(), ssum = 0.f;
 
-  constexpr int D = DFL_LMH_DEPTH;
+  constexpr int D = WK == W_Q8_0 ? DFL_LMH_DEPTH_Q8 : DFL_LMH_DEPTH;
   LmStage<TA, WK> st[D];
   // load cursor (tile lt, chunk lk); it stops at the wave's last chunk, so the
   // refills past the end re-read that chunk (a cache hit) instead of branching
@@ -322,22 +325,28 @@ __global__ __launch_bounds__(NW * 64) void lmhead_topk_lds_kernel(TopkArgs a) {
   long ct = t_beg;
   int ck = 0;
   f32x4 acc = zero4();
-  for (int c = 0; c < total; c += D) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      if (c + s < total) {
-        lm_stage_mma(st[s], hs, d, ck * 128, g, tok, acc);
-        lm_stage_load(st[s], a.w, a.scales, min(lt * 16 + r16, V - 1), d, lk * 128, g);
-        advance();
-        if (++ck == nck) {
-          fold_tile<KM>(acc, ct * 16, V, g, m, ssum, tv, ti);
-          acc = zero4();
-          ck = 0;
-          ++ct;
-        }
-      }
+  auto chunk = [&](LmStage<TA, WK> &sg) {
+    lm_stage_mma(sg, hs, d, ck * 128, g, tok, acc);
+    lm_stage_load(sg, a.w, a.scales, min(lt * 16 + r16, V - 1), d, lk * 128, g);
+    advance();
+    if (++ck == nck) {
+      fold_tile<KM>(acc, ct * 16, V, g, m, ssum, tv, ti);
+      acc = zero4();
+      ck = 0;
+      ++ct;
     }
+  };
+  // whole rings without guards (a guarded chunk would leave the compiler
+  // unsure how many loads are in flight, and it would wait for all of them),
+  // then the last total % D chunks
+  int c = 0;
+  for (; c + D <= total; c += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) chunk(st[s]);
   }
+#pragma unroll
+  for (int s = 0; s < D - 1; ++s)
+    if (c + s < total) chunk(st[s]);
   __syncthreads();   // every wave is done with hs: reuse the LDS for the merge
   float *lv = reinterpret_cast<float *>(smem);
   int *li = reinterpret_cast<int *>(lv + NW * 64 * KM);
