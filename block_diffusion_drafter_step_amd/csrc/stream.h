@@ -32,19 +32,26 @@ namespace dfl {
 // Q8_0 dequantisation of 8 codes held in two dwords: value = bf16(fp32(s) * q).
 // (q + 128) comes from v_cvt_f32_ubyte on the sign-flipped byte, and
 // fma(q + 128, s, -128 s) = q s exactly (q s needs at most 19 significant bits),
-// so the single rounding is the bf16 one.
+// so the single rounding is the bf16 one, two values per v_cvt_pk_bf16_f32.
+typedef float dq_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 dq_bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t dq_pair(uint32_t x, int sh, float s, float c) {
+  const dq_f32x2 v = {fmaf((float)((x >> sh) & 0xffu), s, c),
+                      fmaf((float)((x >> (sh + 8)) & 0xffu), s, c)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, dq_bf16x2));
+}
+
 __device__ __forceinline__ Frag<bf16> dq8(uint32_t lo, uint32_t hi, float s) {
   const uint32_t a = lo ^ 0x80808080u, b = hi ^ 0x80808080u;
   const float c = -128.0f * s;
+  u32x4 r;
+  r[0] = dq_pair(a, 0, s, c);
+  r[1] = dq_pair(a, 16, s, c);
+  r[2] = dq_pair(b, 0, s, c);
+  r[3] = dq_pair(b, 16, s, c);
   Frag<bf16> f;
-  f.v[0] = (bf16)fmaf((float)(a & 0xffu), s, c);
-  f.v[1] = (bf16)fmaf((float)((a >> 8) & 0xffu), s, c);
-  f.v[2] = (bf16)fmaf((float)((a >> 16) & 0xffu), s, c);
-  f.v[3] = (bf16)fmaf((float)(a >> 24), s, c);
-  f.v[4] = (bf16)fmaf((float)(b & 0xffu), s, c);
-  f.v[5] = (bf16)fmaf((float)((b >> 8) & 0xffu), s, c);
-  f.v[6] = (bf16)fmaf((float)((b >> 16) & 0xffu), s, c);
-  f.v[7] = (bf16)fmaf((float)(b >> 24), s, c);
+  f.v = __builtin_bit_cast(bf16x8, r);
   return f;
 }
 

@@ -205,6 +205,9 @@ __global__ __launch_bounds__(256) void lmhead_topk_kernel(TopkArgs a) {
 #ifndef DFL_LMH_DEPTH
 #define DFL_LMH_DEPTH 1      // chunks in flight per wave, bf16 / fp32 heads
 #endif
+#ifndef DFL_LMH_SCALE_X4
+#define DFL_LMH_SCALE_X4 1   // Q8_0: one 8-byte scale load per chunk instead of two 2-byte ones
+#endif
 #ifndef DFL_LMH_DEPTH_Q8
 #define DFL_LMH_DEPTH_Q8 2   // ... Q8_0 heads (half the bytes per chunk)
 #endif
@@ -225,21 +228,44 @@ __device__ __forceinline__ int hsw(int t, int k, int d) {
   return t * d + ((ch ^ (t & mask)) << 3) + (k & 7);
 }
 
+// A lane's weight row for the load cursor: values (or codes) and scales.
+struct LmRow {
+  const char *w;
+  const uint16_t *s;
+};
+
+template <typename TA, int WK>
+__device__ __forceinline__ LmRow lm_row(const void *w, const void *scales, long row, int d) {
+  LmRow r;
+  if constexpr (WK == W_Q8_0) {
+    r.w = reinterpret_cast<const char *>(w) + row * d;
+    r.s = reinterpret_cast<const uint16_t *>(scales) + row * (d >> 5);
+  } else {
+    r.w = reinterpret_cast<const char *>(w) + row * d * (long)sizeof(TA);
+    r.s = nullptr;
+  }
+  return r;
+}
+
 // (d % 128 == 0 on this path: every chunk is whole, so no load is guarded)
 template <typename TA, int WK>
-__device__ __forceinline__ void lm_stage_load(LmStage<TA, WK> &s, const void *w, const void *scales,
-                                              long row, int d, int k, int g) {
+__device__ __forceinline__ void lm_stage_load(LmStage<TA, WK> &s, const LmRow &r, int k, int g) {
   if constexpr (WK == W_Q8_0) {
-    const int8_t *p = reinterpret_cast<const int8_t *>(w) + row * d;
-    const uint16_t *sp = reinterpret_cast<const uint16_t *>(scales) + row * (d >> 5);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int off = k + 64 * m + 16 * g;
-      s.c[m] = *reinterpret_cast<const uint4 *>(p + off);
-      s.sc[m] = half_bits_to_f32(sp[off >> 5]);
-    }
+    for (int m = 0; m < 2; ++m) s.c[m] = *reinterpret_cast<const uint4 *>(r.w + k + 64 * m + 16 * g);
+#if DFL_LMH_SCALE_X4
+    // the chunk's four block scales in one 8-byte load (a row's scales are
+    // 8-byte aligned: d % 128 == 0); codes k + 64 m + 16 g use block 2 m + g / 2
+    const uint2 q = *reinterpret_cast<const uint2 *>(r.s + (k >> 5));
+    const uint32_t w0 = g < 2 ? q.x : q.x >> 16, w1 = g < 2 ? q.y : q.y >> 16;
+    s.sc[0] = half_bits_to_f32((uint16_t)w0);
+    s.sc[1] = half_bits_to_f32((uint16_t)w1);
+#else
+#pragma unroll
+    for (int m = 0; m < 2; ++m) s.sc[m] = half_bits_to_f32(r.s[(k + 64 * m + 16 * g) >> 5]);
+#endif
   } else {
-    const TA *p = reinterpret_cast<const TA *>(w) + row * d;
+    const TA *p = reinterpret_cast<const TA *>(r.w);
 #pragma unroll
     for (int j = 0; j < 4; ++j) s.a[j] = load_frag(p + k + 32 * j + 8 * g);
   }
@@ -309,17 +335,20 @@ __global__ __launch_bounds__(NW * 64) void lmhead_topk_lds_kernel(TopkArgs a) {
   const long t_last = t_end > t_beg ? t_end - 1 : t_beg;
   long lt = t_beg;
   int lk = 0;
+  // the cursor's row pointers change once per tile, not per chunk
+  LmRow lrow = lm_row<TA, WK>(a.w, a.scales, min(lt * 16 + r16, V - 1), d);
   auto advance = [&]() {
     if (lk + 1 < nck) {
       ++lk;
     } else if (lt < t_last) {
       lk = 0;
       ++lt;
+      lrow = lm_row<TA, WK>(a.w, a.scales, min(lt * 16 + r16, V - 1), d);
     }
   };
 #pragma unroll
   for (int s = 0; s < D; ++s) {
-    lm_stage_load(st[s], a.w, a.scales, min(lt * 16 + r16, V - 1), d, lk * 128, g);
+    lm_stage_load(st[s], lrow, lk * 128, g);
     advance();
   }
   long ct = t_beg;
@@ -327,7 +356,7 @@ __global__ __launch_bounds__(NW * 64) void lmhead_topk_lds_kernel(TopkArgs a) {
   f32x4 acc = zero4();
   auto chunk = [&](LmStage<TA, WK> &sg) {
     lm_stage_mma(sg, hs, d, ck * 128, g, tok, acc);
-    lm_stage_load(sg, a.w, a.scales, min(lt * 16 + r16, V - 1), d, lk * 128, g);
+    lm_stage_load(sg, lrow, lk * 128, g);
     advance();
     if (++ck == nck) {
       fold_tile<KM>(acc, ct * 16, V, g, m, ssum, tv, ti);
