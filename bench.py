@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the batched-conv, per-kernel and streaming-ceiling measurements "
                          "(for runs under an external profiler)")
+    ap.add_argument("--inject-sweep", action="store_true",
+                    help="only time dflash_inject for 1..64 stashed blocks of B accepted tokens "
+                         "(deferred, batched injection) and print that sweep")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -108,8 +111,12 @@ def main():
         return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(adt)
 
     host = synth.Workload(cfg)
-    W = pipeline.DeviceWeights(host, drop_host=args.no_cpu)
+    W = pipeline.DeviceWeights(host, drop_host=args.no_cpu or args.inject_sweep)
     cache = pipeline.new_cache(cfg)
+    if args.inject_sweep:
+        print(json.dumps({"workload": cfg.name, "inject_sweep": inject_sweep(cfg, W, cache, randn)}),
+              flush=True)
+        return
     prefill = None
     if decode64:
         # long-context decode: the cache already holds prefill_kv seeded rows
@@ -252,6 +259,43 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, host, int(ctx_mean), inj_n)
     print(json.dumps(out), flush=True)
+
+
+def inject_sweep(cfg, W, cache, randn, blocks=(1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128)):
+    """dflash_inject of 16 k rows: the accepted tokens of k blocks stashed and
+    injected at once (deferred injection), k up to 64 and past it.  Each size
+    is timed with HIP events on the current stream (median of 5 after 2
+    untimed calls).  Bytes: features + fc + Wk + Wv + cache rows; FLOPs:
+    fc + Wk + Wv."""
+    import numpy as np
+    import torch
+    from block_diffusion_drafter_step_amd import dflash as D, workmodel
+    res = []
+    for k in blocks:
+        n = cfg.B * k
+        hid = [randn(n, cfg.d_t) for _ in range(cfg.L_t)]
+        ws = D.workspace(D.dflash_inject_workspace(cfg.L_t, n, cfg.d_t, cfg.d, cfg.kv, cfg.act))
+        for _ in range(2):
+            D.dflash_inject(hid, W.fc, None, cfg.eps, W.wk, W.wv, cache, 0, ws)
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            D.dflash_inject(hid, W.fc, None, cfg.eps, W.wk, W.wv, cache, 0, ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = float(np.median(ts))
+        by = workmodel.inject_bytes(cfg, n)
+        fl = workmodel.inject_flops(n, cfg.L_t, cfg.d_t, cfg.d, cfg.kv)
+        # the roofline is whichever of HBM and MFMA takes longer for these bytes and flops
+        t_roof = max(by / (HBM_PEAK_GBS * 1e9), fl / (MFMA_BF16_PEAK_TFS * 1e12))
+        res.append({"blocks": k, "tokens": n, "us": round(t * 1e6, 1), "us_per_token": round(t * 1e6 / n, 3),
+                    "gbs": round(by / t / 1e9, 1), "tflops": round(fl / t / 1e12, 1),
+                    "roofline_us": round(t_roof * 1e6, 1), "frac_of_roofline": round(t_roof / t, 4)})
+        del hid, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def conv_batched(cfg, W, randn, tokens=32768, reps=20):

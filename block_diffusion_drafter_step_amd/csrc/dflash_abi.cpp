@@ -149,11 +149,11 @@ OutSpec out_act(void *p, long ld, const void *resid, long ld_resid) {
 hipError_t gemm(int act, int wkind, const ASrc &A, int M, const WSet &W, float *part, unsigned *cnt,
                 const OutSpec &o, hipStream_t st) {
   if (M <= kSkinnyMaxM) return launch_skinny_gemm(act, wkind, A, M, W, part, cnt, o, st);
-  return launch_tile_gemm(act, wkind, A, M, W, o, st);
+  return launch_tile_gemm(act, wkind, A, M, W, o, part, st);
 }
 
 size_t gemm_partial_bytes(int M, int N, int K) {
-  return M <= kSkinnyMaxM ? skinny_partial_floats(N, K) * sizeof(float) : 0;
+  return (M <= kSkinnyMaxM ? skinny_partial_floats(N, K) : tile_partial_floats(M, N, K)) * sizeof(float);
 }
 
 constexpr int64_t kMaxRows = (int64_t)1 << 26;

@@ -439,8 +439,11 @@ struct TileLoader {
   }
 };
 
-template <typename TA, int WK, int OM>
-__global__ __launch_bounds__(256) void tile_gemm_kernel(ASrc A, int M, WSet W, OutSpec o) {
+// SPLIT: workgroup z covers k-tiles [z kc, (z + 1) kc) (kc in elements) and
+// writes fp32 partials part[z][m][n] for tile_reduce_kernel instead of outputs.
+template <typename TA, int WK, int OM, bool SPLIT>
+__global__ __launch_bounds__(256) void tile_gemm_kernel(ASrc A, int M, WSet W, OutSpec o, int kc,
+                                                        float *__restrict__ part) {
   using C = TileCfg<TA>;
   static_assert(WK == W_SAME || C::BK == 64, "Q8_0 tiles are bf16");
   // Q8_0 loads 8 codes per chunk, so a Q8_0 tile covers 8 * CPR = 64 k as well
@@ -453,7 +456,11 @@ __global__ __launch_bounds__(256) void tile_gemm_kernel(ASrc A, int M, WSet W, O
   const int wm = wave >> 1, wn = wave & 1;
   const int n0 = blockIdx.x * TBN, m0 = blockIdx.y * TBM;
   const int K = W.K;
-  const int nk = K / C::BK;
+  int kt0 = 0, nk = K / C::BK;
+  if constexpr (SPLIT) {
+    kt0 = blockIdx.z * (kc / C::BK);
+    nk = min(nk, kt0 + kc / C::BK);
+  }
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -462,12 +469,12 @@ __global__ __launch_bounds__(256) void tile_gemm_kernel(ASrc A, int M, WSet W, O
     for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
 
   TileLoader<TA, WK> ld;
-  ld.load(A, M, W, m0, n0, 0, tid);
+  ld.load(A, M, W, m0, n0, kt0 * C::BK, tid);
   ld.store(As[0], Ws[0], tid);
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
+  for (int kt = kt0; kt < nk; ++kt) {
+    const int cur = (kt - kt0) & 1;
     // prefetch the next k-tile (the last iteration re-reads its own tile, so
     // the loop body has no branches and the staging registers stay registers)
     ld.load(A, M, W, m0, n0, min(kt + 1, nk - 1) * C::BK, tid);
@@ -501,20 +508,78 @@ __global__ __launch_bounds__(256) void tile_gemm_kernel(ASrc A, int M, WSet W, O
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = m0 + wm * 64 + 16 * i + 4 * g + v;
-        if (m < M) store_out_m<TA, OM>(o, m, n, acc[i][j][v]);
+        if (m < M) {
+          if constexpr (SPLIT)
+            part[((long)blockIdx.z * M + m) * W.n_total + n] = acc[i][j][v];
+          else
+            store_out_m<TA, OM>(o, m, n, acc[i][j][v]);
+        }
       }
     }
 }
 
+// out[m][n] from the partials of tile_gemm_kernel<SPLIT>, summed in k-piece
+// order (bitwise reproducible); one thread per output element.
+template <typename TA, int OM>
+__global__ __launch_bounds__(256) void tile_reduce_kernel(const float *__restrict__ part, int S, int M,
+                                                          int N, OutSpec o) {
+  const long id = (long)blockIdx.x * 256 + threadIdx.x;
+  const long mn = (long)M * N;
+  if (id >= mn) return;
+  float v = 0.f;
+  for (int z = 0; z < S; ++z) v += part[(long)z * mn + id];
+  const long m = id / N;
+  store_out_m<TA, OM>(o, m, id - m * N, v);
+}
+
+// Split-K plan of the 128 x 128 tile GEMM.  With few rows (a batched
+// injection of a few blocks) its grid covers a fraction of the CUs; below
+// kTileSplitTarget workgroups the k-range is cut into S pieces of whole
+// 64-wide k-steps (at least 4 each, at most 64 pieces).  Depends only on the
+// shapes, so the workspace query and the launch agree.
+constexpr int kTileSplitTarget = 512;
+int tile_split_plan(int M, int N, int K, int *kc) {
+  const long tiles = (long)((N + TBN - 1) / TBN) * ((M + TBM - 1) / TBM);
+  const int nk = K / 64;
+  int S = 1;
+  if (tiles < kTileSplitTarget) S = (int)((kTileSplitTarget + tiles - 1) / tiles);
+  S = std::min(S, std::max(1, nk / 4));
+  S = std::min(S, 64);
+  const int kc64 = (nk + S - 1) / S;
+  S = (nk + kc64 - 1) / kc64;
+  *kc = kc64 * 64;
+  return S;
+}
+
+size_t tile_partial_floats(int M, int N, int K) {
+  int kc;
+  const int S = tile_split_plan(M, N, K, &kc);
+  return S > 1 ? (size_t)S * M * N : 0;
+}
+
+template <typename TA, int WK, int OM>
+static void tile_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part, hipStream_t st) {
+  int kc = 0;
+  const int S = part && W.K % 64 == 0 ? tile_split_plan(M, W.n_total, W.K, &kc) : 1;
+  if (S > 1) {
+    dim3 grid((W.n_total + TBN - 1) / TBN, (M + TBM - 1) / TBM, S);
+    hipLaunchKernelGGL((tile_gemm_kernel<TA, WK, OM, true>), grid, dim3(256), 0, st, A, M, W, out, kc, part);
+    const long mn = (long)M * W.n_total;
+    hipLaunchKernelGGL((tile_reduce_kernel<TA, OM>), dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st,
+                       part, S, M, W.n_total, out);
+  } else {
+    dim3 grid((W.n_total + TBN - 1) / TBN, (M + TBM - 1) / TBM);
+    hipLaunchKernelGGL((tile_gemm_kernel<TA, WK, OM, false>), grid, dim3(256), 0, st, A, M, W, out, 0,
+                       part);
+  }
+}
+
 template <typename TA, int WK>
-static void tile_launch_t(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
-  dim3 grid((W.n_total + TBN - 1) / TBN, (M + TBM - 1) / TBM);
-  if (out.mode == OUT_F32)
-    hipLaunchKernelGGL((tile_gemm_kernel<TA, WK, OUT_F32>), grid, dim3(256), 0, st, A, M, W, out);
-  else if (out.mode == OUT_ACT)
-    hipLaunchKernelGGL((tile_gemm_kernel<TA, WK, OUT_ACT>), grid, dim3(256), 0, st, A, M, W, out);
-  else
-    hipLaunchKernelGGL((tile_gemm_kernel<TA, WK, OUT_CACHE>), grid, dim3(256), 0, st, A, M, W, out);
+static void tile_launch_t(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part,
+                          hipStream_t st) {
+  if (out.mode == OUT_F32) tile_go<TA, WK, OUT_F32>(A, M, W, out, part, st);
+  else if (out.mode == OUT_ACT) tile_go<TA, WK, OUT_ACT>(A, M, W, out, part, st);
+  else tile_go<TA, WK, OUT_CACHE>(A, M, W, out, part, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -1092,7 +1157,7 @@ hipError_t launch_expand_q8(const void *codes, const void *scales, long rows, in
 }
 
 hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet &W,
-                            const OutSpec &out, hipStream_t st) {
+                            const OutSpec &out, float *part, hipStream_t st) {
   // 256 x 256 tiles while they give every CU two workgroups; a narrow
   // product (the batched conv's delta, N = 256) takes 128 x 256 tiles while
   // those still cover the CUs, and the 128 x 128 tile kernel below that
@@ -1102,7 +1167,7 @@ hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet
   const bool big = M >= DFL_BIG_GEMM_MIN_M && tiles256 >= 2 * cus;
   const bool half = M >= DFL_BIG_GEMM_MIN_M && !big && tiles128 >= cus;
   if (act == ACT_F32)
-    tile_launch_t<float, W_SAME>(A, M, W, out, st);
+    tile_launch_t<float, W_SAME>(A, M, W, out, part, st);
   else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 3)
     dma8_launch<256>(A, M, W, out, st);
   else if (half && wkind == W_SAME && DFL_PREFILL_KERNEL == 3)
@@ -1114,9 +1179,9 @@ hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet
   else if (big && DFL_PREFILL_KERNEL >= 1)
     big_launch_t<W_SAME>(A, M, W, out, st);
   else if (wkind == W_Q8_0)
-    tile_launch_t<bf16, W_Q8_0>(A, M, W, out, st);
+    tile_launch_t<bf16, W_Q8_0>(A, M, W, out, part, st);
   else
-    tile_launch_t<bf16, W_SAME>(A, M, W, out, st);
+    tile_launch_t<bf16, W_SAME>(A, M, W, out, part, st);
   return hipGetLastError();
 }
 

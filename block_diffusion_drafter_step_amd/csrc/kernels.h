@@ -74,9 +74,13 @@ size_t skinny_partial_floats(int n_total, int K);
 // counters.  `part` holds skinny_partial_floats() floats.
 hipError_t launch_skinny_gemm(int act, int wkind, const ASrc &X, int M, const WSet &W, float *part,
                               unsigned *cnt, const OutSpec &out, hipStream_t st);
-// Y = A . W^T for any M (tiled MFMA GEMM, LDS-staged, no split-K).
+// Y = A . W^T for any M (tiled MFMA GEMMs, LDS-staged).  When the 128 x 128
+// tile grid would leave CUs idle (few rows), the k-range is split and `part`
+// (tile_partial_floats() floats) holds the fp32 partials; part == nullptr
+// never splits.
 hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet &W,
-                            const OutSpec &out, hipStream_t st);
+                            const OutSpec &out, float *part, hipStream_t st);
+size_t tile_partial_floats(int M, int N, int K);
 
 // Products with at least this many activation rows expand a Q8_0 weight once
 // into bf16 (the same values the in-kernel dequantisation produces) and run
