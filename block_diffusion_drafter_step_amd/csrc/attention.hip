@@ -223,8 +223,12 @@ __device__ __forceinline__ void attn_tile(const char *stage, long t0, long key1,
   }
 }
 
+#ifndef DFL_ATTN_OCC
+#define DFL_ATTN_OCC 2   // workgroups per CU the split kernel's registers are sized for
+#endif
+
 template <typename TA, int HD, int HPW>
-__global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, DFL_ATTN_OCC) void attn_split_kernel(AttnArgs a) {
   using C = AttnCfg<TA, HD>;
   extern __shared__ __attribute__((aligned(1024))) char attn_smem[];
   const int tid = threadIdx.x, lane = tid & 63;

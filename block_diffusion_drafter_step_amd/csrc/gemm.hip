@@ -1120,6 +1120,15 @@ static void dma_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, 
   }
 }
 
+// 128 x 256 direct-to-LDS tiles from this many rows, once their tiles cover
+// 1 / DFL_HALF_GEMM_FILL of the CUs
+#ifndef DFL_HALF_GEMM_MIN_M
+#define DFL_HALF_GEMM_MIN_M 256
+#endif
+#ifndef DFL_HALF_GEMM_FILL
+#define DFL_HALF_GEMM_FILL 2
+#endif
+
 #ifndef DFL_PREFILL_KERNEL
 #define DFL_PREFILL_KERNEL 3     // 0: 128-tile, 1: 256-tile register-staged, 2: 256-tile direct-to-LDS,
                                  // 3: 256-tile direct-to-LDS on 8 waves
@@ -1165,7 +1174,7 @@ hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet
   const long tiles256 = (long)((M + 255) / 256) * ((W.n_total + 255) / 256);
   const long tiles128 = (long)((M + 127) / 128) * ((W.n_total + 255) / 256);
   const bool big = M >= DFL_BIG_GEMM_MIN_M && tiles256 >= 2 * cus;
-  const bool half = M >= DFL_BIG_GEMM_MIN_M && !big && tiles128 >= cus;
+  const bool half = M >= DFL_HALF_GEMM_MIN_M && !big && tiles128 * DFL_HALF_GEMM_FILL >= cus;
   if (act == ACT_F32)
     tile_launch_t<float, W_SAME>(A, M, W, out, part, st);
   else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 3)
