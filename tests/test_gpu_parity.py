@@ -109,6 +109,11 @@ def test_inject_batched_blocks(n):
     run_inject(cfg_small(1, capacity=2048), n, 5, rows=rows)
 
 
+def test_inject_q8_0_batched_rows():
+    """Q8_0 weights with 40 rows (split-K tile GEMM with per-tile dequantisation)."""
+    run_inject(cfg_small(4, d=512, d_t=256, L_t=3, Hkv=2, capacity=256), 40, 9)
+
+
 @pytest.mark.parametrize("n", [4095, 4133])
 def test_inject_q8_0_around_expansion_threshold(n):
     """Q8_0 fc / Wk / Wv on every row just below 4096 tokens (per-tile
@@ -134,7 +139,7 @@ def run_conv(cfg, nb, tag="conv"):
     assert_close(f64(out), ref["u"], cfg.act, f"{cfg.name} conv u (n_blocks={nb})")
 
 
-@pytest.mark.parametrize("ci,nb", [(0, 1), (0, 3), (1, 1), (4, 1), (1, 64), (4, 64), (0, 2048)])
+@pytest.mark.parametrize("ci,nb", [(0, 1), (0, 3), (1, 1), (1, 3), (4, 1), (1, 64), (4, 64), (0, 2048)])
 def test_conv(ci, nb):
     run_conv(configs.get(ci), nb)
 
