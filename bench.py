@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--inject-sweep", action="store_true",
                     help="only time dflash_inject for 1..64 stashed blocks of B accepted tokens "
                          "(deferred, batched injection) and print that sweep")
+    ap.add_argument("--topk-rows", action="store_true",
+                    help="only time the row-wise top-K call against torch.topk and a full sort "
+                         "over a grid of shapes and print that")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -98,6 +101,9 @@ def main():
     from block_diffusion_drafter_step_amd import dflash as D
 
     D.load()
+    if args.topk_rows:
+        print(json.dumps({"topk_rows": topk_rows_sweep()}), flush=True)
+        return
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cfg = configs.get(WORKLOADS[args.workload])
@@ -259,6 +265,51 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, host, int(ctx_mean), inj_n)
     print(json.dumps(out), flush=True)
+
+
+def topk_rows_sweep(rows=(2, 64, 4096), cols=(128, 4096, 200000), ks=(64, 1024), reps=10):
+    """dflash_topk_rows on seeded N(0,1) fp32 rows against torch.topk and a
+    full stable descending torch.sort on the same GPU (HIP events, mean of
+    `reps` calls after 2 untimed ones).  HBM roofline: the matrix read once."""
+    import torch
+    from block_diffusion_drafter_step_amd import dflash as D
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20)
+
+    def timed(f):
+        for _ in range(2):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    res = []
+    for r in rows:
+        for c in cols:
+            x = torch.randn(r, c, generator=g, device="cuda")
+            for k in ks:
+                if k > c:
+                    continue
+                idx = torch.empty(r, k, dtype=torch.int32, device="cuda")
+                val = torch.empty(r, k, dtype=torch.float32, device="cuda")
+                ws = D.workspace(D.dflash_topk_rows_workspace(r, c, k))
+                us = timed(lambda: D.dflash_topk_rows(x, k, idx, val, ws))
+                us_topk = timed(lambda: torch.topk(x, k, dim=1, largest=True, sorted=True))
+                us_sort = timed(lambda: torch.sort(x, dim=1, descending=True, stable=True))
+                by = r * c * 4
+                res.append({"rows": r, "cols": c, "K": k, "us": round(us, 1), "torch_topk_us": round(us_topk, 1),
+                            "full_sort_us": round(us_sort, 1), "vs_sort": round(us_sort / us, 2),
+                            "gbs": round(by / us / 1e3, 1), "hbm_frac": round(by / us / 1e3 / HBM_PEAK_GBS, 4)})
+                print(json.dumps(res[-1]), file=sys.stderr, flush=True)
+                del ws, idx, val
+            del x
+            torch.cuda.empty_cache()
+    return res
 
 
 def inject_sweep(cfg, W, cache, randn, blocks=(1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128)):

@@ -556,6 +556,39 @@ dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
   return launched(launch_selector(act, a, st), "selector");
 }
 
+size_t dflash_topk_rows_workspace(int64_t n_rows, int64_t n_cols, int32_t K) {
+  if (n_rows < 1 || n_cols < 1 || K < 1 || K > DFLASH_MAX_ROW_TOPK || K > n_cols) return 0;
+  size_t a, b;
+  rowtopk_plan((long)n_rows, (long)n_cols, K, &a, &b);
+  Carve c(nullptr);
+  c.take(a);
+  c.take(b);
+  return c.off;
+}
+
+dflash_status dflash_topk_rows(const float *x, int64_t n_rows, int64_t n_cols, int32_t K, int32_t *idx,
+                               float *val, void *ws, size_t ws_bytes, void *stream) {
+  TRY(need_ptr(x, "x"));
+  TRY(need_ptr(idx, "idx"));
+  TRY(need_ptr(val, "val"));
+  if (n_rows < 1 || n_rows > 65535) return fail(DFLASH_ERR_INVALID_ARG, "n_rows must be in [1, 65535]");
+  if (n_cols < 1 || n_cols > INT32_MAX) return fail(DFLASH_ERR_INVALID_ARG, "n_cols must be in [1, 2^31)");
+  if (K < 1 || K > DFLASH_MAX_ROW_TOPK || K > n_cols)
+    return fail(DFLASH_ERR_INVALID_ARG, "K must be in [1, min(n_cols, %d)]", DFLASH_MAX_ROW_TOPK);
+  size_t a, b;
+  rowtopk_plan((long)n_rows, (long)n_cols, K, &a, &b);
+  Carve probe(nullptr);
+  probe.take(a);
+  probe.take(b);
+  TRY(check_ws(ws, ws_bytes, probe.off));
+  Carve c(ws);
+  void *buf_a = c.take(a);
+  void *buf_b = c.take(b);
+  return launched(launch_rowtopk(x, (long)n_rows, (long)n_cols, K, idx, val, buf_a, buf_b,
+                                 (hipStream_t)stream),
+                  "topk_rows");
+}
+
 dflash_status dflash_accept_len(const int32_t *draft, const int32_t *target, int32_t n_seq,
                                 int32_t B, int32_t *accept, void *stream) {
   TRY(need_ptr(draft, "draft"));

@@ -149,6 +149,12 @@ int device_cu_count();
 int topk_plan_waves(long V, int wkind);
 hipError_t launch_topk(int act, int wkind, const TopkArgs &a, hipStream_t st);
 
+// ---- row-wise top-K of an fp32 matrix (K <= 1024) -----------------------------------
+// bytes of the two candidate-key buffers the passes alternate between
+void rowtopk_plan(long n_rows, long n_cols, int K, size_t *buf_a, size_t *buf_b);
+hipError_t launch_rowtopk(const float *x, long n_rows, long n_cols, int K, int32_t *idx, float *val,
+                          void *buf_a, void *buf_b, hipStream_t st);
+
 // ---- selector ------------------------------------------------------------------------
 struct SelArgs {
   const float *proj;  // [B][r] fp32

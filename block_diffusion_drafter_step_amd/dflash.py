@@ -63,6 +63,8 @@ _SIGS = {
                                _P], _I32),
     "dflash_selector_edges_workspace": ([_I32, _I32, _I32, _I32], _SZ),
     "dflash_accept_len": ([_P, _P, _I32, _I32, _P, _P], _I32),
+    "dflash_topk_rows": ([_P, _I64, _I64, _I32, _P, _P, _P, _SZ, _P], _I32),
+    "dflash_topk_rows_workspace": ([_I64, _I64, _I32], _SZ),
     "dflash_status_string": ([_I32], ctypes.c_char_p),
     "dflash_last_error": ([], ctypes.c_char_p),
     "dflash_version": ([], _I32),
@@ -264,3 +266,18 @@ def dflash_selector_edges(h: torch.Tensor, proj: Weight, cb_pred: torch.Tensor, 
 def dflash_accept_len(draft: torch.Tensor, target: torch.Tensor, accept: torch.Tensor, stream=None):
     n_seq, B = draft.shape
     _check(load().dflash_accept_len(_ptr(draft), _ptr(target), n_seq, B, _ptr(accept), _stream(stream)))
+
+
+def dflash_topk_rows_workspace(n_rows, n_cols, K) -> int:
+    return load().dflash_topk_rows_workspace(n_rows, n_cols, K)
+
+
+def dflash_topk_rows(x: torch.Tensor, K: int, idx: torch.Tensor, val: torch.Tensor, ws: torch.Tensor,
+                     stream=None):
+    """Row-wise top-K of an fp32 matrix: idx int32 [rows][K], val fp32 [rows][K]."""
+    if x.dtype != torch.float32:
+        raise ValueError("dflash_topk_rows takes fp32 scores")
+    n_rows, n_cols = x.shape
+    wsp, wsb = _ws(ws)
+    _check(load().dflash_topk_rows(_ptr(x), n_rows, n_cols, K, _ptr(idx), _ptr(val), wsp, wsb,
+                                   _stream(stream)))

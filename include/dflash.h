@@ -219,6 +219,21 @@ dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
                                     int32_t *path, void *ws, size_t ws_bytes, void *stream);
 size_t dflash_selector_edges_workspace(int32_t B, int32_t r, int32_t d, int32_t K);
 
+/* Row-wise top-K of a score matrix (a standalone form of the selection in
+ * (4)).  "spec : add DFlash2 support", the top-k kernel review: a small K
+ * chosen from very wide rows, measured against a full sort.
+ *   idx[r][j] = column of the j-th largest x[r][*]: values descending, equal
+ *               values in ascending column order (-0.0 counts as +0.0)
+ *   val[r][j] = x[r][idx[r][j]]
+ * x: fp32 [n_rows][n_cols] (device); idx int32 and val fp32 [n_rows][K].
+ * Requires 1 <= n_rows <= 65535, 1 <= n_cols < 2^31, 1 <= K <=
+ * min(n_cols, DFLASH_MAX_ROW_TOPK); x holds no NaN (the result is then
+ * unspecified).  Results are exact (indices and copied values). */
+#define DFLASH_MAX_ROW_TOPK 1024
+dflash_status dflash_topk_rows(const float *x, int64_t n_rows, int64_t n_cols, int32_t K, int32_t *idx,
+                               float *val, void *ws, size_t ws_bytes, void *stream);
+size_t dflash_topk_rows_workspace(int64_t n_rows, int64_t n_cols, int32_t K);
+
 /* (6) Greedy accept length.
  * "dflash: port #219 onto feature", benchmark sweep (greedy sampling) and
  * "spec : add DFlash2 support", Overview table (acceptance per block):

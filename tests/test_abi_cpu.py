@@ -184,6 +184,26 @@ def test_topk_and_selector_rejections(lib):
     assert lib.dflash_accept_len(None, FAKE, 1, 8, FAKE, None) == 1
 
 
+@no_gpu
+def test_topk_rows_rejections_and_workspace(lib):
+    wide = lib.dflash_topk_rows_workspace(2, 200000, 1024)
+    assert wide > lib.dflash_topk_rows_workspace(2, 2000, 8) > 0
+    assert lib.dflash_topk_rows_workspace(2, 100, 101) == 0
+    assert lib.dflash_topk_rows_workspace(2, 5000, 1025) == 0
+
+    def call(rows=4, cols=1000, K=8, wsb=1 << 30, x=FAKE):
+        return lib.dflash_topk_rows(x, rows, cols, K, FAKE, FAKE, FAKE, wsb, None)
+
+    assert call(K=0) == 1
+    assert call(K=1025, cols=5000) == 1
+    assert call(K=1001) == 1
+    assert call(rows=0) == 1
+    assert call(rows=70000) == 1
+    assert call(cols=1 << 31, K=8) == 1
+    assert call(x=None) == 1
+    assert call(wsb=0) == 4
+
+
 def test_binding_refuses_host_tensors():
     x = torch.zeros(4, 4)
     with pytest.raises(ValueError):

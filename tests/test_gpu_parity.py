@@ -309,6 +309,41 @@ def test_topk_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def run_topk_rows(x: np.ndarray, K: int):
+    """dflash_topk_rows against the oracle's selection (value descending,
+    equal values by ascending column): indices and values bit-exact."""
+    say(f"topk_rows rows={x.shape[0]} cols={x.shape[1]} K={K}")
+    xd = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    idx = torch.empty(x.shape[0], K, dtype=torch.int32, device="cuda")
+    val = torch.empty(x.shape[0], K, dtype=torch.float32, device="cuda")
+    ws = D.workspace(D.dflash_topk_rows_workspace(x.shape[0], x.shape[1], K))
+    D.dflash_topk_rows(xd, K, idx, val, ws)
+    torch.cuda.synchronize()
+    ref = O.top_k_select(x.astype(np.float64), K)
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi, ref), f"first row differing: {np.where((gi != ref).any(1))[0][:3]}"
+    assert np.array_equal(val.cpu().numpy(), np.take_along_axis(x.astype(np.float32), ref, axis=1))
+
+
+@pytest.mark.parametrize("rows,cols,K", [(1, 1, 1), (3, 128, 64), (4096, 128, 64), (5, 1000, 1000),
+                                         (64, 4096, 1024), (2, 200000, 64), (2, 200000, 1024),
+                                         (7, 33333, 333)])
+def test_topk_rows_random(rows, cols, K):
+    rng = np.random.default_rng(rows * 7919 + cols + K)
+    run_topk_rows(rng.standard_normal((rows, cols)).astype(np.float32), K)
+
+
+def test_topk_rows_ties_signed_zero_and_constant_rows():
+    rng = np.random.default_rng(5)
+    x = rng.integers(-3, 4, size=(6, 20000)).astype(np.float32)   # heavy ties
+    x[1] = 0.0
+    x[1, ::3] = -0.0                                              # -0.0 counts as +0.0
+    x[2] = 1.5                                                    # one value everywhere
+    x[3, 100:] = -3.0e38                                         # far below the rest
+    run_topk_rows(x, 700)
+    run_topk_rows(x[:, :900], 900)
+
+
 # ---------------------------------------------------------------------------
 # (5) selector edges + path, (6) accept length
 # ---------------------------------------------------------------------------
