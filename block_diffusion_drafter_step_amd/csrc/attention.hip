@@ -223,16 +223,24 @@ __device__ __forceinline__ void attn_tile(const char *stage, long t0, long key1,
   }
 }
 
+#ifndef DFL_ATTN_STREAMS
+#define DFL_ATTN_STREAMS 2   // key streams per split workgroup (1 or 2)
+#endif
 #ifndef DFL_ATTN_OCC
 #define DFL_ATTN_OCC 2   // workgroups per CU the split kernel's registers are sized for
 #endif
 
-template <typename TA, int HD, int HPW>
-__global__ __launch_bounds__(256, DFL_ATTN_OCC) void attn_split_kernel(AttnArgs a) {
+// NS key streams per workgroup: waves 4 s .. 4 s + 3 walk the s-th contiguous
+// part of the workgroup's keys through their own ring, and the streams'
+// running softmax states are merged in LDS at the end, so one workgroup
+// writes one partial per query row for NS parts of the context.
+template <typename TA, int HD, int HPW, int NS>
+__global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_split_kernel(AttnArgs a) {
   using C = AttnCfg<TA, HD>;
   extern __shared__ __attribute__((aligned(1024))) char attn_smem[];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int stream = wave_all >> 2, wave = wave_all & 3;
   const int g = lane >> 4, r16 = lane & 15;
   const int kvh = blockIdx.y, sp = blockIdx.x;
   const int grp = a.Hq / a.Hkv;
@@ -240,9 +248,18 @@ __global__ __launch_bounds__(256, DFL_ATTN_OCC) void attn_split_kernel(AttnArgs 
   kr.ck = reinterpret_cast<const char *>(a.ck) + (long)kvh * a.cap * C::RK;
   kr.cv = reinterpret_cast<const char *>(a.cv) + (long)kvh * a.cap * HD * C::ES;   // cap/32 panels
   kr.cap = a.cap;
-  kr.key0 = (long)sp * a.chunk;
-  kr.key1 = min(a.n_ctx, kr.key0 + a.chunk);
+  // the workgroup's keys [w0, w1) in NS parts of whole tiles
+  const long w0 = (long)sp * a.chunk, w1 = min(a.n_ctx, w0 + a.chunk);
+  const long part = ((a.chunk / NS + kAttnKT - 1) / kAttnKT) * kAttnKT;
+  kr.key0 = min(w1, w0 + stream * part);
+  kr.key1 = min(w1, kr.key0 + part);
   kr.ntile = (int)((kr.key1 - kr.key0 + kAttnKT - 1) / kAttnKT);
+  // every stream runs the first stream's tile count (the barriers are the
+  // workgroup's); past its own tiles a stream re-reads its last tile and
+  // skips the arithmetic, and a stream without keys loads nothing
+  const int nloop = (int)((min(w1, w0 + part) - w0 + kAttnKT - 1) / kAttnKT);
+  const bool loads = kr.ntile > 0;
+  char *ring = attn_smem + stream * (kAttnStages * C::STAGE);
   const long qld = (long)(a.Hq + 2 * a.Hkv) * HD;
   const float sl2 = a.scale * kLog2e;
 
@@ -269,16 +286,59 @@ __global__ __launch_bounds__(256, DFL_ATTN_OCC) void attn_split_kernel(AttnArgs 
 
   // ring: tile t is read from stage t % S; stages t+1 .. t+S-2 are in flight
   constexpr int S = kAttnStages;
+  if (loads) {
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) attn_issue<TA, HD>(kr, attn_smem + s * C::STAGE, s, wave, lane);
-  for (int tI = 0; tI < kr.ntile; ++tI) {
+    for (int s = 0; s < S - 1; ++s) attn_issue<TA, HD>(kr, ring + s * C::STAGE, s, wave, lane);
+  }
+  for (int tI = 0; tI < nloop; ++tI) {
     attn_wait_vm<C::NPW * (S - 2)>();   // this wave's loads of tile tI have landed
     attn_ring_barrier();                // ... everyone's; tile tI-1 is no longer read
-    attn_issue<TA, HD>(kr, attn_smem + ((tI + S - 1) % S) * C::STAGE, tI + S - 1, wave, lane);
-    attn_tile<TA, HD, HPW>(attn_smem + (tI % S) * C::STAGE, kr.key0 + (long)tI * kAttnKT, kr.key1,
-                           sl2, g, r16, qf, o, m_run, l_run, active);
+    if (loads) attn_issue<TA, HD>(kr, ring + ((tI + S - 1) % S) * C::STAGE, tI + S - 1, wave, lane);
+    if (tI < kr.ntile)
+      attn_tile<TA, HD, HPW>(ring + (tI % S) * C::STAGE, kr.key0 + (long)tI * kAttnKT, kr.key1, sl2, g,
+                             r16, qf, o, m_run, l_run, active);
   }
   attn_wait_vm<0>();
+
+  if constexpr (NS > 1) {
+    // streams 1.. hand their (o, m, l) to stream 0 through the (now idle)
+    // ring memory; stream 0 merges them in stream order
+    static_assert(NS == 2, "two streams");
+    static_assert((4 * HPW * C::NDT * 4 * 64 + 4 * HPW * 64 * 2) * 4 <= NS * kAttnStages * C::STAGE,
+                  "the merge area fits the rings' LDS");
+    float *xo = reinterpret_cast<float *>(attn_smem);
+    float *xm = xo + 4 * HPW * C::NDT * 4 * 64;
+    __syncthreads();   // every wave is done reading the rings
+    if (stream == 1) {
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const int base = (wave * HPW + hh) * 64 + lane;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xo[((base * C::NDT + dt) << 2) + i] = o[hh][dt][i];
+        xm[2 * base] = m_run[hh];
+        xm[2 * base + 1] = l_run[hh];
+      }
+    }
+    __syncthreads();
+    if (stream == 1) return;
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int base = (wave * HPW + hh) * 64 + lane;
+      const float m1 = xm[2 * base], l1 = xm[2 * base + 1];
+      const float m = fmaxf(m_run[hh], m1);
+      if (m == -__builtin_inff()) continue;   // neither stream saw a key
+      const float a0 = exp2f(m_run[hh] - m), a1 = exp2f(m1 - m);
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[hh][dt][i] = o[hh][dt][i] * a0 + xo[((base * C::NDT + dt) << 2) + i] * a1;
+      l_run[hh] = l_run[hh] * a0 + l1 * a1;
+      m_run[hh] = m;
+    }
+  }
 
   // partials: lane holds dims 16*dt + 4g + i of token r16
 #pragma unroll
@@ -435,14 +495,14 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 
 // the cached context keys are split over about DFL_ATTN_WGS workgroups in
 // chunks of whole tiles; no context, no splits
-void attn_plan(long n_keys, int Hkv, int *chunk, int *n_split) {
+void attn_plan(long n_keys, int Hkv, int streams, int *chunk, int *n_split) {
   if (n_keys <= 0) {
     *chunk = kAttnKT;
     *n_split = 0;
     return;
   }
   const int hk = Hkv > 0 ? Hkv : 1;
-  long target = DFL_ATTN_WGS / hk;
+  long target = DFL_ATTN_WGS / (streams > 1 ? streams : 1) / hk;
   if (target < 1) target = 1;
   long c = (n_keys + target - 1) / target;
   c = ((c + kAttnKT - 1) / kAttnKT) * kAttnKT;
@@ -470,20 +530,32 @@ int attn_max_splits(long n_keys, int Hkv) {
   return (int)(b < kMaxSplit ? b : kMaxSplit);
 }
 
-template <typename TA, int HD, int HPW>
+template <typename TA, int HD, int HPW, int NS>
 static void attn_split_go(const AttnArgs &a, hipStream_t st) {
-  const size_t lds = (size_t)kAttnStages * AttnCfg<TA, HD>::STAGE;
-  auto *k = &attn_split_kernel<TA, HD, HPW>;
+  const size_t lds = (size_t)NS * kAttnStages * AttnCfg<TA, HD>::STAGE;
+  auto *k = &attn_split_kernel<TA, HD, HPW, NS>;
   (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(k, dim3(a.n_split, a.Hkv), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(k, dim3(a.n_split, a.Hkv), dim3(256 * NS), lds, st, a);
+}
+
+// key streams per split workgroup: two when both rings fit the LDS (and the
+// merge area, 4 HPW waves' (o, m, l), fits one of them)
+template <typename TA, int HD>
+constexpr int attn_streams_t() {
+  return DFL_ATTN_STREAMS >= 2 && 2 * kAttnStages * AttnCfg<TA, HD>::STAGE <= 160 * 1024 ? 2 : 1;
+}
+int attn_streams(int act, int hd) {
+  if (act == ACT_F32) return hd == 64 ? attn_streams_t<float, 64>() : attn_streams_t<float, 128>();
+  return hd == 64 ? attn_streams_t<bf16, 64>() : attn_streams_t<bf16, 128>();
 }
 
 template <typename TA, int HD>
 static void attn_launch_t(const AttnArgs &a, hipStream_t st) {
+  constexpr int NS = attn_streams_t<TA, HD>();
   if (a.n_split > 0) {
-    if (a.Hq / a.Hkv <= 4) attn_split_go<TA, HD, 1>(a, st);
-    else attn_split_go<TA, HD, 2>(a, st);
+    if (a.Hq / a.Hkv <= 4) attn_split_go<TA, HD, 1, NS>(a, st);
+    else attn_split_go<TA, HD, 2, NS>(a, st);
   }
   hipLaunchKernelGGL((attn_combine_kernel<TA, HD>), dim3(a.Hq * a.B), dim3(64), 0, st, a);
 }

@@ -429,7 +429,7 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   void *qkv = c.take((size_t)B * nqkv * 4);
   AttnArgs a;
   memset(&a, 0, sizeof a);
-  attn_plan(n_ctx, Hkv, &a.chunk, &a.n_split);
+  attn_plan(n_ctx, Hkv, attn_streams(act, hd), &a.chunk, &a.n_split);
   const int ns_max = attn_max_splits(n_ctx, Hkv);
   a.part_o = (float *)c.take((size_t)n_q_heads * B * ns_max * hd * 4);
   a.part_ml = (float *)c.take((size_t)n_q_heads * B * ns_max * 2 * 4);

@@ -116,7 +116,9 @@ struct AttnArgs {
   float *part_ml;    // [Hq][B][n_split][2]
   void *o;           // [B][Hq*hd] in the act type
 };
-void attn_plan(long n_keys, int Hkv, int *chunk, int *n_split);
+// keys per split workgroup and split count; `streams` from attn_streams()
+void attn_plan(long n_keys, int Hkv, int streams, int *chunk, int *n_split);
+int attn_streams(int act, int hd);
 int attn_max_splits(long n_keys, int Hkv);
 hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st);
 
