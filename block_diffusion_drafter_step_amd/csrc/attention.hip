@@ -375,14 +375,14 @@ __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_s
 // where (m_b, l_b, O_b) is the block's own B keys, scored here from Q, Kb, Vb
 // (probabilities rounded to the act type as the split kernel rounds them).
 // One wave per (query head, token), no barriers: lane l owns dims
-// DPL*l .. DPL*l+DPL-1 (DPL = HD/64) and split l of every group of 64 splits;
-// every load of the first 64 splits and of the block is issued before the
-// first use.  Weights reach all lanes by readlane; splits are added in
+// DPL*l .. DPL*l+DPL-1 (DPL = HD/64) and split l of every group of SG (32 or
+// 64) splits; every load of the first SG splits and of the block is issued
+// before the first use.  Weights reach all lanes by readlane; splits are added in
 // increasing order and the block term last, so the result is bitwise
 // reproducible.
 constexpr int kMaxSplit = 1024;
 
-template <typename TA, int HD>
+template <typename TA, int HD, int SG>
 __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   constexpr int DPL = HD / 64;
   const int ht = blockIdx.x;  // hq * B + t
@@ -396,14 +396,14 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   const float *ml = a.part_ml + (long)ht * ns * 2;
 
   // loads: partial rows 0..63, (m, l) of split `lane`, Q, Kb[0..15], Vb[0..15]
-  float ov[64][DPL];
+  float ov[SG][DPL];
   float2 mlv = make_float2(-__builtin_inff(), 0.f);
   if (ns > 0) {
 #pragma unroll
-    for (int s = 0; s < 64; ++s)
+    for (int s = 0; s < SG; ++s)
 #pragma unroll
       for (int e = 0; e < DPL; ++e) ov[s][e] = po[(long)min(s, ns - 1) * HD + e];
-    if (lane < ns) mlv = *reinterpret_cast<const float2 *>(ml + 2 * lane);
+    if (lane < ns && lane < SG) mlv = *reinterpret_cast<const float2 *>(ml + 2 * lane);
   }
   float qv[DPL], kv[16][DPL], vv[16][DPL];
   {
@@ -445,22 +445,23 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 
   // the global maximum over every split and the block
   float mx = mlv.x;
-  for (int s = lane + 64; s < ns; s += 64) mx = fmaxf(mx, ml[2 * s]);
+  for (int s = lane + SG; s < ns; s += SG)
+    if (lane < SG) mx = fmaxf(mx, ml[2 * s]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
   const float M = fmaxf(mx, mb);
 
-  // weighted sums over the splits, 64 at a time
+  // weighted sums over the splits, SG at a time
   float acc[DPL], lsum = 0.f;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
+  for (int s0 = 0; s0 < ns; s0 += SG) {
     float2 m_l = mlv;
     if (s0 > 0) {
       m_l = make_float2(-__builtin_inff(), 0.f);
-      if (s0 + lane < ns) m_l = *reinterpret_cast<const float2 *>(ml + 2 * (s0 + lane));
+      if (lane < SG && s0 + lane < ns) m_l = *reinterpret_cast<const float2 *>(ml + 2 * (s0 + lane));
 #pragma unroll
-      for (int s = 0; s < 64; ++s)
+      for (int s = 0; s < SG; ++s)
 #pragma unroll
         for (int e = 0; e < DPL; ++e) ov[s][e] = po[(long)min(s0 + s, ns - 1) * HD + e];
     }
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
     for (int o = 32; o >= 1; o >>= 1) lw += shfl_xor(lw, o);
     lsum += lw;
 #pragma unroll
-    for (int s = 0; s < 64; ++s) {
+    for (int s = 0; s < SG; ++s) {
       const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[e] += ws * ov[s][e];
@@ -557,7 +558,11 @@ static void attn_launch_t(const AttnArgs &a, hipStream_t st) {
     if (a.Hq / a.Hkv <= 4) attn_split_go<TA, HD, 1, NS>(a, st);
     else attn_split_go<TA, HD, 2, NS>(a, st);
   }
-  hipLaunchKernelGGL((attn_combine_kernel<TA, HD>), dim3(a.Hq * a.B), dim3(64), 0, st, a);
+  // splits 32 at a time when there are at most 32 (half the loads and broadcasts)
+  if (a.n_split <= 32)
+    hipLaunchKernelGGL((attn_combine_kernel<TA, HD, 32>), dim3(a.Hq * a.B), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<TA, HD, 64>), dim3(a.Hq * a.B), dim3(64), 0, st, a);
 }
 
 hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st) {
