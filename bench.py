@@ -65,14 +65,17 @@ def src_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_counters():
+def traffic_from_counters(cfg):
     """HBM bytes per LM-head launch from the committed rocprofv3 counter
-    summary, or None when there is none or the kernel source changed since."""
+    summary, or None when there is none, the kernel source changed since, or
+    the summary was taken on an LM head of another shape or weight type."""
     try:
         c = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
     if c.get("source_hash") != src_hash("topk.hip", "common.h", "stream.h", "dflash_abi.cpp"):
+        return None
+    if c.get("lm_head_shape") != {"V": cfg.V, "d": cfg.d, "B": cfg.B, "K": cfg.K, "weights": cfg.weight}:
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -239,7 +242,7 @@ def main():
     attn_bytes = workmodel.attn_bytes(cfg, int(ctx_mean))
     roofline = {"bound": "hbm", "kernel": "dflash_topk_unary (LM-head top-K kernel + topk_merge_kernel)",
                 "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_counters(),
+                "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_counters(cfg),
                 "bytes_per_launch": lm_bytes, "launch_ms": round(topk_ms, 4),
                 "launch_samples": len(ev)}
 
