@@ -551,9 +551,11 @@ int tile_split_plan(int M, int N, int K, int *kc) {
   return S;
 }
 
+static int dma8s_plan(int M, int N, int K, int *kc);
+
 size_t tile_partial_floats(int M, int N, int K) {
   int kc;
-  const int S = tile_split_plan(M, N, K, &kc);
+  const int S = std::max(tile_split_plan(M, N, K, &kc), dma8s_plan(M, N, K, &kc));
   return S > 1 ? (size_t)S * M * N : 0;
 }
 
@@ -930,8 +932,12 @@ constexpr int D8STAGES = DFL_DMA8_STAGES;
 template <int TBM>
 constexpr int d8_stage_bytes() { return (TBM + DBN) * DBK * 2; }
 
-template <int OM, int TBM>
-__global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, OutSpec o) {
+// SPLIT: blockIdx.y takes k-steps [y kc, (y + 1) kc) (kc in elements, a
+// multiple of 64) and writes fp32 partials part[y][m][n] for
+// tile_reduce_kernel instead of outputs.
+template <int OM, int TBM, bool SPLIT>
+__global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, OutSpec o, int kc,
+                                                        float *__restrict__ part) {
   static_assert(TBM == 256 || TBM == 128, "block rows");
   constexpr int NA = TBM / 128;        // A row blocks each wave issues per stage
   constexpr int MI = TBM / 32;         // 16-row fragments of a wave tile along M
@@ -946,7 +952,11 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
   int tm, tn;
   big_tile_of(blockIdx.x, mt, nt, &tm, &tn);
   const int m0 = tm * TBM, n0 = tn * DBN;
-  const int nk = W.K / DBK;
+  int kt0 = 0, nk = W.K / DBK;   // first k-step and k-step count of this workgroup
+  if constexpr (SPLIT) {
+    kt0 = blockIdx.y * (kc / DBK);
+    nk = min(nk - kt0, kc / DBK);
+  }
   const int kps = A.k_per_src;
 
   // this lane's DMA rows: A blocks NA*wave+j and W blocks 2*wave+j of 16
@@ -966,11 +976,11 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
     int lr;
     const int n = min(n0 + row, W.n_total - 1);
     const int sg = seg_of(W, n, &lr);
-    w_row[j] = reinterpret_cast<const bf16 *>(pick(W.data, sg)) + (long)lr * W.K + 8 * c;
+    w_row[j] = reinterpret_cast<const bf16 *>(pick(W.data, sg)) + (long)lr * W.K + 8 * c + kt0 * DBK;
   }
-  // next k-step to issue and its activation source
-  int ki = 0, src_i = 0, kl = 0;
-  const bf16 *src = reinterpret_cast<const bf16 *>(pick(A.ptr, 0));
+  // next k-step to issue (counted from kt0) and its activation source
+  int ki = 0, src_i = (kt0 * DBK) / kps, kl = kt0 * DBK - src_i * kps;
+  const bf16 *src = reinterpret_cast<const bf16 *>(pick(A.ptr, src_i));
   // the loads of one stage (no branches, so they share a basic block with
   // the k-step's MFMAs and can be scheduled between them)
   auto issue_loads = [&](char *stage) {
@@ -1079,7 +1089,12 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = m0 + wm * (TBM / 2) + 16 * i + 4 * g + v;
-        if (m < M) store_out_m<bf16, OM>(o, m, n, acc[i][j][v]);
+        if (m < M) {
+          if constexpr (SPLIT)
+            part[((long)blockIdx.y * M + m) * W.n_total + n] = acc[i][j][v];
+          else
+            store_out_m<bf16, OM>(o, m, n, acc[i][j][v]);
+        }
       }
     }
 }
@@ -1088,9 +1103,10 @@ template <int OM, int TBM>
 static void dma8_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
   const int mt = (M + TBM - 1) / TBM, nt = (W.n_total + DBN - 1) / DBN;
   const size_t lds = (size_t)D8STAGES * d8_stage_bytes<TBM>();
-  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma8_gemm_kernel<OM, TBM>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma8_gemm_kernel<OM, TBM, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((dma8_gemm_kernel<OM, TBM>), dim3(mt * nt), dim3(512), lds, st, A, M, W, out);
+  hipLaunchKernelGGL((dma8_gemm_kernel<OM, TBM, false>), dim3(mt * nt), dim3(512), lds, st, A, M, W, out,
+                     0, nullptr);
 }
 
 template <int TBM>
@@ -1098,6 +1114,49 @@ static void dma8_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out,
   if (out.mode == OUT_F32) dma8_go<OUT_F32, TBM>(A, M, W, out, st);
   else if (out.mode == OUT_ACT) dma8_go<OUT_ACT, TBM>(A, M, W, out, st);
   else dma8_go<OUT_CACHE, TBM>(A, M, W, out, st);
+}
+
+// k-split of the 128 x 256 direct-to-LDS tiles for products with few rows
+// (the same rule as the 128 x 128 tile plan, over this kernel's tiles)
+static int dma8s_plan(int M, int N, int K, int *kc) {
+  const long tiles = (long)((N + DBN - 1) / DBN) * ((M + 127) / 128);
+  const int nk = K / 64;
+  int S = 1;
+  if (tiles < kTileSplitTarget) S = (int)((kTileSplitTarget + tiles - 1) / tiles);
+  S = std::min(S, std::max(1, nk / 4));
+  S = std::min(S, 64);
+  const int kc64 = (nk + S - 1) / S;
+  S = (nk + kc64 - 1) / kc64;
+  *kc = kc64 * 64;
+  return S;
+}
+
+template <int OM>
+static void dma8s_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part, int kc, int S,
+                     hipStream_t st) {
+  const int mt = (M + 127) / 128, nt = (W.n_total + DBN - 1) / DBN;
+  const size_t lds = (size_t)D8STAGES * d8_stage_bytes<128>();
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma8_gemm_kernel<OM, 128, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((dma8_gemm_kernel<OM, 128, true>), dim3(mt * nt, S), dim3(512), lds, st, A, M, W, out,
+                     kc, part);
+  const long mn = (long)M * W.n_total;
+  hipLaunchKernelGGL((tile_reduce_kernel<bf16, OM>), dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st,
+                     part, S, M, W.n_total, out);
+}
+
+// bf16 products whose 128 x 256 tiles leave CUs idle: split k over the
+// direct-to-LDS kernel (true when launched)
+static bool dma8_split_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part,
+                              hipStream_t st) {
+  if (!part || W.K % 64 || A.k_per_src % 32) return false;
+  int kc;
+  const int S = dma8s_plan(M, W.n_total, W.K, &kc);
+  if (S <= 1) return false;
+  if (out.mode == OUT_F32) dma8s_go<OUT_F32>(A, M, W, out, part, kc, S, st);
+  else if (out.mode == OUT_ACT) dma8s_go<OUT_ACT>(A, M, W, out, part, kc, S, st);
+  else dma8s_go<OUT_CACHE>(A, M, W, out, part, kc, S, st);
+  return true;
 }
 
 constexpr size_t kDmaLds = (size_t)DSTAGES * DSTAGE_BYTES;
@@ -1127,6 +1186,12 @@ static void dma_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, 
 #endif
 #ifndef DFL_HALF_GEMM_FILL
 #define DFL_HALF_GEMM_FILL 2
+#endif
+
+// bf16 products too small to fill the CUs: split-K 128 x 256 direct-to-LDS
+// tiles (1) or split-K 128 x 128 register-staged tiles (0)
+#ifndef DFL_SMALL_M_DMA8
+#define DFL_SMALL_M_DMA8 1
 #endif
 
 #ifndef DFL_PREFILL_KERNEL
@@ -1177,6 +1242,9 @@ hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet
   const bool half = M >= DFL_HALF_GEMM_MIN_M && !big && tiles128 * DFL_HALF_GEMM_FILL >= cus;
   if (act == ACT_F32)
     tile_launch_t<float, W_SAME>(A, M, W, out, part, st);
+  else if (!big && !half && wkind == W_SAME && DFL_PREFILL_KERNEL == 3 && DFL_SMALL_M_DMA8 &&
+           dma8_split_launch(A, M, W, out, part, st))
+    return hipGetLastError();
   else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 3)
     dma8_launch<256>(A, M, W, out, st);
   else if (half && wkind == W_SAME && DFL_PREFILL_KERNEL == 3)
