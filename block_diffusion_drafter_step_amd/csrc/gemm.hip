@@ -1190,6 +1190,9 @@ static void dma_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, 
 
 // bf16 products too small to fill the CUs: split-K 128 x 256 direct-to-LDS
 // tiles (1) or split-K 128 x 128 register-staged tiles (0)
+#ifndef DFL_SPLIT_HALF
+#define DFL_SPLIT_HALF 1   // 1: also split 128 x 256 tiles whose last wave is under 3/4 full
+#endif
 #ifndef DFL_SMALL_M_DMA8
 #define DFL_SMALL_M_DMA8 1
 #endif
@@ -1240,10 +1243,13 @@ hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet
   const long tiles128 = (long)((M + 127) / 128) * ((W.n_total + 255) / 256);
   const bool big = M >= DFL_BIG_GEMM_MIN_M && tiles256 >= 2 * cus;
   const bool half = M >= DFL_HALF_GEMM_MIN_M && !big && tiles128 * DFL_HALF_GEMM_FILL >= cus;
+  // the last wave of 128 x 256 tiles less than three quarters full: split k
+  const long tail = tiles128 % cus;
+  const bool ragged = tail != 0 && tail * 4 < cus * 3;
   if (act == ACT_F32)
     tile_launch_t<float, W_SAME>(A, M, W, out, part, st);
-  else if (!big && !half && wkind == W_SAME && DFL_PREFILL_KERNEL == 3 && DFL_SMALL_M_DMA8 &&
-           dma8_split_launch(A, M, W, out, part, st))
+  else if (!big && (!half || (DFL_SPLIT_HALF && ragged)) && wkind == W_SAME && DFL_PREFILL_KERNEL == 3 &&
+           DFL_SMALL_M_DMA8 && dma8_split_launch(A, M, W, out, part, st))
     return hipGetLastError();
   else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 3)
     dma8_launch<256>(A, M, W, out, st);

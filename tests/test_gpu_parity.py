@@ -100,13 +100,13 @@ def test_inject_prefill_32k_sampled(ci):
     run_inject(cfg, cfg.n_ctx, 0, rows=rows)
 
 
-@pytest.mark.parametrize("n", [32, 48, 64, 256, 1024])
+@pytest.mark.parametrize("n", [32, 48, 64, 256, 1024, 2048])
 def test_inject_batched_blocks(n):
     """Deferred injection: the rows of several stashed blocks at once (split-K
-    tile GEMMs below 512 tiles), Qwen-27B shapes; every row up to 64, sampled
-    rows (first, last, tile edges) beyond."""
+    GEMMs while the tiles leave CUs idle), Qwen-27B shapes; every row up to
+    64, sampled rows (first, last, tile edges) beyond."""
     rows = None if n <= 64 else [0, 1, 127, 128, n // 2, n - 2, n - 1]
-    run_inject(cfg_small(1, capacity=2048), n, 5, rows=rows)
+    run_inject(cfg_small(1, capacity=max(2048, n + 64)), n, 5, rows=rows)
 
 
 def test_inject_q8_0_batched_rows():
