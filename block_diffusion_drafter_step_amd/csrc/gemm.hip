@@ -257,6 +257,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
   }
 }
 
+#ifndef DFL_Q8_SCALE_X4
+#define DFL_Q8_SCALE_X4 1   // Q8_0 skinny GEMMs: 8-byte scale loads where k-ranges allow
+#endif
+
 struct SkinnyPlan {
   int tpw, wpg, kchunk, kgroups, groups;
   bool split_tiles;
@@ -287,7 +291,7 @@ struct SkinnyPlan {
 #ifndef DFL_SKINNY_COUNTERS
 #define DFL_SKINNY_COUNTERS 1
 #endif
-static SkinnyPlan skinny_plan(int N, int K, bool f32) {
+static SkinnyPlan skinny_plan(int N, int K, bool f32, int align = 64) {
   SkinnyPlan p;
   const int ntile = (N + 15) / 16;
   p.split_tiles = ntile >= DFL_SKINNY_BIG_TILES;
@@ -300,7 +304,7 @@ static SkinnyPlan skinny_plan(int N, int K, bool f32) {
     int ks = (DFL_SKINNY_WAVES + wave_groups - 1) / wave_groups;
     if (ks < 1) ks = 1;
     int kc = (K + ks - 1) / ks;
-    kc = ((kc + 63) / 64) * 64;
+    kc = ((kc + align - 1) / align) * align;
     if (kc < 128) kc = 128;
     p.kchunk = kc;
     p.kgroups = (K + kc - 1) / kc;
@@ -313,7 +317,7 @@ static SkinnyPlan skinny_plan(int N, int K, bool f32) {
     if (kw > kw_max) kw = kw_max;
     if (kw < p.wpg) kw = p.wpg;
     int kc = (K + kw - 1) / kw;
-    kc = ((kc + 63) / 64) * 64;
+    kc = ((kc + align - 1) / align) * align;
     if (kc < 128) kc = 128;
     p.kchunk = kc;
     p.kgroups = (K + p.wpg * kc - 1) / (p.wpg * kc);
@@ -323,17 +327,18 @@ static SkinnyPlan skinny_plan(int N, int K, bool f32) {
 
 size_t skinny_partial_floats(int n_total, int K) {
   size_t most = 0;
-  for (const bool f32 : {false, true}) {
-    const SkinnyPlan p = skinny_plan(n_total, K, f32);
-    if (p.kgroups > 1) most = std::max(most, (size_t)p.kgroups * (size_t)((n_total + 15) / 16) * 256);
-  }
+  for (const bool f32 : {false, true})
+    for (const int align : {64, 128}) {
+      const SkinnyPlan p = skinny_plan(n_total, K, f32, align);
+      if (p.kgroups > 1) most = std::max(most, (size_t)p.kgroups * (size_t)((n_total + 15) / 16) * 256);
+    }
   return most;
 }
 
 template <typename TA, int WK>
 static hipError_t skinny_launch_t(const ASrc &X, int M, const WSet &W, float *part, unsigned *cnt,
                                   const OutSpec &out, hipStream_t st) {
-  const SkinnyPlan p = skinny_plan(W.n_total, W.K, sizeof(TA) == 4);
+  const SkinnyPlan p = skinny_plan(W.n_total, W.K, sizeof(TA) == 4, WK == W_Q8_0_S4 ? 128 : 64);
   const dim3 grid(p.groups, p.kgroups);
   unsigned *c = nullptr;
   if (p.split_tiles) {
@@ -366,6 +371,10 @@ static hipError_t skinny_launch_t(const ASrc &X, int M, const WSet &W, float *pa
 hipError_t launch_skinny_gemm(int act, int wkind, const ASrc &X, int M, const WSet &W, float *part,
                               unsigned *cnt, const OutSpec &out, hipStream_t st) {
   if (act == ACT_F32) return skinny_launch_t<float, W_SAME>(X, M, W, part, cnt, out, st);
+  // Q8_0 with every k-range on a 128 boundary (k-chunks rounded to 128):
+  // one 8-byte scale load per 128-wide chunk
+  if (wkind == W_Q8_0 && DFL_Q8_SCALE_X4 && W.K % 128 == 0 && X.k_per_src % 128 == 0)
+    return skinny_launch_t<bf16, W_Q8_0_S4>(X, M, W, part, cnt, out, st);
   if (wkind == W_Q8_0) return skinny_launch_t<bf16, W_Q8_0>(X, M, W, part, cnt, out, st);
   return skinny_launch_t<bf16, W_SAME>(X, M, W, part, cnt, out, st);
 }

@@ -29,6 +29,12 @@
 
 namespace dfl {
 
+// Q8_0 weights whose k-ranges all start on 128-element boundaries: the four
+// block scales of a 128-wide chunk come from one 8-byte load (2-byte loads
+// measured slow on this path).  Internal to the streaming kernels.
+constexpr int W_Q8_0_S4 = 2;
+constexpr bool is_q8(int wk) { return wk == W_Q8_0 || wk == W_Q8_0_S4; }
+
 // Q8_0 dequantisation of 8 codes held in two dwords: value = bf16(fp32(s) * q).
 // (q + 128) comes from v_cvt_f32_ubyte on the sign-flipped byte, and
 // fma(q + 128, s, -128 s) = q s exactly (q s needs at most 19 significant bits),
@@ -55,6 +61,21 @@ __device__ __forceinline__ Frag<bf16> dq8(uint32_t lo, uint32_t hi, float s) {
   return f;
 }
 
+// Scales of a lane's code vectors k + 64 m + 16 g .. + 16 (block k/32 + 2 m
+// + g/2).  W_Q8_0_S4 with a whole 128-wide chunk: k % 128 == 0 and the row's
+// scales start 8-byte aligned, so the chunk's four scales are one 8-byte load.
+template <int WK, int NJ>
+__device__ __forceinline__ void q8_chunk_scales(const uint16_t *s, int k, int g, float (&sc)[NJ / 2]) {
+  if constexpr (WK == W_Q8_0_S4 && NJ == 4) {
+    const uint2 q = *reinterpret_cast<const uint2 *>(s + (k >> 5));
+    sc[0] = half_bits_to_f32((uint16_t)(g < 2 ? q.x : q.x >> 16));
+    sc[1] = half_bits_to_f32((uint16_t)(g < 2 ? q.y : q.y >> 16));
+  } else {
+#pragma unroll
+    for (int m = 0; m < NJ / 2; ++m) sc[m] = half_bits_to_f32(s[(k + 64 * m + 16 * g) >> 5]);
+  }
+}
+
 // One weight row as seen by a lane.
 template <typename TA, int WK>
 struct SRow {
@@ -65,7 +86,7 @@ struct SRow {
 template <typename TA, int WK>
 __device__ __forceinline__ SRow<TA, WK> srow(const void *base, const void *scales, long row, int K) {
   SRow<TA, WK> r;
-  if constexpr (WK == W_Q8_0) {
+  if constexpr (is_q8(WK)) {
     r.p = reinterpret_cast<const int8_t *>(base) + row * K;
     r.s = reinterpret_cast<const uint16_t *>(scales) + row * (K >> 5);
   } else {
@@ -114,18 +135,18 @@ __device__ __forceinline__ Frag<float> wfrag(const float *p) {
 // TPW tiles (Q8_0: 16-byte code vectors plus one scale per vector).
 template <typename TA, int WK, int TPW, int NJ>
 struct Chunk {
-  using FB = typename std::conditional<WK == W_Q8_0, Frag<bf16>, Frag<TA>>::type;
+  using FB = typename std::conditional<is_q8(WK), Frag<bf16>, Frag<TA>>::type;
   FB b[NJ];
-  Frag<TA> a[WK == W_Q8_0 ? 1 : TPW][WK == W_Q8_0 ? 1 : NJ];
-  uint4 c[WK == W_Q8_0 ? TPW : 1][WK == W_Q8_0 ? NJ / 2 : 1];
-  float sc[WK == W_Q8_0 ? TPW : 1][WK == W_Q8_0 ? NJ / 2 : 1];
+  Frag<TA> a[is_q8(WK) ? 1 : TPW][is_q8(WK) ? 1 : NJ];
+  uint4 c[is_q8(WK) ? TPW : 1][is_q8(WK) ? NJ / 2 : 1];
+  float sc[is_q8(WK) ? TPW : 1][is_q8(WK) ? NJ / 2 : 1];
 };
 
 template <typename TA, int WK, int TPW, int NJ>
 __device__ __forceinline__ void chunk_load(Chunk<TA, WK, TPW, NJ> &ch, const TA *xr,
                                            const SRow<TA, WK> (&rows)[TPW], int cnt, int k, int g,
                                            bool tok_ok) {
-  if constexpr (WK == W_Q8_0) {
+  if constexpr (is_q8(WK)) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int off = k + 64 * (j >> 1) + 16 * g + 8 * (j & 1);
@@ -137,8 +158,8 @@ __device__ __forceinline__ void chunk_load(Chunk<TA, WK, TPW, NJ> &ch, const TA 
       for (int m = 0; m < NJ / 2; ++m) {
         const int off = k + 64 * m + 16 * g;
         ch.c[u][m] = wload16(reinterpret_cast<const int8_t *>(rows[u].p) + off);
-        ch.sc[u][m] = half_bits_to_f32(rows[u].s[off >> 5]);
       }
+      q8_chunk_scales<WK, NJ>(rows[u].s, k, g, ch.sc[u]);
     }
   } else {
 #pragma unroll
@@ -156,7 +177,7 @@ template <typename TA, int WK, int TPW, int NJ>
 __device__ __forceinline__ void chunk_mma(const Chunk<TA, WK, TPW, NJ> &ch, f32x4 (&acc)[TPW]) {
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    if constexpr (WK == W_Q8_0) {
+    if constexpr (is_q8(WK)) {
 #pragma unroll
       for (int m = 0; m < NJ / 2; ++m) {
         mma(acc[u], dq8(ch.c[u][m].x, ch.c[u][m].y, ch.sc[u][m]), ch.b[2 * m]);
@@ -210,7 +231,7 @@ template <typename TA, int WK, int TPW, int NJ>
 __device__ __forceinline__ void chunk_load_g(Chunk<TA, WK, TPW, NJ> &ch, const TA *xr,
                                            const SRow<TA, WK> (&rows)[TPW], int cnt, int k, int g,
                                            bool tok_ok) {
-  if constexpr (WK == W_Q8_0) {
+  if constexpr (is_q8(WK)) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int off = k + 64 * (j >> 1) + 16 * g + 8 * (j & 1);
@@ -223,8 +244,8 @@ __device__ __forceinline__ void chunk_load_g(Chunk<TA, WK, TPW, NJ> &ch, const T
         for (int m = 0; m < NJ / 2; ++m) {
           const int off = k + 64 * m + 16 * g;
           ch.c[u][m] = wload16(reinterpret_cast<const int8_t *>(rows[u].p) + off);
-          ch.sc[u][m] = half_bits_to_f32(rows[u].s[off >> 5]);
         }
+        q8_chunk_scales<WK, NJ>(rows[u].s, k, g, ch.sc[u]);
       }
     }
   } else {
@@ -248,7 +269,7 @@ __device__ __forceinline__ void chunk_mma_g(const Chunk<TA, WK, TPW, NJ> &ch, in
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     if (u < cnt) {
-      if constexpr (WK == W_Q8_0) {
+      if constexpr (is_q8(WK)) {
 #pragma unroll
         for (int m = 0; m < NJ / 2; ++m) {
           mma(acc[u], dq8(ch.c[u][m].x, ch.c[u][m].y, ch.sc[u][m]), ch.b[2 * m]);
