@@ -109,6 +109,14 @@ def test_inject_batched_blocks(n):
     run_inject(cfg_small(1, capacity=max(2048, n + 64)), n, 5, rows=rows)
 
 
+@pytest.mark.parametrize("d,d_t,n", [(512, 256, 16), (512, 256, 5), (576, 192, 16), (576, 192, 5)])
+def test_inject_q8_0_decode_rows(d, d_t, n):
+    """Q8_0 weight streaming for a few rows: with every K a multiple of 128
+    (fc 768, Wk/Wv 512) the four block scales of a chunk come from one 8-byte
+    load; with K = 576 the 2-byte scale loads."""
+    run_inject(cfg_small(4, d=d, d_t=d_t, L_t=3, Hkv=2, capacity=256), n, 3)
+
+
 def test_inject_q8_0_batched_rows():
     """Q8_0 weights with 40 rows (split-K tile GEMM with per-tile dequantisation)."""
     run_inject(cfg_small(4, d=512, d_t=256, L_t=3, Hkv=2, capacity=256), 40, 9)
