@@ -84,9 +84,12 @@ size_t tile_partial_floats(int M, int N, int K);
 
 // Products with at least this many activation rows expand a Q8_0 weight once
 // into bf16 (the same values the in-kernel dequantisation produces) and run
-// the bf16 tile GEMM: every 256-row tile would otherwise decode the whole
-// weight again.
-constexpr int kQ8ExpandMinM = 4096;
+// the bf16 direct-to-LDS GEMMs: every row tile would otherwise decode the
+// whole weight again (measured break-even near 640 rows of the 32k Q8_0 layer).
+#ifndef DFL_Q8_EXPAND_MIN_M
+#define DFL_Q8_EXPAND_MIN_M 768
+#endif
+constexpr int kQ8ExpandMinM = DFL_Q8_EXPAND_MIN_M;
 // out[r][c] = bf16_rne(fp32(scales[r][c/32]) * codes[r][c]), cols % 32 == 0
 hipError_t launch_expand_q8(const void *codes, const void *scales, long rows, int cols, void *out,
                             hipStream_t st);

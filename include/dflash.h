@@ -127,7 +127,7 @@ typedef struct {
  * in `act`.  gamma: [d] in `act`, or NULL for ones.  Requires
  * 0 <= pos0 && pos0 + n_tokens <= capacity (else DFLASH_ERR_CAPACITY),
  * d_t % 64 == 0, d % 64 == 0, n_tokens >= 1.  Cache positions outside
- * [pos0, pos0 + n_tokens) are not touched.  From 4096 tokens on, the
+ * [pos0, pos0 + n_tokens) are not touched.  From 768 tokens on, the
  * workspace also holds bf16 copies of fc, Wk and Wv (2 bytes per weight,
  * reserved whatever their dtype): Q8_0 weights are expanded there once per
  * call, to the same bf16 values the per-tile dequantisation would give. */

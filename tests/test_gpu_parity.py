@@ -122,10 +122,10 @@ def test_inject_q8_0_batched_rows():
     run_inject(cfg_small(4, d=512, d_t=256, L_t=3, Hkv=2, capacity=256), 40, 9)
 
 
-@pytest.mark.parametrize("n", [4095, 4133])
+@pytest.mark.parametrize("n", [767, 800, 4133])
 def test_inject_q8_0_around_expansion_threshold(n):
-    """Q8_0 fc / Wk / Wv on every row just below 4096 tokens (per-tile
-    dequantisation) and just above (one bf16 expansion per call), ragged tail."""
+    """Q8_0 fc / Wk / Wv on every row just below 768 tokens (per-tile
+    dequantisation) and above (one bf16 expansion per call), ragged tails."""
     cfg = cfg_small(4, d=512, d_t=256, L_t=3, Hkv=2, capacity=4224)
     run_inject(cfg, n, 17)
 
