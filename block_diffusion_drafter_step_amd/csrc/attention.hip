@@ -177,6 +177,16 @@ __device__ __forceinline__ void attn_tile(const char *stage, long t0, long key1,
     const int c = (8 * g) / C::EPC;
     vf[dt] = lds_frag2<TA>(vr, vswz<C::NVC>(d, c), vswz<C::NVC>(d, c + CPF - 1));
   }
+  // a tile that ends inside its V^T panel: the panel's positions from key1 on
+  // may hold anything (a NaN would survive its zero probability), so their
+  // values are replaced by zeros; element e of a fragment is key 8g + e
+  if (t0 + kAttnKT > key1) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (t0 + 8 * g + e >= key1) vf[dt].v[e] = from_f32<TA>(0.f);
+  }
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     if (!active[hh]) continue;

@@ -187,7 +187,9 @@ def test_conv_batched_32k_tokens():
 # (3) block attention
 # ---------------------------------------------------------------------------
 
-def run_attn(cfg, n_ctx, cap=None, resid=True, B=None):
+def run_attn(cfg, n_ctx, cap=None, resid=True, B=None, poison=False):
+    """poison: cache positions from n_ctx on hold NaN (the attention must not
+    read them into the result, also where a tile ends inside a V panel)."""
     B = cfg.B if B is None else B
     cap = cap or -(-(n_ctx + 64) // 64) * 64   # the library wants a multiple of 64
     say(f"attn {cfg.name} B={B} n_ctx={n_ctx} cap={cap}")
@@ -198,7 +200,11 @@ def run_attn(cfg, n_ctx, cap=None, resid=True, B=None):
     u = synth.normal(cfg.seed, "attn.u", (B, cfg.d), 1.0, cfg.act)
     x = synth.normal(cfg.seed, "attn.x", (B, cfg.d), 1.0, cfg.act)
     wq, wk, wv, wo = w.wq(), w.wk(), w.wv(), w.wo()
-    cache = D.KVCache(dev(ck, cfg.act), D.v_panels(dev(cv, cfg.act)))
+    ck_d, cv_d = dev(ck, cfg.act), dev(cv, cfg.act)
+    if poison:
+        ck_d[:, n_ctx:, :] = float("nan")
+        cv_d[:, n_ctx:, :] = float("nan")
+    cache = D.KVCache(ck_d, D.v_panels(cv_d))
     out = torch.empty((B, cfg.d), dtype=P.act_dtype(cfg.act), device="cuda")
     ws = D.workspace(D.dflash_block_attn_workspace(B, cfg.d, cfg.Hq, cfg.Hkv, cfg.hd, n_ctx))
     xd = dev(x, cfg.act)
@@ -231,6 +237,13 @@ def test_attn_many_splits():
     combine kernel's multi-group path, with a partial last group."""
     run_attn(cfg_small(0, n_ctx=5000), 5000)                           # fp32, hd 64: 157 splits
     run_attn(cfg_small(1, Hq=8, Hkv=2, n_ctx=8000), 8000)              # bf16, hd 128: 250 splits
+
+
+@pytest.mark.parametrize("ci,n_ctx", [(0, 77), (0, 200), (1, 1000), (1, 31), (4, 4133)])
+def test_attn_cache_tail_not_finite(ci, n_ctx):
+    """The context ends inside a 32-position V panel whose other positions
+    hold NaN: they get zero weight and must not turn the output into NaN."""
+    run_attn(configs.get(ci), n_ctx, poison=True)
 
 
 def test_attn_deterministic():
