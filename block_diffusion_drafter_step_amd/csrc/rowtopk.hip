@@ -9,21 +9,27 @@
 // is exactly the requested set.
 //
 // One workgroup of 512 threads owns one segment of a row (at most 8192
-// keys, held in LDS).  It finds the K-th largest key with eight radix passes
-// over 8-bit digits (most significant first: a 256-bin histogram of the keys
-// that still match the chosen prefix, then the digit whose bins reach the
-// remaining rank; it stops early once that digit's keys are all kept), keeps
-// the K keys at or above it.  A row wider than one segment yields one
-// candidate list per segment; the same kernel then selects from those lists,
-// until one segment is left, whose K keys are bitonic-sorted descending.  The
-// final pass writes indices and re-reads the values from the input, so they
-// are exact copies.
+// keys, 16 per thread, kept in registers; every load of a thread is issued
+// before the first is used).  It finds the K-th largest key with eight radix
+// passes over 8-bit digits (most significant first: a 256-bin histogram of
+// the keys that still match the chosen prefix, then the digit whose bins
+// reach the remaining rank; it stops early once that digit's keys are all
+// kept), keeps the K keys at or above it.  A row wider than one segment
+// yields one candidate list per segment, padded with the key 0 (no element
+// has it: the index word of a real key is at least 2^31) when the segment
+// held fewer than K; the same kernel then selects from those lists, pads not
+// counted, until one segment is left, whose K keys are bitonic-sorted
+// descending.  The final pass writes indices and re-reads the values from
+// the input, so they are exact copies.
 #include "common.h"
 #include "kernels.h"
 
 namespace dfl {
 
 constexpr int kRowSelThreads = 512;
+constexpr int kRowSelMaxSeg = 8192;
+constexpr int kRowSelPer = kRowSelMaxSeg / kRowSelThreads;   // keys per thread
+constexpr int kRowSelMaxK = 1024;
 
 __device__ __forceinline__ unsigned long long row_key(float v, long col) {
   unsigned u = __float_as_uint(v);
@@ -33,46 +39,80 @@ __device__ __forceinline__ unsigned long long row_key(float v, long col) {
 }
 
 // one pass: keys of row blockIdx.y, segment blockIdx.x ([seg0, seg0 + len)
-// of a row of n_in inputs) -> the segment's K largest, sorted descending.
-// FROM_KEYS: the input is a previous pass's key lists, else fp32 scores.
-// Output: `keys_out` [row][n_seg][K] (0 pads a short segment), or, when
-// n_seg == 1 and idx != nullptr, the final indices and values.
+// of a row of n_in inputs) -> the segment's K largest keys (sorted
+// descending in the final pass).  FROM_KEYS: the input is a previous pass's
+// key lists, else fp32 scores.  Output: `keys_out` [row][n_seg][K] (0 pads
+// a short list), or, when n_seg == 1 and idx != nullptr, the final indices
+// and values.
 template <bool FROM_KEYS>
 __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__restrict__ in, long n_in,
                                                                 int seg, int K, const float *__restrict__ x,
                                                                 long n_cols, unsigned long long *keys_out,
                                                                 int32_t *idx, float *val) {
-  extern __shared__ __attribute__((aligned(16))) unsigned long long rs_keys[];
   __shared__ unsigned hist[256];
-  __shared__ unsigned long long sel[1024];
-  __shared__ unsigned sel_n;
+  __shared__ unsigned long long sel[kRowSelMaxK];
+  __shared__ unsigned sel_n, n_real;
   __shared__ unsigned pick_digit, pick_above;
   const int tid = threadIdx.x;
   const long row = blockIdx.y;
   const int n_seg = gridDim.x;
   const long seg0 = (long)blockIdx.x * seg;
   const int len = (int)min((long)seg, n_in - seg0);
+  const long base = row * n_in + seg0;
 
-  // load the segment's keys
-  for (int i = tid; i < len; i += kRowSelThreads) {
-    if constexpr (FROM_KEYS)
-      rs_keys[i] = reinterpret_cast<const unsigned long long *>(in)[row * n_in + seg0 + i];
-    else
-      rs_keys[i] = row_key(reinterpret_cast<const float *>(in)[row * n_in + seg0 + i], seg0 + i);
+  // this thread's keys: segment entries tid + j * 512; 0 = no key (past the
+  // segment, or a pad).  Loads past the segment re-read its last entry, so
+  // all of them are issued unconditionally, back to back.
+  unsigned long long kv[kRowSelPer];
+  if constexpr (FROM_KEYS) {
+    const unsigned long long *src = reinterpret_cast<const unsigned long long *>(in) + base;
+#pragma unroll
+    for (int j = 0; j < kRowSelPer; ++j)
+      if (j * kRowSelThreads < seg) kv[j] = src[min(tid + j * kRowSelThreads, len - 1)];
+#pragma unroll
+    for (int j = 0; j < kRowSelPer; ++j)
+      if (!(j * kRowSelThreads < seg && tid + j * kRowSelThreads < len)) kv[j] = 0ull;
+  } else {
+    const float *src = reinterpret_cast<const float *>(in) + base;
+    float xv[kRowSelPer];
+#pragma unroll
+    for (int j = 0; j < kRowSelPer; ++j)
+      if (j * kRowSelThreads < seg) xv[j] = src[min(tid + j * kRowSelThreads, len - 1)];
+#pragma unroll
+    for (int j = 0; j < kRowSelPer; ++j) {
+      const int i = tid + j * kRowSelThreads;
+      kv[j] = j * kRowSelThreads < seg && i < len ? row_key(xv[j], seg0 + i) : 0ull;
+    }
   }
-  if (tid == 0) sel_n = 0;
+  if (tid == 0) {
+    sel_n = 0;
+    n_real = 0;
+  }
   __syncthreads();
+  // keys in the segment (pads of a previous pass excluded)
+  unsigned nr = (unsigned)len;
+  if constexpr (FROM_KEYS) {
+    unsigned c = 0;
+#pragma unroll
+    for (int j = 0; j < kRowSelPer; ++j) c += kv[j] != 0ull;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, 64);
+    if ((tid & 63) == 0) atomicAdd(&n_real, c);
+    __syncthreads();
+    nr = n_real;
+  }
 
-  unsigned long long thr = 0;   // keys >= thr are kept
-  if (len > K) {
+  unsigned long long thr = 1ull;   // keys >= thr are kept (every key when nr <= K)
+  if (nr > (unsigned)K) {
     unsigned long long prefix = 0, mask = 0;
     unsigned remaining = (unsigned)K;
     for (int shift = 56; shift >= 0; shift -= 8) {
       for (int b = tid; b < 256; b += kRowSelThreads) hist[b] = 0;
       __syncthreads();
-      for (int i = tid; i < len; i += kRowSelThreads) {
-        const unsigned long long k = rs_keys[i];
-        if ((k & mask) == prefix) atomicAdd(&hist[(unsigned)(k >> shift) & 255u], 1u);
+#pragma unroll
+      for (int j = 0; j < kRowSelPer; ++j) {
+        const unsigned long long k = kv[j];
+        if (k != 0ull && (k & mask) == prefix) atomicAdd(&hist[(unsigned)(k >> shift) & 255u], 1u);
       }
       __syncthreads();
       // wave 0: lane l holds bins 252 - 4l .. 255 - 4l (descending digits);
@@ -115,14 +155,18 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
       __syncthreads();   // pick_* and hist are rewritten by the next pass
       if (done) break;
     }
-    thr = prefix;   // exactly K keys are >= it
+    thr = prefix;   // exactly K keys are >= it (keys are unique and nonzero)
   }
 
-  // keep keys >= thr (all of them when len <= K)
-  const int n_keep = len > K ? K : len;
-  for (int i = tid; i < len; i += kRowSelThreads) {
-    const unsigned long long k = rs_keys[i];
-    if (k >= thr) sel[atomicAdd(&sel_n, 1u)] = k;
+  // keep keys >= thr; the bound on the slot only guards a broken invariant
+  const int n_keep = nr > (unsigned)K ? K : (int)nr;
+#pragma unroll
+  for (int j = 0; j < kRowSelPer; ++j) {
+    const unsigned long long k = kv[j];
+    if (k != 0ull && k >= thr) {
+      const unsigned slot = atomicAdd(&sel_n, 1u);
+      if (slot < (unsigned)kRowSelMaxK) sel[slot] = k;
+    }
   }
   __syncthreads();
   // bitonic sort of sel[0, P) descending, P = next power of two >= K, pads 0;
@@ -164,12 +208,12 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
   }
 }
 
-// Segment width of a pass over rows of n elements: at most 8192 (LDS),
-// at least 2K so every pass shrinks the candidates, smaller while the grid
-// would leave CUs idle.
+// Segment width of a pass over rows of n elements: at most 8192 (16 keys
+// per thread), at least 2K so every pass shrinks the candidates, smaller
+// while the grid would leave CUs idle.
 static int rowsel_seg(long n_rows, long n, int K) {
   const int lo = K * 2 > 1024 ? K * 2 : 1024;
-  int seg = 8192;
+  int seg = kRowSelMaxSeg;
   while (seg / 2 >= lo && n_rows * ((n + seg - 1) / seg) < 2 * 256) seg /= 2;
   return seg;
 }
@@ -203,18 +247,12 @@ hipError_t launch_rowtopk(const float *x, long n_rows, long n_cols, int K, int32
     unsigned long long *out =
         n_seg == 1 ? nullptr : reinterpret_cast<unsigned long long *>((pass & 1) ? buf_b : buf_a);
     const dim3 grid((unsigned)n_seg, (unsigned)n_rows);
-    const size_t lds = (size_t)seg * 8;
-    if (keys) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&rowsel_kernel<true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      hipLaunchKernelGGL(rowsel_kernel<true>, grid, dim3(kRowSelThreads), lds, st, in, n, seg, K, x, n_cols,
+    if (keys)
+      hipLaunchKernelGGL(rowsel_kernel<true>, grid, dim3(kRowSelThreads), 0, st, in, n, seg, K, x, n_cols, out,
+                         idx, val);
+    else
+      hipLaunchKernelGGL(rowsel_kernel<false>, grid, dim3(kRowSelThreads), 0, st, in, n, seg, K, x, n_cols,
                          out, idx, val);
-    } else {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&rowsel_kernel<false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      hipLaunchKernelGGL(rowsel_kernel<false>, grid, dim3(kRowSelThreads), lds, st, in, n, seg, K, x,
-                         n_cols, out, idx, val);
-    }
     if (n_seg == 1) break;
     in = out;
     n = n_seg * K;

@@ -354,6 +354,20 @@ def test_topk_rows_random(rows, cols, K):
     run_topk_rows(rng.standard_normal((rows, cols)).astype(np.float32), K)
 
 
+@pytest.mark.parametrize("rows,cols,K", [(3, 11284, 100), (2, 22548, 1000), (4, 81925, 1000)])
+def test_topk_rows_short_last_list(rows, cols, K):
+    """Widths whose last segment holds fewer than K scores: its candidate
+    list is padded, and a later pass then sees a segment with more than K
+    entries but fewer than K real keys.  Row 0 increases along the row, so
+    its top K are exactly the keys in that segment; the other rows are
+    random or decreasing."""
+    rng = np.random.default_rng(cols + K)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[0] = np.arange(cols, dtype=np.float32)
+    x[-1] = -np.arange(cols, dtype=np.float32)
+    run_topk_rows(x, K)
+
+
 def test_topk_rows_ties_signed_zero_and_constant_rows():
     rng = np.random.default_rng(5)
     x = rng.integers(-3, 4, size=(6, 20000)).astype(np.float32)   # heavy ties
