@@ -30,6 +30,11 @@ constexpr int kRowSelThreads = 512;
 constexpr int kRowSelMaxSeg = 8192;
 constexpr int kRowSelPer = kRowSelMaxSeg / kRowSelThreads;   // keys per thread
 constexpr int kRowSelMaxK = 1024;
+#ifndef DFL_ROWSEL_COPIES
+#define DFL_ROWSEL_COPIES 8   // histogram copies (lane l adds to copy l % copies)
+#endif
+constexpr int kRowSelCopies = DFL_ROWSEL_COPIES;
+static_assert((kRowSelCopies & (kRowSelCopies - 1)) == 0 && kRowSelCopies <= 64, "copies: a power of two");
 
 __device__ __forceinline__ unsigned long long row_key(float v, long col) {
   unsigned u = __float_as_uint(v);
@@ -49,6 +54,7 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
                                                                 int seg, int K, const float *__restrict__ x,
                                                                 long n_cols, unsigned long long *keys_out,
                                                                 int32_t *idx, float *val) {
+  __shared__ unsigned histc[kRowSelCopies * 257];   // copy c at 257 c (banks staggered)
   __shared__ unsigned hist[256];
   __shared__ unsigned long long sel[kRowSelMaxK];
   __shared__ unsigned sel_n, n_real;
@@ -88,6 +94,7 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
     sel_n = 0;
     n_real = 0;
   }
+  for (int b = tid; b < kRowSelCopies * 257; b += kRowSelThreads) histc[b] = 0;
   __syncthreads();
   // keys in the segment (pads of a previous pass excluded)
   unsigned nr = (unsigned)len;
@@ -107,12 +114,24 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
     unsigned long long prefix = 0, mask = 0;
     unsigned remaining = (unsigned)K;
     for (int shift = 56; shift >= 0; shift -= 8) {
-      for (int b = tid; b < 256; b += kRowSelThreads) hist[b] = 0;
-      __syncthreads();
+      // keys crowd into few bins (the leading digits of similar floats
+      // agree), so the lanes of a wave add to separate copies; the copies
+      // are zero here (cleared at the start, and by each pass's summation)
+      unsigned *mine = histc + (tid & (kRowSelCopies - 1)) * 257;
 #pragma unroll
       for (int j = 0; j < kRowSelPer; ++j) {
         const unsigned long long k = kv[j];
-        if (k != 0ull && (k & mask) == prefix) atomicAdd(&hist[(unsigned)(k >> shift) & 255u], 1u);
+        if (k != 0ull && (k & mask) == prefix) atomicAdd(&mine[(unsigned)(k >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 256) {
+        unsigned sum = 0;
+#pragma unroll
+        for (int c = 0; c < kRowSelCopies; ++c) {
+          sum += histc[c * 257 + tid];
+          histc[c * 257 + tid] = 0;
+        }
+        hist[tid] = sum;
       }
       __syncthreads();
       // wave 0: lane l holds bins 252 - 4l .. 255 - 4l (descending digits);
