@@ -301,12 +301,29 @@ __global__ __launch_bounds__(NW * 64) void lmhead_topk_lds_kernel(TopkArgs a) {
   const int d = a.d, B = a.B;
   const long V = a.V;
   constexpr int VEC = 16 / (int)sizeof(TA);
-  // stage h (B rows) into LDS, swizzled
+  // stage h (B rows) into LDS, swizzled; SB loads per thread in flight at a
+  // time (a load-then-store loop would wait for every load in turn).
+  // Chunks past the end re-read the last one and store it again (the same
+  // bytes to the same place), so no load or store is conditional.
   const TA *hg = reinterpret_cast<const TA *>(a.h);
-  for (int c = tid; c < B * (d / VEC); c += NW * 64) {
-    const int t = c / (d / VEC), k = (c - t * (d / VEC)) * VEC;
-    *reinterpret_cast<uint4 *>(hs + hsw<TA>(t, k, d)) =
-        *reinterpret_cast<const uint4 *>(hg + (long)t * d + k);
+  {
+    constexpr int SB = 8;
+    const int nch = B * (d / VEC);
+    for (int c0 = tid; c0 < nch; c0 += SB * NW * 64) {
+      u32x4 v[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int c = min(c0 + u * NW * 64, nch - 1);
+        const int t = c / (d / VEC), k = (c - t * (d / VEC)) * VEC;
+        v[u] = *reinterpret_cast<const u32x4 *>(hg + (long)t * d + k);
+      }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int c = min(c0 + u * NW * 64, nch - 1);
+        const int t = c / (d / VEC), k = (c - t * (d / VEC)) * VEC;
+        *reinterpret_cast<u32x4 *>(hs + hsw<TA>(t, k, d)) = v[u];
+      }
+    }
   }
   __syncthreads();
 
