@@ -8,6 +8,8 @@ the seeded generator writes (fp32, bf16 bit patterns, Q8_0 codes + scales).
 
 Sources (web pages, cited by title and section):
   [P1] "dflash: port #219 onto feature (rebased full CL)"
+       - "DFlash Benchmark Sweep": every result table runs the draft with
+         q8_0 K and V caches (the Cache K / Cache V columns).
        - "DFlash Prompt Processing Speed", Root Cause: the encoder is an fc
          matmul over the concatenated target-layer features plus a norm.
        - "Why We Can't Easily Fix It": the chain target features -> encode ->
@@ -49,6 +51,12 @@ Readings where the pages are silent (each also listed in the design notes):
   R-Q8 Q8_0 weight value = bf16_rne(fp32(scale) * q).
   R-RP in bf16 workloads the values the GPU stores as bf16 are rounded to
        bf16 here too: z, the cache rows, conv output u, Q/Kb/Vb, O and h_out.
+  R-KVQ a Q8_0 KV cache holds, per (KV head, position), blocks of 32 along
+       the head dim: scale = max|x| / 127 stored as fp16, code = x / scale
+       rounded to the nearest integer with ties away from zero (all codes 0
+       when the block is all zero), x being the unrounded projection output;
+       the attention reads value = bf16_rne(fp32(scale) * code) in bf16
+       workloads (as R-Q8), fp32(scale) * code in fp32 ones.
 """
 from __future__ import annotations
 
@@ -155,6 +163,35 @@ def cache_write(cache_k: np.ndarray, cache_v: np.ndarray, k_rows: np.ndarray,
         raise ValueError("cache capacity")
     cache_k[:, pos0:pos0 + n, :] = k_rows.reshape(n, hkv, hd).transpose(1, 0, 2)
     cache_v[:, pos0:pos0 + n, :] = v_rows.reshape(n, hkv, hd).transpose(1, 0, 2)
+
+
+def kv_quant_q8_0(x: np.ndarray):
+    """Q8_0 cache rows (reading R-KVQ).  [P1] DFlash Benchmark Sweep: the
+    draft's K and V caches are q8_0 in every measurement.  x [..., hd] with
+    hd a multiple of 32 -> (codes int8 [..., hd], scales fp16 [..., hd/32])."""
+    x = np.asarray(x, dtype=np.float64)
+    hd = x.shape[-1]
+    if hd % QBLOCK:
+        raise ValueError("head dim not a multiple of 32")
+    blocks = x.reshape(*x.shape[:-1], hd // QBLOCK, QBLOCK)
+    scale = np.max(np.abs(blocks), axis=-1) / 127.0
+    safe = np.where(scale > 0, scale, 1.0)
+    t = np.where(scale[..., None] > 0, blocks / safe[..., None], 0.0)
+    codes = np.sign(t) * np.floor(np.abs(t) + 0.5)          # ties away from zero
+    return codes.astype(np.int8).reshape(x.shape), scale.astype(np.float16)
+
+
+def kv_dequant_q8_0(codes: np.ndarray, scales: np.ndarray, bf16_points: bool) -> np.ndarray:
+    """Values the attention reads from a Q8_0 cache (reading R-KVQ):
+    fp32(scale) * code, rounded to bf16 in bf16 workloads (the product of an
+    fp16 scale and an 8-bit code is exact in fp32)."""
+    q = np.asarray(codes, dtype=np.float64)
+    hd = q.shape[-1]
+    s = np.asarray(scales, dtype=np.float16).astype(np.float32).astype(np.float64)
+    if s.shape != q.shape[:-1] + (hd // QBLOCK,):
+        raise ValueError("scale shape")
+    v = (q.reshape(*q.shape[:-1], hd // QBLOCK, QBLOCK) * s[..., None]).reshape(q.shape)
+    return _rp(v, bf16_points)
 
 
 # ---------------------------------------------------------------------------

@@ -284,6 +284,80 @@ def test_attention_ignores_rows_past_n_ctx():
 
 
 # --------------------------------------------------------------------------
+# Q8_0 KV cache rows (quantisation, and the values attention reads)
+# --------------------------------------------------------------------------
+
+def test_kv_q8_0_exact_blocks_round_trip():
+    """Blocks that are exactly a power-of-two scale times integers with one
+    +-127 per block come back unchanged: codes, scale and values (bf16 and
+    fp32).  Catches a 128 divisor, a scale over the wrong axis or a dropped
+    scale."""
+    r = np.random.default_rng(7)
+    q = r.integers(-126, 127, size=(3, 4, 128))
+    q[..., ::32] = 127 * np.where(r.random((3, 4, 4)) < 0.5, -1, 1)   # one +-127 per block
+    x = q * 2.0 ** -6
+    codes, scales = O.kv_quant_q8_0(x)
+    assert np.array_equal(codes.astype(np.int64), q)
+    assert np.all(scales.astype(np.float64) == 2.0 ** -6)
+    assert np.array_equal(O.kv_dequant_q8_0(codes, scales, True), x)
+    assert np.array_equal(O.kv_dequant_q8_0(codes, scales, False), x)
+
+
+def test_kv_q8_0_ties_away_from_zero():
+    """x / scale = k + 1/2 rounds away from zero (numpy's round-half-even would
+    give 2, 0, 2 for 2.5, 0.5, 1.5).  Catches banker's rounding and
+    truncation."""
+    x = np.zeros(32)
+    x[0] = 127.0
+    x[1:7] = [2.5, -2.5, 0.5, -0.5, 1.5, -1.5]
+    codes, scales = O.kv_quant_q8_0(x * 2.0 ** -4)
+    assert float(scales[0]) == 2.0 ** -4
+    assert list(codes[:7]) == [127, 3, -3, 1, -1, 2, -2]
+
+
+def test_kv_q8_0_zero_block_sign_symmetry_and_block_order():
+    """An all-zero block gives scale 0 and codes 0 (no NaN); negating x negates
+    the codes and keeps the scales; block b's scale multiplies dims 32b ..
+    32b+31 (catches a transposed scale index)."""
+    r = np.random.default_rng(8)
+    x = r.standard_normal((5, 128))
+    x[2, 32:64] = 0.0
+    c, s = O.kv_quant_q8_0(x)
+    assert float(s[2, 1]) == 0.0 and not np.any(c[2, 32:64])
+    assert np.all(np.isfinite(O.kv_dequant_q8_0(c, s, False)))
+    cn, sn = O.kv_quant_q8_0(-x)
+    assert np.array_equal(cn, -c) and np.array_equal(sn, s)
+    ones = np.ones((1, 128), dtype=np.int8)
+    sc = np.array([[1.0, 2.0, 4.0, 8.0]], dtype=np.float16)
+    assert np.array_equal(O.kv_dequant_q8_0(ones, sc, True)[0], np.repeat([1.0, 2.0, 4.0, 8.0], 32))
+
+
+def test_kv_q8_0_codes_are_the_nearest_level_by_brute_force():
+    """On random blocks each code is the integer level in [-127, 127] nearest
+    to x at the block's unrounded scale max|x|/127 (brute force over all 255
+    levels), the largest |x| of a block takes +-127, and the value read back
+    is within half a level plus the fp16 rounding of the scale."""
+    r = np.random.default_rng(9)
+    x = r.standard_normal((6, 64)) * r.uniform(0.01, 10.0, size=(6, 1))
+    c, s = O.kv_quant_q8_0(x)
+    blocks = x.reshape(6, 2, 32)
+    exact = np.max(np.abs(blocks), axis=-1) / 127.0
+    levels = np.arange(-127, 128)
+    for i in range(6):
+        for b in range(2):
+            for e in range(32):
+                v = blocks[i, b, e]
+                dist = np.abs(v - exact[i, b] * levels)
+                best = levels[np.argmin(dist)]
+                assert c[i, 32 * b + e] == best, (i, b, e)
+            assert np.max(np.abs(c[i, 32 * b:32 * b + 32])) == 127
+    back = O.kv_dequant_q8_0(c, s, False).reshape(6, 2, 32)
+    s16 = s.astype(np.float64)
+    bound = exact / 2 + np.abs(s16 - exact) * 127 + 1e-12
+    assert np.all(np.abs(back - blocks) <= bound[..., None])
+
+
+# --------------------------------------------------------------------------
 # (4) LM head
 # --------------------------------------------------------------------------
 
