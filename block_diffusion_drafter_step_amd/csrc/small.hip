@@ -17,32 +17,59 @@ __device__ __forceinline__ float wave_sum(float v) {
 // z = y / sqrt(mean(y^2) + eps) * gamma, one workgroup per row, fixed-order sum.
 // ---------------------------------------------------------------------------
 template <typename TA>
+__device__ __forceinline__ void rmsnorm_store4(TA *zr, int c, f32x4 v, float inv, const TA *gamma) {
+  float o[4] = {v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv};
+  if (gamma) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] *= to_f32(gamma[c + j]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) zr[c + j] = from_f32<TA>(o[j]);
+}
+
+// Rows up to kRmsHeld float4 per thread (8192 wide) are read once into
+// registers, every load issued before the first is used; wider rows are
+// read twice (the second time from the cache).
+constexpr int kRmsHeld = 8;
+
+template <typename TA>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ y, int d,
                                                       const TA *__restrict__ gamma, float eps,
                                                       TA *__restrict__ z) {
   const long row = blockIdx.x;
+  const int tid = threadIdx.x;
   const float *yr = y + row * d;
+  const f32x4 *yv = reinterpret_cast<const f32x4 *>(yr);
+  const int nv = d / 4;
+  const bool held = nv <= kRmsHeld * 256;
+  f32x4 v[kRmsHeld];
   float ss = 0.f;
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
-    const float4 v = *reinterpret_cast<const float4 *>(yr + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  if (held) {
+#pragma unroll
+    for (int j = 0; j < kRmsHeld; ++j)
+      if (j * 256 < nv) v[j] = yv[min(tid + j * 256, nv - 1)];
+#pragma unroll
+    for (int j = 0; j < kRmsHeld; ++j)
+      if (j * 256 < nv && tid + j * 256 < nv) ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
+  } else {
+    for (int c = tid; c < nv; c += 256) {
+      const f32x4 t = yv[c];
+      ss += t[0] * t[0] + t[1] * t[1] + t[2] * t[2] + t[3] * t[3];
+    }
   }
   __shared__ float red[4];
   ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
   TA *zr = z + row * d;
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
-    const float4 v = *reinterpret_cast<const float4 *>(yr + c);
-    float o[4] = {v.x * inv, v.y * inv, v.z * inv, v.w * inv};
-    if (gamma) {
+  if (held) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] *= to_f32(gamma[c + j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) zr[c + j] = from_f32<TA>(o[j]);
+    for (int j = 0; j < kRmsHeld; ++j)
+      if (j * 256 < nv && tid + j * 256 < nv) rmsnorm_store4<TA>(zr, 4 * (tid + j * 256), v[j], inv, gamma);
+  } else {
+    for (int c = tid; c < nv; c += 256) rmsnorm_store4<TA>(zr, 4 * c, yv[c], inv, gamma);
   }
 }
 
