@@ -222,7 +222,8 @@ __global__ __launch_bounds__(WPG * 64, WPG >= 8 ? WPG / 4 : 2) void skinny_gemm_
 
 // Outputs from the partials part[y][tile][lane] (float4) summed in k-group
 // order, as the last workgroup of skinny_gemm_kernel does; 8 k-groups' loads
-// are issued together to hide their latency.  One thread per (tile, lane).
+// are issued together to hide their latency (also in the last, partial
+// group).  One thread per (tile, lane).
 template <typename TA>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int nky,
                                                             int N, int M, OutSpec o) {
@@ -234,20 +235,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
   const long tstride = (long)ntile * 64;
   const f32x4 *src = reinterpret_cast<const f32x4 *>(part) + id;
   f32x4 v = zero4();
-  int ky = 0;
-  for (; ky + 8 <= nky; ky += 8) {
+  // groups past nky re-read the last one and are not added
+  for (int ky = 0; ky < nky; ky += 8) {
     f32x4 t[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = src[(long)(ky + j) * tstride];
+    for (int j = 0; j < 8; ++j) t[j] = src[(long)min(ky + j, nky - 1) * tstride];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
+      if (ky + j < nky) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] += t[j][i];
-  }
-  for (; ky < nky; ++ky) {
-    const f32x4 t = src[(long)ky * tstride];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] += t[i];
+        for (int i = 0; i < 4; ++i) v[i] += t[j][i];
+      }
   }
   if (r16 >= M) return;
 #pragma unroll
@@ -535,8 +533,18 @@ __global__ __launch_bounds__(256) void tile_reduce_kernel(const float *__restric
   const long id = (long)blockIdx.x * 256 + threadIdx.x;
   const long mn = (long)M * N;
   if (id >= mn) return;
+  // eight pieces' loads in flight at a time (a load-then-add loop waits for
+  // each); pieces past S re-read the last one and are not added, so the sum
+  // is taken in piece order
   float v = 0.f;
-  for (int z = 0; z < S; ++z) v += part[(long)z * mn + id];
+  for (int z = 0; z < S; z += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = part[(long)min(z + j, S - 1) * mn + id];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (z + j < S) v += t[j];
+  }
   const long m = id / N;
   store_out_m<TA, OM>(o, m, id - m * N, v);
 }
