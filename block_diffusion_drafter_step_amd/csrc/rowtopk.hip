@@ -68,7 +68,8 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
 
   // this thread's keys: segment entries tid + j * 512; 0 = no key (past the
   // segment, or a pad).  Loads past the segment re-read its last entry, so
-  // all of them are issued unconditionally, back to back.
+  // the only condition on a load is the segment width (the same for every
+  // thread) and they are issued back to back.
   unsigned long long kv[kRowSelPer];
   if constexpr (FROM_KEYS) {
     const unsigned long long *src = reinterpret_cast<const unsigned long long *>(in) + base;
