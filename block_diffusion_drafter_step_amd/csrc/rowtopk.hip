@@ -8,8 +8,9 @@
 // ascending index order, and no two keys are equal, so "the K largest keys"
 // is exactly the requested set.
 //
-// One workgroup of 512 threads owns one segment of a row (at most 8192
-// keys, 16 per thread, kept in registers; every load of a thread is issued
+// One workgroup of 512 threads (128 for segments of at most
+// DFL_ROWSEL_SMALL_SEG keys) owns one segment of a row (at most 8192 keys,
+// 16 per thread, kept in registers; every load of a thread is issued
 // before the first is used).  It finds the K-th largest key with eight radix
 // passes over 8-bit digits (most significant first: a 256-bin histogram of
 // the keys that still match the chosen prefix, then the digit whose bins
@@ -34,6 +35,10 @@ constexpr int kRowSelMaxK = 1024;
 #define DFL_ROWSEL_COPIES 8   // histogram copies (lane l adds to copy l % copies)
 #endif
 constexpr int kRowSelCopies = DFL_ROWSEL_COPIES;
+#ifndef DFL_ROWSEL_SMALL_SEG
+#define DFL_ROWSEL_SMALL_SEG 512   // segments up to this many keys run on 128 threads
+#endif
+static_assert(DFL_ROWSEL_SMALL_SEG <= 128 * kRowSelPer, "a 128-thread segment holds 16 keys per thread");
 static_assert((kRowSelCopies & (kRowSelCopies - 1)) == 0 && kRowSelCopies <= 64, "copies: a power of two");
 
 __device__ __forceinline__ unsigned long long row_key(float v, long col) {
@@ -49,8 +54,8 @@ __device__ __forceinline__ unsigned long long row_key(float v, long col) {
 // key lists, else fp32 scores.  Output: `keys_out` [row][n_seg][K] (0 pads
 // a short list), or, when n_seg == 1 and idx != nullptr, the final indices
 // and values.
-template <bool FROM_KEYS>
-__global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__restrict__ in, long n_in,
+template <bool FROM_KEYS, int NT>
+__global__ __launch_bounds__(NT) void rowsel_kernel(const void *__restrict__ in, long n_in,
                                                                 int seg, int K, const float *__restrict__ x,
                                                                 long n_cols, unsigned long long *keys_out,
                                                                 int32_t *idx, float *val) {
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
   const int len = (int)min((long)seg, n_in - seg0);
   const long base = row * n_in + seg0;
 
-  // this thread's keys: segment entries tid + j * 512; 0 = no key (past the
+  // this thread's keys: segment entries tid + j * NT; 0 = no key (past the
   // segment, or a pad).  Loads past the segment re-read its last entry, so
   // the only condition on a load is the segment width (the same for every
   // thread) and they are issued back to back.
@@ -75,27 +80,27 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
     const unsigned long long *src = reinterpret_cast<const unsigned long long *>(in) + base;
 #pragma unroll
     for (int j = 0; j < kRowSelPer; ++j)
-      if (j * kRowSelThreads < seg) kv[j] = src[min(tid + j * kRowSelThreads, len - 1)];
+      if (j * NT < seg) kv[j] = src[min(tid + j * NT, len - 1)];
 #pragma unroll
     for (int j = 0; j < kRowSelPer; ++j)
-      if (!(j * kRowSelThreads < seg && tid + j * kRowSelThreads < len)) kv[j] = 0ull;
+      if (!(j * NT < seg && tid + j * NT < len)) kv[j] = 0ull;
   } else {
     const float *src = reinterpret_cast<const float *>(in) + base;
     float xv[kRowSelPer];
 #pragma unroll
     for (int j = 0; j < kRowSelPer; ++j)
-      if (j * kRowSelThreads < seg) xv[j] = src[min(tid + j * kRowSelThreads, len - 1)];
+      if (j * NT < seg) xv[j] = src[min(tid + j * NT, len - 1)];
 #pragma unroll
     for (int j = 0; j < kRowSelPer; ++j) {
-      const int i = tid + j * kRowSelThreads;
-      kv[j] = j * kRowSelThreads < seg && i < len ? row_key(xv[j], seg0 + i) : 0ull;
+      const int i = tid + j * NT;
+      kv[j] = j * NT < seg && i < len ? row_key(xv[j], seg0 + i) : 0ull;
     }
   }
   if (tid == 0) {
     sel_n = 0;
     n_real = 0;
   }
-  for (int b = tid; b < kRowSelCopies * 257; b += kRowSelThreads) histc[b] = 0;
+  for (int b = tid; b < kRowSelCopies * 257; b += NT) histc[b] = 0;
   __syncthreads();
   // keys in the segment (pads of a previous pass excluded)
   unsigned nr = (unsigned)len;
@@ -125,14 +130,14 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
         if (k != 0ull && (k & mask) == prefix) atomicAdd(&mine[(unsigned)(k >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid < 256) {
+      for (int b = tid; b < 256; b += NT) {
         unsigned sum = 0;
 #pragma unroll
         for (int c = 0; c < kRowSelCopies; ++c) {
-          sum += histc[c * 257 + tid];
-          histc[c * 257 + tid] = 0;
+          sum += histc[c * 257 + b];
+          histc[c * 257 + b] = 0;
         }
-        hist[tid] = sum;
+        hist[b] = sum;
       }
       __syncthreads();
       // wave 0: lane l holds bins 252 - 4l .. 255 - 4l (descending digits);
@@ -195,11 +200,11 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
   int P = 1;
   while (last && P < K) P <<= 1;
   if (!last) P = 0;
-  for (int i = n_keep + tid; i < (last ? P : K); i += kRowSelThreads) sel[i] = 0ull;
+  for (int i = n_keep + tid; i < (last ? P : K); i += NT) sel[i] = 0ull;
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < P / 2; t += kRowSelThreads) {
+      for (int t = tid; t < P / 2; t += NT) {
         const int i = 2 * t - (t & (stride - 1));   // lower element of the pair
         const int j = i + stride;
         const bool desc = (i & size) == 0;          // direction of this run
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
   }
 
   if (last) {
-    for (int j = tid; j < K; j += kRowSelThreads) {
+    for (int j = tid; j < K; j += NT) {
       // a row holds at least K real keys, so no pad (0) reaches the output;
       // the check only keeps a broken invariant from reading out of range
       const unsigned col = ~(unsigned)(sel[j] & 0xffffffffull);
@@ -223,18 +228,25 @@ __global__ __launch_bounds__(kRowSelThreads) void rowsel_kernel(const void *__re
       val[row * K + j] = ok ? x[row * n_cols + col] : __builtin_nanf("");
     }
   } else {
-    for (int j = tid; j < K; j += kRowSelThreads)
+    for (int j = tid; j < K; j += NT)
       keys_out[(row * n_seg + blockIdx.x) * (long)K + j] = sel[j];
   }
 }
 
 // Segment width of a pass over rows of n elements: at most 8192 (16 keys
 // per thread), at least 2K so every pass shrinks the candidates, smaller
-// while the grid would leave CUs idle.
+// while the grid would leave CUs idle.  A row that fits one segment takes
+// the smallest width (a power of two, at least 512) that holds it, so its
+// threads issue no loads past the row.
 static int rowsel_seg(long n_rows, long n, int K) {
   const int lo = K * 2 > 1024 ? K * 2 : 1024;
   int seg = kRowSelMaxSeg;
   while (seg / 2 >= lo && n_rows * ((n + seg - 1) / seg) < 2 * 256) seg /= 2;
+  if (n <= seg) {
+    int fit = kRowSelThreads;
+    while (fit < n) fit *= 2;
+    seg = fit;
+  }
   return seg;
 }
 
@@ -267,12 +279,19 @@ hipError_t launch_rowtopk(const float *x, long n_rows, long n_cols, int K, int32
     unsigned long long *out =
         n_seg == 1 ? nullptr : reinterpret_cast<unsigned long long *>((pass & 1) ? buf_b : buf_a);
     const dim3 grid((unsigned)n_seg, (unsigned)n_rows);
-    if (keys)
-      hipLaunchKernelGGL(rowsel_kernel<true>, grid, dim3(kRowSelThreads), 0, st, in, n, seg, K, x, n_cols, out,
+    const bool small = seg <= DFL_ROWSEL_SMALL_SEG;
+    if (keys && small)
+      hipLaunchKernelGGL((rowsel_kernel<true, 128>), grid, dim3(128), 0, st, in, n, seg, K, x, n_cols, out,
+                         idx, val);
+    else if (keys)
+      hipLaunchKernelGGL((rowsel_kernel<true, kRowSelThreads>), grid, dim3(kRowSelThreads), 0, st, in, n, seg,
+                         K, x, n_cols, out, idx, val);
+    else if (small)
+      hipLaunchKernelGGL((rowsel_kernel<false, 128>), grid, dim3(128), 0, st, in, n, seg, K, x, n_cols, out,
                          idx, val);
     else
-      hipLaunchKernelGGL(rowsel_kernel<false>, grid, dim3(kRowSelThreads), 0, st, in, n, seg, K, x, n_cols,
-                         out, idx, val);
+      hipLaunchKernelGGL((rowsel_kernel<false, kRowSelThreads>), grid, dim3(kRowSelThreads), 0, st, in, n,
+                         seg, K, x, n_cols, out, idx, val);
     if (n_seg == 1) break;
     in = out;
     n = n_seg * K;

@@ -354,6 +354,14 @@ def test_topk_rows_random(rows, cols, K):
     run_topk_rows(rng.standard_normal((rows, cols)).astype(np.float32), K)
 
 
+@pytest.mark.parametrize("rows,cols,K", [(65535, 130, 7), (3, 200000, 1), (2, 16384, 64), (1, 8192, 1024)])
+def test_topk_rows_limits(rows, cols, K):
+    """The most rows a call takes (one grid row each), K = 1 from wide rows,
+    widths that are whole segments, and the largest K on one segment."""
+    rng = np.random.default_rng(rows + cols + K)
+    run_topk_rows(rng.standard_normal((rows, cols)).astype(np.float32), K)
+
+
 @pytest.mark.parametrize("rows,cols,K", [(3, 11284, 100), (2, 22548, 1000), (4, 81925, 1000)])
 def test_topk_rows_short_last_list(rows, cols, K):
     """Widths whose last segment holds fewer than K scores: its candidate
