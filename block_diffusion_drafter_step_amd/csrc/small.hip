@@ -50,7 +50,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ 
       if (j * 256 < nv) v[j] = yv[min(tid + j * 256, nv - 1)];
 #pragma unroll
     for (int j = 0; j < kRmsHeld; ++j)
-      if (j * 256 < nv && tid + j * 256 < nv) ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
+      if (j * 256 < nv && tid + j * 256 < nv)
+        ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
   } else {
     for (int c = tid; c < nv; c += 256) {
       const f32x4 t = yv[c];
