@@ -446,28 +446,29 @@ __global__ __launch_bounds__(1024) void selector_fused_kernel(SelArgs a) {
   const int anchor = a.anchor < 0 ? 0 : a.anchor;   // row unused without an anchor
   const int vpr = r / EPV, nvec = 2 * BK * vpr;
   constexpr int UNR = 4;
+  // the loads of a thread are issued back to back: no branch around them or
+  // their addresses; vectors past the end reload the last one and store it
+  // again (the same bytes to the same place)
   for (int v0 = tid; v0 < nvec; v0 += 1024 * UNR) {
-    uint4 buf[UNR];
+    u32x4 buf[UNR];
 #pragma unroll
-    for (int j = 0; j < UNR; ++j) {   // past the end: reload the last vector
+    for (int j = 0; j < UNR; ++j) {
       const int v = min(v0 + 1024 * j, nvec - 1);
       const int row = v / vpr, part = v - row * vpr;
-      const TA *src;
-      if (row < BK) {   // predecessor a of position i: A[idx[i-1][a]] (A[anchor] at i = 0)
-        const int i = row / K, ai = row - i * K;
-        src = A + (long)(i == 0 ? anchor : sidx[(i - 1) * K + ai]) * r;
-      } else {          // candidate b of position i: B[idx[i][b]]
-        src = Bc + (long)sidx[row - BK] * r;
-      }
-      buf[j] = *reinterpret_cast<const uint4 *>(src + part * EPV);
+      // rows [0, BK): predecessor a of position i, A[idx[i-1][a]] (A[anchor]
+      // at i = 0); rows [BK, 2 BK): candidate b of position i, B[idx[i][b]]
+      const bool pred = row < BK;
+      const int rr = pred ? row : row - BK;
+      const int i = rr / K, ai = rr - i * K;
+      const int pid = i == 0 ? anchor : sidx[max((i - 1) * K + ai, 0)];
+      const TA *src = pred ? A + (long)pid * r : Bc + (long)sidx[rr] * r;
+      buf[j] = *reinterpret_cast<const u32x4 *>(src + part * EPV);
     }
 #pragma unroll
     for (int j = 0; j < UNR; ++j) {
-      const int v = v0 + 1024 * j;
-      if (v < nvec) {
-        const int row = v / vpr, part = v - row * vpr;
-        *reinterpret_cast<uint4 *>(rows + row * rs + part * EPV) = buf[j];
-      }
+      const int v = min(v0 + 1024 * j, nvec - 1);
+      const int row = v / vpr, part = v - row * vpr;
+      *reinterpret_cast<u32x4 *>(rows + row * rs + part * EPV) = buf[j];
     }
   }
   __syncthreads();
