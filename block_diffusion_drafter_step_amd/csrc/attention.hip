@@ -24,10 +24,6 @@
 #include "common.h"
 #include "kernels.h"
 
-#ifndef DFL_ATTN_NT_PART
-#define DFL_ATTN_NT_PART 0   // 1: split partials written with non-temporal stores
-#endif
-
 namespace dfl {
 
 #ifndef DFL_ATTN_WGS
@@ -357,17 +353,6 @@ __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_s
     const int hq = kvh * grp + wave + 4 * hh;
     const long base = ((long)hq * a.B + r16) * a.n_split + sp;
     float *po = a.part_o + base * HD;
-#if DFL_ATTN_NT_PART
-    // streamed past L2: the combine kernel reads them from memory anyway
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-      __builtin_nontemporal_store(f32x4{o[hh][dt][0], o[hh][dt][1], o[hh][dt][2], o[hh][dt][3]},
-                                  reinterpret_cast<f32x4 *>(po + 16 * dt + 4 * g));
-    if (g == 0) {
-      __builtin_nontemporal_store(m_run[hh], a.part_ml + base * 2);
-      __builtin_nontemporal_store(l_run[hh], a.part_ml + base * 2 + 1);
-    }
-#else
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -376,7 +361,6 @@ __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_s
       a.part_ml[base * 2] = m_run[hh];
       a.part_ml[base * 2 + 1] = l_run[hh];
     }
-#endif
   }
 }
 

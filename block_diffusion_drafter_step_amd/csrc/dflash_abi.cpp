@@ -92,8 +92,8 @@ dflash_status check_ws(void *ws, size_t ws_bytes, size_t need) {
 struct Carve {
   char *base;
   size_t off = 0;
-  unsigned *counters;
-  explicit Carve(void *p) : base((char *)p) { counters = (unsigned *)take(kCounterBytes); }
+  unsigned long long *counters;
+  explicit Carve(void *p) : base((char *)p) { counters = (unsigned long long *)take(kCounterBytes); }
   void *take(size_t bytes) {
     void *p = base ? base + off : nullptr;
     off += (bytes + 255) & ~(size_t)255;
@@ -146,8 +146,8 @@ OutSpec out_act(void *p, long ld, const void *resid, long ld_resid) {
   return o;
 }
 
-hipError_t gemm(int act, int wkind, const ASrc &A, int M, const WSet &W, float *part, unsigned *cnt,
-                const OutSpec &o, hipStream_t st) {
+hipError_t gemm(int act, int wkind, const ASrc &A, int M, const WSet &W, float *part,
+                unsigned long long *cnt, const OutSpec &o, hipStream_t st) {
   if (M <= kSkinnyMaxM) return launch_skinny_gemm(act, wkind, A, M, W, part, cnt, o, st);
   return launch_tile_gemm(act, wkind, A, M, W, o, part, st);
 }
@@ -165,10 +165,12 @@ constexpr int64_t kMaxRows = (int64_t)1 << 26;
 
 // --- workspace sizes (buffers in the act type are sized for fp32) --------------
 
-size_t inject_ws(int32_t n_layers, int64_t n, int32_t d_t, int32_t d, int32_t kv) {
+// `z_off`, when given, receives z's offset
+size_t inject_ws(int32_t n_layers, int64_t n, int32_t d_t, int32_t d, int32_t kv, size_t *z_off = nullptr) {
   Carve c(nullptr);
   c.take(std::max(gemm_partial_bytes((int)n, d, n_layers * d_t), gemm_partial_bytes((int)n, 2 * kv, d)));
   c.take((size_t)n * d * 4);  // y
+  if (z_off) *z_off = c.off;
   c.take((size_t)n * d * 4);  // z
   if (n >= kQ8ExpandMinM) {   // bf16 expansions of Q8_0 fc, Wk and Wv
     c.take((size_t)d * n_layers * d_t * 2);
@@ -186,14 +188,18 @@ size_t conv_ws(int32_t n_blocks, int32_t B, int32_t C, int32_t G, int32_t T) {
   return c.off;
 }
 
-size_t attn_ws(int32_t B, int32_t d, int32_t Hq, int32_t Hkv, int32_t hd, int64_t n_ctx) {
+// `qkv_off` / `o_off`, when given, receive the offsets of Q | Kb | Vb and O
+size_t attn_ws(int32_t B, int32_t d, int32_t Hq, int32_t Hkv, int32_t hd, int64_t n_ctx,
+               size_t *qkv_off = nullptr, size_t *o_off = nullptr) {
   Carve c(nullptr);
   const int qdim = Hq * hd, kv = Hkv * hd;
   c.take(std::max(gemm_partial_bytes(B, qdim + 2 * kv, d), gemm_partial_bytes(B, d, qdim)));
+  if (qkv_off) *qkv_off = c.off;
   c.take((size_t)B * (qdim + 2 * kv) * 4);  // Q | Kb | Vb
   const int n_split = attn_max_splits(n_ctx, Hkv);   // >= the plan's split count
   c.take((size_t)Hq * B * n_split * hd * 4);  // partial O
   c.take((size_t)Hq * B * n_split * 2 * 4);   // partial (max, sum)
+  if (o_off) *o_off = c.off;
   c.take((size_t)B * qdim * 4);               // O
   return c.off;
 }
@@ -259,6 +265,31 @@ size_t dflash_inject_workspace(int32_t n_layers, int64_t n_tokens, int32_t d_t, 
   (void)act;
   if (n_layers < 1 || n_tokens < 1 || d_t < 1 || d < 1 || kv < 1) return 0;
   return inject_ws(n_layers, n_tokens, d_t, d, kv);
+}
+
+size_t dflash_inject_z_offset(int32_t n_layers, int64_t n_tokens, int32_t d_t, int32_t d, int32_t kv,
+                              int32_t act) {
+  (void)act;
+  if (n_layers < 1 || n_tokens < 1 || d_t < 1 || d < 1 || kv < 1) return 0;
+  size_t z = 0;
+  inject_ws(n_layers, n_tokens, d_t, d, kv, &z);
+  return z;
+}
+
+size_t dflash_block_attn_qkv_offset(int32_t B, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, int64_t n_ctx) {
+  if (B < 1 || d < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1 || n_ctx < 0) return 0;
+  size_t q = 0;
+  attn_ws(B, d, n_q_heads, n_kv_heads, head_dim, n_ctx, &q, nullptr);
+  return q;
+}
+
+size_t dflash_block_attn_o_offset(int32_t B, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int64_t n_ctx) {
+  if (B < 1 || d < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1 || n_ctx < 0) return 0;
+  size_t o = 0;
+  attn_ws(B, d, n_q_heads, n_kv_heads, head_dim, n_ctx, nullptr, &o);
+  return o;
 }
 
 size_t dflash_conv_workspace(int32_t n_blocks, int32_t B, int32_t C, int32_t G, int32_t T) {

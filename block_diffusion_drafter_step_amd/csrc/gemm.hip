@@ -14,6 +14,7 @@
 //    next k-tile.  The activation operand may be several arrays side by side
 //    along K (the concatenated target-layer features are never materialised).
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "kernels.h"
@@ -81,18 +82,39 @@ __device__ __forceinline__ int seg_of(const WSet &W, int n, int *local) {
 //    k-ranges (WPG y + wave) * kchunk of it; their accumulators are summed in
 //    LDS in a fixed pairwise order.  With one k-group the workgroup writes
 //    the outputs.  Otherwise it writes one partial per tile, and the last
-//    workgroup of the tile group to finish -- found with the counter cnt[x],
-//    which it returns to zero -- sums the partials in k-group order and
+//    workgroup of the tile group to finish -- found with the completion
+//    counter cnt[x] (arrive_last) -- sums the partials in k-group order and
 //    writes the outputs: one kernel, bitwise reproducible (the order never
-//    depends on which workgroup finishes last).  Partials are written and
-//    read with device-scope (cross-XCD coherent) accesses, so no cache-wide
-//    write-back or invalidate is needed, and no workgroup ever waits for
-//    another.  Best for small weights, where a second launch would cost more
-//    than the stream.  cnt == nullptr: partials only, as for SPLIT_TILES.
+//    depends on which workgroup finishes last), and no workgroup ever waits
+//    for another.  Best for small weights, where a second launch would cost
+//    more than the stream.  cnt == nullptr: partials only, as for SPLIT_TILES.
+//
+// Ordering of that hand-over (HIP's scoped memory model): partials are
+// agent-scope atomic stores; each wave waits for its own stores, a
+// workgroup barrier follows, then one thread counts the arrival with an
+// agent-scope release CAS.  The thread that sees the last arrival issues an
+// agent-scope acquire fence before a second barrier, so every partial
+// happens-before the loads that sum them (on gfx950: buffer_wbl2 sc1 before
+// each arrival, buffer_inv sc1 once per tile group, sc1 loads and stores).
+// Completion counter of one tile group: a 64-bit word (stamp << 16) | count.
+// `stamp` is unique to the launch, so a word holding any other stamp (left by
+// an earlier launch, a call that never completed, or anything else written
+// there) counts as zero arrivals: the counters need no clearing, in any
+// order of calls.  Returns true for the n-th arrival of this launch.  Release
+// on the CAS: this workgroup's partials are visible before it is counted.
+__device__ __forceinline__ bool arrive_last(unsigned long long *c, unsigned long long stamp, int n) {
+  unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), nw;
+  do {
+    nw = (old >> 16) == stamp ? old + 1 : ((stamp << 16) | 1ull);
+  } while (!__hip_atomic_compare_exchange_weak(c, &old, nw, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT));
+  return (int)(nw & 0xffffu) == n;
+}
+
 template <typename TA, int WK, int TPW, int WPG, bool SPLIT_TILES>
 __global__ __launch_bounds__(WPG * 64, WPG >= 8 ? WPG / 4 : 2) void skinny_gemm_kernel(
-    ASrc X, int M, WSet W, int kchunk, float *__restrict__ part, unsigned *__restrict__ cnt,
-    OutSpec o) {
+    ASrc X, int M, WSet W, int kchunk, float *__restrict__ part,
+    unsigned long long *__restrict__ cnt, unsigned long long stamp, OutSpec o) {
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a scalar: tiles, k-range and loop bounds stay uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -179,17 +201,17 @@ __global__ __launch_bounds__(WPG * 64, WPG >= 8 ? WPG / 4 : 2) void skinny_gemm_
                              __HIP_MEMORY_SCOPE_AGENT);
       }
       if (!cnt) return;
-      // this workgroup's partials are complete device-wide before it counts
+      // every wave's partial stores have completed before the arrival counts
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (tid == 0)
-        last = __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(nky - 1);
+      if (tid == 0) {
+        const bool l = arrive_last(&cnt[blockIdx.x], stamp, nky);
+        if (l) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        last = l;
+      }
       __syncthreads();
-      if (!last) return;
-      if (tid == 0) __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (!mine) return;
+      if (!last || !mine) return;
       v = zero4();
       int ky = 0;
       for (; ky + 4 <= nky; ky += 4) {
@@ -285,10 +307,6 @@ struct SkinnyPlan {
 #ifndef DFL_SKINNY_TPW
 #define DFL_SKINNY_TPW 2
 #endif
-// 0: always sum the partials with splitk_reduce_kernel
-#ifndef DFL_SKINNY_COUNTERS
-#define DFL_SKINNY_COUNTERS 1
-#endif
 static SkinnyPlan skinny_plan(int N, int K, bool f32, int align = 64) {
   SkinnyPlan p;
   const int ntile = (N + 15) / 16;
@@ -333,30 +351,43 @@ size_t skinny_partial_floats(int n_total, int K) {
   return most;
 }
 
+// launch stamps of the completion counters: 48 bits, never 0 (a zeroed
+// word then never matches), one per launch that uses counters
+static std::atomic<unsigned long long> g_stamp{0};
+static unsigned long long next_stamp() {
+  unsigned long long s;
+  do {
+    s = (g_stamp.fetch_add(1, std::memory_order_relaxed) + 1) & 0xFFFFFFFFFFFFull;
+  } while (s == 0);
+  return s;
+}
+
 template <typename TA, int WK>
-static hipError_t skinny_launch_t(const ASrc &X, int M, const WSet &W, float *part, unsigned *cnt,
-                                  const OutSpec &out, hipStream_t st) {
+static hipError_t skinny_launch_t(const ASrc &X, int M, const WSet &W, float *part,
+                                  unsigned long long *cnt, const OutSpec &out, hipStream_t st) {
   const SkinnyPlan p = skinny_plan(W.n_total, W.K, sizeof(TA) == 4, WK == W_Q8_0_S4 ? 128 : 64);
   const dim3 grid(p.groups, p.kgroups);
-  unsigned *c = nullptr;
+  unsigned long long *c = nullptr;
+  unsigned long long stamp = 0;
   if (p.split_tiles) {
     if (sizeof(TA) == 2 && p.tpw == 4)
       hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, sizeof(TA) == 2 ? 4 : 2, 4, true>), grid,
-                         dim3(256), 0, st, X, M, W, p.kchunk, part, c, out);
+                         dim3(256), 0, st, X, M, W, p.kchunk, part, c, stamp, out);
     else if (p.tpw == 2)
       hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 2, 4, true>), grid, dim3(256), 0, st, X, M, W,
-                         p.kchunk, part, c, out);
+                         p.kchunk, part, c, stamp, out);
     else
       hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 1, 4, true>), grid, dim3(256), 0, st, X, M, W,
-                         p.kchunk, part, c, out);
+                         p.kchunk, part, c, stamp, out);
   } else {
-    c = DFL_SKINNY_COUNTERS && p.groups <= kMaxCounters ? cnt : nullptr;
+    c = p.groups <= kMaxCounters && p.kgroups < (1 << 16) ? cnt : nullptr;
+    if (c) stamp = next_stamp();
     if (p.wpg == 4)
       hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 1, 4, false>), grid, dim3(256), 0, st, X, M, W,
-                         p.kchunk, part, c, out);
+                         p.kchunk, part, c, stamp, out);
     else
       hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 1, 8, false>), grid, dim3(512), 0, st, X, M, W,
-                         p.kchunk, part, c, out);
+                         p.kchunk, part, c, stamp, out);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c || p.kgroups == 1) return e;
@@ -367,7 +398,7 @@ static hipError_t skinny_launch_t(const ASrc &X, int M, const WSet &W, float *pa
 }
 
 hipError_t launch_skinny_gemm(int act, int wkind, const ASrc &X, int M, const WSet &W, float *part,
-                              unsigned *cnt, const OutSpec &out, hipStream_t st) {
+                              unsigned long long *cnt, const OutSpec &out, hipStream_t st) {
   if (act == ACT_F32) return skinny_launch_t<float, W_SAME>(X, M, W, part, cnt, out, st);
   // Q8_0 with every k-range on a 128 boundary (k-chunks rounded to 128):
   // one 8-byte scale load per 128-wide chunk
@@ -601,92 +632,6 @@ static void tile_launch_t(const ASrc &A, int M, const WSet &W, const OutSpec &ou
   else tile_go<TA, WK, OUT_CACHE>(A, M, W, out, part, st);
 }
 
-// ---------------------------------------------------------------------------
-// big-tile GEMM for the prefill injection: 256 x 256 x 64 tiles, 4 waves each
-// computing a 128 x 128 block (8 x 8 MFMA tiles, 256 fp32 accumulators), so
-// every fragment read from LDS feeds 8 MFMAs and LDS bandwidth stays below the
-// MFMA rate.  Double-buffered LDS (2 x 2 x 256 x 72 bf16 = 147 KB), the next
-// k-tile prefetched into registers while the current one is multiplied.
-// Tiles are ordered XCD-aware: workgroups are dealt to the 8 XCDs round-robin,
-// so each XCD is given a contiguous band of M-tiles, walked in groups of 4
-// M-tiles x all N-tiles, and the workgroups resident on one XCD share A and B
-// tiles in that XCD's L2.
-// ---------------------------------------------------------------------------
-constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8;
-
-template <int WK>
-struct BigLoader {
-  uint4 a[8];
-  uint4 w[8];      // SAME: 16-byte chunks; Q8_0: 4 x 16 codes in w[0..3]
-  float sc[4];
-
-  __device__ __forceinline__ void load(const ASrc &A, int M, const WSet &W, int m0, int n0, int k0,
-                                       int tid) {
-    const int s = k0 / A.k_per_src;
-    const int kl = k0 - s * A.k_per_src;
-    const bf16 *src = reinterpret_cast<const bf16 *>(pick(A.ptr, s));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = tid + 256 * j;          // 2048 chunks: row c / 8, chunk c % 8
-      const int row = c >> 3, ch = c & 7;
-      const int m = min(m0 + row, M - 1);
-      a[j] = *reinterpret_cast<const uint4 *>(src + (long)m * A.k_per_src + kl + ch * 8);
-    }
-    if constexpr (WK == W_Q8_0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = tid + 256 * j;        // 1024 chunks of 16 codes: row c / 4, chunk c % 4
-        const int row = c >> 2, ch = c & 3;
-        const int n = min(n0 + row, W.n_total - 1);
-        int lr;
-        const int sg = seg_of(W, n, &lr);
-        const int8_t *q = reinterpret_cast<const int8_t *>(pick(W.data, sg)) + (long)lr * W.K + k0 + ch * 16;
-        w[j] = *reinterpret_cast<const uint4 *>(q);
-        const uint16_t *scp = reinterpret_cast<const uint16_t *>(pick(W.scales, sg)) + (long)lr * (W.K >> 5);
-        sc[j] = half_bits_to_f32(scp[(k0 + ch * 16) >> 5]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = tid + 256 * j;
-        const int row = c >> 3, ch = c & 7;
-        const int n = min(n0 + row, W.n_total - 1);
-        int lr;
-        const int sg = seg_of(W, n, &lr);
-        w[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const bf16 *>(pick(W.data, sg)) +
-                                                (long)lr * W.K + k0 + ch * 8);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(bf16 *As, bf16 *Ws, int tid) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c >> 3, ch = c & 7;
-      *reinterpret_cast<uint4 *>(As + row * GLD + ch * 8) = a[j];
-    }
-    if constexpr (WK == W_Q8_0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = tid + 256 * j;
-        const int row = c >> 2, ch = c & 3;
-        const Frag<bf16> lo = dequant8(make_uint2(w[j].x, w[j].y), sc[j]);
-        const Frag<bf16> hi = dequant8(make_uint2(w[j].z, w[j].w), sc[j]);
-        *reinterpret_cast<bf16x8 *>(Ws + row * GLD + ch * 16) = lo.v;
-        *reinterpret_cast<bf16x8 *>(Ws + row * GLD + ch * 16 + 8) = hi.v;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = tid + 256 * j;
-        const int row = c >> 3, ch = c & 7;
-        *reinterpret_cast<uint4 *>(Ws + row * GLD + ch * 8) = w[j];
-      }
-    }
-  }
-};
-
 // workgroup id -> (m-tile, n-tile)
 #ifndef DFL_TILE_GROUP_M
 #define DFL_TILE_GROUP_M 4
@@ -707,103 +652,19 @@ __device__ __forceinline__ void big_tile_of(int L, int mt, int nt, int *tm, int 
   *tm = grp * GM + (rem - *tn * gm);
 }
 
-template <int WK, int OM>
-__global__ __launch_bounds__(256) void big_gemm_kernel(ASrc A, int M, WSet W, OutSpec o) {
-  extern __shared__ __attribute__((aligned(16))) char smem_big[];
-  bf16 *As = reinterpret_cast<bf16 *>(smem_big);            // [2][256][GLD]
-  bf16 *Ws = As + 2 * GBM * GLD;                            // [2][256][GLD]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int mt = (M + GBM - 1) / GBM, nt = (W.n_total + GBN - 1) / GBN;
-  int tm, tn;
-  big_tile_of(blockIdx.x, mt, nt, &tm, &tn);
-  const int m0 = tm * GBM, n0 = tn * GBN;
-  const int nk = W.K / GBK;
-
-  f32x4 acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = zero4();
-
-  BigLoader<WK> ld;
-  ld.load(A, M, W, m0, n0, 0, tid);
-  ld.store(As, Ws, tid);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    ld.load(A, M, W, m0, n0, min(kt + 1, nk - 1) * GBK, tid);
-    const bf16 *as = As + cur * GBM * GLD + (wm * 128 + r16) * GLD + 8 * g;
-    const bf16 *ws = Ws + cur * GBN * GLD + (wn * 128 + r16) * GLD + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < GBK; kk += 32) {
-      Frag<bf16> fb[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) fb[j] = load_frag(ws + 16 * j * GLD + kk);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const Frag<bf16> fa = load_frag(as + 16 * i * GLD + kk);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mma(acc[i][j], fa, fb[j]);
-      }
-    }
-    ld.store(As + (cur ^ 1) * GBM * GLD, Ws + (cur ^ 1) * GBN * GLD, tid);
-    __syncthreads();
-  }
-  // acc[i][j][v]: row m0 + wm*128 + 16 i + 4 g + v, column n0 + wn*128 + 16 j + r16
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = n0 + wn * 128 + 16 * j + r16;
-      if (n >= W.n_total) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * 128 + 16 * i + 4 * g + v;
-        if (m < M) store_out_m<bf16, OM>(o, m, n, acc[i][j][v]);
-      }
-    }
-}
-
-constexpr size_t kBigLds = (size_t)2 * (GBM + GBN) * GLD * sizeof(bf16);
-
-template <int WK>
-static void big_launch_t(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
-  const int mt = (M + GBM - 1) / GBM, nt = (W.n_total + GBN - 1) / GBN;
-  const dim3 grid(mt * nt);
-  if (out.mode == OUT_F32) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&big_gemm_kernel<WK, OUT_F32>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
-    hipLaunchKernelGGL((big_gemm_kernel<WK, OUT_F32>), grid, dim3(256), kBigLds, st, A, M, W, out);
-  } else if (out.mode == OUT_ACT) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&big_gemm_kernel<WK, OUT_ACT>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
-    hipLaunchKernelGGL((big_gemm_kernel<WK, OUT_ACT>), grid, dim3(256), kBigLds, st, A, M, W, out);
-  } else {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&big_gemm_kernel<WK, OUT_CACHE>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
-    hipLaunchKernelGGL((big_gemm_kernel<WK, OUT_CACHE>), grid, dim3(256), kBigLds, st, A, M, W, out);
-  }
-}
-
 #ifndef DFL_BIG_GEMM_MIN_M
 #define DFL_BIG_GEMM_MIN_M 1024
 #endif
 
 // ---------------------------------------------------------------------------
-// prefill GEMM with direct-to-LDS loads (bf16 activations and weights).
-// 256 x 256 tile, k-step 32, 4 waves each owning a 128 x 128 block.  Global
-// memory is copied into LDS by global_load_lds_dwordx4 (no register staging)
-// into a 4-stage ring of 32 KB stages, so three k-steps of loads are in flight
-// while one is multiplied; one barrier per k-step.  A wave instruction writes
-// 1 KB of LDS in lane order (16 rows x 64 bytes); within a row the four
-// 16-byte slots hold chunks c ^ ((row / 4) & 3), so the 16 rows read by one
-// fragment load fall in 16 different bank groups.
+// prefill GEMM with direct-to-LDS loads (bf16 activations and weights): a
+// 256-wide block tile along N, k-steps of 32.  Global memory is copied into
+// LDS by global_load_lds_dwordx4 (no register staging) into a ring of
+// stages, so several k-steps of loads are in flight while one is multiplied;
+// one barrier per k-step.  A wave instruction writes 1 KB of LDS in lane
+// order (16 rows x 64 bytes).
 // ---------------------------------------------------------------------------
-constexpr int DBM = 256, DBN = 256, DBK = 32, DSTAGES = 4;
-constexpr int DSTAGE_BYTES = (DBM + DBN) * DBK * 2;   // 32 KB
+constexpr int DBN = 256, DBK = 32;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -837,104 +698,13 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// issue one stage: A rows [m0, m0+256) and W rows [n0, n0+256), k [k0, k0+32)
-__device__ __forceinline__ void dma_stage(char *stage, const ASrc &A, int M, const WSet &W, int m0,
-                                          int n0, int k0, int wave, int lane) {
-  const int s = k0 / A.k_per_src;
-  const int kl = k0 - s * A.k_per_src;
-  const bf16 *src = reinterpret_cast<const bf16 *>(pick(A.ptr, s));
-  const int rl = lane >> 2, slot = lane & 3;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (wave * 4 + j) * 16 + rl;
-    const int c = dslot(row, slot);
-    const int m = min(m0 + row, M - 1);
-    dma16(src + (long)m * A.k_per_src + kl + 8 * c,
-          (lds_void *)(stage + (wave * 4 + j) * 1024));
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (wave * 4 + j) * 16 + rl;
-    const int c = dslot(row, slot);
-    const int n = min(n0 + row, W.n_total - 1);
-    int lr;
-    const int sg = seg_of(W, n, &lr);
-    const bf16 *wp = reinterpret_cast<const bf16 *>(pick(W.data, sg)) + (long)lr * W.K + k0 + 8 * c;
-    dma16(wp, (lds_void *)(stage + DBM * DBK * 2 + (wave * 4 + j) * 1024));
-  }
-}
-
-template <int OM>
-__global__ __launch_bounds__(256) void dma_gemm_kernel(ASrc A, int M, WSet W, OutSpec o) {
-  extern __shared__ __attribute__((aligned(1024))) char smem_dma[];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int mt = (M + DBM - 1) / DBM, nt = (W.n_total + DBN - 1) / DBN;
-  int tm, tn;
-  big_tile_of(blockIdx.x, mt, nt, &tm, &tn);
-  const int m0 = tm * DBM, n0 = tn * DBN;
-  const int nk = W.K / DBK;
-
-  f32x4 acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = zero4();
-
-  // prologue: stages 0 .. DSTAGES-2 in flight (re-issuing the last k-step when
-  // nk is short keeps the count of outstanding loads fixed)
-#pragma unroll
-  for (int s = 0; s < DSTAGES - 1; ++s)
-    dma_stage(smem_dma + s * DSTAGE_BYTES, A, M, W, m0, n0, min(s, nk - 1) * DBK, wave, lane);
-
-  // this lane's fragment rows and swizzled slots
-  const int ar = wm * 128 + r16, br = wn * 128 + r16;
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vm<8 * (DSTAGES - 2)>();   // this wave's loads of stage kt have landed
-    __syncthreads();                 // ... everyone's, and stage kt-1 is no longer read
-    dma_stage(smem_dma + ((kt + DSTAGES - 1) % DSTAGES) * DSTAGE_BYTES, A, M, W, m0, n0,
-              min(kt + DSTAGES - 1, nk - 1) * DBK, wave, lane);
-    const char *st = smem_dma + (kt % DSTAGES) * DSTAGE_BYTES;
-    const bf16 *as = reinterpret_cast<const bf16 *>(st);
-    const bf16 *ws = reinterpret_cast<const bf16 *>(st + DBM * DBK * 2);
-    Frag<bf16> fb[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = br + 16 * j;
-      fb[j] = load_frag(ws + row * DBK + 8 * dslot(row, g));
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = ar + 16 * i;
-      const Frag<bf16> fa = load_frag(as + row * DBK + 8 * dslot(row, g));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mma(acc[i][j], fa, fb[j]);
-    }
-  }
-  wait_vm<0>();
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = n0 + wn * 128 + 16 * j + r16;
-      if (n >= W.n_total) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * 128 + 16 * i + 4 * g + v;
-        if (m < M) store_out_m<bf16, OM>(o, m, n, acc[i][j][v]);
-      }
-    }
-}
-
 // 256 x 256 block tile on 8 waves (2 along M x 4 along N, 128 x 64 each):
 // 128 accumulator registers per wave leave the fragments and addresses in
 // VGPRs (a 128 x 128 wave tile fills the VGPR file with accumulators and the
 // compiler shuttles operands through AGPRs), and two waves per SIMD hide each
-// other's LDS and barrier stalls.  Same 4-stage direct-to-LDS ring and
-// swizzle as dma_gemm_kernel; each wave issues 2 A and 2 W row blocks per
-// stage from row pointers fixed before the loop, and the activation source
+// other's LDS and barrier stalls.  A 4-stage direct-to-LDS ring with the
+// dslot swizzle; each wave issues 2 A and 2 W row blocks per stage from row
+// pointers fixed before the loop, and the activation source
 // advances without a division.  TBM = 128 halves the block along M (64 x 64
 // wave tiles, one A row block per wave per stage) for products whose 256-row
 // tiles would leave CUs idle, e.g. the conv's delta (N = T*G = 256).
@@ -942,9 +712,6 @@ __global__ __launch_bounds__(256) void dma_gemm_kernel(ASrc A, int M, WSet W, Ou
 #define DFL_DMA8_STAGES 4
 #endif
 constexpr int D8STAGES = DFL_DMA8_STAGES;
-#ifndef DFL_DMA8_SCHED
-#define DFL_DMA8_SCHED 1   // 1: loads and LDS reads scheduled between a k-step's MFMAs
-#endif
 
 template <int TBM>
 constexpr int d8_stage_bytes() { return (TBM + DBN) * DBK * 2; }
@@ -1063,7 +830,6 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
                   Frag<bf16> (&na)[MI], Frag<bf16> (&nb)[4]) {
     wait_vm<LPS * (D8STAGES - 3)>();   // this wave's loads of stage kt+1 have landed
     ring_barrier();                    // ... everyone's; stage kt-1 is no longer read
-#if DFL_DMA8_SCHED
     // one basic block: the stage loads and the fragment reads of kt+1 (the
     // last k-step re-reads its own stage) issue between the MFMAs of kt,
     // so the matrix pipe is fed right after the barrier
@@ -1082,11 +848,6 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4 * MI - LPS - MI - 4, 0);
     advance();
-#else
-    issue(smem_dma8 + ((kt + D8STAGES - 1) % D8STAGES) * SB);
-    if (kt + 1 < nk) read_frags(kt + 1, na, nb);
-    mmas(fa, fb);
-#endif
   };
   Frag<bf16> fa0[MI], fb0[4], fa1[MI], fb1[4];
   wait_vm<LPS * (D8STAGES - 2)>();
@@ -1176,26 +937,6 @@ static bool dma8_split_launch(const ASrc &A, int M, const WSet &W, const OutSpec
   return true;
 }
 
-constexpr size_t kDmaLds = (size_t)DSTAGES * DSTAGE_BYTES;
-
-static void dma_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
-  const int mt = (M + DBM - 1) / DBM, nt = (W.n_total + DBN - 1) / DBN;
-  const dim3 grid(mt * nt);
-  if (out.mode == OUT_F32) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma_gemm_kernel<OUT_F32>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds);
-    hipLaunchKernelGGL((dma_gemm_kernel<OUT_F32>), grid, dim3(256), kDmaLds, st, A, M, W, out);
-  } else if (out.mode == OUT_ACT) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma_gemm_kernel<OUT_ACT>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds);
-    hipLaunchKernelGGL((dma_gemm_kernel<OUT_ACT>), grid, dim3(256), kDmaLds, st, A, M, W, out);
-  } else {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma_gemm_kernel<OUT_CACHE>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds);
-    hipLaunchKernelGGL((dma_gemm_kernel<OUT_CACHE>), grid, dim3(256), kDmaLds, st, A, M, W, out);
-  }
-}
-
 // 128 x 256 direct-to-LDS tiles from this many rows, once their tiles cover
 // 1 / DFL_HALF_GEMM_FILL of the CUs
 #ifndef DFL_HALF_GEMM_MIN_M
@@ -1205,19 +946,7 @@ static void dma_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, 
 #define DFL_HALF_GEMM_FILL 2
 #endif
 
-// bf16 products too small to fill the CUs: split-K 128 x 256 direct-to-LDS
-// tiles (1) or split-K 128 x 128 register-staged tiles (0)
-#ifndef DFL_SPLIT_HALF
-#define DFL_SPLIT_HALF 1   // 1: also split 128 x 256 tiles whose last wave is under 3/4 full
-#endif
-#ifndef DFL_SMALL_M_DMA8
-#define DFL_SMALL_M_DMA8 1
-#endif
 
-#ifndef DFL_PREFILL_KERNEL
-#define DFL_PREFILL_KERNEL 3     // 0: 128-tile, 1: 256-tile register-staged, 2: 256-tile direct-to-LDS,
-                                 // 3: 256-tile direct-to-LDS on 8 waves
-#endif
 
 
 // Q8_0 -> bf16 expansion: one thread per 32-code block (two 16-byte code
@@ -1265,21 +994,14 @@ hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet
   const bool ragged = tail != 0 && tail * 4 < cus * 3;
   if (act == ACT_F32)
     tile_launch_t<float, W_SAME>(A, M, W, out, part, st);
-  else if (!big && (!half || (DFL_SPLIT_HALF && ragged)) && wkind == W_SAME && DFL_PREFILL_KERNEL == 3 &&
-           DFL_SMALL_M_DMA8 && dma8_split_launch(A, M, W, out, part, st))
-    return hipGetLastError();
-  else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 3)
-    dma8_launch<256>(A, M, W, out, st);
-  else if (half && wkind == W_SAME && DFL_PREFILL_KERNEL == 3)
-    dma8_launch<128>(A, M, W, out, st);
-  else if (big && wkind == W_SAME && DFL_PREFILL_KERNEL == 2)
-    dma_launch(A, M, W, out, st);
-  else if (big && wkind == W_Q8_0 && DFL_PREFILL_KERNEL >= 1)
-    big_launch_t<W_Q8_0>(A, M, W, out, st);
-  else if (big && DFL_PREFILL_KERNEL >= 1)
-    big_launch_t<W_SAME>(A, M, W, out, st);
-  else if (wkind == W_Q8_0)
+  else if (wkind == W_Q8_0)   // fewer rows than kQ8ExpandMinM: dequantised per tile
     tile_launch_t<bf16, W_Q8_0>(A, M, W, out, part, st);
+  else if (!big && (!half || ragged) && dma8_split_launch(A, M, W, out, part, st))
+    return hipGetLastError();
+  else if (big)
+    dma8_launch<256>(A, M, W, out, st);
+  else if (half)
+    dma8_launch<128>(A, M, W, out, st);
   else
     tile_launch_t<bf16, W_SAME>(A, M, W, out, part, st);
   return hipGetLastError();

@@ -61,10 +61,10 @@ struct OutSpec {
 // Rows of the weight-streaming path: M <= 16 activation rows.
 constexpr int kSkinnyMaxM = 16;
 
-// Completion counters at the start of every workspace: zero before a
-// kernel that uses them starts, and zero again when it ends.
-constexpr int kMaxCounters = 16384;
-constexpr size_t kCounterBytes = kMaxCounters * sizeof(unsigned);
+// Completion counters at the start of every workspace: 64-bit words stamped
+// by the launch that uses them, so they need no initial value.
+constexpr int kMaxCounters = 8192;
+constexpr size_t kCounterBytes = kMaxCounters * sizeof(unsigned long long);
 
 // Workspace floats of the split-K partials of a skinny GEMM.
 size_t skinny_partial_floats(int n_total, int K);
@@ -73,7 +73,7 @@ size_t skinny_partial_floats(int n_total, int K);
 // them), or by a second kernel when there are more tile groups than
 // counters.  `part` holds skinny_partial_floats() floats.
 hipError_t launch_skinny_gemm(int act, int wkind, const ASrc &X, int M, const WSet &W, float *part,
-                              unsigned *cnt, const OutSpec &out, hipStream_t st);
+                              unsigned long long *cnt, const OutSpec &out, hipStream_t st);
 // Y = A . W^T for any M (tiled MFMA GEMMs, LDS-staged).  When the 128 x 128
 // tile grid would leave CUs idle (few rows), the k-range is split and `part`
 // (tile_partial_floats() floats) holds the fp32 partials; part == nullptr

@@ -8,12 +8,10 @@
 // Each weight load instruction reads 16 rows x 64 contiguous bytes straight
 // into registers; measured on MI355X this pattern streams at ~6 TB/s.
 //
-// Two forms of the chunk loop: guarded (loads only for tiles the wave owns and
-// chunks that exist) and unguarded (every load issued, rows clamped, results
-// past the end discarded; the compiler can then wait for one chunk at a time
-// instead of all outstanding loads).  Measured on MI355X the guarded form is
-// faster for these kernels (injection fc 65 vs 80 us, streaming LM head 308 vs
-// 388 us), so it is the default (DFL_STREAM_GUARDED).
+// Loads are guarded (issued only for tiles the wave owns and chunks that
+// exist); measured on MI355X this beat an unguarded form that clamps rows and
+// discards the extra results (injection fc 65 vs 80 us, streaming LM head 308
+// vs 388 us): the extra bytes cost more than the waits.
 //
 // k-slot layouts (any assignment is valid if A and B fragments agree):
 //   bf16 / fp32 weights: MFMA j of a chunk takes k = 32 j + 8 g .. + 8 from
@@ -96,19 +94,10 @@ __device__ __forceinline__ SRow<TA, WK> srow(const void *base, const void *scale
   return r;
 }
 
-// Weight loads may be marked non-temporal; measured on MI355X that is slower
-// (LM head 384 vs 302 us), so by default they are ordinary loads.
-#ifndef DFL_NT_WEIGHTS
-#define DFL_NT_WEIGHTS 0
-#endif
-
-
+// Weight loads are ordinary loads (non-temporal ones measured slower on
+// MI355X: LM head 384 vs 302 us).
 __device__ __forceinline__ uint4 wload16(const void *p) {
-#if DFL_NT_WEIGHTS
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-#else
   const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
-#endif
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -142,91 +131,7 @@ struct Chunk {
   float sc[is_q8(WK) ? TPW : 1][is_q8(WK) ? NJ / 2 : 1];
 };
 
-template <typename TA, int WK, int TPW, int NJ>
-__device__ __forceinline__ void chunk_load(Chunk<TA, WK, TPW, NJ> &ch, const TA *xr,
-                                           const SRow<TA, WK> (&rows)[TPW], int cnt, int k, int g,
-                                           bool tok_ok) {
-  if constexpr (is_q8(WK)) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int off = k + 64 * (j >> 1) + 16 * g + 8 * (j & 1);
-      ch.b[j] = load_frag(reinterpret_cast<const bf16 *>(xr) + off);
-    }
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-#pragma unroll
-      for (int m = 0; m < NJ / 2; ++m) {
-        const int off = k + 64 * m + 16 * g;
-        ch.c[u][m] = wload16(reinterpret_cast<const int8_t *>(rows[u].p) + off);
-      }
-      q8_chunk_scales<WK, NJ>(rows[u].s, k, g, ch.sc[u]);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) ch.b[j] = load_frag(xr + k + 32 * j + 8 * g);
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        ch.a[u][j] = wfrag(reinterpret_cast<const TA *>(rows[u].p) + k + 32 * j + 8 * g);
-    }
-  }
-}
-
-template <typename TA, int WK, int TPW, int NJ>
-__device__ __forceinline__ void chunk_mma(const Chunk<TA, WK, TPW, NJ> &ch, f32x4 (&acc)[TPW]) {
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    if constexpr (is_q8(WK)) {
-#pragma unroll
-      for (int m = 0; m < NJ / 2; ++m) {
-        mma(acc[u], dq8(ch.c[u][m].x, ch.c[u][m].y, ch.sc[u][m]), ch.b[2 * m]);
-        mma(acc[u], dq8(ch.c[u][m].z, ch.c[u][m].w, ch.sc[u][m]), ch.b[2 * m + 1]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) mma(acc[u], ch.a[u][j], ch.b[j]);
-    }
-  }
-}
-
-// acc[u] += W_u[16 rows][ka, kb) . X[16 tokens][ka, kb)^T for u < cnt; ka, kb
-// multiples of 64.  xr points at this lane's token row of X (xr[k] = X[t][k]).
-// Software-pipelined: the next 128-wide chunk's loads are issued before the
-// current chunk's MFMAs, so two chunks of loads are in flight per wave.
-template <typename TA, int WK, int TPW>
-__device__ __forceinline__ void stream_range(const TA *xr, const SRow<TA, WK> (&rows)[TPW], int cnt,
-                                             int ka, int kb, int g, bool tok_ok,
-                                             f32x4 (&acc)[TPW]) {
-  (void)cnt;
-  (void)tok_ok;
-  const int nfull = (kb - ka) >> 7;
-  int k = ka;
-  if (nfull > 0) {
-    const int klast = ka + (nfull - 1) * 128;
-    Chunk<TA, WK, TPW, 4> c0, c1;
-    chunk_load(c0, xr, rows, 0, k, g, true);
-    int c = 0;
-    for (; c + 2 <= nfull; c += 2) {
-      chunk_load(c1, xr, rows, 0, k + 128, g, true);
-      chunk_mma(c0, acc);
-      chunk_load(c0, xr, rows, 0, min(k + 256, klast), g, true);
-      chunk_mma(c1, acc);
-      k += 256;
-    }
-    if (c < nfull) {   // odd count: c0 holds the last chunk
-      chunk_mma(c0, acc);
-      k += 128;
-    }
-  }
-  if (k < kb) {
-    Chunk<TA, WK, TPW, 2> ct;
-    chunk_load(ct, xr, rows, 0, k, g, true);
-    chunk_mma(ct, acc);
-  }
-}
-
-// ---- guarded-load variant (loads under `u < cnt` and prefetch conditions) ----
+// ---- chunk loads (under `u < cnt` and the prefetch conditions) and products ----
 template <typename TA, int WK, int TPW, int NJ>
 __device__ __forceinline__ void chunk_load_g(Chunk<TA, WK, TPW, NJ> &ch, const TA *xr,
                                            const SRow<TA, WK> (&rows)[TPW], int cnt, int k, int g,
@@ -294,13 +199,7 @@ __device__ __forceinline__ void stream_range_g(const TA *xr, const SRow<TA, WK> 
                                              f32x4 (&acc)[TPW]) {
   const int nfull = (kb - ka) >> 7;
   int k = ka;
-  if (false) {
-    for (; k + 128 <= kb; k += 128) {
-      Chunk<TA, WK, TPW, 4> c0;
-      chunk_load_g(c0, xr, rows, cnt, k, g, tok_ok);
-      chunk_mma_g(c0, cnt, acc);
-    }
-  } else if (nfull > 0) {
+  if (nfull > 0) {
     Chunk<TA, WK, TPW, 4> c0, c1;
     chunk_load_g(c0, xr, rows, cnt, k, g, tok_ok);
     for (int c = 0; c < nfull; c += 2) {
@@ -321,17 +220,10 @@ __device__ __forceinline__ void stream_range_g(const TA *xr, const SRow<TA, WK> 
   }
 }
 
-#ifndef DFL_STREAM_GUARDED
-#define DFL_STREAM_GUARDED 1
-#endif
-
 template <typename TA, int WK, int TPW>
 __device__ __forceinline__ void stream_k(const TA *xr, const SRow<TA, WK> (&rows)[TPW], int cnt, int ka,
                                          int kb, int g, bool tok_ok, f32x4 (&acc)[TPW]) {
-  if (DFL_STREAM_GUARDED)
-    stream_range_g<TA, WK, TPW>(xr, rows, cnt, ka, kb, g, tok_ok, acc);
-  else
-    stream_range<TA, WK, TPW>(xr, rows, cnt, ka, kb, g, tok_ok, acc);
+  stream_range_g<TA, WK, TPW>(xr, rows, cnt, ka, kb, g, tok_ok, acc);
 }
 
 }  // namespace dfl

@@ -1,7 +1,7 @@
 // Shared LM head with top-K candidates and log-softmax unary scores
 // ("Turbo dflash", Overview: the draft uses the target's output matrix;
-// "spec : add DFlash2 support", Overview: unary[c] is the draft's own score,
-// and the top-k review: small K over a very wide row).
+// "spec : add DFlash2 support", Overview: the unary term of an edge is the
+// draft's log-softmax score of the candidate; and the top-k review: small K over a very wide row).
 //
 // The logits l = h . W_lm^T are never stored.  The LM head weight is by far
 // the largest stream of the block step, so the first kernel streams it once:

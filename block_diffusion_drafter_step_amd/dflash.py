@@ -52,11 +52,14 @@ _SIGS = {
     "dflash_inject": ([ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _I32, _PW, _P, _F32, _PW, _PW,
                        _PC, _I64, _P, _SZ, _P], _I32),
     "dflash_inject_workspace": ([_I32, _I64, _I32, _I32, _I32, _I32], _SZ),
+    "dflash_inject_z_offset": ([_I32, _I64, _I32, _I32, _I32, _I32], _SZ),
     "dflash_conv": ([_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _PW, _P, _P, _SZ, _P], _I32),
     "dflash_conv_workspace": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "dflash_block_attn": ([_P, _P, _I32, _I32, _I32, _I32, _PW, _PW, _PW, _PW, _PC, _I64, _F32, _P, _P,
                            _SZ, _P], _I32),
     "dflash_block_attn_workspace": ([_I32, _I32, _I32, _I32, _I32, _I64], _SZ),
+    "dflash_block_attn_qkv_offset": ([_I32, _I32, _I32, _I32, _I32, _I64], _SZ),
+    "dflash_block_attn_o_offset": ([_I32, _I32, _I32, _I32, _I32, _I64], _SZ),
     "dflash_topk_unary": ([_P, _I32, _I32, _PW, _I32, _P, _P, _P, _SZ, _P], _I32),
     "dflash_topk_unary_workspace": ([_I32, _I64, _I32], _SZ),
     "dflash_selector_edges": ([_P, _I32, _I32, _PW, _P, _P, _I64, _P, _P, _I32, _I32, _P, _P, _P, _SZ,
@@ -186,6 +189,27 @@ def dflash_inject_workspace(n_layers, n_tokens, d_t, d, kv, act="bf16") -> int:
     return load().dflash_inject_workspace(n_layers, n_tokens, d_t, d, kv, _DT[act])
 
 
+def dflash_inject_z_offset(n_layers, n_tokens, d_t, d, kv, act="bf16") -> int:
+    return load().dflash_inject_z_offset(n_layers, n_tokens, d_t, d, kv, _DT[act])
+
+
+def dflash_block_attn_qkv_offset(B, d, n_q_heads, n_kv_heads, head_dim, n_ctx) -> int:
+    return load().dflash_block_attn_qkv_offset(B, d, n_q_heads, n_kv_heads, head_dim, n_ctx)
+
+
+def dflash_block_attn_o_offset(B, d, n_q_heads, n_kv_heads, head_dim, n_ctx) -> int:
+    return load().dflash_block_attn_o_offset(B, d, n_q_heads, n_kv_heads, head_dim, n_ctx)
+
+
+def ws_view(ws: torch.Tensor, offset: int, shape, dtype) -> torch.Tensor:
+    """A view of `shape` elements of `dtype` at byte `offset` of a workspace."""
+    n = 1
+    for s in shape:
+        n *= s
+    es = torch.empty((), dtype=dtype).element_size()
+    return ws[offset:offset + n * es].view(dtype).view(*shape)
+
+
 def dflash_conv_workspace(n_blocks, B, C, G, T) -> int:
     return load().dflash_conv_workspace(n_blocks, B, C, G, T)
 
@@ -203,8 +227,8 @@ def dflash_selector_edges_workspace(B, r, d, K) -> int:
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace (its leading completion counters must start at zero)."""
-    return torch.zeros(max(16, nbytes), dtype=torch.uint8, device=device)
+    """A workspace of at least `nbytes` (no initial contents needed)."""
+    return torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
 
 
 # ---- the six calls -------------------------------------------------------------

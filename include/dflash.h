@@ -50,12 +50,15 @@
  * - Workspace.  A call that needs scratch device memory takes (ws, ws_bytes);
  *   the matching *_workspace() function returns the bytes it needs for the
  *   given shapes (0 for none).  A smaller workspace -> DFLASH_ERR_WORKSPACE.
- *   The first 64 KiB of a workspace hold completion counters that the
- *   kernels expect at zero: fill a new workspace with zeros once before its
- *   first use (hipMemset).  Every call returns the counters to zero by the
- *   time its work completes, so a workspace can be reused by later calls
- *   (of any entry point) without clearing it again, as long as nothing else
- *   writes to it in between.
+ *   A workspace needs no initial contents and no clearing between calls: its
+ *   first 64 KiB hold completion counters that each kernel launch stamps
+ *   with a 48-bit value of its own, so whatever an earlier call (complete or
+ *   not) or anything else left there is ignored.  Calls that share one
+ *   workspace must be ordered (one stream, or events); overlapping calls on
+ *   one workspace race.
+ * - Intermediates.  After a call completes, its workspace holds the act-type
+ *   intermediates named by the *_offset() queries until a later call reuses
+ *   it (for stage-wise checking of each step against a reference).
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -138,12 +141,16 @@ dflash_status dflash_inject(const void *const *layer_hidden, int32_t n_layers, i
                             void *stream);
 size_t dflash_inject_workspace(int32_t n_layers, int64_t n_tokens, int32_t d_t, int32_t d,
                                int32_t kv, int32_t act);
+/* Byte offset into the injection's workspace of z [n_tokens][d] in `act`
+ * (the RMSNorm output that Wk and Wv multiply), for the same arguments. */
+size_t dflash_inject_z_offset(int32_t n_layers, int64_t n_tokens, int32_t d_t, int32_t d,
+                              int32_t kv, int32_t act);
 
 /* (2) DFlash2 grouped dynamic depthwise convolution.
  * "spec : add DFlash2 support", Overview:
  *   out[i,c] = sum_{t<T} (base[t,c] + delta[i,t,g(c)]) * x[i-t,c]
- * with delta[i][t*G + g] = x[i] . W_delta[t*G + g] (predicted from the input,
- * shared by the channels of a group), contiguous groups g(c) = c / (C/G),
+ * with delta[i][t*G + g] = x[i] . W_delta[t*G + g] (computed from the same
+ * input row, shared by the channels of a group), contiguous groups g(c) = c / (C/G),
  * tap 0 = the current position, x before the block start = 0.
  * x, out: [n_blocks][B][C] in `act` (blocks are independent); base: [T][C]
  * in `act`; w_delta: [T*G][C] in `act`.  Requires C % G == 0, C % 64 == 0,
@@ -176,11 +183,18 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
                                 void *stream);
 size_t dflash_block_attn_workspace(int32_t B, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
                                    int32_t head_dim, int64_t n_ctx);
+/* Byte offsets into the attention's workspace, for the same arguments, of
+ * Q | Kb | Vb [B][(n_q_heads + 2 n_kv_heads) head_dim] and of
+ * O [B][n_q_heads head_dim] (the softmax output before Wo), both in `act`. */
+size_t dflash_block_attn_qkv_offset(int32_t B, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, int64_t n_ctx);
+size_t dflash_block_attn_o_offset(int32_t B, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int64_t n_ctx);
 
 /* (4) Shared LM head, top-K candidates and log-softmax unary scores.
  * "Turbo dflash", Overview (the draft uses the target's output matrix);
- * "spec : add DFlash2 support", Overview ("unary[c] is the draft's own score
- * for c") and the top-k review (small K over a wide vocabulary):
+ * "spec : add DFlash2 support", Overview (the unary term of an edge is the
+ * draft's log-softmax score of the candidate) and the top-k review (small K over a wide vocabulary):
  *   l = h . W_lm^T  (fp32, never stored)
  *   idx[i] = the K largest l[i][.], largest first, equal logits -> lower index
  *   unary[i][k] = l[i][idx[i][k]] - log(sum_v exp(l[i][v]))

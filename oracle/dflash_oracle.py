@@ -22,7 +22,8 @@ Sources (web pages, cited by title and section):
          which the decoder reads when it drafts.
   [P3] "spec : add DFlash2 support (local convolution + candidate selector)"
        - Overview: the grouped dynamic depthwise convolution and the
-         candidate-selector edge formula; unary[c] is the draft's own score.
+         candidate-selector edge formula, whose unary term is the draft's
+         log-softmax score of the candidate.
        - review of tensor names: attn_conv_base / attn_conv_proj, selector
          predecessor / successor / hidden tensors.
   [P4] "dflash: pass missing NVFP4 scales to attention operations"
@@ -133,6 +134,23 @@ def rmsnorm(y: np.ndarray, gamma, eps: float) -> np.ndarray:
     return z
 
 
+def encode(hidden: list, fc: np.ndarray, gamma, eps: float, bf16_points: bool) -> dict:
+    """The encoder of the injection: [P1] Root Cause, an fc matmul over the
+    concatenated features of the chosen target layers followed by a norm.
+      h = [h_1 | ... | h_Lt]  (R1)     y = h . fc^T      z = RMSNorm(y)  (R-RP: bf16)
+    """
+    h = np.concatenate(hidden, axis=1)
+    y = h @ fc.T
+    z = _rp(rmsnorm(y, gamma, eps), bf16_points)
+    return {"y": y, "z": z}
+
+
+def kv_project(z: np.ndarray, wk: np.ndarray, wv: np.ndarray, bf16_points: bool) -> dict:
+    """[P2] The Problem: the injected rows' K and V are the Wk / Wv projections
+    of the encoder output.  K = z . Wk^T, V = z . Wv^T  (R-RP: bf16)."""
+    return {"k": _rp(z @ wk.T, bf16_points), "v": _rp(z @ wv.T, bf16_points)}
+
+
 def inject(hidden: list, fc: np.ndarray, gamma, eps: float, wk: np.ndarray,
            wv: np.ndarray, bf16_points: bool) -> dict:
     """Encoder plus K/V projections for n injected tokens.
@@ -140,17 +158,12 @@ def inject(hidden: list, fc: np.ndarray, gamma, eps: float, wk: np.ndarray,
     [P1] Root Cause: the encoder is the fc matmul over the features of the
     chosen target layers, then a norm.  [P2] The Problem: injection is the
     Wk / Wv matmuls plus the cache write.  [P4] merge log: encoder and
-    injection form one pass.
-      h = [h_1 | ... | h_Lt]  (R1)     y = h . fc^T      z = RMSNorm(y)
-      K = z . Wk^T            V = z . Wv^T
+    injection form one pass.  The two stages are encode() and kv_project().
     Returns the intermediates and the K / V rows [n][Hkv*hd] as stored.
     """
-    h = np.concatenate(hidden, axis=1)
-    y = h @ fc.T
-    z = _rp(rmsnorm(y, gamma, eps), bf16_points)
-    k = _rp(z @ wk.T, bf16_points)
-    v = _rp(z @ wv.T, bf16_points)
-    return {"y": y, "z": z, "k": k, "v": v}
+    e = encode(hidden, fc, gamma, eps, bf16_points)
+    kv = kv_project(e["z"], wk, wv, bf16_points)
+    return {"y": e["y"], "z": e["z"], "k": kv["k"], "v": kv["v"]}
 
 
 def cache_write(cache_k: np.ndarray, cache_v: np.ndarray, k_rows: np.ndarray,
@@ -200,8 +213,8 @@ def kv_dequant_q8_0(codes: np.ndarray, scales: np.ndarray, bf16_points: bool) ->
 
 
 def conv_delta(x: np.ndarray, w_delta: np.ndarray) -> np.ndarray:
-    """Reading R6: the dynamic part predicted from the input,
-    delta[..., i, t*G + g] = x[..., i, :] . W_delta[t*G + g, :]."""
+    """Reading R6: the per-position kernel offsets, computed from the same
+    input row, delta[..., i, t*G + g] = x[..., i, :] . W_delta[t*G + g, :]."""
     return x @ w_delta.T
 
 
@@ -235,56 +248,103 @@ def conv(x: np.ndarray, base: np.ndarray, w_delta: np.ndarray, G: int,
 # ---------------------------------------------------------------------------
 
 
-def softmax_attend(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float) -> np.ndarray:
-    """Softmax attention of queries [m][hd] over keys/values [S][hd], no mask."""
+# unit roundoff of bf16 (8 significant bits): |bf16_rne(x) - x| <= U_BF16 |x|
+U_BF16 = 2.0 ** -8
+
+
+def softmax_attend(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float,
+                   weight_rounding: float = 0.0) -> tuple:
+    """Softmax attention of queries [m][hd] over keys/values [S][hd], no mask.
+
+    Returns (out, bound).  `weight_rounding` = u > 0 declares that an
+    implementation may round each unnormalised softmax weight to a relative
+    error of at most u before it multiplies V (and sums the rounded weights as
+    the normaliser); then out_impl = sum_s w_s (1+e_s) V_s / sum_s w_s (1+e_s)
+    with |e_s| <= u, so |out_impl - out| <= u / (1 - u) * sum_s w_s |V_s - out|
+    per element, which is `bound` (zeros for u = 0)."""
     s = (q @ keys.T) * scale
     s = s - s.max(axis=1, keepdims=True)
     p = np.exp(s)
     p = p / p.sum(axis=1, keepdims=True)
-    return p @ vals
+    out = p @ vals
+    bound = np.zeros_like(out)
+    if weight_rounding:
+        for i in range(q.shape[0]):
+            bound[i] = p[i] @ np.abs(vals - out[i][None, :])
+        bound *= weight_rounding / (1.0 - weight_rounding)
+    return out, bound
 
 
-def block_attn(u: np.ndarray, resid, wq: np.ndarray, wk: np.ndarray, wv: np.ndarray,
-               wo: np.ndarray, cache_k: np.ndarray, cache_v: np.ndarray, n_ctx: int,
-               n_q_heads: int, scale: float, bf16_points: bool) -> dict:
-    """B draft queries attend [injected context | block] keys, no mask.
+def attn_qkv(u: np.ndarray, wq: np.ndarray, wk: np.ndarray, wv: np.ndarray,
+             bf16_points: bool) -> dict:
+    """[P4] Overview: the decoder's Q, K and V projections of the block input.
+    Q = u Wq^T, Kb = u Wk^T, Vb = u Wv^T  (R-RP: bf16), each [B][heads*hd]."""
+    return {"q": _rp(u @ wq.T, bf16_points), "kb": _rp(u @ wk.T, bf16_points),
+            "vb": _rp(u @ wv.T, bf16_points)}
 
-    [P2] Overview: the block is drafted at once (block diffusion), so the
-    block's positions see each other; The Problem: the decoder reads the
-    injected cache.  [P4] Overview: Q, K, V and output projections.
-      Q = u Wq^T, Kb = u Wk^T, Vb = u Wv^T                       (R-RP: bf16)
-      head h uses KV head h // (Hq/Hkv) (R9), scale 1/sqrt(hd) unless given
-      O_h = softmax(Q_h [Kctx | Kb]^T * scale) [Vctx | Vb]         (R-RP: bf16)
-      out = resid + O Wo^T                                         (R10, R-RP)
-    u, resid [B][d]; cache [Hkv][capacity][hd] with n_ctx valid rows.
-    """
-    B = u.shape[0]
+
+def attn_core(q: np.ndarray, kb: np.ndarray, vb: np.ndarray, cache_k: np.ndarray,
+              cache_v: np.ndarray, n_ctx: int, n_q_heads: int, scale: float,
+              bf16_points: bool) -> dict:
+    """[P2] Overview / The Problem: each query head attends the injected
+    context and the whole block, no mask (block diffusion drafts the block at
+    once).  Head h uses KV head h // (Hq/Hkv) (R9); scale 1/sqrt(hd) unless
+    given; O is rounded to bf16 in bf16 workloads (R-RP).
+    q [B][Hq*hd], kb / vb [B][Hkv*hd]; cache [Hkv][capacity][hd], n_ctx rows.
+    "o_bound" is softmax_attend's bound for weights rounded to bf16 (the GPU's
+    P.V operands), zeros in fp32 workloads."""
+    B = q.shape[0]
     hkv, cap, hd = cache_k.shape
     if n_q_heads % hkv or n_ctx > cap:
         raise ValueError("attention shapes")
     grp = n_q_heads // hkv
     if not scale:
         scale = 1.0 / np.sqrt(hd)
-    q = _rp(u @ wq.T, bf16_points).reshape(B, n_q_heads, hd)
-    kb = _rp(u @ wk.T, bf16_points).reshape(B, hkv, hd)
-    vb = _rp(u @ wv.T, bf16_points).reshape(B, hkv, hd)
+    q = q.reshape(B, n_q_heads, hd)
+    kb = kb.reshape(B, hkv, hd)
+    vb = vb.reshape(B, hkv, hd)
     o = np.zeros((B, n_q_heads, hd))
+    ob = np.zeros_like(o)
+    u_w = U_BF16 if bf16_points else 0.0
     for h in range(n_q_heads):
         g = h // grp
         keys = np.concatenate([cache_k[g, :n_ctx], kb[:, g]], axis=0)
         vals = np.concatenate([cache_v[g, :n_ctx], vb[:, g]], axis=0)
-        o[:, h] = softmax_attend(q[:, h], keys, vals, scale)
-    o = _rp(o.reshape(B, n_q_heads * hd), bf16_points)
+        o[:, h], ob[:, h] = softmax_attend(q[:, h], keys, vals, scale, u_w)
+    o = o.reshape(B, n_q_heads * hd)
+    return {"o_pre": o, "o": _rp(o, bf16_points), "o_bound": ob.reshape(B, n_q_heads * hd)}
+
+
+def attn_out(o: np.ndarray, wo: np.ndarray, resid, bf16_points: bool) -> np.ndarray:
+    """[P4] Overview: the output projection; R10: plus the residual.
+    out = resid + O Wo^T  (R-RP: bf16)."""
     out = o @ wo.T
     if resid is not None:
         out = out + resid
-    return {"q": q.reshape(B, -1), "kb": kb.reshape(B, -1), "vb": vb.reshape(B, -1),
-            "o": o, "out": _rp(out, bf16_points)}
+    return _rp(out, bf16_points)
+
+
+def block_attn(u: np.ndarray, resid, wq: np.ndarray, wk: np.ndarray, wv: np.ndarray,
+               wo: np.ndarray, cache_k: np.ndarray, cache_v: np.ndarray, n_ctx: int,
+               n_q_heads: int, scale: float, bf16_points: bool) -> dict:
+    """B draft queries attend [injected context | block] keys, no mask:
+    attn_qkv -> attn_core -> attn_out.
+
+    [P2] Overview: the block is drafted at once (block diffusion), so the
+    block's positions see each other; The Problem: the decoder reads the
+    injected cache.  [P4] Overview: Q, K, V and output projections.
+    u, resid [B][d]; cache [Hkv][capacity][hd] with n_ctx valid rows.
+    """
+    p = attn_qkv(u, wq, wk, wv, bf16_points)
+    c = attn_core(p["q"], p["kb"], p["vb"], cache_k, cache_v, n_ctx, n_q_heads, scale, bf16_points)
+    out = attn_out(c["o"], wo, resid, bf16_points)
+    return {"q": p["q"], "kb": p["kb"], "vb": p["vb"], "o": c["o"], "o_bound": c["o_bound"],
+            "out": out}
 
 
 # ---------------------------------------------------------------------------
 # (4) shared LM head, top-K candidates, log-softmax unary  [P2] Overview;
-#     [P3] Overview ("unary[c] is the draft's own score") and top-k review
+#     [P3] Overview (the unary term of an edge) and top-k review
 # ---------------------------------------------------------------------------
 
 
@@ -370,8 +430,8 @@ def selector_edges(h: np.ndarray, P: np.ndarray, A: np.ndarray, Bc: np.ndarray,
     """edge(p -> c) = < A[p] (.) project(h), B[c] > + unary[c].
 
     [P3] Overview: A / B are the predecessor / candidate codebooks, project(h)
-    maps this position's hidden state to the codebook rank, unary[c] is the
-    draft's own score.  Candidates of position i are c_{i,b} = idx[i][b];
+    maps this position's hidden state to the codebook rank, and unary[c] is
+    the draft's log-softmax score of candidate c.  Candidates of position i are c_{i,b} = idx[i][b];
     predecessors are p_{i,a} = idx[i-1][a] for i >= 1 and the anchor token
     for i = 0 (R12).  Row 0 has one predecessor slot (a = 0); its other slots
     are -inf.  With anchor = -1 row 0 is the unary score alone.

@@ -28,3 +28,17 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With DFLASH_PARITY_MARGINS=<path>, write the float-parity margins of the
+    session there (markdown)."""
+    path = os.environ.get("DFLASH_PARITY_MARGINS")
+    if not path:
+        return
+    try:
+        from tests import gpu_util
+    except Exception:
+        return
+    if gpu_util.MARGINS:
+        gpu_util.write_margins(path, ["python"] + sys.argv)

@@ -68,6 +68,22 @@ def test_workspace_queries_are_host_only(lib):
     assert lib.dflash_inject_workspace(0, 16, 5120, 5120, 1024, 1) == 0
 
 
+def test_intermediate_offsets_lie_inside_the_workspace(lib):
+    """z, Q | Kb | Vb and O sit after the counters, 256-byte aligned, and
+    inside the workspace the matching query returns."""
+    for n in (1, 16, 64, 1000, 32768):
+        ws = lib.dflash_inject_workspace(5, n, 5120, 5120, 1024, 1)
+        z = lib.dflash_inject_z_offset(5, n, 5120, 5120, 1024, 1)
+        assert z >= 65536 and z % 256 == 0 and z + n * 5120 * 2 <= ws
+    for n_ctx in (0, 1, 1024, 32768, 65552):
+        ws = lib.dflash_block_attn_workspace(16, 5120, 32, 8, 128, n_ctx)
+        q = lib.dflash_block_attn_qkv_offset(16, 5120, 32, 8, 128, n_ctx)
+        o = lib.dflash_block_attn_o_offset(16, 5120, 32, 8, 128, n_ctx)
+        assert 65536 <= q < o and q % 256 == 0 and o % 256 == 0
+        assert q + 16 * 6144 * 2 <= o and o + 16 * 4096 * 2 <= ws
+    assert lib.dflash_inject_z_offset(0, 16, 5120, 5120, 1024, 1) == 0
+
+
 FAKE = 0x10000        # aligned, never dereferenced: every case below is invalid
 
 

@@ -2,11 +2,17 @@
 inputs, element by element, at small sizes that still span several tiles and
 a ragged tail, and at the workloads' full sizes on sampled outputs.
 
-Each call is checked on its own inputs drawn from the seeded generator (the
-oracle never reads a GPU result).  Floats: |gpu - ref| <= atol + rtol |ref|
-with (2e-2, 1e-2) for bf16 workloads and (1e-4, 1e-4) for fp32.  Integer
-results (top-K indices, the path, accept lengths) are exact wherever the
-oracle's score gap makes them unique (> 1e-3) and valid elsewhere.
+Floats: per element |gpu - ref| <= atol + rtol |ref|, (2e-2, 1e-2) for bf16
+workloads and (1e-4, 1e-4) for fp32.  Checks are stage-wise where a call has
+internal bf16 rounding points: each oracle stage is fed the GPU's own output
+of the stage before it, once that output has itself passed (the injection's
+encoder output z; the attention's Q | Kb | Vb and O, read from the call's
+workspace).  Two allowances are named where they apply: the softmax weights
+the attention rounds to bf16 before its P.V product (a per-element bound the
+oracle computes), and, for end-to-end comparisons of the Q8_0 workload, the
+propagation of the stage-checked differences at the upstream rounding point.
+Integer results (top-K indices, the path, accept lengths) are exact wherever
+the oracle's score gap makes them unique (> 1e-3) and valid elsewhere.
 """
 import numpy as np
 import pytest
@@ -40,39 +46,83 @@ def wnp(w):
     return O.weight_to_f64(w)
 
 
+def garbage(ws: torch.Tensor, seed: int):
+    """Fill a workspace with seeded random bytes (stale counters included)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    ws.copy_(torch.randint(0, 256, ws.shape, generator=g, device="cuda", dtype=torch.int32).to(torch.uint8))
+
+
+def rows_of_cache(cache, pos):
+    """K and V rows [len(pos)][Hkv*hd] of the cache at positions `pos`."""
+    p = torch.as_tensor(np.asarray(pos), device="cuda")
+    n = len(pos)
+    gk = f64(cache.k[:, p, :].permute(1, 0, 2).reshape(n, -1))
+    gv = f64(D.v_rows(cache.v)[:, p, :].permute(1, 0, 2).reshape(n, -1))   # V^T panels
+    return gk, gv
+
+
 # ---------------------------------------------------------------------------
 # (1) injection
 # ---------------------------------------------------------------------------
 
-def run_inject(cfg, n, pos0, rows=None, prefill=None):
-    """GPU injection of n seeded rows at pos0; oracle check on `rows`."""
-    say(f"inject {cfg.name} n={n} pos0={pos0} weight={cfg.weight}")
+def check_inject(cfg, hid_rows, fc, gamma, wk, wv, zg, gk, gv, what):
+    """Stage-wise and end-to-end checks of injected rows: the GPU's z against
+    the oracle's encoder; its K / V against the oracle's projections of that
+    same z; then K / V against the oracle chain (Q8_0 weights: plus the
+    propagation |W| |z_gpu - z_ref| of the stage-checked z differences)."""
+    bp = cfg.act == "bf16"
+    Wk, Wv = wnp(wk), wnp(wv)
+    enc = O.encode(hid_rows, wnp(fc), gamma, cfg.eps, bp)
+    assert_close(zg, enc["z"], cfg.act, f"{what} z")
+    st = O.kv_project(zg, Wk, Wv, bp)
+    assert_close(gk, st["k"], cfg.act, f"{what} K from the GPU's z")
+    assert_close(gv, st["v"], cfg.act, f"{what} V from the GPU's z")
+    ref = O.kv_project(enc["z"], Wk, Wv, bp)
+    if cfg.weight == "q8_0":
+        dz = np.abs(zg - enc["z"])
+        assert_close(gk, ref["k"], cfg.act, f"{what} K end to end", term=dz @ np.abs(Wk).T)
+        assert_close(gv, ref["v"], cfg.act, f"{what} V end to end", term=dz @ np.abs(Wv).T)
+    else:
+        assert_close(gk, ref["k"], cfg.act, f"{what} K end to end")
+        assert_close(gv, ref["v"], cfg.act, f"{what} V end to end")
+
+
+def run_inject(cfg, n, pos0, rows=None, prefill=None, gamma=None, garbage_seed=None, tag=None,
+               cache=None, hid=None):
+    """GPU injection of n seeded rows at pos0; oracle checks on `rows`.
+    Returns (cache, K rows, V rows) of the checked rows."""
+    say(f"inject {cfg.name} n={n} pos0={pos0} weight={cfg.weight} gamma={gamma is not None} "
+        f"garbage_ws={garbage_seed is not None}")
     w = synth.Workload(cfg)
-    hid = [w.hidden(l, n, tag=f"inj{n}") for l in range(cfg.L_t)]
+    if hid is None:
+        hid = [w.hidden(l, n, tag=tag or f"inj{n}") for l in range(cfg.L_t)]
     fc, wk, wv = w.fc(), w.wk(), w.wv()
-    cache = P.new_cache(cfg)
-    if prefill is not None:
-        cache.k.fill_(prefill)
-        cache.v.fill_(prefill)
+    if cache is None:
+        cache = P.new_cache(cfg)
+        if prefill is not None:
+            cache.k.fill_(prefill)
+            cache.v.fill_(prefill)
     ws = D.workspace(D.dflash_inject_workspace(cfg.L_t, n, cfg.d_t, cfg.d, cfg.kv, cfg.act))
-    D.dflash_inject([dev(h, cfg.act) for h in hid], wdev(fc), None, cfg.eps, wdev(wk), wdev(wv), cache, pos0, ws)
+    if garbage_seed is not None:
+        garbage(ws, garbage_seed)
+    gdev = dev(gamma, cfg.act) if gamma is not None else None
+    D.dflash_inject([dev(h, cfg.act) for h in hid], wdev(fc), gdev, cfg.eps, wdev(wk), wdev(wv), cache, pos0,
+                    ws)
     torch.cuda.synchronize()
     rows = np.arange(n) if rows is None else np.asarray(rows)
-    bp = cfg.act == "bf16"
-    ref = O.inject([act_np(h[rows], cfg.act) for h in hid], wnp(fc), None, cfg.eps, wnp(wk), wnp(wv), bp)
-    gk = f64(cache.k[:, pos0 + torch.as_tensor(rows, device="cuda"), :].permute(1, 0, 2).reshape(len(rows), -1))
-    # V is cached in transposed 32-position panels
-    gv = f64(D.v_rows(cache.v)[:, pos0 + torch.as_tensor(rows, device="cuda"), :].permute(1, 0, 2)
-             .reshape(len(rows), -1))
-    assert_close(gk, ref["k"], cfg.act, f"{cfg.name} cache K")
-    assert_close(gv, ref["v"], cfg.act, f"{cfg.name} cache V")
-    return cache
+    zoff = D.dflash_inject_z_offset(cfg.L_t, n, cfg.d_t, cfg.d, cfg.kv, cfg.act)
+    zg = f64(D.ws_view(ws, zoff, (n, cfg.d), P.act_dtype(cfg.act))[torch.as_tensor(rows, device="cuda")])
+    gk, gv = rows_of_cache(cache, pos0 + rows)
+    gam = act_np(gamma, cfg.act) if gamma is not None else None
+    check_inject(cfg, [act_np(h[rows], cfg.act) for h in hid], fc, gam, wk, wv, zg, gk, gv, cfg.name)
+    return cache, gk, gv
 
 
 @pytest.mark.parametrize("n,pos0", [(64, 0), (16, 5), (5, 100), (70, 3)])
 def test_inject_tiny_fp32(n, pos0):
     cfg = cfg_small(0, capacity=256)
-    cache = run_inject(cfg, n, pos0, prefill=7.0)
+    cache, _, _ = run_inject(cfg, n, pos0, prefill=7.0)
     # rows outside [pos0, pos0 + n) are untouched
     k = cache.k.cpu()
     assert torch.all(k[:, :pos0] == 7.0) and torch.all(k[:, pos0 + n:] == 7.0)
@@ -83,10 +133,26 @@ def test_inject_qwen27b_shapes(n, pos0):
     run_inject(cfg_small(1, capacity=512), n, pos0)
 
 
+def test_inject_gamma():
+    """A non-trivial RMSNorm gain (gamma != NULL) on the weight-streaming
+    (16 rows) and tile (200 rows) paths, bf16 and fp32."""
+    for ci, n in [(1, 16), (1, 200), (0, 16)]:
+        cfg = cfg_small(ci, capacity=512)
+        gamma = synth.normal(cfg.seed, "gamma", (cfg.d,), 1.0, cfg.act)
+        run_inject(cfg, n, 7, gamma=gamma, tag=f"gam{n}")
+
+
+def test_inject_wide_rows_rmsnorm():
+    """d > 8192: the RMSNorm reads a row twice (its two-pass path)."""
+    cfg = cfg_small(1, d=8320, d_t=512, L_t=2, Hkv=1, capacity=256)
+    run_inject(cfg, 5, 11, tag="wide")
+    run_inject(cfg, 40, 64, tag="wide40")
+
+
 def test_inject_decode_rows_at_64k():
     """Config 3: 16 rows injected behind 65536 pre-filled rows."""
     cfg = configs.get(3)
-    cache = run_inject(cfg, 16, 65536, prefill=0.5)
+    cache, _, _ = run_inject(cfg, 16, 65536, prefill=0.5)
     assert torch.all(cache.k[:, 65536 + 16:].cpu().float() == 0.5)
     assert torch.all(cache.k[:, :65536].cpu().float() == 0.5)
 
@@ -130,17 +196,36 @@ def test_inject_q8_0_around_expansion_threshold(n):
     run_inject(cfg, n, 17)
 
 
+@pytest.mark.parametrize("n", [16, 64])
+def test_inject_deterministic(n):
+    """Bitwise-equal caches from two calls: the counter-based small-weight
+    GEMM (16 rows) and the split-K tile path (64 rows) sum in a fixed order."""
+    cfg = cfg_small(1, capacity=256)
+    a, _, _ = run_inject(cfg, n, 3, tag="det")
+    b, _, _ = run_inject(cfg, n, 3, tag="det", garbage_seed=n)
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+
+
+def test_inject_garbage_workspace():
+    """A workspace full of random bytes (any stale completion counter) gives
+    correct rows: the counters carry each launch's own stamp."""
+    run_inject(cfg_small(1, capacity=256), 16, 40, garbage_seed=7, tag="garb")
+    run_inject(cfg_small(0, capacity=256), 16, 40, garbage_seed=8, tag="garb")
+
+
 # ---------------------------------------------------------------------------
 # (2) conv
 # ---------------------------------------------------------------------------
 
-def run_conv(cfg, nb, tag="conv"):
+def run_conv(cfg, nb, tag="conv", garbage_seed=None):
     say(f"conv {cfg.name} n_blocks={nb} B={cfg.B} C={cfg.C} G={cfg.G} T={cfg.T}")
     w = synth.Workload(cfg)
     x = synth.normal(cfg.seed, f"{tag}.x.{nb}", (nb, cfg.B, cfg.C), 1.0, cfg.act)
     base, wd = w.conv_base(), w.w_delta()
     out = torch.empty((nb, cfg.B, cfg.C), dtype=P.act_dtype(cfg.act), device="cuda")
     ws = D.workspace(D.dflash_conv_workspace(nb, cfg.B, cfg.C, cfg.G, cfg.T))
+    if garbage_seed is not None:
+        garbage(ws, garbage_seed)
     D.dflash_conv(dev(x, cfg.act), cfg.G, dev(base, cfg.act), wdev(wd), out, ws)
     torch.cuda.synchronize()
     ref = O.conv(act_np(x, cfg.act), act_np(base, cfg.act), wnp(wd), cfg.G, cfg.act == "bf16")
@@ -183,16 +268,47 @@ def test_conv_batched_32k_tokens():
     run_conv(configs.get(2), 2050, tag="convr")
 
 
+def test_conv_garbage_workspace():
+    run_conv(configs.get(1), 1, tag="convg", garbage_seed=3)
+    run_conv(configs.get(0), 1, tag="convg", garbage_seed=4)
+
+
 # ---------------------------------------------------------------------------
 # (3) block attention
 # ---------------------------------------------------------------------------
 
-def run_attn(cfg, n_ctx, cap=None, resid=True, B=None, poison=False):
+def check_attn(cfg, U, X, wq, wk, wv, wo, CK, CV, n_ctx, scale, qkvg, og, outg, what, B):
+    """Stage-wise: Q | Kb | Vb against the oracle's projections of u; O
+    against the oracle's softmax over the GPU's Q, Kb, Vb (plus the bound for
+    softmax weights rounded to bf16); out against the oracle's Wo product of
+    the GPU's O.  End to end: out against the oracle chain (Q8_0 weights:
+    plus |Wo| |O_gpu - O_ref|, the propagation of the stage-checked O)."""
+    bp = cfg.act == "bf16"
+    Wq, Wk, Wv, Wo = wnp(wq), wnp(wk), wnp(wv), wnp(wo)
+    qd, kv = cfg.Hq * cfg.hd, cfg.Hkv * cfg.hd
+    p = O.attn_qkv(U, Wq, Wk, Wv, bp)
+    assert_close(qkvg[:, :qd], p["q"], cfg.act, f"{what} Q")
+    assert_close(qkvg[:, qd:qd + kv], p["kb"], cfg.act, f"{what} Kb")
+    assert_close(qkvg[:, qd + kv:], p["vb"], cfg.act, f"{what} Vb")
+    c = O.attn_core(qkvg[:, :qd], qkvg[:, qd:qd + kv], qkvg[:, qd + kv:], CK, CV, n_ctx, cfg.Hq, scale, bp)
+    assert_close(og, c["o"], cfg.act, f"{what} O from the GPU's Q, Kb, Vb",
+                 term=c["o_bound"] if bp else None)
+    assert_close(outg, O.attn_out(og, Wo, X, bp), cfg.act, f"{what} out from the GPU's O")
+    ref = O.block_attn(U, X, Wq, Wk, Wv, Wo, CK, CV, n_ctx, cfg.Hq, scale, bp)
+    if cfg.weight == "q8_0":
+        assert_close(outg, ref["out"], cfg.act, f"{what} out end to end",
+                     term=np.abs(og - ref["o"]) @ np.abs(Wo).T)
+    else:
+        assert_close(outg, ref["out"], cfg.act, f"{what} out end to end")
+    return ref
+
+
+def run_attn(cfg, n_ctx, cap=None, resid=True, B=None, poison=False, scale=0.0, garbage_seed=None):
     """poison: cache positions from n_ctx on hold NaN (the attention must not
     read them into the result, also where a tile ends inside a V panel)."""
     B = cfg.B if B is None else B
     cap = cap or -(-(n_ctx + 64) // 64) * 64   # the library wants a multiple of 64
-    say(f"attn {cfg.name} B={B} n_ctx={n_ctx} cap={cap}")
+    say(f"attn {cfg.name} B={B} n_ctx={n_ctx} cap={cap} scale={scale}")
     w = synth.Workload(cfg)
     shp = (cfg.Hkv, cap, cfg.hd)
     ck = synth.normal(cfg.seed, f"attn.ck.{cap}", shp, 1.0, cfg.act)
@@ -205,16 +321,22 @@ def run_attn(cfg, n_ctx, cap=None, resid=True, B=None, poison=False):
         ck_d[:, n_ctx:, :] = float("nan")
         cv_d[:, n_ctx:, :] = float("nan")
     cache = D.KVCache(ck_d, D.v_panels(cv_d))
-    out = torch.empty((B, cfg.d), dtype=P.act_dtype(cfg.act), device="cuda")
-    ws = D.workspace(D.dflash_block_attn_workspace(B, cfg.d, cfg.Hq, cfg.Hkv, cfg.hd, n_ctx))
+    dt = P.act_dtype(cfg.act)
+    out = torch.empty((B, cfg.d), dtype=dt, device="cuda")
+    args = (B, cfg.d, cfg.Hq, cfg.Hkv, cfg.hd, n_ctx)
+    ws = D.workspace(D.dflash_block_attn_workspace(*args))
+    if garbage_seed is not None:
+        garbage(ws, garbage_seed)
     xd = dev(x, cfg.act)
     D.dflash_block_attn(dev(u, cfg.act), xd if resid else None, cfg.Hq, wdev(wq), wdev(wk), wdev(wv),
-                        wdev(wo), cache, n_ctx, 0.0, out, ws)
+                        wdev(wo), cache, n_ctx, scale, out, ws)
     torch.cuda.synchronize()
-    ref = O.block_attn(act_np(u, cfg.act), act_np(x, cfg.act) if resid else None, wnp(wq), wnp(wk), wnp(wv),
-                       wnp(wo), act_np(ck, cfg.act), act_np(cv, cfg.act), n_ctx, cfg.Hq, 0.0,
-                       cfg.act == "bf16")
-    assert_close(f64(out), ref["out"], cfg.act, f"{cfg.name} attn out (n_ctx={n_ctx})")
+    qd, kv = cfg.Hq * cfg.hd, cfg.Hkv * cfg.hd
+    qkvg = f64(D.ws_view(ws, D.dflash_block_attn_qkv_offset(*args), (B, qd + 2 * kv), dt))
+    og = f64(D.ws_view(ws, D.dflash_block_attn_o_offset(*args), (B, qd), dt))
+    check_attn(cfg, act_np(u, cfg.act), act_np(x, cfg.act) if resid else None, wq, wk, wv, wo,
+               act_np(ck, cfg.act), act_np(cv, cfg.act), n_ctx, scale, qkvg, og, f64(out),
+               f"{cfg.name} attn (n_ctx={n_ctx})", B)
     return out
 
 
@@ -230,6 +352,19 @@ def test_attn_tiny_no_residual_short_block():
 @pytest.mark.parametrize("ci,n_ctx", [(1, 1024), (1, 1000), (2, 32768), (3, 65536 + 16), (4, 32768)])
 def test_attn_full(ci, n_ctx):
     run_attn(configs.get(ci), n_ctx)
+
+
+def test_attn_explicit_scale():
+    """A caller-given softmax scale (scale != 0) instead of 1/sqrt(hd)."""
+    run_attn(configs.get(0), 200, scale=0.05)
+    run_attn(configs.get(1), 1000, scale=0.21)
+
+
+def test_attn_garbage_workspace():
+    """Random bytes in the workspace: the Q|Kb|Vb product of the small fp32
+    layer runs on the counter path."""
+    run_attn(configs.get(0), 200, garbage_seed=5)
+    run_attn(configs.get(1), 1000, garbage_seed=6)
 
 
 def test_attn_many_splits():
@@ -391,7 +526,22 @@ def test_topk_rows_ties_signed_zero_and_constant_rows():
 # (5) selector edges + path, (6) accept length
 # ---------------------------------------------------------------------------
 
-def run_selector(cfg, anchor=None, tag="sel"):
+def check_selector(ref, ge, gp, idx, what):
+    """Edges element by element (fp32 arithmetic on exact inputs); the path
+    exact where the best path beats the runner-up by more than GAP, else the
+    GPU's path scores within GAP of the best."""
+    assert_close(ge, ref["edges"], "f32", f"{what} edges")
+    gap = ref["score"] - ref["runner_up"]
+    if gap > GAP:
+        assert np.array_equal(gp, ref["path"]), (gp, ref["path"])
+    else:
+        slots = [int(np.where(idx[i] == gp[i])[0][0]) for i in range(len(gp))]
+        assert O.path_score(ref["edges"], slots) >= ref["score"] - GAP
+    say(f"  {what}: path gap {gap:.3g}")
+    return gap
+
+
+def run_selector(cfg, anchor=None, tag="sel", garbage_seed=None):
     say(f"selector {cfg.name} B={cfg.B} K={cfg.K} r={cfg.r} V={cfg.V}")
     w = synth.Workload(cfg)
     h = synth.normal(cfg.seed, tag + ".h", (cfg.B, cfg.d), 1.0, cfg.act)
@@ -403,23 +553,16 @@ def run_selector(cfg, anchor=None, tag="sel"):
     edges = torch.empty((cfg.B, cfg.K, cfg.K), dtype=torch.float32, device="cuda")
     path = torch.empty((cfg.B,), dtype=torch.int32, device="cuda")
     ws = D.workspace(D.dflash_selector_edges_workspace(cfg.B, cfg.r, cfg.d, cfg.K))
+    if garbage_seed is not None:
+        garbage(ws, garbage_seed)
     D.dflash_selector_edges(dev(h, cfg.act), wdev(Pw), dev(A, cfg.act), dev(Bc, cfg.act),
                             torch.from_numpy(idx).cuda(), torch.from_numpy(un.astype(np.float32)).cuda(),
                             anchor, edges, path, ws)
     torch.cuda.synchronize()
     ref = O.selector(act_np(h, cfg.act), wnp(Pw), act_np(A, cfg.act), act_np(Bc, cfg.act), idx,
                      un.astype(np.float32).astype(np.float64), anchor)
-    ge = edges.cpu().numpy().astype(np.float64)
-    # edges are fp32 results of fp32 arithmetic on exact inputs
-    assert_close(ge, ref["edges"], "f32", f"{cfg.name} edges")
     gp = path.cpu().numpy()
-    gap = ref["score"] - ref["runner_up"]
-    if gap > GAP:
-        assert np.array_equal(gp, ref["path"]), (gp, ref["path"])
-    else:
-        slots = [int(np.where(idx[i] == gp[i])[0][0]) for i in range(cfg.B)]
-        assert O.path_score(ref["edges"], slots) >= ref["score"] - GAP
-    say(f"  path gap {gap:.3g}")
+    check_selector(ref, edges.cpu().numpy().astype(np.float64), gp, idx, cfg.name)
     return gp, ref
 
 
@@ -435,6 +578,10 @@ def test_selector_no_anchor_and_wide_k():
     # one-workgroup path with more than 64 KB of LDS (K=32, r=256 above does
     # not fit in LDS and takes the two-kernel path)
     run_selector(cfg_small(1, K=16, B=16, r=64), tag="selK16")
+
+
+def test_selector_garbage_workspace():
+    run_selector(configs.get(1), tag="selg", garbage_seed=9)
 
 
 def test_accept_len():
@@ -453,12 +600,14 @@ def test_accept_len():
 
 @pytest.mark.parametrize("ci", [0, 1])
 def test_block_step_chain(ci):
-    """inject(n_ctx) -> conv -> attention -> top-K -> selector -> accept, GPU
-    chain against the oracle chain (each on its own intermediates)."""
+    """inject(n_ctx) -> conv -> attention -> top-K -> selector -> accept on the
+    GPU.  Each stage is checked against the oracle fed the GPU's previous
+    outputs (the cache rows, u, h, idx / unary, path); the block output h is
+    also checked against the oracle's own chain."""
     cfg = configs.get(ci)
     say(f"chain {cfg.name}")
     w = synth.Workload(cfg)
-    W = P.DeviceWeights(w)
+    W = P.DeviceWeights(w, drop_host=False)
     cache = P.new_cache(cfg)
     step = P.BlockStep(cfg, W, cache, inject_n=cfg.n_ctx)
     hid = [w.hidden(l) for l in range(cfg.L_t)]
@@ -466,11 +615,12 @@ def test_block_step_chain(ci):
     anchor = int(w.anchor()[0])
     bp = cfg.act == "bf16"
     a = lambda t: act_np(t, cfg.act)
+    A, Bc = w.codebooks()
+    # the oracle's own chain, for the end-to-end check of h
     inj = O.inject([a(h) for h in hid], wnp(w.fc()), None, cfg.eps, wnp(w.wk()), wnp(w.wv()), bp)
     ck = np.zeros((cfg.Hkv, cfg.cap, cfg.hd))
     cv = np.zeros_like(ck)
     O.cache_write(ck, cv, inj["k"], inj["v"], 0)
-    A, Bc = w.codebooks()
     ref = O.block_step(a(x)[0], a(w.conv_base()), wnp(w.w_delta()), cfg.G, wnp(w.wq()), wnp(w.wk()),
                        wnp(w.wv()), wnp(w.wo()), ck, cv, cfg.n_ctx, cfg.Hq, O.weight_to_f64(w.w_lm()),
                        cfg.K, wnp(w.sel_proj()), a(A), a(Bc), anchor, bp)
@@ -478,20 +628,71 @@ def test_block_step_chain(ci):
     step.run(dev(x, cfg.act), cfg.n_ctx, anchor, torch.from_numpy(tgt).cuda(),
              hidden=[dev(h, cfg.act) for h in hid], pos0=0)
     torch.cuda.synchronize()
+    # stage by stage on the GPU's own intermediates
+    gk, gv = rows_of_cache(cache, np.arange(cfg.n_ctx))
+    assert_close(gk, inj["k"], cfg.act, f"{cfg.name} chain cache K")
+    assert_close(gv, inj["v"], cfg.act, f"{cfg.name} chain cache V")
+    CK = np.zeros((cfg.Hkv, cfg.cap, cfg.hd))
+    CV = np.zeros_like(CK)
+    O.cache_write(CK, CV, gk, gv, 0)
+    c = O.conv(a(x), a(w.conv_base()), wnp(w.w_delta()), cfg.G, bp)
+    ug = f64(step.u)
+    assert_close(ug, c["u"], cfg.act, f"{cfg.name} chain u")
     gh = f64(step.h)
-    assert_close(gh, ref["attn"]["out"], cfg.act, f"{cfg.name} chain h_out")
-    # the GPU's LM head ran on its own h: by Cauchy-Schwarz its logits sit
-    # within |h_gpu - h_ref| * max_v |W_lm[v]| of the oracle's
-    wl = w.w_lm()
-    wmax = max(np.sqrt((O.act_to_f64(wl["data"][r0:r0 + 16384], wl["dtype"]) ** 2).sum(1)).max()
-               for r0 in range(0, cfg.V, 16384)) if wl["dtype"] != "q8_0" else None
-    drift = np.sqrt(((gh - ref["attn"]["out"]) ** 2).sum(1)) * wmax
-    say(f"  chain logit drift bound per row: max {drift.max():.3g}")
-    check_topk(step.idx.cpu().numpy(), step.unary.cpu().numpy(), ref["topk"]["logits"], cfg.K, cfg.act,
-               f"{cfg.name} chain top-K", drift=drift)
-    gap = ref["sel"]["score"] - ref["sel"]["runner_up"]
-    same_idx = np.array_equal(step.idx.cpu().numpy(), ref["topk"]["idx"])
-    say(f"  chain: top-K identical={same_idx}, path gap {gap:.3g}")
-    if same_idx and gap > 0.05:
-        assert np.array_equal(step.path.cpu().numpy()[0], ref["path"])
-        assert int(step.accept.cpu()[0]) == int(m[0])
+    at = O.block_attn(ug[0], a(x)[0], wnp(w.wq()), wnp(w.wk()), wnp(w.wv()), wnp(w.wo()), CK, CV, cfg.n_ctx,
+                      cfg.Hq, 0.0, bp)
+    assert_close(gh, at["out"], cfg.act, f"{cfg.name} chain h from the GPU's u and cache")
+    logits = O.lm_logits_stored(gh, w.w_lm())
+    gi, gu = step.idx.cpu().numpy(), step.unary.cpu().numpy()
+    check_topk(gi, gu, logits, cfg.K, cfg.act, f"{cfg.name} chain top-K from the GPU's h")
+    sel = O.selector(gh, wnp(w.sel_proj()), a(A), a(Bc), gi, gu.astype(np.float64), anchor)
+    gp = step.path.cpu().numpy()[0]
+    check_selector(sel, step.edges.cpu().numpy().astype(np.float64), gp, gi, f"{cfg.name} chain selector")
+    assert int(step.accept.cpu()[0]) == int(O.accept_len(gp[None, :], tgt)[0])
+    # end to end: the GPU's h against the oracle's own chain
+    assert_close(gh, ref["attn"]["out"], cfg.act, f"{cfg.name} chain h end to end")
+
+
+def test_decode_64k_three_steps():
+    """The 64k decode workload as a sequence: the cache holds 65536 seeded
+    rows; step s injects 16 rows at 65536 + 16 s (half a V panel each, so the
+    steps alternate between starting a panel and finishing it) and then
+    attends 65536 + 16 (s + 1) context keys plus the block.  Each step's rows
+    and output are checked; the oracle's cache takes the GPU's injected rows
+    once they have passed."""
+    cfg = configs.get(3)
+    w = synth.Workload(cfg)
+    n0, n = cfg.prefill_kv, cfg.inject_per_step
+    shp = (cfg.Hkv, n0, cfg.hd)
+    ck0 = synth.normal(cfg.seed, "seq.ck", shp, 1.0, cfg.act)
+    cv0 = synth.normal(cfg.seed, "seq.cv", shp, 1.0, cfg.act)
+    cache = P.new_cache(cfg)
+    cache.k[:, :n0] = dev(ck0, cfg.act)
+    cache.v[:, :n0 // 32] = D.v_panels(dev(cv0, cfg.act))
+    CK = np.zeros((cfg.Hkv, cfg.cap, cfg.hd))
+    CV = np.zeros_like(CK)
+    CK[:, :n0] = act_np(ck0, cfg.act)
+    CV[:, :n0] = act_np(cv0, cfg.act)
+    del ck0, cv0
+    wq, wk, wv, wo = w.wq(), w.wk(), w.wv(), w.wo()
+    dt = P.act_dtype(cfg.act)
+    for s in range(3):
+        pos0 = n0 + n * s
+        hid = [synth.normal(cfg.seed, f"seq.h{s}.{l}", (n, cfg.d_t), 1.0, cfg.act) for l in range(cfg.L_t)]
+        _, gk, gv = run_inject(cfg, n, pos0, cache=cache, hid=hid)
+        O.cache_write(CK, CV, gk, gv, pos0)
+        n_ctx = pos0 + n
+        u = synth.normal(cfg.seed, f"seq.u{s}", (cfg.B, cfg.d), 1.0, cfg.act)
+        x = synth.normal(cfg.seed, f"seq.x{s}", (cfg.B, cfg.d), 1.0, cfg.act)
+        out = torch.empty((cfg.B, cfg.d), dtype=dt, device="cuda")
+        args = (cfg.B, cfg.d, cfg.Hq, cfg.Hkv, cfg.hd, n_ctx)
+        ws = D.workspace(D.dflash_block_attn_workspace(*args))
+        say(f"attn step {s}: n_ctx={n_ctx}")
+        D.dflash_block_attn(dev(u, cfg.act), dev(x, cfg.act), cfg.Hq, wdev(wq), wdev(wk), wdev(wv), wdev(wo),
+                            cache, n_ctx, 0.0, out, ws)
+        torch.cuda.synchronize()
+        qd, kv = cfg.Hq * cfg.hd, cfg.Hkv * cfg.hd
+        qkvg = f64(D.ws_view(ws, D.dflash_block_attn_qkv_offset(*args), (cfg.B, qd + 2 * kv), dt))
+        og = f64(D.ws_view(ws, D.dflash_block_attn_o_offset(*args), (cfg.B, qd), dt))
+        check_attn(cfg, act_np(u, cfg.act), act_np(x, cfg.act), wq, wk, wv, wo, CK, CV, n_ctx, 0.0, qkvg, og,
+                   f64(out), f"64k step {s} attn (n_ctx={n_ctx})", cfg.B)

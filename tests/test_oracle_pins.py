@@ -245,7 +245,7 @@ def test_attention_identical_keys_give_mean_v():
 def test_attention_single_key_returns_v():
     q = randn(3, 8)
     k, v = randn(1, 8), randn(1, 8)
-    np.testing.assert_allclose(O.softmax_attend(q, k, v, 0.3), np.tile(v, (3, 1)), rtol=1e-14)
+    np.testing.assert_allclose(O.softmax_attend(q, k, v, 0.3)[0], np.tile(v, (3, 1)), rtol=1e-14)
 
 
 def test_attention_matches_torch_sdpa_mha():
@@ -281,6 +281,55 @@ def test_attention_ignores_rows_past_n_ctx():
     ck = c["ck"].copy()
     ck[:, c["n_ctx"]:] = 1e6
     np.testing.assert_array_equal(_run_attn(c, ck=ck)["out"], r["out"])
+
+
+def test_attention_weight_rounding_bound_holds_and_is_needed():
+    """The bound for softmax weights rounded to bf16 before they multiply V
+    (the GPU's P.V operands): brute force emulates every way of rounding each
+    weight up or down by at most one unit roundoff and never leaves the bound,
+    and a single adversarial rounding comes within a few percent of it, so the
+    bound is neither wrong nor vacuous.  Catches a dropped |V - out| (the
+    bound would then not shrink for equal values) or a wrong roundoff."""
+    q, keys, vals = randn(2, 8), randn(40, 8), randn(40, 8) * 3.0
+    out, bound = O.softmax_attend(q, keys, vals, 0.4, O.U_BF16)
+    assert np.all(bound > 0)
+    s = (q @ keys.T) * 0.4
+    w = np.exp(s - s.max(1, keepdims=True))
+    w /= w.sum(1, keepdims=True)
+    u = O.U_BF16
+    for trial in range(200):
+        e = rng.uniform(-u, u, size=w.shape)
+        e[:, :trial % 3] = u                           # some weights at the extreme
+        we = w * (1 + e)
+        o2 = (we @ vals) / we.sum(1, keepdims=True)
+        assert np.all(np.abs(o2 - out) <= bound * (1 + 1e-12))
+    # the worst case for element (0, j): weights of values above out[0, j]
+    # rounded up, below it rounded down
+    j = 3
+    e = np.where(vals[:, j] > out[0, j], u, -u)
+    we = w[0] * (1 + e)
+    o2 = (we @ vals[:, j]) / we.sum()
+    assert abs(o2 - out[0, j]) >= 0.95 * bound[0, j]
+    # equal values: rounding the weights cannot move the output
+    _, b0 = O.softmax_attend(q, keys, np.ones((40, 8)), 0.4, O.U_BF16)
+    np.testing.assert_allclose(b0, 0.0, atol=1e-15)
+    _, bz = O.softmax_attend(q, keys, vals, 0.4)
+    assert np.all(bz == 0)
+    # bf16's unit roundoff: 8 significant bits, |bf16(x) - x| <= 2^-8 |x|
+    xs = rng.uniform(0.5, 4.0, 20000)
+    assert np.max(np.abs(O.round_bf16(xs) - xs) / xs) <= O.U_BF16
+    assert np.max(np.abs(O.round_bf16(xs) - xs) / xs) > 0.9 * O.U_BF16
+
+
+def test_attention_stages_compose():
+    """attn_qkv -> attn_core -> attn_out is block_attn, and attn_core fed the
+    projections reproduces the same O (the stage-fed GPU checks rely on it)."""
+    c = _attn_case()
+    r = _run_attn(c)
+    p = O.attn_qkv(c["u"], c["wq"], c["wk"], c["wv"], False)
+    co = O.attn_core(p["q"], p["kb"], p["vb"], c["ck"], c["cv"], c["n_ctx"], c["Hq"], 0.0, False)
+    np.testing.assert_array_equal(co["o"], r["o"])
+    np.testing.assert_array_equal(O.attn_out(co["o"], c["wo"], c["resid"], False), r["out"])
 
 
 # --------------------------------------------------------------------------
@@ -511,6 +560,74 @@ def test_tiny_config_step_runs_fast():
     assert r["path"].shape == (cfg.B,)
     assert np.all(np.isfinite(r["attn"]["out"]))
     assert np.all((r["path"] >= 0) & (r["path"] < cfg.V))
+
+
+def _step_inputs(cfg):
+    w = synth.Workload(cfg)
+    f = lambda wt: O.weight_to_f64(wt)
+    a = lambda x: O.act_to_f64(x, cfg.act)
+    inj = O.inject([a(w.hidden(l)) for l in range(cfg.L_t)], f(w.fc()), None, cfg.eps, f(w.wk()), f(w.wv()), False)
+    ck = np.zeros((cfg.Hkv, cfg.cap, cfg.hd))
+    cv = np.zeros_like(ck)
+    O.cache_write(ck, cv, inj["k"], inj["v"], 0)
+    A, Bc = w.codebooks()
+    return dict(x=a(w.x())[0], base=a(w.conv_base()), w_delta=f(w.w_delta()), G=cfg.G, wq=f(w.wq()),
+                wk=f(w.wk()), wv=f(w.wv()), wo=f(w.wo()), cache_k=ck, cache_v=cv, n_ctx=cfg.n_ctx,
+                n_q_heads=cfg.Hq, w_lm=f(w.w_lm()), K=cfg.K, P=f(w.sel_proj()), A=a(A), Bc=a(Bc),
+                anchor=int(w.anchor()[0]), bf16_points=False)
+
+
+def test_block_step_wiring_residual_is_x():
+    """Wo = 0 leaves the block output equal to the block input x exactly, so
+    the residual is x (not the conv output u) and nothing else is added
+    (reading R10); the LM head and selector then run on x."""
+    cfg = configs.get(0)
+    kw = _step_inputs(cfg)
+    r = O.block_step(**dict(kw, wo=np.zeros_like(kw["wo"])))
+    np.testing.assert_array_equal(r["attn"]["out"], kw["x"])
+    np.testing.assert_allclose(r["topk"]["logits"], kw["x"] @ kw["w_lm"].T, rtol=1e-13, atol=1e-13)
+
+
+def test_block_step_wiring_conv_feeds_attention():
+    """base = the single tap e_0 with W_delta = 0 makes the conv the identity
+    (reading R7), so the attention's Q / Kb / Vb are projections of x itself
+    (the conv output feeds Q / K / V, reading R8); with a zero tap 0 instead,
+    u = 0 and Q / Kb / Vb vanish."""
+    cfg = configs.get(0)
+    kw = _step_inputs(cfg)
+    e0 = np.zeros_like(kw["base"])
+    e0[0] = 1.0
+    r = O.block_step(**dict(kw, base=e0, w_delta=np.zeros_like(kw["w_delta"])))
+    np.testing.assert_array_equal(r["conv"]["u"][0], kw["x"])
+    np.testing.assert_array_equal(r["attn"]["q"], kw["x"] @ kw["wq"].T)
+    np.testing.assert_array_equal(r["attn"]["kb"], kw["x"] @ kw["wk"].T)
+    r0 = O.block_step(**dict(kw, base=np.zeros_like(kw["base"]), w_delta=np.zeros_like(kw["w_delta"])))
+    assert not np.any(r0["attn"]["q"]) and not np.any(r0["attn"]["vb"])
+
+
+@pytest.mark.parametrize("kind", ["bf16", "q8_0"])
+def test_lm_logits_stored_matches_a_direct_matmul(kind):
+    """lm_logits_stored decodes the head a chunk of rows at a time; against
+    torch's own decoding (bf16 -> fp64; Q8_0 codes times fp32 scales cast to
+    bf16) and one fp64 matmul, across 16384-row chunk boundaries and a ragged
+    last chunk.  Catches an off-by-one chunk edge, a chunk written to the
+    wrong columns or a scale row misaligned with its codes."""
+    V, d, B = 2 * 16384 + 1234, 64, 3
+    h = randn(B, d)
+    if kind == "bf16":
+        wl = synth.weight(5, "lmpin", V, d, "bf16")
+        wt = torch.from_numpy(wl["data"].view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    else:
+        wl = synth.weight(5, "lmpin", V, d, "q8_0")
+        q = torch.from_numpy(wl["data"].astype(np.float32)).view(V, d // 32, 32)
+        sc = torch.from_numpy(wl["scales"]).to(torch.float32)[:, :, None]
+        wt = (q * sc).to(torch.bfloat16).to(torch.float64).reshape(V, d)
+    ref = (torch.from_numpy(h) @ wt.T).numpy()
+    got = O.lm_logits_stored(h, wl)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-12)
+    # the rows at the chunk edges are where they belong
+    for v in (16383, 16384, 32767, 32768, V - 1):
+        np.testing.assert_allclose(got[:, v], h @ wt[v].numpy(), rtol=1e-13, atol=1e-12)
 
 
 # --------------------------------------------------------------------------
