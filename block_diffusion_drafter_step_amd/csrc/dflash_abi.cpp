@@ -486,9 +486,12 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   return launched(e, "wo");
 }
 
-dflash_status dflash_topk_unary(const void *h, int32_t B, int32_t act,
-                                const dflash_weight *lm_head, int32_t K, int32_t *idx,
-                                float *unary, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+dflash_status topk_check(const void *h, int32_t B, int32_t act, const dflash_weight *lm_head, int32_t K,
+                         int32_t *idx, float *unary) {
   TRY(check_act(act));
   TRY(need_ptr(h, "h"));
   TRY(need_ptr(idx, "idx"));
@@ -502,9 +505,13 @@ dflash_status dflash_topk_unary(const void *h, int32_t B, int32_t act,
   TRY(check_weight(lm_head, "lm_head", V, d, act, true));
   if (K < 1 || K > DFLASH_MAX_TOPK || K > V)
     return fail(DFLASH_ERR_INVALID_ARG, "K must be in [1, min(V, %d)]", DFLASH_MAX_TOPK);
-  const size_t need = topk_ws(V, K);
-  TRY(check_ws(ws, ws_bytes, need));
+  return DFLASH_OK;
+}
 
+// carve `ws` (at least topk_ws(V, K) bytes) and enqueue the LM head + merge
+dflash_status topk_enqueue(const void *h, int32_t B, int32_t act, const dflash_weight *lm_head, int32_t K,
+                           int32_t *idx, float *unary, void *ws, void *stream) {
+  const int64_t V = lm_head->rows, d = lm_head->cols;
   Carve c(ws);
   TopkArgs a;
   memset(&a, 0, sizeof a);
@@ -536,6 +543,35 @@ dflash_status dflash_topk_unary(const void *h, int32_t B, int32_t act,
   a.idx = idx;
   a.unary = unary;
   return launched(launch_topk(act, wkind_of(lm_head), a, (hipStream_t)stream), "topk");
+}
+
+static_assert(DFLASH_TOPK_NOALLOC_SCRATCH_BYTES == kTopkScratchBytes, "header and library agree");
+
+}  // namespace
+
+extern "C" {
+
+dflash_status dflash_topk_unary(const void *h, int32_t B, int32_t act,
+                                const dflash_weight *lm_head, int32_t K, int32_t *idx,
+                                float *unary, void *ws, size_t ws_bytes, void *stream) {
+  TRY(topk_check(h, B, act, lm_head, K, idx, unary));
+  TRY(check_ws(ws, ws_bytes, topk_ws(lm_head->rows, K)));
+  return topk_enqueue(h, B, act, lm_head, K, idx, unary, ws, stream);
+}
+
+dflash_status dflash_topk_unary_noalloc(const void *h, int32_t B, int32_t act,
+                                        const dflash_weight *lm_head, int32_t K, int32_t *idx,
+                                        float *unary, void *stream) {
+  TRY(topk_check(h, B, act, lm_head, K, idx, unary));
+  const size_t need = topk_ws(lm_head->rows, K);
+  if (need > kTopkScratchBytes)
+    return fail(DFLASH_ERR_UNSUPPORTED,
+                "V = %lld, K = %d needs %zu bytes of scratch, more than the %zu of the static array",
+                (long long)lm_head->rows, K, need, kTopkScratchBytes);
+  void *ws = nullptr;
+  const hipError_t e = topk_scratch_ptr(&ws);
+  if (e != hipSuccess) return fail(DFLASH_ERR_LAUNCH, "static scratch: %s", hipGetErrorString(e));
+  return topk_enqueue(h, B, act, lm_head, K, idx, unary, ws, stream);
 }
 
 dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,

@@ -153,6 +153,11 @@ constexpr int kMaxCUs = 1024;
 int device_cu_count();
 int topk_plan_waves(long V, int wkind);
 hipError_t launch_topk(int act, int wkind, const TopkArgs &a, hipStream_t st);
+// The no-allocation LM-head call's static scratch: its size (the workspace
+// of K <= 32 for any vocabulary whose plan has at most kMaxCUs workgroups,
+// i.e. V <= 2^20) and the current device's address of it.
+constexpr size_t kTopkScratchBytes = 4390912;
+hipError_t topk_scratch_ptr(void **out);
 
 // ---- row-wise top-K of an fp32 matrix (K <= 1024) -----------------------------------
 // bytes of the two candidate-key buffers the passes alternate between

@@ -15,6 +15,8 @@
 // (top-K, max, sum) per token per workgroup is written.  A second kernel
 // merges the partials in a fixed order: deterministic, and the ordering is
 // (logit descending, index ascending) throughout.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 #include "stream.h"
@@ -616,6 +618,36 @@ int device_cu_count() {
     cached[dev] = n;
   }
   return cached[dev];
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the LM head's no-allocation entry point: a static device array
+// (each GPU holds its own copy until the process ends).  In host code the
+// array's name is not its device address, so it is never passed to a kernel
+// or a copy: topk_scratch_ptr() looks the address up with
+// hipGetSymbolAddress, once per device with that device current, and every
+// later use takes that pointer.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kTopkScratchBytes];
+
+hipError_t topk_scratch_ptr(void **out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace dfl

@@ -62,6 +62,7 @@ _SIGS = {
     "dflash_block_attn_o_offset": ([_I32, _I32, _I32, _I32, _I32, _I64], _SZ),
     "dflash_topk_unary": ([_P, _I32, _I32, _PW, _I32, _P, _P, _P, _SZ, _P], _I32),
     "dflash_topk_unary_workspace": ([_I32, _I64, _I32], _SZ),
+    "dflash_topk_unary_noalloc": ([_P, _I32, _I32, _PW, _I32, _P, _P, _P], _I32),
     "dflash_selector_edges": ([_P, _I32, _I32, _PW, _P, _P, _I64, _P, _P, _I32, _I32, _P, _P, _P, _SZ,
                                _P], _I32),
     "dflash_selector_edges_workspace": ([_I32, _I32, _I32, _I32], _SZ),
@@ -273,6 +274,15 @@ def dflash_topk_unary(h: torch.Tensor, lm_head: Weight, K: int, idx: torch.Tenso
     wsp, wsb = _ws(ws)
     _check(load().dflash_topk_unary(_ptr(h), B, _act_of(h), ctypes.byref(w), K, _ptr(idx), _ptr(unary),
                                     wsp, wsb, _stream(stream)))
+
+
+def dflash_topk_unary_noalloc(h: torch.Tensor, lm_head: Weight, K: int, idx: torch.Tensor,
+                              unary: torch.Tensor, stream=None):
+    """dflash_topk_unary with the library's static scratch (no workspace)."""
+    B = h.shape[0]
+    w = lm_head.c()
+    _check(load().dflash_topk_unary_noalloc(_ptr(h), B, _act_of(h), ctypes.byref(w), K, _ptr(idx),
+                                            _ptr(unary), _stream(stream)))
 
 
 def dflash_selector_edges(h: torch.Tensor, proj: Weight, cb_pred: torch.Tensor, cb_succ: torch.Tensor,

@@ -206,6 +206,22 @@ dflash_status dflash_topk_unary(const void *h, int32_t B, int32_t act,
                                 float *unary, void *ws, size_t ws_bytes, void *stream);
 size_t dflash_topk_unary_workspace(int32_t B, int64_t V, int32_t K);
 
+/* dflash_topk_unary without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments (minus ws), results, determinism and
+ * errors as dflash_topk_unary; nothing is allocated.  Its scratch is a static
+ * device array of DFLASH_TOPK_NOALLOC_SCRATCH_BYTES in the library, one per
+ * GPU, held until the process ends; it serves any K <= DFLASH_MAX_TOPK for
+ * vocabularies up to 2^20 rows, and a call that would need more returns
+ * DFLASH_ERR_UNSUPPORTED before launching anything.  Calls on one GPU share
+ * that array (it keeps the last call's contents, which no call reads):
+ * calls that may overlap on one GPU (different streams without ordering)
+ * race and must not be issued. */
+#define DFLASH_TOPK_NOALLOC_SCRATCH_BYTES 4390912
+dflash_status dflash_topk_unary_noalloc(const void *h, int32_t B, int32_t act,
+                                        const dflash_weight *lm_head, int32_t K, int32_t *idx,
+                                        float *unary, void *stream);
+
 /* (5) Candidate-selector edges and the best path through them.
  * "spec : add DFlash2 support", Overview:
  *   edge(p -> c) = < A[p] (.) project(h), B[c] > + unary[c]

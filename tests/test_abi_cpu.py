@@ -224,3 +224,18 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(4, 4)
     with pytest.raises(ValueError):
         D._ptr(x)
+
+
+@no_gpu
+def test_noalloc_topk_validates_before_any_device_call(lib):
+    """Bad arguments and a vocabulary beyond the static scratch are rejected
+    on the host (no device is touched: there is none here)."""
+    h, idx, un = FAKE, FAKE, FAKE
+    w = W(1, (1 << 20) + 16, 64)
+    assert lib.dflash_topk_unary_noalloc(h, 16, 1, ctypes.byref(w), 32, idx, un, None) == 2
+    assert b"static array" in lib.dflash_last_error()
+    w = W(1, 1000, 64)
+    assert lib.dflash_topk_unary_noalloc(h, 16, 1, ctypes.byref(w), 33, idx, un, None) == 1
+    assert lib.dflash_topk_unary_noalloc(h, 17, 1, ctypes.byref(w), 8, idx, un, None) == 1
+    assert lib.dflash_topk_unary_noalloc(None, 16, 1, ctypes.byref(w), 8, idx, un, None) == 1
+
