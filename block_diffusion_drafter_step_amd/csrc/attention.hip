@@ -364,6 +364,275 @@ __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_s
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split kernel for Q8_0 caches (head_dim 128, GQA group x block of at most 64
+// query rows).  Every wave owns a contiguous range of keys and carries all
+// query rows of the group as MFMA columns (column c = local head c / B, token
+// c % B), so each code and scale is loaded by exactly one wave, straight into
+// registers, and dequantised once: no LDS staging, no barrier in the loop.
+// Per 32-key tile a lane loads 4 x 16 bytes of K codes (each instruction 16
+// key rows x 64 contiguous bytes), 8 x 8 bytes of V^T codes (16 panel rows x
+// 32 bytes), its keys' K scales and the 64 bytes of V scales of its eight
+// keys: 8.5 KB per tile against 16 KB for bf16.  A tile is dequantised to
+// bf16 (value = bf16_rne(fp32(scale) * code)), the next tile's loads are
+// issued into the codes' registers, and the tile is multiplied:
+//   S^T = K Q^T  (keys x columns),  online softmax per column (base 2),
+//   O^T = V^T P^T (dims x columns)
+// with the interleaved key order of the two 16-key S^T tiles (row r of tile
+// st is key 8(r/4) + 4st + r%4), so each lane's eight weights of one column
+// are eight consecutive keys: the P^T operand whose V^T partner is one 8-byte
+// run of a panel row.  MFMA j of the score product takes head dims
+// 64 (j/2) + 16 g + 8 (j%2) .. + 8 from lane group g (for the codes and Q
+// alike).  The weights are taken relative to a reference maximum that moves
+// only when the scores exceed it by more than 2^8, so the accumulators are
+// rescaled about once.  The four waves of a workgroup hold four consecutive
+// parts of its keys; their (O, m, l) are merged in LDS in wave order and
+// written as one split partial per query row, in attn_combine_kernel's layout.
+// ---------------------------------------------------------------------------
+constexpr int kWaveHD = 128;
+constexpr int kWaveMaxCols = 64;
+constexpr float kLazyMax = 8.f;   // log2 of the largest unnormalised weight
+
+struct Q8Tile {
+  uint4 kc[2][2];   // K codes: S^T tile st, dims 64 m + 16 g .. + 16 of the lane's key row
+  uint2 ks[2];      // the four K scales of that key row
+  uint2 vc[kWaveHD / 16];   // V^T codes: dim 16 dt + r16, keys 8 g .. 8 g + 7
+  uint4 vs[4];      // V scales of keys 8 g .. 8 g + 7 (four per key)
+};
+
+__device__ __forceinline__ float f16_lo(unsigned w) { return half_bits_to_f32((uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(unsigned w) { return half_bits_to_f32((uint16_t)(w >> 16)); }
+
+template <int NCT>
+__global__ __launch_bounds__(256, 1) void attn_q8_kernel(AttnArgs a) {
+  constexpr int HD = kWaveHD, NQF = HD / 32, NDT = HD / 16, NB = HD / 32;
+  __shared__ float xch[3][(NDT * NCT * 4 + 2 * NCT) * 64];
+  __shared__ Frag<bf16> qs[NCT * NQF * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int kvh = blockIdx.y, sp = blockIdx.x;
+  const int grp = a.Hq / a.Hkv, B = a.B, ncol = grp * B;
+  // this wave's keys [k0, k1): part `wave` of the workgroup's chunk, whole tiles
+  const long w0 = (long)sp * a.chunk, w1 = min(a.n_ctx, w0 + (long)a.chunk);
+  const long part = ((a.chunk / 4 + kAttnKT - 1) / kAttnKT) * kAttnKT;
+  const long k0 = min(w1, w0 + wave * part), k1 = min(w1, k0 + part);
+  const int ntile = (int)((k1 - k0 + kAttnKT - 1) / kAttnKT);
+  const char *kq = reinterpret_cast<const char *>(a.ck) + (long)kvh * a.cap * HD;
+  const char *vq = reinterpret_cast<const char *>(a.cv) + (long)kvh * a.cap * HD;
+  const char *ksc = reinterpret_cast<const char *>(a.cks) + (long)kvh * a.cap * NB * 2;
+  const char *vsc = reinterpret_cast<const char *>(a.cvs) + (long)kvh * a.cap * NB * 2;
+  const long qld = (long)(a.Hq + 2 * a.Hkv) * HD;
+  const float sl2 = a.scale * kLog2e;
+
+  // Q^T fragments in LDS (read where they are used, leaving the registers to
+  // the accumulators and the tiles in flight): slot (ct, j) of lane l
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int c = 16 * ct + r16;
+    const bool ok = c < ncol;
+    const int hl = ok ? c / B : 0, t = ok ? c - hl * B : 0;
+    const bf16 *qp = reinterpret_cast<const bf16 *>(a.qkv) + (long)t * qld + (long)(kvh * grp + hl) * HD;
+    if (wave == 0) {
+#pragma unroll
+      for (int j = 0; j < NQF; ++j)
+        qs[(ct * NQF + j) * 64 + lane] =
+            ok ? load_frag(qp + 64 * (j >> 1) + 16 * g + 8 * (j & 1)) : frag_zero<bf16>();
+    }
+  }
+  __syncthreads();
+  f32x4 o[NDT][NCT];
+  float mr[NCT], lr[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt][ct] = zero4();
+    mr[ct] = -__builtin_inff();
+    lr[ct] = 0.f;
+  }
+
+  // a tile's loads from a wave-uniform base plus 32-bit lane offsets: key
+  // rows t0 + row (all 32 below the capacity; rows past k1 feed masked
+  // scores) and the tile's V^T panel (inside the capacity)
+  unsigned krow[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) krow[st] = (unsigned)(8 * (r16 >> 2) + 4 * st + (r16 & 3));
+  auto load = [&](Q8Tile &T, long t0) {
+    const char *kb = kq + t0 * HD, *sb = ksc + t0 * (NB * 2);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        T.kc[st][m] = *reinterpret_cast<const uint4 *>(kb + krow[st] * HD + 64 * m + 16 * g);
+      T.ks[st] = *reinterpret_cast<const uint2 *>(sb + krow[st] * (NB * 2));
+    }
+    const char *vb = vq + (t0 >> 5) * (long)(HD * 32);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      T.vc[dt] = *reinterpret_cast<const uint2 *>(vb + (16 * dt + r16) * 32 + 8 * g);
+    const char *vs = vsc + (t0 + 8 * g) * (NB * 2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) T.vs[q] = *reinterpret_cast<const uint4 *>(vs + 16 * q);
+  };
+
+  // a tile's bf16 fragments (keys past lim: V^T entries 0)
+  auto dequant = [&](const Q8Tile &T, int lim, Frag<bf16> (&kf)[2][NQF], Frag<bf16> (&vf)[NDT]) {
+    // K fragments: MFMA j takes codes 8 (j%2) .. of the 16 at dims 64 (j/2) + 16 g
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const float s0 = (g >> 1) ? f16_hi(T.ks[st].x) : f16_lo(T.ks[st].x);   // block g/2
+      const float s1 = (g >> 1) ? f16_hi(T.ks[st].y) : f16_lo(T.ks[st].y);   // block 2 + g/2
+      kf[st][0] = dequant8(make_uint2(T.kc[st][0].x, T.kc[st][0].y), s0);
+      kf[st][1] = dequant8(make_uint2(T.kc[st][0].z, T.kc[st][0].w), s0);
+      kf[st][2] = dequant8(make_uint2(T.kc[st][1].x, T.kc[st][1].y), s1);
+      kf[st][3] = dequant8(make_uint2(T.kc[st][1].z, T.kc[st][1].w), s1);
+    }
+    // V^T fragments: element e is key 8g + e at dim 16 dt + r16, scale of
+    // block dt / 2 of that key; keys from k1 on become 0 (a tile that ends
+    // inside its panel: the rest of the panel may hold anything)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint4 w = T.vs[e >> 1];
+        const int hi = (e & 1) * 4 + b;   // fp16 index within the uint4
+        const unsigned word = (hi >> 1) == 0 ? w.x : (hi >> 1) == 1 ? w.y : (hi >> 1) == 2 ? w.z : w.w;
+        sv[e] = (hi & 1) ? f16_hi(word) : f16_lo(word);
+        if (8 * g + e >= lim) sv[e] = 0.f;
+      }
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd) {
+        const int dt = 2 * b + dd;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const unsigned word = e < 4 ? T.vc[dt].x : T.vc[dt].y;
+          const int code = ((int)(word << (24 - 8 * (e & 3)))) >> 24;
+          vf[dt].v[e] = from_f32<bf16>((float)code * sv[e]);
+        }
+      }
+    }
+  };
+  auto math = [&](const Frag<bf16> (&kf)[2][NQF], const Frag<bf16> (&vf)[NDT], int lim) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 s[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        s[st] = zero4();
+#pragma unroll
+        for (int j = 0; j < NQF; ++j) mma(s[st], kf[st][j], qs[(ct * NQF + j) * 64 + lane]);
+      }
+      // lane: column r16, keys 8g + 4st + i
+      float p[8];
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = 8 * g + 4 * st + i < lim ? s[st][i] * sl2 : -__builtin_inff();
+          p[st * 4 + i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      // the column's reference maximum moves only when the scores rise more
+      // than 2^8 above it (a wave-uniform branch, rare after the first tile)
+      const bool up = mx > mr[ct] + kLazyMax;
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float alpha = up ? exp2f(mr[ct] - mx) : 1.f;   // mr = -inf: 0
+        if (up) mr[ct] = mx;
+        lr[ct] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt][ct] *= alpha;
+      }
+      // the row sum uses the weights exactly as the P.V product sees them
+      float ls = 0.f;
+      Frag<bf16> pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pf.v[e] = from_f32<bf16>(p[e] == -__builtin_inff() ? 0.f : exp2f(p[e] - mr[ct]));
+        ls += to_f32(pf.v[e]);
+      }
+      ls += shfl_xor(ls, 16);
+      ls += shfl_xor(ls, 32);
+      lr[ct] += ls;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) mma(o[dt][ct], vf[dt], pf);
+    }
+  };
+
+  // one tile of codes in registers: once a tile is dequantised its codes are
+  // dead, so the next tile's loads are issued there and land while this
+  // tile is multiplied
+  if (ntile > 0) {
+    Q8Tile T;
+    load(T, k0);
+    for (int i = 0; i < ntile; ++i) {
+      const long t0 = k0 + (long)i * kAttnKT;
+      const int lim = (int)min(k1 - t0, (long)kAttnKT);   // keys of this tile inside the range
+      Frag<bf16> kf[2][NQF], vf[NDT];
+      dequant(T, lim, kf, vf);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < ntile) load(T, t0 + kAttnKT);
+      __builtin_amdgcn_sched_barrier(0);
+      math(kf, vf, lim);
+    }
+  }
+
+  // waves 1..3 hand (o, m, l) to wave 0, which merges them in wave order
+  constexpr int NO = NDT * NCT * 4;
+  if (wave > 0) {
+    float *x = xch[wave - 1];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[((dt * NCT + ct) * 4 + i) * 64 + lane] = o[dt][ct][i];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      x[(NO + 2 * ct) * 64 + lane] = mr[ct];
+      x[(NO + 2 * ct + 1) * 64 + lane] = lr[ct];
+    }
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll 1
+  for (int w = 0; w < 3; ++w) {
+    const float *x = xch[w];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float m1 = x[(NO + 2 * ct) * 64 + lane], l1 = x[(NO + 2 * ct + 1) * 64 + lane];
+      const float mm = fmaxf(mr[ct], m1);
+      if (mm == -__builtin_inff()) continue;   // neither part saw a key
+      const float a0 = exp2f(mr[ct] - mm), a1 = exp2f(m1 - mm);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[dt][ct][i] = o[dt][ct][i] * a0 + x[((dt * NCT + ct) * 4 + i) * 64 + lane] * a1;
+      lr[ct] = lr[ct] * a0 + l1 * a1;
+      mr[ct] = mm;
+    }
+  }
+  // partials of column (hl, t): lane holds dims 16 dt + 4 g + i
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int c = 16 * ct + r16;
+    if (c >= ncol) continue;
+    const int hl = c / B, t = c - hl * B;
+    const long base = ((long)(kvh * grp + hl) * B + t) * a.n_split + sp;
+    float *po = a.part_o + base * HD + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt) = o[dt][ct];
+    if (g == 0) {
+      a.part_ml[base * 2] = mr[ct];
+      a.part_ml[base * 2 + 1] = lr[ct];
+    }
+  }
+}
+
 // O[t][h*hd + d] = (sum_s 2^(m_s - M) O_s + 2^(m_b - M) O_b) /
 //                  (sum_s 2^(m_s - M) l_s + 2^(m_b - M) l_b),
 // where (m_b, l_b, O_b) is the block's own B keys, scored here from Q, Kb, Vb
@@ -545,13 +814,22 @@ int attn_streams(int act, int hd) {
   return hd == 64 ? attn_streams_t<bf16, 64>() : attn_streams_t<bf16, 128>();
 }
 
+bool attn_q8_ok(int hd, int grp, int B) { return hd == kWaveHD && grp * B <= kWaveMaxCols; }
+
+void attn_plan_call(int act, int hd, int grp, int B, int kvq, long n_keys, int Hkv, int *chunk, int *n_split) {
+  (void)grp;
+  (void)B;
+  // the Q8_0 kernel: one 4-wave workgroup per CU (as the two-stream ring kernel)
+  attn_plan(n_keys, Hkv, kvq ? 2 : attn_streams(act, hd), chunk, n_split);
+}
+
+template <int NCT>
+static void attn_q8_go(const AttnArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL((attn_q8_kernel<NCT>), dim3(a.n_split, a.Hkv), dim3(256), 0, st, a);
+}
+
 template <typename TA, int HD>
-static void attn_launch_t(const AttnArgs &a, hipStream_t st) {
-  constexpr int NS = attn_streams_t<TA, HD>();
-  if (a.n_split > 0) {
-    if (a.Hq / a.Hkv <= 4) attn_split_go<TA, HD, 1, NS>(a, st);
-    else attn_split_go<TA, HD, 2, NS>(a, st);
-  }
+static void attn_combine_go(const AttnArgs &a, hipStream_t st) {
   // splits 32 at a time when there are at most 32 (half the loads and broadcasts)
   if (a.n_split <= 32)
     hipLaunchKernelGGL((attn_combine_kernel<TA, HD, 32>), dim3(a.Hq * a.B), dim3(64), 0, st, a);
@@ -559,8 +837,26 @@ static void attn_launch_t(const AttnArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((attn_combine_kernel<TA, HD, 64>), dim3(a.Hq * a.B), dim3(64), 0, st, a);
 }
 
+template <typename TA, int HD>
+static void attn_launch_t(const AttnArgs &a, hipStream_t st) {
+  constexpr int NS = attn_streams_t<TA, HD>();
+  if (a.n_split > 0) {
+    if (a.Hq / a.Hkv <= 4) attn_split_go<TA, HD, 1, NS>(a, st);
+    else attn_split_go<TA, HD, 2, NS>(a, st);
+  }
+  attn_combine_go<TA, HD>(a, st);
+}
+
 hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st) {
-  if (act == ACT_F32) {
+  if (a.kvq) {   // bf16 activations, head_dim 128 (checked by the caller)
+    if (a.n_split > 0) {
+      const int nct = (a.Hq / a.Hkv * a.B + 15) / 16;
+      if (nct == 1) attn_q8_go<1>(a, st);
+      else if (nct == 2) attn_q8_go<2>(a, st);
+      else attn_q8_go<4>(a, st);
+    }
+    attn_combine_go<bf16, 128>(a, st);
+  } else if (act == ACT_F32) {
     if (a.hd == 64) attn_launch_t<float, 64>(a, st);
     else attn_launch_t<float, 128>(a, st);
   } else {

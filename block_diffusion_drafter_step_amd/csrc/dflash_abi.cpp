@@ -169,7 +169,7 @@ constexpr int64_t kMaxRows = (int64_t)1 << 26;
 size_t inject_ws(int32_t n_layers, int64_t n, int32_t d_t, int32_t d, int32_t kv, size_t *z_off = nullptr) {
   Carve c(nullptr);
   c.take(std::max(gemm_partial_bytes((int)n, d, n_layers * d_t), gemm_partial_bytes((int)n, 2 * kv, d)));
-  c.take((size_t)n * d * 4);  // y
+  c.take((size_t)n * std::max(d, 2 * kv) * 4);  // y, then the fp32 K | V rows of a Q8_0 cache
   if (z_off) *z_off = c.off;
   c.take((size_t)n * d * 4);  // z
   if (n >= kQ8ExpandMinM) {   // bf16 expansions of Q8_0 fc, Wk and Wv
@@ -224,9 +224,16 @@ size_t sel_ws(int32_t B, int32_t r, int32_t d) {
 
 dflash_status check_cache(const dflash_kv_cache *cache, int32_t act) {
   if (!cache) return fail(DFLASH_ERR_INVALID_ARG, "cache is NULL");
-  if (cache->dtype != act)
+  if (cache->dtype == DFLASH_Q8_0) {
+    if (act != DFLASH_BF16) return fail(DFLASH_ERR_INVALID_ARG, "a Q8_0 cache needs bf16 activations");
+    if (cache->head_dim != 128)
+      return fail(DFLASH_ERR_UNSUPPORTED, "a Q8_0 cache needs head_dim 128 (got %d)", cache->head_dim);
+    TRY(need_ptr(cache->k_scales, "cache.k_scales"));
+    TRY(need_ptr(cache->v_scales, "cache.v_scales"));
+  } else if (cache->dtype != act) {
     return fail(DFLASH_ERR_INVALID_ARG, "cache dtype %d does not match the activation type %d",
                 cache->dtype, act);
+  }
   if (cache->head_dim != 64 && cache->head_dim != 128)
     return fail(DFLASH_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", cache->head_dim);
   if (cache->n_kv_heads < 1) return fail(DFLASH_ERR_INVALID_ARG, "n_kv_heads must be >= 1");
@@ -351,7 +358,7 @@ dflash_status dflash_inject(const void *const *layer_hidden, int32_t n_layers, i
   const int n = (int)n_tokens;
   float *part = (float *)c.take(std::max(gemm_partial_bytes(n, (int)d, n_layers * d_t),
                                          gemm_partial_bytes(n, 2 * (int)kv, (int)d)));
-  float *y = (float *)c.take((size_t)n * d * 4);
+  float *y = (float *)c.take((size_t)n * std::max<int64_t>(d, 2 * kv) * 4);
   void *z = c.take((size_t)n * d * 4);
 
   // many rows: Q8_0 weights are expanded once to bf16 in the workspace
@@ -379,6 +386,15 @@ dflash_status dflash_inject(const void *const *layer_hidden, int32_t n_layers, i
   if (e != hipSuccess) return launched(e, "fc");
   e = launch_rmsnorm(act, y, n, (int)d, gamma, eps, z, st);
   if (e != hipSuccess) return launched(e, "rmsnorm");
+  if (cache->dtype == DFLASH_Q8_0) {
+    // fp32 K | V rows into y (free once z exists), then codes and scales
+    e = gemm(act, wkind_of(&wk_e), asrc1(z, (int)d), n, wset({&wk_e, &wv_e}), part, c.counters,
+             out_f32(y, 2 * kv), st);
+    if (e != hipSuccess) return launched(e, "wk/wv");
+    e = launch_kv_quant(y, n, cache->n_kv_heads, cache->head_dim, cache->capacity, pos0, cache->k, cache->v,
+                        cache->k_scales, cache->v_scales, st);
+    return launched(e, "kv quantisation");
+  }
   OutSpec oc;
   memset(&oc, 0, sizeof oc);
   oc.mode = OUT_CACHE;
@@ -439,6 +455,9 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   if (n_q_heads < 1 || n_q_heads % Hkv)
     return fail(DFLASH_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
   if (n_q_heads / Hkv > 8) return fail(DFLASH_ERR_UNSUPPORTED, "at most 8 query heads per KV head");
+  const int kvq = cache->dtype == DFLASH_Q8_0;
+  if (kvq && !attn_q8_ok(hd, n_q_heads / Hkv, B))
+    return fail(DFLASH_ERR_UNSUPPORTED, "a Q8_0 cache needs (query heads per KV head) x B <= 64");
   const int64_t qdim = (int64_t)n_q_heads * hd, kv = (int64_t)Hkv * hd;
   TRY(check_weight(wq, "wq", qdim, d, act, true));
   TRY(check_weight(wk, "wk", kv, d, act, true));
@@ -460,7 +479,7 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   void *qkv = c.take((size_t)B * nqkv * 4);
   AttnArgs a;
   memset(&a, 0, sizeof a);
-  attn_plan(n_ctx, Hkv, attn_streams(act, hd), &a.chunk, &a.n_split);
+  attn_plan_call(act, hd, n_q_heads / Hkv, B, kvq, n_ctx, Hkv, &a.chunk, &a.n_split);
   const int ns_max = attn_max_splits(n_ctx, Hkv);
   a.part_o = (float *)c.take((size_t)n_q_heads * B * ns_max * hd * 4);
   a.part_ml = (float *)c.take((size_t)n_q_heads * B * ns_max * 2 * 4);
@@ -472,6 +491,9 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   a.qkv = qkv;
   a.ck = cache->k;
   a.cv = cache->v;
+  a.cks = cache->k_scales;
+  a.cvs = cache->v_scales;
+  a.kvq = kvq;
   a.cap = cache->capacity;
   a.n_ctx = n_ctx;
   a.B = B;

@@ -99,6 +99,13 @@ hipError_t launch_expand_q8(const void *codes, const void *scales, long rows, in
 hipError_t launch_rmsnorm(int act, const float *y, int n, int d, const void *gamma, float eps,
                           void *z, hipStream_t st);
 
+// Q8_0 cache rows from fp32 K | V rows kv [n][2 * Hkv * hd] (K columns first):
+// per (row, head, 32-dim block) scale = fp16(max|x| / 127), codes
+// round-half-away(x / (max|x| / 127)); K codes [Hkv][cap][hd], V codes in
+// transposed 32-position panels, scales [Hkv][cap][hd / 32].
+hipError_t launch_kv_quant(const float *kv, int n, int Hkv, int hd, long cap, long pos0, void *ck,
+                           void *cv, void *cks, void *cvs, hipStream_t st);
+
 // ---- conv ------------------------------------------------------------------------
 // out[b][i][c] = sum_t (base[t][c] + delta[b*B + i][t*G + g(c)]) * x[b][i - t][c]
 hipError_t launch_conv(int act, const void *x, int n_blocks, int B, int C, int G, int T,
@@ -109,6 +116,9 @@ struct AttnArgs {
   const void *qkv;   // [B][Hq*hd + 2*Hkv*hd] in the act type: Q | Kb | Vb
   const void *ck;    // cache [Hkv][cap][hd]
   const void *cv;
+  const void *cks;   // Q8_0 cache: fp16 scales [Hkv][cap][hd/32] of K and V
+  const void *cvs;
+  int kvq;           // 1: the cache holds Q8_0 codes
   long cap;
   long n_ctx;
   int B, Hq, Hkv, hd;
@@ -122,6 +132,11 @@ struct AttnArgs {
 // keys per split workgroup and split count; `streams` from attn_streams()
 void attn_plan(long n_keys, int Hkv, int streams, int *chunk, int *n_split);
 int attn_streams(int act, int hd);
+// the plan of the split kernel launch_attention picks for these shapes
+void attn_plan_call(int act, int hd, int grp, int B, int kvq, long n_keys, int Hkv, int *chunk,
+                    int *n_split);
+// Q8_0 caches: head_dim 128 and at most 64 query rows (group x block)
+bool attn_q8_ok(int hd, int grp, int B);
 int attn_max_splits(long n_keys, int Hkv);
 hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st);
 

@@ -86,6 +86,72 @@ hipError_t launch_rmsnorm(int act, const float *y, int n, int d, const void *gam
 }
 
 // ---------------------------------------------------------------------------
+// Q8_0 KV-cache rows ("dflash: port #219 onto feature", DFlash Benchmark
+// Sweep: q8_0 K and V caches).  One thread per (row, K or V, head, block of 32
+// head dims): scale d = max|x| / 127 of the fp32 projection output, stored as
+// fp16; codes round-half-away(x / d) (x * (1 / d) in fp32), all 0 for a zero
+// block.  K codes land as 32 contiguous bytes of the key's row, V codes in
+// the transposed 32-position panels (one byte per dim row).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void kv_quant_kernel(const float *__restrict__ kv, int n, int Hkv,
+                                                       int hd, long cap, long pos0,
+                                                       int8_t *__restrict__ ck, int8_t *__restrict__ cv,
+                                                       _Float16 *__restrict__ cks,
+                                                       _Float16 *__restrict__ cvs) {
+  const int nb = hd >> 5, per_row = 2 * Hkv * nb;
+  const long id = (long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (long)n * per_row) return;
+  const int t = (int)(id / per_row);
+  const int r = (int)(id - (long)t * per_row);
+  const int isv = r / (Hkv * nb), hb = r - isv * Hkv * nb;
+  const int h = hb / nb, b = hb - h * nb;
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(kv + (long)t * 2 * Hkv * hd + (long)isv * Hkv * hd +
+                                                     (long)h * hd + 32 * b);
+  f32x4 x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = src[j];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(x[j][i]));
+  const float d = amax / 127.f;
+  const float inv = d != 0.f ? 1.f / d : 0.f;
+  int8_t q[32];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float c = fminf(fmaxf(roundf(x[j][i] * inv), -127.f), 127.f);
+      q[4 * j + i] = (int8_t)(int)c;
+    }
+  const long pos = pos0 + t;
+  const long srow = ((long)h * cap + pos) * nb + b;
+  if (!isv) {
+    uint4 w[2];
+    __builtin_memcpy(w, q, 32);
+    uint4 *dst = reinterpret_cast<uint4 *>(ck + ((long)h * cap + pos) * hd + 32 * b);
+    dst[0] = w[0];
+    dst[1] = w[1];
+    cks[srow] = (_Float16)d;
+  } else {
+    int8_t *panel = cv + ((long)h * (cap >> 5) + (pos >> 5)) * hd * 32 + (pos & 31);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) panel[(long)(32 * b + j) * 32] = q[j];
+    cvs[srow] = (_Float16)d;
+  }
+}
+
+hipError_t launch_kv_quant(const float *kv, int n, int Hkv, int hd, long cap, long pos0, void *ck,
+                           void *cv, void *cks, void *cvs, hipStream_t st) {
+  const long threads = (long)n * 2 * Hkv * (hd / 32);
+  hipLaunchKernelGGL(kv_quant_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, kv, n, Hkv,
+                     hd, cap, pos0, static_cast<int8_t *>(ck), static_cast<int8_t *>(cv),
+                     static_cast<_Float16 *>(cks), static_cast<_Float16 *>(cvs));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Grouped dynamic depthwise conv ("spec : add DFlash2 support", Overview):
 // out[i,c] = sum_t (base[t,c] + delta[i, t*G + g(c)]) * x[i-t, c], x[<0] = 0.
 // One thread per (block, 8 adjacent channels): it loads the block's B input

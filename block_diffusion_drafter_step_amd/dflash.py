@@ -40,7 +40,7 @@ class _Weight(ctypes.Structure):
 class _Cache(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("capacity", ctypes.c_int64), ("k", ctypes.c_void_p),
-                ("v", ctypes.c_void_p)]
+                ("v", ctypes.c_void_p), ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -124,14 +124,20 @@ class Weight:
 @dataclass
 class KVCache:
     """K [n_kv_heads][capacity][head_dim] and V in transposed 32-position
-    panels, [n_kv_heads][capacity/32][head_dim][32], in the activation type;
-    capacity is a multiple of 64.  `v_panels` / `v_rows` convert V between
-    [n_kv_heads][positions][head_dim] and the panel layout."""
+    panels, [n_kv_heads][capacity/32][head_dim][32]; capacity is a multiple of
+    64.  In the activation type, or Q8_0: int8 codes in those layouts plus
+    fp16 scales k_scales / v_scales [n_kv_heads][capacity][head_dim/32].
+    `v_panels` / `v_rows` convert V between [n_kv_heads][positions][head_dim]
+    and the panel layout."""
     k: torch.Tensor
     v: torch.Tensor
+    k_scales: Optional[torch.Tensor] = None
+    v_scales: Optional[torch.Tensor] = None
 
     @property
-    def act(self) -> str:
+    def dtype(self) -> str:
+        if self.k.dtype == torch.int8:
+            return "q8_0"
         return "f32" if self.k.dtype == torch.float32 else "bf16"
 
     def c(self) -> _Cache:
@@ -139,7 +145,12 @@ class KVCache:
         if tuple(self.v.shape) != (h, cap // 32, hd, 32):
             raise ValueError(f"V must be [n_kv_heads][capacity/32][head_dim][32] = "
                              f"{(h, cap // 32, hd, 32)}, got {tuple(self.v.shape)}")
-        return _Cache(_DT[self.act], h, hd, 0, cap, _ptr(self.k), _ptr(self.v))
+        if self.dtype == "q8_0":
+            for s in (self.k_scales, self.v_scales):
+                if s is None or s.dtype != torch.float16 or tuple(s.shape) != (h, cap, hd // 32):
+                    raise ValueError(f"Q8_0 scales must be fp16 [{h}][{cap}][{hd // 32}]")
+        return _Cache(_DT[self.dtype], h, hd, 0, cap, _ptr(self.k), _ptr(self.v), _ptr(self.k_scales),
+                      _ptr(self.v_scales))
 
 
 def v_panels(v_rows: torch.Tensor) -> torch.Tensor:

@@ -31,8 +31,15 @@ def act_dtype(act: str):
     return torch.bfloat16 if act == "bf16" else torch.float32
 
 
-def new_cache(cfg, device="cuda") -> D.KVCache:
-    """Zeroed cache: K [Hkv][cap][hd], V in transposed panels [Hkv][cap/32][hd][32]."""
+def new_cache(cfg, device="cuda", kv: str = None) -> D.KVCache:
+    """Zeroed cache: K [Hkv][cap][hd], V in transposed panels [Hkv][cap/32][hd][32],
+    in the activation type, or Q8_0 codes with fp16 scales [Hkv][cap][hd/32]
+    (kv="q8_0")."""
+    if kv == "q8_0":
+        return D.KVCache(torch.zeros((cfg.Hkv, cfg.cap, cfg.hd), dtype=torch.int8, device=device),
+                         torch.zeros((cfg.Hkv, cfg.cap // 32, cfg.hd, 32), dtype=torch.int8, device=device),
+                         torch.zeros((cfg.Hkv, cfg.cap, cfg.hd // 32), dtype=torch.float16, device=device),
+                         torch.zeros((cfg.Hkv, cfg.cap, cfg.hd // 32), dtype=torch.float16, device=device))
     dt = act_dtype(cfg.act)
     return D.KVCache(torch.zeros((cfg.Hkv, cfg.cap, cfg.hd), dtype=dt, device=device),
                      torch.zeros((cfg.Hkv, cfg.cap // 32, cfg.hd, 32), dtype=dt, device=device))

@@ -26,12 +26,12 @@ def fc_flops(n: int, fc_in: int, fc_out: int) -> int:
     return 2 * n * fc_in * fc_out
 
 
-def inject_bytes(cfg, n: int) -> int:
+def inject_bytes(cfg, n: int, kv: str = None) -> int:
     a = ACT_BYTES[cfg.act]
     return (n * cfg.L_t * cfg.d_t * a                      # features
             + weight_bytes(cfg.d, cfg.fc_in, cfg.weight)   # fc
             + 2 * weight_bytes(cfg.kv, cfg.d, cfg.weight)  # Wk, Wv
-            + 2 * n * cfg.kv * a)                          # cache rows written
+            + 2 * n * cfg.Hkv * kv_row_bytes(cfg, kv))     # cache rows written
 
 
 def conv_bytes(cfg, n_blocks: int = 1) -> int:
@@ -46,19 +46,27 @@ def attn_weight_bytes(cfg) -> int:
             + weight_bytes(cfg.d, cfg.qdim, cfg.weight))
 
 
-def attn_kv_bytes(cfg, n_ctx: int) -> int:
-    return 2 * cfg.Hkv * n_ctx * cfg.hd * ACT_BYTES[cfg.act]
+def kv_row_bytes(cfg, kv: str = None) -> int:
+    """Bytes of one cached position of one KV head, for K or for V: the act
+    type, or Q8_0 codes plus one fp16 scale per 32 dims."""
+    if kv == "q8_0":
+        return cfg.hd + (cfg.hd // 32) * 2
+    return cfg.hd * ACT_BYTES[cfg.act]
 
 
-def attn_bytes(cfg, n_ctx: int) -> int:
+def attn_kv_bytes(cfg, n_ctx: int, kv: str = None) -> int:
+    return 2 * cfg.Hkv * n_ctx * kv_row_bytes(cfg, kv)
+
+
+def attn_bytes(cfg, n_ctx: int, kv: str = None) -> int:
     a = ACT_BYTES[cfg.act]
-    return attn_weight_bytes(cfg) + attn_kv_bytes(cfg, n_ctx) + 3 * cfg.B * cfg.d * a
+    return attn_weight_bytes(cfg) + attn_kv_bytes(cfg, n_ctx, kv) + 3 * cfg.B * cfg.d * a
 
 
-def attn_core_bytes(cfg, n_ctx: int) -> int:
+def attn_core_bytes(cfg, n_ctx: int, kv: str = None) -> int:
     """What the attention kernels alone must move: KV plus Q in, O out."""
     a = ACT_BYTES[cfg.act]
-    return attn_kv_bytes(cfg, n_ctx) + 2 * cfg.B * cfg.qdim * a + 2 * cfg.B * cfg.kv * a
+    return attn_kv_bytes(cfg, n_ctx, kv) + 2 * cfg.B * cfg.qdim * a + 2 * cfg.B * cfg.kv * a
 
 
 def lmhead_bytes(cfg) -> int:
@@ -87,11 +95,11 @@ def selector_params_factorised(d: int, r: int) -> int:
     return 3 * d * r
 
 
-def step_bytes(cfg, n_ctx: int, inject_n: int = 0) -> int:
+def step_bytes(cfg, n_ctx: int, inject_n: int = 0, kv: str = None) -> int:
     """One block step (conv, attention over n_ctx context keys plus the block,
     LM head, selector, accept), plus an injection of inject_n rows when the
-    step injects."""
-    b = conv_bytes(cfg) + attn_bytes(cfg, n_ctx) + lmhead_bytes(cfg) + selector_bytes(cfg)
+    step injects; kv = "q8_0" for a Q8_0 KV cache."""
+    b = conv_bytes(cfg) + attn_bytes(cfg, n_ctx, kv) + lmhead_bytes(cfg) + selector_bytes(cfg)
     if inject_n:
-        b += inject_bytes(cfg, inject_n)
+        b += inject_bytes(cfg, inject_n, kv)
     return b

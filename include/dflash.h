@@ -92,21 +92,32 @@ typedef struct {
   const void *scales;
 } dflash_weight;
 
-/* The draft decoder's KV cache in the act type: K is [n_kv_heads][capacity]
- * [head_dim] (a key is one contiguous row); V is stored in transposed panels
- * of 32 positions, [n_kv_heads][capacity/32][head_dim][32]: element
- * (h, pos, j) of V sits at ((h*(capacity/32) + pos/32)*head_dim + j)*32 +
- * pos%32.  32 positions of K and of V^T are then each one contiguous block
- * for the attention's streaming loads.  head_dim is 64 or 128; capacity is a
- * multiple of 64. */
+/* The draft decoder's KV cache.  K is [n_kv_heads][capacity][head_dim] (a
+ * key is one contiguous row); V is stored in transposed panels of 32
+ * positions, [n_kv_heads][capacity/32][head_dim][32]: element (h, pos, j) of
+ * V sits at ((h*(capacity/32) + pos/32)*head_dim + j)*32 + pos%32.  32
+ * positions of K and of V^T are then each one contiguous block for the
+ * attention's streaming loads.  head_dim is 64 or 128; capacity is a
+ * multiple of 64.
+ * dtype is the act type, or DFLASH_Q8_0 with bf16 activations and head_dim
+ * 128 ("dflash: port #219 onto feature", DFlash Benchmark Sweep: the draft's
+ * K and V caches are q8_0): k and v then hold int8 codes in the same layouts,
+ * and k_scales / v_scales fp16 [n_kv_heads][capacity][head_dim/32], one scale
+ * per position and block of 32 consecutive head dims.  A row x (one position
+ * of one head, the projection's fp32 output) is stored per block as
+ * scale = fp16(max|x| / 127) and code = round-half-away(x / (max|x| / 127))
+ * (0 for an all-zero block); the attention reads bf16_rne(fp32(scale) *
+ * code).  k_scales / v_scales are NULL for other dtypes. */
 typedef struct {
-  int32_t dtype;  /* DFLASH_F32 or DFLASH_BF16 */
+  int32_t dtype;  /* DFLASH_F32, DFLASH_BF16 or DFLASH_Q8_0 */
   int32_t n_kv_heads;
   int32_t head_dim;
   int32_t reserved;
   int64_t capacity;
   void *k;
   void *v;
+  void *k_scales;
+  void *v_scales;
 } dflash_kv_cache;
 
 /* Limits checked by every call. */
@@ -126,6 +137,8 @@ typedef struct {
  *   cache.k[h][pos0 + t][j] = K[t][h*hd + j], t < n_tokens
  *   V[t][h*hd + j] -> cache.v at position pos0 + t, head h, dim j
  *                     (transposed 32-position panels, see above)
+ * A Q8_0 cache stores codes and scales of the fp32 K and V rows (not of
+ * their bf16 roundings), as dflash_kv_cache describes.
  * layer_hidden: HOST array of n_layers device pointers, each [n_tokens][d_t]
  * in `act`.  gamma: [d] in `act`, or NULL for ones.  Requires
  * 0 <= pos0 && pos0 + n_tokens <= capacity (else DFLASH_ERR_CAPACITY),

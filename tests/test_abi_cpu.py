@@ -239,3 +239,29 @@ def test_noalloc_topk_validates_before_any_device_call(lib):
     assert lib.dflash_topk_unary_noalloc(h, 17, 1, ctypes.byref(w), 8, idx, un, None) == 1
     assert lib.dflash_topk_unary_noalloc(None, 16, 1, ctypes.byref(w), 8, idx, un, None) == 1
 
+
+@no_gpu
+def test_q8_0_cache_validation(lib):
+    """A Q8_0 cache needs bf16 activations, head_dim 128 and both scale
+    arrays; the attention also needs group x block <= 64 query rows."""
+    hid = (ctypes.c_void_p * 1)(FAKE)
+    fc, wk = W(1, 512, 512), W(1, 1024, 512)
+    ok = D._Cache(2, 8, 128, 0, 4096, FAKE, FAKE, FAKE, FAKE)
+    ws_big = 1 << 40
+    st = lib.dflash_inject(hid, 1, 16, 512, 0, ctypes.byref(W(0, 512, 512)), None, 1e-6, ctypes.byref(W(0, 1024, 512)),
+                           ctypes.byref(W(0, 1024, 512)), ctypes.byref(ok), 0, FAKE, ws_big, None)
+    assert st == 1 and b"bf16" in lib.dflash_last_error()
+    hd64 = D._Cache(2, 8, 64, 0, 4096, FAKE, FAKE, FAKE, FAKE)
+    wk64 = W(1, 512, 512)
+    assert lib.dflash_inject(hid, 1, 16, 512, 1, ctypes.byref(fc), None, 1e-6, ctypes.byref(wk64), ctypes.byref(wk64),
+                             ctypes.byref(hd64), 0, FAKE, ws_big, None) == 2
+    noscale = D._Cache(2, 8, 128, 0, 4096, FAKE, FAKE, None, FAKE)
+    assert lib.dflash_inject(hid, 1, 16, 512, 1, ctypes.byref(fc), None, 1e-6, ctypes.byref(wk), ctypes.byref(wk),
+                             ctypes.byref(noscale), 0, FAKE, ws_big, None) == 1
+    assert b"k_scales" in lib.dflash_last_error()
+    # attention: 8 query heads per KV head x B = 16 is 128 query rows, more than the Q8_0 kernel carries
+    wq, wkv, wo = W(1, 128 * 64, 512), W(1, 1024, 512), W(1, 512, 128 * 64)
+    st = lib.dflash_block_attn(FAKE, None, 16, 512, 64, 1, ctypes.byref(wq), ctypes.byref(wkv), ctypes.byref(wkv),
+                               ctypes.byref(wo), ctypes.byref(ok), 100, 0.0, FAKE, FAKE, ws_big, None)
+    assert st == 2 and b"Q8_0" in lib.dflash_last_error()
+

@@ -389,6 +389,138 @@ def test_attn_deterministic():
 
 
 # ---------------------------------------------------------------------------
+# Q8_0 KV cache: the quantising injection and the attention over codes
+# ---------------------------------------------------------------------------
+
+def q8_fill(cache, k_rows, v_rows, p0=0):
+    """Oracle-quantised rows [Hkv][n][hd] (fp64) into a device Q8_0 cache at
+    positions [p0, p0 + n), p0 and n multiples of 32; returns the values the
+    attention must read (the oracle's dequantisation, reading R-KVQ)."""
+    kc, ks = O.kv_quant_q8_0(k_rows)
+    vc, vs = O.kv_quant_q8_0(v_rows)
+    n = k_rows.shape[1]
+    cache.k[:, p0:p0 + n] = torch.from_numpy(kc).cuda()
+    cache.v[:, p0 // 32:(p0 + n) // 32] = D.v_panels(torch.from_numpy(vc).cuda())
+    cache.k_scales[:, p0:p0 + n] = torch.from_numpy(ks).cuda()
+    cache.v_scales[:, p0:p0 + n] = torch.from_numpy(vs).cuda()
+    return O.kv_dequant_q8_0(kc, ks, True), O.kv_dequant_q8_0(vc, vs, True)
+
+
+def q8_rows(cache, pos):
+    """Codes and fp16 scales [Hkv][len(pos)][.] of K and V at positions `pos`."""
+    p = torch.as_tensor(np.asarray(pos), device="cuda")
+    return (cache.k[:, p].cpu().numpy(), cache.k_scales[:, p].cpu().numpy(),
+            D.v_rows(cache.v)[:, p].cpu().numpy(), cache.v_scales[:, p].cpu().numpy())
+
+
+def check_q8_rows(what, codes, scales, ref_codes, ref_scales):
+    """Codes within one level and scales within one fp16 step of the oracle's
+    quantisation of the same fp32 rows (the GPU forms 1 / scale and the
+    products in fp32, the oracle in fp64, so a value on a rounding boundary
+    may go either way); report how many are exactly equal."""
+    dc = np.abs(codes.astype(np.int32) - ref_codes.astype(np.int32))
+    sb = scales.view(np.int16).astype(np.int32) - ref_scales.view(np.int16).astype(np.int32)
+    assert dc.max() <= 1, (what, "codes", int(dc.max()))
+    assert np.abs(sb).max() <= 1, (what, "scales", int(np.abs(sb).max()))
+    say(f"  {what}: {int((dc == 0).sum())}/{dc.size} codes and {int((sb == 0).sum())}/{sb.size} scales equal "
+        f"to the oracle's, the rest one step off")
+
+
+def run_inject_q8(cfg, n, pos0, cache=None, hid=None, tag=None):
+    """Injection into a Q8_0 cache: the GPU's z against the oracle; the codes
+    and scales against the oracle's quantisation of z_gpu . Wk^T / Wv^T (the
+    unrounded projections).  Returns (cache, K values, V values) as the
+    attention reads them (the oracle's dequantisation of the GPU's codes)."""
+    say(f"inject q8_0 cache {cfg.name} n={n} pos0={pos0}")
+    w = synth.Workload(cfg)
+    if hid is None:
+        hid = [w.hidden(l, n, tag=tag or f"injq{n}") for l in range(cfg.L_t)]
+    fc, wk, wv = w.fc(), w.wk(), w.wv()
+    if cache is None:
+        cache = P.new_cache(cfg, kv="q8_0")
+    ws = D.workspace(D.dflash_inject_workspace(cfg.L_t, n, cfg.d_t, cfg.d, cfg.kv, cfg.act))
+    D.dflash_inject([dev(h, cfg.act) for h in hid], wdev(fc), None, cfg.eps, wdev(wk), wdev(wv), cache, pos0, ws)
+    torch.cuda.synchronize()
+    zoff = D.dflash_inject_z_offset(cfg.L_t, n, cfg.d_t, cfg.d, cfg.kv, cfg.act)
+    zg = f64(D.ws_view(ws, zoff, (n, cfg.d), P.act_dtype(cfg.act)))
+    enc = O.encode([act_np(h, cfg.act) for h in hid], wnp(fc), None, cfg.eps, True)
+    assert_close(zg, enc["z"], cfg.act, f"{cfg.name} z (Q8_0 cache)")
+    shp = lambda x: x.reshape(n, cfg.Hkv, cfg.hd).transpose(1, 0, 2)
+    rk, rks = O.kv_quant_q8_0(shp(zg @ wnp(wk).T))
+    rv, rvs = O.kv_quant_q8_0(shp(zg @ wnp(wv).T))
+    kc, ks, vc, vs = q8_rows(cache, pos0 + np.arange(n))
+    check_q8_rows(f"{cfg.name} K codes", kc, ks, rk, rks)
+    check_q8_rows(f"{cfg.name} V codes", vc, vs, rv, rvs)
+    return cache, O.kv_dequant_q8_0(kc, ks, True), O.kv_dequant_q8_0(vc, vs, True)
+
+
+@pytest.mark.parametrize("n,pos0", [(16, 40), (5, 0), (200, 77)])
+def test_inject_q8_0_cache(n, pos0):
+    """The quantising store: decode rows (16, ragged 5, and a 200-row tile
+    GEMM) at offsets inside and across V panels; positions around are
+    untouched."""
+    cfg = cfg_small(1, capacity=512)
+    cache = P.new_cache(cfg, kv="q8_0")
+    cache.k.fill_(3)
+    cache.k_scales.fill_(1.5)
+    run_inject_q8(cfg, n, pos0, cache=cache)
+    k = cache.k.cpu()
+    assert torch.all(k[:, :pos0] == 3) and torch.all(k[:, pos0 + n:] == 3)
+    assert torch.all(cache.k_scales[:, pos0 + n:].cpu().float() == 1.5)
+
+
+def run_attn_q8(cfg, n_ctx, poison=False, B=None):
+    """Attention over a Q8_0 cache of seeded N(0,1) rows quantised by the
+    oracle; stage-fed checks as for the bf16 cache, with the oracle reading
+    the dequantised codes.  poison: scales past n_ctx are NaN."""
+    B = cfg.B if B is None else B
+    cap = -(-(n_ctx + 64) // 64) * 64
+    say(f"attn q8_0 cache {cfg.name} B={B} n_ctx={n_ctx} cap={cap}")
+    w = synth.Workload(cfg)
+    shp = (cfg.Hkv, cap, cfg.hd)
+    kr = synth.normal(cfg.seed, f"attnq.ck.{cap}", shp, 1.0, "f32").astype(np.float64)
+    vr = synth.normal(cfg.seed, f"attnq.cv.{cap}", shp, 1.0, "f32").astype(np.float64)
+    cache = P.new_cache(configs.shrink(cfg, capacity=cap), kv="q8_0")
+    CK, CV = q8_fill(cache, kr, vr)
+    if poison:
+        cache.k_scales[:, n_ctx:] = float("nan")
+        cache.v_scales[:, n_ctx:] = float("nan")
+    u = synth.normal(cfg.seed, "attnq.u", (B, cfg.d), 1.0, cfg.act)
+    x = synth.normal(cfg.seed, "attnq.x", (B, cfg.d), 1.0, cfg.act)
+    wq, wk, wv, wo = w.wq(), w.wk(), w.wv(), w.wo()
+    dt = P.act_dtype(cfg.act)
+    out = torch.empty((B, cfg.d), dtype=dt, device="cuda")
+    args = (B, cfg.d, cfg.Hq, cfg.Hkv, cfg.hd, n_ctx)
+    ws = D.workspace(D.dflash_block_attn_workspace(*args))
+    D.dflash_block_attn(dev(u, cfg.act), dev(x, cfg.act), cfg.Hq, wdev(wq), wdev(wk), wdev(wv), wdev(wo), cache,
+                        n_ctx, 0.0, out, ws)
+    torch.cuda.synchronize()
+    qd, kv = cfg.Hq * cfg.hd, cfg.Hkv * cfg.hd
+    qkvg = f64(D.ws_view(ws, D.dflash_block_attn_qkv_offset(*args), (B, qd + 2 * kv), dt))
+    og = f64(D.ws_view(ws, D.dflash_block_attn_o_offset(*args), (B, qd), dt))
+    check_attn(cfg, act_np(u, cfg.act), act_np(x, cfg.act), wq, wk, wv, wo, CK, CV, n_ctx, 0.0, qkvg, og, f64(out),
+               f"{cfg.name} attn over a Q8_0 cache (n_ctx={n_ctx})", B)
+
+
+@pytest.mark.parametrize("ci,n_ctx", [(1, 1000), (1, 31), (1, 0), (1, 1), (2, 32768), (3, 65552), (4, 32768),
+                                      (4, 4133)])
+def test_attn_q8_0_cache(ci, n_ctx):
+    """Full-size contexts, ragged ends inside a panel, no or one context key;
+    the Q8_0-weight workload at B = 8 (two column tiles per wave)."""
+    run_attn_q8(configs.get(ci), n_ctx)
+
+
+@pytest.mark.parametrize("ci,n_ctx", [(1, 77), (4, 1000)])
+def test_attn_q8_0_cache_tail_not_finite(ci, n_ctx):
+    run_attn_q8(configs.get(ci), n_ctx, poison=True)
+
+
+def test_attn_q8_0_cache_small_groups():
+    """One column tile per wave: two query heads per KV head, B = 5."""
+    run_attn_q8(cfg_small(1, Hq=16, Hkv=8), 777, B=5)
+
+
+# ---------------------------------------------------------------------------
 # (4) LM head, top-K, unary
 # ---------------------------------------------------------------------------
 
@@ -653,46 +785,59 @@ def test_block_step_chain(ci):
     assert_close(gh, ref["attn"]["out"], cfg.act, f"{cfg.name} chain h end to end")
 
 
-def test_decode_64k_three_steps():
+@pytest.mark.parametrize("kv", ["bf16", "q8_0"])
+def test_decode_64k_three_steps(kv):
     """The 64k decode workload as a sequence: the cache holds 65536 seeded
     rows; step s injects 16 rows at 65536 + 16 s (half a V panel each, so the
     steps alternate between starting a panel and finishing it) and then
     attends 65536 + 16 (s + 1) context keys plus the block.  Each step's rows
     and output are checked; the oracle's cache takes the GPU's injected rows
-    once they have passed."""
+    once they have passed.  kv = q8_0: the same with a Q8_0 cache (seeded rows
+    quantised by the oracle, injected rows quantised by the library)."""
     cfg = configs.get(3)
     w = synth.Workload(cfg)
     n0, n = cfg.prefill_kv, cfg.inject_per_step
     shp = (cfg.Hkv, n0, cfg.hd)
-    ck0 = synth.normal(cfg.seed, "seq.ck", shp, 1.0, cfg.act)
-    cv0 = synth.normal(cfg.seed, "seq.cv", shp, 1.0, cfg.act)
-    cache = P.new_cache(cfg)
-    cache.k[:, :n0] = dev(ck0, cfg.act)
-    cache.v[:, :n0 // 32] = D.v_panels(dev(cv0, cfg.act))
     CK = np.zeros((cfg.Hkv, cfg.cap, cfg.hd))
     CV = np.zeros_like(CK)
-    CK[:, :n0] = act_np(ck0, cfg.act)
-    CV[:, :n0] = act_np(cv0, cfg.act)
-    del ck0, cv0
+    if kv == "q8_0":
+        cache = P.new_cache(cfg, kv="q8_0")
+        kr = synth.normal(cfg.seed, "seqq.ck", shp, 1.0, "f32").astype(np.float64)
+        vr = synth.normal(cfg.seed, "seqq.cv", shp, 1.0, "f32").astype(np.float64)
+        CK[:, :n0], CV[:, :n0] = q8_fill(cache, kr, vr)
+        del kr, vr
+    else:
+        ck0 = synth.normal(cfg.seed, "seq.ck", shp, 1.0, cfg.act)
+        cv0 = synth.normal(cfg.seed, "seq.cv", shp, 1.0, cfg.act)
+        cache = P.new_cache(cfg)
+        cache.k[:, :n0] = dev(ck0, cfg.act)
+        cache.v[:, :n0 // 32] = D.v_panels(dev(cv0, cfg.act))
+        CK[:, :n0] = act_np(ck0, cfg.act)
+        CV[:, :n0] = act_np(cv0, cfg.act)
+        del ck0, cv0
     wq, wk, wv, wo = w.wq(), w.wk(), w.wv(), w.wo()
     dt = P.act_dtype(cfg.act)
     for s in range(3):
         pos0 = n0 + n * s
         hid = [synth.normal(cfg.seed, f"seq.h{s}.{l}", (n, cfg.d_t), 1.0, cfg.act) for l in range(cfg.L_t)]
-        _, gk, gv = run_inject(cfg, n, pos0, cache=cache, hid=hid)
-        O.cache_write(CK, CV, gk, gv, pos0)
+        if kv == "q8_0":
+            _, kvals, vvals = run_inject_q8(cfg, n, pos0, cache=cache, hid=hid)
+            CK[:, pos0:pos0 + n], CV[:, pos0:pos0 + n] = kvals, vvals
+        else:
+            _, gk, gv = run_inject(cfg, n, pos0, cache=cache, hid=hid)
+            O.cache_write(CK, CV, gk, gv, pos0)
         n_ctx = pos0 + n
         u = synth.normal(cfg.seed, f"seq.u{s}", (cfg.B, cfg.d), 1.0, cfg.act)
         x = synth.normal(cfg.seed, f"seq.x{s}", (cfg.B, cfg.d), 1.0, cfg.act)
         out = torch.empty((cfg.B, cfg.d), dtype=dt, device="cuda")
         args = (cfg.B, cfg.d, cfg.Hq, cfg.Hkv, cfg.hd, n_ctx)
         ws = D.workspace(D.dflash_block_attn_workspace(*args))
-        say(f"attn step {s}: n_ctx={n_ctx}")
+        say(f"attn step {s}: n_ctx={n_ctx} ({kv} cache)")
         D.dflash_block_attn(dev(u, cfg.act), dev(x, cfg.act), cfg.Hq, wdev(wq), wdev(wk), wdev(wv), wdev(wo),
                             cache, n_ctx, 0.0, out, ws)
         torch.cuda.synchronize()
-        qd, kv = cfg.Hq * cfg.hd, cfg.Hkv * cfg.hd
-        qkvg = f64(D.ws_view(ws, D.dflash_block_attn_qkv_offset(*args), (cfg.B, qd + 2 * kv), dt))
+        qd, kvd = cfg.Hq * cfg.hd, cfg.Hkv * cfg.hd
+        qkvg = f64(D.ws_view(ws, D.dflash_block_attn_qkv_offset(*args), (cfg.B, qd + 2 * kvd), dt))
         og = f64(D.ws_view(ws, D.dflash_block_attn_o_offset(*args), (cfg.B, qd), dt))
         check_attn(cfg, act_np(u, cfg.act), act_np(x, cfg.act), wq, wk, wv, wo, CK, CV, n_ctx, 0.0, qkvg, og,
-                   f64(out), f"64k step {s} attn (n_ctx={n_ctx})", cfg.B)
+                   f64(out), f"64k step {s} attn (n_ctx={n_ctx}, {kv} cache)", cfg.B)
