@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--kv", default="act", choices=["act", "q8_0"],
+                    help="KV cache in the activation type or Q8_0 (codes + fp16 block scales)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU-baseline leg")
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true",
@@ -121,7 +123,9 @@ def main():
 
     host = synth.Workload(cfg)
     W = pipeline.DeviceWeights(host, drop_host=args.no_cpu or args.inject_sweep)
-    cache = pipeline.new_cache(cfg)
+    kvq = args.kv == "q8_0"
+    kvt = "q8_0" if kvq else None
+    cache = pipeline.new_cache(cfg, kv=kvt)
     if args.inject_sweep:
         print(json.dumps({"workload": cfg.name, "inject_sweep": inject_sweep(cfg, W, cache, randn)}),
               flush=True)
@@ -129,8 +133,16 @@ def main():
     prefill = None
     if decode64:
         # long-context decode: the cache already holds prefill_kv seeded rows
-        cache.k[:, :cfg.prefill_kv].copy_(randn(cfg.Hkv, cfg.prefill_kv, cfg.hd))
-        cache.v[:, :cfg.prefill_kv // 32].copy_(randn(cfg.Hkv, cfg.prefill_kv // 32, cfg.hd, 32))   # V panels
+        if kvq:   # codes uniform in [-127, 127], scales of N(0, 1) rows (max |x| ~ 3.5 over 32 values)
+            p = cfg.prefill_kv
+            for t in (cache.k[:, :p], cache.v[:, :p // 32]):
+                t.copy_(torch.randint(-127, 128, t.shape, generator=gen, device=dev, dtype=torch.int32)
+                        .to(torch.int8))
+            for t in (cache.k_scales[:, :p], cache.v_scales[:, :p]):
+                t.copy_((torch.rand(t.shape, generator=gen, device=dev) * 0.01 + 0.022).half())
+        else:
+            cache.k[:, :cfg.prefill_kv].copy_(randn(cfg.Hkv, cfg.prefill_kv, cfg.hd))
+            cache.v[:, :cfg.prefill_kv // 32].copy_(randn(cfg.Hkv, cfg.prefill_kv // 32, cfg.hd, 32))
         n_ctx0 = cfg.prefill_kv
     else:
         # prefill injection of n_ctx tokens (the MFMA-bound tile GEMM path)
@@ -170,46 +182,41 @@ def main():
             return n_ctx0 + inj_n * s, n_ctx0 + inj_n * (s + 1)
         return n_ctx0 - inj_n, n_ctx0
 
-    names = ["inject", "conv", "attn", "topk", "select", "accept"]
+    # the selector call also forms the accept length against the target tokens
+    names = ["inject", "conv", "attn", "topk", "select+accept"]
     calls = [lambda i: step.inject(hid16, positions(i)[0]),
              lambda i: step.conv(x),
              lambda i: step.attn(x, positions(i)[1]),
              lambda i: step.topk(),
-             lambda i: step.select(anchor),
-             lambda i: step.accept_len(target)]
+             lambda i: step.select(anchor, target)]
 
     for i in range(args.warmup):
         for c in calls:
             c(i)
     torch.cuda.synchronize()
 
-    # timed region: whole steps, wall clock between two device synchronisations;
-    # the LM-head call (the dominant kernel) is bracketed by HIP events on its
-    # stream every EVERY-th step (an event record leaves a gap of several
-    # microseconds in the queue, so bracketing every call of every step would
-    # distort the step)
+    # timed region: whole steps, wall clock between two device synchronisations
     K = args.steps
-    EVERY = 16
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range((K + EVERY - 1) // EVERY)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        calls[0](i)
-        calls[1](i)
-        calls[2](i)
-        if i % EVERY == 0:
-            ev[i // EVERY][0].record()
-            calls[3](i)
-            ev[i // EVERY][1].record()
-        else:
-            calls[3](i)
-        calls[4](i)
-        calls[5](i)
+        for c in calls:
+            c(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / K
     steps_s = K / (t1 - t0)
+
+    # the dominant kernel's launch duration: a pass of LM_CALLS LM-head calls
+    # after the timed region, each bracketed by HIP events on the stream it is
+    # launched on (the current stream)
+    LM_CALLS = 64
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(LM_CALLS)]
+    for e0, e1 in ev:
+        e0.record()
+        calls[3](0)
+        e1.record()
+    torch.cuda.synchronize()
     topk_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     # per-call breakdown: a separate pass after the timed region, events around every call
@@ -229,17 +236,17 @@ def main():
     if not args.no_extras:
         extras["conv_batched"] = conv_batched(cfg, W, randn)
         ctx_prof = int(np.mean([positions(i)[1] for i in range(20)]))
-        extras["kernels"] = kernel_profile(cfg, calls, ctx_prof)
+        extras["kernels"] = kernel_profile(cfg, calls, ctx_prof, kvt)
         extras["hbm_ceiling"] = stream_ceiling()
 
     if decode64:
         ctx_mean = float(np.mean([positions(i)[1] for i in range(cfg.steps)]))
     else:
         ctx_mean = n_ctx0
-    step_bytes = workmodel.step_bytes(cfg, int(ctx_mean), inject_n=inj_n)
+    step_bytes = workmodel.step_bytes(cfg, int(ctx_mean), inject_n=inj_n, kv=kvt)
     lm_bytes = workmodel.lmhead_bytes(cfg)
     lm_gbs = lm_bytes / (topk_ms * 1e-3) / 1e9
-    attn_bytes = workmodel.attn_bytes(cfg, int(ctx_mean))
+    attn_bytes = workmodel.attn_bytes(cfg, int(ctx_mean), kv=kvt)
     roofline = {"bound": "hbm", "kernel": "dflash_topk_unary (LM-head top-K kernel + topk_merge_kernel)",
                 "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_counters(cfg),
@@ -250,10 +257,12 @@ def main():
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16" if cfg.weight == "bf16" else "bf16 x q8_0",
            "data": "synthetic (seeded; random weights of the workload's shapes)",
-           "config": {"workload": f"{cfg.name}: decode step at {int(ctx_mean)}-row context",
+           "config": {"workload": f"{cfg.name}: decode step at {int(ctx_mean)}-row context"
+                                  + (", Q8_0 KV cache" if kvq else ""),
                       "B": cfg.B, "n_ctx": int(ctx_mean), "inject_per_step": inj_n, "d": cfg.d,
                       "L_t": cfg.L_t, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "hd": cfg.hd, "C": cfg.C, "G": cfg.G,
-                      "T": cfg.T, "V": cfg.V, "K": cfg.K, "r": cfg.r, "weights": cfg.weight},
+                      "T": cfg.T, "V": cfg.V, "K": cfg.K, "r": cfg.r, "weights": cfg.weight,
+                      "kv_cache": "q8_0" if kvq else cfg.act},
            "drafted_tok_per_s": round(steps_s * cfg.B, 1),
            "step_bytes": step_bytes,
            "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -266,7 +275,7 @@ def main():
     out.update(extras)
 
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(cfg, host, int(ctx_mean), inj_n)
+        out["cpu_baseline"] = cpu_baseline(cfg, host, int(ctx_mean), inj_n, kvq)
     print(json.dumps(out), flush=True)
 
 
@@ -380,7 +389,7 @@ def conv_batched(cfg, W, randn, tokens=32768, reps=20):
             "frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def kernel_profile(cfg, calls, n_ctx, steps=20):
+def kernel_profile(cfg, calls, n_ctx, kvt=None, steps=20):
     """Average device time of every kernel over `steps` whole steps, from a
     torch.profiler device trace (it records every dispatch of the process,
     libdflash's included), and the HBM fractions of the kernels it names:
@@ -410,10 +419,10 @@ def kernel_profile(cfg, calls, n_ctx, steps=20):
         return sum(v[1] for k, v in avg.items() if sub in k)
 
     out = {"steps": steps, "avg_us": {k[:90]: round(v[1], 2) for k, v in sorted(avg.items(), key=lambda kv: -kv[1][1] * kv[1][0])}}
-    split, comb = us("attn_split_kernel"), us("attn_combine_kernel")
+    split, comb = us("attn_split_kernel") + us("attn_q8_kernel"), us("attn_combine_kernel")
     lm, merge = us("lmhead_topk"), us("topk_merge_kernel")
     if split + comb > 0:
-        kv = workmodel.attn_kv_bytes(cfg, n_ctx)
+        kv = workmodel.attn_kv_bytes(cfg, n_ctx, kvt)
         out["attention_kv"] = {"n_ctx": n_ctx, "bytes": kv, "split_us": round(split, 2),
                                "combine_us": round(comb, 2),
                                "achieved": round(kv / ((split + comb) * 1e-6) / 1e9, 1),
@@ -451,10 +460,12 @@ def stream_ceiling(reps=10):
     return r
 
 
-def cpu_baseline(cfg, host, n_ctx, inj_n):
-    """The oracle (fp64 numpy, untuned) running one whole block step of the
-    same workload on the host cores: injection of 16 rows, conv, attention over
-    n_ctx + B keys, LM head over V, selector, accept."""
+def cpu_baseline(cfg, host, n_ctx, inj_n, kvq=False, reps=3):
+    """The oracle (fp64 numpy, untuned) running whole block steps of the same
+    workload on the host cores: injection of 16 rows, conv, attention over
+    n_ctx + B keys, LM head over V, selector, accept.  Each stage is timed
+    (median of `reps` steps), and the 32k prefill injection of the prefill
+    workloads is timed on 512 of its rows and extrapolated to all of them."""
     import numpy as np
     import threadpoolctl
 
@@ -466,32 +477,73 @@ def cpu_baseline(cfg, host, n_ctx, inj_n):
     a = lambda t: O.act_to_f64(t, cfg.act)
     bp = cfg.act == "bf16"
     # the context rows the step attends are drawn on the host (same distribution)
-    ck = a(synth.normal(cfg.seed, "cpu.ck", (cfg.Hkv, n_ctx, cfg.hd), 1.0, cfg.act))
-    cv = a(synth.normal(cfg.seed, "cpu.cv", (cfg.Hkv, n_ctx, cfg.hd), 1.0, cfg.act))
+    shp = (cfg.Hkv, n_ctx, cfg.hd)
+    if kvq:
+        ck = O.kv_dequant_q8_0(*O.kv_quant_q8_0(synth.normal(cfg.seed, "cpu.ck", shp, 1.0, "f32")), bp)
+        cv = O.kv_dequant_q8_0(*O.kv_quant_q8_0(synth.normal(cfg.seed, "cpu.cv", shp, 1.0, "f32")), bp)
+    else:
+        ck = a(synth.normal(cfg.seed, "cpu.ck", shp, 1.0, cfg.act))
+        cv = a(synth.normal(cfg.seed, "cpu.cv", shp, 1.0, cfg.act))
     hid = [a(synth.normal(cfg.seed, f"cpu.hid.{l}", (inj_n, cfg.d_t), 1.0, cfg.act)) for l in range(cfg.L_t)]
     x = a(host.x())[0]
     A, Bc = host.codebooks()
     A, Bc = a(A), a(Bc)
     anchor = int(host.anchor()[0])
+    fc, wk, wv, wq, wo = f(host.fc()), f(host.wk()), f(host.wv()), f(host.wq()), f(host.wo())
+    base, wd, P, wl = a(host.conv_base()), f(host.w_delta()), f(host.sel_proj()), host.w_lm()
     setup = time.perf_counter() - t_setup
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    t0 = time.perf_counter()
-    inj = O.inject(hid, f(host.fc()), None, cfg.eps, f(host.wk()), f(host.wv()), bp)
-    ck[:, n_ctx - inj_n:] = inj["k"].reshape(inj_n, cfg.Hkv, cfg.hd).transpose(1, 0, 2)
-    cv[:, n_ctx - inj_n:] = inj["v"].reshape(inj_n, cfg.Hkv, cfg.hd).transpose(1, 0, 2)
-    c = O.conv(x[None], a(host.conv_base()), f(host.w_delta()), cfg.G, bp)
-    at = O.block_attn(c["u"][0], x, f(host.wq()), f(host.wk()), f(host.wv()), f(host.wo()), ck, cv, n_ctx,
-                      cfg.Hq, 0.0, bp)
-    logits = O.lm_logits_stored(at["out"], host.w_lm())
-    tk = O.topk_unary_from_logits(logits, cfg.K)
-    sel = O.selector(at["out"], f(host.sel_proj()), A, Bc, tk["idx"], tk["unary"], anchor)
-    O.accept_len(sel["path"][None, :], sel["path"][None, :])
-    t = time.perf_counter() - t0
-    return {"value": round(1.0 / t, 5), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one whole oracle block step of the same workload ({t:.1f} s; fp64 numpy, "
-                      f"untuned; input staging {setup:.1f} s not counted)",
-            "affinity_cpus": len(os.sched_getaffinity(0))}
+    rows = lambda m: m.reshape(inj_n, cfg.Hkv, cfg.hd).transpose(1, 0, 2)
+
+    def one_step():
+        t = {}
+        t0 = time.perf_counter()
+        if kvq:   # the cache keeps codes of the unrounded projections
+            z = O.encode(hid, fc, None, cfg.eps, bp)["z"]
+            ck[:, n_ctx - inj_n:] = O.kv_dequant_q8_0(*O.kv_quant_q8_0(rows(z @ wk.T)), bp)
+            cv[:, n_ctx - inj_n:] = O.kv_dequant_q8_0(*O.kv_quant_q8_0(rows(z @ wv.T)), bp)
+        else:
+            inj = O.inject(hid, fc, None, cfg.eps, wk, wv, bp)
+            ck[:, n_ctx - inj_n:] = rows(inj["k"])
+            cv[:, n_ctx - inj_n:] = rows(inj["v"])
+        t["inject"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        c = O.conv(x[None], base, wd, cfg.G, bp)
+        t["conv"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        at = O.block_attn(c["u"][0], x, wq, wk, wv, wo, ck, cv, n_ctx, cfg.Hq, 0.0, bp)
+        t["attn"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        tk = O.topk_unary_from_logits(O.lm_logits_stored(at["out"], wl), cfg.K)
+        t["topk"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        sel = O.selector(at["out"], P, A, Bc, tk["idx"], tk["unary"], anchor)
+        t["select"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.accept_len(sel["path"][None, :], sel["path"][None, :])
+        t["accept"] = time.perf_counter() - t0
+        return t
+
+    runs = [one_step() for _ in range(reps)]
+    stages = {k: float(np.median([r[k] for r in runs])) for k in runs[0]}
+    step_s = float(np.median([sum(r.values()) for r in runs]))
+    out = {"value": round(1.0 / step_s, 5), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"median of {reps} whole oracle block steps of the same workload ({step_s:.2f} s each; "
+                     f"fp64 numpy, untuned; input staging {setup:.1f} s not counted)",
+           "stage_s": {k: round(v, 4) for k, v in stages.items()},
+           "affinity_cpus": len(os.sched_getaffinity(0))}
+    if cfg.n_ctx >= 4096 and not cfg.prefill_kv:
+        # the prefill injection on 512 seeded rows, extrapolated to n_ctx rows
+        m = 512
+        ph = [a(synth.normal(cfg.seed, f"cpu.pf.{l}", (m, cfg.d_t), 1.0, cfg.act)) for l in range(cfg.L_t)]
+        t0 = time.perf_counter()
+        O.inject(ph, fc, None, cfg.eps, wk, wv, bp)
+        tp = time.perf_counter() - t0
+        out["prefill_sample"] = {"rows": m, "s": round(tp, 3), "tokens": cfg.n_ctx,
+                                 "extrapolated_s": round(tp * cfg.n_ctx / m, 2),
+                                 "note": "extrapolated from 512 rows (rows are independent)"}
+    return out
 
 
 if __name__ == "__main__":

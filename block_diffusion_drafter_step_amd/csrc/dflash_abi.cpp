@@ -600,7 +600,8 @@ dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
                                     const dflash_weight *proj, const void *cb_pred,
                                     const void *cb_succ, int64_t V, const int32_t *idx,
                                     const float *unary, int32_t K, int32_t anchor, float *edges,
-                                    int32_t *path, void *ws, size_t ws_bytes, void *stream) {
+                                    int32_t *path, const int32_t *target, int32_t *accept, void *ws,
+                                    size_t ws_bytes, void *stream) {
   TRY(check_act(act));
   TRY(need_ptr(h, "h"));
   TRY(need_ptr(cb_pred, "cb_pred"));
@@ -609,6 +610,12 @@ dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
   TRY(need_ptr(unary, "unary"));
   TRY(need_ptr(edges, "edges"));
   TRY(need_ptr(path, "path"));
+  if ((target == nullptr) != (accept == nullptr))
+    return fail(DFLASH_ERR_INVALID_ARG, "target and accept must be both given or both NULL");
+  if (target) {
+    TRY(need_ptr(target, "target"));
+    TRY(need_ptr(accept, "accept"));
+  }
   if (B < 1 || B > DFLASH_MAX_BLOCK)
     return fail(DFLASH_ERR_INVALID_ARG, "B must be in [1, %d]", DFLASH_MAX_BLOCK);
   if (K < 1 || K > DFLASH_MAX_TOPK)
@@ -642,6 +649,8 @@ dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
   a.unary = unary;
   a.edges = edges;
   a.path = path;
+  a.target = target;
+  a.accept = accept;
   return launched(launch_selector(act, a, st), "selector");
 }
 

@@ -190,6 +190,8 @@ struct SelArgs {
   const float *unary;
   float *edges;       // [B][K][K]
   int *path;          // [B]
+  const int *target;  // [B] or null: accept = length of the prefix where path == target
+  int *accept;        // [1] or null
 };
 hipError_t launch_selector(int act, const SelArgs &a, hipStream_t st);
 

@@ -473,10 +473,13 @@ __global__ __launch_bounds__(256) void selector_path_kernel(SelArgs a) {
         best = score[fin][b];
         bsl = b;
       }
+    int acc = B;
     for (int i = B - 1; i >= 0; --i) {
       a.path[i] = sidx[i * K + bsl];
+      if (a.target && a.path[i] != a.target[i]) acc = i;
       if (i > 0) bsl = back[i * K + bsl];
     }
+    if (a.accept) a.accept[0] = acc;
   }
 }
 
@@ -617,14 +620,18 @@ __global__ __launch_bounds__(1024) void selector_fused_kernel(SelArgs a) {
     }
   }
   int b = __builtin_amdgcn_readfirstlane(bb);
+  const int tg = a.target && lane < B ? a.target[lane] : 0;   // target token of position `lane`
+  int acc = B;   // the first position where the path leaves the target
 #pragma unroll
   for (int i = kSelMaxB - 1; i >= 0; --i) {
     if (i < B) {
       const int id = __builtin_amdgcn_readlane(sidr[i], b);
       if (lane == 0) a.path[i] = id;
+      if (id != __builtin_amdgcn_readlane(tg, i)) acc = i;
       if (i > 0) b = __builtin_amdgcn_readlane(backr[i], b);
     }
   }
+  if (a.accept && lane == 0) a.accept[0] = acc;
 }
 
 static size_t selector_fused_lds(int act, const SelArgs &a) {

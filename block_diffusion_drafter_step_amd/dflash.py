@@ -63,8 +63,8 @@ _SIGS = {
     "dflash_topk_unary": ([_P, _I32, _I32, _PW, _I32, _P, _P, _P, _SZ, _P], _I32),
     "dflash_topk_unary_workspace": ([_I32, _I64, _I32], _SZ),
     "dflash_topk_unary_noalloc": ([_P, _I32, _I32, _PW, _I32, _P, _P, _P], _I32),
-    "dflash_selector_edges": ([_P, _I32, _I32, _PW, _P, _P, _I64, _P, _P, _I32, _I32, _P, _P, _P, _SZ,
-                               _P], _I32),
+    "dflash_selector_edges": ([_P, _I32, _I32, _PW, _P, _P, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P,
+                               _SZ, _P], _I32),
     "dflash_selector_edges_workspace": ([_I32, _I32, _I32, _I32], _SZ),
     "dflash_accept_len": ([_P, _P, _I32, _I32, _P, _P], _I32),
     "dflash_topk_rows": ([_P, _I64, _I64, _I32, _P, _P, _P, _SZ, _P], _I32),
@@ -298,14 +298,16 @@ def dflash_topk_unary_noalloc(h: torch.Tensor, lm_head: Weight, K: int, idx: tor
 
 def dflash_selector_edges(h: torch.Tensor, proj: Weight, cb_pred: torch.Tensor, cb_succ: torch.Tensor,
                           idx: torch.Tensor, unary: torch.Tensor, anchor: int, edges: torch.Tensor,
-                          path: torch.Tensor, ws: torch.Tensor, stream=None):
+                          path: torch.Tensor, ws: torch.Tensor, stream=None, target=None, accept=None):
+    """target int32 [B] / accept int32 [1] (both or neither): also the accept length."""
     B = h.shape[0]
     K = idx.shape[1]
     w = proj.c()
     wsp, wsb = _ws(ws)
     _check(load().dflash_selector_edges(_ptr(h), B, _act_of(h), ctypes.byref(w), _ptr(cb_pred),
                                         _ptr(cb_succ), cb_pred.shape[0], _ptr(idx), _ptr(unary), K, anchor,
-                                        _ptr(edges), _ptr(path), wsp, wsb, _stream(stream)))
+                                        _ptr(edges), _ptr(path), _ptr(target), _ptr(accept), wsp, wsb,
+                                        _stream(stream)))
 
 
 def dflash_accept_len(draft: torch.Tensor, target: torch.Tensor, accept: torch.Tensor, stream=None):

@@ -109,10 +109,14 @@ class BlockStep:
     def topk(self, stream=None):
         D.dflash_topk_unary(self.h, self.W.w_lm, self.cfg.K, self.idx, self.unary, self.ws, stream)
 
-    def select(self, anchor: int, stream=None):
+    def select(self, anchor: int, target=None, stream=None):
+        """Edges and path; with `target` ([1][B] int32) also the accept length,
+        in the selector's own kernel."""
         W = self.W
         D.dflash_selector_edges(self.h, W.sel_P, W.cb_pred, W.cb_succ, self.idx, self.unary, anchor,
-                                self.edges, self.path[0], self.ws, stream)
+                                self.edges, self.path[0], self.ws, stream,
+                                target=None if target is None else target[0], accept=
+                                None if target is None else self.accept)
 
     def accept_len(self, target, stream=None):
         D.dflash_accept_len(self.path, target, self.accept, stream)
@@ -123,5 +127,4 @@ class BlockStep:
         self.conv(x, stream)
         self.attn(x, n_ctx, stream)
         self.topk(stream)
-        self.select(anchor, stream)
-        self.accept_len(target, stream)
+        self.select(anchor, target, stream)

@@ -254,12 +254,16 @@ dflash_status dflash_topk_unary_noalloc(const void *h, int32_t B, int32_t act,
  * [B][K]; edges fp32 [B][K][K]; path int32 [B].  Requires
  * 1 <= B <= DFLASH_MAX_BLOCK, 1 <= K <= DFLASH_MAX_TOPK, r % 16 == 0,
  * r <= 256, -1 <= anchor < V, d % 64 == 0.  Indices in idx outside [0, V)
- * are clamped into range by the kernel (never read out of bounds). */
+ * are clamped into range by the kernel (never read out of bounds).
+ * target int32 [B] and accept int32 [1]: both NULL, or both given, and then
+ * accept[0] = the greedy accept length of path against target, as
+ * dflash_accept_len computes it for one sequence (in the same kernel). */
 dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
                                     const dflash_weight *proj, const void *cb_pred,
                                     const void *cb_succ, int64_t V, const int32_t *idx,
                                     const float *unary, int32_t K, int32_t anchor, float *edges,
-                                    int32_t *path, void *ws, size_t ws_bytes, void *stream);
+                                    int32_t *path, const int32_t *target, int32_t *accept, void *ws,
+                                    size_t ws_bytes, void *stream);
 size_t dflash_selector_edges_workspace(int32_t B, int32_t r, int32_t d, int32_t K);
 
 /* Row-wise top-K of a score matrix (a standalone form of the selection in

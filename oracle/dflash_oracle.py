@@ -285,14 +285,14 @@ def attn_qkv(u: np.ndarray, wq: np.ndarray, wk: np.ndarray, wv: np.ndarray,
 
 def attn_core(q: np.ndarray, kb: np.ndarray, vb: np.ndarray, cache_k: np.ndarray,
               cache_v: np.ndarray, n_ctx: int, n_q_heads: int, scale: float,
-              bf16_points: bool) -> dict:
+              bf16_points: bool, with_bound: bool = False) -> dict:
     """[P2] Overview / The Problem: each query head attends the injected
     context and the whole block, no mask (block diffusion drafts the block at
     once).  Head h uses KV head h // (Hq/Hkv) (R9); scale 1/sqrt(hd) unless
     given; O is rounded to bf16 in bf16 workloads (R-RP).
     q [B][Hq*hd], kb / vb [B][Hkv*hd]; cache [Hkv][capacity][hd], n_ctx rows.
-    "o_bound" is softmax_attend's bound for weights rounded to bf16 (the GPU's
-    P.V operands), zeros in fp32 workloads."""
+    "o_bound" (with_bound) is softmax_attend's bound for weights rounded to
+    bf16 (the GPU's P.V operands), zeros in fp32 workloads."""
     B = q.shape[0]
     hkv, cap, hd = cache_k.shape
     if n_q_heads % hkv or n_ctx > cap:
@@ -305,7 +305,7 @@ def attn_core(q: np.ndarray, kb: np.ndarray, vb: np.ndarray, cache_k: np.ndarray
     vb = vb.reshape(B, hkv, hd)
     o = np.zeros((B, n_q_heads, hd))
     ob = np.zeros_like(o)
-    u_w = U_BF16 if bf16_points else 0.0
+    u_w = U_BF16 if (bf16_points and with_bound) else 0.0
     for h in range(n_q_heads):
         g = h // grp
         keys = np.concatenate([cache_k[g, :n_ctx], kb[:, g]], axis=0)
@@ -338,8 +338,7 @@ def block_attn(u: np.ndarray, resid, wq: np.ndarray, wk: np.ndarray, wv: np.ndar
     p = attn_qkv(u, wq, wk, wv, bf16_points)
     c = attn_core(p["q"], p["kb"], p["vb"], cache_k, cache_v, n_ctx, n_q_heads, scale, bf16_points)
     out = attn_out(c["o"], wo, resid, bf16_points)
-    return {"q": p["q"], "kb": p["kb"], "vb": p["vb"], "o": c["o"], "o_bound": c["o_bound"],
-            "out": out}
+    return {"q": p["q"], "kb": p["kb"], "vb": p["vb"], "o": c["o"], "out": out}
 
 
 # ---------------------------------------------------------------------------

@@ -185,9 +185,9 @@ def test_topk_and_selector_rejections(lib):
                                  None) == 1
     P = W(1, 64, 256)
 
-    def sel(r=64, V=1000, K=8, anchor=3, B=16, P=P, wsb=1 << 30):
+    def sel(r=64, V=1000, K=8, anchor=3, B=16, P=P, wsb=1 << 30, target=None, accept=None):
         return lib.dflash_selector_edges(FAKE, B, 1, ref(P), FAKE, FAKE, V, FAKE, FAKE, K, anchor, FAKE, FAKE,
-                                         FAKE, wsb, None)
+                                         target, accept, FAKE, wsb, None)
 
     assert sel(P=W(1, 63, 256)) == 1
     assert sel(P=W(1, 512, 256)) == 1
@@ -196,6 +196,8 @@ def test_topk_and_selector_rejections(lib):
     assert sel(K=33) == 1
     assert sel(V=4) == 1
     assert sel(wsb=0) == 4
+    assert sel(target=FAKE) == 1          # target without accept
+    assert sel(accept=FAKE) == 1          # accept without target
     assert lib.dflash_accept_len(FAKE, FAKE, 0, 8, FAKE, None) == 1
     assert lib.dflash_accept_len(None, FAKE, 1, 8, FAKE, None) == 1
 

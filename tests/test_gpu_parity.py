@@ -290,7 +290,8 @@ def check_attn(cfg, U, X, wq, wk, wv, wo, CK, CV, n_ctx, scale, qkvg, og, outg, 
     assert_close(qkvg[:, :qd], p["q"], cfg.act, f"{what} Q")
     assert_close(qkvg[:, qd:qd + kv], p["kb"], cfg.act, f"{what} Kb")
     assert_close(qkvg[:, qd + kv:], p["vb"], cfg.act, f"{what} Vb")
-    c = O.attn_core(qkvg[:, :qd], qkvg[:, qd:qd + kv], qkvg[:, qd + kv:], CK, CV, n_ctx, cfg.Hq, scale, bp)
+    c = O.attn_core(qkvg[:, :qd], qkvg[:, qd:qd + kv], qkvg[:, qd + kv:], CK, CV, n_ctx, cfg.Hq, scale, bp,
+                    with_bound=True)
     assert_close(og, c["o"], cfg.act, f"{what} O from the GPU's Q, Kb, Vb",
                  term=c["o_bound"] if bp else None)
     assert_close(outg, O.attn_out(og, Wo, X, bp), cfg.act, f"{what} out from the GPU's O")
@@ -687,14 +688,19 @@ def run_selector(cfg, anchor=None, tag="sel", garbage_seed=None):
     ws = D.workspace(D.dflash_selector_edges_workspace(cfg.B, cfg.r, cfg.d, cfg.K))
     if garbage_seed is not None:
         garbage(ws, garbage_seed)
-    D.dflash_selector_edges(dev(h, cfg.act), wdev(Pw), dev(A, cfg.act), dev(Bc, cfg.act),
-                            torch.from_numpy(idx).cuda(), torch.from_numpy(un.astype(np.float32)).cuda(),
-                            anchor, edges, path, ws)
-    torch.cuda.synchronize()
     ref = O.selector(act_np(h, cfg.act), wnp(Pw), act_np(A, cfg.act), act_np(Bc, cfg.act), idx,
                      un.astype(np.float32).astype(np.float64), anchor)
+    # targets that agree with the oracle's path up to a seeded position: the
+    # accept length computed in the selector's kernel
+    tgt, m = synth.targets_with_mismatch(cfg.seed, tag + ".tgt", ref["path"][None, :], cfg.V)
+    acc = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    D.dflash_selector_edges(dev(h, cfg.act), wdev(Pw), dev(A, cfg.act), dev(Bc, cfg.act),
+                            torch.from_numpy(idx).cuda(), torch.from_numpy(un.astype(np.float32)).cuda(),
+                            anchor, edges, path, ws, target=torch.from_numpy(tgt[0]).cuda(), accept=acc)
+    torch.cuda.synchronize()
     gp = path.cpu().numpy()
     check_selector(ref, edges.cpu().numpy().astype(np.float64), gp, idx, cfg.name)
+    assert int(acc.cpu()[0]) == int(O.accept_len(gp[None, :], tgt)[0])
     return gp, ref
 
 
@@ -780,6 +786,7 @@ def test_block_step_chain(ci):
     sel = O.selector(gh, wnp(w.sel_proj()), a(A), a(Bc), gi, gu.astype(np.float64), anchor)
     gp = step.path.cpu().numpy()[0]
     check_selector(sel, step.edges.cpu().numpy().astype(np.float64), gp, gi, f"{cfg.name} chain selector")
+    # the accept length the selector's kernel formed against the targets
     assert int(step.accept.cpu()[0]) == int(O.accept_len(gp[None, :], tgt)[0])
     # end to end: the GPU's h against the oracle's own chain
     assert_close(gh, ref["attn"]["out"], cfg.act, f"{cfg.name} chain h end to end")
