@@ -795,12 +795,13 @@ int attn_max_splits(long n_keys, int Hkv) {
 }
 
 template <typename TA, int HD, int HPW, int NS>
-static void attn_split_go(const AttnArgs &a, hipStream_t st) {
+static hipError_t attn_split_go(const AttnArgs &a, hipStream_t st) {
   const size_t lds = (size_t)NS * kAttnStages * AttnCfg<TA, HD>::STAGE;
   auto *k = &attn_split_kernel<TA, HD, HPW, NS>;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3(a.n_split, a.Hkv), dim3(256 * NS), lds, st, a);
+  return hipSuccess;
 }
 
 // key streams per split workgroup: two when both rings fit the LDS (and the
@@ -838,13 +839,15 @@ static void attn_combine_go(const AttnArgs &a, hipStream_t st) {
 }
 
 template <typename TA, int HD>
-static void attn_launch_t(const AttnArgs &a, hipStream_t st) {
+static hipError_t attn_launch_t(const AttnArgs &a, hipStream_t st) {
   constexpr int NS = attn_streams_t<TA, HD>();
   if (a.n_split > 0) {
-    if (a.Hq / a.Hkv <= 4) attn_split_go<TA, HD, 1, NS>(a, st);
-    else attn_split_go<TA, HD, 2, NS>(a, st);
+    const hipError_t e = a.Hq / a.Hkv <= 4 ? attn_split_go<TA, HD, 1, NS>(a, st)
+                                           : attn_split_go<TA, HD, 2, NS>(a, st);
+    if (e != hipSuccess) return e;
   }
   attn_combine_go<TA, HD>(a, st);
+  return hipSuccess;
 }
 
 hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st) {
@@ -856,12 +859,11 @@ hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st) {
       else attn_q8_go<4>(a, st);
     }
     attn_combine_go<bf16, 128>(a, st);
-  } else if (act == ACT_F32) {
-    if (a.hd == 64) attn_launch_t<float, 64>(a, st);
-    else attn_launch_t<float, 128>(a, st);
   } else {
-    if (a.hd == 64) attn_launch_t<bf16, 64>(a, st);
-    else attn_launch_t<bf16, 128>(a, st);
+    hipError_t e;
+    if (act == ACT_F32) e = a.hd == 64 ? attn_launch_t<float, 64>(a, st) : attn_launch_t<float, 128>(a, st);
+    else e = a.hd == 64 ? attn_launch_t<bf16, 64>(a, st) : attn_launch_t<bf16, 128>(a, st);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }

@@ -119,6 +119,28 @@ __device__ __forceinline__ int pick(const int (&a)[N], int i) {
   return r;
 }
 
+// Completion counter of one group of workgroups: a 64-bit word (stamp << 16)
+// | count.  `stamp` is unique to the launch, so a word holding any other
+// stamp (left by an earlier launch, a call that never completed, or anything
+// else written there) counts as zero arrivals: the counters need no clearing,
+// in any order of calls.  An arrival first claims the word for its launch --
+// a compare-and-swap to (stamp << 16) | 0, tried only while the word still
+// holds another stamp, so it never undoes an arrival of this launch -- and
+// then counts itself with one fetch-and-add.  No arrival retries more than
+// once, however many workgroups finish together (a compare-and-swap loop on
+// the count serialises them at one agent-scope round trip each).  Returns
+// true for the n-th arrival of this launch.  Release on the add: this
+// workgroup's partials are visible before it is counted.
+__device__ __forceinline__ bool arrive_last(unsigned long long *c, unsigned long long stamp, int n) {
+  unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while ((old >> 16) != stamp &&
+         !__hip_atomic_compare_exchange_strong(c, &old, stamp << 16, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)) {
+  }
+  const unsigned long long prev = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  return (int)(prev & 0xffffu) + 1 == n;
+}
+
 // Cross-lane helpers over the 64-wide wave.
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 

@@ -15,6 +15,8 @@
 //    along K (the concatenated target-layer features are never materialised).
 #include <algorithm>
 #include <atomic>
+#include <chrono>
+#include <random>
 
 #include "common.h"
 #include "kernels.h"
@@ -96,21 +98,6 @@ __device__ __forceinline__ int seg_of(const WSet &W, int n, int *local) {
 // agent-scope acquire fence before a second barrier, so every partial
 // happens-before the loads that sum them (on gfx950: buffer_wbl2 sc1 before
 // each arrival, buffer_inv sc1 once per tile group, sc1 loads and stores).
-// Completion counter of one tile group: a 64-bit word (stamp << 16) | count.
-// `stamp` is unique to the launch, so a word holding any other stamp (left by
-// an earlier launch, a call that never completed, or anything else written
-// there) counts as zero arrivals: the counters need no clearing, in any
-// order of calls.  Returns true for the n-th arrival of this launch.  Release
-// on the CAS: this workgroup's partials are visible before it is counted.
-__device__ __forceinline__ bool arrive_last(unsigned long long *c, unsigned long long stamp, int n) {
-  unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), nw;
-  do {
-    nw = (old >> 16) == stamp ? old + 1 : ((stamp << 16) | 1ull);
-  } while (!__hip_atomic_compare_exchange_weak(c, &old, nw, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT));
-  return (int)(nw & 0xffffu) == n;
-}
-
 template <typename TA, int WK, int TPW, int WPG, bool SPLIT_TILES>
 __global__ __launch_bounds__(WPG * 64, WPG >= 8 ? WPG / 4 : 2) void skinny_gemm_kernel(
     ASrc X, int M, WSet W, int kchunk, float *__restrict__ part,
@@ -351,10 +338,27 @@ size_t skinny_partial_floats(int n_total, int K) {
   return most;
 }
 
-// launch stamps of the completion counters: 48 bits, never 0 (a zeroed
-// word then never matches), one per launch that uses counters
-static std::atomic<unsigned long long> g_stamp{0};
-static unsigned long long next_stamp() {
+hipError_t allow_dynamic_lds(const void *k, size_t bytes) {
+  hipFuncAttributes at;
+  hipError_t e = hipFuncGetAttributes(&at, k);
+  if (e != hipSuccess) return e;
+  if (at.sharedSizeBytes + bytes > kMaxLdsBytes) return hipErrorInvalidValue;
+  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// Launch stamps of the completion counters: 48 bits, never 0 (a zeroed word
+// then never matches), one per launch that uses counters.  The sequence
+// starts at a per-process random point, so a counter word that another
+// process left in reused device memory is as unlikely to carry a live stamp
+// as one left by this process.
+static unsigned long long stamp_seed() {
+  std::random_device rd;
+  const unsigned long long t =
+      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+  return (((unsigned long long)rd() << 32) ^ rd() ^ (t * 0x9E3779B97F4A7C15ull)) & 0xFFFFFFFFFFFFull;
+}
+static std::atomic<unsigned long long> g_stamp{stamp_seed()};
+unsigned long long next_launch_stamp() {
   unsigned long long s;
   do {
     s = (g_stamp.fetch_add(1, std::memory_order_relaxed) + 1) & 0xFFFFFFFFFFFFull;
@@ -381,7 +385,7 @@ static hipError_t skinny_launch_t(const ASrc &X, int M, const WSet &W, float *pa
                          p.kchunk, part, c, stamp, out);
   } else {
     c = p.groups <= kMaxCounters && p.kgroups < (1 << 16) ? cnt : nullptr;
-    if (c) stamp = next_stamp();
+    if (c) stamp = next_launch_stamp();
     if (p.wpg == 4)
       hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 1, 4, false>), grid, dim3(256), 0, st, X, M, W,
                          p.kchunk, part, c, stamp, out);
@@ -878,20 +882,21 @@ __global__ __launch_bounds__(512) void dma8_gemm_kernel(ASrc A, int M, WSet W, O
 }
 
 template <int OM, int TBM>
-static void dma8_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
+static hipError_t dma8_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
   const int mt = (M + TBM - 1) / TBM, nt = (W.n_total + DBN - 1) / DBN;
   const size_t lds = (size_t)D8STAGES * d8_stage_bytes<TBM>();
-  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma8_gemm_kernel<OM, TBM, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(&dma8_gemm_kernel<OM, TBM, false>), lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dma8_gemm_kernel<OM, TBM, false>), dim3(mt * nt), dim3(512), lds, st, A, M, W, out,
                      0, nullptr);
+  return hipSuccess;
 }
 
 template <int TBM>
-static void dma8_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
-  if (out.mode == OUT_F32) dma8_go<OUT_F32, TBM>(A, M, W, out, st);
-  else if (out.mode == OUT_ACT) dma8_go<OUT_ACT, TBM>(A, M, W, out, st);
-  else dma8_go<OUT_CACHE, TBM>(A, M, W, out, st);
+static hipError_t dma8_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, hipStream_t st) {
+  if (out.mode == OUT_F32) return dma8_go<OUT_F32, TBM>(A, M, W, out, st);
+  if (out.mode == OUT_ACT) return dma8_go<OUT_ACT, TBM>(A, M, W, out, st);
+  return dma8_go<OUT_CACHE, TBM>(A, M, W, out, st);
 }
 
 // k-split of the 128 x 256 direct-to-LDS tiles for products with few rows
@@ -910,30 +915,31 @@ static int dma8s_plan(int M, int N, int K, int *kc) {
 }
 
 template <int OM>
-static void dma8s_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part, int kc, int S,
-                     hipStream_t st) {
+static hipError_t dma8s_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part, int kc,
+                           int S, hipStream_t st) {
   const int mt = (M + 127) / 128, nt = (W.n_total + DBN - 1) / DBN;
   const size_t lds = (size_t)D8STAGES * d8_stage_bytes<128>();
-  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&dma8_gemm_kernel<OM, 128, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(&dma8_gemm_kernel<OM, 128, true>), lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dma8_gemm_kernel<OM, 128, true>), dim3(mt * nt, S), dim3(512), lds, st, A, M, W, out,
                      kc, part);
   const long mn = (long)M * W.n_total;
   hipLaunchKernelGGL((tile_reduce_kernel<bf16, OM>), dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st,
                      part, S, M, W.n_total, out);
+  return hipSuccess;
 }
 
 // bf16 products whose 128 x 256 tiles leave CUs idle: split k over the
-// direct-to-LDS kernel (true when launched)
+// direct-to-LDS kernel (true when taken; *err then holds the launch's error)
 static bool dma8_split_launch(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part,
-                              hipStream_t st) {
+                              hipStream_t st, hipError_t *err) {
   if (!part || W.K % 64 || A.k_per_src % 32) return false;
   int kc;
   const int S = dma8s_plan(M, W.n_total, W.K, &kc);
   if (S <= 1) return false;
-  if (out.mode == OUT_F32) dma8s_go<OUT_F32>(A, M, W, out, part, kc, S, st);
-  else if (out.mode == OUT_ACT) dma8s_go<OUT_ACT>(A, M, W, out, part, kc, S, st);
-  else dma8s_go<OUT_CACHE>(A, M, W, out, part, kc, S, st);
+  if (out.mode == OUT_F32) *err = dma8s_go<OUT_F32>(A, M, W, out, part, kc, S, st);
+  else if (out.mode == OUT_ACT) *err = dma8s_go<OUT_ACT>(A, M, W, out, part, kc, S, st);
+  else *err = dma8s_go<OUT_CACHE>(A, M, W, out, part, kc, S, st);
   return true;
 }
 
@@ -992,19 +998,20 @@ hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet
   // the last wave of 128 x 256 tiles less than three quarters full: split k
   const long tail = tiles128 % cus;
   const bool ragged = tail != 0 && tail * 4 < cus * 3;
+  hipError_t e = hipSuccess;
   if (act == ACT_F32)
     tile_launch_t<float, W_SAME>(A, M, W, out, part, st);
   else if (wkind == W_Q8_0)   // fewer rows than kQ8ExpandMinM: dequantised per tile
     tile_launch_t<bf16, W_Q8_0>(A, M, W, out, part, st);
-  else if (!big && (!half || ragged) && dma8_split_launch(A, M, W, out, part, st))
-    return hipGetLastError();
+  else if (!big && (!half || ragged) && dma8_split_launch(A, M, W, out, part, st, &e))
+    return e != hipSuccess ? e : hipGetLastError();
   else if (big)
-    dma8_launch<256>(A, M, W, out, st);
+    e = dma8_launch<256>(A, M, W, out, st);
   else if (half)
-    dma8_launch<128>(A, M, W, out, st);
+    e = dma8_launch<128>(A, M, W, out, st);
   else
     tile_launch_t<bf16, W_SAME>(A, M, W, out, part, st);
-  return hipGetLastError();
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace dfl

@@ -64,6 +64,8 @@ constexpr int kSkinnyMaxM = 16;
 // Completion counters at the start of every workspace: 64-bit words stamped
 // by the launch that uses them, so they need no initial value.
 constexpr int kMaxCounters = 8192;
+// stamp of the next launch that uses completion counters (48 bits, never 0)
+unsigned long long next_launch_stamp();
 constexpr size_t kCounterBytes = kMaxCounters * sizeof(unsigned long long);
 
 // Workspace floats of the split-K partials of a skinny GEMM.
@@ -152,9 +154,9 @@ struct TopkArgs {
   int n_waves;        // waves that own vocabulary tiles (<= 4 * n_wg)
   int lds_path;       // 1: h resident in LDS, one persistent workgroup per CU
   int lds_bytes;      // dynamic LDS of the resident path
-  float *part_val;    // [n_wg][16][K]
-  int *part_idx;      // [n_wg][16][K]
-  float *part_ms;     // [n_wg][16][2]
+  float *part_val;    // [16][K][n_wg]
+  int *part_idx;      // [16][K][n_wg]
+  float *part_ms;     // [16][2][n_wg]
   int *idx;           // [B][K]
   float *unary;       // [B][K]
 };
@@ -164,6 +166,10 @@ int topk_plan_wgs(long V, int wkind);
 size_t topk_lds_bytes(int B, int d, int act, int K);
 int topk_lds_waves();
 constexpr size_t kMaxLdsBytes = 160 * 1024;
+// Allows `bytes` of dynamic LDS for kernel `k`.  An error -- the kernel's
+// static LDS and `bytes` together over a CU's 160 KB, or the runtime's own --
+// means the kernel must not be launched.
+hipError_t allow_dynamic_lds(const void *k, size_t bytes);
 constexpr int kMaxCUs = 1024;
 int device_cu_count();
 int topk_plan_waves(long V, int wkind);

@@ -641,11 +641,12 @@ static size_t selector_fused_lds(int act, const SelArgs &a) {
 }
 
 template <typename TA, int KM>
-static void selector_fused_go(const SelArgs &a, size_t lds, hipStream_t st) {
+static hipError_t selector_fused_go(const SelArgs &a, size_t lds, hipStream_t st) {
   auto *k = &selector_fused_kernel<TA, KM>;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3(1), dim3(1024), lds, st, a);
+  return hipSuccess;
 }
 
 #ifndef DFL_SEL_FUSED
@@ -655,14 +656,12 @@ static void selector_fused_go(const SelArgs &a, size_t lds, hipStream_t st) {
 hipError_t launch_selector(int act, const SelArgs &a, hipStream_t st) {
   const size_t flds = selector_fused_lds(act, a);
   if (DFL_SEL_FUSED && flds <= kMaxLdsBytes) {
-    if (act == ACT_F32) {
-      if (a.K <= 8) selector_fused_go<float, 8>(a, flds, st);
-      else selector_fused_go<float, 32>(a, flds, st);
-    } else {
-      if (a.K <= 8) selector_fused_go<bf16, 8>(a, flds, st);
-      else selector_fused_go<bf16, 32>(a, flds, st);
-    }
-    return hipGetLastError();
+    hipError_t e;
+    if (act == ACT_F32)
+      e = a.K <= 8 ? selector_fused_go<float, 8>(a, flds, st) : selector_fused_go<float, 32>(a, flds, st);
+    else
+      e = a.K <= 8 ? selector_fused_go<bf16, 8>(a, flds, st) : selector_fused_go<bf16, 32>(a, flds, st);
+    return e != hipSuccess ? e : hipGetLastError();
   }
   const size_t lds = (size_t)2 * a.K * (a.r + 1) * sizeof(float);
   if (act == ACT_F32)

@@ -50,6 +50,13 @@ __device__ __forceinline__ void list_insert(float (&v)[KM], int (&ix)[KM], float
   }
 }
 
+// Partial lists of the workgroups, [token (16)][entry][workgroup]: values and
+// indices have K entries per token, the (max, sum) pairs 2.  Lanes of the
+// merges take consecutive workgroups, so their loads are coalesced.
+__device__ __forceinline__ long part_at(const TopkArgs &a, int tok, int entry, int per_tok, int wg) {
+  return ((long)tok * per_tok + entry) * a.n_wg + wg;
+}
+
 // Merge the 16 per-lane lists of each token in a workgroup (4 lane groups x
 // 4 waves) and write the workgroup's partial (top-K, max, sum of exp) per token.
 // Thread (token = tid / 16, list q = tid % 16) offers its list's head; a
@@ -78,10 +85,10 @@ __device__ __forceinline__ void wg_merge_write(const float (&tv)[KM], const int 
   float ps = ls[src] > 0.f ? ls[src] * exp2f((pm - M) * kL2e) : 0.f;
 #pragma unroll
   for (int o = 1; o < LQ; o <<= 1) ps += shfl_xor(ps, o);
-  const long ob = (long)blockIdx.x * 16 + tok;
+  const int wg = blockIdx.x;
   if (q == 0) {
-    a.part_ms[ob * 2] = M;
-    a.part_ms[ob * 2 + 1] = ps;
+    a.part_ms[part_at(a, tok, 0, 2, wg)] = M;
+    a.part_ms[part_at(a, tok, 1, 2, wg)] = ps;
   }
   int head = 0;
   for (int k = 0; k < a.K; ++k) {
@@ -101,8 +108,8 @@ __device__ __forceinline__ void wg_merge_write(const float (&tv)[KM], const int 
     }
     if (bq == q) ++head;
     if (q == 0) {
-      a.part_val[ob * a.K + k] = bv;
-      a.part_idx[ob * a.K + k] = bi;
+      a.part_val[part_at(a, tok, k, a.K, wg)] = bv;
+      a.part_idx[part_at(a, tok, k, a.K, wg)] = bi;
     }
   }
 }
@@ -454,23 +461,21 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkArgs a) {
   float m = -__builtin_inff(), s = 0.f;
   if (tid < a.n_wg) {
     // entries j >= K re-read entry K-1 (in bounds) and are dropped
-    const long ob = (long)tid * 16 + tok;
     float pv[KM];
     int pi[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
-      const long e = ob * K + min(j, K - 1);
+      const long e = part_at(a, tok, min(j, K - 1), K, tid);
       pv[j] = a.part_val[e];
       pi[j] = a.part_idx[e];
     }
-    m = a.part_ms[ob * 2];
-    s = a.part_ms[ob * 2 + 1];
+    m = a.part_ms[part_at(a, tok, 0, 2, tid)];
+    s = a.part_ms[part_at(a, tok, 1, 2, tid)];
 #pragma unroll
     for (int j = 0; j < KM; ++j) key[j] = j < K ? cand_key(pv[j], pi[j]) : 0ull;
   }
   for (int w = tid + 256; w < a.n_wg; w += 256) {
-    const long ob = (long)w * 16 + tok;
-    const float pm = a.part_ms[ob * 2], ps = a.part_ms[ob * 2 + 1];
+    const float pm = a.part_ms[part_at(a, tok, 0, 2, w)], ps = a.part_ms[part_at(a, tok, 1, 2, w)];
     if (ps > 0.f) {
       if (pm > m) {
         s = s * exp2f((m - pm) * kL2e);
@@ -479,7 +484,8 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkArgs a) {
       s += ps * exp2f((pm - m) * kL2e);
     }
     for (int j = 0; j < K; ++j) {
-      unsigned long long x = cand_key(a.part_val[ob * K + j], a.part_idx[ob * K + j]);
+      const long e = part_at(a, tok, j, K, w);
+      unsigned long long x = cand_key(a.part_val[e], a.part_idx[e]);
       if (x <= key[KM - 1]) break;   // the partial list is sorted: no later entry fits
 #pragma unroll
       for (int q = 0; q < KM; ++q) {   // insert, keeping key[] descending
@@ -580,31 +586,30 @@ static void topk_launch_tpw(const TopkArgs &a, hipStream_t st) {
 }
 
 template <typename TA, int WK, int KM>
-static void topk_launch_lds(const TopkArgs &a, hipStream_t st) {
+static hipError_t topk_launch_lds(const TopkArgs &a, hipStream_t st) {
   auto *kern = &lmhead_topk_lds_kernel<TA, WK, KM, DFL_LMH_WAVES>;
   // more than 64 KB of dynamic LDS has to be allowed explicitly
-  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes);
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kern), (size_t)a.lds_bytes);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(a.n_wg), dim3(DFL_LMH_WAVES * 64), (size_t)a.lds_bytes, st, a);
   hipLaunchKernelGGL((topk_merge_kernel<KM>), dim3(a.B), dim3(256), 0, st, a);
+  return hipSuccess;
 }
 
 template <typename TA, int WK>
-static void topk_launch_k(const TopkArgs &a, hipStream_t st) {
-  if (a.lds_path) {
-    if (a.K <= 8) topk_launch_lds<TA, WK, 8>(a, st);
-    else topk_launch_lds<TA, WK, 32>(a, st);
-  } else {
-    if (a.K <= 8) topk_launch_tpw<TA, WK, 8>(a, st);
-    else topk_launch_tpw<TA, WK, 32>(a, st);
-  }
+static hipError_t topk_launch_k(const TopkArgs &a, hipStream_t st) {
+  if (a.lds_path) return a.K <= 8 ? topk_launch_lds<TA, WK, 8>(a, st) : topk_launch_lds<TA, WK, 32>(a, st);
+  if (a.K <= 8) topk_launch_tpw<TA, WK, 8>(a, st);
+  else topk_launch_tpw<TA, WK, 32>(a, st);
+  return hipSuccess;
 }
 
 hipError_t launch_topk(int act, int wkind, const TopkArgs &a, hipStream_t st) {
-  if (act == ACT_F32) topk_launch_k<float, W_SAME>(a, st);
-  else if (wkind == W_Q8_0) topk_launch_k<bf16, W_Q8_0>(a, st);
-  else topk_launch_k<bf16, W_SAME>(a, st);
-  return hipGetLastError();
+  hipError_t e;
+  if (act == ACT_F32) e = topk_launch_k<float, W_SAME>(a, st);
+  else if (wkind == W_Q8_0) e = topk_launch_k<bf16, W_Q8_0>(a, st);
+  else e = topk_launch_k<bf16, W_SAME>(a, st);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 int device_cu_count() {
