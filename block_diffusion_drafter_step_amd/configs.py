@@ -14,6 +14,9 @@ Field names follow the pages' notation:
   Hq/Hkv query / key-value heads         hd    head dim
   C/G/T  conv channels / groups / taps   V     vocabulary
   K      top-K candidates per position   r     selector rank
+  d_ff   width of the feed-forward site's gated MLP (the pages give none:
+         17408 at d = 5120 and 21504 at d = 5376, widths of public model
+         families at those d; 512 in the tiny fp32 config)
 """
 from __future__ import annotations
 
@@ -40,6 +43,7 @@ class Config:
     V: int
     K: int
     r: int
+    d_ff: int = 0
     eps: float = 1e-6
     # long-context decode regime: rows of seeded K/V already in the cache,
     # tokens injected per step and number of steps
@@ -72,14 +76,14 @@ class Config:
 
 def _qwen27b(**kw) -> Config:
     base = dict(act="bf16", weight="bf16", d=5120, d_t=5120, L_t=5, B=16,
-                Hq=32, Hkv=8, hd=128, C=5120, G=64, T=4, V=151936, K=8, r=64)
+                Hq=32, Hkv=8, hd=128, C=5120, G=64, T=4, V=151936, K=8, r=64, d_ff=17408)
     base.update(kw)
     return Config(**base)
 
 
 CONFIGS: list[Config] = [
     Config(name="c0_tiny_fp32", seed=0, act="f32", weight="f32", d=256, d_t=256, L_t=2,
-           n_ctx=64, B=8, Hq=4, Hkv=2, hd=64, C=256, G=8, T=4, V=1024, K=4, r=16,
+           n_ctx=64, B=8, Hq=4, Hkv=2, hd=64, C=256, G=8, T=4, V=1024, K=4, r=16, d_ff=512,
            notes="tiny fp32 step; the oracle finishes it in well under a second"),
     _qwen27b(name="c1_qwen27b_1k", seed=1, n_ctx=1024,
              notes="one Qwen-27B-shaped draft layer, 1024 injected tokens"),
@@ -90,7 +94,7 @@ CONFIGS: list[Config] = [
              notes="cache pre-filled with 65536 seeded K/V rows; each step injects 16 rows, "
                    "then runs a block step; 64 steps"),
     Config(name="c4_q8_0_32k", seed=4, act="bf16", weight="q8_0", d=5376, d_t=5376, L_t=5,
-           n_ctx=32768, B=8, Hq=32, Hkv=8, hd=128, C=5376, G=64, T=4, V=262144, K=8, r=64,
+           n_ctx=32768, B=8, Hq=32, Hkv=8, hd=128, C=5376, G=64, T=4, V=262144, K=8, r=64, d_ff=21504,
            notes="Q8_0 fc / Wq / Wk / Wv / Wo / LM head, bf16 activations, 32768-token context"),
 ]
 

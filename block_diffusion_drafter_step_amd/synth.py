@@ -248,6 +248,32 @@ class Workload:
         return self._get("cb", lambda: (normal(c.seed, "cb_pred", (c.V, c.r), 0.25, c.act),
                                         normal(c.seed, "cb_succ", (c.V, c.r), 0.25, c.act)))
 
+    # --- feed-forward site (second conv pair and the gated MLP) --------------
+    def h_ffn(self, n_blocks: int = 1, tag: str = "ffn"):
+        c = self.cfg
+        nm = f"h.{tag}"
+        return self._get((nm, n_blocks), lambda: normal(c.seed, nm, (n_blocks, c.B, c.d), 1.0, c.act))
+
+    def ffn_conv_base(self):
+        c = self.cfg
+        return self._get("ffn_base", lambda: normal(c.seed, "ffn_conv_base", (c.T, c.d), 0.5, c.act))
+
+    def ffn_w_delta(self):
+        c = self.cfg
+        return self._get("ffn_wdelta", lambda: weight(c.seed, "ffn_w_delta", c.T * c.G, c.d, c.act))
+
+    def w_gate(self):
+        c = self.cfg
+        return self._get("wgate", lambda: weight(c.seed, "w_gate", c.d_ff, c.d, c.weight))
+
+    def w_up(self):
+        c = self.cfg
+        return self._get("wup", lambda: weight(c.seed, "w_up", c.d_ff, c.d, c.weight))
+
+    def w_down(self):
+        c = self.cfg
+        return self._get("wdown", lambda: weight(c.seed, "w_down", c.d, c.d_ff, c.weight))
+
     def anchor(self, n_seq: int = 1):
         c = self.cfg
         return integers(c.seed, "anchor", 0, c.V, (n_seq,))

@@ -631,6 +631,107 @@ def test_lm_logits_stored_matches_a_direct_matmul(kind):
 
 
 # --------------------------------------------------------------------------
+# feed-forward site (readings R16 - R18)
+# --------------------------------------------------------------------------
+
+def test_silu_is_x_times_the_logistic_function():
+    """SiLU against scipy's logistic function expit, including large |x|
+    where 1 + e^-x overflows; catches e^x for e^-x or a missing factor x."""
+    x = np.concatenate([randn(20000, scale=4.0), [-800.0, -50.0, -1e-300, 0.0, 1e-300, 50.0, 800.0]])
+    np.testing.assert_allclose(O.silu(x), x * scipy.special.expit(x), rtol=1e-14, atol=1e-300)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+
+
+def test_silu_odd_part_is_the_identity():
+    """silu(x) - silu(-x) = x (the logistic function satisfies s(x) + s(-x) = 1);
+    catches a sign error in the exponent."""
+    x = randn(5000, scale=6.0)
+    np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, rtol=1e-12, atol=1e-12)
+
+
+def _ffn_inputs(d=64, d_ff=96, G=8, T=4, nb=3, B=5):
+    return dict(h=randn(nb, B, d), base=randn(T, d, scale=0.7), w_delta=randn(T * G, d, scale=d ** -0.5),
+                G=G, w_gate=randn(d_ff, d, scale=d ** -0.5), w_up=randn(d_ff, d, scale=d ** -0.5),
+                w_down=randn(d, d_ff, scale=d_ff ** -0.5))
+
+
+@pytest.mark.parametrize("bf16_points", [False, True])
+def test_ffn_block_zero_down_projection_returns_the_input(bf16_points):
+    """Wd = 0 leaves the block output equal to its input exactly: the residual
+    is h itself (reading R18), not the conv output u, and nothing else is
+    added (a bf16 h is unchanged by rounding)."""
+    kw = _ffn_inputs()
+    h = O.round_bf16(kw["h"]) if bf16_points else kw["h"]
+    r = O.ffn_block(**dict(kw, h=h, w_down=np.zeros_like(kw["w_down"])), bf16_points=bf16_points)
+    np.testing.assert_array_equal(r["out"], h)
+
+
+def test_ffn_block_zero_conv_silences_the_mlp():
+    """base = 0 and W_delta = 0 make u = 0, so gate, up and act vanish and the
+    output is h: the MLP reads the conv output (R16), not h."""
+    kw = _ffn_inputs()
+    r = O.ffn_block(**dict(kw, base=np.zeros_like(kw["base"]), w_delta=np.zeros_like(kw["w_delta"])),
+                    bf16_points=False)
+    assert not np.any(r["u"]) and not np.any(r["act"])
+    np.testing.assert_array_equal(r["out"], kw["h"])
+
+
+def test_ffn_block_identity_weights_closed_form():
+    """base = e_0 with W_delta = 0 makes the conv the identity (R7), and with
+    d_ff = d, Wg = a I, Wu = I and Wd = I the block is elementwise:
+    out = h + w a h^2 expit(a h) (scipy's logistic function), Wd = diag(w).
+    Catches gate and up swapped (act would be a h^2 expit(h)) and a missing
+    SiLU; the permutation below catches a transposed down projection."""
+    d, a = 48, 1.7
+    kw = _ffn_inputs(d=d, d_ff=d)
+    h = kw["h"]
+    e0 = np.zeros_like(kw["base"])
+    e0[0] = 1.0
+    w = randn(d)
+    r = O.ffn_block(h=h, base=e0, w_delta=np.zeros_like(kw["w_delta"]), G=kw["G"], w_gate=a * np.eye(d),
+                    w_up=np.eye(d), w_down=np.diag(w), bf16_points=False)
+    np.testing.assert_allclose(r["out"], h + w * a * h ** 2 * scipy.special.expit(a * h), rtol=1e-12, atol=1e-12)
+    # a permutation as the down projection: act column j lands in output row perm[j]
+    perm = rng.permutation(d)
+    wd = np.zeros((d, d))
+    wd[perm, np.arange(d)] = 1.0
+    r2 = O.ffn_block(h=h, base=e0, w_delta=np.zeros_like(kw["w_delta"]), G=kw["G"], w_gate=a * np.eye(d),
+                     w_up=np.eye(d), w_down=wd, bf16_points=False)
+    ref = h.copy()
+    ref[..., perm] += (a * h ** 2 * scipy.special.expit(a * h))
+    np.testing.assert_allclose(r2["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_ffn_block_brute_force_tiny():
+    """One output element by explicit sums over the pages' conv formula and the
+    MLP, on a tiny case with dynamic taps (catches a wrong group, tap or
+    position in the feed-forward site's conv and any index slip in the MLP)."""
+    d, d_ff, G, T, B = 8, 6, 2, 3, 4
+    kw = _ffn_inputs(d=d, d_ff=d_ff, G=G, T=T, nb=1, B=B)
+    r = O.ffn_block(**kw, bf16_points=False)
+    h, base, wd_, wg, wu, wdn = (kw["h"][0], kw["base"], kw["w_delta"], kw["w_gate"], kw["w_up"], kw["w_down"])
+    cpg = d // G
+    u = np.zeros((B, d))
+    for i in range(B):
+        for c in range(d):
+            acc = 0.0
+            for t in range(T):
+                if i - t < 0:
+                    continue
+                delta = sum(h[i, k] * wd_[t * G + c // cpg, k] for k in range(d))
+                acc += (base[t, c] + delta) * h[i - t, c]
+            u[i, c] = acc
+    for i in range(B):
+        for c in range(d):
+            tot = h[i, c]
+            for j in range(d_ff):
+                g = sum(u[i, k] * wg[j, k] for k in range(d))
+                p = sum(u[i, k] * wu[j, k] for k in range(d))
+                tot += g / (1.0 + np.exp(-g)) * p * wdn[c, j]
+            assert abs(r["out"][0, i, c] - tot) <= 1e-12 * max(1.0, abs(tot))
+
+
+# --------------------------------------------------------------------------
 # generator
 # --------------------------------------------------------------------------
 
