@@ -235,6 +235,7 @@ def main():
     extras = {}
     if not args.no_extras:
         extras["conv_batched"] = conv_batched(cfg, W, randn)
+        extras["ffn_block"] = ffn_block_line(cfg, randn)
         ctx_prof = int(np.mean([positions(i)[1] for i in range(20)]))
         extras["kernels"] = kernel_profile(cfg, calls, ctx_prof, kvt)
         extras["hbm_ceiling"] = stream_ceiling()
@@ -385,6 +386,47 @@ def conv_batched(cfg, W, randn, tokens=32768, reps=20):
     del x, u, ws
     torch.cuda.empty_cache()
     return {"blocks": nb, "B": cfg.B, "us": round(t * 1e6, 1), "bytes": b,
+            "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def ffn_block_line(cfg, randn, reps=20):
+    """The feed-forward site (dflash_ffn_block: its conv pair, the gated SiLU
+    MLP and the residual) on one block of B rows, with random weights of the
+    workload's shapes (Q8_0 codes and scales for the quantised workload); HBM
+    bytes = h in, out, the conv pair and the three MLP weights over the call
+    time (HIP events on the current stream)."""
+    import torch
+    from block_diffusion_drafter_step_amd import dflash as D, workmodel
+    d, F = cfg.d, cfg.d_ff
+
+    def weight(rows, cols, dtype):
+        if dtype == "q8_0":
+            q = torch.randint(-127, 128, (rows, cols), dtype=torch.int8, device="cuda")
+            s = (torch.rand(rows, cols // 32, device="cuda") * 0.019 + 0.001).half()
+            return D.Weight("q8_0", q, s)
+        return D.Weight(dtype, randn(rows, cols) * cols ** -0.5)
+
+    h = randn(1, cfg.B, d)
+    out = torch.empty_like(h)
+    base = randn(cfg.T, d) * 0.7
+    wd = weight(cfg.T * cfg.G, d, cfg.act)
+    wg, wu, wn = weight(F, d, cfg.weight), weight(F, d, cfg.weight), weight(d, F, cfg.weight)
+    ws = D.workspace(D.dflash_ffn_block_workspace(1, cfg.B, d, cfg.G, cfg.T, F))
+    for _ in range(3):
+        D.dflash_ffn_block(h, cfg.G, base, wd, wg, wu, wn, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        D.dflash_ffn_block(h, cfg.G, base, wd, wg, wu, wn, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    b = workmodel.ffn_bytes(cfg, 1)
+    del wg, wu, wn, ws
+    torch.cuda.empty_cache()
+    return {"B": cfg.B, "d": d, "d_ff": F, "weights": cfg.weight, "us": round(t * 1e6, 1), "bytes": b,
             "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
 

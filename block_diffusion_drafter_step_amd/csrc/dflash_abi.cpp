@@ -188,6 +188,22 @@ size_t conv_ws(int32_t n_blocks, int32_t B, int32_t C, int32_t G, int32_t T) {
   return c.off;
 }
 
+// `u_off` / `act_off`, when given, receive the offsets of u and act
+size_t ffn_ws(int32_t n_blocks, int32_t B, int32_t d, int32_t G, int32_t T, int32_t d_ff,
+              size_t *u_off = nullptr, size_t *act_off = nullptr) {
+  Carve c(nullptr);
+  const int64_t M = (int64_t)n_blocks * B;
+  c.take(std::max(std::max(gemm_partial_bytes((int)M, T * G, d), gemm_partial_bytes((int)M, 2 * d_ff, d)),
+                  gemm_partial_bytes((int)M, d, d_ff)));
+  c.take((size_t)M * T * G * 4);       // delta
+  if (u_off) *u_off = c.off;
+  c.take((size_t)M * d * 4);           // u
+  c.take((size_t)M * 2 * d_ff * 4);    // gate | up, fp32
+  if (act_off) *act_off = c.off;
+  c.take((size_t)M * d_ff * 4);        // act
+  return c.off;
+}
+
 // `qkv_off` / `o_off`, when given, receive the offsets of Q | Kb | Vb and O
 size_t attn_ws(int32_t B, int32_t d, int32_t Hq, int32_t Hkv, int32_t hd, int64_t n_ctx,
                size_t *qkv_off = nullptr, size_t *o_off = nullptr) {
@@ -302,6 +318,33 @@ size_t dflash_block_attn_o_offset(int32_t B, int32_t d, int32_t n_q_heads, int32
 size_t dflash_conv_workspace(int32_t n_blocks, int32_t B, int32_t C, int32_t G, int32_t T) {
   if (n_blocks < 1 || B < 1 || C < 1 || G < 1 || T < 1) return 0;
   return conv_ws(n_blocks, B, C, G, T);
+}
+
+static bool ffn_args_ok(int32_t n_blocks, int32_t B, int32_t d, int32_t G, int32_t T, int32_t d_ff) {
+  return n_blocks >= 1 && B >= 1 && d >= 1 && G >= 1 && T >= 1 && d_ff >= 1 &&
+         (int64_t)n_blocks * B <= kMaxRows;
+}
+
+size_t dflash_ffn_block_workspace(int32_t n_blocks, int32_t B, int32_t d, int32_t G, int32_t T,
+                                  int32_t d_ff) {
+  if (!ffn_args_ok(n_blocks, B, d, G, T, d_ff)) return 0;
+  return ffn_ws(n_blocks, B, d, G, T, d_ff);
+}
+
+size_t dflash_ffn_block_u_offset(int32_t n_blocks, int32_t B, int32_t d, int32_t G, int32_t T,
+                                 int32_t d_ff) {
+  if (!ffn_args_ok(n_blocks, B, d, G, T, d_ff)) return 0;
+  size_t o = 0;
+  ffn_ws(n_blocks, B, d, G, T, d_ff, &o, nullptr);
+  return o;
+}
+
+size_t dflash_ffn_block_act_offset(int32_t n_blocks, int32_t B, int32_t d, int32_t G, int32_t T,
+                                   int32_t d_ff) {
+  if (!ffn_args_ok(n_blocks, B, d, G, T, d_ff)) return 0;
+  size_t o = 0;
+  ffn_ws(n_blocks, B, d, G, T, d_ff, nullptr, &o);
+  return o;
 }
 
 size_t dflash_block_attn_workspace(int32_t B, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
@@ -435,6 +478,57 @@ dflash_status dflash_conv(const void *x, int32_t n_blocks, int32_t B, int32_t C,
   if (e != hipSuccess) return launched(e, "delta");
   e = launch_conv(act, x, n_blocks, B, C, G, T, base, delta, out, st);
   return launched(e, "conv");
+}
+
+dflash_status dflash_ffn_block(const void *h, int32_t n_blocks, int32_t B, int32_t d, int32_t G,
+                               int32_t T, int32_t act, const void *base, const dflash_weight *w_delta,
+                               const dflash_weight *w_gate, const dflash_weight *w_up,
+                               const dflash_weight *w_down, void *out, void *ws, size_t ws_bytes,
+                               void *stream) {
+  TRY(check_act(act));
+  TRY(need_ptr(h, "h"));
+  TRY(need_ptr(base, "base"));
+  TRY(need_ptr(out, "out"));
+  if (out == h) return fail(DFLASH_ERR_INVALID_ARG, "out must not overlap h");
+  if (n_blocks < 1 || B < 1 || (int64_t)n_blocks * B > kMaxRows)
+    return fail(DFLASH_ERR_INVALID_ARG, "n_blocks and B must be >= 1");
+  if (B > DFLASH_MAX_BLOCK)
+    return fail(DFLASH_ERR_INVALID_ARG, "B must be in [1, %d]", DFLASH_MAX_BLOCK);
+  if (d < 64 || d % 64) return fail(DFLASH_ERR_INVALID_ARG, "d must be a positive multiple of 64");
+  if (G < 1 || d % G) return fail(DFLASH_ERR_INVALID_ARG, "G must divide d");
+  if (T < 1 || T > 16) return fail(DFLASH_ERR_INVALID_ARG, "T must be in [1, 16]");
+  TRY(check_weight(w_delta, "w_delta", (int64_t)T * G, d, act, false));
+  if (!w_gate) return fail(DFLASH_ERR_INVALID_ARG, "w_gate is NULL");
+  const int64_t d_ff = w_gate->rows;
+  if (d_ff < 64 || d_ff % 64 || d_ff > (1 << 20))
+    return fail(DFLASH_ERR_INVALID_ARG, "d_ff (w_gate rows) must be a positive multiple of 64, at most 2^20");
+  TRY(check_weight(w_gate, "w_gate", d_ff, d, act, true));
+  TRY(check_weight(w_up, "w_up", d_ff, d, act, true));
+  TRY(check_weight(w_down, "w_down", d, d_ff, act, true));
+  if (w_gate->dtype != w_up->dtype) return fail(DFLASH_ERR_UNSUPPORTED, "w_gate and w_up must share a dtype");
+  const size_t need = ffn_ws(n_blocks, B, d, G, T, (int)d_ff);
+  TRY(check_ws(ws, ws_bytes, need));
+
+  hipStream_t st = (hipStream_t)stream;
+  Carve c(ws);
+  const int M = n_blocks * B, F = (int)d_ff;
+  float *part = (float *)c.take(std::max(std::max(gemm_partial_bytes(M, T * G, d), gemm_partial_bytes(M, 2 * F, d)),
+                                         gemm_partial_bytes(M, d, F)));
+  float *delta = (float *)c.take((size_t)M * T * G * 4);
+  void *u = c.take((size_t)M * d * 4);
+  float *gu = (float *)c.take((size_t)M * 2 * F * 4);
+  void *av = c.take((size_t)M * F * 4);
+  // the feed-forward site's conv: the same kernels as dflash_conv
+  hipError_t e = gemm(act, W_SAME, asrc1(h, d), M, wset({w_delta}), part, c.counters, out_f32(delta, T * G), st);
+  if (e != hipSuccess) return launched(e, "ffn delta");
+  e = launch_conv(act, h, n_blocks, B, d, G, T, base, delta, u, st);
+  if (e != hipSuccess) return launched(e, "ffn conv");
+  e = gemm(act, wkind_of(w_gate), asrc1(u, d), M, wset({w_gate, w_up}), part, c.counters, out_f32(gu, 2 * F), st);
+  if (e != hipSuccess) return launched(e, "gate/up");
+  e = launch_silu_mul(act, gu, M, F, av, st);
+  if (e != hipSuccess) return launched(e, "silu");
+  e = gemm(act, wkind_of(w_down), asrc1(av, F), M, wset({w_down}), part, c.counters, out_act(out, d, h, d), st);
+  return launched(e, "down");
 }
 
 dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, int32_t d,

@@ -110,6 +110,9 @@ hipError_t launch_kv_quant(const float *kv, int n, int Hkv, int hd, long cap, lo
 
 // ---- conv ------------------------------------------------------------------------
 // out[b][i][c] = sum_t (base[t][c] + delta[b*B + i][t*G + g(c)]) * x[b][i - t][c]
+// act [M][F] = silu(gu[:, :F]) * gu[:, F:] in the act type, gu fp32 [M][2F],
+// F % 4 == 0.
+hipError_t launch_silu_mul(int act, const float *gu, long M, int F, void *out, hipStream_t st);
 hipError_t launch_conv(int act, const void *x, int n_blocks, int B, int C, int G, int T,
                        const void *base, const float *delta, void *out, hipStream_t st);
 

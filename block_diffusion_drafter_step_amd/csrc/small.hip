@@ -152,6 +152,37 @@ hipError_t launch_kv_quant(const float *kv, int n, int Hkv, int hd, long cap, lo
 }
 
 // ---------------------------------------------------------------------------
+// Gated MLP activation of the feed-forward site: act[m][j] = silu(g) * p with
+// g = gu[m][j], p = gu[m][F + j] (the stacked gate | up product, fp32),
+// SiLU(x) = x / (1 + e^-x), rounded once to the activation type.  One thread
+// per 4 adjacent j: two 16-byte loads, four outputs.
+// ---------------------------------------------------------------------------
+template <typename TA>
+__global__ __launch_bounds__(256) void silu_mul_kernel(const float *__restrict__ gu, long M, int F,
+                                                       TA *__restrict__ out) {
+  const long q = F / 4;
+  const long id = (long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= M * q) return;
+  const long m = id / q;
+  const int j = (int)(id - m * q) * 4;
+  const float *row = gu + m * 2 * (long)F;
+  const f32x4 g = *reinterpret_cast<const f32x4 *>(row + j);
+  const f32x4 p = *reinterpret_cast<const f32x4 *>(row + F + j);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[m * F + j + i] = from_f32<TA>(g[i] / (1.f + expf(-g[i])) * p[i]);
+}
+
+hipError_t launch_silu_mul(int act, const float *gu, long M, int F, void *out, hipStream_t st) {
+  const long threads = M * (F / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (act == ACT_F32)
+    hipLaunchKernelGGL((silu_mul_kernel<float>), grid, dim3(256), 0, st, gu, M, F, static_cast<float *>(out));
+  else
+    hipLaunchKernelGGL((silu_mul_kernel<bf16>), grid, dim3(256), 0, st, gu, M, F, static_cast<bf16 *>(out));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Grouped dynamic depthwise conv ("spec : add DFlash2 support", Overview):
 // out[i,c] = sum_t (base[t,c] + delta[i, t*G + g(c)]) * x[i-t, c], x[<0] = 0.
 // One thread per (block, 8 adjacent channels): it loads the block's B input

@@ -55,6 +55,11 @@ _SIGS = {
     "dflash_inject_z_offset": ([_I32, _I64, _I32, _I32, _I32, _I32], _SZ),
     "dflash_conv": ([_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _PW, _P, _P, _SZ, _P], _I32),
     "dflash_conv_workspace": ([_I32, _I32, _I32, _I32, _I32], _SZ),
+    "dflash_ffn_block": ([_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _PW, _PW, _PW, _PW, _P, _P, _SZ, _P],
+                         _I32),
+    "dflash_ffn_block_workspace": ([_I32, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "dflash_ffn_block_u_offset": ([_I32, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "dflash_ffn_block_act_offset": ([_I32, _I32, _I32, _I32, _I32, _I32], _SZ),
     "dflash_block_attn": ([_P, _P, _I32, _I32, _I32, _I32, _PW, _PW, _PW, _PW, _PC, _I64, _F32, _P, _P,
                            _SZ, _P], _I32),
     "dflash_block_attn_workspace": ([_I32, _I32, _I32, _I32, _I32, _I64], _SZ),
@@ -226,6 +231,18 @@ def dflash_conv_workspace(n_blocks, B, C, G, T) -> int:
     return load().dflash_conv_workspace(n_blocks, B, C, G, T)
 
 
+def dflash_ffn_block_workspace(n_blocks, B, d, G, T, d_ff) -> int:
+    return load().dflash_ffn_block_workspace(n_blocks, B, d, G, T, d_ff)
+
+
+def dflash_ffn_block_u_offset(n_blocks, B, d, G, T, d_ff) -> int:
+    return load().dflash_ffn_block_u_offset(n_blocks, B, d, G, T, d_ff)
+
+
+def dflash_ffn_block_act_offset(n_blocks, B, d, G, T, d_ff) -> int:
+    return load().dflash_ffn_block_act_offset(n_blocks, B, d, G, T, d_ff)
+
+
 def dflash_block_attn_workspace(B, d, n_q_heads, n_kv_heads, head_dim, n_ctx) -> int:
     return load().dflash_block_attn_workspace(B, d, n_q_heads, n_kv_heads, head_dim, n_ctx)
 
@@ -265,6 +282,18 @@ def dflash_conv(x: torch.Tensor, G: int, base: torch.Tensor, w_delta: Weight, ou
     wsp, wsb = _ws(ws)
     _check(load().dflash_conv(_ptr(x), nb, B, C, G, T, _act_of(x), _ptr(base), ctypes.byref(w), _ptr(out),
                               wsp, wsb, _stream(stream)))
+
+
+def dflash_ffn_block(h: torch.Tensor, G: int, base: torch.Tensor, w_delta: Weight, w_gate: Weight,
+                     w_up: Weight, w_down: Weight, out: torch.Tensor, ws: torch.Tensor, stream=None):
+    """The feed-forward site: h [n_blocks][B][d] -> out (same shape)."""
+    nb, B, d = h.shape
+    T = base.shape[0]
+    wd, wg, wu, wn = w_delta.c(), w_gate.c(), w_up.c(), w_down.c()
+    wsp, wsb = _ws(ws)
+    _check(load().dflash_ffn_block(_ptr(h), nb, B, d, G, T, _act_of(h), _ptr(base), ctypes.byref(wd),
+                                   ctypes.byref(wg), ctypes.byref(wu), ctypes.byref(wn), _ptr(out), wsp, wsb,
+                                   _stream(stream)))
 
 
 def dflash_block_attn(u: torch.Tensor, residual, n_q_heads: int, wq: Weight, wk: Weight, wv: Weight,

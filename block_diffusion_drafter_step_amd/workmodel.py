@@ -41,6 +41,15 @@ def conv_bytes(cfg, n_blocks: int = 1) -> int:
             + weight_bytes(cfg.T * cfg.G, cfg.C, cfg.act))  # W_delta
 
 
+def ffn_bytes(cfg, n_blocks: int = 1) -> int:
+    """The feed-forward site: h in, out, its conv pair and the gate, up and
+    down weights."""
+    a = ACT_BYTES[cfg.act]
+    return (2 * n_blocks * cfg.B * cfg.d * a
+            + cfg.T * cfg.d * a + weight_bytes(cfg.T * cfg.G, cfg.d, cfg.act)
+            + 2 * weight_bytes(cfg.d_ff, cfg.d, cfg.weight) + weight_bytes(cfg.d, cfg.d_ff, cfg.weight))
+
+
 def attn_weight_bytes(cfg) -> int:
     return (weight_bytes(cfg.qdim, cfg.d, cfg.weight) + 2 * weight_bytes(cfg.kv, cfg.d, cfg.weight)
             + weight_bytes(cfg.d, cfg.qdim, cfg.weight))

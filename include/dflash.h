@@ -12,7 +12,8 @@
  *     decoder's own KV cache, which the decoder reads when it drafts.
  *   "spec : add DFlash2 support (local convolution + candidate selector)",
  *     Overview: the grouped dynamic depthwise convolution and the candidate
- *     selector edge formula.
+ *     selector edge formula; review of tensor names: a conv pair at the
+ *     attention site and one at the feed-forward site of each layer.
  *   "dflash: pass missing NVFP4 scales to attention operations", Overview:
  *     every per-block weight scale of the injection K/V, the decoder Q/K/V and
  *     both output projections must be applied.
@@ -29,7 +30,8 @@
  * - Types.  Activations, the KV cache, the conv base, W_delta, the selector
  *   projection and codebooks are either all fp32 or all bf16 (the "act" type).
  *   With fp32 activations every weight is fp32; with bf16 activations the fc,
- *   Wq, Wk, Wv, Wo and LM-head weights are bf16 or Q8_0.  Arithmetic is fp32.
+ *   Wq, Wk, Wv, Wo, LM-head and feed-forward (gate, up, down) weights are bf16
+ *   or Q8_0.  Arithmetic is fp32.
  * - Q8_0.  Blocks of 32 int8 codes along the input dim share one fp16 scale:
  *   data is int8 [rows][cols], scales is fp16 [rows][cols/32].  The value a
  *   kernel multiplies with is bf16_rne(fp32(scale) * code), i.e. the weight
@@ -172,6 +174,35 @@ dflash_status dflash_conv(const void *x, int32_t n_blocks, int32_t B, int32_t C,
                           int32_t T, int32_t act, const void *base, const dflash_weight *w_delta,
                           void *out, void *ws, size_t ws_bytes, void *stream);
 size_t dflash_conv_workspace(int32_t n_blocks, int32_t B, int32_t C, int32_t G, int32_t T);
+
+/* (2b) DFlash2 feed-forward site.  "spec : add DFlash2 support", review of
+ * tensor names: each layer carries a second conv pair, ffn_conv_base /
+ * ffn_conv_proj, beside the attention site's.  The pages name the tensors
+ * only; this call takes the plainest reading of the site: the convolution of
+ * (2) on the feed-forward input h, then a gated SiLU MLP and the residual,
+ * with no biases and no norm:
+ *   u   = conv(h)                         (as dflash_conv, act type)
+ *   act = silu(u Wg^T) * (u Wu^T)         (products fp32, act in the act type)
+ *   out = h + act Wd^T                    (act type)
+ * silu(x) = x / (1 + e^-x).  h, out: [n_blocks][B][d] in `act`, not
+ * overlapping; base [T][d] in `act`; w_delta [T*G][d] in `act`; w_gate,
+ * w_up [d_ff][d] and w_down [d][d_ff] (bf16 / fp32 as `act`, or Q8_0 with
+ * bf16 activations; w_gate and w_up share a dtype).  Requires d % 64 == 0,
+ * d % G == 0, 1 <= T <= 16, 1 <= B <= DFLASH_MAX_BLOCK, d_ff % 64 == 0,
+ * d_ff <= 2^20. */
+dflash_status dflash_ffn_block(const void *h, int32_t n_blocks, int32_t B, int32_t d, int32_t G,
+                               int32_t T, int32_t act, const void *base, const dflash_weight *w_delta,
+                               const dflash_weight *w_gate, const dflash_weight *w_up,
+                               const dflash_weight *w_down, void *out, void *ws, size_t ws_bytes,
+                               void *stream);
+size_t dflash_ffn_block_workspace(int32_t n_blocks, int32_t B, int32_t d, int32_t G, int32_t T,
+                                  int32_t d_ff);
+/* Byte offsets into that workspace, for the same arguments, of u
+ * [n_blocks * B][d] and act [n_blocks * B][d_ff], both in `act`. */
+size_t dflash_ffn_block_u_offset(int32_t n_blocks, int32_t B, int32_t d, int32_t G, int32_t T,
+                                 int32_t d_ff);
+size_t dflash_ffn_block_act_offset(int32_t n_blocks, int32_t B, int32_t d, int32_t G, int32_t T,
+                                   int32_t d_ff);
 
 /* (3) Non-causal block attention with the injected context.
  * "Turbo dflash", Overview (block diffusion drafting) and The Problem (the

@@ -82,6 +82,15 @@ def test_intermediate_offsets_lie_inside_the_workspace(lib):
         assert 65536 <= q < o and q % 256 == 0 and o % 256 == 0
         assert q + 16 * 6144 * 2 <= o and o + 16 * 4096 * 2 <= ws
     assert lib.dflash_inject_z_offset(0, 16, 5120, 5120, 1024, 1) == 0
+    for nb in (1, 3, 2048):
+        ws = lib.dflash_ffn_block_workspace(nb, 16, 5120, 64, 4, 17408)
+        u = lib.dflash_ffn_block_u_offset(nb, 16, 5120, 64, 4, 17408)
+        a = lib.dflash_ffn_block_act_offset(nb, 16, 5120, 64, 4, 17408)
+        M = nb * 16
+        assert 65536 <= u < a and u % 256 == 0 and a % 256 == 0
+        assert u + M * 5120 * 2 <= a and a + M * 17408 * 2 <= ws
+    assert lib.dflash_ffn_block_workspace(0, 16, 5120, 64, 4, 17408) == 0
+    assert lib.dflash_ffn_block_act_offset(1, 16, 5120, 64, 4, 0) == 0
 
 
 FAKE = 0x10000        # aligned, never dereferenced: every case below is invalid
@@ -148,6 +157,37 @@ def test_conv_rejections(lib):
     assert call(w=W(1, 33, 256)) == 1
     assert call(w=W(2, 32, 256, scales=FAKE)) == 2            # W_delta cannot be Q8_0
     assert call(wsb=8) == 4
+
+
+@no_gpu
+def test_ffn_block_rejections(lib):
+    ref = ctypes.byref
+    wd, wg, wu, wn = W(1, 4 * 8, 256), W(1, 512, 256), W(1, 512, 256), W(1, 256, 512)
+
+    def call(h=FAKE, nb=1, B=8, d=256, G=8, T=4, act=1, wd=wd, wg=wg, wu=wu, wn=wn, out=FAKE + 4096,
+             ws=FAKE, wsb=1 << 30):
+        return lib.dflash_ffn_block(h, nb, B, d, G, T, act, FAKE, ref(wd), ref(wg), ref(wu), ref(wn), out,
+                                    ws, wsb, None)
+
+    assert call(act=5) == 1
+    assert call(h=None) == 1
+    assert call(out=FAKE) == 1 and "overlap" in err(lib)       # out == h
+    assert call(nb=0) == 1
+    assert call(B=17) == 1
+    assert call(d=200) == 1
+    assert call(G=7) == 1
+    assert call(T=17) == 1
+    assert call(wd=W(1, 33, 256)) == 1
+    assert call(wd=W(2, 32, 256, scales=FAKE)) == 2            # W_delta cannot be Q8_0
+    assert call(wg=W(1, 500, 256), wu=W(1, 500, 256), wn=W(1, 256, 500)) == 1 and "d_ff" in err(lib)
+    assert call(wu=W(1, 512, 128)) == 1                        # up's input width is not d
+    assert call(wn=W(1, 256, 448)) == 1                        # down's input width is not d_ff
+    assert call(wg=W(0, 512, 256)) == 1                        # fp32 weight with bf16 activations
+    assert call(wg=W(2, 512, 256, scales=FAKE)) == 2           # gate and up dtypes differ
+    assert call(wn=W(2, 256, 512, scales=None)) == 1           # Q8_0 without scales
+    assert call(act=0) == 1                                    # bf16 weights with fp32 activations
+    assert call(ws=None) == 4
+    assert call(wsb=64) == 4
 
 
 @no_gpu

@@ -274,6 +274,67 @@ def test_conv_garbage_workspace():
 
 
 # ---------------------------------------------------------------------------
+# (2b) feed-forward site: second conv pair, gated SiLU MLP, residual
+# ---------------------------------------------------------------------------
+
+def run_ffn(cfg, nb, tag="ffn", garbage_seed=None):
+    """Stage-wise: u against the oracle's conv of h; act against the oracle's
+    gated MLP of the GPU's u; out against the oracle's down product of the
+    GPU's act plus h.  End to end: out against the oracle chain (plus, for
+    bf16 workloads, |act_gpu - act_ref| |Wd|^T, the propagation of the
+    stage-checked act through the down product)."""
+    d, G, T, F = cfg.d, cfg.G, cfg.T, cfg.d_ff
+    say(f"ffn {cfg.name} n_blocks={nb} B={cfg.B} d={d} d_ff={F} G={G} T={T} weight={cfg.weight}")
+    w = synth.Workload(cfg)
+    h = synth.normal(cfg.seed, f"{tag}.h.{nb}", (nb, cfg.B, d), 1.0, cfg.act)
+    base, wd, wg, wu, wn = w.ffn_conv_base(), w.ffn_w_delta(), w.w_gate(), w.w_up(), w.w_down()
+    dt = P.act_dtype(cfg.act)
+    out = torch.empty((nb, cfg.B, d), dtype=dt, device="cuda")
+    args = (nb, cfg.B, d, G, T, F)
+    ws = D.workspace(D.dflash_ffn_block_workspace(*args))
+    if garbage_seed is not None:
+        garbage(ws, garbage_seed)
+    D.dflash_ffn_block(dev(h, cfg.act), G, dev(base, cfg.act), wdev(wd), wdev(wg), wdev(wu), wdev(wn), out, ws)
+    torch.cuda.synchronize()
+    M = nb * cfg.B
+    ug = f64(D.ws_view(ws, D.dflash_ffn_block_u_offset(*args), (M, d), dt))
+    ag = f64(D.ws_view(ws, D.dflash_ffn_block_act_offset(*args), (M, F), dt))
+    outg = f64(out).reshape(M, d)
+    bp = cfg.act == "bf16"
+    H = act_np(h, cfg.act)
+    Wg, Wu, Wn = wnp(wg), wnp(wu), wnp(wn)
+    c = O.conv(H, act_np(base, cfg.act), wnp(wd), G, bp)
+    assert_close(ug, c["u"].reshape(M, d), cfg.act, f"{cfg.name} ffn u (n_blocks={nb})")
+    f = O.ffn_hidden(ug, Wg, Wu, bp)
+    assert_close(ag, f["act"], cfg.act, f"{cfg.name} ffn act from the GPU's u")
+    H2 = H.reshape(M, d)
+    assert_close(outg, O.ffn_out(H2, ag, Wn, bp), cfg.act, f"{cfg.name} ffn out from the GPU's act")
+    ref = O.ffn_block(H, act_np(base, cfg.act), wnp(wd), G, Wg, Wu, Wn, bp)
+    term = np.abs(ag - ref["act"].reshape(M, F)) @ np.abs(Wn).T if bp else None
+    assert_close(outg, ref["out"].reshape(M, d), cfg.act, f"{cfg.name} ffn out end to end", term=term)
+
+
+@pytest.mark.parametrize("ci,nb", [(0, 1), (0, 3), (1, 1), (4, 1)])
+def test_ffn_block(ci, nb):
+    run_ffn(configs.get(ci), nb)
+
+
+def test_ffn_block_many_rows():
+    """1024 and 1040 rows (the tiled GEMMs, the second with a ragged tile) at
+    a narrower width, bf16 and Q8_0 weights; 600 fp32 rows."""
+    run_ffn(cfg_small(1, d=1024, C=1024, d_ff=2048), 64, tag="ffnm")
+    run_ffn(cfg_small(1, d=1024, C=1024, d_ff=2048, B=13), 80, tag="ffnr")
+    run_ffn(cfg_small(4, d=1024, C=1024, d_ff=1536), 50, tag="ffnq")
+    run_ffn(configs.get(0), 75, tag="ffnf")
+
+
+def test_ffn_block_odd_shapes_and_garbage_workspace():
+    """B = 5, T = 2, groups of 96 channels, d_ff = 64; random workspace bytes."""
+    run_ffn(cfg_small(1, d=384, C=384, G=4, T=2, B=5, d_ff=64), 2, tag="ffno", garbage_seed=11)
+    run_ffn(configs.get(0), 1, tag="ffng", garbage_seed=12)
+
+
+# ---------------------------------------------------------------------------
 # (3) block attention
 # ---------------------------------------------------------------------------
 
