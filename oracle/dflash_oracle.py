@@ -44,7 +44,8 @@ Readings where the pages are silent (each also listed in the design notes):
   R8 the conv runs on the block input before the Q/K/V projections.
   R9 attention scale 1/sqrt(hd), GQA kv_head = h // (Hq/Hkv), no mask over
      [context | block]; block K/V are not written to the cache.
-  R10 h_out = x + O . Wo^T; no FFN, no final norm; logit scale 1, no softcap.
+  R10 h_out = x + O . Wo^T; no FFN inside the block step (the feed-forward
+      site is its own call, R19 - R21), no final norm; logit scale 1, no softcap.
   R11 top-K in descending logit order, equal logits -> lower vocab index;
       unary = logit - logsumexp(all logits).
   R12 predecessors of position 0: the anchor token only (anchor -1: none).
@@ -53,12 +54,12 @@ Readings where the pages are silent (each also listed in the design notes):
   R-Q8 Q8_0 weight value = bf16_rne(fp32(scale) * q).
   R-RP in bf16 workloads the values the GPU stores as bf16 are rounded to
        bf16 here too: z, the cache rows, conv output u, Q/Kb/Vb, O and h_out.
-  R16 the DFlash2 layer's second conv pair (ffn_conv_base / ffn_conv_proj)
+  R19 the DFlash2 layer's second conv pair (ffn_conv_base / ffn_conv_proj)
       runs the same grouped dynamic conv on the feed-forward block's input,
       which is the attention block's output h_out.
-  R17 the feed-forward block is a gated MLP with SiLU on the gate, no
+  R20 the feed-forward block is a gated MLP with SiLU on the gate, no
       biases: act = silu(u Wg^T) * (u Wu^T), SiLU(x) = x / (1 + e^-x).
-  R18 it adds its output to its input (residual); no norm is applied
+  R21 it adds its output to its input (residual); no norm is applied
       (the pages name none).  In bf16 workloads u, act and the block output
       are rounded to bf16 (R-RP); the gate and up products are not.
   R-KVQ a Q8_0 KV cache holds, per (KV head, position), blocks of 32 along
@@ -531,30 +532,30 @@ def accept_len(draft: np.ndarray, target: np.ndarray) -> np.ndarray:
 
 
 def silu(x: np.ndarray) -> np.ndarray:
-    """R17: SiLU(x) = x / (1 + e^-x), the gate activation."""
+    """R20: SiLU(x) = x / (1 + e^-x), the gate activation."""
     x = np.asarray(x, dtype=np.float64)
     with np.errstate(over="ignore"):
         return x / (1.0 + np.exp(-x))
 
 
 def ffn_hidden(u: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, bf16_points: bool) -> dict:
-    """R17: gate = u Wg^T and up = u Wu^T (no rounding point), then
-    act = silu(gate) * up (R18: bf16 in bf16 workloads)."""
+    """R20: gate = u Wg^T and up = u Wu^T (no rounding point), then
+    act = silu(gate) * up (R21: bf16 in bf16 workloads)."""
     g = u @ w_gate.T
     p = u @ w_up.T
     return {"gate": g, "up": p, "act": _rp(silu(g) * p, bf16_points)}
 
 
 def ffn_out(h: np.ndarray, act: np.ndarray, w_down: np.ndarray, bf16_points: bool) -> np.ndarray:
-    """R18: out = h + act Wd^T (bf16 in bf16 workloads)."""
+    """R21: out = h + act Wd^T (bf16 in bf16 workloads)."""
     return _rp(h + act @ w_down.T, bf16_points)
 
 
 def ffn_block(h: np.ndarray, base: np.ndarray, w_delta: np.ndarray, G: int, w_gate: np.ndarray,
               w_up: np.ndarray, w_down: np.ndarray, bf16_points: bool) -> dict:
     """[P3] review of tensor names: besides the attention site's conv pair a
-    layer holds ffn_conv_base / ffn_conv_proj.  R16: that conv runs on the
-    feed-forward input h [n_blocks][B][d]; R17: the gated MLP follows; R18:
+    layer holds ffn_conv_base / ffn_conv_proj.  R19: that conv runs on the
+    feed-forward input h [n_blocks][B][d]; R20: the gated MLP follows; R21:
     with the residual.  u = conv(h); act = silu(u Wg^T) * (u Wu^T);
     out = h + act Wd^T."""
     c = conv(h, base, w_delta, G, bf16_points)

@@ -631,7 +631,7 @@ def test_lm_logits_stored_matches_a_direct_matmul(kind):
 
 
 # --------------------------------------------------------------------------
-# feed-forward site (readings R16 - R18)
+# feed-forward site (readings R19 - R21)
 # --------------------------------------------------------------------------
 
 def test_silu_is_x_times_the_logistic_function():
@@ -658,7 +658,7 @@ def _ffn_inputs(d=64, d_ff=96, G=8, T=4, nb=3, B=5):
 @pytest.mark.parametrize("bf16_points", [False, True])
 def test_ffn_block_zero_down_projection_returns_the_input(bf16_points):
     """Wd = 0 leaves the block output equal to its input exactly: the residual
-    is h itself (reading R18), not the conv output u, and nothing else is
+    is h itself (reading R21), not the conv output u, and nothing else is
     added (a bf16 h is unchanged by rounding)."""
     kw = _ffn_inputs()
     h = O.round_bf16(kw["h"]) if bf16_points else kw["h"]
@@ -668,7 +668,7 @@ def test_ffn_block_zero_down_projection_returns_the_input(bf16_points):
 
 def test_ffn_block_zero_conv_silences_the_mlp():
     """base = 0 and W_delta = 0 make u = 0, so gate, up and act vanish and the
-    output is h: the MLP reads the conv output (R16), not h."""
+    output is h: the MLP reads the conv output (R19), not h."""
     kw = _ffn_inputs()
     r = O.ffn_block(**dict(kw, base=np.zeros_like(kw["base"]), w_delta=np.zeros_like(kw["w_delta"])),
                     bf16_points=False)
