@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--topk-rows", action="store_true",
                     help="only time the row-wise top-K call against torch.topk and a full sort "
                          "over a grid of shapes and print that")
+    ap.add_argument("--site-lines", action="store_true",
+                    help="only time the batched conv (2048 blocks) and the feed-forward site and "
+                         "print those two lines (for counter runs under an external profiler)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -129,6 +132,10 @@ def main():
     if args.inject_sweep:
         print(json.dumps({"workload": cfg.name, "inject_sweep": inject_sweep(cfg, W, cache, randn)}),
               flush=True)
+        return
+    if args.site_lines:
+        print(json.dumps({"workload": cfg.name, "conv_batched": conv_batched(cfg, W, randn),
+                          "ffn_block": ffn_block_line(cfg, randn)}), flush=True)
         return
     prefill = None
     if decode64:

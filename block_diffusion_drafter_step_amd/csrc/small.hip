@@ -534,6 +534,9 @@ __global__ __launch_bounds__(1024) void selector_fused_kernel(SelArgs a) {
   float *se = pj + B * r;                                      // [B][K][K]
   float *un = se + BK * K;                                     // [B][K]
   int *sidx = reinterpret_cast<int *>(un + BK);                // [B][K]
+  // target token of position `lane` (wave 0), loaded now so that its latency
+  // overlaps the first loads instead of following the best-path pass
+  const int tg = a.target && tid < B ? a.target[tid] : 0;
   for (int e = tid; e < BK; e += 1024) {
     sidx[e] = clamp_idx(a.idx[e], a.V);
     un[e] = a.unary[e];
@@ -651,7 +654,6 @@ __global__ __launch_bounds__(1024) void selector_fused_kernel(SelArgs a) {
     }
   }
   int b = __builtin_amdgcn_readfirstlane(bb);
-  const int tg = a.target && lane < B ? a.target[lane] : 0;   // target token of position `lane`
   int acc = B;   // the first position where the path leaves the target
 #pragma unroll
   for (int i = kSelMaxB - 1; i >= 0; --i) {

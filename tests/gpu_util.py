@@ -116,6 +116,16 @@ def check_topk(gpu_idx, gpu_unary, logits, K, act, what, drift=None):
     return unique_rows
 
 
+def _command(argv) -> str:
+    """The pytest command line as typed (python -m pytest for the module's path)."""
+    argv = list(argv)
+    if argv and argv[0] == "python":
+        argv = argv[1:]
+    if argv and argv[0].endswith(os.path.join("pytest", "__main__.py")):
+        argv = ["-m", "pytest"] + argv[1:]
+    return "python " + " ".join(argv)
+
+
 def write_margins(path: str, argv, records=None) -> None:
     """The parity margins of this session as markdown: one row per test (its
     checks, elements compared and worst error / bar), then every check that
@@ -126,7 +136,7 @@ def write_margins(path: str, argv, records=None) -> None:
              "`atol + rtol * |ref|` per element (bf16 workloads 2e-2 / 1e-2, fp32 1e-4 / 1e-4), "
              "plus, where the check names one, a rounding-point term. `max err / bar` below 1 "
              "passes; `beyond plain bar` counts the elements that needed the term.", "",
-             "Command: `DFLASH_PARITY_MARGINS=" + path + " " + " ".join(argv) + "`", "",
+             "Command: `DFLASH_PARITY_MARGINS=" + path + " " + _command(argv) + "`", "",
              "| test | checks | elements | worst check | max err / bar |", "|---|---|---|---|---|"]
     by = {}
     for m in records:

@@ -277,12 +277,24 @@ def test_conv_garbage_workspace():
 # (2b) feed-forward site: second conv pair, gated SiLU MLP, residual
 # ---------------------------------------------------------------------------
 
+def fp32_sum_term(x, W):
+    """Higham's bound on fp32 summation of the products x_j W[c, j], n = K + 64
+    of them (a k split adds at most 64 partials) in any order, each addition
+    correctly rounded: gamma_n sum_j |x_j| |W[c, j]|, gamma_n = n u / (1 - n u),
+    u = 2^-24.  It matters only where a long product cancels to a result far
+    below its terms (the Q8_0 workload's weights are O(1), not O(1/sqrt(K)))."""
+    n = x.shape[-1] + 64
+    u = 2.0 ** -24
+    return n * u / (1 - n * u) * (np.abs(x) @ np.abs(W).T)
+
+
 def run_ffn(cfg, nb, tag="ffn", garbage_seed=None):
     """Stage-wise: u against the oracle's conv of h; act against the oracle's
     gated MLP of the GPU's u; out against the oracle's down product of the
-    GPU's act plus h.  End to end: out against the oracle chain (plus, for
-    bf16 workloads, |act_gpu - act_ref| |Wd|^T, the propagation of the
-    stage-checked act through the down product)."""
+    GPU's act plus h, with the fp32 summation term of the down product.  End
+    to end: out against the oracle chain (plus, for bf16 workloads,
+    |act_gpu - act_ref| |Wd|^T, the propagation of the stage-checked act
+    through the down product, and the same summation term)."""
     d, G, T, F = cfg.d, cfg.G, cfg.T, cfg.d_ff
     say(f"ffn {cfg.name} n_blocks={nb} B={cfg.B} d={d} d_ff={F} G={G} T={T} weight={cfg.weight}")
     w = synth.Workload(cfg)
@@ -308,9 +320,11 @@ def run_ffn(cfg, nb, tag="ffn", garbage_seed=None):
     f = O.ffn_hidden(ug, Wg, Wu, bp)
     assert_close(ag, f["act"], cfg.act, f"{cfg.name} ffn act from the GPU's u")
     H2 = H.reshape(M, d)
-    assert_close(outg, O.ffn_out(H2, ag, Wn, bp), cfg.act, f"{cfg.name} ffn out from the GPU's act")
+    sum_term = fp32_sum_term(ag, Wn)
+    assert_close(outg, O.ffn_out(H2, ag, Wn, bp), cfg.act, f"{cfg.name} ffn out from the GPU's act",
+                 term=sum_term)
     ref = O.ffn_block(H, act_np(base, cfg.act), wnp(wd), G, Wg, Wu, Wn, bp)
-    term = np.abs(ag - ref["act"].reshape(M, F)) @ np.abs(Wn).T if bp else None
+    term = sum_term + (np.abs(ag - ref["act"].reshape(M, F)) @ np.abs(Wn).T if bp else 0.0)
     assert_close(outg, ref["out"].reshape(M, d), cfg.act, f"{cfg.name} ffn out end to end", term=term)
 
 
@@ -321,11 +335,15 @@ def test_ffn_block(ci, nb):
 
 def test_ffn_block_many_rows():
     """1024 and 1040 rows (the tiled GEMMs, the second with a ragged tile) at
-    a narrower width, bf16 and Q8_0 weights; 600 fp32 rows."""
+    a narrower width, bf16 and Q8_0 weights; 600 fp32 rows; 520 Q8_0 rows
+    whose gate | up product runs without a k split."""
     run_ffn(cfg_small(1, d=1024, C=1024, d_ff=2048), 64, tag="ffnm")
     run_ffn(cfg_small(1, d=1024, C=1024, d_ff=2048, B=13), 80, tag="ffnr")
     run_ffn(cfg_small(4, d=1024, C=1024, d_ff=1536), 50, tag="ffnq")
     run_ffn(configs.get(0), 75, tag="ffnf")
+    # Q8_0 gate | up over 1280 tiles of 128 x 128: the tile kernel without a k split;
+    # the down product sums 16384 O(1)-weighted terms (the fp32 summation term)
+    run_ffn(cfg_small(4, d=1024, C=1024, d_ff=16384), 65, tag="ffnqw")
 
 
 def test_ffn_block_odd_shapes_and_garbage_workspace():
