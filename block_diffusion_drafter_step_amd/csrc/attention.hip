@@ -23,6 +23,7 @@
 // fixed order.
 #include "common.h"
 #include "kernels.h"
+#include "stream.h"
 
 namespace dfl {
 
@@ -35,6 +36,16 @@ constexpr int kAttnKT = 32;      // keys per tile (one ring stage)
 #endif
 constexpr int kAttnStages = DFL_ATTN_STAGES;
 constexpr float kLog2e = 1.4426950408889634f;
+// Lazy softmax reference: a column's reference maximum moves only when its
+// scores exceed it by more than 2^kLazyMax, so the accumulators are rescaled
+// about once per split and the unnormalised weights stay <= 2^kLazyMax.  The
+// reference starts at a finite floor (not -inf), so masked scores (-inf) give
+// weight exp2(-inf) = 0 with no special case.
+constexpr float kLazyMax = 8.f;
+constexpr float kRefFloor = -1e30f;
+// 2^x by the hardware instruction (v_exp_f32): the weights are rounded to the
+// act type right after, and exp2(-inf) = 0
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef __attribute__((address_space(3))) void attn_lds_void;
 
@@ -91,10 +102,100 @@ __device__ __forceinline__ void attn_ring_barrier() {
 // the context keys [key0, key1) of KV head kvh that one workgroup owns
 struct KeyRange {
   const char *ck, *cv;   // this head's K rows and V^T panels
+  const char *sk, *sv;   // Q8_0 caches: this head's K and V scales ([cap][hd/32] fp16)
   long cap;
   long key0, key1;
   int ntile;
 };
+
+// ---------------------------------------------------------------------------
+// Q8_0 caches (head_dim 128) through the same ring: a stage holds a tile's
+// raw codes and scales, 9 KB against 16 KB of bf16,
+//   [K codes 32 keys x 128 | V^T codes 128 dims x 32 | K scales 32 x 4 fp16 |
+//    V scales 32 x 4 fp16 | 512 spare bytes]
+// each wave issuing two 1 KB code loads and one 256-byte scale load (waves
+// 2-3 repeat the scales into the spare bytes, so every wave counts the same
+// loads).  Once a stage has landed, the workgroup's 256 threads decode it
+// into one bf16 tile in the layout (and swizzle) of a bf16 stage, each code
+// once, to bf16_rne(fp32(scale) * code); the bf16 tile code then runs on it.
+// ---------------------------------------------------------------------------
+constexpr int kQ8HD = 128;
+constexpr int kQ8Codes = kAttnKT * kQ8HD;        // 4 KB of K codes, 4 KB of V^T codes
+constexpr int kQ8Stage = 2 * kQ8Codes + 1024;    // + K scales, V scales, spare
+constexpr int kQ8NPW = 3;                        // loads per wave per stage
+#ifndef DFL_ATTN_Q8_STAGES
+#define DFL_ATTN_Q8_STAGES 3
+#endif
+constexpr int kQ8Stages = DFL_ATTN_Q8_STAGES;
+
+__device__ __forceinline__ void attn_dma4(const void *g, attn_lds_void *l) {
+  __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+}
+
+__device__ __forceinline__ void attn_issue_q8(const KeyRange &kr, char *stage, int tI, int wave, int lane) {
+  const long t0 = kr.key0 + (long)min(tI, kr.ntile - 1) * kAttnKT;
+  // K piece `wave`: keys 8 wave .. + 8 (a tile starts inside the capacity,
+  // which is a multiple of 64, so all 32 rows of it lie inside too)
+  {
+    const int row = 8 * wave + (lane >> 3), c = lane & 7;
+    attn_dma16(kr.ck + (t0 + row) * kQ8HD + 16 * c, (attn_lds_void *)(stage + wave * 1024));
+  }
+  // V^T piece `wave`: dims 32 wave .. + 32 of the tile's panel
+  {
+    const int d = 32 * wave + (lane >> 1), h = lane & 1;
+    const char *panel = kr.cv + (t0 / kAttnKT) * (long)(kQ8HD * kAttnKT);
+    attn_dma16(panel + d * kAttnKT + 16 * h, (attn_lds_void *)(stage + kQ8Codes + wave * 1024));
+  }
+  // scales of the tile's 32 positions: 256 contiguous bytes each
+  const char *sc = (wave & 1) ? kr.sv : kr.sk;
+  attn_dma4(sc + t0 * (kQ8HD / 32) * 2 + 4 * lane, (attn_lds_void *)(stage + 2 * kQ8Codes + 256 * wave));
+}
+
+// eight codes, each with its own scale, to bf16 (exact product, one rounding)
+__device__ __forceinline__ Frag<bf16> dq8_each(uint32_t lo, uint32_t hi, const float (&s)[8]) {
+  const uint32_t a = lo ^ 0x80808080u, b = hi ^ 0x80808080u;
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = j < 2 ? a : b;
+    const int sh = 16 * (j & 1);
+    const dq_f32x2 v = {fmaf((float)((w >> sh) & 0xffu), s[2 * j], -128.f * s[2 * j]),
+                        fmaf((float)((w >> (sh + 8)) & 0xffu), s[2 * j + 1], -128.f * s[2 * j + 1])};
+    r[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, dq_bf16x2));
+  }
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, r);
+  return f;
+}
+
+// the 256 threads of a workgroup decode a landed Q8_0 stage into `dec`, a
+// bf16 tile laid out as a bf16 stage of AttnCfg<bf16, 128>
+__device__ __forceinline__ void attn_decode_q8(const char *raw, char *dec, int tid) {
+  using C = AttnCfg<bf16, kQ8HD>;
+  const char *ksc = raw + 2 * kQ8Codes, *vsc = ksc + 256;
+  {   // K: key tid / 8, dims 16 c .. + 16 under the scale of block c / 2
+    const int key = tid >> 3, c = tid & 7;
+    const uint4 q = *reinterpret_cast<const uint4 *>(raw + key * kQ8HD + 16 * c);
+    const float sc = half_bits_to_f32(*reinterpret_cast<const uint16_t *>(ksc + key * 8 + 2 * (c >> 1)));
+    char *row = dec + key * C::RK;
+    *reinterpret_cast<Frag<bf16> *>(row + 16 * kswz<C::NKC>(key, 2 * c)) = dq8(q.x, q.y, sc);
+    *reinterpret_cast<Frag<bf16> *>(row + 16 * kswz<C::NKC>(key, 2 * c + 1)) = dq8(q.z, q.w, sc);
+  }
+  {   // V^T: dim tid / 2, keys 16 h .. + 16, each under its own key's scale of block d / 32
+    const int d = tid >> 1, h = tid & 1;
+    const uint4 q = *reinterpret_cast<const uint4 *>(raw + kQ8Codes + d * kAttnKT + 16 * h);
+    const char *vs = vsc + (16 * h) * 8 + 2 * (d >> 5);
+    float s0[8], s1[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s0[e] = half_bits_to_f32(*reinterpret_cast<const uint16_t *>(vs + 8 * e));
+      s1[e] = half_bits_to_f32(*reinterpret_cast<const uint16_t *>(vs + 8 * (8 + e)));
+    }
+    char *row = dec + C::KBYTES + d * C::RV;
+    *reinterpret_cast<Frag<bf16> *>(row + 16 * vswz<C::NVC>(d, 2 * h)) = dq8_each(q.x, q.y, s0);
+    *reinterpret_cast<Frag<bf16> *>(row + 16 * vswz<C::NVC>(d, 2 * h + 1)) = dq8_each(q.z, q.w, s1);
+  }
+}
 
 // Issue tile tI (clamped to the last) into `stage`: this wave's NPW of the
 // stage's 1 KB loads.  K rows past the chunk re-read its last key (they only
@@ -173,15 +274,17 @@ __device__ __forceinline__ void attn_tile(const char *stage, long t0, long key1,
     const int c = (8 * g) / C::EPC;
     vf[dt] = lds_frag2<TA>(vr, vswz<C::NVC>(d, c), vswz<C::NVC>(d, c + CPF - 1));
   }
+  // keys of this tile inside the range (wave-uniform, 32 but for the last)
+  const int lim = (int)min(key1 - t0, (long)kAttnKT);
   // a tile that ends inside its V^T panel: the panel's positions from key1 on
   // may hold anything (a NaN would survive its zero probability), so their
   // values are replaced by zeros; element e of a fragment is key 8g + e
-  if (t0 + kAttnKT > key1) {
+  if (lim < kAttnKT) {
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (t0 + 8 * g + e >= key1) vf[dt].v[e] = from_f32<TA>(0.f);
+        if (8 * g + e >= lim) vf[dt].v[e] = from_f32<TA>(0.f);
   }
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
@@ -200,32 +303,34 @@ __device__ __forceinline__ void attn_tile(const char *stage, long t0, long key1,
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const long key = t0 + 8 * g + 4 * st + i;
-        const float v = key < key1 ? s[st][i] * sl2 : -__builtin_inff();
+        const float v = 8 * g + 4 * st + i < lim ? s[st][i] * sl2 : -__builtin_inff();
         p[st * 4 + i] = v;
         mx = fmaxf(mx, v);
       }
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run[hh], mx);
-    const float alpha = m_new == -__builtin_inff() ? 1.f : exp2f(m_run[hh] - m_new);
-    // the row sum uses the probabilities exactly as the P.V product sees them
+    // lazy reference maximum (a wave-uniform branch, rare after the first tile)
+    const bool up = mx > m_run[hh] + kLazyMax;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float alpha = up ? hw_exp2(m_run[hh] - mx) : 1.f;
+      if (up) m_run[hh] = mx;
+      l_run[hh] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) o[hh][dt] *= alpha;
+    }
+    // the row sum uses the weights exactly as the P.V product sees them
     float ls = 0.f;
     Frag<TA> pf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pf.v[e] = from_f32<TA>(p[e] == -__builtin_inff() ? 0.f : exp2f(p[e] - m_new));
+      pf.v[e] = from_f32<TA>(hw_exp2(p[e] - m_run[hh]));
       ls += to_f32(pf.v[e]);
     }
     ls += shfl_xor(ls, 16);
     ls += shfl_xor(ls, 32);
-    l_run[hh] = l_run[hh] * alpha + ls;
-    m_run[hh] = m_new;
+    l_run[hh] += ls;
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-      o[hh][dt] *= alpha;
-      mma(o[hh][dt], vf[dt], pf);
-    }
+    for (int dt = 0; dt < C::NDT; ++dt) mma(o[hh][dt], vf[dt], pf);
   }
 }
 
@@ -240,9 +345,17 @@ __device__ __forceinline__ void attn_tile(const char *stage, long t0, long key1,
 // part of the workgroup's keys through their own ring, and the streams'
 // running softmax states are merged in LDS at the end, so one workgroup
 // writes one partial per query row for NS parts of the context.
-template <typename TA, int HD, int HPW, int NS>
+// KQ8: the cache holds Q8_0 codes and scales (bf16 activations, head_dim
+// 128, one stream): the ring carries raw stages and each landed stage is
+// decoded once into one of two bf16 tiles; tile t+1 is decoded in the same
+// barrier interval in which tile t is multiplied (one barrier per tile).
+template <typename TA, int HD, int HPW, int NS, bool KQ8 = false>
 __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_split_kernel(AttnArgs a) {
   using C = AttnCfg<TA, HD>;
+  static_assert(!KQ8 || (NS == 1 && HD == kQ8HD && sizeof(TA) == 2), "Q8_0: bf16, head_dim 128, one stream");
+  constexpr int STG = KQ8 ? kQ8Stage : C::STAGE;   // bytes of one ring stage
+  constexpr int NPW = KQ8 ? kQ8NPW : C::NPW;       // loads per wave per stage
+  constexpr int S = KQ8 ? kQ8Stages : kAttnStages; // ring stages
   extern __shared__ __attribute__((aligned(1024))) char attn_smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -251,8 +364,16 @@ __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_s
   const int kvh = blockIdx.y, sp = blockIdx.x;
   const int grp = a.Hq / a.Hkv;
   KeyRange kr;
-  kr.ck = reinterpret_cast<const char *>(a.ck) + (long)kvh * a.cap * C::RK;
-  kr.cv = reinterpret_cast<const char *>(a.cv) + (long)kvh * a.cap * HD * C::ES;   // cap/32 panels
+  if constexpr (KQ8) {   // one byte per code, four fp16 scales per position
+    kr.ck = reinterpret_cast<const char *>(a.ck) + (long)kvh * a.cap * HD;
+    kr.cv = reinterpret_cast<const char *>(a.cv) + (long)kvh * a.cap * HD;
+    kr.sk = reinterpret_cast<const char *>(a.cks) + (long)kvh * a.cap * (HD / 32) * 2;
+    kr.sv = reinterpret_cast<const char *>(a.cvs) + (long)kvh * a.cap * (HD / 32) * 2;
+  } else {
+    kr.ck = reinterpret_cast<const char *>(a.ck) + (long)kvh * a.cap * C::RK;
+    kr.cv = reinterpret_cast<const char *>(a.cv) + (long)kvh * a.cap * HD * C::ES;   // cap/32 panels
+    kr.sk = kr.sv = nullptr;
+  }
   kr.cap = a.cap;
   // the workgroup's keys [w0, w1) in NS parts of whole tiles
   const long w0 = (long)sp * a.chunk, w1 = min(a.n_ctx, w0 + a.chunk);
@@ -265,7 +386,8 @@ __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_s
   // skips the arithmetic, and a stream without keys loads nothing
   const int nloop = (int)((min(w1, w0 + part) - w0 + kAttnKT - 1) / kAttnKT);
   const bool loads = kr.ntile > 0;
-  char *ring = attn_smem + stream * (kAttnStages * C::STAGE);
+  char *ring = attn_smem + stream * (S * STG);
+  char *dec = attn_smem + NS * S * STG;   // KQ8: two decoded bf16 tiles
   const long qld = (long)(a.Hq + 2 * a.Hkv) * HD;
   const float sl2 = a.scale * kLog2e;
 
@@ -286,23 +408,50 @@ __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_s
       qf[hh][f] = tok_ok ? load_frag(qp + 32 * f + 8 * g) : frag_zero<TA>();
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) o[hh][dt] = zero4();
-    m_run[hh] = -__builtin_inff();
+    m_run[hh] = kRefFloor;
     l_run[hh] = 0.f;
   }
 
   // ring: tile t is read from stage t % S; stages t+1 .. t+S-2 are in flight
-  constexpr int S = kAttnStages;
-  if (loads) {
+  auto issue = [&](int t) {
+    if constexpr (KQ8) attn_issue_q8(kr, ring + (t % S) * STG, t, wave, lane);
+    else attn_issue<TA, HD>(kr, ring + (t % S) * STG, t, wave, lane);
+  };
+  if constexpr (KQ8) {
+    // one stream (nloop == ntile).  Tiles 0 .. S-1 fill every stage; at the
+    // top of iteration t tiles up to t+S-1 are issued, tile t+1 has landed
+    // after the barrier, whose other side also orders iteration t-1 (reads
+    // of decoded tile t-1, decode of tile t) before this one.  Stage t % S
+    // was decoded in iteration t-1, so tile t+S refills it.
+    constexpr int DB = AttnCfg<bf16, kQ8HD>::STAGE;
+    if (loads) {
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) attn_issue<TA, HD>(kr, ring + s * C::STAGE, s, wave, lane);
-  }
-  for (int tI = 0; tI < nloop; ++tI) {
-    attn_wait_vm<C::NPW * (S - 2)>();   // this wave's loads of tile tI have landed
-    attn_ring_barrier();                // ... everyone's; tile tI-1 is no longer read
-    if (loads) attn_issue<TA, HD>(kr, ring + ((tI + S - 1) % S) * C::STAGE, tI + S - 1, wave, lane);
-    if (tI < kr.ntile)
-      attn_tile<TA, HD, HPW>(ring + (tI % S) * C::STAGE, kr.key0 + (long)tI * kAttnKT, kr.key1, sl2, g,
-                             r16, qf, o, m_run, l_run, active);
+      for (int s = 0; s < S; ++s) issue(s);
+      attn_wait_vm<NPW * (S - 1)>();   // tile 0 has landed
+      attn_ring_barrier();
+      attn_decode_q8(ring, dec, tid);
+    }
+    for (int tI = 0; tI < nloop; ++tI) {
+      attn_wait_vm<NPW * (S - 2)>();   // this wave's loads of tile tI+1 have landed
+      attn_ring_barrier();             // ... everyone's; decoded tile tI is complete
+      issue(tI + S);
+      attn_tile<TA, HD, HPW>(dec + (tI & 1) * DB, kr.key0 + (long)tI * kAttnKT, kr.key1, sl2, g, r16, qf,
+                             o, m_run, l_run, active);
+      if (tI + 1 < kr.ntile) attn_decode_q8(ring + ((tI + 1) % S) * STG, dec + ((tI + 1) & 1) * DB, tid);
+    }
+  } else {
+    if (loads) {
+#pragma unroll
+      for (int s = 0; s < S - 1; ++s) issue(s);
+    }
+    for (int tI = 0; tI < nloop; ++tI) {
+      attn_wait_vm<NPW * (S - 2)>();   // this wave's loads of tile tI have landed
+      attn_ring_barrier();             // ... everyone's; tile tI-1 is no longer read
+      if (loads) issue(tI + S - 1);
+      if (tI < kr.ntile)
+        attn_tile<TA, HD, HPW>(ring + (tI % S) * STG, kr.key0 + (long)tI * kAttnKT, kr.key1, sl2, g, r16,
+                               qf, o, m_run, l_run, active);
+    }
   }
   attn_wait_vm<0>();
 
@@ -360,275 +509,6 @@ __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_s
     if (g == 0) {
       a.part_ml[base * 2] = m_run[hh];
       a.part_ml[base * 2 + 1] = l_run[hh];
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Split kernel for Q8_0 caches (head_dim 128, GQA group x block of at most 64
-// query rows).  Every wave owns a contiguous range of keys and carries all
-// query rows of the group as MFMA columns (column c = local head c / B, token
-// c % B), so each code and scale is loaded by exactly one wave, straight into
-// registers, and dequantised once: no LDS staging, no barrier in the loop.
-// Per 32-key tile a lane loads 4 x 16 bytes of K codes (each instruction 16
-// key rows x 64 contiguous bytes), 8 x 8 bytes of V^T codes (16 panel rows x
-// 32 bytes), its keys' K scales and the 64 bytes of V scales of its eight
-// keys: 8.5 KB per tile against 16 KB for bf16.  A tile is dequantised to
-// bf16 (value = bf16_rne(fp32(scale) * code)), the next tile's loads are
-// issued into the codes' registers, and the tile is multiplied:
-//   S^T = K Q^T  (keys x columns),  online softmax per column (base 2),
-//   O^T = V^T P^T (dims x columns)
-// with the interleaved key order of the two 16-key S^T tiles (row r of tile
-// st is key 8(r/4) + 4st + r%4), so each lane's eight weights of one column
-// are eight consecutive keys: the P^T operand whose V^T partner is one 8-byte
-// run of a panel row.  MFMA j of the score product takes head dims
-// 64 (j/2) + 16 g + 8 (j%2) .. + 8 from lane group g (for the codes and Q
-// alike).  The weights are taken relative to a reference maximum that moves
-// only when the scores exceed it by more than 2^8, so the accumulators are
-// rescaled about once.  The four waves of a workgroup hold four consecutive
-// parts of its keys; their (O, m, l) are merged in LDS in wave order and
-// written as one split partial per query row, in attn_combine_kernel's layout.
-// ---------------------------------------------------------------------------
-constexpr int kWaveHD = 128;
-constexpr int kWaveMaxCols = 64;
-constexpr float kLazyMax = 8.f;   // log2 of the largest unnormalised weight
-
-struct Q8Tile {
-  uint4 kc[2][2];   // K codes: S^T tile st, dims 64 m + 16 g .. + 16 of the lane's key row
-  uint2 ks[2];      // the four K scales of that key row
-  uint2 vc[kWaveHD / 16];   // V^T codes: dim 16 dt + r16, keys 8 g .. 8 g + 7
-  uint4 vs[4];      // V scales of keys 8 g .. 8 g + 7 (four per key)
-};
-
-__device__ __forceinline__ float f16_lo(unsigned w) { return half_bits_to_f32((uint16_t)(w & 0xffffu)); }
-__device__ __forceinline__ float f16_hi(unsigned w) { return half_bits_to_f32((uint16_t)(w >> 16)); }
-
-template <int NCT>
-__global__ __launch_bounds__(256, 1) void attn_q8_kernel(AttnArgs a) {
-  constexpr int HD = kWaveHD, NQF = HD / 32, NDT = HD / 16, NB = HD / 32;
-  __shared__ float xch[3][(NDT * NCT * 4 + 2 * NCT) * 64];
-  __shared__ Frag<bf16> qs[NCT * NQF * 64];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, r16 = lane & 15;
-  const int kvh = blockIdx.y, sp = blockIdx.x;
-  const int grp = a.Hq / a.Hkv, B = a.B, ncol = grp * B;
-  // this wave's keys [k0, k1): part `wave` of the workgroup's chunk, whole tiles
-  const long w0 = (long)sp * a.chunk, w1 = min(a.n_ctx, w0 + (long)a.chunk);
-  const long part = ((a.chunk / 4 + kAttnKT - 1) / kAttnKT) * kAttnKT;
-  const long k0 = min(w1, w0 + wave * part), k1 = min(w1, k0 + part);
-  const int ntile = (int)((k1 - k0 + kAttnKT - 1) / kAttnKT);
-  const char *kq = reinterpret_cast<const char *>(a.ck) + (long)kvh * a.cap * HD;
-  const char *vq = reinterpret_cast<const char *>(a.cv) + (long)kvh * a.cap * HD;
-  const char *ksc = reinterpret_cast<const char *>(a.cks) + (long)kvh * a.cap * NB * 2;
-  const char *vsc = reinterpret_cast<const char *>(a.cvs) + (long)kvh * a.cap * NB * 2;
-  const long qld = (long)(a.Hq + 2 * a.Hkv) * HD;
-  const float sl2 = a.scale * kLog2e;
-
-  // Q^T fragments in LDS (read where they are used, leaving the registers to
-  // the accumulators and the tiles in flight): slot (ct, j) of lane l
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int c = 16 * ct + r16;
-    const bool ok = c < ncol;
-    const int hl = ok ? c / B : 0, t = ok ? c - hl * B : 0;
-    const bf16 *qp = reinterpret_cast<const bf16 *>(a.qkv) + (long)t * qld + (long)(kvh * grp + hl) * HD;
-    if (wave == 0) {
-#pragma unroll
-      for (int j = 0; j < NQF; ++j)
-        qs[(ct * NQF + j) * 64 + lane] =
-            ok ? load_frag(qp + 64 * (j >> 1) + 16 * g + 8 * (j & 1)) : frag_zero<bf16>();
-    }
-  }
-  __syncthreads();
-  f32x4 o[NDT][NCT];
-  float mr[NCT], lr[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt][ct] = zero4();
-    mr[ct] = -__builtin_inff();
-    lr[ct] = 0.f;
-  }
-
-  // a tile's loads from a wave-uniform base plus 32-bit lane offsets: key
-  // rows t0 + row (all 32 below the capacity; rows past k1 feed masked
-  // scores) and the tile's V^T panel (inside the capacity)
-  unsigned krow[2];
-#pragma unroll
-  for (int st = 0; st < 2; ++st) krow[st] = (unsigned)(8 * (r16 >> 2) + 4 * st + (r16 & 3));
-  auto load = [&](Q8Tile &T, long t0) {
-    const char *kb = kq + t0 * HD, *sb = ksc + t0 * (NB * 2);
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        T.kc[st][m] = *reinterpret_cast<const uint4 *>(kb + krow[st] * HD + 64 * m + 16 * g);
-      T.ks[st] = *reinterpret_cast<const uint2 *>(sb + krow[st] * (NB * 2));
-    }
-    const char *vb = vq + (t0 >> 5) * (long)(HD * 32);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      T.vc[dt] = *reinterpret_cast<const uint2 *>(vb + (16 * dt + r16) * 32 + 8 * g);
-    const char *vs = vsc + (t0 + 8 * g) * (NB * 2);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) T.vs[q] = *reinterpret_cast<const uint4 *>(vs + 16 * q);
-  };
-
-  // a tile's bf16 fragments (keys past lim: V^T entries 0)
-  auto dequant = [&](const Q8Tile &T, int lim, Frag<bf16> (&kf)[2][NQF], Frag<bf16> (&vf)[NDT]) {
-    // K fragments: MFMA j takes codes 8 (j%2) .. of the 16 at dims 64 (j/2) + 16 g
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const float s0 = (g >> 1) ? f16_hi(T.ks[st].x) : f16_lo(T.ks[st].x);   // block g/2
-      const float s1 = (g >> 1) ? f16_hi(T.ks[st].y) : f16_lo(T.ks[st].y);   // block 2 + g/2
-      kf[st][0] = dequant8(make_uint2(T.kc[st][0].x, T.kc[st][0].y), s0);
-      kf[st][1] = dequant8(make_uint2(T.kc[st][0].z, T.kc[st][0].w), s0);
-      kf[st][2] = dequant8(make_uint2(T.kc[st][1].x, T.kc[st][1].y), s1);
-      kf[st][3] = dequant8(make_uint2(T.kc[st][1].z, T.kc[st][1].w), s1);
-    }
-    // V^T fragments: element e is key 8g + e at dim 16 dt + r16, scale of
-    // block dt / 2 of that key; keys from k1 on become 0 (a tile that ends
-    // inside its panel: the rest of the panel may hold anything)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float sv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint4 w = T.vs[e >> 1];
-        const int hi = (e & 1) * 4 + b;   // fp16 index within the uint4
-        const unsigned word = (hi >> 1) == 0 ? w.x : (hi >> 1) == 1 ? w.y : (hi >> 1) == 2 ? w.z : w.w;
-        sv[e] = (hi & 1) ? f16_hi(word) : f16_lo(word);
-        if (8 * g + e >= lim) sv[e] = 0.f;
-      }
-#pragma unroll
-      for (int dd = 0; dd < 2; ++dd) {
-        const int dt = 2 * b + dd;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const unsigned word = e < 4 ? T.vc[dt].x : T.vc[dt].y;
-          const int code = ((int)(word << (24 - 8 * (e & 3)))) >> 24;
-          vf[dt].v[e] = from_f32<bf16>((float)code * sv[e]);
-        }
-      }
-    }
-  };
-  auto math = [&](const Frag<bf16> (&kf)[2][NQF], const Frag<bf16> (&vf)[NDT], int lim) {
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      f32x4 s[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s[st] = zero4();
-#pragma unroll
-        for (int j = 0; j < NQF; ++j) mma(s[st], kf[st][j], qs[(ct * NQF + j) * 64 + lane]);
-      }
-      // lane: column r16, keys 8g + 4st + i
-      float p[8];
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = 8 * g + 4 * st + i < lim ? s[st][i] * sl2 : -__builtin_inff();
-          p[st * 4 + i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      // the column's reference maximum moves only when the scores rise more
-      // than 2^8 above it (a wave-uniform branch, rare after the first tile)
-      const bool up = mx > mr[ct] + kLazyMax;
-      if (__builtin_amdgcn_ballot_w64(up)) {
-        const float alpha = up ? exp2f(mr[ct] - mx) : 1.f;   // mr = -inf: 0
-        if (up) mr[ct] = mx;
-        lr[ct] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt][ct] *= alpha;
-      }
-      // the row sum uses the weights exactly as the P.V product sees them
-      float ls = 0.f;
-      Frag<bf16> pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pf.v[e] = from_f32<bf16>(p[e] == -__builtin_inff() ? 0.f : exp2f(p[e] - mr[ct]));
-        ls += to_f32(pf.v[e]);
-      }
-      ls += shfl_xor(ls, 16);
-      ls += shfl_xor(ls, 32);
-      lr[ct] += ls;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) mma(o[dt][ct], vf[dt], pf);
-    }
-  };
-
-  // one tile of codes in registers: once a tile is dequantised its codes are
-  // dead, so the next tile's loads are issued there and land while this
-  // tile is multiplied
-  if (ntile > 0) {
-    Q8Tile T;
-    load(T, k0);
-    for (int i = 0; i < ntile; ++i) {
-      const long t0 = k0 + (long)i * kAttnKT;
-      const int lim = (int)min(k1 - t0, (long)kAttnKT);   // keys of this tile inside the range
-      Frag<bf16> kf[2][NQF], vf[NDT];
-      dequant(T, lim, kf, vf);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < ntile) load(T, t0 + kAttnKT);
-      __builtin_amdgcn_sched_barrier(0);
-      math(kf, vf, lim);
-    }
-  }
-
-  // waves 1..3 hand (o, m, l) to wave 0, which merges them in wave order
-  constexpr int NO = NDT * NCT * 4;
-  if (wave > 0) {
-    float *x = xch[wave - 1];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[((dt * NCT + ct) * 4 + i) * 64 + lane] = o[dt][ct][i];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      x[(NO + 2 * ct) * 64 + lane] = mr[ct];
-      x[(NO + 2 * ct + 1) * 64 + lane] = lr[ct];
-    }
-  }
-  __syncthreads();
-  if (wave > 0) return;
-#pragma unroll 1
-  for (int w = 0; w < 3; ++w) {
-    const float *x = xch[w];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const float m1 = x[(NO + 2 * ct) * 64 + lane], l1 = x[(NO + 2 * ct + 1) * 64 + lane];
-      const float mm = fmaxf(mr[ct], m1);
-      if (mm == -__builtin_inff()) continue;   // neither part saw a key
-      const float a0 = exp2f(mr[ct] - mm), a1 = exp2f(m1 - mm);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o[dt][ct][i] = o[dt][ct][i] * a0 + x[((dt * NCT + ct) * 4 + i) * 64 + lane] * a1;
-      lr[ct] = lr[ct] * a0 + l1 * a1;
-      mr[ct] = mm;
-    }
-  }
-  // partials of column (hl, t): lane holds dims 16 dt + 4 g + i
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int c = 16 * ct + r16;
-    if (c >= ncol) continue;
-    const int hl = c / B, t = c - hl * B;
-    const long base = ((long)(kvh * grp + hl) * B + t) * a.n_split + sp;
-    float *po = a.part_o + base * HD + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt) = o[dt][ct];
-    if (g == 0) {
-      a.part_ml[base * 2] = mr[ct];
-      a.part_ml[base * 2 + 1] = lr[ct];
     }
   }
 }
@@ -804,6 +684,17 @@ static hipError_t attn_split_go(const AttnArgs &a, hipStream_t st) {
   return hipSuccess;
 }
 
+// Q8_0 cache through the ring: raw stages plus the decoded bf16 tile
+template <int HPW>
+static hipError_t attn_split_q8_go(const AttnArgs &a, hipStream_t st) {
+  const size_t lds = (size_t)kQ8Stages * kQ8Stage + 2 * AttnCfg<bf16, kQ8HD>::STAGE;
+  auto *k = &attn_split_kernel<bf16, kQ8HD, HPW, 1, true>;
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3(a.n_split, a.Hkv), dim3(256), lds, st, a);
+  return hipSuccess;
+}
+
 // key streams per split workgroup: two when both rings fit the LDS (and the
 // merge area, 4 HPW waves' (o, m, l), fits one of them)
 template <typename TA, int HD>
@@ -815,18 +706,16 @@ int attn_streams(int act, int hd) {
   return hd == 64 ? attn_streams_t<bf16, 64>() : attn_streams_t<bf16, 128>();
 }
 
-bool attn_q8_ok(int hd, int grp, int B) { return hd == kWaveHD && grp * B <= kWaveMaxCols; }
+bool attn_q8_ok(int hd, int grp, int B) {
+  (void)B;
+  return hd == kQ8HD && grp <= 8;
+}
 
 void attn_plan_call(int act, int hd, int grp, int B, int kvq, long n_keys, int Hkv, int *chunk, int *n_split) {
   (void)grp;
   (void)B;
-  // the Q8_0 kernel: one 4-wave workgroup per CU (as the two-stream ring kernel)
-  attn_plan(n_keys, Hkv, kvq ? 2 : attn_streams(act, hd), chunk, n_split);
-}
-
-template <int NCT>
-static void attn_q8_go(const AttnArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_q8_kernel<NCT>), dim3(a.n_split, a.Hkv), dim3(256), 0, st, a);
+  // Q8_0 caches: one stream per workgroup, two workgroups per CU
+  attn_plan(n_keys, Hkv, kvq ? 1 : attn_streams(act, hd), chunk, n_split);
 }
 
 template <typename TA, int HD>
@@ -853,10 +742,8 @@ static hipError_t attn_launch_t(const AttnArgs &a, hipStream_t st) {
 hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st) {
   if (a.kvq) {   // bf16 activations, head_dim 128 (checked by the caller)
     if (a.n_split > 0) {
-      const int nct = (a.Hq / a.Hkv * a.B + 15) / 16;
-      if (nct == 1) attn_q8_go<1>(a, st);
-      else if (nct == 2) attn_q8_go<2>(a, st);
-      else attn_q8_go<4>(a, st);
+      const hipError_t e = a.Hq / a.Hkv <= 4 ? attn_split_q8_go<1>(a, st) : attn_split_q8_go<2>(a, st);
+      if (e != hipSuccess) return e;
     }
     attn_combine_go<bf16, 128>(a, st);
   } else {

@@ -551,7 +551,7 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   if (n_q_heads / Hkv > 8) return fail(DFLASH_ERR_UNSUPPORTED, "at most 8 query heads per KV head");
   const int kvq = cache->dtype == DFLASH_Q8_0;
   if (kvq && !attn_q8_ok(hd, n_q_heads / Hkv, B))
-    return fail(DFLASH_ERR_UNSUPPORTED, "a Q8_0 cache needs (query heads per KV head) x B <= 64");
+    return fail(DFLASH_ERR_UNSUPPORTED, "a Q8_0 cache needs head_dim 128");
   const int64_t qdim = (int64_t)n_q_heads * hd, kv = (int64_t)Hkv * hd;
   TRY(check_weight(wq, "wq", qdim, d, act, true));
   TRY(check_weight(wk, "wk", kv, d, act, true));

@@ -140,7 +140,7 @@ int attn_streams(int act, int hd);
 // the plan of the split kernel launch_attention picks for these shapes
 void attn_plan_call(int act, int hd, int grp, int B, int kvq, long n_keys, int Hkv, int *chunk,
                     int *n_split);
-// Q8_0 caches: head_dim 128 and at most 64 query rows (group x block)
+// Q8_0 caches: head_dim 128 (and at most 8 query heads per KV head)
 bool attn_q8_ok(int hd, int grp, int B);
 int attn_max_splits(long n_keys, int Hkv);
 hipError_t launch_attention(int act, const AttnArgs &a, hipStream_t st);

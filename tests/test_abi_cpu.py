@@ -301,9 +301,9 @@ def test_q8_0_cache_validation(lib):
     assert lib.dflash_inject(hid, 1, 16, 512, 1, ctypes.byref(fc), None, 1e-6, ctypes.byref(wk), ctypes.byref(wk),
                              ctypes.byref(noscale), 0, FAKE, ws_big, None) == 1
     assert b"k_scales" in lib.dflash_last_error()
-    # attention: 8 query heads per KV head x B = 16 is 128 query rows, more than the Q8_0 kernel carries
-    wq, wkv, wo = W(1, 128 * 64, 512), W(1, 1024, 512), W(1, 512, 128 * 64)
+    # attention over a Q8_0 cache of head_dim 64: not implemented
+    wq, wkv, wo = W(1, 64 * 64, 512), W(1, 512, 512), W(1, 512, 64 * 64)
     st = lib.dflash_block_attn(FAKE, None, 16, 512, 64, 1, ctypes.byref(wq), ctypes.byref(wkv), ctypes.byref(wkv),
-                               ctypes.byref(wo), ctypes.byref(ok), 100, 0.0, FAKE, FAKE, ws_big, None)
-    assert st == 2 and b"Q8_0" in lib.dflash_last_error()
+                               ctypes.byref(wo), ctypes.byref(hd64), 100, 0.0, FAKE, FAKE, ws_big, None)
+    assert st == 2
 

@@ -596,8 +596,14 @@ def test_attn_q8_0_cache_tail_not_finite(ci, n_ctx):
 
 
 def test_attn_q8_0_cache_small_groups():
-    """One column tile per wave: two query heads per KV head, B = 5."""
+    """Two query heads per KV head (waves 2-3 without a head), B = 5."""
     run_attn_q8(cfg_small(1, Hq=16, Hkv=8), 777, B=5)
+
+
+def test_attn_q8_0_cache_eight_head_groups():
+    """Eight query heads per KV head (two per wave) at B = 16: 128 query rows
+    per KV head; a context that ends inside a tile."""
+    run_attn_q8(cfg_small(1, Hq=64, Hkv=8), 3001)
 
 
 # ---------------------------------------------------------------------------
