@@ -352,7 +352,7 @@ __device__ __forceinline__ void attn_tile(const char *stage, long t0, long key1,
 template <typename TA, int HD, int HPW, int NS, bool KQ8 = false>
 __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_split_kernel(AttnArgs a) {
   using C = AttnCfg<TA, HD>;
-  static_assert(!KQ8 || (NS == 1 && HD == kQ8HD && sizeof(TA) == 2), "Q8_0: bf16, head_dim 128, one stream");
+  static_assert(!KQ8 || (HD == kQ8HD && sizeof(TA) == 2), "Q8_0: bf16, head_dim 128");
   constexpr int STG = KQ8 ? kQ8Stage : C::STAGE;   // bytes of one ring stage
   constexpr int NPW = KQ8 ? kQ8NPW : C::NPW;       // loads per wave per stage
   constexpr int S = KQ8 ? kQ8Stages : kAttnStages; // ring stages
@@ -387,7 +387,8 @@ __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_s
   const int nloop = (int)((min(w1, w0 + part) - w0 + kAttnKT - 1) / kAttnKT);
   const bool loads = kr.ntile > 0;
   char *ring = attn_smem + stream * (S * STG);
-  char *dec = attn_smem + NS * S * STG;   // KQ8: two decoded bf16 tiles
+  // KQ8: this stream's two decoded bf16 tiles
+  char *dec = attn_smem + NS * S * STG + stream * 2 * AttnCfg<bf16, kQ8HD>::STAGE;
   const long qld = (long)(a.Hq + 2 * a.Hkv) * HD;
   const float sl2 = a.scale * kLog2e;
 
@@ -418,26 +419,29 @@ __global__ __launch_bounds__(256 * NS, (NS == 1 ? DFL_ATTN_OCC : 1)) void attn_s
     else attn_issue<TA, HD>(kr, ring + (t % S) * STG, t, wave, lane);
   };
   if constexpr (KQ8) {
-    // one stream (nloop == ntile).  Tiles 0 .. S-1 fill every stage; at the
-    // top of iteration t tiles up to t+S-1 are issued, tile t+1 has landed
-    // after the barrier, whose other side also orders iteration t-1 (reads
-    // of decoded tile t-1, decode of tile t) before this one.  Stage t % S
-    // was decoded in iteration t-1, so tile t+S refills it.
+    // Tiles 0 .. S-1 fill every stage; at the top of iteration t tiles up
+    // to t+S-1 are issued, tile t+1 has landed after the barrier, whose
+    // other side also orders iteration t-1 (reads of decoded tile t-1,
+    // decode of tile t) before this one.  Stage t % S was decoded in
+    // iteration t-1, so tile t+S refills it.  The stream's 256 threads
+    // decode; past its own tiles a stream only keeps the barriers.
     constexpr int DB = AttnCfg<bf16, kQ8HD>::STAGE;
+    const int stid = tid & 255;
     if (loads) {
 #pragma unroll
       for (int s = 0; s < S; ++s) issue(s);
-      attn_wait_vm<NPW * (S - 1)>();   // tile 0 has landed
-      attn_ring_barrier();
-      attn_decode_q8(ring, dec, tid);
     }
+    attn_wait_vm<NPW * (S - 1)>();   // tile 0 has landed
+    attn_ring_barrier();
+    if (loads) attn_decode_q8(ring, dec, stid);
     for (int tI = 0; tI < nloop; ++tI) {
       attn_wait_vm<NPW * (S - 2)>();   // this wave's loads of tile tI+1 have landed
       attn_ring_barrier();             // ... everyone's; decoded tile tI is complete
-      issue(tI + S);
-      attn_tile<TA, HD, HPW>(dec + (tI & 1) * DB, kr.key0 + (long)tI * kAttnKT, kr.key1, sl2, g, r16, qf,
-                             o, m_run, l_run, active);
-      if (tI + 1 < kr.ntile) attn_decode_q8(ring + ((tI + 1) % S) * STG, dec + ((tI + 1) & 1) * DB, tid);
+      if (loads) issue(tI + S);
+      if (tI < kr.ntile)
+        attn_tile<TA, HD, HPW>(dec + (tI & 1) * DB, kr.key0 + (long)tI * kAttnKT, kr.key1, sl2, g, r16, qf,
+                               o, m_run, l_run, active);
+      if (tI + 1 < kr.ntile) attn_decode_q8(ring + ((tI + 1) % S) * STG, dec + ((tI + 1) & 1) * DB, stid);
     }
   } else {
     if (loads) {
@@ -685,13 +689,17 @@ static hipError_t attn_split_go(const AttnArgs &a, hipStream_t st) {
 }
 
 // Q8_0 cache through the ring: raw stages plus the decoded bf16 tile
+#ifndef DFL_ATTN_Q8_STREAMS
+#define DFL_ATTN_Q8_STREAMS 2   // key streams per workgroup of the Q8_0-cache kernel (1 or 2)
+#endif
 template <int HPW>
 static hipError_t attn_split_q8_go(const AttnArgs &a, hipStream_t st) {
-  const size_t lds = (size_t)kQ8Stages * kQ8Stage + 2 * AttnCfg<bf16, kQ8HD>::STAGE;
-  auto *k = &attn_split_kernel<bf16, kQ8HD, HPW, 1, true>;
+  constexpr int NS = DFL_ATTN_Q8_STREAMS;
+  const size_t lds = (size_t)NS * (kQ8Stages * kQ8Stage + 2 * AttnCfg<bf16, kQ8HD>::STAGE);
+  auto *k = &attn_split_kernel<bf16, kQ8HD, HPW, NS, true>;
   const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3(a.n_split, a.Hkv), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(k, dim3(a.n_split, a.Hkv), dim3(256 * NS), lds, st, a);
   return hipSuccess;
 }
 
@@ -714,8 +722,8 @@ bool attn_q8_ok(int hd, int grp, int B) {
 void attn_plan_call(int act, int hd, int grp, int B, int kvq, long n_keys, int Hkv, int *chunk, int *n_split) {
   (void)grp;
   (void)B;
-  // Q8_0 caches: one stream per workgroup, two workgroups per CU
-  attn_plan(n_keys, Hkv, kvq ? 1 : attn_streams(act, hd), chunk, n_split);
+  // Q8_0 caches: DFL_ATTN_Q8_STREAMS streams per workgroup
+  attn_plan(n_keys, Hkv, kvq ? DFL_ATTN_Q8_STREAMS : attn_streams(act, hd), chunk, n_split);
 }
 
 template <typename TA, int HD>
