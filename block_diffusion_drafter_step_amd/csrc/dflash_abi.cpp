@@ -233,7 +233,7 @@ size_t topk_ws(int64_t V, int32_t K) {
 
 size_t sel_ws(int32_t B, int32_t r, int32_t d) {
   Carve c(nullptr);
-  c.take(gemm_partial_bytes(B, r, d));
+  c.take(std::max(gemm_partial_bytes(B, r, d), selector_part_bytes(r, d)));
   c.take((size_t)B * r * 4);
   return c.off;
 }
@@ -726,12 +726,10 @@ dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
 
   hipStream_t st = (hipStream_t)stream;
   Carve c(ws);
-  float *part = (float *)c.take(gemm_partial_bytes(B, (int)r, (int)d));
+  float *part = (float *)c.take(std::max(gemm_partial_bytes(B, (int)r, (int)d), selector_part_bytes((int)r, (int)d)));
   float *pj = (float *)c.take((size_t)B * r * 4);
-  hipError_t e = gemm(act, W_SAME, asrc1(h, (int)d), B, wset({proj}), part, c.counters, out_f32(pj, r), st);
-  if (e != hipSuccess) return launched(e, "project");
   SelArgs a;
-  a.proj = pj;
+  memset(&a, 0, sizeof a);
   a.cb_pred = cb_pred;
   a.cb_succ = cb_succ;
   a.V = V;
@@ -745,6 +743,21 @@ dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
   a.path = path;
   a.target = target;
   a.accept = accept;
+  a.h = h;
+  a.pw = proj->data;
+  a.d = (int)d;
+  if (selector_fused_fits(act, a)) {
+    // one launch: the projection is formed inside the selector kernel
+    selector_fused_plan(a);
+    a.fused = true;
+    a.part = part;
+    a.cnt = c.counters;
+    if (a.n_wg > 1) a.stamp = next_launch_stamp();
+    return launched(launch_selector(act, a, st), "selector");
+  }
+  hipError_t e = gemm(act, W_SAME, asrc1(h, (int)d), B, wset({proj}), part, c.counters, out_f32(pj, r), st);
+  if (e != hipSuccess) return launched(e, "project");
+  a.proj = pj;
   return launched(launch_selector(act, a, st), "selector");
 }
 

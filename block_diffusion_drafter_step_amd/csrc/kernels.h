@@ -191,7 +191,7 @@ hipError_t launch_rowtopk(const float *x, long n_rows, long n_cols, int K, int32
 
 // ---- selector ------------------------------------------------------------------------
 struct SelArgs {
-  const float *proj;  // [B][r] fp32
+  const float *proj;  // [B][r] fp32 (two-kernel path: formed by a GEMM beforehand)
   const void *cb_pred, *cb_succ;  // [V][r] act type
   long V;
   int r, B, K, anchor;
@@ -201,7 +201,18 @@ struct SelArgs {
   int *path;          // [B]
   const int *target;  // [B] or null: accept = length of the prefix where path == target
   int *accept;        // [1] or null
+  // one-launch path: proj = h . P^T is formed inside the selector kernel
+  bool fused;
+  const void *h, *pw;  // [B][d], [r][d] act type
+  int d, pieces, n_wg; // 128-wide k-pieces per wave; workgroups (k-slices)
+  float *part;         // [n_wg][r/16][64] float4 partial projections
+  unsigned long long *cnt, stamp;   // completion counter (n_wg > 1)
 };
+// Whether the one-launch selector (projection inside) fits in LDS; if so,
+// selector_fused_plan fills pieces and n_wg from B, K, r and d.
+bool selector_fused_fits(int act, const SelArgs &a);
+void selector_fused_plan(SelArgs &a);
+size_t selector_part_bytes(int r, int d);
 hipError_t launch_selector(int act, const SelArgs &a, hipStream_t st);
 
 hipError_t launch_accept(const int *draft, const int *target, int n_seq, int B, int *accept,

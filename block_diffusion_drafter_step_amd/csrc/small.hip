@@ -1,6 +1,8 @@
 // The small kernels of the draft block step: the injection RMSNorm, the
 // DFlash2 grouped dynamic depthwise convolution, the candidate-selector
 // edges with their best-path readout, and the greedy accept length.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -514,52 +516,101 @@ __global__ __launch_bounds__(256) void selector_path_kernel(SelArgs a) {
   }
 }
 
-// The whole selector in one workgroup (used when the candidate rows fit in
-// LDS): gather every position's predecessor rows of A and candidate rows of B
-// with 16-byte loads issued together, form all B x K x K edges (the same
-// arithmetic, in the same order, as selector_edges_kernel; one edge per
-// thread, 16-element chunks of each dot product read from LDS at once), write
-// them, and run the max-sum recursion in one wave: lane b holds state b, its
-// back-pointers and candidate ids in registers, and each step reads its
-// K x K edges from LDS in one batch.
-template <typename TA, int KM>
-__global__ __launch_bounds__(1024) void selector_fused_kernel(SelArgs a) {
+// The whole selector in one launch (used when the candidate rows fit in
+// LDS).  Every workgroup forms a k-slice of proj = h . P^T: wave w streams
+// 16 rows of P (tile w / Q) over piece range q = w % Q of the slice, the
+// pieces of a tile are summed in LDS in order, and the slice is written as a
+// partial.  Every workgroup also gathers each position's predecessor rows of
+// A and candidate rows of B into LDS (16-byte loads issued together), so
+// that the last workgroup to finish (completion counter) finds them there.
+// It sums the slices in slice order (the projection never depends on
+// arrival order), forms all B x K x K edges (one edge per thread, 16-element
+// chunks of each dot product read from LDS at once, the same arithmetic as
+// selector_edges_kernel), writes them, and runs the max-sum recursion in one
+// wave: lane b holds state b and its back-pointers (8 bits per position).
+// The hand-over of the slices follows the skinny GEMMs' (agent-scope
+// stores, release before the arrival, acquire by the last workgroup).
+//
+// The serial part runs once per launch, so its code is kept small (rolled
+// loops over positions): straight-line code executed once waits on
+// instruction fetch for every cache line.
+constexpr int kSelWaves = 16;
+
+template <typename TA, int KM, bool EXACT>
+__global__ __launch_bounds__(kSelWaves * 64) void selector_fused_kernel(SelArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ unsigned last;
   constexpr int EPV = 16 / sizeof(TA);   // elements per 16-byte vector
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int B = a.B, K = a.K, r = a.r, BK = a.B * a.K;
+  constexpr int NT = kSelWaves * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int B = a.B, K = a.K, r = a.r, BK = a.B * a.K, d = a.d;
   const int rs = r + EPV;                // padded LDS row stride (elements)
-  TA *rows = reinterpret_cast<TA *>(smem);            // [2][B*K][rs]: A side, B side
+  f32x4 *red = reinterpret_cast<f32x4 *>(smem);                               // [16][64]
+  TA *rows = reinterpret_cast<TA *>(smem + kSelWaves * 64 * sizeof(f32x4));   // [2][B*K][rs]
   float *pj = reinterpret_cast<float *>(rows + 2 * BK * rs);   // [B][r]
   float *se = pj + B * r;                                      // [B][K][K]
   float *un = se + BK * K;                                     // [B][K]
   int *sidx = reinterpret_cast<int *>(un + BK);                // [B][K]
-  // target token of position `lane` (wave 0), loaded now so that its latency
-  // overlaps the first loads instead of following the best-path pass
-  const int tg = a.target && tid < B ? a.target[tid] : 0;
-  for (int e = tid; e < BK; e += 1024) {
-    sidx[e] = clamp_idx(a.idx[e], a.V);
-    un[e] = a.unary[e];
+
+  // candidate ids, unaries and the target (first: the gathers wait on them)
+  int ix = 0;
+  float uv = 0.f;
+  if (tid < BK) {
+    ix = a.idx[tid];
+    uv = a.unary[tid];
   }
-  for (int e = tid; e < B * r; e += 1024) pj[e] = a.proj[e];
+  const int tg = a.target && tid < B ? a.target[tid] : 0;   // wave 0: position `lane`
+
+  // ---- the workgroup's k-slice of the projection ----
+  const int nt = r >> 4, Q = kSelWaves / nt, span = a.pieces * 128;
+  const int t = wave / Q, q = wave - t * Q;
+  const int k_lo = min(d, ((int)blockIdx.x * Q + q) * span), k_hi = min(d, k_lo + span);
+  f32x4 acc = zero4();
+  if (wave < nt * Q && k_lo < k_hi) {
+    // lane (g, r16): row 16 t + r16 of P and position min(r16, B - 1) of h
+    // (columns r16 >= B of the product are never stored)
+    const TA *wr = reinterpret_cast<const TA *>(a.pw) + (long)(t * 16 + r16) * d;
+    const TA *xr = reinterpret_cast<const TA *>(a.h) + (long)min(r16, B - 1) * d;
+    for (int k = k_lo; k < k_hi; k += 128) {
+      // a piece's four 32-wide steps loaded together; steps past the range
+      // (a 64-wide last piece) reload the range's last step and are not used
+      Frag<TA> wf[4], xf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kc = min(k + 32 * j, k_hi - 32) + 8 * g;
+        wf[j] = load_frag(wr + kc);
+        xf[j] = load_frag(xr + kc);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (k + 32 * j < k_hi) mma(acc, wf[j], xf[j]);
+    }
+  }
+  if (tid < BK) {
+    sidx[tid] = clamp_idx(ix, a.V);
+    un[tid] = uv;
+  }
+  red[wave * 64 + lane] = acc;
   __syncthreads();
 
+  // gathers: rows [0, BK) are predecessor a of position i, A[idx[i-1][a]]
+  // (A[anchor] at i = 0); rows [BK, 2 BK) candidate b of position i,
+  // B[idx[i][b]].  A thread's loads are issued back to back (no branch
+  // around them or their addresses); vectors past the end reload the last
+  // one and store it again (the same bytes to the same place).
   const TA *A = reinterpret_cast<const TA *>(a.cb_pred);
   const TA *Bc = reinterpret_cast<const TA *>(a.cb_succ);
   const int anchor = a.anchor < 0 ? 0 : a.anchor;   // row unused without an anchor
   const int vpr = r / EPV, nvec = 2 * BK * vpr;
   constexpr int UNR = 4;
-  // the loads of a thread are issued back to back: no branch around them or
-  // their addresses; vectors past the end reload the last one and store it
-  // again (the same bytes to the same place)
-  for (int v0 = tid; v0 < nvec; v0 += 1024 * UNR) {
+  for (int v0 = tid; v0 < nvec; v0 += NT * UNR) {
     u32x4 buf[UNR];
 #pragma unroll
     for (int j = 0; j < UNR; ++j) {
-      const int v = min(v0 + 1024 * j, nvec - 1);
-      const int row = v / vpr, part = v - row * vpr;
-      // rows [0, BK): predecessor a of position i, A[idx[i-1][a]] (A[anchor]
-      // at i = 0); rows [BK, 2 BK): candidate b of position i, B[idx[i][b]]
+      const int vv = min(v0 + NT * j, nvec - 1);
+      const int row = vv / vpr, part = vv - row * vpr;
       const bool pred = row < BK;
       const int rr = pred ? row : row - BK;
       const int i = rr / K, ai = rr - i * K;
@@ -569,26 +620,80 @@ __global__ __launch_bounds__(1024) void selector_fused_kernel(SelArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < UNR; ++j) {
-      const int v = min(v0 + 1024 * j, nvec - 1);
-      const int row = v / vpr, part = v - row * vpr;
+      const int vv = min(v0 + NT * j, nvec - 1);
+      const int row = vv / vpr, part = vv - row * vpr;
       *reinterpret_cast<u32x4 *>(rows + row * rs + part * EPV) = buf[j];
     }
   }
+
+  // this slice of the projection: tile `wave`, lane (g, r16)
+  f32x4 v = zero4();
+  if (wave < nt) {
+#pragma unroll 1
+    for (int j = 0; j < Q; ++j) {
+      const f32x4 x = red[(wave * Q + j) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += x[i];
+    }
+  }
+  const int S = gridDim.x;
+  if (S > 1) {
+    const long sstride = (long)nt * 64;   // float4 per slice
+    if (wave < nt) {
+      float *pp = a.part + (((long)blockIdx.x * sstride) + wave * 64 + lane) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) __hip_atomic_store(pp + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // every wave's partial stores (and gathers) have completed before the
+    // arrival counts
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const bool l = arrive_last(a.cnt, a.stamp, S);
+      if (l) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      last = l;
+    }
+    __syncthreads();
+    if (!last) return;
+    if (wave < nt) {
+      // the slices happen-before these loads (release by every arrival,
+      // acquire above), so ordinary 16-byte loads see them; eight in flight
+      const f32x4 *src = reinterpret_cast<const f32x4 *>(a.part) + wave * 64 + lane;
+      v = zero4();
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        f32x4 x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = src[(long)min(s0 + j, S - 1) * sstride];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (s0 + j < S) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] += x[j][i];
+          }
+      }
+    }
+  }
+  // the projection of position r16, features 16 t + 4 g + i
+  if (wave < nt && r16 < B) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pj[r16 * r + wave * 16 + 4 * g + i] = v[i];
+  }
   __syncthreads();
 
-  for (int e = tid; e < BK * K; e += 1024) {
+  for (int e = tid; e < BK * K; e += NT) {
     const int i = e / (K * K), rem = e - i * K * K, ai = rem / K, bi = rem - ai * K;
     const int npred = i == 0 ? (a.anchor < 0 ? 0 : 1) : K;
-    float v;
+    float ev;
     if (i == 0 && ai > 0) {
-      v = -__builtin_inff();
+      ev = -__builtin_inff();
     } else if (npred == 0) {
-      v = un[i * K + bi];
+      ev = un[i * K + bi];
     } else {
       const TA *x = rows + (i * K + ai) * rs;
       const TA *y = rows + (BK + i * K + bi) * rs;
       const float *p = pj + i * r;
-      float acc = 0.f;
+      float s = 0.f;
       for (int k0 = 0; k0 < r; k0 += 16) {   // r is a multiple of 16
         float xv[16], yv[16], pv[16];
 #pragma unroll
@@ -600,100 +705,131 @@ __global__ __launch_bounds__(1024) void selector_fused_kernel(SelArgs a) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const float ap = xv[k] * pv[k];
-          acc += ap * yv[k];
+          s += ap * yv[k];
         }
       }
-      v = acc + un[i * K + bi];
+      ev = s + un[i * K + bi];
     }
-    se[e] = v;
-    a.edges[e] = v;
+    se[e] = ev;
+    a.edges[e] = ev;
   }
   __syncthreads();
   if (wave != 0) return;
 
   // s_0[b] = edge[0][0][b]; s_i[b] = max_a s_{i-1}[a] + edge[i][a][b], the
-  // first (lowest a) maximum wins
-  const int bl = min(lane, K - 1);   // lanes >= K shadow state K-1 (never chosen)
+  // first (lowest a) maximum wins.  Lanes >= K shadow state K-1 (never
+  // chosen).  EXACT (K == KM): no per-candidate bound checks in the loop.
+  const int bl = min(lane, K - 1);
   float sc = se[bl];
-  int backr[kSelMaxB], sidr[kSelMaxB];
-  sidr[0] = sidx[bl];
+  unsigned long long bp0 = 0, bp1 = 0;   // back-pointers, 8 bits per position (0-7, 8-15)
+#pragma unroll 1
+  for (int i = 1; i < B; ++i) {
+    const float *ei = se + i * K * K;
+    float ecol[KM];
 #pragma unroll
-  for (int i = 1; i < kSelMaxB; ++i) {
-    if (i < B) {
-      const float *ei = se + i * K * K;
-      float ecol[KM];
+    for (int qq = 0; qq < KM; ++qq) ecol[qq] = ei[(EXACT ? qq : min(qq, K - 1)) * K + bl];
+    float best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), 0)) + ecol[0];
+    int arg = 0;
 #pragma unroll
-      for (int q = 0; q < KM; ++q) ecol[q] = ei[min(q, K - 1) * K + bl];
-      sidr[i] = sidx[i * K + bl];
-      float best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), 0)) + ecol[0];
-      int arg = 0;
-#pragma unroll
-      for (int q = 1; q < KM; ++q) {
-        if (q < K) {
-          const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), q)) + ecol[q];
-          if (v > best) {
-            best = v;
-            arg = q;
-          }
-        }
+    for (int qq = 1; qq < KM; ++qq) {
+      const float ev = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), qq)) + ecol[qq];
+      if ((EXACT || qq < K) && ev > best) {
+        best = ev;
+        arg = qq;
       }
-      sc = best;
-      backr[i] = arg;
     }
+    sc = best;
+    const unsigned long long bits = (unsigned long long)arg << (8 * (i & 7));
+    if (i < 8) bp0 |= bits;
+    else bp1 |= bits;
   }
   // best final state, the lowest b on ties
-  float bv = lane < K ? sc : -__builtin_inff();
-  int bb = lane < K ? lane : K;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float ov = shfl_xor(bv, o);
-    const int ob = __shfl_xor(bb, o, kWave);
-    if (ov > bv || (ov == bv && ob < bb)) {
-      bv = ov;
-      bb = ob;
+  int b = 0;
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), 0));
+#pragma unroll 1
+  for (int qq = 1; qq < K; ++qq) {
+    const float ev = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), qq));
+    if (ev > bv) {
+      bv = ev;
+      b = qq;
     }
   }
-  int b = __builtin_amdgcn_readfirstlane(bb);
-  int acc = B;   // the first position where the path leaves the target
-#pragma unroll
-  for (int i = kSelMaxB - 1; i >= 0; --i) {
-    if (i < B) {
-      const int id = __builtin_amdgcn_readlane(sidr[i], b);
-      if (lane == 0) a.path[i] = id;
-      if (id != __builtin_amdgcn_readlane(tg, i)) acc = i;
-      if (i > 0) b = __builtin_amdgcn_readlane(backr[i], b);
+  // backtrack: lane i receives the path's state at position i
+  int ps = 0;
+#pragma unroll 1
+  for (int i = B - 1; i >= 0; --i) {
+    ps = lane == i ? b : ps;
+    if (i > 0) {
+      const unsigned long long w = i < 8 ? bp0 : bp1;
+      const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)w, b);
+      const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(w >> 32), b);
+      b = (int)(((((unsigned long long)hi << 32) | lo) >> (8 * (i & 7))) & 0xffu);
     }
   }
-  if (a.accept && lane == 0) a.accept[0] = acc;
+  // lanes < B: the candidate id on the path and the accept length (the
+  // first position where the path leaves the target)
+  const int id = lane < B ? sidx[lane * K + ps] : 0;
+  if (lane < B) a.path[lane] = id;
+  const unsigned long long miss = __ballot(lane < B && id != tg);
+  if (a.accept && lane == 0) a.accept[0] = miss ? (int)__builtin_ctzll(miss) : B;
 }
 
 static size_t selector_fused_lds(int act, const SelArgs &a) {
   const size_t es = act == ACT_F32 ? 4 : 2;
   const size_t bk = (size_t)a.B * a.K;
-  return 2 * bk * (a.r + 16 / es) * es + ((size_t)a.B * a.r + bk * a.K + bk) * 4 + bk * 4;
-}
-
-template <typename TA, int KM>
-static hipError_t selector_fused_go(const SelArgs &a, size_t lds, hipStream_t st) {
-  auto *k = &selector_fused_kernel<TA, KM>;
-  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3(1), dim3(1024), lds, st, a);
-  return hipSuccess;
+  return kSelWaves * 64 * 16 + 2 * bk * (a.r + 16 / es) * es + ((size_t)a.B * a.r + bk * a.K + bk) * 4 +
+         bk * 4;
 }
 
 #ifndef DFL_SEL_FUSED
 #define DFL_SEL_FUSED 1
 #endif
 
+bool selector_fused_fits(int act, const SelArgs &a) {
+  return DFL_SEL_FUSED && a.r % 16 == 0 && a.r / 16 <= kSelWaves && a.d % 64 == 0 &&
+         selector_fused_lds(act, a) + sizeof(unsigned) <= kMaxLdsBytes;
+}
+
+// Q waves per 16-row tile of P, each over `pieces` 128-wide k-pieces; at most
+// 64 workgroups (k-slices)
+void selector_fused_plan(SelArgs &a) {
+  const int nt = a.r / 16, Q = kSelWaves / nt;
+  const int nchunk = (a.d + 127) / 128;
+  a.pieces = std::max(1, (nchunk + Q * 64 - 1) / (Q * 64));
+  a.n_wg = (nchunk + Q * a.pieces - 1) / (Q * a.pieces);
+}
+
+size_t selector_part_bytes(int r, int d) {
+  SelArgs a;
+  a.r = r;
+  a.d = d;
+  selector_fused_plan(a);
+  return (size_t)a.n_wg * (r / 16) * 64 * 16;
+}
+
+template <typename TA, int KM, bool EXACT>
+static hipError_t selector_fused_go(const SelArgs &a, size_t lds, hipStream_t st) {
+  auto *k = &selector_fused_kernel<TA, KM, EXACT>;
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3(a.n_wg), dim3(kSelWaves * 64), lds, st, a);
+  return hipSuccess;
+}
+
 hipError_t launch_selector(int act, const SelArgs &a, hipStream_t st) {
-  const size_t flds = selector_fused_lds(act, a);
-  if (DFL_SEL_FUSED && flds <= kMaxLdsBytes) {
+  if (a.fused) {
+    if (!selector_fused_fits(act, a) || a.n_wg < 1 || a.n_wg > 64 || (a.n_wg > 1 && (!a.part || !a.cnt)))
+      return hipErrorInvalidValue;
+    const size_t flds = selector_fused_lds(act, a);
     hipError_t e;
     if (act == ACT_F32)
-      e = a.K <= 8 ? selector_fused_go<float, 8>(a, flds, st) : selector_fused_go<float, 32>(a, flds, st);
+      e = a.K == 8  ? selector_fused_go<float, 8, true>(a, flds, st)
+          : a.K < 8 ? selector_fused_go<float, 8, false>(a, flds, st)
+                    : selector_fused_go<float, 32, false>(a, flds, st);
     else
-      e = a.K <= 8 ? selector_fused_go<bf16, 8>(a, flds, st) : selector_fused_go<bf16, 32>(a, flds, st);
+      e = a.K == 8  ? selector_fused_go<bf16, 8, true>(a, flds, st)
+          : a.K < 8 ? selector_fused_go<bf16, 8, false>(a, flds, st)
+                    : selector_fused_go<bf16, 32, false>(a, flds, st);
     return e != hipSuccess ? e : hipGetLastError();
   }
   const size_t lds = (size_t)2 * a.K * (a.r + 1) * sizeof(float);
