@@ -180,10 +180,28 @@ size_t inject_ws(int32_t n_layers, int64_t n, int32_t d_t, int32_t d, int32_t kv
   return c.off;
 }
 
+// partial sums of the conv's delta product (either form)
+size_t conv_part_bytes(int M, int C, int G, int T) {
+  return std::max(gemm_partial_bytes(M, T * G, C), conv_fused_part_bytes(M, C, G, T));
+}
+
+// The conv of dflash_conv and of the feed-forward site: at most 16 rows in
+// one launch (delta formed inside), otherwise the delta GEMM then the conv.
+hipError_t run_conv(int32_t act, const void *x, int n_blocks, int B, int C, int G, int T, const void *base,
+                    const dflash_weight *w_delta, void *out, float *part, float *delta,
+                    unsigned long long *counters, hipStream_t st) {
+  const int M = n_blocks * B;
+  if (conv_fused_ok(M, C, G, T))
+    return launch_conv_fused(act, x, n_blocks, B, C, G, T, base, w_delta->data, out, part, counters, st);
+  hipError_t e = gemm(act, W_SAME, asrc1(x, C), M, wset({w_delta}), part, counters, out_f32(delta, T * G), st);
+  if (e != hipSuccess) return e;
+  return launch_conv(act, x, n_blocks, B, C, G, T, base, delta, out, st);
+}
+
 size_t conv_ws(int32_t n_blocks, int32_t B, int32_t C, int32_t G, int32_t T) {
   Carve c(nullptr);
   const int64_t M = (int64_t)n_blocks * B;
-  c.take(gemm_partial_bytes((int)M, T * G, C));
+  c.take(conv_part_bytes((int)M, C, G, T));
   c.take((size_t)M * T * G * 4);  // delta
   return c.off;
 }
@@ -193,7 +211,7 @@ size_t ffn_ws(int32_t n_blocks, int32_t B, int32_t d, int32_t G, int32_t T, int3
               size_t *u_off = nullptr, size_t *act_off = nullptr) {
   Carve c(nullptr);
   const int64_t M = (int64_t)n_blocks * B;
-  c.take(std::max(std::max(gemm_partial_bytes((int)M, T * G, d), gemm_partial_bytes((int)M, 2 * d_ff, d)),
+  c.take(std::max(std::max(conv_part_bytes((int)M, d, G, T), gemm_partial_bytes((int)M, 2 * d_ff, d)),
                   gemm_partial_bytes((int)M, d, d_ff)));
   c.take((size_t)M * T * G * 4);       // delta
   if (u_off) *u_off = c.off;
@@ -472,12 +490,10 @@ dflash_status dflash_conv(const void *x, int32_t n_blocks, int32_t B, int32_t C,
   hipStream_t st = (hipStream_t)stream;
   Carve c(ws);
   const int M = n_blocks * B;
-  float *part = (float *)c.take(gemm_partial_bytes(M, T * G, C));
+  float *part = (float *)c.take(conv_part_bytes(M, C, G, T));
   float *delta = (float *)c.take((size_t)M * T * G * 4);
-  hipError_t e = gemm(act, W_SAME, asrc1(x, C), M, wset({w_delta}), part, c.counters, out_f32(delta, T * G), st);
-  if (e != hipSuccess) return launched(e, "delta");
-  e = launch_conv(act, x, n_blocks, B, C, G, T, base, delta, out, st);
-  return launched(e, "conv");
+  return launched(run_conv(act, x, n_blocks, B, C, G, T, base, w_delta, out, part, delta, c.counters, st),
+                  "conv");
 }
 
 dflash_status dflash_ffn_block(const void *h, int32_t n_blocks, int32_t B, int32_t d, int32_t G,
@@ -512,16 +528,14 @@ dflash_status dflash_ffn_block(const void *h, int32_t n_blocks, int32_t B, int32
   hipStream_t st = (hipStream_t)stream;
   Carve c(ws);
   const int M = n_blocks * B, F = (int)d_ff;
-  float *part = (float *)c.take(std::max(std::max(gemm_partial_bytes(M, T * G, d), gemm_partial_bytes(M, 2 * F, d)),
+  float *part = (float *)c.take(std::max(std::max(conv_part_bytes(M, d, G, T), gemm_partial_bytes(M, 2 * F, d)),
                                          gemm_partial_bytes(M, d, F)));
   float *delta = (float *)c.take((size_t)M * T * G * 4);
   void *u = c.take((size_t)M * d * 4);
   float *gu = (float *)c.take((size_t)M * 2 * F * 4);
   void *av = c.take((size_t)M * F * 4);
   // the feed-forward site's conv: the same kernels as dflash_conv
-  hipError_t e = gemm(act, W_SAME, asrc1(h, d), M, wset({w_delta}), part, c.counters, out_f32(delta, T * G), st);
-  if (e != hipSuccess) return launched(e, "ffn delta");
-  e = launch_conv(act, h, n_blocks, B, d, G, T, base, delta, u, st);
+  hipError_t e = run_conv(act, h, n_blocks, B, d, G, T, base, w_delta, u, part, delta, c.counters, st);
   if (e != hipSuccess) return launched(e, "ffn conv");
   e = gemm(act, wkind_of(w_gate), asrc1(u, d), M, wset({w_gate, w_up}), part, c.counters, out_f32(gu, 2 * F), st);
   if (e != hipSuccess) return launched(e, "gate/up");

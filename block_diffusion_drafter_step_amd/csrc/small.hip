@@ -5,6 +5,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "stream.h"
 
 namespace dfl {
 
@@ -400,6 +401,193 @@ static void conv_launch_t(const void *x, int n_blocks, int B, int C, int G, int 
     conv_launch_bm<TA, 8>(grid, xp, n_blocks, B, C, G, T, bp, delta, op, st);
   else
     conv_launch_bm<TA, 16>(grid, xp, n_blocks, B, C, G, T, bp, delta, op, st);
+}
+
+// ---------------------------------------------------------------------------
+// One block's conv in one launch.  A tile is gpt = 16 / T groups: its 16
+// MFMA rows are the W_delta rows t*G + g of those groups (lane row r16 =
+// (g - g0) * T + t; rows past gpt * T re-read row t*G + g0 and are dropped),
+// so a tile holds every tap of its groups.  Workgroup (tile, y): its 8 waves
+// stream consecutive k-ranges of kchunk, summed in LDS in a fixed pairwise
+// order; with several k-groups each writes a partial and the last to finish
+// (completion counter cnt[tile]) sums them in k-group order, as the small
+// skinny GEMMs do.  That workgroup then applies the taps to the tile's
+// columns: one thread per (row, 8 columns), the same arithmetic in the same
+// order as conv_pos_kernel.
+// ---------------------------------------------------------------------------
+struct ConvFusedArgs {
+  const void *x, *base, *wd;
+  void *out;
+  float *part;
+  unsigned long long *cnt, stamp;
+  int M, B, C, G, T, gpt, kchunk;
+};
+
+constexpr int kConvFusedWaves = 8;
+
+static void conv_fused_plan(int C, int G, int T, int *gpt, int *ntile, int *kchunk, int *kgroups) {
+  *gpt = std::max(1, 16 / T);
+  *ntile = (G + *gpt - 1) / *gpt;
+  int kw = (2048 + *ntile - 1) / *ntile;   // waves per tile
+  const int kw_max = (C + 127) / 128;
+  kw = std::max(kConvFusedWaves, std::min(kw, kw_max));
+  int kc = (C + kw - 1) / kw;
+  kc = std::max(128, (kc + 63) / 64 * 64);
+  *kchunk = kc;
+  *kgroups = (C + kConvFusedWaves * kc - 1) / (kConvFusedWaves * kc);
+}
+
+bool conv_fused_ok(int M, int C, int G, int T) { return M <= 16 && (C / G) % 8 == 0 && T <= 16; }
+
+size_t conv_fused_part_bytes(int M, int C, int G, int T) {
+  if (!conv_fused_ok(M, C, G, T)) return 0;
+  int gpt, ntile, kc, kg;
+  conv_fused_plan(C, G, T, &gpt, &ntile, &kc, &kg);
+  return kg > 1 ? (size_t)kg * ntile * 64 * sizeof(f32x4) : 0;
+}
+
+template <typename TA>
+__global__ __launch_bounds__(kConvFusedWaves * 64) void conv_fused_kernel(ConvFusedArgs a) {
+  __shared__ f32x4 red[kConvFusedWaves][64];
+  __shared__ float dl[16][16];   // delta of the tile: [row][lane row r16]
+  __shared__ unsigned last;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int M = a.M, C = a.C, G = a.G, T = a.T, gpt = a.gpt;
+  const int tile = blockIdx.x, g0 = tile * gpt;
+  const int ng = min(gpt, G - g0);   // groups of this tile
+  // this lane's W_delta row
+  const int gl = r16 / T, tl = r16 - gl * T;
+  const int wrow = tl * G + g0 + (gl < ng ? gl : 0);
+  const int k0 = (blockIdx.y * kConvFusedWaves + wave) * a.kchunk, k1 = min(C, k0 + a.kchunk);
+  f32x4 acc[1] = {zero4()};
+  if (k0 < k1) {
+    const SRow<TA, W_SAME> rows[1] = {srow<TA, W_SAME>(a.wd, nullptr, wrow, C)};
+    const TA *xr = reinterpret_cast<const TA *>(a.x) + (long)min(r16, M - 1) * C;
+    stream_k<TA, W_SAME, 1>(xr, rows, 1, k0, k1, g, r16 < M, acc);
+  }
+  red[wave][lane] = acc[0];
+  __syncthreads();
+  f32x4 v = zero4();
+  if (wave == 0) {
+    f32x4 t[kConvFusedWaves];
+#pragma unroll
+    for (int w = 0; w < kConvFusedWaves; ++w) t[w] = red[w][lane];
+#pragma unroll
+    for (int h = kConvFusedWaves / 2; h >= 1; h /= 2)
+#pragma unroll
+      for (int w = 0; w < h; ++w)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[w][i] += t[w + h][i];
+    v = t[0];
+  }
+  const int nky = gridDim.y;
+  if (nky > 1) {
+    const long tstride = (long)gridDim.x * 64;   // float4 per k-group
+    if (wave == 0) {
+      float *pp = a.part + (((long)blockIdx.y * tstride) + (long)tile * 64 + lane) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) __hip_atomic_store(pp + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the partial stores have completed before the arrival counts
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const bool l = arrive_last(&a.cnt[tile], a.stamp, nky);
+      if (l) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      last = l;
+    }
+    __syncthreads();
+    if (!last) return;
+    if (wave == 0) {
+      // the partials happen-before these loads (release by every arrival,
+      // acquire above): ordinary 16-byte loads, eight in flight
+      const f32x4 *src = reinterpret_cast<const f32x4 *>(a.part) + (long)tile * 64 + lane;
+      v = zero4();
+      for (int y0 = 0; y0 < nky; y0 += 8) {
+        f32x4 x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = src[(long)min(y0 + j, nky - 1) * tstride];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (y0 + j < nky) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] += x[j][i];
+          }
+      }
+    }
+  }
+  // lane (g, r16) holds delta[row r16][lane row 4 g + i]
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dl[r16][4 * g + i] = v[i];
+  }
+  __syncthreads();
+
+  // the taps on this tile's columns [g0 cpg, (g0 + ng) cpg): one thread per
+  // (row, 8 columns of one group)
+  const int cpg = C / G, vpg = cpg >> 3, nvec = M * ng * vpg;
+  const TA *xp = reinterpret_cast<const TA *>(a.x);
+  const TA *bp = reinterpret_cast<const TA *>(a.base);
+  for (int e = tid; e < nvec; e += kConvFusedWaves * 64) {
+    const int row = e / (ng * vpg), rem = e - row * (ng * vpg), gq = rem / vpg;
+    const int c = (g0 + gq) * cpg + (rem - gq * vpg) * 8;
+    const int i = row % a.B;
+    float o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // taps in fours, their loads issued together; t ascending
+    for (int t0 = 0; t0 < T; t0 += 4) {
+      Frag<TA> xr[4], bv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = min(t0 + u, T - 1), tt = min(t, i);   // taps past T or the block start: valid rows, unused
+        xr[u] = load_frag(xp + (long)(row - tt) * C + c);
+        bv[u] = load_frag(bp + (long)t * C + c);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + u;
+        if (t < T && t <= i) {
+          const float dv = dl[row][gq * T + t];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o8[j] += (to_f32(bv[u].v[j]) + dv) * to_f32(xr[u].v[j]);
+        }
+      }
+    }
+    Frag<TA> o;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o.v[j] = from_f32<TA>(o8[j]);
+    store_frag(reinterpret_cast<TA *>(a.out) + (long)row * C + c, o);
+  }
+}
+
+hipError_t launch_conv_fused(int act, const void *x, int n_blocks, int B, int C, int G, int T,
+                             const void *base, const void *wd, void *out, float *part,
+                             unsigned long long *cnt, hipStream_t st) {
+  const int M = n_blocks * B;
+  if (!conv_fused_ok(M, C, G, T)) return hipErrorInvalidValue;
+  ConvFusedArgs a;
+  int ntile, kg;
+  conv_fused_plan(C, G, T, &a.gpt, &ntile, &a.kchunk, &kg);
+  if (kg > 1 && (!part || !cnt || ntile > kMaxCounters)) return hipErrorInvalidValue;
+  a.x = x;
+  a.base = base;
+  a.wd = wd;
+  a.out = out;
+  a.part = part;
+  a.cnt = cnt;
+  a.stamp = kg > 1 ? next_launch_stamp() : 0;
+  a.M = M;
+  a.B = B;
+  a.C = C;
+  a.G = G;
+  a.T = T;
+  if (act == ACT_F32)
+    hipLaunchKernelGGL(conv_fused_kernel<float>, dim3(ntile, kg), dim3(kConvFusedWaves * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL(conv_fused_kernel<bf16>, dim3(ntile, kg), dim3(kConvFusedWaves * 64), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_conv(int act, const void *x, int n_blocks, int B, int C, int G, int T,

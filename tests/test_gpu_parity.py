@@ -260,6 +260,21 @@ def test_conv_group_spans_and_long_filters():
     run_conv(cfg_small(0, C=256, G=8, T=6, B=16), 600, tag="conv6b")
 
 
+def test_conv_one_launch_shapes():
+    """At most 16 rows with whole 8-channel chunks per group take the
+    one-launch kernel (delta formed per tile of groups, the last workgroup
+    of a tile applies the taps): T = 16 (one group per tile), T = 5 and 3
+    (tiles of 3 and 5 groups, 15 of 16 rows used, a short last tile), two
+    blocks of 8, fp32, and the Qwen-27B width with one k-group per wave
+    pair."""
+    run_conv(cfg_small(1, C=128, G=16, T=16, B=16), 1, tag="conv1l16")
+    run_conv(cfg_small(1, C=512, G=16, T=5, B=16), 1, tag="conv1l5")
+    run_conv(cfg_small(0, C=256, G=16, T=3, B=16), 1, tag="conv1l3")
+    run_conv(cfg_small(1, C=1024, G=32, T=4, B=8), 2, tag="conv1l2b")
+    run_conv(cfg_small(0, C=256, G=8, T=6, B=16), 1, tag="conv1lf")
+    run_conv(configs.get(2), 1, tag="conv1lq")
+
+
 def test_conv_batched_32k_tokens():
     """2048 blocks of 16 (32768 tokens, the 32k workload's token count) at
     the Qwen-27B width, checked on every output; then 2050 blocks, whose
