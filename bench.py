@@ -468,7 +468,7 @@ def kernel_profile(cfg, calls, n_ctx, kvt=None, steps=20):
         return sum(v[1] for k, v in avg.items() if sub in k)
 
     out = {"steps": steps, "avg_us": {k[:90]: round(v[1], 2) for k, v in sorted(avg.items(), key=lambda kv: -kv[1][1] * kv[1][0])}}
-    split, comb = us("attn_split_kernel") + us("attn_q8_kernel"), us("attn_combine_kernel")
+    split, comb = us("attn_split_kernel"), us("attn_combine_kernel")
     lm, merge = us("lmhead_topk"), us("topk_merge_kernel")
     if split + comb > 0:
         kv = workmodel.attn_kv_bytes(cfg, n_ctx, kvt)
