@@ -818,6 +818,17 @@ def test_selector_no_anchor_and_wide_k():
     run_selector(cfg_small(1, K=16, B=16, r=64), tag="selK16")
 
 
+def test_selector_one_launch_slices():
+    """The one-launch selector's k-slices of the projection: d with a
+    64-wide last piece (5184 = 40.5 pieces of 128), r = 48 (three P tiles of
+    five waves each), d = 64 (one 64-wide piece, one workgroup), and fp32
+    activations over several slices."""
+    run_selector(cfg_small(1, d=5184), tag="sel1l1")
+    run_selector(cfg_small(1, r=48, d=1024), tag="sel1l2")
+    run_selector(cfg_small(1, d=64, r=16), tag="sel1l3")
+    run_selector(cfg_small(0, d=2112), tag="sel1l4")
+
+
 def test_selector_garbage_workspace():
     run_selector(configs.get(1), tag="selg", garbage_seed=9)
 
