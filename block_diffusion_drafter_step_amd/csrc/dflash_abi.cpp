@@ -638,11 +638,10 @@ dflash_status topk_check(const void *h, int32_t B, int32_t act, const dflash_wei
   return DFLASH_OK;
 }
 
-// carve `ws` (at least topk_ws(V, K) bytes) and enqueue the LM head + merge
-dflash_status topk_enqueue(const void *h, int32_t B, int32_t act, const dflash_weight *lm_head, int32_t K,
-                           int32_t *idx, float *unary, void *ws, void *stream) {
+// the LM head's arguments, its partial lists carved from `c`
+TopkArgs topk_setup(const void *h, int32_t B, int32_t act, const dflash_weight *lm_head, int32_t K,
+                    int32_t *idx, float *unary, Carve &c) {
   const int64_t V = lm_head->rows, d = lm_head->cols;
-  Carve c(ws);
   TopkArgs a;
   memset(&a, 0, sizeof a);
   a.h = h;
@@ -672,7 +671,94 @@ dflash_status topk_enqueue(const void *h, int32_t B, int32_t act, const dflash_w
   a.part_ms = (float *)c.take((size_t)a.n_wg * 16 * 2 * 4);
   a.idx = idx;
   a.unary = unary;
+  return a;
+}
+
+// carve `ws` (at least topk_ws(V, K) bytes) and enqueue the LM head + merge
+dflash_status topk_enqueue(const void *h, int32_t B, int32_t act, const dflash_weight *lm_head, int32_t K,
+                           int32_t *idx, float *unary, void *ws, void *stream) {
+  Carve c(ws);
+  const TopkArgs a = topk_setup(h, B, act, lm_head, K, idx, unary, c);
   return launched(launch_topk(act, wkind_of(lm_head), a, (hipStream_t)stream), "topk");
+}
+
+dflash_status sel_check(const void *h, int32_t B, int32_t act, const dflash_weight *proj, const void *cb_pred,
+                        const void *cb_succ, int64_t V, const int32_t *idx, const float *unary, int32_t K,
+                        int32_t anchor, float *edges, int32_t *path, const int32_t *target, int32_t *accept) {
+  TRY(check_act(act));
+  TRY(need_ptr(h, "h"));
+  TRY(need_ptr(cb_pred, "cb_pred"));
+  TRY(need_ptr(cb_succ, "cb_succ"));
+  TRY(need_ptr(idx, "idx"));
+  TRY(need_ptr(unary, "unary"));
+  TRY(need_ptr(edges, "edges"));
+  TRY(need_ptr(path, "path"));
+  if ((target == nullptr) != (accept == nullptr))
+    return fail(DFLASH_ERR_INVALID_ARG, "target and accept must be both given or both NULL");
+  if (target) {
+    TRY(need_ptr(target, "target"));
+    TRY(need_ptr(accept, "accept"));
+  }
+  if (B < 1 || B > DFLASH_MAX_BLOCK)
+    return fail(DFLASH_ERR_INVALID_ARG, "B must be in [1, %d]", DFLASH_MAX_BLOCK);
+  if (K < 1 || K > DFLASH_MAX_TOPK)
+    return fail(DFLASH_ERR_INVALID_ARG, "K must be in [1, %d]", DFLASH_MAX_TOPK);
+  if (!proj) return fail(DFLASH_ERR_INVALID_ARG, "proj is NULL");
+  const int64_t r = proj->rows, d = proj->cols;
+  if (r < 16 || r % 16 || r > 256) return fail(DFLASH_ERR_INVALID_ARG, "r must be a multiple of 16 in [16, 256]");
+  if (d < 64 || d % 64) return fail(DFLASH_ERR_INVALID_ARG, "d must be a positive multiple of 64");
+  TRY(check_weight(proj, "proj", r, d, act, false));
+  if (V < K || V >= ((int64_t)1 << 31)) return fail(DFLASH_ERR_INVALID_ARG, "V must be in [K, 2^31)");
+  if (anchor < -1 || anchor >= V) return fail(DFLASH_ERR_INVALID_ARG, "anchor must be in [-1, V)");
+  return DFLASH_OK;
+}
+
+// the selector's arguments, its buffers carved from `c` (sel_ws bytes)
+SelArgs sel_setup(const void *h, int32_t B, const dflash_weight *proj, const void *cb_pred, const void *cb_succ,
+                  int64_t V, const int32_t *idx, const float *unary, int32_t K, int32_t anchor, float *edges,
+                  int32_t *path, const int32_t *target, int32_t *accept, Carve &c, float **pj) {
+  const int64_t r = proj->rows, d = proj->cols;
+  SelArgs a;
+  memset(&a, 0, sizeof a);
+  a.part = (float *)c.take(std::max(gemm_partial_bytes(B, (int)r, (int)d), selector_part_bytes((int)r, (int)d)));
+  *pj = (float *)c.take((size_t)B * r * 4);
+  a.cb_pred = cb_pred;
+  a.cb_succ = cb_succ;
+  a.V = V;
+  a.r = (int)r;
+  a.B = B;
+  a.K = K;
+  a.anchor = anchor;
+  a.idx = idx;
+  a.unary = unary;
+  a.edges = edges;
+  a.path = path;
+  a.target = target;
+  a.accept = accept;
+  a.h = h;
+  a.pw = proj->data;
+  a.d = (int)d;
+  a.cnt = c.counters;
+  return a;
+}
+
+// the selector (projection, edges, path, accept) on arguments from sel_setup
+dflash_status sel_enqueue(int32_t act, SelArgs a, const dflash_weight *proj, float *pj, hipStream_t st) {
+  if (selector_fused_fits(act, a)) {
+    // one launch: the projection is formed inside the selector kernel
+    selector_fused_plan(a);
+    a.fused = true;
+    if (a.n_wg > 1) a.stamp = next_launch_stamp();
+    return launched(launch_selector(act, a, st), "selector");
+  }
+  hipError_t e = gemm(act, W_SAME, asrc1(a.h, a.d), a.B, wset({proj}), a.part, a.cnt, out_f32(pj, a.r), st);
+  if (e != hipSuccess) return launched(e, "project");
+  a.proj = pj;
+  return launched(launch_selector(act, a, st), "selector");
+}
+
+size_t topk_select_ws(int32_t B, int64_t V, int32_t K, int32_t r, int32_t d) {
+  return topk_ws(V, K) + sel_ws(B, r, d);
 }
 
 static_assert(DFLASH_TOPK_NOALLOC_SCRATCH_BYTES == kTopkScratchBytes, "header and library agree");
@@ -710,69 +796,49 @@ dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
                                     const float *unary, int32_t K, int32_t anchor, float *edges,
                                     int32_t *path, const int32_t *target, int32_t *accept, void *ws,
                                     size_t ws_bytes, void *stream) {
-  TRY(check_act(act));
-  TRY(need_ptr(h, "h"));
-  TRY(need_ptr(cb_pred, "cb_pred"));
-  TRY(need_ptr(cb_succ, "cb_succ"));
-  TRY(need_ptr(idx, "idx"));
-  TRY(need_ptr(unary, "unary"));
-  TRY(need_ptr(edges, "edges"));
-  TRY(need_ptr(path, "path"));
-  if ((target == nullptr) != (accept == nullptr))
-    return fail(DFLASH_ERR_INVALID_ARG, "target and accept must be both given or both NULL");
-  if (target) {
-    TRY(need_ptr(target, "target"));
-    TRY(need_ptr(accept, "accept"));
-  }
-  if (B < 1 || B > DFLASH_MAX_BLOCK)
-    return fail(DFLASH_ERR_INVALID_ARG, "B must be in [1, %d]", DFLASH_MAX_BLOCK);
-  if (K < 1 || K > DFLASH_MAX_TOPK)
-    return fail(DFLASH_ERR_INVALID_ARG, "K must be in [1, %d]", DFLASH_MAX_TOPK);
-  if (!proj) return fail(DFLASH_ERR_INVALID_ARG, "proj is NULL");
-  const int64_t r = proj->rows, d = proj->cols;
-  if (r < 16 || r % 16 || r > 256) return fail(DFLASH_ERR_INVALID_ARG, "r must be a multiple of 16 in [16, 256]");
-  if (d < 64 || d % 64) return fail(DFLASH_ERR_INVALID_ARG, "d must be a positive multiple of 64");
-  TRY(check_weight(proj, "proj", r, d, act, false));
-  if (V < K || V >= ((int64_t)1 << 31)) return fail(DFLASH_ERR_INVALID_ARG, "V must be in [K, 2^31)");
-  if (anchor < -1 || anchor >= V) return fail(DFLASH_ERR_INVALID_ARG, "anchor must be in [-1, V)");
-  const size_t need = sel_ws(B, (int)r, (int)d);
-  TRY(check_ws(ws, ws_bytes, need));
+  TRY(sel_check(h, B, act, proj, cb_pred, cb_succ, V, idx, unary, K, anchor, edges, path, target, accept));
+  TRY(check_ws(ws, ws_bytes, sel_ws(B, (int)proj->rows, (int)proj->cols)));
+  Carve c(ws);
+  float *pj;
+  const SelArgs a = sel_setup(h, B, proj, cb_pred, cb_succ, V, idx, unary, K, anchor, edges, path, target, accept,
+                              c, &pj);
+  return sel_enqueue(act, a, proj, pj, (hipStream_t)stream);
+}
 
+size_t dflash_topk_select_workspace(int32_t B, int64_t V, int32_t K, int32_t r, int32_t d) {
+  if (B < 1 || B > DFLASH_MAX_BLOCK || V < 1 || V >= ((int64_t)1 << 31) || K < 1 || K > DFLASH_MAX_TOPK ||
+      K > V || r < 16 || r % 16 || r > 256 || d < 64 || d % 64)
+    return 0;
+  return topk_select_ws(B, V, K, r, d);
+}
+
+dflash_status dflash_topk_select(const void *h, int32_t B, int32_t act, const dflash_weight *lm_head,
+                                 int32_t K, const dflash_weight *proj, const void *cb_pred,
+                                 const void *cb_succ, int32_t anchor, int32_t *idx, float *unary,
+                                 float *edges, int32_t *path, const int32_t *target, int32_t *accept,
+                                 void *ws, size_t ws_bytes, void *stream) {
+  TRY(topk_check(h, B, act, lm_head, K, idx, unary));
+  const int64_t V = lm_head->rows;
+  TRY(sel_check(h, B, act, proj, cb_pred, cb_succ, V, idx, unary, K, anchor, edges, path, target, accept));
+  if (proj->cols != lm_head->cols) return fail(DFLASH_ERR_INVALID_ARG, "proj and lm_head must share d");
+  TRY(check_ws(ws, ws_bytes, topk_select_ws(B, V, K, (int)proj->rows, (int)proj->cols)));
   hipStream_t st = (hipStream_t)stream;
   Carve c(ws);
-  float *part = (float *)c.take(std::max(gemm_partial_bytes(B, (int)r, (int)d), selector_part_bytes((int)r, (int)d)));
-  float *pj = (float *)c.take((size_t)B * r * 4);
-  SelArgs a;
-  memset(&a, 0, sizeof a);
-  a.cb_pred = cb_pred;
-  a.cb_succ = cb_succ;
-  a.V = V;
-  a.r = (int)r;
-  a.B = B;
-  a.K = K;
-  a.anchor = anchor;
-  a.idx = idx;
-  a.unary = unary;
-  a.edges = edges;
-  a.path = path;
-  a.target = target;
-  a.accept = accept;
-  a.h = h;
-  a.pw = proj->data;
-  a.d = (int)d;
-  if (selector_fused_fits(act, a)) {
-    // one launch: the projection is formed inside the selector kernel
+  const TopkArgs ta = topk_setup(h, B, act, lm_head, K, idx, unary, c);
+  float *pj;
+  SelArgs a = sel_setup(h, B, proj, cb_pred, cb_succ, V, idx, unary, K, anchor, edges, path, target, accept, c,
+                        &pj);
+  if (topk_select_ok(act, ta, a)) {
+    // the LM head's partial lists, then its merge and the selector in one launch
     selector_fused_plan(a);
     a.fused = true;
-    a.part = part;
-    a.cnt = c.counters;
-    if (a.n_wg > 1) a.stamp = next_launch_stamp();
-    return launched(launch_selector(act, a, st), "selector");
+    a.stamp = next_launch_stamp();
+    hipError_t e = launch_topk_partials(act, wkind_of(lm_head), ta, st);
+    if (e != hipSuccess) return launched(e, "topk");
+    return launched(launch_topk_select(act, ta, a, st), "topk + selector");
   }
-  hipError_t e = gemm(act, W_SAME, asrc1(h, (int)d), B, wset({proj}), part, c.counters, out_f32(pj, r), st);
-  if (e != hipSuccess) return launched(e, "project");
-  a.proj = pj;
-  return launched(launch_selector(act, a, st), "selector");
+  TRY(launched(launch_topk(act, wkind_of(lm_head), ta, st), "topk"));
+  return sel_enqueue(act, a, proj, pj, st);
 }
 
 size_t dflash_topk_rows_workspace(int64_t n_rows, int64_t n_cols, int32_t K) {

@@ -225,6 +225,14 @@ bool selector_fused_fits(int act, const SelArgs &a);
 void selector_fused_plan(SelArgs &a);
 size_t selector_part_bytes(int r, int d);
 hipError_t launch_selector(int act, const SelArgs &a, hipStream_t st);
+// The LM head's partial lists only (the h-resident kernel, K <= 8); their
+// merge is left to launch_topk_select.
+hipError_t launch_topk_partials(int act, int wkind, const TopkArgs &a, hipStream_t st);
+// The LM head's final merge and the one-launch selector in one kernel, after
+// launch_topk_partials: applies when topk_select_ok; `a` planned by
+// selector_fused_plan, with its counter and a fresh stamp.
+bool topk_select_ok(int act, const TopkArgs &ta, const SelArgs &a);
+hipError_t launch_topk_select(int act, const TopkArgs &ta, const SelArgs &a, hipStream_t st);
 
 hipError_t launch_accept(const int *draft, const int *target, int n_seq, int B, int *accept,
                          hipStream_t st);

@@ -5,6 +5,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "merge.h"
 #include "stream.h"
 
 namespace dfl {
@@ -723,38 +724,42 @@ __global__ __launch_bounds__(256) void selector_path_kernel(SelArgs a) {
 // loops over positions): straight-line code executed once waits on
 // instruction fetch for every cache line.
 constexpr int kSelWaves = 16;
+constexpr int kSelThreads = kSelWaves * 64;
 
-template <typename TA, int KM, bool EXACT>
-__global__ __launch_bounds__(kSelWaves * 64) void selector_fused_kernel(SelArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ unsigned last;
-  constexpr int EPV = 16 / sizeof(TA);   // elements per 16-byte vector
-  constexpr int NT = kSelWaves * 64;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, r16 = lane & 15;
-  const int B = a.B, K = a.K, r = a.r, BK = a.B * a.K, d = a.d;
-  const int rs = r + EPV;                // padded LDS row stride (elements)
-  f32x4 *red = reinterpret_cast<f32x4 *>(smem);                               // [16][64]
-  TA *rows = reinterpret_cast<TA *>(smem + kSelWaves * 64 * sizeof(f32x4));   // [2][B*K][rs]
-  float *pj = reinterpret_cast<float *>(rows + 2 * BK * rs);   // [B][r]
-  float *se = pj + B * r;                                      // [B][K][K]
-  float *un = se + BK * K;                                     // [B][K]
-  int *sidx = reinterpret_cast<int *>(un + BK);                // [B][K]
-
-  // candidate ids, unaries and the target (first: the gathers wait on them)
-  int ix = 0;
-  float uv = 0.f;
-  if (tid < BK) {
-    ix = a.idx[tid];
-    uv = a.unary[tid];
+// the selector's LDS: tile sums, gathered rows, projection, edges, unaries, ids
+template <typename TA>
+struct SelLds {
+  static constexpr int EPV = 16 / sizeof(TA);   // elements per 16-byte vector
+  f32x4 *red;     // [16][64]
+  TA *rows;       // [2][B*K][rs]
+  float *pj;      // [B][r]
+  float *se;      // [B][K][K]
+  float *un;      // [B][K]
+  int *sidx;      // [B][K]
+  int rs;         // padded row stride (elements)
+  __device__ SelLds(unsigned char *smem, const SelArgs &a) {
+    const int BK = a.B * a.K;
+    rs = a.r + EPV;
+    red = reinterpret_cast<f32x4 *>(smem);
+    rows = reinterpret_cast<TA *>(smem + kSelThreads * sizeof(f32x4));
+    pj = reinterpret_cast<float *>(rows + 2 * BK * rs);
+    se = pj + a.B * a.r;
+    un = se + BK * a.K;
+    sidx = reinterpret_cast<int *>(un + BK);
   }
-  const int tg = a.target && tid < B ? a.target[tid] : 0;   // wave 0: position `lane`
+};
 
-  // ---- the workgroup's k-slice of the projection ----
-  const int nt = r >> 4, Q = kSelWaves / nt, span = a.pieces * 128;
+// This wave's share of slice `slice` of the projection: tile t = wave / Q of
+// P over piece range q = wave % Q (zero for waves past nt * Q).
+template <typename TA>
+__device__ __forceinline__ f32x4 sel_product(const SelArgs &a, int slice) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int B = a.B, d = a.d;
+  const int nt = a.r >> 4, Q = kSelWaves / nt, span = a.pieces * 128;
   const int t = wave / Q, q = wave - t * Q;
-  const int k_lo = min(d, ((int)blockIdx.x * Q + q) * span), k_hi = min(d, k_lo + span);
+  const int k_lo = min(d, (slice * Q + q) * span), k_hi = min(d, k_lo + span);
   f32x4 acc = zero4();
   if (wave < nt * Q && k_lo < k_hi) {
     // lane (g, r16): row 16 t + r16 of P and position min(r16, B - 1) of h
@@ -776,18 +781,97 @@ __global__ __launch_bounds__(kSelWaves * 64) void selector_fused_kernel(SelArgs 
         if (k + 32 * j < k_hi) mma(acc, wf[j], xf[j]);
     }
   }
-  if (tid < BK) {
-    sidx[tid] = clamp_idx(ix, a.V);
-    un[tid] = uv;
-  }
+  return acc;
+}
+
+// The slice's tile sums (pieces added in order): thread (wave < nt, lane)
+// holds tile `wave`, lane (g, r16).  Ends with the workgroup barrier that
+// publishes what was written to LDS before it.
+__device__ __forceinline__ f32x4 sel_tile_sum(f32x4 *red, f32x4 acc, int r) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nt = r >> 4, Q = kSelWaves / nt;
   red[wave * 64 + lane] = acc;
   __syncthreads();
+  f32x4 v = zero4();
+  if (wave < nt) {
+#pragma unroll 1
+    for (int j = 0; j < Q; ++j) {
+      const f32x4 x = red[(wave * Q + j) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += x[i];
+    }
+  }
+  return v;
+}
 
-  // gathers: rows [0, BK) are predecessor a of position i, A[idx[i-1][a]]
-  // (A[anchor] at i = 0); rows [BK, 2 BK) candidate b of position i,
-  // B[idx[i][b]].  A thread's loads are issued back to back (no branch
-  // around them or their addresses); vectors past the end reload the last
-  // one and store it again (the same bytes to the same place).
+// slice `slice` of the projection into the partials (waves < nt), agent scope
+__device__ __forceinline__ void sel_store_slice(const SelArgs &a, int slice, f32x4 v) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nt = a.r >> 4;
+  if (wave < nt) {
+    float *pp = a.part + (((long)slice * nt + wave) * 64 + lane) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __hip_atomic_store(pp + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The arrival of a workgroup (its stores completed first); true in the last
+// of `n` to arrive, which has acquired every earlier release
+__device__ __forceinline__ bool sel_arrive(unsigned long long *cnt, unsigned long long stamp, int n) {
+  __shared__ unsigned last;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const bool l = arrive_last(cnt, stamp, n);
+    if (l) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    last = l;
+  }
+  __syncthreads();
+  return last;
+}
+
+// the S slices summed in slice order (waves < nt); the slices happen-before
+// these loads (release by every arrival, acquire by this workgroup), so
+// ordinary 16-byte loads see them, eight in flight
+__device__ __forceinline__ f32x4 sel_sum_slices(const SelArgs &a, int S) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nt = a.r >> 4;
+  const long sstride = (long)nt * 64;   // float4 per slice
+  f32x4 v = zero4();
+  if (wave < nt) {
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(a.part) + wave * 64 + lane;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      f32x4 x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = src[(long)min(s0 + j, S - 1) * sstride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < S) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] += x[j][i];
+        }
+    }
+  }
+  return v;
+}
+
+// Gathers: rows [0, BK) are predecessor a of position i, A[idx[i-1][a]]
+// (A[anchor] at i = 0); rows [BK, 2 BK) candidate b of position i,
+// B[idx[i][b]] (L.sidx must be visible).  A thread's loads are issued back to
+// back (no branch around them or their addresses); vectors past the end
+// reload the last one and store it again (the same bytes to the same place).
+template <typename TA>
+__device__ __forceinline__ void sel_gather(const SelArgs &a, const SelLds<TA> &L) {
+  constexpr int EPV = SelLds<TA>::EPV;
+  constexpr int NT = kSelThreads;
+  const int tid = threadIdx.x;
+  const int K = a.K, r = a.r, BK = a.B * a.K, rs = L.rs;
+  TA *rows = L.rows;
+  const int *sidx = L.sidx;
   const TA *A = reinterpret_cast<const TA *>(a.cb_pred);
   const TA *Bc = reinterpret_cast<const TA *>(a.cb_succ);
   const int anchor = a.anchor < 0 ? 0 : a.anchor;   // row unused without an anchor
@@ -813,55 +897,21 @@ __global__ __launch_bounds__(kSelWaves * 64) void selector_fused_kernel(SelArgs 
       *reinterpret_cast<u32x4 *>(rows + row * rs + part * EPV) = buf[j];
     }
   }
+}
 
-  // this slice of the projection: tile `wave`, lane (g, r16)
-  f32x4 v = zero4();
-  if (wave < nt) {
-#pragma unroll 1
-    for (int j = 0; j < Q; ++j) {
-      const f32x4 x = red[(wave * Q + j) * 64 + lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] += x[i];
-    }
-  }
-  const int S = gridDim.x;
-  if (S > 1) {
-    const long sstride = (long)nt * 64;   // float4 per slice
-    if (wave < nt) {
-      float *pp = a.part + (((long)blockIdx.x * sstride) + wave * 64 + lane) * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) __hip_atomic_store(pp + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // every wave's partial stores (and gathers) have completed before the
-    // arrival counts
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      const bool l = arrive_last(a.cnt, a.stamp, S);
-      if (l) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      last = l;
-    }
-    __syncthreads();
-    if (!last) return;
-    if (wave < nt) {
-      // the slices happen-before these loads (release by every arrival,
-      // acquire above), so ordinary 16-byte loads see them; eight in flight
-      const f32x4 *src = reinterpret_cast<const f32x4 *>(a.part) + wave * 64 + lane;
-      v = zero4();
-      for (int s0 = 0; s0 < S; s0 += 8) {
-        f32x4 x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = src[(long)min(s0 + j, S - 1) * sstride];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (s0 + j < S) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] += x[j][i];
-          }
-      }
-    }
-  }
+// The projection v (waves < nt) into LDS, then the edges, the max-sum path
+// and the accept length (the gathered rows, ids and unaries are in LDS).
+template <typename TA, int KM, bool EXACT>
+__device__ __forceinline__ void sel_finish(const SelArgs &a, const SelLds<TA> &L, f32x4 v, int tg) {
+  constexpr int NT = kSelThreads;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int B = a.B, K = a.K, r = a.r, BK = a.B * a.K, rs = L.rs, nt = r >> 4;
+  const TA *rows = L.rows;
+  float *pj = L.pj, *se = L.se;
+  const float *un = L.un;
+  const int *sidx = L.sidx;
   // the projection of position r16, features 16 t + 4 g + i
   if (wave < nt && r16 < B) {
 #pragma unroll
@@ -962,6 +1012,66 @@ __global__ __launch_bounds__(kSelWaves * 64) void selector_fused_kernel(SelArgs 
   if (a.accept && lane == 0) a.accept[0] = miss ? (int)__builtin_ctzll(miss) : B;
 }
 
+template <typename TA, int KM, bool EXACT>
+__global__ __launch_bounds__(kSelThreads) void selector_fused_kernel(SelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const SelLds<TA> L(smem, a);
+  const int tid = threadIdx.x, B = a.B, BK = a.B * a.K;
+  // candidate ids, unaries and the target (first: the gathers wait on them)
+  int ix = 0;
+  float uv = 0.f;
+  if (tid < BK) {
+    ix = a.idx[tid];
+    uv = a.unary[tid];
+  }
+  const int tg = a.target && tid < B ? a.target[tid] : 0;   // wave 0: position `lane`
+  const f32x4 acc = sel_product<TA>(a, blockIdx.x);
+  if (tid < BK) {
+    L.sidx[tid] = clamp_idx(ix, a.V);
+    L.un[tid] = uv;
+  }
+  f32x4 v = sel_tile_sum(L.red, acc, a.r);   // its barrier publishes the ids too
+  sel_gather<TA>(a, L);
+  const int S = gridDim.x;
+  if (S > 1) {
+    sel_store_slice(a, blockIdx.x, v);
+    if (!sel_arrive(a.cnt, a.stamp, S)) return;
+    v = sel_sum_slices(a, S);
+  }
+  sel_finish<TA, KM, EXACT>(a, L, v, tg);
+}
+
+// The LM head's final merge and the whole selector in one launch (the
+// top-K + selector call): workgroups [0, S) form the projection's slices,
+// workgroups S + t merge token t's top-K lists and write its ids and unary
+// scores (merge_token, the same results as topk_merge_kernel).  The last of
+// all S + B workgroups to finish reads the ids, gathers the candidate rows,
+// sums the slices and finishes as selector_fused_kernel does.
+template <typename TA, int KM, bool EXACT>
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs ta, SelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const SelLds<TA> L(smem, a);
+  const int tid = threadIdx.x, B = a.B, BK = a.B * a.K;
+  const int S = a.n_wg;
+  if ((int)blockIdx.x < S) {
+    const f32x4 acc = sel_product<TA>(a, blockIdx.x);
+    sel_store_slice(a, blockIdx.x, sel_tile_sum(L.red, acc, a.r));
+  } else {
+    merge_token<KM, kSelThreads>(ta, (int)blockIdx.x - S);
+  }
+  if (!sel_arrive(a.cnt, a.stamp, S + B)) return;
+  // every token's ids and unaries were written before its arrival
+  if (tid < BK) {
+    L.sidx[tid] = clamp_idx(a.idx[tid], a.V);
+    L.un[tid] = a.unary[tid];
+  }
+  const int tg = a.target && tid < B ? a.target[tid] : 0;
+  __syncthreads();
+  sel_gather<TA>(a, L);
+  const f32x4 v = sel_sum_slices(a, S);
+  sel_finish<TA, KM, EXACT>(a, L, v, tg);
+}
+
 static size_t selector_fused_lds(int act, const SelArgs &a) {
   const size_t es = act == ACT_F32 ? 4 : 2;
   const size_t bk = (size_t)a.B * a.K;
@@ -1029,6 +1139,30 @@ hipError_t launch_selector(int act, const SelArgs &a, hipStream_t st) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(selector_path_kernel, dim3(1), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+bool topk_select_ok(int act, const TopkArgs &ta, const SelArgs &a) {
+  // the merge's own LDS (a few hundred bytes) beside the selector's
+  return ta.lds_path && ta.K <= 8 && ta.B == a.B && ta.n_wg >= 1 && selector_fused_fits(act, a) &&
+         selector_fused_lds(act, a) + 1024 <= kMaxLdsBytes;
+}
+
+template <typename TA, bool EXACT>
+static hipError_t topk_select_go(const TopkArgs &ta, const SelArgs &a, size_t lds, hipStream_t st) {
+  auto *k = &topk_select_kernel<TA, 8, EXACT>;
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3(a.n_wg + a.B), dim3(kSelThreads), lds, st, ta, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_select(int act, const TopkArgs &ta, const SelArgs &a, hipStream_t st) {
+  if (!topk_select_ok(act, ta, a) || !a.fused || a.n_wg < 1 || a.n_wg > 64 || !a.part || !a.cnt)
+    return hipErrorInvalidValue;
+  const size_t lds = selector_fused_lds(act, a);
+  if (act == ACT_F32)
+    return a.K == 8 ? topk_select_go<float, true>(ta, a, lds, st) : topk_select_go<float, false>(ta, a, lds, st);
+  return a.K == 8 ? topk_select_go<bf16, true>(ta, a, lds, st) : topk_select_go<bf16, false>(ta, a, lds, st);
 }
 
 // ---------------------------------------------------------------------------

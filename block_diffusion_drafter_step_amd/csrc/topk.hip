@@ -20,11 +20,10 @@
 #include "common.h"
 #include "kernels.h"
 #include "stream.h"
+#include "merge.h"
 
 namespace dfl {
 
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kL2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
@@ -48,13 +47,6 @@ __device__ __forceinline__ void list_insert(float (&v)[KM], int (&ix)[KM], float
       ix[j] = sw ? ti : ix[j];
     }
   }
-}
-
-// Partial lists of the workgroups, [token (16)][entry][workgroup]: values and
-// indices have K entries per token, the (max, sum) pairs 2.  Lanes of the
-// merges take consecutive workgroups, so their loads are coalesced.
-__device__ __forceinline__ long part_at(const TopkArgs &a, int tok, int entry, int per_tok, int wg) {
-  return ((long)tok * per_tok + entry) * a.n_wg + wg;
 }
 
 // Merge the 16 per-lane lists of each token in a workgroup (4 lane groups x
@@ -425,115 +417,10 @@ size_t topk_lds_bytes(int B, int d, int act, int K) {
   return h > mg ? h : mg;
 }
 
-// one workgroup per token: merge n_wg partial lists and (max, sum) pairs
-// (value, index) as one 64-bit key whose unsigned order is the candidate
-// order: value descending, then index ascending.  High word: the float's bits
-// made monotonic; low word: the complemented index.  0 = no candidate.
-__device__ __forceinline__ unsigned long long cand_key(float v, int i) {
-  const unsigned u = __float_as_uint(v);
-  const unsigned o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((unsigned long long)o << 32) | (unsigned)(~(unsigned)i);
-}
-__device__ __forceinline__ float key_value(unsigned long long k) {
-  const unsigned o = (unsigned)(k >> 32);
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
-}
-__device__ __forceinline__ int key_index(unsigned long long k) { return (int)~(unsigned)k; }
-__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x, int o) {
-  const int lo = __shfl_xor((int)(unsigned)x, o, kWave);
-  const int hi = __shfl_xor((int)(unsigned)(x >> 32), o, kWave);
-  return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
-}
-
-// Final merge, one workgroup per token: thread t holds partial list t (and,
-// with more than 256 workgroup partials, merges lists t + 256 j into it), the
-// log-sum-exp is a fixed-order tree over the threads, and the K winners are
-// picked one at a time by a block-wide max over the list heads.  Every
-// vocabulary row sits in exactly one partial, so the winning key names the
-// one list whose head advances.
+// Final merge, one workgroup of 256 threads per token (merge_token).
 template <int KM>
 __global__ __launch_bounds__(256) void topk_merge_kernel(TopkArgs a) {
-  const int tok = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.K;
-  unsigned long long key[KM];
-#pragma unroll
-  for (int j = 0; j < KM; ++j) key[j] = 0;
-  float m = -__builtin_inff(), s = 0.f;
-  if (tid < a.n_wg) {
-    // entries j >= K re-read entry K-1 (in bounds) and are dropped
-    float pv[KM];
-    int pi[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      const long e = part_at(a, tok, min(j, K - 1), K, tid);
-      pv[j] = a.part_val[e];
-      pi[j] = a.part_idx[e];
-    }
-    m = a.part_ms[part_at(a, tok, 0, 2, tid)];
-    s = a.part_ms[part_at(a, tok, 1, 2, tid)];
-#pragma unroll
-    for (int j = 0; j < KM; ++j) key[j] = j < K ? cand_key(pv[j], pi[j]) : 0ull;
-  }
-  for (int w = tid + 256; w < a.n_wg; w += 256) {
-    const float pm = a.part_ms[part_at(a, tok, 0, 2, w)], ps = a.part_ms[part_at(a, tok, 1, 2, w)];
-    if (ps > 0.f) {
-      if (pm > m) {
-        s = s * exp2f((m - pm) * kL2e);
-        m = pm;
-      }
-      s += ps * exp2f((pm - m) * kL2e);
-    }
-    for (int j = 0; j < K; ++j) {
-      const long e = part_at(a, tok, j, K, w);
-      unsigned long long x = cand_key(a.part_val[e], a.part_idx[e]);
-      if (x <= key[KM - 1]) break;   // the partial list is sorted: no later entry fits
-#pragma unroll
-      for (int q = 0; q < KM; ++q) {   // insert, keeping key[] descending
-        const unsigned long long hi = key[q] > x ? key[q] : x;
-        x = key[q] > x ? x : key[q];
-        key[q] = hi;
-      }
-    }
-  }
-  __shared__ float wm[4], wsum[4];
-  __shared__ unsigned long long wbest[2][4];
-  // log-sum-exp: fixed-order tree over the 256 threads
-  float M = m;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, shfl_xor(M, o));
-  if (lane == 0) wm[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
-  float S = s > 0.f ? s * exp2f((m - M) * kL2e) : 0.f;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) S += shfl_xor(S, o);
-  if (lane == 0) wsum[wave] = S;
-  __syncthreads();
-  S = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-  const float lse = M + log2f(S) * kLn2;
-  for (int k = 0; k < K; ++k) {
-    unsigned long long b = key[0];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const unsigned long long x = shfl_xor_u64(b, o);
-      b = x > b ? x : b;
-    }
-    // two slots: a wave that runs ahead writes the other one
-    if (lane == 0) wbest[k & 1][wave] = b;
-    __syncthreads();
-    unsigned long long w = wbest[k & 1][0];
-#pragma unroll
-    for (int q = 1; q < 4; ++q) w = wbest[k & 1][q] > w ? wbest[k & 1][q] : w;
-    if (key[0] == w) {
-#pragma unroll
-      for (int j = 0; j < KM - 1; ++j) key[j] = key[j + 1];
-      key[KM - 1] = 0;
-    }
-    if (tid == 0) {
-      a.idx[(long)tok * K + k] = key_index(w);
-      a.unary[(long)tok * K + k] = key_value(w) - lse;
-    }
-  }
+  merge_token<KM, 256>(a, blockIdx.x);
 }
 
 // about DFL_TOPK_WAVES waves, each owning at most TPW consecutive 16-row
@@ -586,14 +473,23 @@ static void topk_launch_tpw(const TopkArgs &a, hipStream_t st) {
 }
 
 template <typename TA, int WK, int KM>
-static hipError_t topk_launch_lds(const TopkArgs &a, hipStream_t st) {
+static hipError_t topk_launch_lds(const TopkArgs &a, hipStream_t st, bool merge = true) {
   auto *kern = &lmhead_topk_lds_kernel<TA, WK, KM, DFL_LMH_WAVES>;
   // more than 64 KB of dynamic LDS has to be allowed explicitly
   const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kern), (size_t)a.lds_bytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(a.n_wg), dim3(DFL_LMH_WAVES * 64), (size_t)a.lds_bytes, st, a);
-  hipLaunchKernelGGL((topk_merge_kernel<KM>), dim3(a.B), dim3(256), 0, st, a);
+  if (merge) hipLaunchKernelGGL((topk_merge_kernel<KM>), dim3(a.B), dim3(256), 0, st, a);
   return hipSuccess;
+}
+
+hipError_t launch_topk_partials(int act, int wkind, const TopkArgs &a, hipStream_t st) {
+  if (!a.lds_path || a.K > 8) return hipErrorInvalidValue;
+  hipError_t e;
+  if (act == ACT_F32) e = topk_launch_lds<float, W_SAME, 8>(a, st, false);
+  else if (wkind == W_Q8_0) e = topk_launch_lds<bf16, W_Q8_0, 8>(a, st, false);
+  else e = topk_launch_lds<bf16, W_SAME, 8>(a, st, false);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 template <typename TA, int WK>

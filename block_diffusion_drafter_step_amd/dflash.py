@@ -71,6 +71,9 @@ _SIGS = {
     "dflash_selector_edges": ([_P, _I32, _I32, _PW, _P, _P, _I64, _P, _P, _I32, _I32, _P, _P, _P, _P, _P,
                                _SZ, _P], _I32),
     "dflash_selector_edges_workspace": ([_I32, _I32, _I32, _I32], _SZ),
+    "dflash_topk_select": ([_P, _I32, _I32, _PW, _I32, _PW, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+                           _I32),
+    "dflash_topk_select_workspace": ([_I32, _I64, _I32, _I32, _I32], _SZ),
     "dflash_accept_len": ([_P, _P, _I32, _I32, _P, _P], _I32),
     "dflash_topk_rows": ([_P, _I64, _I64, _I32, _P, _P, _P, _SZ, _P], _I32),
     "dflash_topk_rows_workspace": ([_I64, _I64, _I32], _SZ),
@@ -255,6 +258,10 @@ def dflash_selector_edges_workspace(B, r, d, K) -> int:
     return load().dflash_selector_edges_workspace(B, r, d, K)
 
 
+def dflash_topk_select_workspace(B, V, K, r, d) -> int:
+    return load().dflash_topk_select_workspace(B, V, K, r, d)
+
+
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A workspace of at least `nbytes` (no initial contents needed)."""
     return torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
@@ -337,6 +344,19 @@ def dflash_selector_edges(h: torch.Tensor, proj: Weight, cb_pred: torch.Tensor, 
                                         _ptr(cb_succ), cb_pred.shape[0], _ptr(idx), _ptr(unary), K, anchor,
                                         _ptr(edges), _ptr(path), _ptr(target), _ptr(accept), wsp, wsb,
                                         _stream(stream)))
+
+
+def dflash_topk_select(h: torch.Tensor, lm_head: Weight, K: int, proj: Weight, cb_pred: torch.Tensor,
+                       cb_succ: torch.Tensor, anchor: int, idx: torch.Tensor, unary: torch.Tensor,
+                       edges: torch.Tensor, path: torch.Tensor, ws: torch.Tensor, stream=None, target=None,
+                       accept=None):
+    """dflash_topk_unary then dflash_selector_edges (V = lm_head rows) in one call."""
+    B = h.shape[0]
+    wl, wp = lm_head.c(), proj.c()
+    wsp, wsb = _ws(ws)
+    _check(load().dflash_topk_select(_ptr(h), B, _act_of(h), ctypes.byref(wl), K, ctypes.byref(wp), _ptr(cb_pred),
+                                     _ptr(cb_succ), anchor, _ptr(idx), _ptr(unary), _ptr(edges), _ptr(path),
+                                     _ptr(target), _ptr(accept), wsp, wsb, _stream(stream)))
 
 
 def dflash_accept_len(draft: torch.Tensor, target: torch.Tensor, accept: torch.Tensor, stream=None):

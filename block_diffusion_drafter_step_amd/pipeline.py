@@ -69,8 +69,9 @@ class DeviceWeights:
 
 class BlockStep:
     """Buffers of one block step: conv -> block attention (+ residual) ->
-    LM-head top-K -> selector edges + path -> accept length; optionally an
-    injection of `inject_n` rows first."""
+    LM-head top-K -> selector edges + path -> accept length (the last three
+    in one call, run(); or one at a time); optionally an injection of
+    `inject_n` rows first."""
 
     def __init__(self, cfg, weights: DeviceWeights, cache: D.KVCache, inject_n: int = 0, device="cuda"):
         self.cfg, self.W, self.cache = cfg, weights, cache
@@ -88,7 +89,8 @@ class BlockStep:
         sizes = [D.dflash_conv_workspace(1, B, cfg.C, cfg.G, cfg.T),
                  D.dflash_block_attn_workspace(B, d, cfg.Hq, cfg.Hkv, cfg.hd, n_ctx_max),
                  D.dflash_topk_unary_workspace(B, cfg.V, cfg.K),
-                 D.dflash_selector_edges_workspace(B, cfg.r, d, cfg.K)]
+                 D.dflash_selector_edges_workspace(B, cfg.r, d, cfg.K),
+                 D.dflash_topk_select_workspace(B, cfg.V, cfg.K, cfg.r, d)]
         if inject_n:
             sizes.append(D.dflash_inject_workspace(cfg.L_t, inject_n, cfg.d_t, d, cfg.kv, cfg.act))
         # one workspace reused by every call: the calls are stream-ordered
@@ -118,6 +120,14 @@ class BlockStep:
                                 target=None if target is None else target[0], accept=
                                 None if target is None else self.accept)
 
+    def topk_select(self, anchor: int, target=None, stream=None):
+        """topk() then select() as one call (dflash_topk_select)."""
+        W = self.W
+        D.dflash_topk_select(self.h, W.w_lm, self.cfg.K, W.sel_P, W.cb_pred, W.cb_succ, anchor, self.idx,
+                             self.unary, self.edges, self.path[0], self.ws, stream,
+                             target=None if target is None else target[0],
+                             accept=None if target is None else self.accept)
+
     def accept_len(self, target, stream=None):
         D.dflash_accept_len(self.path, target, self.accept, stream)
 
@@ -126,5 +136,4 @@ class BlockStep:
             self.inject(hidden, pos0, stream)
         self.conv(x, stream)
         self.attn(x, n_ctx, stream)
-        self.topk(stream)
-        self.select(anchor, target, stream)
+        self.topk_select(anchor, target, stream)

@@ -297,6 +297,23 @@ dflash_status dflash_selector_edges(const void *h, int32_t B, int32_t act,
                                     size_t ws_bytes, void *stream);
 size_t dflash_selector_edges_workspace(int32_t B, int32_t r, int32_t d, int32_t K);
 
+/* (4) + (5) in one call: exactly the outputs of dflash_topk_unary followed
+ * by dflash_selector_edges with V = lm_head->rows and the same h ("Turbo
+ * dflash", Overview; "spec : add DFlash2 support", Overview).  Arguments
+ * and requirements are those of the two calls; proj and lm_head share d.
+ * Where the LM head keeps h resident in LDS, K <= 8 and the candidate rows
+ * fit in LDS, the LM head's final merge and the whole selector (projection
+ * included) run in one kernel after the LM head's kernel; otherwise the two
+ * calls' kernels run in turn.  Either way idx, unary, edges, path (and
+ * accept) are bit for bit those of the two calls.  ws:
+ * dflash_topk_select_workspace(B, V, K, r, d) bytes (0 for invalid sizes). */
+dflash_status dflash_topk_select(const void *h, int32_t B, int32_t act, const dflash_weight *lm_head,
+                                 int32_t K, const dflash_weight *proj, const void *cb_pred,
+                                 const void *cb_succ, int32_t anchor, int32_t *idx, float *unary,
+                                 float *edges, int32_t *path, const int32_t *target, int32_t *accept,
+                                 void *ws, size_t ws_bytes, void *stream);
+size_t dflash_topk_select_workspace(int32_t B, int64_t V, int32_t K, int32_t r, int32_t d);
+
 /* Row-wise top-K of a score matrix (a standalone form of the selection in
  * (4)).  "spec : add DFlash2 support", the top-k kernel review: a small K
  * chosen from very wide rows, measured against a full sort.

@@ -241,6 +241,25 @@ def test_topk_and_selector_rejections(lib):
     assert lib.dflash_accept_len(FAKE, FAKE, 0, 8, FAKE, None) == 1
     assert lib.dflash_accept_len(None, FAKE, 1, 8, FAKE, None) == 1
 
+    # the combined call checks both calls' arguments (V = the LM head's rows)
+    def tks(lm=lm, K=8, P=P, anchor=3, B=16, wsb=1 << 30, target=None, accept=None):
+        return lib.dflash_topk_select(FAKE, B, 1, ref(lm), K, ref(P), FAKE, FAKE, anchor, FAKE, FAKE, FAKE, FAKE,
+                                      target, accept, FAKE, wsb, None)
+
+    assert tks(K=0) == 1
+    assert tks(K=33) == 1
+    assert tks(B=17) == 1
+    assert tks(P=W(1, 63, 256)) == 1
+    assert tks(P=W(1, 64, 320)) == 1       # proj and lm_head disagree on d
+    assert tks(anchor=1000) == 1           # anchor past the LM head's rows
+    assert tks(target=FAKE) == 1
+    assert tks(wsb=4) == 4
+    need = lib.dflash_topk_select_workspace(16, 1000, 8, 64, 256)
+    assert need >= lib.dflash_topk_unary_workspace(16, 1000, 8) + lib.dflash_selector_edges_workspace(16, 64, 256, 8) - 65536
+    assert tks(wsb=need - 1) == 4
+    assert lib.dflash_topk_select_workspace(16, 1000, 8, 63, 256) == 0
+    assert lib.dflash_topk_select_workspace(17, 1000, 8, 64, 256) == 0
+
 
 @no_gpu
 def test_topk_rows_rejections_and_workspace(lib):

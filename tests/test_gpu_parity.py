@@ -833,6 +833,70 @@ def test_selector_garbage_workspace():
     run_selector(configs.get(1), tag="selg", garbage_seed=9)
 
 
+def run_topk_select(cfg, tag="tks", garbage_seed=None):
+    """dflash_topk_select against dflash_topk_unary then dflash_selector_edges
+    on the same inputs: idx, unary, edges, path and accept bit for bit; the
+    top-K also against the oracle's logits."""
+    say(f"topk_select {cfg.name} V={cfg.V} K={cfg.K} B={cfg.B} r={cfg.r} weight={cfg.weight}")
+    w = synth.Workload(cfg)
+    h = synth.normal(cfg.seed, tag + ".h", (cfg.B, cfg.d), 1.0, cfg.act)
+    w_lm = w.w_lm()
+    A, Bc = w.codebooks()
+    hd, wl, pw = dev(h, cfg.act), wdev(w_lm), wdev(w.sel_proj())
+    ad, bd = dev(A, cfg.act), dev(Bc, cfg.act)
+    anchor = int(w.anchor()[0])
+    B, K = cfg.B, cfg.K
+
+    def outs():
+        return (torch.empty((B, K), dtype=torch.int32, device="cuda"),
+                torch.empty((B, K), dtype=torch.float32, device="cuda"),
+                torch.empty((B, K, K), dtype=torch.float32, device="cuda"),
+                torch.empty((B,), dtype=torch.int32, device="cuda"),
+                torch.full((1,), -1, dtype=torch.int32, device="cuda"))
+
+    i1, u1, e1, p1, a1 = outs()
+    D.dflash_topk_unary(hd, wl, K, i1, u1, D.workspace(D.dflash_topk_unary_workspace(B, cfg.V, K)))
+    # a target that leaves the first path at position min(5, B - 1)
+    D.dflash_selector_edges(hd, pw, ad, bd, i1, u1, anchor, e1, p1,
+                            D.workspace(D.dflash_selector_edges_workspace(B, cfg.r, cfg.d, K)))
+    torch.cuda.synchronize()
+    tgt = p1.clone()
+    m = min(5, B - 1)
+    tgt[m] = (tgt[m] + 1) % cfg.V
+    D.dflash_selector_edges(hd, pw, ad, bd, i1, u1, anchor, e1, p1,
+                            D.workspace(D.dflash_selector_edges_workspace(B, cfg.r, cfg.d, K)),
+                            target=tgt, accept=a1)
+    i2, u2, e2, p2, a2 = outs()
+    ws = D.workspace(D.dflash_topk_select_workspace(B, cfg.V, K, cfg.r, cfg.d))
+    if garbage_seed is not None:
+        garbage(ws, garbage_seed)
+    D.dflash_topk_select(hd, wl, K, pw, ad, bd, anchor, i2, u2, e2, p2, ws, target=tgt, accept=a2)
+    torch.cuda.synchronize()
+    for x, y, what in [(i1, i2, "idx"), (u1, u2, "unary"), (e1, e2, "edges"), (p1, p2, "path"),
+                       (a1, a2, "accept")]:
+        assert torch.equal(x, y), f"{cfg.name} {what} differs from the two calls"
+    assert int(a2[0]) == m
+    logits = O.lm_logits_stored(act_np(h, cfg.act), w_lm)
+    check_topk(i2.cpu().numpy(), u2.cpu().numpy(), logits, K, cfg.act, f"{cfg.name} combined top-{K}")
+
+
+@pytest.mark.parametrize("ci", [0, 1, 4])
+def test_topk_select_matches_two_calls(ci):
+    """c1 (bf16 head) and c4 (Q8_0 head, B = 8) take the one-kernel merge +
+    selector; c0's small head takes the two calls' kernels."""
+    run_topk_select(configs.get(ci))
+
+
+def test_topk_select_shapes_and_garbage_workspace():
+    """K < 8 and B < 16 on the one-kernel form (the merge and selector sized
+    from B and K), r = 48, a garbage workspace (stale counters), fp32 with a
+    resident head, and K = 16 (the two calls' kernels)."""
+    run_topk_select(cfg_small(1, V=40009, K=5, B=7), tag="tks5", garbage_seed=21)
+    run_topk_select(cfg_small(1, V=40009, r=48), tag="tks48")
+    run_topk_select(cfg_small(0, V=70001, K=8, B=8), tag="tksf")
+    run_topk_select(cfg_small(1, V=40009, K=16), tag="tks16")
+
+
 def test_accept_len():
     rng_path = synth.integers(11, "acc.path", 0, 1000, (300, 16))
     tgt, m = synth.targets_with_mismatch(11, "acc.tgt", rng_path, 1000)
