@@ -78,7 +78,7 @@ def traffic_from_counters(cfg):
         c = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
-    if c.get("source_hash") != src_hash("topk.hip", "common.h", "stream.h", "dflash_abi.cpp"):
+    if c.get("source_hash") != src_hash("topk.hip", "merge.h", "common.h", "stream.h", "dflash_abi.cpp"):
         return None
     if c.get("lm_head_shape") != {"V": cfg.V, "d": cfg.d, "B": cfg.B, "K": cfg.K, "weights": cfg.weight}:
         return None

@@ -44,6 +44,28 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x,
   const int hi = __shfl_xor((int)(unsigned)(x >> 32), o, kWave);
   return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
 }
+// a 64-bit value moved between the lanes of each 16-lane row by DPP control CTRL
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)x, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(x >> 32), CTRL, 0xf, 0xf, false);
+  return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+}
+__device__ __forceinline__ unsigned long long umax_u64(unsigned long long x, unsigned long long y) {
+  return x > y ? x : y;
+}
+// the largest key of the wave, in every lane (all 64 lanes active): within
+// each row of 16, DPP swaps lanes j ^ 1 and j ^ 2, then mirrors the quads
+// of each half-row and the halves of the row (each step pairs two groups
+// that already agree); across the rows, two lane permutes (j ^ 16, j ^ 32)
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long b) {
+  b = umax_u64(b, dpp_u64<0xB1>(b));    // quad_perm 1,0,3,2
+  b = umax_u64(b, dpp_u64<0x4E>(b));    // quad_perm 2,3,0,1
+  b = umax_u64(b, dpp_u64<0x141>(b));   // row_half_mirror
+  b = umax_u64(b, dpp_u64<0x140>(b));   // row_mirror
+  b = umax_u64(b, shfl_xor_u64(b, 16));
+  return umax_u64(b, shfl_xor_u64(b, 32));
+}
 
 // Final merge of token `tok` by one workgroup of NT threads (all of them call
 // it): thread t holds partial list t (and, with more than NT workgroup
@@ -52,12 +74,14 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x,
 // block-wide max over the list heads.  Every vocabulary row sits in exactly
 // one partial, so the winning key names the one list whose head advances.
 // Threads without a list hold nothing, so 256 or 1024 threads give the same
-// results bit for bit.
+// results bit for bit; the cross-wave steps read only the `nact` waves that
+// hold lists (the others contribute -inf maxima and empty keys).
 template <int KM, int NT>
 __device__ __forceinline__ void merge_token(const TopkArgs &a, int tok) {
   constexpr int NWV = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K;
+  const int nact = min(NWV, (a.n_wg + 63) / 64);
   unsigned long long key[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) key[j] = 0;
@@ -107,8 +131,7 @@ __device__ __forceinline__ void merge_token(const TopkArgs &a, int tok) {
   if (lane == 0) wm[wave] = M;
   __syncthreads();
   M = wm[0];
-#pragma unroll
-  for (int q = 1; q < NWV; ++q) M = fmaxf(M, wm[q]);
+  for (int q = 1; q < nact; ++q) M = fmaxf(M, wm[q]);
   float S = s > 0.f ? s * exp2f((m - M) * kL2e) : 0.f;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) S += shfl_xor(S, o);
@@ -117,18 +140,14 @@ __device__ __forceinline__ void merge_token(const TopkArgs &a, int tok) {
   S = tree_sum<NWV>(wsum);
   const float lse = M + log2f(S) * kLn2;
   for (int k = 0; k < K; ++k) {
-    unsigned long long b = key[0];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const unsigned long long x = shfl_xor_u64(b, o);
-      b = x > b ? x : b;
-    }
     // two slots: a wave that runs ahead writes the other one
-    if (lane == 0) wbest[k & 1][wave] = b;
+    if (wave < nact) {
+      const unsigned long long b = wave_max_u64(key[0]);
+      if (lane == 0) wbest[k & 1][wave] = b;
+    }
     __syncthreads();
     unsigned long long w = wbest[k & 1][0];
-#pragma unroll
-    for (int q = 1; q < NWV; ++q) w = wbest[k & 1][q] > w ? wbest[k & 1][q] : w;
+    for (int q = 1; q < nact; ++q) w = umax_u64(w, wbest[k & 1][q]);
     if (key[0] == w) {
 #pragma unroll
       for (int j = 0; j < KM - 1; ++j) key[j] = key[j + 1];

@@ -835,8 +835,9 @@ __device__ __forceinline__ bool sel_arrive(unsigned long long *cnt, unsigned lon
 
 // the S slices summed in slice order (waves < nt); the slices happen-before
 // these loads (release by every arrival, acquire by this workgroup), so
-// ordinary 16-byte loads see them, eight in flight
+// ordinary 16-byte loads see them, sixteen in flight
 __device__ __forceinline__ f32x4 sel_sum_slices(const SelArgs &a, int S) {
+  constexpr int NF = 16;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nt = a.r >> 4;
@@ -844,12 +845,12 @@ __device__ __forceinline__ f32x4 sel_sum_slices(const SelArgs &a, int S) {
   f32x4 v = zero4();
   if (wave < nt) {
     const f32x4 *src = reinterpret_cast<const f32x4 *>(a.part) + wave * 64 + lane;
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      f32x4 x[8];
+    for (int s0 = 0; s0 < S; s0 += NF) {
+      f32x4 x[NF];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = src[(long)min(s0 + j, S - 1) * sstride];
+      for (int j = 0; j < NF; ++j) x[j] = src[(long)min(s0 + j, S - 1) * sstride];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < NF; ++j)
         if (s0 + j < S) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] += x[j][i];
@@ -919,37 +920,52 @@ __device__ __forceinline__ void sel_finish(const SelArgs &a, const SelLds<TA> &L
   }
   __syncthreads();
 
-  for (int e = tid; e < BK * K; e += NT) {
-    const int i = e / (K * K), rem = e - i * K * K, ai = rem / K, bi = rem - ai * K;
-    const int npred = i == 0 ? (a.anchor < 0 ? 0 : 1) : K;
-    float ev;
-    if (i == 0 && ai > 0) {
-      ev = -__builtin_inff();
-    } else if (npred == 0) {
-      ev = un[i * K + bi];
-    } else {
+  // thread: predecessor ai of position i and EB successors b0 + j, so that
+  // each product x[k] p[k] is formed once for both; every edge is still one
+  // running sum over k of (x[k] p[k]) y[k], the arithmetic of
+  // selector_edges_kernel.  (Two successors per thread keep eight waves
+  // busy: four per thread left one wave per SIMD waiting on its own
+  // dependent adds.)
+  constexpr int EB = 2, EK = 16;
+  const int nbg = (K + EB - 1) / EB;
+  for (int t = tid; t < BK * nbg; t += NT) {
+    const int pr = t / nbg, b0 = (t - pr * nbg) * EB;
+    const int i = pr / K, ai = pr - i * K;
+    const bool dead = i == 0 && ai > 0;                // no such predecessor
+    const bool lone = i == 0 && a.anchor < 0;          // no predecessor at all
+    float s[EB];
+#pragma unroll
+    for (int j = 0; j < EB; ++j) s[j] = 0.f;
+    if (!dead && !lone) {
       const TA *x = rows + (i * K + ai) * rs;
-      const TA *y = rows + (BK + i * K + bi) * rs;
+      const TA *y[EB];
+#pragma unroll
+      for (int j = 0; j < EB; ++j) y[j] = rows + (BK + i * K + min(b0 + j, K - 1)) * rs;
       const float *p = pj + i * r;
-      float s = 0.f;
-      for (int k0 = 0; k0 < r; k0 += 16) {   // r is a multiple of 16
-        float xv[16], yv[16], pv[16];
+      for (int k0 = 0; k0 < r; k0 += EK) {   // r is a multiple of EK
+        float ap[EK];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          xv[k] = to_f32(x[k0 + k]);
-          yv[k] = to_f32(y[k0 + k]);
-          pv[k] = p[k0 + k];
-        }
+        for (int k = 0; k < EK; ++k) ap[k] = to_f32(x[k0 + k]) * p[k0 + k];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const float ap = xv[k] * pv[k];
-          s += ap * yv[k];
+        for (int j = 0; j < EB; ++j) {
+          float yv[EK];
+#pragma unroll
+          for (int k = 0; k < EK; ++k) yv[k] = to_f32(y[j][k0 + k]);
+#pragma unroll
+          for (int k = 0; k < EK; ++k) s[j] += ap[k] * yv[k];
         }
       }
-      ev = s + un[i * K + bi];
     }
-    se[e] = ev;
-    a.edges[e] = ev;
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      const int bi = b0 + j;
+      if (bi < K) {
+        const float ev = dead ? -__builtin_inff() : lone ? un[i * K + bi] : s[j] + un[i * K + bi];
+        const int e = pr * K + bi;
+        se[e] = ev;
+        a.edges[e] = ev;
+      }
+    }
   }
   __syncthreads();
   if (wave != 0) return;
@@ -1060,15 +1076,22 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs ta, S
     merge_token<KM, kSelThreads>(ta, (int)blockIdx.x - S);
   }
   if (!sel_arrive(a.cnt, a.stamp, S + B)) return;
-  // every token's ids and unaries were written before its arrival
+  // every token's ids and unaries were written before its arrival; their
+  // loads and the slices' are in flight together, the gather follows
+  int ix = 0;
+  float uv = 0.f;
   if (tid < BK) {
-    L.sidx[tid] = clamp_idx(a.idx[tid], a.V);
-    L.un[tid] = a.unary[tid];
+    ix = a.idx[tid];
+    uv = a.unary[tid];
   }
   const int tg = a.target && tid < B ? a.target[tid] : 0;
+  const f32x4 v = sel_sum_slices(a, S);
+  if (tid < BK) {
+    L.sidx[tid] = clamp_idx(ix, a.V);
+    L.un[tid] = uv;
+  }
   __syncthreads();
   sel_gather<TA>(a, L);
-  const f32x4 v = sel_sum_slices(a, S);
   sel_finish<TA, KM, EXACT>(a, L, v, tg);
 }
 
