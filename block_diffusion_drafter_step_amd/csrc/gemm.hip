@@ -433,8 +433,7 @@ struct TileLoader {
   using C = TileCfg<TA>;
   static constexpr int NA = TBM * C::CPR / 256;  // 4
   uint4 a[NA];
-  uint4 w[NA];        // SAME: 16-byte chunks; Q8_0: half chunks (8 codes) in .x/.y
-  float wscale[NA];
+  uint4 w[NA];
 
   __device__ __forceinline__ void load(const ASrc &A, int M, const WSet &W, int m0, int n0, int k0,
                                        int tid) {
@@ -450,17 +449,8 @@ struct TileLoader {
       const int n = min(n0 + row, W.n_total - 1);
       int lr;
       const int sg = seg_of(W, n, &lr);
-      if constexpr (WK == W_Q8_0) {
-        const int8_t *q = reinterpret_cast<const int8_t *>(pick(W.data, sg)) + (long)lr * W.K + k0 + ch * 8;
-        const uint2 v = *reinterpret_cast<const uint2 *>(q);
-        w[j].x = v.x;
-        w[j].y = v.y;
-        const uint16_t *sc = reinterpret_cast<const uint16_t *>(pick(W.scales, sg)) + (long)lr * (W.K >> 5);
-        wscale[j] = half_bits_to_f32(sc[(k0 + ch * 8) >> 5]);
-      } else {
-        w[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TA *>(pick(W.data, sg)) +
-                                                (long)lr * W.K + k0 + ch * C::VEC);
-      }
+      w[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const TA *>(pick(W.data, sg)) + (long)lr * W.K +
+                                              k0 + ch * C::VEC);
     }
   }
 
@@ -470,13 +460,7 @@ struct TileLoader {
       const int c = tid + 256 * j;
       const int row = c / C::CPR, ch = c % C::CPR;
       *reinterpret_cast<uint4 *>(As + row * C::LD + ch * C::VEC) = a[j];
-      if constexpr (WK == W_Q8_0) {
-        // 8 codes -> 8 bf16 at k = ch*8 (the bf16 tile row holds BK = 64)
-        const Frag<bf16> f = dequant8(make_uint2(w[j].x, w[j].y), wscale[j]);
-        *reinterpret_cast<bf16x8 *>(Ws + row * C::LD + ch * 8) = f.v;
-      } else {
-        *reinterpret_cast<uint4 *>(Ws + row * C::LD + ch * C::VEC) = w[j];
-      }
+      *reinterpret_cast<uint4 *>(Ws + row * C::LD + ch * C::VEC) = w[j];
     }
   }
 };
@@ -487,8 +471,7 @@ template <typename TA, int WK, int OM, bool SPLIT>
 __global__ __launch_bounds__(256) void tile_gemm_kernel(ASrc A, int M, WSet W, OutSpec o, int kc,
                                                         float *__restrict__ part) {
   using C = TileCfg<TA>;
-  static_assert(WK == W_SAME || C::BK == 64, "Q8_0 tiles are bf16");
-  // Q8_0 loads 8 codes per chunk, so a Q8_0 tile covers 8 * CPR = 64 k as well
+  static_assert(WK == W_SAME, "Q8_0 weights take dma8q_gemm_kernel");
   __shared__ __attribute__((aligned(16))) TA As[2][TBM * C::LD];
   __shared__ __attribute__((aligned(16))) TA Ws[2][TBN * C::LD];
 
@@ -604,10 +587,12 @@ int tile_split_plan(int M, int N, int K, int *kc) {
 }
 
 static int dma8s_plan(int M, int N, int K, int *kc);
+static int dma8q_plan(int M, int N, int K, int *kc);
 
 size_t tile_partial_floats(int M, int N, int K) {
   int kc;
-  const int S = std::max(tile_split_plan(M, N, K, &kc), dma8s_plan(M, N, K, &kc));
+  const int S = std::max(std::max(tile_split_plan(M, N, K, &kc), dma8s_plan(M, N, K, &kc)),
+                         K % 64 == 0 ? dma8q_plan(M, N, K, &kc) : 1);
   return S > 1 ? (size_t)S * M * N : 0;
 }
 
@@ -955,6 +940,256 @@ static bool dma8_split_launch(const ASrc &A, int M, const WSet &W, const OutSpec
 
 
 
+// ---------------------------------------------------------------------------
+// Q8_0 weights with few rows (a batched injection of up to kQ8ExpandMinM - 1
+// rows): TBM x 256 direct-to-LDS tiles (TBM = 64 or 128) whose ring holds
+// the weights' raw codes and scales.  A k-step is 64 wide (two Q8_0 blocks);
+// a stage holds
+//  * the activations as two 32-wide halves in the bf16 layout above (the
+//    dslot swizzle, 16-row blocks),
+//  * the codes as 256 rows of 64 bytes (the same 16-row x 64-byte DMA
+//    geometry and swizzle, two blocks per wave),
+//  * the scales as one dword per row (both blocks' fp16 scales), ordered so
+//    that the rows a lane multiplies (16 apart) are one 16-byte read; the
+//    dwords no lane reads repeat rows, so every wave issues the same loads.
+// The 8 waves tile the block as (TBM / 64) x (8 / (TBM / 64)), 64 rows
+// each: with 64-row tiles every code is dequantised by one wave only.
+// Weight fragments are dequantised as they are read from LDS (dequant8, the
+// products rounded to bf16 as on the other Q8_0 paths) and three k-steps of
+// loads are in flight per CU.  Every LDS read is 16 bytes: narrower reads
+// are paired by the compiler into instructions that lose their memory
+// operands, after which it waits for all direct-to-LDS loads in flight
+// before each k-step's reads.
+// ---------------------------------------------------------------------------
+constexpr int QBK = 64;                    // k per stage
+constexpr int QSW = DBN * QBK;             // codes (16 KB)
+constexpr int QSS = 8 * 64 * 4;            // scales: 64 dwords per wave (2 KB)
+constexpr int Q8STAGES = 4;
+template <int TBM>
+constexpr int q8_stage_bytes() { return 2 * TBM * 64 + QSW + QSS; }   // 34 KB or 26 KB
+
+template <int OM, int TBM, bool SPLIT>
+__global__ __launch_bounds__(512) void dma8q_gemm_kernel(ASrc A, int M, WSet W, OutSpec o, int kc,
+                                                         float *__restrict__ part) {
+  static_assert(TBM == 128 || TBM == 64, "block rows");
+  constexpr int WNW = 8 / (TBM / 64);   // waves along N
+  constexpr int CW = DBN / WNW;         // columns per wave (64 or 32)
+  constexpr int NJ = CW / 16;           // weight fragments per wave and half
+  constexpr int NAQ = TBM / 64;         // activation row blocks per wave per stage
+  constexpr int BPH = TBM / 16;         // activation row blocks per half
+  constexpr int QSA = TBM * 64;         // one activation half
+  constexpr int QSB = q8_stage_bytes<TBM>();
+  constexpr int QLPS = NAQ + 3;         // loads per wave per stage
+  extern __shared__ __attribute__((aligned(1024))) char smem_q8[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int mt = (M + TBM - 1) / TBM, nt = (W.n_total + DBN - 1) / DBN;
+  int tm, tn;
+  big_tile_of(blockIdx.x, mt, nt, &tm, &tn);
+  const int m0 = tm * TBM, n0 = tn * DBN;
+  int kt0 = 0, nk = W.K / QBK;   // first k-step and k-step count of this workgroup
+  if constexpr (SPLIT) {
+    kt0 = blockIdx.y * (kc / QBK);
+    nk = min(nk - kt0, kc / QBK);
+  }
+  const int kps = A.k_per_src;
+
+  // this lane's DMA rows: activation blocks wave NAQ + q (half t / BPH, block
+  // t % BPH), code blocks 2 wave + j (16-byte chunk dslot(row, slot) stored
+  // at slot lane & 3), and the scales of the row read as dword d = 64 wave
+  // + lane: p = d / 4 is the reading lane's wn 16 + r16, entry d % 4 its
+  // fragment (entries past NJ repeat a row)
+  const int rl = lane >> 2, slot = lane & 3;
+  long a_off[NAQ];
+  int a_dst[NAQ];
+#pragma unroll
+  for (int q = 0; q < NAQ; ++q) {
+    const int t = wave * NAQ + q, h = t / BPH, row = (t % BPH) * 16 + rl;
+    a_off[q] = (long)min(m0 + row, M - 1) * kps + 32 * h + 8 * dslot(row, slot);
+    a_dst[q] = h * QSA + (t % BPH) * 1024;
+  }
+  const int8_t *w_row[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = (2 * wave + j) * 16 + rl;
+    int lr;
+    const int n = min(n0 + row, W.n_total - 1);
+    const int sg = seg_of(W, n, &lr);
+    w_row[j] = reinterpret_cast<const int8_t *>(pick(W.data, sg)) + (long)lr * W.K + 16 * dslot(row, slot) +
+               (long)kt0 * QBK;
+  }
+  const uint16_t *s_row;
+  {
+    const int d = wave * 64 + lane, p = d >> 2;
+    const int row = ((p >> 4) % WNW) * CW + (p & 15) + 16 * ((d & 3) % NJ);
+    int lr;
+    const int n = min(n0 + row, W.n_total - 1);
+    const int sg = seg_of(W, n, &lr);
+    s_row = reinterpret_cast<const uint16_t *>(pick(W.scales, sg)) + (long)lr * (W.K >> 5) + 2 * kt0;
+  }
+  // next k-step to issue (counted from kt0) and its activation source
+  int ki = 0, src_i = (kt0 * QBK) / kps, kl = kt0 * QBK - src_i * kps;
+  const bf16 *src = reinterpret_cast<const bf16 *>(pick(A.ptr, src_i));
+  // the loads of one stage (no branches, so that they share a basic block
+  // with the k-step's LDS reads: a branch between them makes the compiler
+  // wait for every load in flight before the reads)
+  auto issue_loads = [&](char *stage) {
+#pragma unroll
+    for (int q = 0; q < NAQ; ++q) dma16(src + kl + a_off[q], (lds_void *)(stage + a_dst[q]));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      dma16(w_row[j] + (long)ki * QBK, (lds_void *)(stage + 2 * QSA + (2 * wave + j) * 1024));
+    __builtin_amdgcn_global_load_lds(s_row + 2 * ki, (lds_void *)(stage + 2 * QSA + QSW + wave * 256), 4, 0, 0);
+  };
+  auto advance = [&]() {
+    if (ki + 1 < nk) {   // past the last k-step the same one is issued again
+      ++ki;
+      kl += QBK;
+      if (kl == kps) {
+        kl = 0;
+        ++src_i;
+        src = reinterpret_cast<const bf16 *>(pick(A.ptr, src_i));
+      }
+    }
+  };
+
+  f32x4 acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = zero4();
+
+#pragma unroll
+  for (int s = 0; s < Q8STAGES - 1; ++s) {
+    issue_loads(smem_q8 + s * QSB);
+    advance();
+  }
+
+  const int ar = wm * 64 + r16, br = wn * CW + r16;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vm<QLPS * (Q8STAGES - 2)>();   // this wave's loads of stage kt have landed
+    ring_barrier();                      // ... everyone's; stage kt-1 is no longer read
+    issue_loads(smem_q8 + ((kt + Q8STAGES - 1) % Q8STAGES) * QSB);
+    const char *st = smem_q8 + (kt % Q8STAGES) * QSB;
+    const char *wq = st + 2 * QSA;
+    // scales of rows br + 16 j: dwords 4 (wn 16 + r16) + j
+    const u32x4 sv = *reinterpret_cast<const u32x4 *>(wq + QSW + (wn * 16 + r16) * 16);
+    float sc[NJ][2];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      sc[j][0] = half_bits_to_f32((uint16_t)(sv[j] & 0xffffu));
+      sc[j][1] = half_bits_to_f32((uint16_t)(sv[j] >> 16));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16 *as = reinterpret_cast<const bf16 *>(st + h * QSA);
+      Frag<bf16> fa[4], fb[NJ];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = ar + 16 * i;
+        fa[i] = load_frag(as + row * 32 + 8 * dslot(row, g));
+      }
+      // codes 32 h + 8 g ... + 7 of the row: half g & 1 of chunk 2 h + g / 2
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int row = br + 16 * j;
+        const u32x4 c = *reinterpret_cast<const u32x4 *>(wq + row * QBK + 16 * dslot(row, 2 * h + (g >> 1)));
+        fb[j] = dequant8((g & 1) ? make_uint2(c[2], c[3]) : make_uint2(c[0], c[1]), sc[j][h]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) mma(acc[i][j], fa[i], fb[j]);
+    }
+    advance();
+  }
+  wait_vm<0>();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int n = n0 + wn * CW + 16 * j + r16;
+      if (n >= W.n_total) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * 64 + 16 * i + 4 * g + v;
+        if (m < M) {
+          if constexpr (SPLIT)
+            part[((long)blockIdx.y * M + m) * W.n_total + n] = acc[i][j][v];
+          else
+            store_out_m<bf16, OM>(o, m, n, acc[i][j][v]);
+        }
+      }
+    }
+}
+
+// One workgroup per CU (the ring takes 104 or 136 KB of LDS), so the grid is
+// sized to one pass over kQ8Wgs CUs.  64-row tiles (each code dequantised by
+// one wave) while they still leave a k-split of at least two over those CUs
+// (measured on the Q8_0 workload's fc: 24 rows 103 -> 73 us, 192 rows
+// 177 -> 147 us; at 512 rows the 168 unsplit 64-row tiles took 413 us
+// against 306 for 128-row tiles split three ways).
+constexpr int kQ8Wgs = 256;
+static int q8_tbm(int M, int N) {
+  const long nt = (N + DBN - 1) / DBN;
+  return (long)((M + 63) / 64) * nt * 2 <= kQ8Wgs ? 64 : 128;
+}
+
+// k-split of the Q8_0 tiles
+static int dma8q_plan(int M, int N, int K, int *kc) {
+  const int tbm = q8_tbm(M, N);
+  const long tiles = (long)((N + DBN - 1) / DBN) * ((M + tbm - 1) / tbm);
+  const int nk = K / QBK;
+  int S = (int)std::max(1L, kQ8Wgs / tiles);
+  S = std::min(S, std::max(1, nk / 4));
+  S = std::min(S, 64);
+  const int kcq = (nk + S - 1) / S;
+  S = (nk + kcq - 1) / kcq;
+  *kc = kcq * QBK;
+  return S;
+}
+
+template <int OM, int TBM, bool SPLIT>
+static hipError_t dma8q_go1(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part, int kc,
+                            int S, hipStream_t st) {
+  const int mt = (M + TBM - 1) / TBM, nt = (W.n_total + DBN - 1) / DBN;
+  const size_t lds = (size_t)Q8STAGES * q8_stage_bytes<TBM>();
+  auto *k = &dma8q_gemm_kernel<OM, TBM, SPLIT>;
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3(mt * nt, S), dim3(512), lds, st, A, M, W, out, kc, part);
+  if (SPLIT) {
+    const long mn = (long)M * W.n_total;
+    hipLaunchKernelGGL((tile_reduce_kernel<bf16, OM>), dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st,
+                       part, S, M, W.n_total, out);
+  }
+  return hipSuccess;
+}
+
+template <int OM, int TBM>
+static hipError_t dma8q_go_t(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part,
+                             hipStream_t st) {
+  int kc = 0;
+  const int S = part ? dma8q_plan(M, W.n_total, W.K, &kc) : 1;
+  return S > 1 ? dma8q_go1<OM, TBM, true>(A, M, W, out, part, kc, S, st)
+               : dma8q_go1<OM, TBM, false>(A, M, W, out, nullptr, 0, 1, st);
+}
+
+template <int OM>
+static hipError_t dma8q_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part,
+                           hipStream_t st) {
+  return q8_tbm(M, W.n_total) == 64 ? dma8q_go_t<OM, 64>(A, M, W, out, part, st)
+                         : dma8q_go_t<OM, 128>(A, M, W, out, part, st);
+}
+
+// Q8_0 weights through the ring above: bf16 activations, k-ranges of whole
+// 64-wide steps that never straddle two activation sources
+static bool dma8q_ok(int act, int wkind, const ASrc &A, const WSet &W) {
+  return act == ACT_BF16 && wkind == W_Q8_0 && W.K % QBK == 0 && A.k_per_src % QBK == 0;
+}
+
 // Q8_0 -> bf16 expansion: one thread per 32-code block (two 16-byte code
 // loads, one scale, four 16-byte stores), consecutive threads on consecutive
 // blocks of a row, so reads and writes are both contiguous.
@@ -1001,8 +1236,12 @@ hipError_t launch_tile_gemm(int act, int wkind, const ASrc &A, int M, const WSet
   hipError_t e = hipSuccess;
   if (act == ACT_F32)
     tile_launch_t<float, W_SAME>(A, M, W, out, part, st);
-  else if (wkind == W_Q8_0)   // fewer rows than kQ8ExpandMinM: dequantised per tile
-    tile_launch_t<bf16, W_Q8_0>(A, M, W, out, part, st);
+  else if (dma8q_ok(act, wkind, A, W)) {   // fewer rows than kQ8ExpandMinM: codes in the ring
+    if (out.mode == OUT_F32) e = dma8q_go<OUT_F32>(A, M, W, out, part, st);
+    else if (out.mode == OUT_ACT) e = dma8q_go<OUT_ACT>(A, M, W, out, part, st);
+    else e = dma8q_go<OUT_CACHE>(A, M, W, out, part, st);
+  } else if (wkind == W_Q8_0)   // the callers keep K and the sources to multiples of 64
+    return hipErrorInvalidValue;
   else if (!big && (!half || ragged) && dma8_split_launch(A, M, W, out, part, st, &e))
     return e != hipSuccess ? e : hipGetLastError();
   else if (big)

@@ -184,14 +184,38 @@ def test_inject_q8_0_decode_rows(d, d_t, n):
 
 
 def test_inject_q8_0_batched_rows():
-    """Q8_0 weights with 40 rows (split-K tile GEMM with per-tile dequantisation)."""
+    """Q8_0 weights with 40 rows (split-K direct-to-LDS ring of raw codes)."""
     run_inject(cfg_small(4, d=512, d_t=256, L_t=3, Hkv=2, capacity=256), 40, 9)
+
+
+@pytest.mark.parametrize("d,d_t,L_t,n", [(576, 320, 3, 100), (448, 192, 2, 300), (640, 128, 4, 17)])
+def test_inject_q8_0_ring_shapes(d, d_t, L_t, n):
+    """Q8_0 weights with 17 ... 767 rows through the direct-to-LDS ring of raw
+    codes: a ragged last 256-column tile (d = 576, 448, 640), k-splits of
+    several 64-wide steps (K = 960, 576, 512, 640), the unsplit form (K = 384
+    and 448, fewer than eight steps), ragged 128-row tiles (100, 300, 17
+    rows), activation sources of 320, 192 and 128 columns."""
+    run_inject(cfg_small(4, d=d, d_t=d_t, L_t=L_t, Hkv=2, capacity=512), n, 7)
+
+
+@pytest.mark.parametrize("d_t,L_t", [(256, 2), (448, 1)])
+def test_inject_q8_0_ring_128_row_tiles(d_t, L_t):
+    """767 rows against a 2816-wide fc: 64-row tiles would leave no k-split
+    over the CUs, so the fc takes 128-row tiles, split (K = 512) and unsplit
+    (K = 448, fewer than eight 64-wide steps); checked on sampled rows."""
+    run_inject(cfg_small(4, d=2816, d_t=d_t, L_t=L_t, Hkv=2, capacity=1024), 767, 0, rows=[0, 100, 700, 766])
+
+
+def test_inject_q8_0_ring_full_width():
+    """The Q8_0 workload's own fc and Wk / Wv (d = 5376) on 48 rows, checked
+    on sampled rows."""
+    run_inject(cfg_small(4, capacity=512), 48, 0, rows=[0, 1, 31, 47])
 
 
 @pytest.mark.parametrize("n", [767, 800, 4133])
 def test_inject_q8_0_around_expansion_threshold(n):
-    """Q8_0 fc / Wk / Wv on every row just below 768 tokens (per-tile
-    dequantisation) and above (one bf16 expansion per call), ragged tails."""
+    """Q8_0 fc / Wk / Wv on every row just below 768 tokens (the ring of raw
+    codes) and above (one bf16 expansion per call), ragged tails."""
     cfg = cfg_small(4, d=512, d_t=256, L_t=3, Hkv=2, capacity=4224)
     run_inject(cfg, n, 17)
 
