@@ -545,12 +545,16 @@ dflash_status dflash_ffn_block(const void *h, int32_t n_blocks, int32_t B, int32
   return launched(e, "down");
 }
 
-dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, int32_t d,
-                                int32_t n_q_heads, int32_t act, const dflash_weight *wq,
-                                const dflash_weight *wk, const dflash_weight *wv,
-                                const dflash_weight *wo, const dflash_kv_cache *cache,
-                                int64_t n_ctx, float scale, void *out, void *ws, size_t ws_bytes,
-                                void *stream) {
+}  // extern "C"
+
+// The block attention; with `cache_ready`, the stream waits for that event
+// after the Q | Kb | Vb projection, before the first kernel that reads the
+// cache.
+static dflash_status block_attn(const void *u, const void *residual, int32_t B, int32_t d, int32_t n_q_heads,
+                                int32_t act, const dflash_weight *wq, const dflash_weight *wk,
+                                const dflash_weight *wv, const dflash_weight *wo,
+                                const dflash_kv_cache *cache, int64_t n_ctx, float scale, void *out, void *ws,
+                                size_t ws_bytes, void *stream, hipEvent_t cache_ready) {
   TRY(check_act(act));
   TRY(need_ptr(u, "u"));
   if (residual) TRY(need_ptr(residual, "residual"));
@@ -596,6 +600,10 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   hipError_t e = gemm(act, wkind_of(wq), asrc1(u, d), B, wset({wq, wk, wv}), part, c.counters,
                       out_act(qkv, nqkv, nullptr, 0), st);
   if (e != hipSuccess) return launched(e, "qkv");
+  if (cache_ready) {
+    e = hipStreamWaitEvent(st, cache_ready, 0);
+    if (e != hipSuccess) return launched(e, "wait for the cache");
+  }
   a.qkv = qkv;
   a.ck = cache->k;
   a.cv = cache->v;
@@ -614,6 +622,29 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
   if (e != hipSuccess) return launched(e, "attention");
   e = gemm(act, wkind_of(wo), asrc1(o, (int)qdim), B, wset({wo}), part, c.counters, out_act(out, d, residual, d), st);
   return launched(e, "wo");
+}
+
+extern "C" {
+
+dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, int32_t d,
+                                int32_t n_q_heads, int32_t act, const dflash_weight *wq,
+                                const dflash_weight *wk, const dflash_weight *wv,
+                                const dflash_weight *wo, const dflash_kv_cache *cache,
+                                int64_t n_ctx, float scale, void *out, void *ws, size_t ws_bytes,
+                                void *stream) {
+  return block_attn(u, residual, B, d, n_q_heads, act, wq, wk, wv, wo, cache, n_ctx, scale, out, ws, ws_bytes,
+                    stream, nullptr);
+}
+
+dflash_status dflash_block_attn_after(const void *u, const void *residual, int32_t B, int32_t d,
+                                      int32_t n_q_heads, int32_t act, const dflash_weight *wq,
+                                      const dflash_weight *wk, const dflash_weight *wv,
+                                      const dflash_weight *wo, const dflash_kv_cache *cache,
+                                      int64_t n_ctx, float scale, void *out, void *ws, size_t ws_bytes,
+                                      void *stream, void *cache_ready) {
+  if (!cache_ready) return fail(DFLASH_ERR_INVALID_ARG, "cache_ready is NULL");
+  return block_attn(u, residual, B, d, n_q_heads, act, wq, wk, wv, wo, cache, n_ctx, scale, out, ws, ws_bytes,
+                    stream, (hipEvent_t)cache_ready);
 }
 
 }  // extern "C"

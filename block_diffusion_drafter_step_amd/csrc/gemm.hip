@@ -964,9 +964,12 @@ static bool dma8_split_launch(const ASrc &A, int M, const WSet &W, const OutSpec
 constexpr int QBK = 64;                    // k per stage
 constexpr int QSW = DBN * QBK;             // codes (16 KB)
 constexpr int QSS = 8 * 64 * 4;            // scales: 64 dwords per wave (2 KB)
-constexpr int Q8STAGES = 4;
 template <int TBM>
 constexpr int q8_stage_bytes() { return 2 * TBM * 64 + QSW + QSS; }   // 34 KB or 26 KB
+// ring stages (five or six for the 64-row tiles measured slower: 24 rows
+// 72 -> 77 us)
+template <int TBM>
+constexpr int q8_stages() { return 4; }
 
 template <int OM, int TBM, bool SPLIT>
 __global__ __launch_bounds__(512) void dma8q_gemm_kernel(ASrc A, int M, WSet W, OutSpec o, int kc,
@@ -980,6 +983,7 @@ __global__ __launch_bounds__(512) void dma8q_gemm_kernel(ASrc A, int M, WSet W, 
   constexpr int QSA = TBM * 64;         // one activation half
   constexpr int QSB = q8_stage_bytes<TBM>();
   constexpr int QLPS = NAQ + 3;         // loads per wave per stage
+  constexpr int Q8STAGES = q8_stages<TBM>();
   extern __shared__ __attribute__((aligned(1024))) char smem_q8[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1155,7 +1159,7 @@ template <int OM, int TBM, bool SPLIT>
 static hipError_t dma8q_go1(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part, int kc,
                             int S, hipStream_t st) {
   const int mt = (M + TBM - 1) / TBM, nt = (W.n_total + DBN - 1) / DBN;
-  const size_t lds = (size_t)Q8STAGES * q8_stage_bytes<TBM>();
+  const size_t lds = (size_t)q8_stages<TBM>() * q8_stage_bytes<TBM>();
   auto *k = &dma8q_gemm_kernel<OM, TBM, SPLIT>;
   const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), lds);
   if (e != hipSuccess) return e;

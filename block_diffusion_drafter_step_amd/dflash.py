@@ -62,6 +62,8 @@ _SIGS = {
     "dflash_ffn_block_act_offset": ([_I32, _I32, _I32, _I32, _I32, _I32], _SZ),
     "dflash_block_attn": ([_P, _P, _I32, _I32, _I32, _I32, _PW, _PW, _PW, _PW, _PC, _I64, _F32, _P, _P,
                            _SZ, _P], _I32),
+    "dflash_block_attn_after": ([_P, _P, _I32, _I32, _I32, _I32, _PW, _PW, _PW, _PW, _PC, _I64, _F32, _P,
+                                 _P, _SZ, _P, _P], _I32),
     "dflash_block_attn_workspace": ([_I32, _I32, _I32, _I32, _I32, _I64], _SZ),
     "dflash_block_attn_qkv_offset": ([_I32, _I32, _I32, _I32, _I32, _I64], _SZ),
     "dflash_block_attn_o_offset": ([_I32, _I32, _I32, _I32, _I32, _I64], _SZ),
@@ -312,6 +314,20 @@ def dflash_block_attn(u: torch.Tensor, residual, n_q_heads: int, wq: Weight, wk:
     _check(load().dflash_block_attn(_ptr(u), _ptr(residual), B, d, n_q_heads, _act_of(u), ctypes.byref(q),
                                     ctypes.byref(k), ctypes.byref(v), ctypes.byref(o), ctypes.byref(c),
                                     n_ctx, scale, _ptr(out), wsp, wsb, _stream(stream)))
+
+
+def dflash_block_attn_after(u: torch.Tensor, residual, n_q_heads: int, wq: Weight, wk: Weight, wv: Weight,
+                            wo: Weight, cache: KVCache, n_ctx: int, scale: float, out: torch.Tensor,
+                            ws: torch.Tensor, cache_ready: torch.cuda.Event, stream=None):
+    """dflash_block_attn whose stream waits for `cache_ready` (a recorded
+    torch.cuda.Event) before the kernels that read the cache."""
+    B, d = u.shape
+    q, k, v, o, c = wq.c(), wk.c(), wv.c(), wo.c(), cache.c()
+    wsp, wsb = _ws(ws)
+    _check(load().dflash_block_attn_after(_ptr(u), _ptr(residual), B, d, n_q_heads, _act_of(u),
+                                          ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(o),
+                                          ctypes.byref(c), n_ctx, scale, _ptr(out), wsp, wsb, _stream(stream),
+                                          cache_ready.cuda_event))
 
 
 def dflash_topk_unary(h: torch.Tensor, lm_head: Weight, K: int, idx: torch.Tensor, unary: torch.Tensor,

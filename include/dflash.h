@@ -225,6 +225,22 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
                                 const dflash_weight *wo, const dflash_kv_cache *cache,
                                 int64_t n_ctx, float scale, void *out, void *ws, size_t ws_bytes,
                                 void *stream);
+/* (3) with the cache written on another stream: the same operation and
+ * outputs, but `stream` waits for `cache_ready` (a hipEvent_t recorded
+ * after the writes of cache positions [0, n_ctx), e.g. dflash_inject on a
+ * second stream) once Q | Kb | Vb are enqueued and before the first kernel
+ * that reads the cache.  "Turbo dflash", Deferred KV Injection
+ * Optimization (the injection and the draft's own work are separate
+ * steps): the projection of the block does not depend on the injection, so
+ * the two can overlap.  cache_ready NULL -> DFLASH_ERR_INVALID_ARG.  The
+ * workspace is this call's alone while the event is pending: the injection
+ * that overlaps it needs a workspace of its own. */
+dflash_status dflash_block_attn_after(const void *u, const void *residual, int32_t B, int32_t d,
+                                      int32_t n_q_heads, int32_t act, const dflash_weight *wq,
+                                      const dflash_weight *wk, const dflash_weight *wv,
+                                      const dflash_weight *wo, const dflash_kv_cache *cache,
+                                      int64_t n_ctx, float scale, void *out, void *ws, size_t ws_bytes,
+                                      void *stream, void *cache_ready);
 size_t dflash_block_attn_workspace(int32_t B, int32_t d, int32_t n_q_heads, int32_t n_kv_heads,
                                    int32_t head_dim, int64_t n_ctx);
 /* Byte offsets into the attention's workspace, for the same arguments, of

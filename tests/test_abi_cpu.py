@@ -210,6 +210,13 @@ def test_attn_rejections(lib):
     assert call(wk=W(2, 1024, 5120, scales=FAKE)) == 2
     assert call(scale=-1.0) == 1
     assert call(wsb=1024) == 4
+    # the variant that waits for the cache's event: the same checks, and the
+    # event itself is required
+    after = lambda ev, B=16: lib.dflash_block_attn_after(FAKE, None, B, 5120, 32, 1, ref(wq), ref(wk), ref(wv),
+                                                         ref(wo), ref(cache()), 1024, 0.0, FAKE, FAKE, 1 << 30,
+                                                         None, ev)
+    assert after(None) == 1
+    assert after(FAKE, B=17) == 1
 
 
 @no_gpu

@@ -991,6 +991,45 @@ def test_block_step_chain(ci):
     assert_close(gh, ref["attn"]["out"], cfg.act, f"{cfg.name} chain h end to end")
 
 
+@pytest.mark.parametrize("ci", [1, 4])
+def test_block_step_overlap_matches_serial(ci):
+    """run() with the injection on its own stream (the attention waits for
+    it before reading the cache) against the same steps in one stream: the
+    cache, u, h, top-K, edges, path and accept length bit for bit, over three
+    steps whose injected rows are the newest keys attended.  Before each
+    injection its rows hold a constant, so an attention that read them early
+    would differ."""
+    cfg = configs.get(ci)
+    say(f"overlap {cfg.name}")
+    w = synth.Workload(cfg)
+    W = P.DeviceWeights(w, drop_host=True)
+    n, n0 = 16, 256
+    anchor = int(w.anchor()[0])
+    runs = []
+    for overlap in (False, True):
+        cache = P.new_cache(configs.shrink(cfg, capacity=n0 + 3 * n))
+        cache.k[:, :n0].normal_(generator=torch.Generator(device="cuda").manual_seed(5))
+        cache.v[:, :n0 // 32].normal_(generator=torch.Generator(device="cuda").manual_seed(6))
+        step = P.BlockStep(cfg, W, cache, inject_n=n)
+        outs = []
+        for s in range(3):
+            pos0 = n0 + n * s
+            cache.k[:, pos0:pos0 + n].fill_(3.0)
+            hid = [dev(synth.normal(cfg.seed, f"ovl.h{s}.{l}", (n, cfg.d_t), 1.0, cfg.act), cfg.act)
+                   for l in range(cfg.L_t)]
+            x = dev(synth.normal(cfg.seed, f"ovl.x{s}", (1, cfg.B, cfg.d), 1.0, cfg.act), cfg.act)
+            tgt = torch.zeros((1, cfg.B), dtype=torch.int32, device="cuda")
+            step.run(x, pos0 + n, anchor, tgt, hidden=hid, pos0=pos0, overlap=overlap)
+            torch.cuda.synchronize()
+            outs.append([t.clone() for t in (step.u, step.h, step.idx, step.unary, step.edges, step.path,
+                                             step.accept)])
+        outs.append([cache.k.clone(), cache.v.clone()])
+        runs.append(outs)
+    for s, (a, b) in enumerate(zip(*runs)):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), f"{cfg.name} step {s}: the overlapped step differs from the serial one"
+
+
 @pytest.mark.parametrize("kv", ["bf16", "q8_0"])
 def test_decode_64k_three_steps(kv):
     """The 64k decode workload as a sequence: the cache holds 65536 seeded
