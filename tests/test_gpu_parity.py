@@ -166,6 +166,15 @@ def test_inject_prefill_32k_sampled(ci):
     run_inject(cfg, cfg.n_ctx, 0, rows=rows)
 
 
+@pytest.mark.parametrize("d,d_t,L_t", [(5184, 1024, 2), (5120, 1088, 1)])
+def test_inject_prefill_tile_forms(d, d_t, L_t):
+    """6400 rows on the 256 x 256 prefill tiles: a ragged last 256-column
+    tile (d = 5184) and K = 1088 (34 k-steps); checked on sampled rows
+    including the last tile."""
+    rows = [0, 1, 255, 256, 3333, 6143, 6144, 6399]
+    run_inject(cfg_small(1, d=d, d_t=d_t, L_t=L_t, capacity=6400), 6400, 0, rows=rows)
+
+
 @pytest.mark.parametrize("n", [32, 48, 64, 256, 1024, 2048])
 def test_inject_batched_blocks(n):
     """Deferred injection: the rows of several stashed blocks at once (split-K
