@@ -232,7 +232,7 @@ __global__ __launch_bounds__(WPG * 64, WPG >= 8 ? WPG / 4 : 2) void skinny_gemm_
 // Outputs from the partials part[y][tile][lane] (float4) summed in k-group
 // order, as the last workgroup of skinny_gemm_kernel does; 8 k-groups' loads
 // are issued together to hide their latency (also in the last, partial
-// group).  One thread per (tile, lane).
+// group; 16 measured no faster in the step).  One thread per (tile, lane).
 template <typename TA>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int nky,
                                                             int N, int M, OutSpec o) {
@@ -245,12 +245,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
   const f32x4 *src = reinterpret_cast<const f32x4 *>(part) + id;
   f32x4 v = zero4();
   // groups past nky re-read the last one and are not added
-  for (int ky = 0; ky < nky; ky += 8) {
-    f32x4 t[8];
+  constexpr int NF = 8;
+  for (int ky = 0; ky < nky; ky += NF) {
+    f32x4 t[NF];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = src[(long)min(ky + j, nky - 1) * tstride];
+    for (int j = 0; j < NF; ++j) t[j] = src[(long)min(ky + j, nky - 1) * tstride];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < NF; ++j)
       if (ky + j < nky) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] += t[j][i];
@@ -552,15 +553,16 @@ __global__ __launch_bounds__(256) void tile_reduce_kernel(const float *__restric
   const long mn = (long)M * N;
   if (id >= mn) return;
   // eight pieces' loads in flight at a time (a load-then-add loop waits for
-  // each); pieces past S re-read the last one and are not added, so the sum
-  // is taken in piece order
+  // each; sixteen slowed the larger sums); pieces past S re-read the last one
+  // and are not added, so the sum is taken in piece order
+  constexpr int NF = 8;
   float v = 0.f;
-  for (int z = 0; z < S; z += 8) {
-    float t[8];
+  for (int z = 0; z < S; z += NF) {
+    float t[NF];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = part[(long)min(z + j, S - 1) * mn + id];
+    for (int j = 0; j < NF; ++j) t[j] = part[(long)min(z + j, S - 1) * mn + id];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < NF; ++j)
       if (z + j < S) v += t[j];
   }
   const long m = id / N;
@@ -971,10 +973,13 @@ constexpr int q8_stage_bytes() { return 2 * TBM * 64 + QSW + QSS; }   // 34 KB o
 template <int TBM>
 constexpr int q8_stages() { return 4; }
 
-template <int OM, int TBM, bool SPLIT>
+// MI: 16-row activation fragments a wave multiplies (2 when a 64-row tile
+// holds at most 32 rows: the other two would be padding)
+template <int OM, int TBM, bool SPLIT, int MI>
 __global__ __launch_bounds__(512) void dma8q_gemm_kernel(ASrc A, int M, WSet W, OutSpec o, int kc,
                                                          float *__restrict__ part) {
   static_assert(TBM == 128 || TBM == 64, "block rows");
+  static_assert(MI == 4 || (MI == 2 && TBM == 64), "live fragments");
   constexpr int WNW = 8 / (TBM / 64);   // waves along N
   constexpr int CW = DBN / WNW;         // columns per wave (64 or 32)
   constexpr int NJ = CW / 16;           // weight fragments per wave and half
@@ -1059,9 +1064,9 @@ __global__ __launch_bounds__(512) void dma8q_gemm_kernel(ASrc A, int M, WSet W, 
     }
   };
 
-  f32x4 acc[4][NJ];
+  f32x4 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = zero4();
 
@@ -1089,9 +1094,9 @@ __global__ __launch_bounds__(512) void dma8q_gemm_kernel(ASrc A, int M, WSet W, 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const bf16 *as = reinterpret_cast<const bf16 *>(st + h * QSA);
-      Frag<bf16> fa[4], fb[NJ];
+      Frag<bf16> fa[MI], fb[NJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MI; ++i) {
         const int row = ar + 16 * i;
         fa[i] = load_frag(as + row * 32 + 8 * dslot(row, g));
       }
@@ -1103,7 +1108,7 @@ __global__ __launch_bounds__(512) void dma8q_gemm_kernel(ASrc A, int M, WSet W, 
         fb[j] = dequant8((g & 1) ? make_uint2(c[2], c[3]) : make_uint2(c[0], c[1]), sc[j][h]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) mma(acc[i][j], fa[i], fb[j]);
     }
@@ -1111,7 +1116,7 @@ __global__ __launch_bounds__(512) void dma8q_gemm_kernel(ASrc A, int M, WSet W, 
   }
   wait_vm<0>();
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int n = n0 + wn * CW + 16 * j + r16;
@@ -1155,12 +1160,12 @@ static int dma8q_plan(int M, int N, int K, int *kc) {
   return S;
 }
 
-template <int OM, int TBM, bool SPLIT>
+template <int OM, int TBM, bool SPLIT, int MI>
 static hipError_t dma8q_go1(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part, int kc,
                             int S, hipStream_t st) {
   const int mt = (M + TBM - 1) / TBM, nt = (W.n_total + DBN - 1) / DBN;
   const size_t lds = (size_t)q8_stages<TBM>() * q8_stage_bytes<TBM>();
-  auto *k = &dma8q_gemm_kernel<OM, TBM, SPLIT>;
+  auto *k = &dma8q_gemm_kernel<OM, TBM, SPLIT, MI>;
   const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3(mt * nt, S), dim3(512), lds, st, A, M, W, out, kc, part);
@@ -1172,20 +1177,20 @@ static hipError_t dma8q_go1(const ASrc &A, int M, const WSet &W, const OutSpec &
   return hipSuccess;
 }
 
-template <int OM, int TBM>
+template <int OM, int TBM, int MI>
 static hipError_t dma8q_go_t(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part,
                              hipStream_t st) {
   int kc = 0;
   const int S = part ? dma8q_plan(M, W.n_total, W.K, &kc) : 1;
-  return S > 1 ? dma8q_go1<OM, TBM, true>(A, M, W, out, part, kc, S, st)
-               : dma8q_go1<OM, TBM, false>(A, M, W, out, nullptr, 0, 1, st);
+  return S > 1 ? dma8q_go1<OM, TBM, true, MI>(A, M, W, out, part, kc, S, st)
+               : dma8q_go1<OM, TBM, false, MI>(A, M, W, out, nullptr, 0, 1, st);
 }
 
 template <int OM>
 static hipError_t dma8q_go(const ASrc &A, int M, const WSet &W, const OutSpec &out, float *part,
                            hipStream_t st) {
-  return q8_tbm(M, W.n_total) == 64 ? dma8q_go_t<OM, 64>(A, M, W, out, part, st)
-                         : dma8q_go_t<OM, 128>(A, M, W, out, part, st);
+  if (q8_tbm(M, W.n_total) == 128) return dma8q_go_t<OM, 128, 4>(A, M, W, out, part, st);
+  return M <= 32 ? dma8q_go_t<OM, 64, 2>(A, M, W, out, part, st) : dma8q_go_t<OM, 64, 4>(A, M, W, out, part, st);
 }
 
 // Q8_0 weights through the ring above: bf16 activations, k-ranges of whole

@@ -197,13 +197,15 @@ def test_inject_q8_0_batched_rows():
     run_inject(cfg_small(4, d=512, d_t=256, L_t=3, Hkv=2, capacity=256), 40, 9)
 
 
-@pytest.mark.parametrize("d,d_t,L_t,n", [(576, 320, 3, 100), (448, 192, 2, 300), (640, 128, 4, 17)])
+@pytest.mark.parametrize("d,d_t,L_t,n", [(576, 320, 3, 100), (448, 192, 2, 300), (640, 128, 4, 17),
+                                          (512, 256, 3, 32)])
 def test_inject_q8_0_ring_shapes(d, d_t, L_t, n):
     """Q8_0 weights with 17 ... 767 rows through the direct-to-LDS ring of raw
     codes: a ragged last 256-column tile (d = 576, 448, 640), k-splits of
     several 64-wide steps (K = 960, 576, 512, 640), the unsplit form (K = 384
-    and 448, fewer than eight steps), ragged 128-row tiles (100, 300, 17
-    rows), activation sources of 320, 192 and 128 columns."""
+    and 448, fewer than eight steps), ragged row tiles (100, 300, 17, 32
+    rows; 17 and 32 rows multiply two 16-row fragments per wave), activation
+    sources of 320, 192, 128 and 256 columns."""
     run_inject(cfg_small(4, d=d, d_t=d_t, L_t=L_t, Hkv=2, capacity=512), n, 7)
 
 
