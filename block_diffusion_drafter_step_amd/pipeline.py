@@ -3,8 +3,8 @@
 `to_device` moves the seeded inputs of synth.Workload onto the GPU in the
 storage formats libdflash reads; `BlockStep` owns the outputs and
 workspaces of one block step and enqueues the library calls: in order on
-one stream, or (run) with the injection on a second stream beside the conv
-and the attention's projection.  No arithmetic of the method happens here.
+one stream, or (run(overlap=True)) with the injection on a second stream
+beside the conv and the attention's projection.  No arithmetic of the method happens here.
 """
 from __future__ import annotations
 
@@ -93,8 +93,8 @@ class BlockStep:
                  D.dflash_selector_edges_workspace(B, cfg.r, d, cfg.K),
                  D.dflash_topk_select_workspace(B, cfg.V, cfg.K, cfg.r, d)]
         # one workspace reused by the calls of the main stream (stream-ordered);
-        # the injection has its own, as run() overlaps it with the conv and
-        # the attention's projection
+        # the injection has its own, as run(overlap=True) overlaps it with the
+        # conv and the attention's projection
         self.ws = D.workspace(max(sizes), device)
         if inject_n:
             self.ws_inj = D.workspace(D.dflash_inject_workspace(cfg.L_t, inject_n, cfg.d_t, d, cfg.kv, cfg.act),

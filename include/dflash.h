@@ -232,9 +232,11 @@ dflash_status dflash_block_attn(const void *u, const void *residual, int32_t B, 
  * that reads the cache.  "Turbo dflash", Deferred KV Injection
  * Optimization (the injection and the draft's own work are separate
  * steps): the projection of the block does not depend on the injection, so
- * the two can overlap.  cache_ready NULL -> DFLASH_ERR_INVALID_ARG.  The
- * workspace is this call's alone while the event is pending: the injection
- * that overlaps it needs a workspace of its own. */
+ * the two can overlap.  cache_ready NULL -> DFLASH_ERR_INVALID_ARG (before
+ * any HIP call); an event handle HIP rejects -> DFLASH_ERR_LAUNCH after the
+ * projection was enqueued (only the workspace is written).  The workspace
+ * is this call's alone while the event is pending: the injection that
+ * overlaps it needs a workspace of its own. */
 dflash_status dflash_block_attn_after(const void *u, const void *residual, int32_t B, int32_t d,
                                       int32_t n_q_heads, int32_t act, const dflash_weight *wq,
                                       const dflash_weight *wk, const dflash_weight *wv,
