@@ -713,10 +713,13 @@ __global__ __launch_bounds__(256) void selector_path_kernel(SelArgs a) {
 // A and candidate rows of B into LDS (16-byte loads issued together), so
 // that the last workgroup to finish (completion counter) finds them there.
 // It sums the slices in slice order (the projection never depends on
-// arrival order), forms all B x K x K edges (one edge per thread, 16-element
-// chunks of each dot product read from LDS at once, the same arithmetic as
-// selector_edges_kernel), writes them, and runs the max-sum recursion in one
-// wave: lane b holds state b and its back-pointers (8 bits per position).
+// arrival order), forms all B x K x K edges (two edges of one predecessor
+// per thread, 16-element chunks of each dot product read from LDS at once,
+// the same arithmetic as selector_edges_kernel), writes them, and runs the
+// max-sum recursion in one wave: lane b holds state b and its back-pointers
+// (8 bits per position).  In the top-K + selector kernel the last
+// workgroup loads the slices together with the merged ids and gathers the
+// candidate rows after them.
 // The hand-over of the slices follows the skinny GEMMs' (agent-scope
 // stores, release before the arrival, acquire by the last workgroup).
 //

@@ -148,7 +148,8 @@ typedef struct {
  * [pos0, pos0 + n_tokens) are not touched.  From 768 tokens on, the
  * workspace also holds bf16 copies of fc, Wk and Wv (2 bytes per weight,
  * reserved whatever their dtype): Q8_0 weights are expanded there once per
- * call, to the same bf16 values the per-tile dequantisation would give. */
+ * call, to the same bf16 values, bf16_rne(fp32(scale) * code), that the
+ * products of fewer rows form as they read the codes. */
 dflash_status dflash_inject(const void *const *layer_hidden, int32_t n_layers, int64_t n_tokens,
                             int32_t d_t, int32_t act, const dflash_weight *fc, const void *gamma,
                             float eps, const dflash_weight *wk, const dflash_weight *wv,
