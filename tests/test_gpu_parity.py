@@ -241,6 +241,16 @@ def test_inject_deterministic(n):
     assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
 
 
+def test_inject_q8_0_ring_deterministic():
+    """Q8_0 weights on the ring of raw codes (40 rows, 64-row tiles split
+    along k): two calls, the second on a workspace of random bytes, give
+    bitwise-equal caches (the partials are summed in k-piece order)."""
+    cfg = cfg_small(4, d=512, d_t=256, L_t=3, Hkv=2, capacity=256)
+    a, _, _ = run_inject(cfg, 40, 3, tag="detq")
+    b, _, _ = run_inject(cfg, 40, 3, tag="detq", garbage_seed=40)
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+
+
 def test_inject_garbage_workspace():
     """A workspace full of random bytes (any stale completion counter) gives
     correct rows: the counters carry each launch's own stamp."""
