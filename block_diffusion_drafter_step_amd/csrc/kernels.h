@@ -115,7 +115,7 @@ hipError_t launch_kv_quant(const float *kv, int n, int Hkv, int hd, long cap, lo
 hipError_t launch_silu_mul(int act, const float *gu, long M, int F, void *out, hipStream_t st);
 hipError_t launch_conv(int act, const void *x, int n_blocks, int B, int C, int G, int T,
                        const void *base, const float *delta, void *out, hipStream_t st);
-// The whole conv of at most 16 rows (n_blocks * B <= 16, (C / G) % 8 == 0)
+// The whole conv of at most 16 rows (n_blocks * B <= 16, (C / G) % 4 == 0)
 // in one launch: delta = x . W_delta^T is formed per tile of groups and the
 // last workgroup of a tile applies the taps to the tile's columns.
 // conv_fused_ok says whether it applies, conv_fused_part_bytes the

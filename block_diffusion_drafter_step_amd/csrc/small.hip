@@ -413,8 +413,9 @@ static void conv_launch_t(const void *x, int n_blocks, int B, int C, int G, int 
 // order; with several k-groups each writes a partial and the last to finish
 // (completion counter cnt[tile]) sums them in k-group order, as the small
 // skinny GEMMs do.  That workgroup then applies the taps to the tile's
-// columns: one thread per (row, 8 columns), the same arithmetic in the same
-// order as conv_pos_kernel.
+// columns: one thread per (row, CV columns of one group; CV = 8, or 4 when
+// C / G is a multiple of 4 only), the same arithmetic in the same order as
+// conv_pos_kernel.
 // ---------------------------------------------------------------------------
 struct ConvFusedArgs {
   const void *x, *base, *wd;
@@ -438,7 +439,7 @@ static void conv_fused_plan(int C, int G, int T, int *gpt, int *ntile, int *kchu
   *kgroups = (C + kConvFusedWaves * kc - 1) / (kConvFusedWaves * kc);
 }
 
-bool conv_fused_ok(int M, int C, int G, int T) { return M <= 16 && (C / G) % 8 == 0 && T <= 16; }
+bool conv_fused_ok(int M, int C, int G, int T) { return M <= 16 && (C / G) % 4 == 0 && T <= 16; }
 
 size_t conv_fused_part_bytes(int M, int C, int G, int T) {
   if (!conv_fused_ok(M, C, G, T)) return 0;
@@ -447,7 +448,39 @@ size_t conv_fused_part_bytes(int M, int C, int G, int T) {
   return kg > 1 ? (size_t)kg * ntile * 64 * sizeof(f32x4) : 0;
 }
 
-template <typename TA>
+// CV consecutive elements of a row (8, 16 or 32 bytes) as 8- or 16-byte
+// accesses
+template <typename TA, int CV>
+struct CVec {
+  TA v[CV];
+};
+template <typename TA, int CV>
+__device__ __forceinline__ CVec<TA, CV> cvec_load(const TA *p) {
+  constexpr int NB = CV * (int)sizeof(TA);
+  static_assert(NB == 8 || NB == 16 || NB == 32, "8, 16 or 32 bytes");
+  if constexpr (NB == 8) {
+    return __builtin_bit_cast(CVec<TA, CV>, *reinterpret_cast<const uint2 *>(p));
+  } else {
+    struct W { u32x4 q[NB / 16]; } w;
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) w.q[i] = reinterpret_cast<const u32x4 *>(p)[i];
+    return __builtin_bit_cast(CVec<TA, CV>, w);
+  }
+}
+template <typename TA, int CV>
+__device__ __forceinline__ void cvec_store(TA *p, const CVec<TA, CV> &c) {
+  constexpr int NB = CV * (int)sizeof(TA);
+  if constexpr (NB == 8) {
+    *reinterpret_cast<uint2 *>(p) = __builtin_bit_cast(uint2, c);
+  } else {
+    struct W { u32x4 q[NB / 16]; };
+    const W w = __builtin_bit_cast(W, c);
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) reinterpret_cast<u32x4 *>(p)[i] = w.q[i];
+  }
+}
+
+template <typename TA, int CV>
 __global__ __launch_bounds__(kConvFusedWaves * 64) void conv_fused_kernel(ConvFusedArgs a) {
   __shared__ f32x4 red[kConvFusedWaves][64];
   __shared__ float dl[16][16];   // delta of the tile: [row][lane row r16]
@@ -528,23 +561,25 @@ __global__ __launch_bounds__(kConvFusedWaves * 64) void conv_fused_kernel(ConvFu
   __syncthreads();
 
   // the taps on this tile's columns [g0 cpg, (g0 + ng) cpg): one thread per
-  // (row, 8 columns of one group)
-  const int cpg = C / G, vpg = cpg >> 3, nvec = M * ng * vpg;
+  // (row, CV columns of one group)
+  const int cpg = C / G, vpg = cpg / CV, nvec = M * ng * vpg;
   const TA *xp = reinterpret_cast<const TA *>(a.x);
   const TA *bp = reinterpret_cast<const TA *>(a.base);
   for (int e = tid; e < nvec; e += kConvFusedWaves * 64) {
     const int row = e / (ng * vpg), rem = e - row * (ng * vpg), gq = rem / vpg;
-    const int c = (g0 + gq) * cpg + (rem - gq * vpg) * 8;
+    const int c = (g0 + gq) * cpg + (rem - gq * vpg) * CV;
     const int i = row % a.B;
-    float o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float oc[CV];
+#pragma unroll
+    for (int j = 0; j < CV; ++j) oc[j] = 0.f;
     // taps in fours, their loads issued together; t ascending
     for (int t0 = 0; t0 < T; t0 += 4) {
-      Frag<TA> xr[4], bv[4];
+      CVec<TA, CV> xr[4], bv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = min(t0 + u, T - 1), tt = min(t, i);   // taps past T or the block start: valid rows, unused
-        xr[u] = load_frag(xp + (long)(row - tt) * C + c);
-        bv[u] = load_frag(bp + (long)t * C + c);
+        xr[u] = cvec_load<TA, CV>(xp + (long)(row - tt) * C + c);
+        bv[u] = cvec_load<TA, CV>(bp + (long)t * C + c);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -552,14 +587,14 @@ __global__ __launch_bounds__(kConvFusedWaves * 64) void conv_fused_kernel(ConvFu
         if (t < T && t <= i) {
           const float dv = dl[row][gq * T + t];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) o8[j] += (to_f32(bv[u].v[j]) + dv) * to_f32(xr[u].v[j]);
+          for (int j = 0; j < CV; ++j) oc[j] += (to_f32(bv[u].v[j]) + dv) * to_f32(xr[u].v[j]);
         }
       }
     }
-    Frag<TA> o;
+    CVec<TA, CV> o;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o.v[j] = from_f32<TA>(o8[j]);
-    store_frag(reinterpret_cast<TA *>(a.out) + (long)row * C + c, o);
+    for (int j = 0; j < CV; ++j) o.v[j] = from_f32<TA>(oc[j]);
+    cvec_store<TA, CV>(reinterpret_cast<TA *>(a.out) + (long)row * C + c, o);
   }
 }
 
@@ -584,10 +619,15 @@ hipError_t launch_conv_fused(int act, const void *x, int n_blocks, int B, int C,
   a.C = C;
   a.G = G;
   a.T = T;
-  if (act == ACT_F32)
-    hipLaunchKernelGGL(conv_fused_kernel<float>, dim3(ntile, kg), dim3(kConvFusedWaves * 64), 0, st, a);
-  else
-    hipLaunchKernelGGL(conv_fused_kernel<bf16>, dim3(ntile, kg), dim3(kConvFusedWaves * 64), 0, st, a);
+  const dim3 grid(ntile, kg), block(kConvFusedWaves * 64);
+  const bool c8 = (C / G) % 8 == 0;
+  if (act == ACT_F32) {
+    if (c8) hipLaunchKernelGGL((conv_fused_kernel<float, 8>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((conv_fused_kernel<float, 4>), grid, block, 0, st, a);
+  } else {
+    if (c8) hipLaunchKernelGGL((conv_fused_kernel<bf16, 8>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((conv_fused_kernel<bf16, 4>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

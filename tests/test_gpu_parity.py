@@ -307,7 +307,7 @@ def test_conv_group_spans_and_long_filters():
 
 def test_conv_one_launch_shapes():
     """At most 16 rows with whole 8-channel chunks per group take the
-    one-launch kernel (delta formed per tile of groups, the last workgroup
+    one-launch kernel with 8-column taps (delta formed per tile of groups, the last workgroup
     of a tile applies the taps): T = 16 (one group per tile), T = 5 and 3
     (tiles of 3 and 5 groups, 15 of 16 rows used, a short last tile), two
     blocks of 8, fp32, and the Qwen-27B width with one k-group per wave
@@ -318,6 +318,16 @@ def test_conv_one_launch_shapes():
     run_conv(cfg_small(1, C=1024, G=32, T=4, B=8), 2, tag="conv1l2b")
     run_conv(cfg_small(0, C=256, G=8, T=6, B=16), 1, tag="conv1lf")
     run_conv(configs.get(2), 1, tag="conv1lq")
+
+
+def test_conv_one_launch_four_channel_chunks():
+    """Groups of a multiple of 4 but not 8 channels (C / G = 20, 12, and the
+    Q8_0 workload's 84) take the one-launch kernel with 4-column taps: bf16
+    (8-byte loads), fp32 (16-byte loads), one block of 8 rows and two of 8."""
+    run_conv(cfg_small(1, C=320, G=16, T=4, B=16), 1, tag="conv4c20")
+    run_conv(cfg_small(0, C=192, G=16, T=3, B=16), 1, tag="conv4c12f")
+    run_conv(configs.get(4), 1, tag="conv4cq")
+    run_conv(cfg_small(4, B=8), 2, tag="conv4cq2")
 
 
 def test_conv_batched_32k_tokens():
