@@ -289,6 +289,13 @@ struct SkinnyPlan {
 #ifndef DFL_SKINNY_WPG
 #define DFL_SKINNY_WPG 8
 #endif
+// Smaller weights aim at fewer waves: for the Wk|Wv product into the cache
+// (128 tiles, K = 5120) 8 waves per tile cover the whole k-range, so each
+// tile's sum stays in its workgroup and no partials or arrivals are needed
+// (2048 waves took two k-groups per tile and a last-arriver hand-over).
+#ifndef DFL_SKINNY_SMALL_WAVES
+#define DFL_SKINNY_SMALL_WAVES 1024
+#endif
 #ifndef DFL_SKINNY_TPW_LONGK
 #define DFL_SKINNY_TPW_LONGK 4
 #endif
@@ -316,7 +323,7 @@ static SkinnyPlan skinny_plan(int N, int K, bool f32, int align = 64) {
     p.tpw = 1;
     p.wpg = DFL_SKINNY_WPG;
     p.groups = ntile;
-    int kw = (DFL_SKINNY_WAVES + p.groups - 1) / p.groups;   // waves per tile
+    int kw = (DFL_SKINNY_SMALL_WAVES + p.groups - 1) / p.groups;   // waves per tile
     const int kw_max = (K + 127) / 128;
     if (kw > kw_max) kw = kw_max;
     if (kw < p.wpg) kw = p.wpg;

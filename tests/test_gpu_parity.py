@@ -234,8 +234,9 @@ def test_inject_q8_0_around_expansion_threshold(n):
 @pytest.mark.parametrize("n", [16, 64])
 def test_inject_deterministic(n):
     """Bitwise-equal caches from two calls: the counter-based small-weight
-    GEMM (16 rows) and the split-K tile path (64 rows) sum in a fixed order."""
-    cfg = cfg_small(1, capacity=256)
+    GEMM (16 rows; two KV heads make Wk|Wv 512 rows, four k-groups per tile)
+    and the split-K tile path (64 rows) sum in a fixed order."""
+    cfg = cfg_small(1, Hkv=2, capacity=256)
     a, _, _ = run_inject(cfg, n, 3, tag="det")
     b, _, _ = run_inject(cfg, n, 3, tag="det", garbage_seed=n)
     assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
@@ -255,6 +256,7 @@ def test_inject_garbage_workspace():
     """A workspace full of random bytes (any stale completion counter) gives
     correct rows: the counters carry each launch's own stamp."""
     run_inject(cfg_small(1, capacity=256), 16, 40, garbage_seed=7, tag="garb")
+    run_inject(cfg_small(1, Hkv=2, capacity=256), 16, 40, garbage_seed=9, tag="garb")
     run_inject(cfg_small(0, capacity=256), 16, 40, garbage_seed=8, tag="garb")
 
 
