@@ -98,7 +98,64 @@ __device__ __forceinline__ int seg_of(const WSet &W, int n, int *local) {
 // agent-scope acquire fence before a second barrier, so every partial
 // happens-before the loads that sum them (on gfx950: buffer_wbl2 sc1 before
 // each arrival, buffer_inv sc1 once per tile group, sc1 loads and stores).
-template <typename TA, int WK, int TPW, int WPG, bool SPLIT_TILES>
+// Q8_0 weights whose k-ranges all lie on 256-element boundaries (K,
+// k_per_src and the k-chunks multiples of 256): chunks come in pairs, and the
+// even chunk of a pair takes each tile's eight block scales (both chunks')
+// in one 16-byte load, handing the odd chunk its two through registers, so a
+// pair issues one scale load per tile instead of two.
+template <typename TA, int TPW, bool EVEN>
+__device__ __forceinline__ void chunk_load_q8p(Chunk<TA, W_Q8_0_S4, TPW, 4> &ch, float (&snext)[TPW][2],
+                                               const TA *xr, const SRow<TA, W_Q8_0_S4> (&rows)[TPW], int cnt,
+                                               int k, int g, bool tok_ok) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int off = k + 64 * (j >> 1) + 16 * g + 8 * (j & 1);
+    ch.b[j] = tok_ok ? load_frag(reinterpret_cast<const bf16 *>(xr) + off) : frag_zero<bf16>();
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    if (u < cnt) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        ch.c[u][m] = wload16(reinterpret_cast<const int8_t *>(rows[u].p) + k + 64 * m + 16 * g);
+      if constexpr (EVEN) {
+        // blocks k/32 + 0..7; codes k + 64 m + 16 g (+ 128 for the odd chunk) use block 2 m + g / 2
+        const uint4 q = *reinterpret_cast<const uint4 *>(rows[u].s + (k >> 5));
+        const int sh = g < 2 ? 0 : 16;
+        ch.sc[u][0] = half_bits_to_f32((uint16_t)(q.x >> sh));
+        ch.sc[u][1] = half_bits_to_f32((uint16_t)(q.y >> sh));
+        snext[u][0] = half_bits_to_f32((uint16_t)(q.z >> sh));
+        snext[u][1] = half_bits_to_f32((uint16_t)(q.w >> sh));
+      } else {
+        ch.sc[u][0] = snext[u][0];
+        ch.sc[u][1] = snext[u][1];
+      }
+    }
+  }
+}
+
+// stream_range_g for such weights: (kb - ka) a multiple of 256, so the
+// double-buffered chunks alternate even (c0) and odd (c1) and no tail is left
+template <typename TA, int TPW>
+__device__ __forceinline__ void stream_range_q8p(const TA *xr, const SRow<TA, W_Q8_0_S4> (&rows)[TPW], int cnt,
+                                                 int ka, int kb, int g, bool tok_ok, f32x4 (&acc)[TPW]) {
+  const int n = (kb - ka) >> 7;
+  if (n <= 0) return;
+  int k = ka;
+  Chunk<TA, W_Q8_0_S4, TPW, 4> c0, c1;
+  float snext[TPW][2];
+  chunk_load_q8p<TA, TPW, true>(c0, snext, xr, rows, cnt, k, g, tok_ok);
+  for (int c = 0; c < n; c += 2) {
+    chunk_load_q8p<TA, TPW, false>(c1, snext, xr, rows, cnt, k + 128, g, tok_ok);
+    chunk_mma_g(c0, cnt, acc);
+    k += 128;
+    if (c + 2 < n) chunk_load_q8p<TA, TPW, true>(c0, snext, xr, rows, cnt, k + 128, g, tok_ok);
+    chunk_mma_g(c1, cnt, acc);
+    k += 128;
+  }
+}
+
+template <typename TA, int WK, int TPW, int WPG, bool SPLIT_TILES, bool Q8P = false>
 __global__ __launch_bounds__(WPG * 64, WPG >= 8 ? WPG / 4 : 2) void skinny_gemm_kernel(
     ASrc X, int M, WSet W, int kchunk, float *__restrict__ part,
     unsigned long long *__restrict__ cnt, unsigned long long stamp, OutSpec o) {
@@ -135,7 +192,10 @@ __global__ __launch_bounds__(WPG * 64, WPG >= 8 ? WPG / 4 : 2) void skinny_gemm_
     for (int s = k0 / kps; s * kps < k1; ++s) {
       const int ka = max(k0, s * kps), kb = min(k1, (s + 1) * kps);
       const TA *xr = reinterpret_cast<const TA *>(pick(X.ptr, s)) + trow - (long)s * kps;
-      stream_k<TA, WK, TPW>(xr, rows, tcnt, ka, kb, g, tok_ok, acc);
+      if constexpr (Q8P && WK == W_Q8_0_S4)
+        stream_range_q8p<TA, TPW>(xr, rows, tcnt, ka, kb, g, tok_ok, acc);
+      else
+        stream_k<TA, WK, TPW>(xr, rows, tcnt, ka, kb, g, tok_ok, acc);
     }
   }
 
@@ -268,6 +328,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 #ifndef DFL_Q8_SCALE_X4
 #define DFL_Q8_SCALE_X4 1   // Q8_0 skinny GEMMs: 8-byte scale loads where k-ranges allow
 #endif
+#ifndef DFL_Q8_SCALE_X8
+#define DFL_Q8_SCALE_X8 1   // ... and 16-byte ones per pair of chunks on split-tile plans
+#endif
 
 struct SkinnyPlan {
   int tpw, wpg, kchunk, kgroups, groups;
@@ -339,7 +402,7 @@ static SkinnyPlan skinny_plan(int N, int K, bool f32, int align = 64) {
 size_t skinny_partial_floats(int n_total, int K) {
   size_t most = 0;
   for (const bool f32 : {false, true})
-    for (const int align : {64, 128}) {
+    for (const int align : {64, 128, 256}) {
       const SkinnyPlan p = skinny_plan(n_total, K, f32, align);
       if (p.kgroups > 1) most = std::max(most, (size_t)p.kgroups * (size_t)((n_total + 15) / 16) * 256);
     }
@@ -377,12 +440,25 @@ unsigned long long next_launch_stamp() {
 template <typename TA, int WK>
 static hipError_t skinny_launch_t(const ASrc &X, int M, const WSet &W, float *part,
                                   unsigned long long *cnt, const OutSpec &out, hipStream_t st) {
-  const SkinnyPlan p = skinny_plan(W.n_total, W.K, sizeof(TA) == 4, WK == W_Q8_0_S4 ? 128 : 64);
+  // Q8_0 split-tile plans on 256 boundaries take the paired scale loads
+  bool q8p = WK == W_Q8_0_S4 && DFL_Q8_SCALE_X8 && W.K % 256 == 0 && X.k_per_src % 256 == 0 &&
+             (W.n_total + 15) / 16 >= DFL_SKINNY_BIG_TILES;
+  for (int i = 0; q8p && i < W.n_seg; ++i) q8p = reinterpret_cast<uintptr_t>(W.scales[i]) % 16 == 0;
+  const SkinnyPlan p = skinny_plan(W.n_total, W.K, sizeof(TA) == 4, q8p ? 256 : WK == W_Q8_0_S4 ? 128 : 64);
   const dim3 grid(p.groups, p.kgroups);
   unsigned long long *c = nullptr;
   unsigned long long stamp = 0;
   if (p.split_tiles) {
-    if (sizeof(TA) == 2 && p.tpw == 4)
+    if (q8p) {
+      if constexpr (WK == W_Q8_0_S4) {
+        if (p.tpw == 4)
+          hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 4, 4, true, true>), grid, dim3(256), 0, st, X, M, W,
+                             p.kchunk, part, c, stamp, out);
+        else
+          hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, 2, 4, true, true>), grid, dim3(256), 0, st, X, M, W,
+                             p.kchunk, part, c, stamp, out);
+      }
+    } else if (sizeof(TA) == 2 && p.tpw == 4)
       hipLaunchKernelGGL((skinny_gemm_kernel<TA, WK, sizeof(TA) == 2 ? 4 : 2, 4, true>), grid,
                          dim3(256), 0, st, X, M, W, p.kchunk, part, c, stamp, out);
     else if (p.tpw == 2)
